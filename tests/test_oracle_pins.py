@@ -1,0 +1,459 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Each test checks the oracle against something other than itself: values the
+pages print (fixtures under tests/golden, each with its citation), independent
+library decoders (torch's float8 E4M3FN / E8M0 types), exact rational
+arithmetic, brute-force nearest-point search, and invariants of the method.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import bf16_bits, bf16_to_f32
+from tests.conftest import read_golden
+
+# Independent decode tables from torch's float8 types (library routines).
+E4M3_TABLE = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+E8M0_TABLE = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).double().numpy()
+
+# Magnitudes of the printed E2M1 code set in ascending order (index = magnitude code).
+PRINTED_MAGS = np.array(sorted({abs(float(v)) for v in read_golden("e2m1_code_set.txt")["_values"]}))
+
+
+def all_positive_finite_bf16():
+    bits = np.arange(1, 0x7F80, dtype=np.uint16)      # +subnormals .. max finite
+    return bits
+
+
+def brute_codes(x_bits, d):
+    """Nearest magnitude index to |x|/d by exhaustive search, ties to even index."""
+    ax = np.abs(bf16_to_f32(x_bits).astype(np.float64))
+    dist = np.abs(ax[..., None] - PRINTED_MAGS[None, :] * np.asarray(d, dtype=np.float64)[..., None])
+    best = dist.min(axis=-1, keepdims=True)
+    cand = dist == best
+    # among tied candidates the even index wins; there are at most two, adjacent
+    idx = np.where(cand[..., ::2].any(axis=-1),
+                   np.argmax(cand[..., ::2], axis=-1) * 2,
+                   np.argmax(cand, axis=-1))
+    sign = (x_bits >> 15).astype(np.uint8)
+    return (sign << 3) | idx.astype(np.uint8)
+
+
+def unpack(codes):
+    lo = codes & 0xF
+    hi = codes >> 4
+    out = np.empty(codes.shape[:-1] + (codes.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+# --------------------------------------------------------------- formats
+
+def test_e2m1_decode_equals_printed_set():
+    printed = sorted(float(v) for v in read_golden("e2m1_code_set.txt")["_values"])
+    decoded = sorted(oracle.e2m1_value(c) for c in range(16))
+    assert decoded == printed
+    assert len({oracle.e2m1_value(c) for c in range(16)}) == 15      # +0 and -0 collapse
+    # sign is the top bit of the nibble; magnitudes increase with the low three bits
+    for c in range(8):
+        assert oracle.e2m1_value(c) == PRINTED_MAGS[c]
+        assert oracle.e2m1_value(c | 8) == -PRINTED_MAGS[c]
+
+
+def test_e4m3_decode_matches_library_and_printed_ceiling():
+    g = read_golden("scale_overflow.txt")
+    for b in range(256):
+        ref = E4M3_TABLE[b]
+        got = oracle.e4m3_value(b)
+        if math.isnan(ref):
+            assert math.isnan(got), hex(b)
+        else:
+            assert got == ref, hex(b)
+    finite = [oracle.e4m3_value(b) for b in range(0x7F)]
+    assert max(finite) == float(g["e4m3_max"]) == oracle.e4m3_value(0x7E)
+
+
+def test_e8m0_decode_matches_library():
+    for b in range(256):
+        ref, got = E8M0_TABLE[b], oracle.e8m0_value(b)
+        if math.isnan(ref):
+            assert math.isnan(got)
+        else:
+            assert got == ref
+
+
+def _e4m3_brute(v):
+    """Nearest finite non-negative E4M3 byte by exhaustive search, ties to even byte;
+    beyond the grid (> 464, the midpoint to the next step of 32) -> None (overflow)."""
+    vals = E4M3_TABLE[:0x7F]
+    d = np.abs(v[:, None] - vals[None, :])
+    best = d.min(axis=1, keepdims=True)
+    cand = d == best
+    even = cand[:, ::2].any(axis=1)
+    idx = np.where(even, np.argmax(cand[:, ::2], axis=1) * 2, np.argmax(cand, axis=1))
+    return idx.astype(np.uint8), v > 464.0
+
+
+def test_e4m3_rounding_brute_force_and_library():
+    rng = np.random.default_rng(1)
+    mant_hi = np.arange(128, dtype=np.uint32) << 16
+    lows = np.array([0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF], dtype=np.uint32)
+    exps = np.arange(100, 137, dtype=np.uint32) << 23          # 2^-27 .. 2^9
+    bits = (exps[:, None, None] | mant_hi[None, :, None] | lows[None, None, :]).reshape(-1)
+    f32 = np.concatenate([bits.view(np.float32),
+                          rng.uniform(0, 600, 200_000).astype(np.float32),
+                          np.array([448, 464, 465, 480, 2 ** -10, 2 ** -9, 2 ** -6], np.float32)])
+    v = f32.astype(np.float64)
+    got_nonsat = oracle.e4m3_from_real(v, saturate=False)
+    got_sat = oracle.e4m3_from_real(v, saturate=True)
+    ref, over = _e4m3_brute(v)
+    assert np.array_equal(got_nonsat[~over], ref[~over])
+    assert np.all(got_nonsat[over] == 0x7F)
+    assert np.array_equal(got_sat, np.where(over, 0x7E, ref))
+    # torch's float32 -> float8_e4m3fn cast (round to nearest even, NaN past 464)
+    lib = torch.from_numpy(f32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    lib = np.where(np.isnan(torch.from_numpy(f32).to(torch.float8_e4m3fn).float().numpy()), 0x7F, lib)
+    assert np.array_equal(got_nonsat, lib)
+    # the printed boundary cases
+    assert list(oracle.e4m3_from_real([448.0, 464.0, 465.0], saturate=False)) == [0x7E, 0x7E, 0x7F]
+
+
+def _fp32_round_exact(fr: Fraction) -> np.float32:
+    """Correctly rounded binary32 of a positive rational (ties to even), by search."""
+    f = np.float32(float(fr))
+    best = None
+    for c in (np.nextafter(f, np.float32(0)), f, np.nextafter(f, np.float32(np.inf))):
+        dist = abs(Fraction(float(c)) - fr)
+        even = (int(np.array(c, np.float32).view(np.uint32)) & 1) == 0
+        key = (dist, not even)
+        if best is None or key < best[0]:
+            best = (key, c)
+    return np.float32(best[1])
+
+
+def test_tensor_scale_is_correctly_rounded_quotient():
+    bits = all_positive_finite_bf16()[::7]
+    for b in bits:
+        g = Fraction(oracle.bf16_value(int(b)))
+        want = _fp32_round_exact(g / 2688)
+        got = oracle.tensor_scale(np.array([[b]], dtype=np.uint16))
+        assert got == want, hex(int(b))
+    assert oracle.tensor_scale(np.zeros((1, 16), np.uint16)) == np.float32(1.0)
+
+
+# --------------------------------------------------------- element rounding
+
+def test_element_rounding_exhaustive_over_bf16_and_scales():
+    """Every finite bf16 |x| <= 6 s against every positive finite E4M3 s (S_t = 1):
+    the oracle's code equals the exhaustive nearest-point search."""
+    pos = all_positive_finite_bf16()
+    pos_val = bf16_to_f32(pos).astype(np.float64)
+    blocks, expect = [], []
+    for sb in range(1, 0x7F):
+        s = E4M3_TABLE[sb]
+        top = bf16_bits(np.array([6.0 * s], np.float32))[0]
+        assert float(bf16_to_f32(np.array([top]))[0]) == 6.0 * s
+        xs = pos[pos_val <= 6.0 * s]
+        xs = np.concatenate([np.array([0, 0x8000], np.uint16), xs, xs | 0x8000])
+        pad = (-len(xs)) % 15
+        xs = np.concatenate([xs, np.zeros(pad, np.uint16)]).reshape(-1, 15)
+        blk = np.concatenate([np.full((xs.shape[0], 1), top, np.uint16), xs], axis=1)
+        blocks.append(blk)
+        expect.append(np.full(xs.shape[0], sb))
+    blocks = np.concatenate(blocks)
+    expect_s = np.concatenate(expect)
+    q = oracle.quantize_nvfp4(blocks, mode=oracle.NAIVE)
+    assert q.tensor_scale == 1.0
+    assert np.array_equal(q.scales[:, 0], expect_s)
+    codes = unpack(q.codes)
+    ref = brute_codes(blocks, E4M3_TABLE[expect_s][:, None] * np.ones((1, 16)))
+    assert np.array_equal(codes, ref)
+
+
+def test_element_rounding_with_random_tensor_scales():
+    rng = np.random.default_rng(7)
+    for trial in range(20):
+        scale = float(2.0 ** rng.uniform(-30, 30))
+        x = bf16_bits(rng.standard_normal((64, 256)).astype(np.float32) * np.float32(scale))
+        q = oracle.quantize_nvfp4(x, mode=oracle.DYNAMIC)
+        st = float(q.tensor_scale)
+        d = E4M3_TABLE[q.scales].repeat(16, axis=1) * st
+        assert np.array_equal(unpack(q.codes), brute_codes(x, d))
+        # block scale = nearest E4M3 to a_b / (6 S_t), by exhaustive search (saturating)
+        ab = np.abs(bf16_to_f32(x).astype(np.float64)).reshape(64, 16, 16).max(axis=2)
+        ref, over = _e4m3_brute((ab / (6.0 * st)).reshape(-1))
+        assert not over.any()
+        assert np.array_equal(q.scales.reshape(-1), ref)
+
+
+# ---------------------------------------------- printed worked examples
+
+def test_max12_and_max24_thresholds():
+    g = read_golden("nvfp4_thresholds.txt")
+    mx = float(g["block_max"])
+    pos = all_positive_finite_bf16()
+    vals = bf16_to_f32(pos).astype(np.float64)
+    xs = pos[vals < mx]
+    n = len(xs) - len(xs) % 15
+    xs = xs[:n].reshape(-1, 15)
+    top = bf16_bits(np.array([mx], np.float32))[0]
+    blk = np.concatenate([np.full((xs.shape[0], 1), top, np.uint16), xs], axis=1)
+    q = oracle.quantize_nvfp4(blk, mode=oracle.NAIVE)
+    assert np.all(q.scales == int(g["scale_byte"], 16))
+    assert oracle.e4m3_value(int(g["scale_byte"], 16)) == float(g["scale_value"])
+    xhat = np.abs(oracle.dequantize(q))[:, 1:]
+    xv = np.abs(bf16_to_f32(blk).astype(np.float64))[:, 1:]
+    thr = float(g["zero_threshold"])
+    assert thr == mx / 24
+    assert np.all(xhat[xv < thr] == 0)
+    assert np.all(xhat[xv == thr] == 0)                 # tie -> even code (zero)
+    assert np.all(xhat[xv > thr] >= float(g["smallest_nonzero"]))
+    assert float(g["smallest_nonzero"]) == mx / 12
+    assert xhat[xhat > 0].min() == mx / 12
+
+
+def test_1000_outlier_zeroes_its_fifteen_neighbours():
+    g = read_golden("outlier_1000.txt")
+    rng = np.random.default_rng(0)
+    nb = rng.standard_normal(15).astype(np.float32)
+    assert np.abs(nb).max() < 4
+    x = bf16_bits(np.concatenate([[np.float32(g["outlier"])], nb])[None, :])
+    q = oracle.quantize_nvfp4(x, mode=oracle.NAIVE)
+    assert q.scales[0, 0] == int(g["naive_scale_byte"], 16)
+    assert oracle.e4m3_value(q.scales[0, 0]) == float(g["naive_scale_value"])
+    codes = unpack(q.codes)[0]
+    assert codes[0] == int(g["outlier_code"], 16)
+    assert oracle.dequantize(q)[0, 0] == float(g["outlier_reconstruction"])
+    assert np.all((codes[1:] & 7) == int(g["neighbour_code_magnitude"]))
+    # two-level (dynamic) scaling on the same single-block tensor: same fate
+    qd = oracle.quantize_nvfp4(x, mode=oracle.DYNAMIC)
+    assert qd.scales[0, 0] == 0x7E
+    assert np.all((unpack(qd.codes)[0, 1:] & 7) == 0)
+    assert abs(oracle.dequantize(qd)[0, 0] - 1000.0) < 1000.0 / 16
+    # MXFP4's 32-value block: the same outlier zeroes 31 neighbours
+    nb31 = rng.standard_normal(31).astype(np.float32)
+    xm = bf16_bits(np.concatenate([[np.float32(g["outlier"])], nb31])[None, :])
+    qm = oracle.quantize_mxfp4(xm)
+    assert np.all((unpack(qm.codes)[0, 1:] & 7) == 0)
+
+
+def test_scale_overflow_past_2688():
+    g = read_golden("scale_overflow.txt")
+    assert float(g["overflow_threshold"]) == 6 * float(g["e4m3_max"])
+    assert round(float(g["probe_block_max"]) / 6) == int(g["probe_scale"])
+    rng = np.random.default_rng(3)
+    for case in g["naive_cases"].split(","):
+        mx, want = case.strip().split(":")
+        nb = rng.standard_normal(15).astype(np.float32)
+        x = bf16_bits(np.concatenate([[np.float32(mx)], nb])[None, :])
+        assert float(bf16_to_f32(x)[0, 0]) == float(mx)
+        q = oracle.quantize_nvfp4(x, mode=oracle.NAIVE)
+        if want == "nan":
+            assert q.scales[0, 0] == 0x7F
+            assert np.isnan(oracle.dequantize(q)).all()
+        else:
+            assert q.scales[0, 0] == int(want, 16)
+            assert oracle.dequantize(q)[0, 0] == 2688.0          # clipped below 2704
+        qd = oracle.quantize_nvfp4(x, mode=oracle.DYNAMIC)
+        assert qd.scales[0, 0] == 0x7E and np.isfinite(oracle.dequantize(qd)).all()
+
+
+# ----------------------------------------------------------- invariants
+
+def test_two_level_dynamic_invariant():
+    rng = np.random.default_rng(11)
+    for _ in range(10):
+        x = bf16_bits((rng.standard_t(3, (32, 512)) * 4).astype(np.float32))
+        q = oracle.quantize_nvfp4(x)
+        assert q.scales.max() == 0x7E                 # the block holding g lands on 448
+        assert np.all(q.scales <= 0x7E)
+        xv = bf16_to_f32(x).astype(np.float64)
+        g = np.abs(xv).max()
+        assert q.tensor_scale == np.float32(g / 2688)
+        ab = np.abs(xv).reshape(32, 32, 16).max(axis=2)
+        # nothing clips: every block maximum is within the block's grid
+        assert np.all(ab / (6.0 * float(q.tensor_scale)) <= 464.0)
+
+
+def test_block_max_maps_to_largest_code():
+    rng = np.random.default_rng(5)
+    x = bf16_bits((rng.standard_normal((256, 256)) * 2.0 ** rng.uniform(-8, 8, (256, 1)))
+                  .astype(np.float32))
+    q = oracle.quantize_nvfp4(x)
+    codes = unpack(q.codes).reshape(256, 16, 16)
+    xv = np.abs(bf16_to_f32(x).astype(np.float64)).reshape(256, 16, 16)
+    arg = xv.argmax(axis=2)
+    maxcode = np.take_along_axis(codes, arg[..., None], axis=2)[..., 0] & 7
+    normal = E4M3_TABLE[q.scales] >= 2.0 ** -6
+    assert normal.any()
+    assert np.all(maxcode[normal] == 7)
+
+
+def test_scale_equivariance_and_sign_symmetry():
+    rng = np.random.default_rng(9)
+    x = bf16_bits(rng.standard_normal((16, 512)).astype(np.float32))
+    xf = bf16_to_f32(x)
+    for k in (-20, -3, 1, 7, 30):
+        y = bf16_bits(xf * np.float32(2.0 ** k))
+        qx, qy = oracle.quantize_nvfp4(x), oracle.quantize_nvfp4(y)
+        assert np.array_equal(qx.codes, qy.codes) and np.array_equal(qx.scales, qy.scales)
+        assert qy.tensor_scale == np.float32(qx.tensor_scale * np.float32(2.0 ** k))
+        mx, my = oracle.quantize_mxfp4(x), oracle.quantize_mxfp4(y)
+        assert np.array_equal(mx.codes, my.codes)
+        assert np.array_equal(my.scales.astype(int), mx.scales.astype(int) + k)
+    neg = x ^ np.uint16(0x8000)
+    for quant in (oracle.quantize_nvfp4, oracle.quantize_mxfp4):
+        a, b = quant(x), quant(neg)
+        assert np.array_equal(a.scales, b.scales)
+        assert np.array_equal(unpack(a.codes) ^ 8, unpack(b.codes))
+
+
+def test_mxfp4_invariants():
+    rng = np.random.default_rng(13)
+    x = bf16_bits((rng.standard_normal((64, 1024)) * 2.0 ** rng.uniform(-20, 20, (64, 1)))
+                  .astype(np.float32))
+    q = oracle.quantize_mxfp4(x)
+    codes = unpack(q.codes).reshape(64, 32, 32)
+    xv = np.abs(bf16_to_f32(x).astype(np.float64)).reshape(64, 32, 32)
+    arg = xv.argmax(axis=2)
+    maxcode = np.take_along_axis(codes, arg[..., None], axis=2)[..., 0] & 7
+    assert set(np.unique(maxcode)) <= {6, 7}
+    scale = E8M0_TABLE[q.scales][..., None]
+    assert np.all((codes & 7)[xv < scale / 4] == 0)
+    # the scale is a power of two with the block maximum in [4, 8) of it
+    ab = xv.max(axis=2)
+    assert np.all((ab / scale[..., 0] >= 4) & (ab / scale[..., 0] < 8))
+    # re-quantizing the reconstruction reproduces it
+    xhat = oracle.dequantize(q)
+    q2 = oracle.quantize_mxfp4(bf16_bits(xhat.astype(np.float32)))
+    assert np.array_equal(q2.codes, q.codes) and np.array_equal(q2.scales, q.scales)
+
+
+def test_bits_per_value():
+    g = read_golden("bits_per_value.txt")
+    x = bf16_bits(np.random.default_rng(0).standard_normal((4, 1024)).astype(np.float32))
+    qn, qm = oracle.quantize_nvfp4(x), oracle.quantize_mxfp4(x)
+    assert (qn.codes.nbytes + qn.scales.nbytes) * 8 / x.size == float(g["nvfp4"])
+    assert (qm.codes.nbytes + qm.scales.nbytes) * 8 / x.size == float(g["mxfp4"])
+    assert qn.scales.shape[1] == 1024 // int(g["nvfp4_block"])
+    assert qm.scales.shape[1] == 1024 // int(g["mxfp4_block"])
+
+
+# --------------------------------------------- brute force on tiny tensors
+
+def _brute_nvfp4(xbits):
+    """Whole NVFP4 dynamic quantization by exact rational search (tiny inputs)."""
+    vals = [Fraction(float(v)) for v in bf16_to_f32(xbits).reshape(-1)]
+    g = max(abs(v) for v in vals)
+    st = Fraction(float(_fp32_round_exact(g / 2688))) if g > 0 else Fraction(1)
+    r, k = xbits.shape
+    finite = [(b, Fraction(float(E4M3_TABLE[b]))) for b in range(0x7F)]
+    codes, scales = np.zeros((r, k), np.uint8), np.zeros((r, k // 16), np.uint8)
+    for i in range(r):
+        for bidx in range(k // 16):
+            blk = vals[i * k + bidx * 16: i * k + bidx * 16 + 16]
+            target = max(abs(v) for v in blk) / (6 * st)
+            best = min(finite, key=lambda bv: (abs(bv[1] - target), bv[0] % 2))
+            if target > 464:
+                best = finite[0x7E]
+            scales[i, bidx] = best[0]
+            d = best[1] * st
+            for j, v in enumerate(blk):
+                if d == 0:
+                    mag = 0
+                else:
+                    dist = [(abs(abs(v) - Fraction(float(m)) * d), c % 2, c)
+                            for c, m in enumerate(PRINTED_MAGS)]
+                    mag = min(dist)[2]
+                sign = 1 if (int(xbits.reshape(-1)[i * k + bidx * 16 + j]) >> 15) else 0
+                codes[i, bidx * 16 + j] = (sign << 3) | mag
+    return codes, scales, np.float32(float(st))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_nvfp4_tiny_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    x = bf16_bits((rng.standard_t(2, (3, 48)) * 2.0 ** rng.uniform(-10, 10)).astype(np.float32))
+    q = oracle.quantize_nvfp4(x)
+    codes, scales, st = _brute_nvfp4(x)
+    assert q.tensor_scale == st
+    assert np.array_equal(q.scales, scales)
+    assert np.array_equal(unpack(q.codes), codes)
+
+
+# ------------------------------------------------------------------ GEMM
+
+def _torch_dequant(q):
+    """Dequantize with torch's decode tables (independent of the oracle's decoders)."""
+    nib = unpack(q.codes)
+    mags = PRINTED_MAGS[nib & 7] * np.where(nib & 8, -1.0, 1.0)
+    if q.fmt == oracle.NVFP4:
+        s = E4M3_TABLE[q.scales].repeat(16, axis=1)
+    else:
+        s = E8M0_TABLE[q.scales].repeat(32, axis=1)
+    return mags * s
+
+
+@pytest.mark.parametrize("fmt", [oracle.NVFP4, oracle.MXFP4])
+def test_gemm_equals_textbook_matmul(fmt):
+    rng = np.random.default_rng(21)
+    a = bf16_bits(rng.standard_normal((7, 96)).astype(np.float32))
+    w = bf16_bits((rng.standard_normal((5, 96)) * 0.02).astype(np.float32))
+    qa, qw = oracle.quantize(fmt, a), oracle.quantize(fmt, w)
+    ad, wd = _torch_dequant(qa), _torch_dequant(qw)
+    alpha = float(qa.tensor_scale) * float(qw.tensor_scale) if fmt == oracle.NVFP4 else 1.0
+    ref = alpha * (ad @ wd.T)
+    refl = alpha * (np.abs(ad) @ np.abs(wd).T)
+    c, l = oracle.gemm_loop(qa, qw)
+    c2, l2 = oracle.gemm(qa, qw)
+    assert np.allclose(c, ref, rtol=0, atol=1e-12 * refl.max())
+    assert np.allclose(l, refl, rtol=1e-14)
+    assert np.allclose(c2, ref, rtol=0, atol=1e-12 * refl.max())
+    rows, cols = np.array([0, 6, 3]), np.array([4, 0, 2])
+    cs, ls = oracle.gemm_sampled(qa, qw, rows, cols)
+    assert np.array_equal(cs, c[rows, cols]) and np.array_equal(ls, l[rows, cols])
+    # the dequantized tensor includes the per-tensor factor
+    if fmt == oracle.NVFP4:
+        assert np.array_equal(oracle.dequantize(qa), ad * float(qa.tensor_scale))
+
+
+def test_gemm_single_block_closed_form():
+    # A: one NVFP4 block of code 1.0 (0x2) with block scale 2 (0x40);
+    # W: one block of code 6.0 (0x7) with block scale 0.5 (0x30). Per-tensor 3 and 5.
+    qa = oracle.Quantized(oracle.NVFP4, np.full((1, 8), 0x22, np.uint8),
+                          np.array([[0x40]], np.uint8), 3.0, 16)
+    qw = oracle.Quantized(oracle.NVFP4, np.full((1, 8), 0x77, np.uint8),
+                          np.array([[0x30]], np.uint8), 5.0, 16)
+    c, l = oracle.gemm_loop(qa, qw)
+    assert c[0, 0] == 3.0 * 5.0 * 2.0 * 0.5 * 16 * 1.0 * 6.0
+    # all codes 1.0 with unit scales: C = K * alpha
+    k = 256
+    for fmt, sbyte in ((oracle.NVFP4, 0x38), (oracle.MXFP4, 127)):
+        bs = oracle.BLOCK[fmt]
+        q = oracle.Quantized(fmt, np.full((2, k // 2), 0x22, np.uint8),
+                             np.full((2, k // bs), sbyte, np.uint8),
+                             1.5 if fmt == oracle.NVFP4 else 1.0, k)
+        c, l = oracle.gemm_loop(q, q)
+        al = 2.25 if fmt == oracle.NVFP4 else 1.0
+        assert np.all(c == k * al) and np.all(l == k * al)
+    # sign: -1 x +1 over one block
+    qn = oracle.Quantized(oracle.MXFP4, np.full((1, 16), 0xAA, np.uint8),
+                          np.array([[127]], np.uint8), 1.0, 32)
+    qp = oracle.Quantized(oracle.MXFP4, np.full((1, 16), 0x22, np.uint8),
+                          np.array([[128]], np.uint8), 1.0, 32)
+    c, l = oracle.gemm_loop(qn, qp)
+    assert c[0, 0] == -64.0 and l[0, 0] == 64.0
+
+
+def test_bf16_ulp_and_tolerance():
+    assert oracle.bf16_ulp(np.array([1.0]))[0] == 2.0 ** -7
+    assert oracle.bf16_ulp(np.array([1.99]))[0] == 2.0 ** -7
+    assert oracle.bf16_ulp(np.array([-3.0]))[0] == 2.0 ** -6
+    assert oracle.bf16_ulp(np.array([0.0]))[0] == 2.0 ** -133
+    t = oracle.gemm_tolerance(np.array([2.0]), np.array([100.0]))
+    assert t[0] == 1e-3 + 2.0 ** -6
