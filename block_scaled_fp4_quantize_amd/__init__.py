@@ -1,0 +1,225 @@
+"""Python binding of the gfx950 W4A4 block-scaled FP4 library (``libfp4amd.so``).
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI
+declared in ``include/fp4.h``; PyTorch supplies device memory and the current
+stream. The functions carry the C names:
+
+    fp4_quantize_weight(w, fmt)                 -> Fp4Tensor (weight cache layout)
+    fp4_quantize_act(a, fmt, static_scale=None) -> Fp4Tensor (canonical layout)
+    fp4_gemm(a_q, w_q)                          -> bf16 [M, N] = A^ W^T
+    fp4_linear(x, w_q, static_scale=None)       -> bf16 [M, N]
+    fp4_export_canonical(w_q)                   -> Fp4Tensor (canonical copy)
+    fp4_dequantize(t)                           -> fp32 [rows, K]
+
+There is no CPU fallback: if the library is missing or the device is not
+gfx950, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+NVFP4, MXFP4 = 0, 1
+CANONICAL, WEIGHT_TILED = 0, 1
+FORMATS = {"nvfp4": NVFP4, "mxfp4": MXFP4}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp4amd.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fp4.h")
+
+
+class fp4_tensor(ctypes.Structure):
+    _fields_ = [
+        ("fmt", ctypes.c_int32),
+        ("layout", ctypes.c_int32),
+        ("rows", ctypes.c_int64),
+        ("cols", ctypes.c_int64),
+        ("codes_pitch", ctypes.c_int64),
+        ("scales_pitch", ctypes.c_int64),
+        ("codes", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("tensor_scale", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib():
+    """Load ``libfp4amd.so`` (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build the HIP library first "
+                "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        T = ctypes.POINTER(fp4_tensor)
+        sig = {
+            "fp4_block_size": (I32, [I32]),
+            "fp4_codes_bytes": (SZ, [I32, I32, I64, I64]),
+            "fp4_scales_bytes": (SZ, [I32, I32, I64, I64]),
+            "fp4_tensor_init": (I32, [T, I32, I32, I64, I64, P, P, P]),
+            "fp4_quantize_workspace_bytes": (SZ, [I32, I64, I64]),
+            "fp4_quantize_weight": (I32, [I32, P, I64, I64, T, P, SZ, P]),
+            "fp4_quantize_act": (I32, [I32, P, I64, I64, P, T, P, SZ, P]),
+            "fp4_gemm_workspace_bytes": (SZ, [I32, I64, I64, I64]),
+            "fp4_gemm": (I32, [T, T, P, I64, P, SZ, P]),
+            "fp4_linear_workspace_bytes": (SZ, [I32, I64, I64, I64]),
+            "fp4_linear": (I32, [P, I64, T, P, P, P, SZ, P]),
+            "fp4_export_canonical": (I32, [T, T, P]),
+            "fp4_dequantize": (I32, [T, P, I64, P]),
+            "fp4_status_string": (ctypes.c_char_p, [I32]),
+            "fp4_last_error": (ctypes.c_char_p, []),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+        return L
+
+
+class Fp4Error(RuntimeError):
+    pass
+
+
+def _check(status: int):
+    if status != 0:
+        L = lib()
+        raise Fp4Error("%s: %s" % (L.fp4_status_string(status).decode(),
+                                   L.fp4_last_error().decode()))
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _fmt(fmt) -> int:
+    if isinstance(fmt, str):
+        return FORMATS[fmt.lower()]
+    if fmt not in (NVFP4, MXFP4):
+        raise ValueError("format must be NVFP4 (0) or MXFP4 (1)")
+    return int(fmt)
+
+
+def _bf16_2d(x: torch.Tensor, name: str) -> torch.Tensor:
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda:
+        raise ValueError(f"{name} must be a 2-D bfloat16 CUDA tensor")
+    return x.contiguous()
+
+
+class Fp4Tensor:
+    """Quantized tensor: device buffers owned by torch plus the C descriptor."""
+
+    def __init__(self, fmt: int, layout: int, rows: int, k: int, device):
+        L = lib()
+        self.fmt, self.layout, self.rows, self.k = fmt, layout, rows, k
+        nc = L.fp4_codes_bytes(fmt, layout, rows, k)
+        ns = L.fp4_scales_bytes(fmt, layout, rows, k)
+        if nc == 0 or ns == 0:
+            raise ValueError("invalid FP4 tensor shape")
+        self.codes = torch.empty(nc, dtype=torch.uint8, device=device)
+        self.scales = torch.empty(ns, dtype=torch.uint8, device=device)
+        self.tensor_scale = torch.empty(1, dtype=torch.float32, device=device)
+        self.desc = fp4_tensor()
+        _check(L.fp4_tensor_init(ctypes.byref(self.desc), fmt, layout, rows, k,
+                                 _ptr(self.codes), _ptr(self.scales), _ptr(self.tensor_scale)))
+
+    @property
+    def device(self):
+        return self.codes.device
+
+    def codes_2d(self) -> torch.Tensor:
+        """Canonical codes as [rows, codes_pitch] bytes."""
+        assert self.layout == CANONICAL
+        return self.codes.view(self.rows, self.desc.codes_pitch)
+
+    def scales_2d(self) -> torch.Tensor:
+        assert self.layout == CANONICAL
+        return self.scales.view(self.rows, self.desc.scales_pitch)
+
+
+def fp4_quantize_weight(w: torch.Tensor, fmt=NVFP4) -> Fp4Tensor:
+    fmt = _fmt(fmt)
+    w = _bf16_2d(w, "w")
+    n, k = w.shape
+    L = lib()
+    out = Fp4Tensor(fmt, WEIGHT_TILED, n, k, w.device)
+    nws = L.fp4_quantize_workspace_bytes(fmt, n, k)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=w.device)
+    _check(L.fp4_quantize_weight(fmt, _ptr(w), n, k, ctypes.byref(out.desc), _ptr(ws), nws,
+                                 _stream(w.device)))
+    return out
+
+
+def fp4_quantize_act(a: torch.Tensor, fmt=NVFP4, static_scale: torch.Tensor | None = None) -> Fp4Tensor:
+    fmt = _fmt(fmt)
+    a = _bf16_2d(a, "a")
+    m, k = a.shape
+    L = lib()
+    out = Fp4Tensor(fmt, CANONICAL, m, k, a.device)
+    nws = L.fp4_quantize_workspace_bytes(fmt, m, k)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=a.device)
+    _check(L.fp4_quantize_act(fmt, _ptr(a), m, k, _ptr(static_scale), ctypes.byref(out.desc),
+                              _ptr(ws), nws, _stream(a.device)))
+    return out
+
+
+def fp4_gemm(a: Fp4Tensor, w: Fp4Tensor, out: torch.Tensor | None = None,
+             workspace: torch.Tensor | None = None) -> torch.Tensor:
+    L = lib()
+    m, n = a.rows, w.rows
+    if out is None:
+        out = torch.empty(m, n, dtype=torch.bfloat16, device=a.device)
+    nws = L.fp4_gemm_workspace_bytes(a.fmt, m, n, a.k)
+    if workspace is None:
+        workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=a.device)
+    _check(L.fp4_gemm(ctypes.byref(a.desc), ctypes.byref(w.desc), _ptr(out), out.stride(0),
+                      _ptr(workspace), workspace.numel(), _stream(a.device)))
+    return out
+
+
+def fp4_linear_workspace_bytes(fmt, m: int, n: int, k: int) -> int:
+    return lib().fp4_linear_workspace_bytes(_fmt(fmt), m, n, k)
+
+
+def fp4_linear(x: torch.Tensor, w: Fp4Tensor, static_scale: torch.Tensor | None = None,
+               out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    x = _bf16_2d(x, "x")
+    m = x.shape[0]
+    if x.shape[1] != w.k:
+        raise ValueError("x has K=%d, weight has K=%d" % (x.shape[1], w.k))
+    L = lib()
+    if out is None:
+        out = torch.empty(m, w.rows, dtype=torch.bfloat16, device=x.device)
+    nws = L.fp4_linear_workspace_bytes(w.fmt, m, w.rows, w.k)
+    if workspace is None:
+        workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=x.device)
+    _check(L.fp4_linear(_ptr(x), m, ctypes.byref(w.desc), _ptr(static_scale), _ptr(out),
+                        _ptr(workspace), workspace.numel(), _stream(x.device)))
+    return out
+
+
+def fp4_export_canonical(t: Fp4Tensor) -> Fp4Tensor:
+    out = Fp4Tensor(t.fmt, CANONICAL, t.rows, t.k, t.device)
+    _check(lib().fp4_export_canonical(ctypes.byref(t.desc), ctypes.byref(out.desc),
+                                      _stream(t.device)))
+    return out
+
+
+def fp4_dequantize(t: Fp4Tensor) -> torch.Tensor:
+    out = torch.empty(t.rows, t.k, dtype=torch.float32, device=t.device)
+    _check(lib().fp4_dequantize(ctypes.byref(t.desc), _ptr(out), t.k, _stream(t.device)))
+    return out

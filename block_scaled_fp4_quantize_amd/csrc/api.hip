@@ -1,0 +1,415 @@
+// api.hip -- host implementation of the C ABI declared in include/fp4.h.
+//
+// Validation happens here, on the host, before any launch; every launch is
+// asynchronous on the caller's stream. The library allocates nothing: all
+// scratch comes from caller-provided workspaces whose sizes these functions
+// report.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/fp4.h"
+#include "fp4_internal.h"
+
+using namespace fp4i;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fp4_status fail(fp4_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+fp4_status ok() {
+  g_last_error.clear();
+  return FP4_OK;
+}
+
+fp4_status hip_fail(hipError_t e, const char *what) {
+  return fail(FP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Per-device "is gfx950" cache.
+std::mutex g_dev_mu;
+int g_dev_state[64];  // 0 unknown, 1 ok, 2 wrong arch
+
+fp4_status check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(FP4_ERR_DEVICE, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if (g_dev_state[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    g_dev_state[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+  }
+  if (g_dev_state[dev] != 1) return fail(FP4_ERR_DEVICE, "device %d is not gfx950", dev);
+  return FP4_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool valid_fmt(int32_t f) { return f == FP4_NVFP4 || f == FP4_MXFP4; }
+bool valid_layout(int32_t l) { return l == FP4_LAYOUT_CANONICAL || l == FP4_LAYOUT_WEIGHT_TILED; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+fp4_status check_shape(int32_t fmt, int64_t rows, int64_t k) {
+  if (!valid_fmt(fmt)) return fail(FP4_ERR_INVALID_ARG, "unknown format %d", (int)fmt);
+  if (rows <= 0 || k <= 0) return fail(FP4_ERR_INVALID_ARG, "rows and k must be positive");
+  if (rows > (int64_t)1 << 30 || k > (int64_t)1 << 30)
+    return fail(FP4_ERR_SHAPE, "rows or k too large");
+  if (k % block_of(fmt) != 0)
+    return fail(FP4_ERR_SHAPE, "k=%lld is not a multiple of the block size %d", (long long)k,
+                block_of(fmt));
+  return FP4_OK;
+}
+
+// Validate a tensor descriptor's self-consistency.
+fp4_status check_tensor(const fp4_tensor *t, const char *name) {
+  if (!t) return fail(FP4_ERR_INVALID_ARG, "%s is null", name);
+  fp4_status st = check_shape(t->fmt, t->rows, t->cols);
+  if (st != FP4_OK) return st;
+  if (!valid_layout(t->layout)) return fail(FP4_ERR_INVALID_ARG, "%s: unknown layout", name);
+  if (!t->codes || !t->scales) return fail(FP4_ERR_INVALID_ARG, "%s: null buffer", name);
+  if (!aligned16(t->codes) || !aligned16(t->scales))
+    return fail(FP4_ERR_ALIGNMENT, "%s: buffers must be 16-byte aligned", name);
+  if (t->fmt == FP4_NVFP4 && !t->tensor_scale)
+    return fail(FP4_ERR_INVALID_ARG, "%s: NVFP4 needs a tensor_scale pointer", name);
+  if (t->layout == FP4_LAYOUT_CANONICAL) {
+    int64_t kp = k_pad(t->cols);
+    if (t->codes_pitch < kp / 2 || t->scales_pitch < kp / block_of(t->fmt))
+      return fail(FP4_ERR_SHAPE, "%s: pitch smaller than K_pad", name);
+    if (t->codes_pitch % 16 != 0 || (t->fmt == FP4_NVFP4 && t->scales_pitch % 2 != 0))
+      return fail(FP4_ERR_ALIGNMENT, "%s: codes pitch must be a multiple of 16 bytes and "
+                  "NVFP4 scales pitch even", name);
+  }
+  return FP4_OK;
+}
+
+size_t quant_ws(int32_t fmt) {
+  return fmt == FP4_NVFP4 ? (size_t)kMaxAmaxParts * sizeof(uint32_t) : 0;
+}
+
+// Everything fp4_linear keeps in its workspace, at fixed offsets.
+struct LinearLayout {
+  size_t codes, scales, ts, parts, gemm, total;
+  int64_t cpitch, spitch;
+};
+
+LinearLayout linear_layout(int32_t fmt, int64_t m, int64_t n, int64_t k) {
+  LinearLayout L;
+  int64_t kp = k_pad(k);
+  L.cpitch = kp / 2;
+  L.spitch = kp / block_of(fmt);
+  size_t off = 0;
+  L.codes = off; off = align256(off + (size_t)(m * L.cpitch));
+  L.scales = off; off = align256(off + (size_t)(m * L.spitch));
+  L.ts = off; off = align256(off + sizeof(float));
+  L.parts = off; off = align256(off + quant_ws(fmt));
+  L.gemm = off;
+  off = align256(off + (m <= kDecodeMaxM ? decode_workspace_bytes(fmt, m, n, k) : 0));
+  L.total = off;
+  return L;
+}
+
+fp4_status run_quant_act(int32_t fmt, const void *a, int64_t m, int64_t k,
+                         const float *static_scale, uint8_t *codes, int64_t cp, uint8_t *scales,
+                         int64_t sp, float *ts, uint32_t *parts, int *zero_ptr, int zero_n,
+                         hipStream_t stream) {
+  int nparts = 0;
+  if (fmt == FP4_NVFP4 && !static_scale) {
+    nparts = amax_parts(m * k);
+    hipError_t e = launch_amax_parts((const uint16_t *)a, m * k, parts, nparts, stream);
+    if (e != hipSuccess) return hip_fail(e, "amax launch");
+  }
+  hipError_t e = launch_quant_canonical(fmt, (const uint16_t *)a, m, k, parts, nparts,
+                                        static_scale, codes, cp, scales, sp, ts, zero_ptr,
+                                        zero_n, stream);
+  if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  return FP4_OK;
+}
+
+fp4_status run_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c, int64_t ldc,
+                    void *gemm_ws, size_t gemm_ws_bytes, bool counters_zeroed,
+                    hipStream_t stream) {
+  GemmArgs g;
+  g.fmt = a->fmt;
+  g.a_codes = (const uint8_t *)a->codes; g.a_cpitch = a->codes_pitch;
+  g.a_scales = (const uint8_t *)a->scales; g.a_spitch = a->scales_pitch;
+  g.a_ts = a->tensor_scale;
+  g.w_codes = (const uint8_t *)w->codes; g.w_scales = (const uint8_t *)w->scales;
+  g.w_ts = w->tensor_scale;
+  g.m = a->rows; g.n = w->rows; g.k = a->cols;
+  g.c = (uint16_t *)c; g.ldc = ldc;
+  hipError_t e;
+  if (g.m <= kDecodeMaxM) {
+    DecodePlan p = decode_plan(g.fmt, g.m, g.n, g.k);
+    size_t need = decode_workspace_bytes(g.fmt, g.m, g.n, g.k);
+    float *partials = nullptr;
+    int *counters = nullptr;
+    if (p.splits > 1) {
+      if (!gemm_ws || gemm_ws_bytes < need) {  // no room for split-K: one split
+        p.kt_per_wg = (int)(k_pad(g.k) / 128);
+        p.splits = 1;
+        p.frags = (p.kt_per_wg + 3) / 4;
+      } else {
+        int64_t nt_n = round_up(g.n, 16) / 16;
+        counters = (int *)gemm_ws;
+        partials = (float *)((char *)gemm_ws + align256((size_t)nt_n * 4));
+        if (!counters_zeroed) {
+          e = launch_zero_ints(counters, (int)nt_n, stream);
+          if (e != hipSuccess) return hip_fail(e, "counter clear launch");
+        }
+      }
+    }
+    e = launch_gemm_decode(g, p, partials, counters, stream);
+  } else {
+    e = launch_gemm_prefill(g, stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "gemm launch");
+  return FP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fp4_block_size(int32_t fmt) { return valid_fmt(fmt) ? block_of(fmt) : 0; }
+
+size_t fp4_codes_bytes(int32_t fmt, int32_t layout, int64_t rows, int64_t k) {
+  if (!valid_fmt(fmt) || !valid_layout(layout) || rows <= 0 || k <= 0) return 0;
+  int64_t r = layout == FP4_LAYOUT_WEIGHT_TILED ? round_up(rows, 16) : rows;
+  return (size_t)(r * (k_pad(k) / 2));
+}
+
+size_t fp4_scales_bytes(int32_t fmt, int32_t layout, int64_t rows, int64_t k) {
+  if (!valid_fmt(fmt) || !valid_layout(layout) || rows <= 0 || k <= 0) return 0;
+  int64_t r = layout == FP4_LAYOUT_WEIGHT_TILED ? round_up(rows, 16) : rows;
+  return (size_t)(r * (k_pad(k) / block_of(fmt)));
+}
+
+fp4_status fp4_tensor_init(fp4_tensor *t, int32_t fmt, int32_t layout, int64_t rows, int64_t k,
+                           void *codes, void *scales, float *tensor_scale) {
+  if (!t) return fail(FP4_ERR_INVALID_ARG, "tensor descriptor is null");
+  fp4_status st = check_shape(fmt, rows, k);
+  if (st != FP4_OK) return st;
+  if (!valid_layout(layout)) return fail(FP4_ERR_INVALID_ARG, "unknown layout %d", (int)layout);
+  t->fmt = fmt;
+  t->layout = layout;
+  t->rows = rows;
+  t->cols = k;
+  t->codes_pitch = layout == FP4_LAYOUT_CANONICAL ? k_pad(k) / 2 : 0;
+  t->scales_pitch = layout == FP4_LAYOUT_CANONICAL ? k_pad(k) / block_of(fmt) : 0;
+  t->codes = codes;
+  t->scales = scales;
+  t->tensor_scale = tensor_scale;
+  return ok();
+}
+
+size_t fp4_quantize_workspace_bytes(int32_t fmt, int64_t rows, int64_t k) {
+  (void)rows;
+  (void)k;
+  return valid_fmt(fmt) ? quant_ws(fmt) : 0;
+}
+
+fp4_status fp4_quantize_weight(int32_t fmt, const void *w_bf16, int64_t n, int64_t k,
+                               fp4_tensor *out, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  fp4_status st = check_shape(fmt, n, k);
+  if (st != FP4_OK) return st;
+  if (!w_bf16) return fail(FP4_ERR_INVALID_ARG, "weight pointer is null");
+  if (!aligned16(w_bf16)) return fail(FP4_ERR_ALIGNMENT, "weight must be 16-byte aligned");
+  if ((st = check_tensor(out, "out")) != FP4_OK) return st;
+  if (out->layout != FP4_LAYOUT_WEIGHT_TILED)
+    return fail(FP4_ERR_FORMAT_MISMATCH, "weights are stored in the WEIGHT_TILED layout");
+  if (out->fmt != fmt || out->rows != n || out->cols != k)
+    return fail(FP4_ERR_FORMAT_MISMATCH, "out descriptor does not match format/shape");
+  if (workspace_bytes < quant_ws(fmt) || (quant_ws(fmt) && !workspace))
+    return fail(FP4_ERR_WORKSPACE, "workspace needs %zu bytes", quant_ws(fmt));
+  if (workspace && !aligned16(workspace))
+    return fail(FP4_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+  if ((st = check_device()) != FP4_OK) return st;
+  int nparts = 0;
+  if (fmt == FP4_NVFP4) {
+    nparts = amax_parts(n * k);
+    hipError_t e = launch_amax_parts((const uint16_t *)w_bf16, n * k, (uint32_t *)workspace,
+                                     nparts, stream);
+    if (e != hipSuccess) return hip_fail(e, "amax launch");
+  }
+  hipError_t e = launch_quant_tiled(fmt, (const uint16_t *)w_bf16, n, k,
+                                    (const uint32_t *)workspace, nparts, (uint8_t *)out->codes,
+                                    (uint8_t *)out->scales, out->tensor_scale, stream);
+  if (e != hipSuccess) return hip_fail(e, "weight quantize launch");
+  return ok();
+}
+
+fp4_status fp4_quantize_act(int32_t fmt, const void *a_bf16, int64_t m, int64_t k,
+                            const float *static_scale, fp4_tensor *out, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  fp4_status st = check_shape(fmt, m, k);
+  if (st != FP4_OK) return st;
+  if (!a_bf16) return fail(FP4_ERR_INVALID_ARG, "activation pointer is null");
+  if (!aligned16(a_bf16)) return fail(FP4_ERR_ALIGNMENT, "activations must be 16-byte aligned");
+  if ((st = check_tensor(out, "out")) != FP4_OK) return st;
+  if (out->layout != FP4_LAYOUT_CANONICAL)
+    return fail(FP4_ERR_FORMAT_MISMATCH, "activations are stored in the CANONICAL layout");
+  if (out->fmt != fmt || out->rows != m || out->cols != k)
+    return fail(FP4_ERR_FORMAT_MISMATCH, "out descriptor does not match format/shape");
+  if (fmt == FP4_MXFP4 && static_scale)
+    return fail(FP4_ERR_INVALID_ARG, "MXFP4 has no per-tensor scale");
+  size_t need = static_scale ? 0 : quant_ws(fmt);
+  if (workspace_bytes < need || (need && !workspace))
+    return fail(FP4_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+  if (workspace && !aligned16(workspace))
+    return fail(FP4_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+  if ((st = check_device()) != FP4_OK) return st;
+  st = run_quant_act(fmt, a_bf16, m, k, static_scale, (uint8_t *)out->codes, out->codes_pitch,
+                     (uint8_t *)out->scales, out->scales_pitch, out->tensor_scale,
+                     (uint32_t *)workspace, nullptr, 0, stream);
+  return st == FP4_OK ? ok() : st;
+}
+
+size_t fp4_gemm_workspace_bytes(int32_t fmt, int64_t m, int64_t n, int64_t k) {
+  if (!valid_fmt(fmt) || m <= 0 || n <= 0 || k <= 0) return 0;
+  return m <= kDecodeMaxM ? decode_workspace_bytes(fmt, m, n, k) : 0;
+}
+
+fp4_status fp4_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c_bf16, int64_t ldc,
+                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  fp4_status st;
+  if ((st = check_tensor(a, "a")) != FP4_OK) return st;
+  if ((st = check_tensor(w, "w")) != FP4_OK) return st;
+  if (a->layout != FP4_LAYOUT_CANONICAL || w->layout != FP4_LAYOUT_WEIGHT_TILED)
+    return fail(FP4_ERR_FORMAT_MISMATCH, "a must be CANONICAL and w WEIGHT_TILED");
+  if (a->fmt != w->fmt) return fail(FP4_ERR_FORMAT_MISMATCH, "a and w differ in format");
+  if (a->cols != w->cols) return fail(FP4_ERR_SHAPE, "a and w differ in K");
+  if (!c_bf16) return fail(FP4_ERR_INVALID_ARG, "output pointer is null");
+  if (ldc < w->rows) return fail(FP4_ERR_SHAPE, "ldc smaller than N");
+  if (((uintptr_t)c_bf16 & 1u) != 0) return fail(FP4_ERR_ALIGNMENT, "output must be 2-byte aligned");
+  if (workspace_bytes && !workspace) return fail(FP4_ERR_WORKSPACE, "null workspace with size");
+  if (workspace && !aligned16(workspace))
+    return fail(FP4_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+  if (a->rows > INT32_MAX || w->rows > INT32_MAX) return fail(FP4_ERR_SHAPE, "too many rows");
+  if ((st = check_device()) != FP4_OK) return st;
+  st = run_gemm(a, w, c_bf16, ldc, workspace, workspace_bytes, false, stream);
+  return st == FP4_OK ? ok() : st;
+}
+
+size_t fp4_linear_workspace_bytes(int32_t fmt, int64_t m, int64_t n, int64_t k) {
+  if (!valid_fmt(fmt) || m <= 0 || n <= 0 || k <= 0) return 0;
+  return linear_layout(fmt, m, n, k).total;
+}
+
+fp4_status fp4_linear(const void *x_bf16, int64_t m, const fp4_tensor *w,
+                      const float *static_scale, void *y_bf16, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  fp4_status st;
+  if ((st = check_tensor(w, "w")) != FP4_OK) return st;
+  if (w->layout != FP4_LAYOUT_WEIGHT_TILED)
+    return fail(FP4_ERR_FORMAT_MISMATCH, "w must be WEIGHT_TILED");
+  const int32_t fmt = w->fmt;
+  const int64_t k = w->cols, n = w->rows;
+  if ((st = check_shape(fmt, m, k)) != FP4_OK) return st;
+  if (!x_bf16 || !y_bf16) return fail(FP4_ERR_INVALID_ARG, "null input or output");
+  if (!aligned16(x_bf16)) return fail(FP4_ERR_ALIGNMENT, "input must be 16-byte aligned");
+  if (((uintptr_t)y_bf16 & 1u) != 0) return fail(FP4_ERR_ALIGNMENT, "output must be 2-byte aligned");
+  if (fmt == FP4_MXFP4 && static_scale)
+    return fail(FP4_ERR_INVALID_ARG, "MXFP4 has no per-tensor scale");
+  LinearLayout L = linear_layout(fmt, m, n, k);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(FP4_ERR_WORKSPACE, "workspace needs %zu bytes", L.total);
+  if (!aligned16(workspace)) return fail(FP4_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+  if ((st = check_device()) != FP4_OK) return st;
+
+  char *ws = (char *)workspace;
+  fp4_tensor a;
+  a.fmt = fmt;
+  a.layout = FP4_LAYOUT_CANONICAL;
+  a.rows = m;
+  a.cols = k;
+  a.codes_pitch = L.cpitch;
+  a.scales_pitch = L.spitch;
+  a.codes = ws + L.codes;
+  a.scales = ws + L.scales;
+  a.tensor_scale = (float *)(ws + L.ts);
+  // The quantize kernel clears the split-K counters of the GEMM that follows.
+  int *zero_ptr = nullptr;
+  int zero_n = 0;
+  size_t gemm_bytes = L.total - L.gemm;
+  if (m <= kDecodeMaxM && decode_plan(fmt, m, n, k).splits > 1) {
+    zero_ptr = (int *)(ws + L.gemm);
+    zero_n = (int)(round_up(n, 16) / 16);
+  }
+  st = run_quant_act(fmt, x_bf16, m, k, static_scale, (uint8_t *)a.codes, a.codes_pitch,
+                     (uint8_t *)a.scales, a.scales_pitch, a.tensor_scale,
+                     (uint32_t *)(ws + L.parts), zero_ptr, zero_n, stream);
+  if (st != FP4_OK) return st;
+  st = run_gemm(&a, w, y_bf16, n, ws + L.gemm, gemm_bytes, true, stream);
+  return st == FP4_OK ? ok() : st;
+}
+
+fp4_status fp4_export_canonical(const fp4_tensor *tiled, fp4_tensor *canonical,
+                                hipStream_t stream) {
+  fp4_status st;
+  if ((st = check_tensor(tiled, "tiled")) != FP4_OK) return st;
+  if ((st = check_tensor(canonical, "canonical")) != FP4_OK) return st;
+  if (tiled->layout != FP4_LAYOUT_WEIGHT_TILED || canonical->layout != FP4_LAYOUT_CANONICAL)
+    return fail(FP4_ERR_FORMAT_MISMATCH, "expected a WEIGHT_TILED source and CANONICAL target");
+  if (tiled->fmt != canonical->fmt || tiled->rows != canonical->rows ||
+      tiled->cols != canonical->cols)
+    return fail(FP4_ERR_FORMAT_MISMATCH, "descriptors differ in format or shape");
+  if ((st = check_device()) != FP4_OK) return st;
+  hipError_t e = launch_export_canonical(
+      tiled->fmt, (const uint8_t *)tiled->codes, (const uint8_t *)tiled->scales, tiled->rows,
+      tiled->cols, (uint8_t *)canonical->codes, canonical->codes_pitch,
+      (uint8_t *)canonical->scales, canonical->scales_pitch,
+      tiled->fmt == FP4_NVFP4 ? tiled->tensor_scale : nullptr,
+      tiled->fmt == FP4_NVFP4 ? canonical->tensor_scale : nullptr, stream);
+  if (e != hipSuccess) return hip_fail(e, "export launch");
+  return ok();
+}
+
+fp4_status fp4_dequantize(const fp4_tensor *t, float *out_f32, int64_t ldo, hipStream_t stream) {
+  fp4_status st;
+  if ((st = check_tensor(t, "t")) != FP4_OK) return st;
+  if (!out_f32) return fail(FP4_ERR_INVALID_ARG, "output pointer is null");
+  if (ldo < t->cols) return fail(FP4_ERR_SHAPE, "ldo smaller than K");
+  if (((uintptr_t)out_f32 & 3u) != 0) return fail(FP4_ERR_ALIGNMENT, "output must be 4-byte aligned");
+  if ((st = check_device()) != FP4_OK) return st;
+  hipError_t e = launch_dequant(t->fmt, t->layout == FP4_LAYOUT_WEIGHT_TILED,
+                                (const uint8_t *)t->codes, t->codes_pitch,
+                                (const uint8_t *)t->scales, t->scales_pitch,
+                                t->fmt == FP4_NVFP4 ? t->tensor_scale : nullptr, t->rows, t->cols,
+                                out_f32, ldo, stream);
+  if (e != hipSuccess) return hip_fail(e, "dequantize launch");
+  return ok();
+}
+
+const char *fp4_status_string(int32_t s) {
+  switch (s) {
+    case FP4_OK: return "FP4_OK";
+    case FP4_ERR_INVALID_ARG: return "FP4_ERR_INVALID_ARG";
+    case FP4_ERR_SHAPE: return "FP4_ERR_SHAPE";
+    case FP4_ERR_ALIGNMENT: return "FP4_ERR_ALIGNMENT";
+    case FP4_ERR_WORKSPACE: return "FP4_ERR_WORKSPACE";
+    case FP4_ERR_FORMAT_MISMATCH: return "FP4_ERR_FORMAT_MISMATCH";
+    case FP4_ERR_DEVICE: return "FP4_ERR_DEVICE";
+    case FP4_ERR_HIP: return "FP4_ERR_HIP";
+    default: return "FP4_ERR_UNKNOWN";
+  }
+}
+
+const char *fp4_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,192 @@
+// fp4_device.h -- device-side number formats for the gfx950 kernels.
+//
+// E2M1 element codes (S|EE|M, exponent bias 1) with magnitudes
+// {0, 0.5, 1, 1.5, 2, 3, 4, 6}, E4M3 block scales (largest finite 448) and
+// E8M0 block exponents, as described on "Hardware FP4 inference for speech on
+// Blackwell" (section "NVFP4, and the two ways it fails") and "FP4 n'existe
+// pas ..." (section "Deux dialectes, deux strategies de scaling").
+//
+// Every rounding decision here is taken on exact values so that the result
+// does not depend on evaluation order:
+//   * block scales: the quotient a_b / (6 S_t) is a correctly rounded binary64
+//     division, rounded to E4M3 from its binary64 bits (a real quotient that is
+//     not an E4M3 midpoint stays >= ~2^-32 away from one, far above the
+//     binary64 error, and an exact midpoint is computed exactly);
+//   * element codes (NVFP4): each midpoint test |x| vs t * s_b * S_t is the sign
+//     of one fused multiply-add, fma(t * s_b, S_t, -|x|), which is exact in
+//     sign because t * s_b is exact in binary32 and the operands are pre-scaled
+//     by 2^64 when S_t is tiny so that no nonzero difference underflows;
+//   * element codes (MXFP4): x * 2^-e is exact, and the hardware FP4 convert
+//     rounds it to nearest, ties to even, saturating at 6.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace fp4d {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// bf16 round-to-nearest-even of a finite FP32 value (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// E4M3 byte (sign clear, not NaN) -> exact FP32 value.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
+  uint32_t e = (byte >> 3) & 15u, m = byte & 7u;
+  if (e == 0) return ldexpf((float)m, -9);
+  return ldexpf((float)(8u + m), (int)e - 10);
+}
+
+// Nearest E4M3 byte to a non-negative binary64 value, ties to even mantissa,
+// saturating at 448 (0x7E). Values >= 448 map to 0x7E (464 is the tie that
+// still rounds to 448; anything above saturates).
+__device__ __forceinline__ uint32_t e4m3_rne_sat(double q) {
+  if (!(q > 0.0)) return 0u;
+  if (q >= 448.0) return 0x7Eu;
+  int e2;
+  (void)frexp(q, &e2);          // q = f * 2^e2, f in [0.5, 1)
+  int fl = e2 - 1;              // floor(log2 q)
+  if (fl < -6) fl = -6;         // subnormals use the 2^-6 binade spacing
+  double n = ldexp(q, 3 - fl);  // exact: q / 2^(fl-3)
+  int r = (int)rint(n);         // round to nearest, ties to even
+  if (r == 0) return 0u;
+  if (fl == -6 && r < 8) return (uint32_t)r;         // subnormal
+  if (r == 16) { fl += 1; r = 8; }
+  return ((uint32_t)(fl + 7) << 3) | (uint32_t)(r - 8);
+}
+
+// Per-tensor NVFP4 decode scale from the tensor's largest magnitude g:
+// S_t = RN_fp32(g / 2688) (2688 = 6 * 448), or 1 when g = 0.
+__device__ __forceinline__ float tensor_scale_from_amax(float g) {
+  if (!(g > 0.0f)) return 1.0f;
+  return (float)((double)g / 2688.0);
+}
+
+// NVFP4 per-block encoder state: thresholds t * s_b for the seven midpoints of
+// the E2M1 grid, the pre-scaled tensor scale and the pre-scale factor.
+struct NvBlockEnc {
+  float t[7];
+  float st;      // S_t * sigma
+  float sigma;   // 1 or 2^64
+  bool zero;     // block scale rounded to zero: every code is +-0
+};
+
+__device__ __forceinline__ NvBlockEnc nv_block_encoder(uint32_t sbyte, float st) {
+  NvBlockEnc e;
+  float sv = e4m3_to_f32(sbyte);
+  e.t[0] = 0.25f * sv; e.t[1] = 0.75f * sv; e.t[2] = 1.25f * sv; e.t[3] = 1.75f * sv;
+  e.t[4] = 2.5f * sv;  e.t[5] = 3.5f * sv;  e.t[6] = 5.0f * sv;
+  e.sigma = (st < 0x1p-64f) ? 0x1p64f : 1.0f;
+  e.st = st * e.sigma;
+  e.zero = (sbyte == 0u);
+  return e;
+}
+
+// E2M1 magnitude index (0..7) of |x| (exact FP32) against the block's grid:
+// midpoints between an odd and an even index are passed with '>', the others
+// with '>=', so ties go to the even index; 6 * d_b saturates.
+__device__ __forceinline__ uint32_t nv_encode_mag(const NvBlockEnc &e, float ax) {
+  if (e.zero) return 0u;
+  float axs = ax * e.sigma;
+  uint32_t m = 0;
+  m += (__builtin_fmaf(e.t[0], e.st, -axs) < 0.0f);
+  m += (__builtin_fmaf(e.t[1], e.st, -axs) <= 0.0f);
+  m += (__builtin_fmaf(e.t[2], e.st, -axs) < 0.0f);
+  m += (__builtin_fmaf(e.t[3], e.st, -axs) <= 0.0f);
+  m += (__builtin_fmaf(e.t[4], e.st, -axs) < 0.0f);
+  m += (__builtin_fmaf(e.t[5], e.st, -axs) <= 0.0f);
+  m += (__builtin_fmaf(e.t[6], e.st, -axs) < 0.0f);
+  return m;
+}
+
+// Encode 8 bf16 values (one uint4) of an NVFP4 block into 8 nibbles (uint32).
+__device__ __forceinline__ uint32_t nv_encode8(const NvBlockEnc &e, uint4 v) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t out = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t b = (w[i] >> (16 * h)) & 0xFFFFu;
+      float ax = bf16_bits_to_f32(b & 0x7FFFu);
+      uint32_t code = nv_encode_mag(e, ax) | ((b >> 12) & 8u);
+      out |= code << (4 * (2 * i + h));
+    }
+  }
+  return out;
+}
+
+// MXFP4 block exponent from the block maximum's bf16 bits (sign clear):
+// e = clamp(floor(log2 a) - 2, -127, 127); the scale byte is e + 127.
+// bf16 subnormals and zero have floor(log2 a) <= -127, so they clamp to -127.
+__device__ __forceinline__ int mx_exponent_from_bits(uint32_t abits) {
+  int ef = (int)(abits >> 7);      // biased exponent field
+  int e = ef - 129;                // floor(log2 a) - 2 for normal a
+  return e < -127 ? -127 : e;
+}
+
+// Encode 8 bf16 values into 8 nibbles with the hardware FP4 convert applied to
+// the exact quotient x * 2^-e (nearest, ties to even, saturating at 6).
+__device__ __forceinline__ uint32_t mx_encode8(int e, uint4 v) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t out = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float lo = ldexpf(bf16_bits_to_f32(w[i] & 0xFFFFu), -e);
+    float hi = ldexpf(bf16_bits_to_f32(w[i] >> 16), -e);
+    uint32_t byte = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, lo, hi, 1.0f, 0) & 0xFFu;
+    out |= byte << (8 * i);
+  }
+  return out;
+}
+
+// ---- decode side ----
+
+// E4M3 scale byte -> f16 bits of s_b * 2^-8 in both halves (exact: the E4M3
+// exponent and mantissa fields land in the f16 fields with a bias offset of 8).
+__device__ __forceinline__ h2v e4m3_scaled_h2(uint32_t byte) {
+  uint32_t h = (byte & 0x7Fu) << 7;
+  return __builtin_bit_cast(h2v, h | (h << 16));
+}
+
+// Dequantize one lane's 32 NVFP4 codes (4 dwords, value j in nibble j) with
+// two E4M3 scales (byte 0: values 0-15, byte 1: values 16-31) into exact f16
+// values q * s_b, returned as four groups of 8 values (group g = values 8g..8g+7).
+// The convert applies only the exponent of its scale (2^8 here); the E4M3
+// mantissa is applied by an exact f16 multiply by s_b * 2^-8.
+__device__ __forceinline__ void nv_dequant32(uint4 q, uint32_t s2, h8v out[4]) {
+  h2v sc0 = e4m3_scaled_h2(s2 & 0xFFu), sc1 = e4m3_scaled_h2((s2 >> 8) & 0xFFu);
+  uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    h2v sc = d < 2 ? sc0 : sc1;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      h2v v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[d] >> (8 * b), 256.0f, 0);
+      v = v * sc;
+      out[d][2 * b] = v[0];
+      out[d][2 * b + 1] = v[1];
+    }
+  }
+}
+
+__device__ __forceinline__ v8i frag_v8i(uint4 q) {
+  v8i r;
+  r[0] = (int)q.x; r[1] = (int)q.y; r[2] = (int)q.z; r[3] = (int)q.w;
+  r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+  return r;
+}
+
+}  // namespace fp4d

@@ -1,0 +1,171 @@
+/*
+ * fp4.h -- C ABI of the MI355X (gfx950) W4A4 block-scaled FP4 linear library.
+ *
+ * What it computes (the pages this project works from):
+ *   - NVFP4: blocks of 16 consecutive values along K share one E4M3 scale
+ *     s_b = cast_E4M3(max|x| / 6); each value is an E2M1 code q from
+ *     {0, +-0.5, +-1, +-1.5, +-2, +-3, +-4, +-6}; x^ = s_b * q
+ *     ("Hardware FP4 inference for speech on Blackwell", section "NVFP4, and
+ *     the two ways it fails", both display equations). A second, per-tensor
+ *     FP32 scale S_t keeps block scales under E4M3's 448 and block scales
+ *     saturate (same section, paragraph on scale overflow; and "FP4 n'existe
+ *     pas ...", section "Deux dialectes", two-level scaling). Here
+ *     S_t = RN_fp32(max|x| / 2688) (dynamic) or a caller-given value (static),
+ *     and x^ = q * s_b * S_t.
+ *   - MXFP4: blocks of 32 values share one E8M0 power-of-two scale
+ *     ("FP4 n'existe pas ...", section "Deux dialectes" and its table).
+ *     Block exponent e_b = clamp(floor(log2 max|x|) - 2, -127, 127).
+ *   - Weights are quantized once and cached; activations are quantized on
+ *     every call; the product runs on the quantized operands with FP32
+ *     accumulation (forum post on a standalone FP4 GEMM library with a
+ *     pre-quantized weight cache, opening paragraphs).
+ *   - The GEMM follows a linear layer: C[M,N] = A[M,K] * W[N,K]^T.
+ *
+ * Codes: E2M1 nibbles, sign in bit 3, magnitude index in bits 0-2 (S|EE|M,
+ * exponent bias 1); two per byte, even k in the low nibble. Element rounding
+ * is nearest with ties to even, against the rounded block scale.
+ *
+ * Conventions for every call:
+ *   - All data pointers are DEVICE pointers owned by the caller; the library
+ *     allocates no memory and keeps no per-call state.
+ *   - Work is enqueued on `stream` (0 = default stream) and the call returns
+ *     without waiting. Faults inside kernels surface at the caller's next
+ *     synchronization.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     rejected call launches nothing and returns a non-zero fp4_status, with
+ *     a description available from fp4_last_error() on the same thread.
+ *   - Inputs are bf16, row-major, contiguous, 16-byte aligned, finite.
+ *   - The library runs on gfx950 devices only (FP4_ERR_DEVICE otherwise).
+ */
+#ifndef FP4_H
+#define FP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FP4_NVFP4 = 0, FP4_MXFP4 = 1 } fp4_format;
+
+typedef enum {
+    FP4_OK = 0,
+    FP4_ERR_INVALID_ARG = 1,     /* null pointer, bad enum, non-positive size */
+    FP4_ERR_SHAPE = 2,           /* K not a multiple of the block, mismatched K */
+    FP4_ERR_ALIGNMENT = 3,       /* pointer or pitch not 16-byte aligned */
+    FP4_ERR_WORKSPACE = 4,       /* workspace missing or smaller than required */
+    FP4_ERR_FORMAT_MISMATCH = 5, /* operands of different formats or layouts */
+    FP4_ERR_DEVICE = 6,          /* current device is not gfx950 */
+    FP4_ERR_HIP = 7              /* a HIP runtime call or launch failed */
+} fp4_status;
+
+/*
+ * CANONICAL: codes row-major [rows][codes_pitch] bytes (pitch >= K_pad/2),
+ *   scales row-major [rows][scales_pitch] bytes (pitch >= K_pad/B); bytes
+ *   past K within a row are zero. This is the activation layout and the
+ *   layout used to compare with a reference byte for byte.
+ * WEIGHT_TILED: the weight cache layout. Rows are padded to N_pad =
+ *   round_up(N, 16) and K to K_pad = round_up(K, 128); the matrix is cut into
+ *   fragments of 16 rows x 128 values, stored fragment-major
+ *   ((row / 16) * (K_pad / 128) + k / 128). A fragment's codes are 1024 bytes:
+ *   16 bytes per lane l = 16 * c + r holding row r, values 32c .. 32c+31 of
+ *   the fragment. Its scales follow the same lane order: 128 bytes (NVFP4,
+ *   two E4M3 bytes per lane) or 64 bytes (MXFP4, one E8M0 byte per lane).
+ *   Padding codes and scales are zero.
+ * K_pad = round_up(K, 128) in both layouts.
+ */
+typedef enum { FP4_LAYOUT_CANONICAL = 0, FP4_LAYOUT_WEIGHT_TILED = 1 } fp4_layout;
+
+typedef struct {
+    int32_t fmt;            /* fp4_format */
+    int32_t layout;         /* fp4_layout */
+    int64_t rows;           /* logical rows (M for activations, N for weights) */
+    int64_t cols;           /* logical K */
+    int64_t codes_pitch;    /* CANONICAL: bytes per row of codes; TILED: 0 */
+    int64_t scales_pitch;   /* CANONICAL: bytes per row of scales; TILED: 0 */
+    void *codes;            /* device, caller-owned */
+    void *scales;           /* device, caller-owned */
+    float *tensor_scale;    /* device FP32 S_t (NVFP4); ignored for MXFP4 */
+} fp4_tensor;
+
+/* Block size along K: 16 (NVFP4) or 32 (MXFP4); 0 for a bad format. */
+int32_t fp4_block_size(int32_t fmt);
+
+/* Bytes needed for the codes / scales of a [rows, k] tensor in `layout`
+ * (padding included). 0 for invalid arguments. */
+size_t fp4_codes_bytes(int32_t fmt, int32_t layout, int64_t rows, int64_t k);
+size_t fp4_scales_bytes(int32_t fmt, int32_t layout, int64_t rows, int64_t k);
+
+/* Fill `t` for caller-allocated buffers sized by the two calls above
+ * (canonical pitches are the minimum: K_pad/2 and K_pad/B bytes). */
+fp4_status fp4_tensor_init(fp4_tensor *t, int32_t fmt, int32_t layout, int64_t rows,
+                           int64_t k, void *codes, void *scales, float *tensor_scale);
+
+/* Workspace for fp4_quantize_act / fp4_quantize_weight: room for the partial
+ * maxima of the per-tensor scale reduction (NVFP4 dynamic). */
+size_t fp4_quantize_workspace_bytes(int32_t fmt, int64_t rows, int64_t k);
+
+/*
+ * Quantize a weight W bf16 [n, k] once, into `out` (WEIGHT_TILED, filled by
+ * fp4_tensor_init with rows = n, cols = k). NVFP4 uses the dynamic per-tensor
+ * scale, written to *out->tensor_scale. k must be a multiple of the block.
+ */
+fp4_status fp4_quantize_weight(int32_t fmt, const void *w_bf16, int64_t n, int64_t k,
+                               fp4_tensor *out, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
+ * Quantize activations A bf16 [m, k] into `out` (CANONICAL). NVFP4:
+ * static_scale == NULL selects the dynamic per-tensor scale; otherwise
+ * *static_scale (device FP32, > 0, finite) is used as S_t and block scales
+ * saturate at 448. MXFP4 requires static_scale == NULL.
+ */
+fp4_status fp4_quantize_act(int32_t fmt, const void *a_bf16, int64_t m, int64_t k,
+                            const float *static_scale, fp4_tensor *out, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace for fp4_gemm (split-K partial sums and their counters). */
+size_t fp4_gemm_workspace_bytes(int32_t fmt, int64_t m, int64_t n, int64_t k);
+
+/*
+ * C[m, n] (bf16, row stride ldc elements) = bf16_RNE(alpha * sum_k a^'[m,k] w^'[n,k]),
+ * with a^' = q * s_b (per-tensor factors pulled into alpha = S_tA * S_tW for
+ * NVFP4, alpha = 1 for MXFP4). `a` is CANONICAL, `w` is WEIGHT_TILED, same
+ * format and K. Accumulation is FP32. `workspace` may be NULL (then
+ * workspace_bytes must be 0 and no split-K is used).
+ */
+fp4_status fp4_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c_bf16, int64_t ldc,
+                    void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace for fp4_linear: quantized activations, reduction scratch, split-K. */
+size_t fp4_linear_workspace_bytes(int32_t fmt, int64_t m, int64_t n, int64_t k);
+
+/*
+ * y[m, N] (bf16, contiguous) = x[m, K] (bf16) through the cached weight `w`:
+ * quantize x as fp4_quantize_act would (same static_scale rule), then
+ * fp4_gemm. All intermediate data lives in `workspace`.
+ */
+fp4_status fp4_linear(const void *x_bf16, int64_t m, const fp4_tensor *w,
+                      const float *static_scale, void *y_bf16, void *workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/* Test aids (not on the hot path). */
+/* Copy a WEIGHT_TILED tensor into a CANONICAL one of the same format/shape
+ * (including the tensor scale when both pointers are set). */
+fp4_status fp4_export_canonical(const fp4_tensor *tiled, fp4_tensor *canonical,
+                                hipStream_t stream);
+/* x^ as FP32 [rows, cols] with row stride ldo (RN_fp32 of q * s_b * S_t). */
+fp4_status fp4_dequantize(const fp4_tensor *t, float *out_f32, int64_t ldo,
+                          hipStream_t stream);
+
+const char *fp4_status_string(int32_t status);
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char *fp4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4_H */

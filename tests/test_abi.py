@@ -1,0 +1,108 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+symbol, sizes its buffers as documented and rejects bad arguments on the host
+before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_fp4_quantize_amd as fp4
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "fp4.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(fp4_[a-z_0-9]+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    L = fp4.lib()
+    names = declared_functions()
+    assert len(names) >= 15
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_sizes_and_pitches():
+    L = fp4.lib()
+    # canonical: rows x K_pad/2 codes, rows x K_pad/B scales; K_pad = round_up(K, 128)
+    assert L.fp4_codes_bytes(fp4.NVFP4, fp4.CANONICAL, 3, 2880) == 3 * 2944 // 2
+    assert L.fp4_scales_bytes(fp4.NVFP4, fp4.CANONICAL, 3, 2880) == 3 * 2944 // 16
+    assert L.fp4_scales_bytes(fp4.MXFP4, fp4.CANONICAL, 3, 2880) == 3 * 2944 // 32
+    # tiled: rows padded to 16
+    assert L.fp4_codes_bytes(fp4.NVFP4, fp4.WEIGHT_TILED, 17, 256) == 32 * 128
+    assert L.fp4_scales_bytes(fp4.MXFP4, fp4.WEIGHT_TILED, 17, 256) == 32 * 8
+    # 4.5 and 4.25 bits per value when nothing is padded
+    k, n = 5120, 5120
+    for fmt, bits in ((fp4.NVFP4, 4.5), (fp4.MXFP4, 4.25)):
+        tot = L.fp4_codes_bytes(fmt, fp4.WEIGHT_TILED, n, k) + L.fp4_scales_bytes(fmt, fp4.WEIGHT_TILED, n, k)
+        assert tot * 8 / (n * k) == bits
+    assert L.fp4_block_size(fp4.NVFP4) == 16 and L.fp4_block_size(fp4.MXFP4) == 32
+    assert L.fp4_block_size(7) == 0
+    assert L.fp4_codes_bytes(9, 0, 4, 32) == 0
+    assert L.fp4_quantize_workspace_bytes(fp4.NVFP4, 8, 64) >= 4096
+    assert L.fp4_linear_workspace_bytes(fp4.NVFP4, 8, 5120, 5120) > 0
+
+
+def test_tensor_init_fills_pitches():
+    L = fp4.lib()
+    t = fp4.fp4_tensor()
+    assert L.fp4_tensor_init(ctypes.byref(t), fp4.NVFP4, fp4.CANONICAL, 5, 2880, 16, 32, 64) == 0
+    assert t.codes_pitch == 1472 and t.scales_pitch == 184 and t.rows == 5 and t.cols == 2880
+    assert L.fp4_tensor_init(ctypes.byref(t), fp4.MXFP4, fp4.CANONICAL, 5, 48, 16, 32, 0) == 2
+    assert b"block size 32" in L.fp4_last_error()
+
+
+def _status(name):
+    return {0: "FP4_OK", 1: "FP4_ERR_INVALID_ARG", 2: "FP4_ERR_SHAPE", 3: "FP4_ERR_ALIGNMENT",
+            4: "FP4_ERR_WORKSPACE", 5: "FP4_ERR_FORMAT_MISMATCH", 6: "FP4_ERR_DEVICE",
+            7: "FP4_ERR_HIP"}[name]
+
+
+def test_status_strings():
+    L = fp4.lib()
+    for s in range(8):
+        assert L.fp4_status_string(s).decode() == _status(s)
+
+
+def test_host_validation_rejects_before_launch():
+    """Each error path returns its status without reaching the device check."""
+    L = fp4.lib()
+    good = fp4.fp4_tensor()
+    assert L.fp4_tensor_init(ctypes.byref(good), fp4.NVFP4, fp4.CANONICAL, 4, 64, 4096, 8192, 64) == 0
+    w = fp4.fp4_tensor()
+    assert L.fp4_tensor_init(ctypes.byref(w), fp4.NVFP4, fp4.WEIGHT_TILED, 32, 64, 4096, 8192, 64) == 0
+    # null input
+    assert L.fp4_quantize_act(0, None, 4, 64, None, ctypes.byref(good), 1024, 4096, None) == 1
+    # K not a multiple of the block
+    assert L.fp4_quantize_act(0, 4096, 4, 40, None, ctypes.byref(good), 1024, 4096, None) == 2
+    # misaligned input
+    assert L.fp4_quantize_act(0, 4097, 4, 64, None, ctypes.byref(good), 1024, 4096, None) == 3
+    # workspace too small for the dynamic scale
+    assert L.fp4_quantize_act(0, 4096, 4, 64, None, ctypes.byref(good), 1024, 16, None) == 4
+    # MXFP4 with a static scale
+    mx = fp4.fp4_tensor()
+    assert L.fp4_tensor_init(ctypes.byref(mx), fp4.MXFP4, fp4.CANONICAL, 4, 64, 4096, 8192, 0) == 0
+    assert L.fp4_quantize_act(1, 4096, 4, 64, 64, ctypes.byref(mx), 0, 0, None) == 1
+    # layout mismatch: activation into a tiled descriptor
+    assert L.fp4_quantize_act(0, 4096, 32, 64, None, ctypes.byref(w), 1024, 4096, None) == 5
+    # gemm: format mismatch, K mismatch, null output, small ldc
+    wmx = fp4.fp4_tensor()
+    assert L.fp4_tensor_init(ctypes.byref(wmx), fp4.MXFP4, fp4.WEIGHT_TILED, 32, 64, 4096, 8192, 0) == 0
+    assert L.fp4_gemm(ctypes.byref(good), ctypes.byref(wmx), 4096, 32, None, 0, None) == 5
+    w128 = fp4.fp4_tensor()
+    assert L.fp4_tensor_init(ctypes.byref(w128), fp4.NVFP4, fp4.WEIGHT_TILED, 32, 128, 4096, 8192, 64) == 0
+    assert L.fp4_gemm(ctypes.byref(good), ctypes.byref(w128), 4096, 32, None, 0, None) == 2
+    assert L.fp4_gemm(ctypes.byref(good), ctypes.byref(w), None, 32, None, 0, None) == 1
+    assert L.fp4_gemm(ctypes.byref(good), ctypes.byref(w), 4096, 16, None, 0, None) == 2
+    # linear: workspace missing
+    assert L.fp4_linear(4096, 4, ctypes.byref(w), None, 8192, None, 0, None) == 4
+    # NVFP4 descriptor without a tensor scale
+    bad = fp4.fp4_tensor()
+    assert L.fp4_tensor_init(ctypes.byref(bad), fp4.NVFP4, fp4.CANONICAL, 4, 64, 4096, 8192, None) == 0
+    assert L.fp4_gemm(ctypes.byref(bad), ctypes.byref(w), 4096, 32, None, 0, None) == 1
+    assert b"tensor_scale" in L.fp4_last_error()

@@ -1,0 +1,111 @@
+"""GPU GEMM / linear parity: |C_gpu - C_ref| <= 1e-5 * sum|a_k w_k| + 1 bf16 ulp of C_ref."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp4_quantize_amd as fp4
+import oracle
+import synth
+from tests.gpu_helpers import F, assert_canonical_equal, assert_gemm_close, bf16_out_to_f64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+FMTS = ["nvfp4", "mxfp4"]
+
+
+def _gemm_case(fmt, a_bits, w_bits, what, use_linear=True):
+    m, k = a_bits.shape
+    n = w_bits.shape[0]
+    print(f"[gemm] {what} fmt={fmt} m={m} n={n} k={k}", flush=True)
+    f = F[fmt]
+    qa_ref, qw_ref = oracle.quantize(f, a_bits), oracle.quantize(f, w_bits)
+    c_ref, l_ref = oracle.gemm(qa_ref, qw_ref)
+    wq = fp4.fp4_quantize_weight(to_dev(w_bits), f)
+    x = to_dev(a_bits)
+    qa = fp4.fp4_quantize_act(x, f)
+    assert_canonical_equal(qa, qa_ref, f, what=what + " (A codes)")
+    c = bf16_out_to_f64(fp4.fp4_gemm(qa, wq))
+    assert_gemm_close(c, c_ref, l_ref, what + " gemm")
+    if use_linear:
+        y = bf16_out_to_f64(fp4.fp4_linear(x, wq))
+        assert_gemm_close(y, c_ref, l_ref, what + " linear")
+    return c
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_single_gemm_config(fmt):
+    a, w = synth.single_gemm_inputs(0)
+    _gemm_case(fmt, a, w, "A[16,256] x W[256,256]")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m,n,k", [(1, 64, 128), (8, 272, 2880), (17, 100, 512), (32, 1040, 1024),
+                                   (5, 520, 5120), (2, 48, 17408)])
+def test_decode_path(fmt, m, n, k):
+    a = synth.normal((m, k), 1.0, 3, m * 31 + k)
+    w = synth.normal((n, k), 0.02, 3, n * 17 + k)
+    _gemm_case(fmt, a, w, "decode")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m,n,k", [(33, 136, 256), (300, 520, 2880), (129, 257, 640),
+                                   (256, 384, 3072)])
+def test_prefill_path(fmt, m, n, k):
+    a = synth.normal((m, k), 1.0, 4, m * 31 + k)
+    w = synth.normal((n, k), 0.02, 4, n * 17 + k)
+    _gemm_case(fmt, a, w, "prefill")
+
+
+def test_prefill_planted_outliers():
+    a, w = synth.prefill_inputs("k", seed=0, m=256)
+    _gemm_case("nvfp4", a, w[:512], "prefill t3 + 3616 plants")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_all_ones_closed_form(fmt):
+    """Every value 1.0: C = K exactly (alpha folds the tensor scales)."""
+    m, n, k = 40, 48, 1024
+    a = np.full((m, k), 0x3F80, np.uint16)   # bf16 1.0
+    w = np.full((n, k), 0x3F80, np.uint16)
+    c = _gemm_case(fmt, a, w, "all ones")
+    assert np.all(c == k)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m", [1, 8, 32])
+@pytest.mark.parametrize("k,n", synth.DECODE_SHAPES)
+def test_decode_full_size_sampled(fmt, m, k, n):
+    """Decode shapes at full size, in the launch configuration the benchmark times;
+    4096 sampled outputs against the oracle's k-ordered sums."""
+    print(f"[decode-full] fmt={fmt} m={m} k={k} n={n}", flush=True)
+    f = F[fmt]
+    a, w = synth.decode_inputs(m, k, n, seed=0)
+    qa_ref, qw_ref = oracle.quantize(f, a), oracle.quantize(f, w)
+    wq = fp4.fp4_quantize_weight(to_dev(w), f)
+    x = to_dev(a)
+    y = fp4.fp4_linear(x, wq)
+    y2 = fp4.fp4_linear(x, wq)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2), "split-K result differs between runs"
+    rng = np.random.default_rng(m * 7 + n)
+    rows = rng.integers(0, m, 4096)
+    cols = rng.integers(0, n, 4096)
+    c_ref, l_ref = oracle.gemm_sampled(qa_ref, qw_ref, rows, cols)
+    yv = bf16_out_to_f64(y)[rows, cols]
+    assert_gemm_close(yv, c_ref, l_ref, f"decode full {m}x{n}x{k}")
+    # the activation codes of the linear path equal the oracle's
+    qa = fp4.fp4_quantize_act(x, f)
+    assert_canonical_equal(qa, qa_ref, f, what="decode activation")
+    # weight codes, compared through the canonical export
+    assert_canonical_equal(fp4.fp4_export_canonical(wq), qw_ref, f, what="decode weight")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemm_deterministic(fmt):
+    a = synth.normal((200, 1024), 1.0, 6, 1)
+    w = synth.normal((300, 1024), 0.02, 6, 2)
+    wq = fp4.fp4_quantize_weight(to_dev(w), F[fmt])
+    x = to_dev(a)
+    y1, y2 = fp4.fp4_linear(x, wq), fp4.fp4_linear(x, wq)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)

@@ -1,0 +1,120 @@
+"""GPU quantization parity: codes, scales and tensor scales byte-identical to the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp4_quantize_amd as fp4
+import oracle
+import synth
+from tests.gpu_helpers import F, assert_canonical_equal, to_dev
+
+pytestmark = pytest.mark.gpu
+
+FMTS = ["nvfp4", "mxfp4"]
+
+
+def _act_case(fmt, bits, what, static=None):
+    print(f"[quant-act] {what} fmt={fmt} shape={bits.shape}", flush=True)
+    f = F[fmt]
+    ref = oracle.quantize(f, bits, mode=oracle.STATIC if static is not None else oracle.DYNAMIC,
+                          static_scale=static)
+    st = None if static is None else torch.tensor([static], dtype=torch.float32, device="cuda")
+    q = fp4.fp4_quantize_act(to_dev(bits), f, static_scale=st)
+    assert_canonical_equal(q, ref, f, what=what)
+    return q, ref
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_single_gemm_activation(fmt):
+    a, _ = synth.single_gemm_inputs(0)
+    _act_case(fmt, a, "A[16,256] with x100 outliers")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m,k", [(1, 32), (3, 96), (17, 2880), (40, 5120), (129, 544), (1, 17408)])
+def test_ragged_shapes(fmt, m, k):
+    bits = synth.normal((m, k), 1.0, 1, m * 100003 + k)
+    _act_case(fmt, bits, f"ragged {m}x{k}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_every_finite_bf16_value(fmt):
+    """All 65,280 finite bf16 patterns (both zeros included), shuffled into rows."""
+    bits = np.arange(0, 0x10000, dtype=np.uint32)
+    exp = (bits >> 7) & 0xFF
+    bits = bits[exp != 0xFF].astype(np.uint16)
+    rng = np.random.default_rng(0)
+    rng.shuffle(bits)
+    k = 2560
+    rows = len(bits) // k
+    x = bits[: rows * k].reshape(rows, k)
+    _act_case(fmt, x, "every finite bf16")
+    # sorted order too: blocks of neighbouring magnitudes exercise every scale
+    xs = np.sort(bits)[: rows * k].reshape(rows, k)
+    _act_case(fmt, xs, "every finite bf16, sorted")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_tiny_and_huge_magnitudes(fmt):
+    rng = np.random.default_rng(5)
+    for scale in (2.0 ** -126, 2.0 ** -110, 2.0 ** -70, 2.0 ** 60, 2.0 ** 120):
+        x = synth.bf16_bits((rng.standard_normal((8, 256)) * scale).astype(np.float32))
+        _act_case(fmt, x, f"magnitude {scale:g}")
+    z = np.zeros((4, 64), np.uint16)
+    z[1, 5] = 0x8000
+    _act_case(fmt, z, "all zeros")
+
+
+def test_nvfp4_ties_and_midpoints():
+    """Blocks whose elements sit exactly on rounding midpoints of their scale."""
+    rng = np.random.default_rng(3)
+    rows = []
+    for _ in range(256):
+        s = float(2.0 ** rng.integers(-8, 8)) * (1 + rng.integers(0, 8) / 8)
+        mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0]) * s
+        blk = np.concatenate([[6 * s], rng.choice(mids, 15) * rng.choice([-1, 1], 15)])
+        rows.append(blk)
+    x = synth.bf16_bits(np.array(rows, np.float32).reshape(16, 256))
+    _act_case("nvfp4", x, "midpoints, dynamic")
+    _act_case("nvfp4", x, "midpoints, static 1/448", static=float(np.float32(1 / 448)))
+
+
+def test_prefill_planted_outliers_two_level():
+    """t(3)*4 activations with planted +-3616 entries: block maxima beyond 2688."""
+    a, _ = synth.prefill_inputs("q", seed=0, m=512)
+    q, ref = _act_case("nvfp4", a, "prefill t3 with 3616 plants")
+    assert ref.scales.max() == 0x7E
+
+
+@pytest.mark.parametrize("static", [1.0, 0.01, 3.5, 1e-30])
+def test_static_scale_saturates(static):
+    a, _ = synth.prefill_inputs("k", seed=1, m=64)
+    _act_case("nvfp4", a, f"static S_t={static}", static=float(np.float32(static)))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n,k", [(256, 256), (520, 2880), (33, 96), (1024, 5120)])
+def test_weight_cache_layout(fmt, n, k):
+    print(f"[quant-weight] fmt={fmt} n={n} k={k}", flush=True)
+    f = F[fmt]
+    w = synth.normal((n, k), 0.02, 2, n * 7 + k)
+    ref = oracle.quantize(f, w)
+    wq = fp4.fp4_quantize_weight(to_dev(w), f)
+    canon = fp4.fp4_export_canonical(wq)
+    assert_canonical_equal(canon, ref, f, what=f"weight {n}x{k}")
+    # dequantized values: RN_fp32 of the exact q * s_b * S_t
+    dq = fp4.fp4_dequantize(wq).cpu().numpy()
+    ref_dq = oracle.dequantize(ref).astype(np.float32)
+    assert np.array_equal(dq, ref_dq)
+    dq2 = fp4.fp4_dequantize(canon).cpu().numpy()
+    assert np.array_equal(dq2, ref_dq)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantize_is_deterministic(fmt):
+    a = synth.normal((64, 4096), 1.0, 9, 1)
+    x = to_dev(a)
+    q1 = fp4.fp4_quantize_act(x, F[fmt])
+    q2 = fp4.fp4_quantize_act(x, F[fmt])
+    torch.cuda.synchronize()
+    assert torch.equal(q1.codes, q2.codes) and torch.equal(q1.scales, q2.scales)
