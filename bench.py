@@ -1,0 +1,284 @@
+"""Benchmark of the W4A4 block-scaled FP4 linear on one MI355X.
+
+Default workload (one step): the decode-shaped NVFP4 W4A4 linear at every
+M in {1, 8, 32} and (K, N) in {(5120, 5120), (5120, 17408), (17408, 5120)} --
+nine fp4_linear calls (activation quantization + GEMM). Weights are bf16
+~N(0, 0.02) quantized once before timing; activations are bf16 ~N(0, 1)
+quantized inside every call. Each weight exists in several copies that the
+steps rotate through, so the bytes between two uses of one copy exceed the
+256 MB Infinity Cache and the weight stream comes from HBM.
+
+Prints one JSON line: throughput incl. activation quantization (TFLOP/s), a
+roofline entry for the dominant kernel (decode GEMM, HBM-bound: algorithmic
+bytes per launch over its average duration, timed with HIP events on the
+launch stream) and the CPU oracle timed on a bounded sample of the same work.
+
+    python bench.py [--steps K] [--warmup W] [--fmt nvfp4|mxfp4]
+                    [--workload decode|prefill|square8192|single]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0              # MI355X HBM3E, published
+FP4_PEAK_TFLOPS = 10100.0          # dense FP4 MFMA, published
+F16_PEAK_TFLOPS = 2500.0           # dense f16/bf16 MFMA, published
+METRIC = "W4A4 NVFP4 GEMM TFLOPS incl. act-quant; % FP4 MFMA peak / % HBM BW"
+ROTATE_BYTES = 768 << 20           # bytes touched between two uses of one weight copy
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--fmt", default="nvfp4", choices=["nvfp4", "mxfp4"])
+    p.add_argument("--workload", default="decode", choices=["decode", "prefill", "square8192", "single"])
+    p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    p.add_argument("--kernel-reps", type=int, default=50)
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def workload_configs(name):
+    import synth
+    if name == "decode":
+        return [(m, k, n) for (k, n) in synth.DECODE_SHAPES for m in synth.DECODE_M], \
+            "decode-shaped W4A4 linear, M in {1,8,32} x (K,N) in {(5120,5120),(5120,17408),(17408,5120)}"
+    if name == "prefill":
+        return [(synth.PREFILL_M, k, n) for (k, n) in synth.PREFILL_LAYERS.values()], \
+            "prefill-shaped W4A4 GEMMs of a Llama-style 3B block, M=4096"
+    if name == "square8192":
+        return [(8192, 8192, 8192)], "square W4A4 GEMM M=N=K=8192"
+    return [(16, 256, 256)], "single W4A4 GEMM A[16,256] x W[256,256]"
+
+
+def gemm_bytes(m, k, n, fmt):
+    """Algorithmic HBM bytes of one GEMM launch: W codes + W scales + A codes +
+    A scales + C (bf16). Padding is not counted."""
+    bs = 16 if fmt == 0 else 32
+    q = k // 2 + k // bs
+    return n * q + m * q + 2 * m * n
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import block_scaled_fp4_quantize_amd as fp4
+    import synth
+
+    if not os.path.exists(fp4.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    fmt = fp4.FORMATS[args.fmt]
+    configs, desc = workload_configs(args.workload)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---- inputs: weights quantized once (several copies), activations per config
+    shapes = sorted({(k, n) for (_, k, n) in configs})
+    step_w_bytes = sum(n * (k // 2 + k // (16 if fmt == 0 else 32)) for (k, n) in shapes)
+    copies = max(1, -(-ROTATE_BYTES // step_w_bytes)) if args.workload == "decode" else 1
+    weights, w_host, a_host = {}, {}, {}
+    for (k, n) in shapes:
+        if args.workload == "decode":
+            w_bits = synth.decode_inputs(1, k, n, seed=0)[1]
+        else:
+            w_bits = synth.normal((n, k), 0.02, 0, 500 + n + k)
+        w_host[(k, n)] = w_bits
+        w_dev = to_dev(w_bits)
+        weights[(k, n)] = [fp4.fp4_quantize_weight(w_dev, fmt) for _ in range(copies)]
+        del w_dev
+    xs, outs, wss = {}, {}, {}
+    for (m, k, n) in configs:
+        if args.workload == "decode":
+            a_bits = synth.normal((m, k), 1.0, 0, 2 * k + 1)   # the activation decode_inputs draws
+        else:
+            a_bits = synth.normal((m, k), 1.0, 0, 600 + m + k)
+        a_host[(m, k, n)] = a_bits
+        xs[(m, k, n)] = to_dev(a_bits)
+        outs[(m, k, n)] = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+        wss[(m, k, n)] = torch.zeros(max(1, fp4.fp4_linear_workspace_bytes(fmt, m, n, k)),
+                                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        for cfg in configs:
+            m, k, n = cfg
+            fp4.fp4_linear(xs[cfg], weights[(k, n)][i % copies], out=outs[cfg], workspace=wss[cfg])
+
+    # ---- graphs: one per weight copy (each replays one full step)
+    use_graph = not args.no_graph
+    graphs = []
+    if use_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for i in range(copies):
+                step(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for i in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(i):
+        if use_graph:
+            graphs[i % copies].replay()
+        else:
+            step(i)
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(args.steps):
+        run(i)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    flops = sum(2.0 * m * n * k for (m, k, n) in configs)
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+
+    # ---- dominant kernel: the GEMM launch alone, back-to-back in a graph,
+    # timed with events on the stream the launches go to.
+    kern = {}
+    reps = max(copies, args.kernel_reps)
+    for cfg in configs:
+        m, k, n = cfg
+        # the activation layout fp4_linear uses internally (fragment-tiled)
+        qa = fp4.fp4_quantize_act(xs[cfg], fmt, layout=fp4.TILED)
+        gws = torch.zeros(max(1, fp4.lib().fp4_gemm_workspace_bytes(fmt, m, n, k)),
+                          dtype=torch.uint8, device=dev)
+        wl = weights[(k, n)]
+        fp4.fp4_gemm(qa, wl[0], out=outs[cfg], workspace=gws)
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                for r in range(reps):
+                    fp4.fp4_gemm(qa, wl[r % copies], out=outs[cfg], workspace=gws)
+            g.replay()
+            s.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            g.replay()
+            e1.record(s)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        if m <= 32:
+            name = "k_gemm_decode<%s,MG=%d>" % (args.fmt, 1 if m <= 16 else 2)
+        else:
+            name = "k_gemm_prefill<%s>" % args.fmt
+        d = kern.setdefault(name, {"launches": 0, "us": 0.0, "bytes": 0.0, "flops": 0.0, "per_cfg": []})
+        d["launches"] += 1
+        d["us"] += us
+        d["bytes"] += gemm_bytes(m, k, n, fmt)
+        d["flops"] += 2.0 * m * n * k
+        d["per_cfg"].append({"m": m, "k": k, "n": n, "us": round(us, 3),
+                             "GBps": round(gemm_bytes(m, k, n, fmt) / (us * 1e-6) / 1e9, 1)})
+    dom_name = max(kern, key=lambda nm: kern[nm]["us"])
+    dk = kern[dom_name]
+    avg_us = dk["us"] / dk["launches"]
+    if args.workload == "decode" or "decode" in dom_name:
+        achieved = dk["bytes"] / dk["launches"] / (avg_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        achieved = dk["flops"] / dk["launches"] / (avg_us * 1e-6) / 1e12
+        peak = FP4_PEAK_TFLOPS if fmt == 1 else F16_PEAK_TFLOPS
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None}
+    roof.update({"kernel": dom_name, "avg_launch_us": round(avg_us, 3), "launches_per_step": dk["launches"],
+                 "per_config": dk["per_cfg"]})
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if fmt == 0 else "fp4",
+        "data": "synthetic",
+        "config": {"workload": desc, "format": args.fmt, "launch": "hip-graph replay" if use_graph else "eager",
+                   "weight_copies": copies, "calls_per_step": len(configs),
+                   "fraction_of_fp4_peak": round(tflops / FP4_PEAK_TFLOPS, 6)},
+        "roofline": roof,
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(configs, fmt, args, a_host, w_host)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(configs, fmt, args, a_host, w_host):
+    """The CPU oracle (plain C, one thread) on a bounded sample of the same
+    linear calls: full activation quantization plus the k-ordered binary64 GEMM
+    on a subset of output columns (weights quantized beforehand, untimed, as on
+    the GPU). Reported in the metric's unit: sampled flops / oracle seconds."""
+    import oracle
+    budget = args.cpu_seconds / len(configs)
+    tot_flops, tot_s, parts = 0.0, 0.0, []
+    wq_cache = {}
+    for (m, k, n) in configs:
+        a_bits, w_bits = a_host[(m, k, n)], w_host[(k, n)]
+        if (k, n) not in wq_cache:
+            wq_cache[(k, n)] = oracle.quantize(fmt, w_bits)
+        qw = wq_cache[(k, n)]
+        # estimate the per-output cost, then size the column sample to the budget
+        t = time.perf_counter()
+        qa = oracle.quantize(fmt, a_bits)
+        t_q = time.perf_counter() - t
+        probe = min(n, 4)
+        t = time.perf_counter()
+        sub = oracle.Quantized(fmt, qw.codes[:probe], qw.scales[:probe], qw.tensor_scale, k)
+        oracle.gemm_loop(qa, sub)
+        per_col = (time.perf_counter() - t) / probe
+        cols = int(max(1, min(n, (budget - t_q) / max(per_col, 1e-9))))
+        t = time.perf_counter()
+        qa = oracle.quantize(fmt, a_bits)
+        sub = oracle.Quantized(fmt, qw.codes[:cols], qw.scales[:cols], qw.tensor_scale, k)
+        oracle.gemm_loop(qa, sub)
+        dt = time.perf_counter() - t
+        fl = 2.0 * m * cols * k
+        tot_flops += fl
+        tot_s += dt
+        parts.append(f"M={m},K={k}: {cols}/{n} cols")
+    return {"value": tot_flops / tot_s / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": "per call: full activation quantization + k-ordered FP64 GEMM on the first "
+                      "columns of the pre-quantized weight (" + "; ".join(parts) + f"); {tot_s:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

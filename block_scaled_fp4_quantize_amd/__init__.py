@@ -23,7 +23,8 @@ import threading
 import torch
 
 NVFP4, MXFP4 = 0, 1
-CANONICAL, WEIGHT_TILED = 0, 1
+CANONICAL, TILED = 0, 1
+WEIGHT_TILED = TILED
 FORMATS = {"nvfp4": NVFP4, "mxfp4": MXFP4}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -156,24 +157,27 @@ def fp4_quantize_weight(w: torch.Tensor, fmt=NVFP4) -> Fp4Tensor:
     w = _bf16_2d(w, "w")
     n, k = w.shape
     L = lib()
-    out = Fp4Tensor(fmt, WEIGHT_TILED, n, k, w.device)
+    out = Fp4Tensor(fmt, TILED, n, k, w.device)
     nws = L.fp4_quantize_workspace_bytes(fmt, n, k)
-    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=w.device)
+    ws = torch.zeros(max(nws, 1), dtype=torch.uint8, device=w.device)
     _check(L.fp4_quantize_weight(fmt, _ptr(w), n, k, ctypes.byref(out.desc), _ptr(ws), nws,
                                  _stream(w.device)))
     return out
 
 
-def fp4_quantize_act(a: torch.Tensor, fmt=NVFP4, static_scale: torch.Tensor | None = None) -> Fp4Tensor:
+def fp4_quantize_act(a: torch.Tensor, fmt=NVFP4, static_scale: torch.Tensor | None = None,
+                     layout: int = CANONICAL, workspace: torch.Tensor | None = None) -> Fp4Tensor:
     fmt = _fmt(fmt)
     a = _bf16_2d(a, "a")
     m, k = a.shape
     L = lib()
-    out = Fp4Tensor(fmt, CANONICAL, m, k, a.device)
+    out = Fp4Tensor(fmt, layout, m, k, a.device)
     nws = L.fp4_quantize_workspace_bytes(fmt, m, k)
-    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=a.device)
+    ws = workspace
+    if ws is None:   # zero-filled once, as the C ABI requires
+        ws = torch.zeros(max(nws, 1), dtype=torch.uint8, device=a.device)
     _check(L.fp4_quantize_act(fmt, _ptr(a), m, k, _ptr(static_scale), ctypes.byref(out.desc),
-                              _ptr(ws), nws, _stream(a.device)))
+                              _ptr(ws), ws.numel(), _stream(a.device)))
     return out
 
 
@@ -184,8 +188,8 @@ def fp4_gemm(a: Fp4Tensor, w: Fp4Tensor, out: torch.Tensor | None = None,
     if out is None:
         out = torch.empty(m, n, dtype=torch.bfloat16, device=a.device)
     nws = L.fp4_gemm_workspace_bytes(a.fmt, m, n, a.k)
-    if workspace is None:
-        workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=a.device)
+    if workspace is None:   # zero-filled once, as the C ABI requires
+        workspace = torch.zeros(max(nws, 1), dtype=torch.uint8, device=a.device)
     _check(L.fp4_gemm(ctypes.byref(a.desc), ctypes.byref(w.desc), _ptr(out), out.stride(0),
                       _ptr(workspace), workspace.numel(), _stream(a.device)))
     return out
@@ -205,8 +209,8 @@ def fp4_linear(x: torch.Tensor, w: Fp4Tensor, static_scale: torch.Tensor | None 
     if out is None:
         out = torch.empty(m, w.rows, dtype=torch.bfloat16, device=x.device)
     nws = L.fp4_linear_workspace_bytes(w.fmt, m, w.rows, w.k)
-    if workspace is None:
-        workspace = torch.empty(max(nws, 1), dtype=torch.uint8, device=x.device)
+    if workspace is None:   # zero-filled once, as the C ABI requires
+        workspace = torch.zeros(max(nws, 1), dtype=torch.uint8, device=x.device)
     _check(L.fp4_linear(_ptr(x), m, ctypes.byref(w.desc), _ptr(static_scale), _ptr(out),
                         _ptr(workspace), workspace.numel(), _stream(x.device)))
     return out

@@ -60,7 +60,7 @@ fp4_status check_device() {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool valid_fmt(int32_t f) { return f == FP4_NVFP4 || f == FP4_MXFP4; }
-bool valid_layout(int32_t l) { return l == FP4_LAYOUT_CANONICAL || l == FP4_LAYOUT_WEIGHT_TILED; }
+bool valid_layout(int32_t l) { return l == FP4_LAYOUT_CANONICAL || l == FP4_LAYOUT_TILED; }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -97,54 +97,43 @@ fp4_status check_tensor(const fp4_tensor *t, const char *name) {
   return FP4_OK;
 }
 
-size_t quant_ws(int32_t fmt) {
-  return fmt == FP4_NVFP4 ? (size_t)kMaxAmaxParts * sizeof(uint32_t) : 0;
-}
+size_t quant_ws(int32_t fmt) { return fmt == FP4_NVFP4 ? kQuantScratchBytes : 0; }
 
-// Everything fp4_linear keeps in its workspace, at fixed offsets.
+// Everything fp4_linear keeps in its workspace, at fixed offsets: the
+// activations quantized into the tiled layout, their tensor scale and the
+// quantizer's scratch.
 struct LinearLayout {
-  size_t codes, scales, ts, parts, gemm, total;
-  int64_t cpitch, spitch;
+  size_t codes, scales, ts, scratch, total;
 };
 
-LinearLayout linear_layout(int32_t fmt, int64_t m, int64_t n, int64_t k) {
+LinearLayout linear_layout(int32_t fmt, int64_t m, int64_t k) {
   LinearLayout L;
-  int64_t kp = k_pad(k);
-  L.cpitch = kp / 2;
-  L.spitch = kp / block_of(fmt);
+  const int64_t mp = round_up(m, 16), kp = k_pad(k);
   size_t off = 0;
-  L.codes = off; off = align256(off + (size_t)(m * L.cpitch));
-  L.scales = off; off = align256(off + (size_t)(m * L.spitch));
+  L.codes = off; off = align256(off + (size_t)(mp * kp / 2));
+  L.scales = off; off = align256(off + (size_t)(mp * kp / block_of(fmt)));
   L.ts = off; off = align256(off + sizeof(float));
-  L.parts = off; off = align256(off + quant_ws(fmt));
-  L.gemm = off;
-  off = align256(off + (m <= kDecodeMaxM ? decode_workspace_bytes(fmt, m, n, k) : 0));
+  L.scratch = off; off = align256(off + kQuantScratchBytes);
   L.total = off;
   return L;
 }
 
-fp4_status run_quant_act(int32_t fmt, const void *a, int64_t m, int64_t k,
-                         const float *static_scale, uint8_t *codes, int64_t cp, uint8_t *scales,
-                         int64_t sp, float *ts, uint32_t *parts, int *zero_ptr, int zero_n,
-                         hipStream_t stream) {
-  int nparts = 0;
-  if (fmt == FP4_NVFP4 && !static_scale) {
-    nparts = amax_parts(m * k);
-    hipError_t e = launch_amax_parts((const uint16_t *)a, m * k, parts, nparts, stream);
-    if (e != hipSuccess) return hip_fail(e, "amax launch");
-  }
-  hipError_t e = launch_quant_canonical(fmt, (const uint16_t *)a, m, k, parts, nparts,
-                                        static_scale, codes, cp, scales, sp, ts, zero_ptr,
-                                        zero_n, stream);
+fp4_status run_quant(int32_t fmt, int tiled, const void *x, int64_t rows, int64_t k,
+                     const float *static_scale, const fp4_tensor *out, void *scratch,
+                     hipStream_t stream) {
+  hipError_t e = launch_quantize(fmt, tiled, (const uint16_t *)x, rows, k, static_scale,
+                                 (uint8_t *)out->codes, out->codes_pitch, (uint8_t *)out->scales,
+                                 out->scales_pitch, fmt == FP4_NVFP4 ? out->tensor_scale : nullptr,
+                                 (uint32_t *)scratch, stream);
   if (e != hipSuccess) return hip_fail(e, "quantize launch");
   return FP4_OK;
 }
 
 fp4_status run_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c, int64_t ldc,
-                    void *gemm_ws, size_t gemm_ws_bytes, bool counters_zeroed,
                     hipStream_t stream) {
   GemmArgs g;
   g.fmt = a->fmt;
+  g.a_tiled = a->layout == FP4_LAYOUT_TILED;
   g.a_codes = (const uint8_t *)a->codes; g.a_cpitch = a->codes_pitch;
   g.a_scales = (const uint8_t *)a->scales; g.a_spitch = a->scales_pitch;
   g.a_ts = a->tensor_scale;
@@ -152,31 +141,7 @@ fp4_status run_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c, int64_t l
   g.w_ts = w->tensor_scale;
   g.m = a->rows; g.n = w->rows; g.k = a->cols;
   g.c = (uint16_t *)c; g.ldc = ldc;
-  hipError_t e;
-  if (g.m <= kDecodeMaxM) {
-    DecodePlan p = decode_plan(g.fmt, g.m, g.n, g.k);
-    size_t need = decode_workspace_bytes(g.fmt, g.m, g.n, g.k);
-    float *partials = nullptr;
-    int *counters = nullptr;
-    if (p.splits > 1) {
-      if (!gemm_ws || gemm_ws_bytes < need) {  // no room for split-K: one split
-        p.kt_per_wg = (int)(k_pad(g.k) / 128);
-        p.splits = 1;
-        p.frags = (p.kt_per_wg + 3) / 4;
-      } else {
-        int64_t nt_n = round_up(g.n, 16) / 16;
-        counters = (int *)gemm_ws;
-        partials = (float *)((char *)gemm_ws + align256((size_t)nt_n * 4));
-        if (!counters_zeroed) {
-          e = launch_zero_ints(counters, (int)nt_n, stream);
-          if (e != hipSuccess) return hip_fail(e, "counter clear launch");
-        }
-      }
-    }
-    e = launch_gemm_decode(g, p, partials, counters, stream);
-  } else {
-    e = launch_gemm_prefill(g, stream);
-  }
+  hipError_t e = g.m <= kDecodeMaxM ? launch_gemm_decode(g, stream) : launch_gemm_prefill(g, stream);
   if (e != hipSuccess) return hip_fail(e, "gemm launch");
   return FP4_OK;
 }
@@ -189,13 +154,13 @@ int32_t fp4_block_size(int32_t fmt) { return valid_fmt(fmt) ? block_of(fmt) : 0;
 
 size_t fp4_codes_bytes(int32_t fmt, int32_t layout, int64_t rows, int64_t k) {
   if (!valid_fmt(fmt) || !valid_layout(layout) || rows <= 0 || k <= 0) return 0;
-  int64_t r = layout == FP4_LAYOUT_WEIGHT_TILED ? round_up(rows, 16) : rows;
+  int64_t r = layout == FP4_LAYOUT_TILED ? round_up(rows, 16) : rows;
   return (size_t)(r * (k_pad(k) / 2));
 }
 
 size_t fp4_scales_bytes(int32_t fmt, int32_t layout, int64_t rows, int64_t k) {
   if (!valid_fmt(fmt) || !valid_layout(layout) || rows <= 0 || k <= 0) return 0;
-  int64_t r = layout == FP4_LAYOUT_WEIGHT_TILED ? round_up(rows, 16) : rows;
+  int64_t r = layout == FP4_LAYOUT_TILED ? round_up(rows, 16) : rows;
   return (size_t)(r * (k_pad(k) / block_of(fmt)));
 }
 
@@ -231,8 +196,8 @@ fp4_status fp4_quantize_weight(int32_t fmt, const void *w_bf16, int64_t n, int64
   if (!w_bf16) return fail(FP4_ERR_INVALID_ARG, "weight pointer is null");
   if (!aligned16(w_bf16)) return fail(FP4_ERR_ALIGNMENT, "weight must be 16-byte aligned");
   if ((st = check_tensor(out, "out")) != FP4_OK) return st;
-  if (out->layout != FP4_LAYOUT_WEIGHT_TILED)
-    return fail(FP4_ERR_FORMAT_MISMATCH, "weights are stored in the WEIGHT_TILED layout");
+  if (out->layout != FP4_LAYOUT_TILED)
+    return fail(FP4_ERR_FORMAT_MISMATCH, "weights are stored in the TILED layout");
   if (out->fmt != fmt || out->rows != n || out->cols != k)
     return fail(FP4_ERR_FORMAT_MISMATCH, "out descriptor does not match format/shape");
   if (workspace_bytes < quant_ws(fmt) || (quant_ws(fmt) && !workspace))
@@ -240,18 +205,8 @@ fp4_status fp4_quantize_weight(int32_t fmt, const void *w_bf16, int64_t n, int64
   if (workspace && !aligned16(workspace))
     return fail(FP4_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
   if ((st = check_device()) != FP4_OK) return st;
-  int nparts = 0;
-  if (fmt == FP4_NVFP4) {
-    nparts = amax_parts(n * k);
-    hipError_t e = launch_amax_parts((const uint16_t *)w_bf16, n * k, (uint32_t *)workspace,
-                                     nparts, stream);
-    if (e != hipSuccess) return hip_fail(e, "amax launch");
-  }
-  hipError_t e = launch_quant_tiled(fmt, (const uint16_t *)w_bf16, n, k,
-                                    (const uint32_t *)workspace, nparts, (uint8_t *)out->codes,
-                                    (uint8_t *)out->scales, out->tensor_scale, stream);
-  if (e != hipSuccess) return hip_fail(e, "weight quantize launch");
-  return ok();
+  st = run_quant(fmt, 1, w_bf16, n, k, nullptr, out, workspace, stream);
+  return st == FP4_OK ? ok() : st;
 }
 
 fp4_status fp4_quantize_act(int32_t fmt, const void *a_bf16, int64_t m, int64_t k,
@@ -262,8 +217,6 @@ fp4_status fp4_quantize_act(int32_t fmt, const void *a_bf16, int64_t m, int64_t 
   if (!a_bf16) return fail(FP4_ERR_INVALID_ARG, "activation pointer is null");
   if (!aligned16(a_bf16)) return fail(FP4_ERR_ALIGNMENT, "activations must be 16-byte aligned");
   if ((st = check_tensor(out, "out")) != FP4_OK) return st;
-  if (out->layout != FP4_LAYOUT_CANONICAL)
-    return fail(FP4_ERR_FORMAT_MISMATCH, "activations are stored in the CANONICAL layout");
   if (out->fmt != fmt || out->rows != m || out->cols != k)
     return fail(FP4_ERR_FORMAT_MISMATCH, "out descriptor does not match format/shape");
   if (fmt == FP4_MXFP4 && static_scale)
@@ -274,41 +227,39 @@ fp4_status fp4_quantize_act(int32_t fmt, const void *a_bf16, int64_t m, int64_t 
   if (workspace && !aligned16(workspace))
     return fail(FP4_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
   if ((st = check_device()) != FP4_OK) return st;
-  st = run_quant_act(fmt, a_bf16, m, k, static_scale, (uint8_t *)out->codes, out->codes_pitch,
-                     (uint8_t *)out->scales, out->scales_pitch, out->tensor_scale,
-                     (uint32_t *)workspace, nullptr, 0, stream);
+  st = run_quant(fmt, out->layout == FP4_LAYOUT_TILED, a_bf16, m, k, static_scale, out,
+                 workspace, stream);
   return st == FP4_OK ? ok() : st;
 }
 
 size_t fp4_gemm_workspace_bytes(int32_t fmt, int64_t m, int64_t n, int64_t k) {
-  if (!valid_fmt(fmt) || m <= 0 || n <= 0 || k <= 0) return 0;
-  return m <= kDecodeMaxM ? decode_workspace_bytes(fmt, m, n, k) : 0;
+  (void)fmt; (void)m; (void)n; (void)k;
+  return 0;
 }
 
 fp4_status fp4_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c_bf16, int64_t ldc,
                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
   fp4_status st;
   if ((st = check_tensor(a, "a")) != FP4_OK) return st;
   if ((st = check_tensor(w, "w")) != FP4_OK) return st;
-  if (a->layout != FP4_LAYOUT_CANONICAL || w->layout != FP4_LAYOUT_WEIGHT_TILED)
-    return fail(FP4_ERR_FORMAT_MISMATCH, "a must be CANONICAL and w WEIGHT_TILED");
+  if (w->layout != FP4_LAYOUT_TILED)
+    return fail(FP4_ERR_FORMAT_MISMATCH, "w must be in the TILED layout");
   if (a->fmt != w->fmt) return fail(FP4_ERR_FORMAT_MISMATCH, "a and w differ in format");
   if (a->cols != w->cols) return fail(FP4_ERR_SHAPE, "a and w differ in K");
   if (!c_bf16) return fail(FP4_ERR_INVALID_ARG, "output pointer is null");
   if (ldc < w->rows) return fail(FP4_ERR_SHAPE, "ldc smaller than N");
   if (((uintptr_t)c_bf16 & 1u) != 0) return fail(FP4_ERR_ALIGNMENT, "output must be 2-byte aligned");
-  if (workspace_bytes && !workspace) return fail(FP4_ERR_WORKSPACE, "null workspace with size");
-  if (workspace && !aligned16(workspace))
-    return fail(FP4_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
   if (a->rows > INT32_MAX || w->rows > INT32_MAX) return fail(FP4_ERR_SHAPE, "too many rows");
   if ((st = check_device()) != FP4_OK) return st;
-  st = run_gemm(a, w, c_bf16, ldc, workspace, workspace_bytes, false, stream);
+  st = run_gemm(a, w, c_bf16, ldc, stream);
   return st == FP4_OK ? ok() : st;
 }
 
 size_t fp4_linear_workspace_bytes(int32_t fmt, int64_t m, int64_t n, int64_t k) {
   if (!valid_fmt(fmt) || m <= 0 || n <= 0 || k <= 0) return 0;
-  return linear_layout(fmt, m, n, k).total;
+  return linear_layout(fmt, m, k).total;
 }
 
 fp4_status fp4_linear(const void *x_bf16, int64_t m, const fp4_tensor *w,
@@ -316,8 +267,8 @@ fp4_status fp4_linear(const void *x_bf16, int64_t m, const fp4_tensor *w,
                       size_t workspace_bytes, hipStream_t stream) {
   fp4_status st;
   if ((st = check_tensor(w, "w")) != FP4_OK) return st;
-  if (w->layout != FP4_LAYOUT_WEIGHT_TILED)
-    return fail(FP4_ERR_FORMAT_MISMATCH, "w must be WEIGHT_TILED");
+  if (w->layout != FP4_LAYOUT_TILED)
+    return fail(FP4_ERR_FORMAT_MISMATCH, "w must be in the TILED layout");
   const int32_t fmt = w->fmt;
   const int64_t k = w->cols, n = w->rows;
   if ((st = check_shape(fmt, m, k)) != FP4_OK) return st;
@@ -326,7 +277,7 @@ fp4_status fp4_linear(const void *x_bf16, int64_t m, const fp4_tensor *w,
   if (((uintptr_t)y_bf16 & 1u) != 0) return fail(FP4_ERR_ALIGNMENT, "output must be 2-byte aligned");
   if (fmt == FP4_MXFP4 && static_scale)
     return fail(FP4_ERR_INVALID_ARG, "MXFP4 has no per-tensor scale");
-  LinearLayout L = linear_layout(fmt, m, n, k);
+  const LinearLayout L = linear_layout(fmt, m, k);
   if (!workspace || workspace_bytes < L.total)
     return fail(FP4_ERR_WORKSPACE, "workspace needs %zu bytes", L.total);
   if (!aligned16(workspace)) return fail(FP4_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
@@ -335,27 +286,17 @@ fp4_status fp4_linear(const void *x_bf16, int64_t m, const fp4_tensor *w,
   char *ws = (char *)workspace;
   fp4_tensor a;
   a.fmt = fmt;
-  a.layout = FP4_LAYOUT_CANONICAL;
+  a.layout = FP4_LAYOUT_TILED;
   a.rows = m;
   a.cols = k;
-  a.codes_pitch = L.cpitch;
-  a.scales_pitch = L.spitch;
+  a.codes_pitch = 0;
+  a.scales_pitch = 0;
   a.codes = ws + L.codes;
   a.scales = ws + L.scales;
   a.tensor_scale = (float *)(ws + L.ts);
-  // The quantize kernel clears the split-K counters of the GEMM that follows.
-  int *zero_ptr = nullptr;
-  int zero_n = 0;
-  size_t gemm_bytes = L.total - L.gemm;
-  if (m <= kDecodeMaxM && decode_plan(fmt, m, n, k).splits > 1) {
-    zero_ptr = (int *)(ws + L.gemm);
-    zero_n = (int)(round_up(n, 16) / 16);
-  }
-  st = run_quant_act(fmt, x_bf16, m, k, static_scale, (uint8_t *)a.codes, a.codes_pitch,
-                     (uint8_t *)a.scales, a.scales_pitch, a.tensor_scale,
-                     (uint32_t *)(ws + L.parts), zero_ptr, zero_n, stream);
+  st = run_quant(fmt, 1, x_bf16, m, k, static_scale, &a, ws + L.scratch, stream);
   if (st != FP4_OK) return st;
-  st = run_gemm(&a, w, y_bf16, n, ws + L.gemm, gemm_bytes, true, stream);
+  st = run_gemm(&a, w, y_bf16, n, stream);
   return st == FP4_OK ? ok() : st;
 }
 
@@ -364,8 +305,8 @@ fp4_status fp4_export_canonical(const fp4_tensor *tiled, fp4_tensor *canonical,
   fp4_status st;
   if ((st = check_tensor(tiled, "tiled")) != FP4_OK) return st;
   if ((st = check_tensor(canonical, "canonical")) != FP4_OK) return st;
-  if (tiled->layout != FP4_LAYOUT_WEIGHT_TILED || canonical->layout != FP4_LAYOUT_CANONICAL)
-    return fail(FP4_ERR_FORMAT_MISMATCH, "expected a WEIGHT_TILED source and CANONICAL target");
+  if (tiled->layout != FP4_LAYOUT_TILED || canonical->layout != FP4_LAYOUT_CANONICAL)
+    return fail(FP4_ERR_FORMAT_MISMATCH, "expected a TILED source and CANONICAL target");
   if (tiled->fmt != canonical->fmt || tiled->rows != canonical->rows ||
       tiled->cols != canonical->cols)
     return fail(FP4_ERR_FORMAT_MISMATCH, "descriptors differ in format or shape");
@@ -387,7 +328,7 @@ fp4_status fp4_dequantize(const fp4_tensor *t, float *out_f32, int64_t ldo, hipS
   if (ldo < t->cols) return fail(FP4_ERR_SHAPE, "ldo smaller than K");
   if (((uintptr_t)out_f32 & 3u) != 0) return fail(FP4_ERR_ALIGNMENT, "output must be 4-byte aligned");
   if ((st = check_device()) != FP4_OK) return st;
-  hipError_t e = launch_dequant(t->fmt, t->layout == FP4_LAYOUT_WEIGHT_TILED,
+  hipError_t e = launch_dequant(t->fmt, t->layout == FP4_LAYOUT_TILED,
                                 (const uint8_t *)t->codes, t->codes_pitch,
                                 (const uint8_t *)t->scales, t->scales_pitch,
                                 t->fmt == FP4_NVFP4 ? t->tensor_scale : nullptr, t->rows, t->cols,

@@ -38,6 +38,43 @@ __device__ __forceinline__ v4f mfma_nv(const h8v a[4], const h8v b[4], v4f c) {
   return c;
 }
 
+// One lane's part of the A fragment (16 rows from 16*g, K values 128*kt ..
+// 128*kt+127): 16 bytes of codes and its scale bytes, from the canonical
+// layout (row-major, 64 bytes of a row per fragment) or the tiled layout (the
+// fragment is 1 KB contiguous, in lane order). Rows at or past m read as zero.
+template <int FMT, int ATILED>
+__device__ __forceinline__ void load_a(const uint8_t *__restrict__ a_codes, int64_t a_cp,
+                                       const uint8_t *__restrict__ a_sc, int64_t a_sp, int kt_n,
+                                       int g, int kt, int lane, int m, uint4 &q, uint32_t &sc) {
+  const int row = 16 * g + (lane & 15);
+  if (row >= m) {
+    q = make_uint4(0u, 0u, 0u, 0u);
+    sc = 0u;
+    return;
+  }
+  if (ATILED) {
+    const int64_t f = (int64_t)g * kt_n + kt;
+    q = *(const uint4 *)(a_codes + f * kFragCodeBytes + lane * 16);
+    sc = FMT == 0 ? (uint32_t)*(const uint16_t *)(a_sc + f * 128 + lane * 2)
+                  : (uint32_t)a_sc[f * 64 + lane];
+  } else {
+    const int lc = lane >> 4;
+    q = *(const uint4 *)(a_codes + (int64_t)row * a_cp + kt * 64 + lc * 16);
+    sc = FMT == 0 ? (uint32_t)*(const uint16_t *)(a_sc + (int64_t)row * a_sp + kt * 8 + lc * 2)
+                  : (uint32_t)a_sc[(int64_t)row * a_sp + kt * 4 + lc];
+  }
+}
+
+// One lane's part of weight fragment (nt, kt) of the tiled weight cache.
+template <int FMT>
+__device__ __forceinline__ void load_w(const uint8_t *__restrict__ w_codes,
+                                       const uint8_t *__restrict__ w_sc, int64_t f, int lane,
+                                       uint4 &q, uint32_t &sc) {
+  q = *(const uint4 *)(w_codes + f * kFragCodeBytes + lane * 16);
+  sc = FMT == 0 ? (uint32_t)*(const uint16_t *)(w_sc + f * 128 + lane * 2)
+                : (uint32_t)w_sc[f * 64 + lane];
+}
+
 // ------------------------------------------------------------------ prefill
 //
 // Workgroup tile 128 x 128 (4 waves in a 2 x 2 grid, 64 x 64 per wave as
@@ -45,14 +82,14 @@ __device__ __forceinline__ v4f mfma_nv(const h8v a[4], const h8v b[4], v4f c) {
 // operand registers: an A fragment lane l reads 16 bytes of row (l % 16) at
 // K offset 32 (l / 16) of the canonical layout; a W fragment is one 1 KB
 // contiguous tile of the weight cache.
-template <int FMT>
+template <int FMT, int ATILED>
 __global__ __launch_bounds__(256) void k_gemm_prefill(
     const uint8_t *__restrict__ a_codes, int64_t a_cp, const uint8_t *__restrict__ a_sc,
     int64_t a_sp, const float *__restrict__ a_ts, const uint8_t *__restrict__ w_codes,
     const uint8_t *__restrict__ w_sc, const float *__restrict__ w_ts, int m, int n, int kt_n,
     int nt_n, uint16_t *__restrict__ c, int64_t ldc) {
-  constexpr int SFB = FMT == 0 ? 128 : 64;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int m0 = blockIdx.y * 128 + (wave >> 1) * 64;
   const int nt0 = (blockIdx.x * 128 + (wave & 1) * 64) >> 4;
   const int lr = lane & 15, lc = lane >> 4;
@@ -66,24 +103,13 @@ __global__ __launch_bounds__(256) void k_gemm_prefill(
     uint4 aq[4], wq[4];
     uint32_t as[4], ws[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int row = m0 + 16 * i + lr;
-      if (row < m) {
-        aq[i] = *(const uint4 *)(a_codes + (int64_t)row * a_cp + kt * 64 + lc * 16);
-        as[i] = FMT == 0 ? *(const uint16_t *)(a_sc + (int64_t)row * a_sp + kt * 8 + lc * 2)
-                         : a_sc[(int64_t)row * a_sp + kt * 4 + lc];
-      } else {
-        aq[i] = make_uint4(0u, 0u, 0u, 0u);
-        as[i] = 0u;
-      }
-    }
+    for (int i = 0; i < 4; ++i)
+      load_a<FMT, ATILED>(a_codes, a_cp, a_sc, a_sp, kt_n, (m0 >> 4) + i, kt, lane, m, aq[i], as[i]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      int nt = nt0 + j;
+      const int nt = nt0 + j;
       if (nt < nt_n) {
-        int64_t f = (int64_t)nt * kt_n + kt;
-        wq[j] = *(const uint4 *)(w_codes + f * kFragCodeBytes + lane * 16);
-        ws[j] = FMT == 0 ? *(const uint16_t *)(w_sc + f * SFB + lane * 2) : w_sc[f * SFB + lane];
+        load_w<FMT>(w_codes, w_sc, (int64_t)nt * kt_n + kt, lane, wq[j], ws[j]);
       } else {
         wq[j] = make_uint4(0u, 0u, 0u, 0u);
         ws[j] = 0u;
@@ -123,187 +149,132 @@ __global__ __launch_bounds__(256) void k_gemm_prefill(
 
 // ------------------------------------------------------------------- decode
 //
-// Skinny GEMM for M <= 32: the weight is streamed once at HBM rate. Workgroup
-// (nt, s) owns one 16-row weight tile and a K range of kt_per_wg fragments;
-// its 4 waves take interleaved fragments so the workgroup reads a contiguous
-// run of the weight cache. The weight tile is the MFMA's A operand (rows n)
-// and the activations its B operand (columns m, MG groups of 16), so the
-// accumulator holds C^T. Waves are summed in LDS in a fixed order; with
-// several K splits each workgroup stores its partial tile and the last one to
-// arrive (counted with an atomic) sums the partials in split order, so the
-// result does not depend on scheduling.
-template <int FMT, int MG>
-__global__ __launch_bounds__(256) void k_gemm_decode(
+// Skinny GEMM for M <= 32: the weight is streamed once at HBM rate. One
+// workgroup per 16-row weight tile covers the whole K range, so there is no
+// cross-workgroup reduction: every workgroup is resident at once and HBM
+// bandwidth is shared among them. The kDecWaves waves take interleaved
+// fragments (kt = wave + kDecWaves * j) and keep two groups of kDecFrags
+// fragments in flight (the next group's loads are issued before the current
+// group's arithmetic). The weight tile is the MFMA's A operand (rows n) and the
+// activations its B operand (columns m, MG groups of 16), so the accumulator
+// holds C^T. The waves' partial sums are added in LDS in a fixed order.
+constexpr int kDecWaves = 8;
+constexpr int kDecFrags = 2;
+
+template <int FMT, int MG, int ATILED>
+__global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(
     const uint8_t *__restrict__ a_codes, int64_t a_cp, const uint8_t *__restrict__ a_sc,
     int64_t a_sp, const float *__restrict__ a_ts, const uint8_t *__restrict__ w_codes,
     const uint8_t *__restrict__ w_sc, const float *__restrict__ w_ts, int m, int n, int kt_n,
-    uint16_t *__restrict__ c, int64_t ldc, int splits, int kt_per_wg,
-    float *__restrict__ partials, int *__restrict__ counters) {
-  constexpr int SFB = FMT == 0 ? 128 : 64;
-  constexpr int U = 2;
-  __shared__ float red[4][MG][4][64];
-  __shared__ int last_flag;
-  const int nt = blockIdx.x, s = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int lr = lane & 15, lc = lane >> 4;
-  const int kt_begin = s * kt_per_wg;
-  const int kt_end = min(kt_n, kt_begin + kt_per_wg);
+    uint16_t *__restrict__ c, int64_t ldc) {
+  constexpr int NW = kDecWaves, FM = kDecFrags;
+  __shared__ float red[NW][MG][4][64];
+  const int nt = blockIdx.x;
+  // readfirstlane makes the wave index (and every fragment guard derived from
+  // it) a scalar, so the guards compile to branches around the matrix
+  // instructions rather than to EXEC masks they would not honour.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   v4f acc[MG];
 #pragma unroll
   for (int g = 0; g < MG; ++g) acc[g] = v4f{0.f, 0.f, 0.f, 0.f};
+  uint4 wq[2][FM], aq[2][FM][MG];
+  uint32_t ws[2][FM], as[2][FM][MG];
 
-  for (int kt0 = kt_begin + wave; kt0 < kt_end; kt0 += 4 * U) {
-    uint4 wq[U], aq[U][MG];
-    uint32_t ws[U], as[U][MG];
+  auto load = [&](int buf, int base) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      int kt = kt0 + 4 * u;
-      bool ok = kt < kt_end;
-      int64_t f = (int64_t)nt * kt_n + kt;
-      wq[u] = ok ? *(const uint4 *)(w_codes + f * kFragCodeBytes + lane * 16)
-                 : make_uint4(0u, 0u, 0u, 0u);
-      ws[u] = ok ? (FMT == 0 ? (uint32_t)*(const uint16_t *)(w_sc + f * SFB + lane * 2)
-                             : (uint32_t)w_sc[f * SFB + lane])
-                 : 0u;
+    for (int u = 0; u < FM; ++u) {
+      const int kt = base + NW * u;
+      if (kt < kt_n) {
+        load_w<FMT>(w_codes, w_sc, (int64_t)nt * kt_n + kt, lane, wq[buf][u], ws[buf][u]);
 #pragma unroll
-      for (int g = 0; g < MG; ++g) {
-        int row = 16 * g + lr;
-        bool aok = ok && row < m;
-        aq[u][g] = aok ? *(const uint4 *)(a_codes + (int64_t)row * a_cp + kt * 64 + lc * 16)
-                       : make_uint4(0u, 0u, 0u, 0u);
-        as[u][g] = aok ? (FMT == 0
-                              ? (uint32_t)*(const uint16_t *)(a_sc + (int64_t)row * a_sp + kt * 8 +
-                                                              lc * 2)
-                              : (uint32_t)a_sc[(int64_t)row * a_sp + kt * 4 + lc])
-                       : 0u;
+        for (int g = 0; g < MG; ++g)
+          load_a<FMT, ATILED>(a_codes, a_cp, a_sc, a_sp, kt_n, g, kt, lane, m, aq[buf][u][g],
+                              as[buf][u][g]);
       }
     }
+  };
+  auto compute = [&](int buf, int base) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < FM; ++u) {
+      if (base + NW * u >= kt_n) break;  // wave-uniform
       if (FMT == 1) {
 #pragma unroll
-        for (int g = 0; g < MG; ++g) acc[g] = mfma_mx(wq[u], aq[u][g], acc[g], ws[u], as[u][g]);
+        for (int g = 0; g < MG; ++g)
+          acc[g] = mfma_mx(wq[buf][u], aq[buf][u][g], acc[g], ws[buf][u], as[buf][u][g]);
       } else {
         h8v wh[4];
-        nv_dequant32(wq[u], ws[u], wh);
+        nv_dequant32(wq[buf][u], ws[buf][u], wh);
 #pragma unroll
         for (int g = 0; g < MG; ++g) {
           h8v ah[4];
-          nv_dequant32(aq[u][g], as[u][g], ah);
+          nv_dequant32(aq[buf][u][g], as[buf][u][g], ah);
           acc[g] = mfma_nv(wh, ah, acc[g]);
         }
       }
     }
+  };
+  constexpr int STEP = NW * FM;
+  load(0, wave);
+  for (int base = wave; base < kt_n; base += 2 * STEP) {
+    load(1, base + STEP);
+    compute(0, base);
+    if (base + STEP >= kt_n) break;
+    load(0, base + 2 * STEP);
+    compute(1, base + STEP);
   }
-  // Sum the 4 waves in a fixed order.
 #pragma unroll
   for (int g = 0; g < MG; ++g)
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[wave][g][r][lane] = acc[g][r];
   __syncthreads();
-  // Threads 0..64*MG-1 each own one (g, lane) column of 4 values.
+  const int tg = threadIdx.x >> 6;  // accumulator group reduced by this wave
+  if (tg >= MG) return;
   const float alpha = FMT == 0 ? a_ts[0] * w_ts[0] : 1.0f;
-  const int tg = threadIdx.x >> 6;  // group handled by this thread (if < MG)
-  float tot[4] = {0.f, 0.f, 0.f, 0.f};
-  if (tg < MG) {
+  const int col = 16 * tg + (lane & 15);  // activation row m
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      tot[r] = ((red[0][tg][r][lane] + red[1][tg][r][lane]) + red[2][tg][r][lane]) +
-               red[3][tg][r][lane];
-  }
-  if (splits > 1) {
-    float *mine = partials + ((int64_t)nt * splits + s) * (MG * 256);
-    if (tg < MG) {
+  for (int r = 0; r < 4; ++r) {
+    float v = red[0][tg][r][lane];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mine[tg * 256 + r * 64 + lane] = tot[r];
-    }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) last_flag = (atomicAdd(&counters[nt], 1) == splits - 1);
-    __syncthreads();
-    if (!last_flag) return;
-    __threadfence();
-    if (tg < MG) {
-      const float *base = partials + (int64_t)nt * splits * (MG * 256);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = 0.f;
-        for (int ss = 0; ss < splits; ++ss)
-          v += __builtin_nontemporal_load(base + (int64_t)ss * (MG * 256) + tg * 256 + r * 64 + lane);
-        tot[r] = v;
-      }
-    }
-  }
-  if (tg < MG) {
-    int col = 16 * tg + lr;  // activation row m
-    if (col < m) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        int row = nt * 16 + 4 * lc + r;  // output column n
-        if (row < n) c[(int64_t)col * ldc + row] = f32_to_bf16_rne(tot[r] * alpha);
-      }
-    }
+    for (int w2 = 1; w2 < NW; ++w2) v += red[w2][tg][r][lane];
+    const int row = nt * 16 + 4 * (lane >> 4) + r;  // output column n
+    if (col < m && row < n) c[(int64_t)col * ldc + row] = f32_to_bf16_rne(v * alpha);
   }
 }
 
 }  // namespace
 
 hipError_t launch_gemm_prefill(const GemmArgs &g, hipStream_t stream) {
-  int kt_n = (int)(k_pad(g.k) / 128);
-  int nt_n = (int)(round_up(g.n, 16) / 16);
+  const int kt_n = (int)(k_pad(g.k) / kFragK);
+  const int nt_n = (int)(round_up(g.n, 16) / 16);
   dim3 grid((unsigned)((g.n + 127) / 128), (unsigned)((g.m + 127) / 128));
-  if (g.fmt == 0)
-    hipLaunchKernelGGL(k_gemm_prefill<0>, grid, dim3(256), 0, stream, g.a_codes, g.a_cpitch,
-                       g.a_scales, g.a_spitch, g.a_ts, g.w_codes, g.w_scales, g.w_ts, (int)g.m,
-                       (int)g.n, kt_n, nt_n, g.c, g.ldc);
-  else
-    hipLaunchKernelGGL(k_gemm_prefill<1>, grid, dim3(256), 0, stream, g.a_codes, g.a_cpitch,
-                       g.a_scales, g.a_spitch, g.a_ts, g.w_codes, g.w_scales, g.w_ts, (int)g.m,
-                       (int)g.n, kt_n, nt_n, g.c, g.ldc);
+#define FP4_PRE(F, T)                                                                          \
+  hipLaunchKernelGGL((k_gemm_prefill<F, T>), grid, dim3(256), 0, stream, g.a_codes,           \
+                     g.a_cpitch, g.a_scales, g.a_spitch, g.a_ts, g.w_codes, g.w_scales, g.w_ts, \
+                     (int)g.m, (int)g.n, kt_n, nt_n, g.c, g.ldc)
+  if (g.fmt == 0 && !g.a_tiled) FP4_PRE(0, 0);
+  else if (g.fmt == 0) FP4_PRE(0, 1);
+  else if (!g.a_tiled) FP4_PRE(1, 0);
+  else FP4_PRE(1, 1);
+#undef FP4_PRE
   return hipGetLastError();
 }
 
-DecodePlan decode_plan(int fmt, int64_t m, int64_t n, int64_t k) {
-  (void)fmt;
-  DecodePlan p;
-  p.mg = m <= 16 ? 1 : 2;
-  int64_t kt_n = k_pad(k) / 128, nt_n = round_up(n, 16) / 16;
-  // Aim for ~16 waves per CU over 256 CUs (4 waves per workgroup) while each
-  // wave streams at least 2 fragments.
-  int64_t target_wg = 1024;
-  int64_t splits = (target_wg + nt_n - 1) / nt_n;
-  int64_t max_splits = (kt_n + 7) / 8;   // >= 8 fragments per workgroup
-  if (splits > max_splits) splits = max_splits;
-  if (splits < 1) splits = 1;
-  int64_t kpw = (kt_n + splits - 1) / splits;
-  p.kt_per_wg = (int)kpw;
-  p.splits = (int)((kt_n + kpw - 1) / kpw);
-  p.frags = (int)((kpw + 3) / 4);
-  return p;
-}
-
-size_t decode_workspace_bytes(int fmt, int64_t m, int64_t n, int64_t k) {
-  DecodePlan p = decode_plan(fmt, m, n, k);
-  if (p.splits <= 1) return 0;
-  int64_t nt_n = round_up(n, 16) / 16;
-  size_t counters = (size_t)round_up(nt_n * 4, 256);
-  size_t parts = (size_t)nt_n * p.splits * p.mg * 256 * 4;
-  return counters + parts;
-}
-
-hipError_t launch_gemm_decode(const GemmArgs &g, const DecodePlan &p, float *partials,
-                              int *counters, hipStream_t stream) {
-  int kt_n = (int)(k_pad(g.k) / 128);
-  int nt_n = (int)(round_up(g.n, 16) / 16);
-  dim3 grid((unsigned)nt_n, (unsigned)p.splits);
-#define FP4_DEC(F, G)                                                                           \
-  hipLaunchKernelGGL((k_gemm_decode<F, G>), grid, dim3(256), 0, stream, g.a_codes, g.a_cpitch, \
-                     g.a_scales, g.a_spitch, g.a_ts, g.w_codes, g.w_scales, g.w_ts, (int)g.m,  \
-                     (int)g.n, kt_n, g.c, g.ldc, p.splits, p.kt_per_wg, partials, counters)
-  if (g.fmt == 0 && p.mg == 1) FP4_DEC(0, 1);
-  else if (g.fmt == 0) FP4_DEC(0, 2);
-  else if (p.mg == 1) FP4_DEC(1, 1);
-  else FP4_DEC(1, 2);
+hipError_t launch_gemm_decode(const GemmArgs &g, hipStream_t stream) {
+  const int kt_n = (int)(k_pad(g.k) / kFragK);
+  const int nt_n = (int)(round_up(g.n, 16) / 16);
+  const int mg = g.m <= 16 ? 1 : 2;
+  dim3 grid((unsigned)nt_n);
+#define FP4_DEC(F, G, T)                                                                        \
+  hipLaunchKernelGGL((k_gemm_decode<F, G, T>), grid, dim3(64 * kDecWaves), 0, stream,          \
+                     g.a_codes, g.a_cpitch, g.a_scales, g.a_spitch, g.a_ts, g.w_codes,         \
+                     g.w_scales, g.w_ts, (int)g.m, (int)g.n, kt_n, g.c, g.ldc)
+#define FP4_DEC_T(F, G) do { if (g.a_tiled) FP4_DEC(F, G, 1); else FP4_DEC(F, G, 0); } while (0)
+  if (g.fmt == 0 && mg == 1) FP4_DEC_T(0, 1);
+  else if (g.fmt == 0) FP4_DEC_T(0, 2);
+  else if (mg == 1) FP4_DEC_T(1, 1);
+  else FP4_DEC_T(1, 2);
+#undef FP4_DEC_T
 #undef FP4_DEC
   return hipGetLastError();
 }

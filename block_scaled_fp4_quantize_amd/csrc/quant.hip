@@ -3,12 +3,26 @@
 // NVFP4 (16-value blocks, E4M3 block scale, FP32 per-tensor scale) and MXFP4
 // (32-value blocks, E8M0 block scale), per "Hardware FP4 inference for speech
 // on Blackwell" (section "NVFP4, and the two ways it fails") and "FP4 n'existe
-// pas ..." (section "Deux dialectes, deux strategies de scaling"). The dynamic
-// per-tensor scale needs the tensor's largest magnitude before any block can be
-// encoded, so it is a two-launch reduction: partial maxima per workgroup, then
-// every quantize workgroup folds the (at most 1024) partials itself. No atomics
-// and no memory clearing are involved, so the result is deterministic and the
-// scratch needs no initialization.
+// pas ..." (section "Deux dialectes, deux strategies de scaling").
+//
+// One thread encodes one block. Output goes to the canonical row-major layout
+// or to the fragment-tiled layout (16 rows x 128 values per 1 KB fragment, the
+// operand order of the scaled matrix instruction), padding included.
+//
+// The dynamic NVFP4 per-tensor scale needs the tensor's largest magnitude
+// before any block can be encoded. Two ways are used:
+//   * small tensors (activations of skinny GEMMs): one launch of a fixed grid
+//     of kActGrid workgroups. Each workgroup keeps its blocks in registers,
+//     publishes its maximum with a device-scope atomic max, then arrives at a
+//     counter and waits (bounded spin) until all workgroups have arrived. Only
+//     one 32-bit value crosses workgroups, inside atomics, so no cache
+//     writeback is needed. The counter grows by kActGrid per call; a call's
+//     epoch (counter / kActGrid) selects one of two maximum words, and the
+//     first arrival clears the other one for the next call. Zero-filled words
+//     are the initial state.
+//   * large tensors: partial maxima per workgroup, then a second launch in
+//     which every workgroup folds the (at most 1024) partials itself.
+// Both are deterministic: a maximum does not depend on evaluation order.
 #include "fp4_device.h"
 #include "fp4_internal.h"
 
@@ -49,6 +63,74 @@ __device__ __forceinline__ uint32_t absmax_bits8(uint4 v) {
   return m;
 }
 
+template <int FMT>
+struct Blk {
+  static constexpr int B = FMT == 0 ? 16 : 32;  // values per block
+  static constexpr int V = B / 8;               // uint4 loads per block
+  static constexpr int BPF = 128 / B;           // blocks per fragment row
+  static constexpr int SFB = FMT == 0 ? 128 : 64;
+};
+
+// Where block b (of 16/32 values) of row r goes.
+template <int FMT, int TILED>
+__device__ __forceinline__ void block_dst(int64_t r, int64_t b, int64_t kt_n, uint8_t *codes,
+                                          int64_t cpitch, uint8_t *scales, int64_t spitch,
+                                          uint8_t *&cdst, uint8_t *&sdst) {
+  using K = Blk<FMT>;
+  if (!TILED) {
+    cdst = codes + r * cpitch + b * (K::B / 2);
+    sdst = scales + r * spitch + b;
+    return;
+  }
+  const int64_t frag = (r >> 4) * kt_n + b / K::BPF;
+  const int rr = (int)(r & 15), bi = (int)(b % K::BPF);
+  if (FMT == 0) {  // lane 16*(bi/2) + rr holds blocks bi (low 8 bytes) and bi^1
+    const int lane = 16 * (bi >> 1) + rr;
+    cdst = codes + frag * kFragCodeBytes + lane * 16 + (bi & 1) * 8;
+    sdst = scales + frag * K::SFB + lane * 2 + (bi & 1);
+  } else {
+    const int lane = 16 * bi + rr;
+    cdst = codes + frag * kFragCodeBytes + lane * 16;
+    sdst = scales + frag * K::SFB + lane;
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t block_absmax(const uint4 (&v)[Blk<FMT>::V]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < Blk<FMT>::V; ++i) m = max(m, absmax_bits8(v[i]));
+  return m;
+}
+
+// Encode one block (values in v) and store codes + scale byte.
+template <int FMT>
+__device__ __forceinline__ void encode_store(const uint4 (&v)[Blk<FMT>::V], float st,
+                                             uint8_t *cdst, uint8_t *sdst) {
+  const uint32_t abits = block_absmax<FMT>(v);
+  if (FMT == 0) {
+    const double q = (double)bf16_bits_to_f32(abits) / (6.0 * (double)st);
+    const uint32_t sbyte = e4m3_rne_sat(q);
+    const NvBlockEnc enc = nv_block_encoder(sbyte, st);
+    *(uint2 *)cdst = make_uint2(nv_encode8(enc, v[0]), nv_encode8(enc, v[1]));
+    *sdst = (uint8_t)sbyte;
+  } else {
+    const int e = mx_exponent_from_bits(abits);
+    *(uint4 *)cdst = make_uint4(mx_encode8(e, v[0]), mx_encode8(e, v[1]), mx_encode8(e, v[2]),
+                                mx_encode8(e, v[3]));
+    *sdst = (uint8_t)(e + 127);
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void zero_store(uint8_t *cdst, uint8_t *sdst) {
+  if (FMT == 0) *(uint2 *)cdst = make_uint2(0u, 0u);
+  else *(uint4 *)cdst = make_uint4(0u, 0u, 0u, 0u);
+  *sdst = 0;
+}
+
+// ------------------------------------------------------------------ large
+
 __global__ __launch_bounds__(kThreads) void k_amax_parts(const uint4 *__restrict__ x, int64_t n8,
                                                          uint32_t *__restrict__ parts) {
   __shared__ uint32_t lds[4];
@@ -60,137 +142,125 @@ __global__ __launch_bounds__(kThreads) void k_amax_parts(const uint4 *__restrict
   if (threadIdx.x == 0) parts[blockIdx.x] = m;
 }
 
-// Per-tensor scale for this launch: static value or the fold of the partials.
-__device__ __forceinline__ float resolve_tensor_scale(const uint32_t *parts, int nparts,
-                                                      const float *static_scale, uint32_t *lds4) {
-  if (static_scale) return *static_scale;
-  uint32_t m = 0;
-  for (int i = threadIdx.x; i < nparts; i += blockDim.x) m = max(m, parts[i]);
-  m = block_max_u32(m, lds4);
-  return tensor_scale_from_amax(bf16_bits_to_f32(m));
-}
-
-// One thread per 16-value block (NVFP4) of the padded row, canonical layout.
-__global__ __launch_bounds__(kThreads) void k_quant_nv_canon(
-    const uint16_t *__restrict__ x, int64_t rows, int64_t k, int64_t nb_pad,
+// Grid-stride over every block of the padded output; S_t (NVFP4) from the
+// static value or the fold of the partial maxima.
+template <int FMT, int TILED>
+__global__ __launch_bounds__(kThreads) void k_quant(
+    const uint16_t *__restrict__ x, int64_t rows, int64_t k, int64_t rows_pad, int64_t kt_n,
     const uint32_t *__restrict__ parts, int nparts, const float *__restrict__ static_scale,
     uint8_t *__restrict__ codes, int64_t cpitch, uint8_t *__restrict__ scales, int64_t spitch,
-    float *__restrict__ ts_out, int *__restrict__ zero_ptr, int zero_n) {
-  __shared__ uint32_t lds[4];
-  float st = resolve_tensor_scale(parts, nparts, static_scale, lds);
-  if (blockIdx.x == 0) {
-    if (threadIdx.x == 0 && ts_out) *ts_out = st;
-    for (int i = threadIdx.x; i < zero_n; i += blockDim.x) zero_ptr[i] = 0;
-  }
-  const int64_t nb = k / 16, total = rows * nb_pad;
-  int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
-    int64_t r = t / nb_pad, b = t - r * nb_pad;
-    uint8_t *crow = codes + r * cpitch;
-    if (b >= nb) {  // zero padding up to K_pad
-      *(uint2 *)(crow + b * 8) = make_uint2(0u, 0u);
-      scales[r * spitch + b] = 0;
-      continue;
-    }
-    const uint4 *src = (const uint4 *)(x + r * k + b * 16);
-    uint4 v0 = src[0], v1 = src[1];
-    uint32_t abits = max(absmax_bits8(v0), absmax_bits8(v1));
-    double q = (double)bf16_bits_to_f32(abits) / (6.0 * (double)st);
-    uint32_t sbyte = e4m3_rne_sat(q);
-    NvBlockEnc enc = nv_block_encoder(sbyte, st);
-    uint2 out = make_uint2(nv_encode8(enc, v0), nv_encode8(enc, v1));
-    *(uint2 *)(crow + b * 8) = out;
-    scales[r * spitch + b] = (uint8_t)sbyte;
-  }
-}
-
-// One thread per 32-value block (MXFP4) of the padded row, canonical layout.
-__global__ __launch_bounds__(kThreads) void k_quant_mx_canon(
-    const uint16_t *__restrict__ x, int64_t rows, int64_t k, int64_t nb_pad,
-    uint8_t *__restrict__ codes, int64_t cpitch, uint8_t *__restrict__ scales, int64_t spitch,
-    int *__restrict__ zero_ptr, int zero_n) {
-  if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i < zero_n; i += blockDim.x) zero_ptr[i] = 0;
-  const int64_t nb = k / 32, total = rows * nb_pad;
-  int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
-    int64_t r = t / nb_pad, b = t - r * nb_pad;
-    uint8_t *crow = codes + r * cpitch;
-    if (b >= nb) {
-      *(uint4 *)(crow + b * 16) = make_uint4(0u, 0u, 0u, 0u);
-      scales[r * spitch + b] = 0;
-      continue;
-    }
-    const uint4 *src = (const uint4 *)(x + r * k + b * 32);
-    uint4 v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
-    uint32_t abits = max(max(absmax_bits8(v0), absmax_bits8(v1)),
-                         max(absmax_bits8(v2), absmax_bits8(v3)));
-    int e = mx_exponent_from_bits(abits);
-    uint4 out = make_uint4(mx_encode8(e, v0), mx_encode8(e, v1), mx_encode8(e, v2),
-                           mx_encode8(e, v3));
-    *(uint4 *)(crow + b * 16) = out;
-    scales[r * spitch + b] = (uint8_t)(e + 127);
-  }
-}
-
-// Weight quantization into the fragment-tiled layout. One thread per block of
-// the padded [N_pad, K_pad] matrix; padding blocks get zero codes and scales.
-template <int FMT>
-__global__ __launch_bounds__(kThreads) void k_quant_tiled(
-    const uint16_t *__restrict__ w, int64_t n, int64_t k, int64_t n_pad, int64_t kt_n,
-    const uint32_t *__restrict__ parts, int nparts, uint8_t *__restrict__ codes,
-    uint8_t *__restrict__ scales, float *__restrict__ ts_out) {
-  constexpr int B = FMT == 0 ? 16 : 32;
-  constexpr int BPF = 128 / B;                   // blocks per fragment row
-  constexpr int SFB = FMT == 0 ? 128 : 64;       // scale bytes per fragment
+    float *__restrict__ ts_out) {
+  using K = Blk<FMT>;
   __shared__ uint32_t lds[4];
   float st = 1.0f;
   if (FMT == 0) {
-    st = resolve_tensor_scale(parts, nparts, nullptr, lds);
-    if (blockIdx.x == 0 && threadIdx.x == 0) *ts_out = st;
-  }
-  const int64_t nb = k / B, nb_pad = kt_n * BPF, total = n_pad * nb_pad;
-  int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
-    int64_t row = t / nb_pad, b = t - row * nb_pad;
-    int64_t frag = (row >> 4) * kt_n + b / BPF;
-    int r = (int)(row & 15), bi = (int)(b % BPF);
-    uint8_t *cdst, *sdst;
-    if (FMT == 0) {  // lane 16*(bi/2) + r holds blocks bi (low 8 bytes) and bi^1
-      int lane = 16 * (bi >> 1) + r;
-      cdst = codes + frag * kFragCodeBytes + lane * 16 + (bi & 1) * 8;
-      sdst = scales + frag * SFB + lane * 2 + (bi & 1);
+    if (static_scale) {
+      st = *static_scale;
     } else {
-      int lane = 16 * bi + r;
-      cdst = codes + frag * kFragCodeBytes + lane * 16;
-      sdst = scales + frag * SFB + lane;
+      uint32_t m = 0;
+      for (int i = threadIdx.x; i < nparts; i += blockDim.x) m = max(m, parts[i]);
+      st = tensor_scale_from_amax(bf16_bits_to_f32(block_max_u32(m, lds)));
     }
-    if (row >= n || b >= nb) {
-      if (FMT == 0) *(uint2 *)cdst = make_uint2(0u, 0u);
-      else *(uint4 *)cdst = make_uint4(0u, 0u, 0u, 0u);
-      *sdst = 0;
+    if (blockIdx.x == 0 && threadIdx.x == 0 && ts_out) *ts_out = st;
+  }
+  const int64_t nb = k / K::B, nb_pad = kt_n * K::BPF, total = rows_pad * nb_pad;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
+    const int64_t r = t / nb_pad, b = t - r * nb_pad;
+    uint8_t *cdst, *sdst;
+    block_dst<FMT, TILED>(r, b, kt_n, codes, cpitch, scales, spitch, cdst, sdst);
+    if (r >= rows || b >= nb) {
+      zero_store<FMT>(cdst, sdst);
       continue;
     }
-    const uint4 *src = (const uint4 *)(w + row * k + b * B);
-    if (FMT == 0) {
-      uint4 v0 = src[0], v1 = src[1];
-      uint32_t abits = max(absmax_bits8(v0), absmax_bits8(v1));
-      double q = (double)bf16_bits_to_f32(abits) / (6.0 * (double)st);
-      uint32_t sbyte = e4m3_rne_sat(q);
-      NvBlockEnc enc = nv_block_encoder(sbyte, st);
-      *(uint2 *)cdst = make_uint2(nv_encode8(enc, v0), nv_encode8(enc, v1));
-      *sdst = (uint8_t)sbyte;
-    } else {
-      uint4 v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
-      uint32_t abits = max(max(absmax_bits8(v0), absmax_bits8(v1)),
-                           max(absmax_bits8(v2), absmax_bits8(v3)));
-      int e = mx_exponent_from_bits(abits);
-      *(uint4 *)cdst = make_uint4(mx_encode8(e, v0), mx_encode8(e, v1), mx_encode8(e, v2),
-                                  mx_encode8(e, v3));
-      *sdst = (uint8_t)(e + 127);
-    }
+    uint4 v[K::V];
+    const uint4 *src = (const uint4 *)(x + r * k + b * K::B);
+#pragma unroll
+    for (int i = 0; i < K::V; ++i) v[i] = src[i];
+    encode_store<FMT>(v, st, cdst, sdst);
   }
 }
+
+// ------------------------------------------------------------------ small
+
+// Maximum over every workgroup of the grid (see the file comment). `sync`
+// holds {arrival counter, max word 0, max word 1}, zero-filled initially.
+__device__ __forceinline__ uint32_t grid_max_u32(uint32_t wg_max, uint32_t *sync,
+                                                 uint32_t *result_lds) {
+  if (threadIdx.x == 0) {
+    const uint32_t g = gridDim.x;
+    const uint32_t epoch =
+        __hip_atomic_load(&sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) / g;
+    uint32_t *slot = &sync[1 + (epoch & 1u)];
+    const uint32_t old = atomicMax(slot, wg_max);
+    // the arrival depends on the returned value, so it is issued only after
+    // the maximum has been performed
+    const uint32_t ticket = atomicAdd(&sync[0], old == 0xFFFFFFFFu ? 2u : 1u);
+    if (ticket == epoch * g)  // first arrival clears the next call's word
+      __hip_atomic_store(&sync[1 + ((epoch + 1u) & 1u)], 0u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t target = (epoch + 1u) * g;
+    for (uint32_t it = 0; it < (1u << 22); ++it) {
+      const uint32_t now = __hip_atomic_load(&sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((int32_t)(now - target) >= 0) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    *result_lds = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  return *result_lds;
+}
+
+// Single-launch quantization of a tensor of at most kActGrid * 256 * kActBpt
+// blocks. Every thread loads its blocks first, so the values are in registers
+// while the maximum is exchanged.
+template <int FMT, int TILED, int DYN>
+__global__ __launch_bounds__(kThreads) void k_quant_small(
+    const uint16_t *__restrict__ x, int64_t rows, int64_t k, int64_t rows_pad, int64_t kt_n,
+    const float *__restrict__ static_scale, uint8_t *__restrict__ codes, int64_t cpitch,
+    uint8_t *__restrict__ scales, int64_t spitch, float *__restrict__ ts_out,
+    uint32_t *__restrict__ sync) {
+  using K = Blk<FMT>;
+  __shared__ uint32_t lds[4];
+  __shared__ uint32_t gmax;
+  const int64_t nb = k / K::B, nb_pad = kt_n * K::BPF, total = rows_pad * nb_pad;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint4 v[kActBpt][K::V];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < kActBpt; ++i) {
+    const int64_t t = t0 + i * stride;
+    const int64_t r = t / nb_pad, b = t - r * nb_pad;
+    if (t < total && r < rows && b < nb) {
+      const uint4 *src = (const uint4 *)(x + r * k + b * K::B);
+#pragma unroll
+      for (int j = 0; j < K::V; ++j) v[i][j] = src[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < K::V; ++j) v[i][j] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    m = max(m, block_absmax<FMT>(v[i]));
+  }
+  float st = 1.0f;
+  if (FMT == 0) {
+    if (DYN) st = tensor_scale_from_amax(bf16_bits_to_f32(grid_max_u32(block_max_u32(m, lds), sync, &gmax)));
+    else st = *static_scale;
+    if (blockIdx.x == 0 && threadIdx.x == 0 && ts_out) *ts_out = st;
+  }
+#pragma unroll
+  for (int i = 0; i < kActBpt; ++i) {
+    const int64_t t = t0 + i * stride;
+    if (t >= total) break;
+    const int64_t r = t / nb_pad, b = t - r * nb_pad;
+    uint8_t *cdst, *sdst;
+    block_dst<FMT, TILED>(r, b, kt_n, codes, cpitch, scales, spitch, cdst, sdst);
+    if (r >= rows || b >= nb) zero_store<FMT>(cdst, sdst);
+    else encode_store<FMT>(v[i], st, cdst, sdst);
+  }
+}
+
+// --------------------------------------------------------------- test aids
 
 // Tiled -> canonical copy (one thread per block of the padded canonical row).
 template <int FMT>
@@ -198,27 +268,18 @@ __global__ __launch_bounds__(kThreads) void k_export(
     const uint8_t *__restrict__ tc, const uint8_t *__restrict__ ts, int64_t rows, int64_t kt_n,
     uint8_t *__restrict__ codes, int64_t cpitch, uint8_t *__restrict__ scales, int64_t spitch,
     const float *__restrict__ tsc_in, float *__restrict__ tsc_out) {
-  constexpr int B = FMT == 0 ? 16 : 32;
-  constexpr int BPF = 128 / B;
-  constexpr int SFB = FMT == 0 ? 128 : 64;
+  using K = Blk<FMT>;
   if (blockIdx.x == 0 && threadIdx.x == 0 && tsc_in && tsc_out) *tsc_out = *tsc_in;
-  const int64_t nb_pad = kt_n * BPF, total = rows * nb_pad;
-  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t nb_pad = kt_n * K::BPF, total = rows * nb_pad;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
-    int64_t row = t / nb_pad, b = t - row * nb_pad;
-    int64_t frag = (row >> 4) * kt_n + b / BPF;
-    int r = (int)(row & 15), bi = (int)(b % BPF);
-    if (FMT == 0) {
-      int lane = 16 * (bi >> 1) + r;
-      *(uint2 *)(codes + row * cpitch + b * 8) =
-          *(const uint2 *)(tc + frag * kFragCodeBytes + lane * 16 + (bi & 1) * 8);
-      scales[row * spitch + b] = ts[frag * SFB + lane * 2 + (bi & 1)];
-    } else {
-      int lane = 16 * bi + r;
-      *(uint4 *)(codes + row * cpitch + b * 16) =
-          *(const uint4 *)(tc + frag * kFragCodeBytes + lane * 16);
-      scales[row * spitch + b] = ts[frag * SFB + lane];
-    }
+    const int64_t r = t / nb_pad, b = t - r * nb_pad;
+    uint8_t *tcd, *tsd, *ccd, *csd;
+    block_dst<FMT, 1>(r, b, kt_n, (uint8_t *)tc, 0, (uint8_t *)ts, 0, tcd, tsd);
+    block_dst<FMT, 0>(r, b, kt_n, codes, cpitch, scales, spitch, ccd, csd);
+    if (FMT == 0) *(uint2 *)ccd = *(const uint2 *)tcd;
+    else *(uint4 *)ccd = *(const uint4 *)tcd;
+    *csd = *tsd;
   }
 }
 
@@ -228,37 +289,23 @@ __global__ __launch_bounds__(kThreads) void k_dequant(
     const uint8_t *__restrict__ codes, int64_t cpitch, const uint8_t *__restrict__ scales,
     int64_t spitch, const float *__restrict__ tsc, int64_t rows, int64_t k, int64_t kt_n,
     float *__restrict__ out, int64_t ldo) {
-  constexpr int B = FMT == 0 ? 16 : 32;
-  constexpr int SFB = FMT == 0 ? 128 : 64;
+  using K = Blk<FMT>;
   const double st = (FMT == 0 && tsc) ? (double)*tsc : 1.0;
   const int64_t total = rows * k;
-  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
-    int64_t row = t / k, kk = t - row * k;
-    uint32_t byte, sbyte;
-    if (!TILED) {
-      byte = codes[row * cpitch + kk / 2];
-      sbyte = scales[row * spitch + kk / B];
-    } else {
-      int64_t frag = (row >> 4) * kt_n + kk / 128;
-      int r = (int)(row & 15), kin = (int)(kk % 128);
-      int lane = 16 * (kin / 32) + r;
-      byte = codes[frag * kFragCodeBytes + lane * 16 + (kin % 32) / 2];
-      sbyte = FMT == 0 ? scales[frag * SFB + lane * 2 + (kin % 32) / 16]
-                       : scales[frag * SFB + lane];
-    }
-    uint32_t code = (kk & 1) ? (byte >> 4) : (byte & 15u);
-    uint32_t ee = (code >> 1) & 3u, mm = code & 1u;
-    float qmag = ee == 0 ? 0.5f * (float)mm : ldexpf(1.0f + 0.5f * (float)mm, (int)ee - 1);
-    double s = FMT == 0 ? (double)e4m3_to_f32(sbyte) : ldexp(1.0, (int)sbyte - 127);
-    double v = (double)qmag * s * st;
-    out[row * ldo + kk] = (code & 8u) ? -(float)v : (float)v;
+    const int64_t r = t / k, kk = t - r * k;
+    uint8_t *cd, *sd;
+    block_dst<FMT, TILED>(r, kk / K::B, kt_n, (uint8_t *)codes, cpitch, (uint8_t *)scales,
+                          spitch, cd, sd);
+    const uint32_t byte = cd[(kk % K::B) / 2];
+    const uint32_t code = (kk & 1) ? (byte >> 4) : (byte & 15u);
+    const uint32_t ee = (code >> 1) & 3u, mm = code & 1u;
+    const float qmag = ee == 0 ? 0.5f * (float)mm : ldexpf(1.0f + 0.5f * (float)mm, (int)ee - 1);
+    const double s = FMT == 0 ? (double)e4m3_to_f32(*sd) : ldexp(1.0, (int)*sd - 127);
+    const double val = (double)qmag * s * st;
+    out[r * ldo + kk] = (code & 8u) ? -(float)val : (float)val;
   }
-}
-
-__global__ void k_zero_ints(int *p, int n) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0;
 }
 
 int grid_for(int64_t work, int cap) {
@@ -268,52 +315,82 @@ int grid_for(int64_t work, int cap) {
   return (int)g;
 }
 
+template <int FMT, int TILED>
+void launch_small(const uint16_t *x, int64_t rows, int64_t k, int64_t rows_pad, int64_t kt_n,
+                  const float *static_scale, uint8_t *codes, int64_t cpitch, uint8_t *scales,
+                  int64_t spitch, float *ts_out, uint32_t *sync, hipStream_t stream) {
+  if (FMT == 0 && !static_scale) {
+    hipLaunchKernelGGL((k_quant_small<FMT, TILED, 1>), dim3(kActGrid), dim3(kThreads), 0, stream,
+                       x, rows, k, rows_pad, kt_n, static_scale, codes, cpitch, scales, spitch,
+                       ts_out, sync);
+  } else {
+    const int64_t total = rows_pad * kt_n * Blk<FMT>::BPF;
+    const int grid = (int)((total + kThreads * kActBpt - 1) / (kThreads * kActBpt));
+    hipLaunchKernelGGL((k_quant_small<FMT, TILED, 0>), dim3(grid), dim3(kThreads), 0, stream, x,
+                       rows, k, rows_pad, kt_n, static_scale, codes, cpitch, scales, spitch,
+                       ts_out, sync);
+  }
+}
+
+template <int FMT, int TILED>
+void launch_large(const uint16_t *x, int64_t rows, int64_t k, int64_t rows_pad, int64_t kt_n,
+                  const uint32_t *parts, int nparts, const float *static_scale, uint8_t *codes,
+                  int64_t cpitch, uint8_t *scales, int64_t spitch, float *ts_out,
+                  hipStream_t stream) {
+  const int grid = grid_for(rows_pad * kt_n * Blk<FMT>::BPF, 8192);
+  hipLaunchKernelGGL((k_quant<FMT, TILED>), dim3(grid), dim3(kThreads), 0, stream, x, rows, k,
+                     rows_pad, kt_n, parts, nparts, static_scale, codes, cpitch, scales, spitch,
+                     ts_out);
+}
+
 }  // namespace
 
 int amax_parts(int64_t n) {
-  int64_t per = (int64_t)kThreads * 8 * 4;   // >= 4 uint4 loads per thread
+  int64_t per = (int64_t)kThreads * 8 * 4;  // >= 4 uint4 loads per thread
   int64_t p = (n + per - 1) / per;
   if (p < 1) p = 1;
   if (p > kMaxAmaxParts) p = kMaxAmaxParts;
   return (int)p;
 }
 
-hipError_t launch_amax_parts(const uint16_t *x, int64_t n, uint32_t *parts, int nparts,
-                             hipStream_t stream) {
-  hipLaunchKernelGGL(k_amax_parts, dim3(nparts), dim3(kThreads), 0, stream,
-                     (const uint4 *)x, n / 8, parts);
-  return hipGetLastError();
+bool quant_fits_small(int fmt, int64_t rows, int64_t k, int tiled) {
+  const int64_t rows_pad = tiled ? round_up(rows, 16) : rows;
+  const int64_t blocks = rows_pad * (k_pad(k) / block_of(fmt));
+  return blocks <= (int64_t)kActGrid * kThreads * kActBpt;
 }
 
-hipError_t launch_quant_canonical(int fmt, const uint16_t *x, int64_t rows, int64_t k,
-                                  const uint32_t *parts, int nparts, const float *static_scale,
-                                  uint8_t *codes, int64_t cpitch, uint8_t *scales,
-                                  int64_t spitch, float *ts_out, int *zero_ptr, int zero_n,
-                                  hipStream_t stream) {
-  int64_t nb_pad = k_pad(k) / block_of(fmt);
-  int grid = grid_for(rows * nb_pad, 4096);
-  if (fmt == 0)
-    hipLaunchKernelGGL(k_quant_nv_canon, dim3(grid), dim3(kThreads), 0, stream, x, rows, k,
-                       nb_pad, parts, nparts, static_scale, codes, cpitch, scales, spitch, ts_out,
-                       zero_ptr, zero_n);
-  else
-    hipLaunchKernelGGL(k_quant_mx_canon, dim3(grid), dim3(kThreads), 0, stream, x, rows, k,
-                       nb_pad, codes, cpitch, scales, spitch, zero_ptr, zero_n);
-  return hipGetLastError();
-}
-
-hipError_t launch_quant_tiled(int fmt, const uint16_t *w, int64_t n, int64_t k,
-                              const uint32_t *parts, int nparts, uint8_t *codes, uint8_t *scales,
-                              float *ts_out, hipStream_t stream) {
-  int64_t n_pad = round_up(n, 16), kt_n = k_pad(k) / 128;
-  int64_t work = n_pad * kt_n * (128 / block_of(fmt));
-  int grid = grid_for(work, 8192);
-  if (fmt == 0)
-    hipLaunchKernelGGL(k_quant_tiled<0>, dim3(grid), dim3(kThreads), 0, stream, w, n, k, n_pad,
-                       kt_n, parts, nparts, codes, scales, ts_out);
-  else
-    hipLaunchKernelGGL(k_quant_tiled<1>, dim3(grid), dim3(kThreads), 0, stream, w, n, k, n_pad,
-                       kt_n, parts, nparts, codes, scales, ts_out);
+hipError_t launch_quantize(int fmt, int tiled, const uint16_t *x, int64_t rows, int64_t k,
+                           const float *static_scale, uint8_t *codes, int64_t cpitch,
+                           uint8_t *scales, int64_t spitch, float *ts_out, uint32_t *scratch,
+                           hipStream_t stream) {
+  const int64_t rows_pad = tiled ? round_up(rows, 16) : rows;
+  const int64_t kt_n = k_pad(k) / kFragK;
+  if (quant_fits_small(fmt, rows, k, tiled)) {
+    uint32_t *sync = scratch + kMaxAmaxParts;
+#define FP4_QS(F, T) launch_small<F, T>(x, rows, k, rows_pad, kt_n, static_scale, codes, cpitch, \
+                                        scales, spitch, ts_out, sync, stream)
+    if (fmt == 0 && !tiled) FP4_QS(0, 0);
+    else if (fmt == 0) FP4_QS(0, 1);
+    else if (!tiled) FP4_QS(1, 0);
+    else FP4_QS(1, 1);
+#undef FP4_QS
+    return hipGetLastError();
+  }
+  int nparts = 0;
+  if (fmt == 0 && !static_scale) {
+    nparts = amax_parts(rows * k);
+    hipLaunchKernelGGL(k_amax_parts, dim3(nparts), dim3(kThreads), 0, stream, (const uint4 *)x,
+                       rows * k / 8, scratch);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+#define FP4_QL(F, T) launch_large<F, T>(x, rows, k, rows_pad, kt_n, scratch, nparts, static_scale, \
+                                        codes, cpitch, scales, spitch, ts_out, stream)
+  if (fmt == 0 && !tiled) FP4_QL(0, 0);
+  else if (fmt == 0) FP4_QL(0, 1);
+  else if (!tiled) FP4_QL(1, 0);
+  else FP4_QL(1, 1);
+#undef FP4_QL
   return hipGetLastError();
 }
 
@@ -321,8 +398,8 @@ hipError_t launch_export_canonical(int fmt, const uint8_t *tcodes, const uint8_t
                                    int64_t rows, int64_t k, uint8_t *codes, int64_t cpitch,
                                    uint8_t *scales, int64_t spitch, const float *ts_in,
                                    float *ts_out, hipStream_t stream) {
-  int64_t kt_n = k_pad(k) / 128;
-  int grid = grid_for(rows * kt_n * (128 / block_of(fmt)), 8192);
+  const int64_t kt_n = k_pad(k) / kFragK;
+  const int grid = grid_for(rows * kt_n * (128 / block_of(fmt)), 8192);
   if (fmt == 0)
     hipLaunchKernelGGL(k_export<0>, dim3(grid), dim3(kThreads), 0, stream, tcodes, tscales, rows,
                        kt_n, codes, cpitch, scales, spitch, ts_in, ts_out);
@@ -335,8 +412,8 @@ hipError_t launch_export_canonical(int fmt, const uint8_t *tcodes, const uint8_t
 hipError_t launch_dequant(int fmt, int tiled, const uint8_t *codes, int64_t cpitch,
                           const uint8_t *scales, int64_t spitch, const float *ts, int64_t rows,
                           int64_t k, float *out, int64_t ldo, hipStream_t stream) {
-  int64_t kt_n = k_pad(k) / 128;
-  int grid = grid_for(rows * k, 8192);
+  const int64_t kt_n = k_pad(k) / kFragK;
+  const int grid = grid_for(rows * k, 8192);
 #define FP4_DQ(F, T)                                                                       \
   hipLaunchKernelGGL((k_dequant<F, T>), dim3(grid), dim3(kThreads), 0, stream, codes, cpitch, \
                      scales, spitch, ts, rows, k, kt_n, out, ldo)
@@ -345,12 +422,6 @@ hipError_t launch_dequant(int fmt, int tiled, const uint8_t *codes, int64_t cpit
   else if (!tiled) FP4_DQ(1, 0);
   else FP4_DQ(1, 1);
 #undef FP4_DQ
-  return hipGetLastError();
-}
-
-hipError_t launch_zero_ints(int *p, int n, hipStream_t stream) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_zero_ints, dim3((n + 255) / 256), dim3(256), 0, stream, p, n);
   return hipGetLastError();
 }
 

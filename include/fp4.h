@@ -66,8 +66,9 @@ typedef enum {
  *   scales row-major [rows][scales_pitch] bytes (pitch >= K_pad/B); bytes
  *   past K within a row are zero. This is the activation layout and the
  *   layout used to compare with a reference byte for byte.
- * WEIGHT_TILED: the weight cache layout. Rows are padded to N_pad =
- *   round_up(N, 16) and K to K_pad = round_up(K, 128); the matrix is cut into
+ * TILED: the weight cache layout, also accepted for activations (the linear
+ *   path uses it internally). Rows are padded to round_up(rows, 16) and K to
+ *   K_pad = round_up(K, 128); the matrix is cut into
  *   fragments of 16 rows x 128 values, stored fragment-major
  *   ((row / 16) * (K_pad / 128) + k / 128). A fragment's codes are 1024 bytes:
  *   16 bytes per lane l = 16 * c + r holding row r, values 32c .. 32c+31 of
@@ -76,7 +77,7 @@ typedef enum {
  *   Padding codes and scales are zero.
  * K_pad = round_up(K, 128) in both layouts.
  */
-typedef enum { FP4_LAYOUT_CANONICAL = 0, FP4_LAYOUT_WEIGHT_TILED = 1 } fp4_layout;
+typedef enum { FP4_LAYOUT_CANONICAL = 0, FP4_LAYOUT_TILED = 1 } fp4_layout;
 
 typedef struct {
     int32_t fmt;            /* fp4_format */
@@ -103,12 +104,14 @@ size_t fp4_scales_bytes(int32_t fmt, int32_t layout, int64_t rows, int64_t k);
 fp4_status fp4_tensor_init(fp4_tensor *t, int32_t fmt, int32_t layout, int64_t rows,
                            int64_t k, void *codes, void *scales, float *tensor_scale);
 
-/* Workspace for fp4_quantize_act / fp4_quantize_weight: room for the partial
- * maxima of the per-tensor scale reduction (NVFP4 dynamic). */
+/* Workspace for fp4_quantize_act / fp4_quantize_weight (NVFP4: the per-tensor
+ * maximum reduction; MXFP4: 0). It must be zero-filled before its first use;
+ * every call leaves it reusable. Calls sharing a workspace must not overlap
+ * in time. */
 size_t fp4_quantize_workspace_bytes(int32_t fmt, int64_t rows, int64_t k);
 
 /*
- * Quantize a weight W bf16 [n, k] once, into `out` (WEIGHT_TILED, filled by
+ * Quantize a weight W bf16 [n, k] once, into `out` (TILED, filled by
  * fp4_tensor_init with rows = n, cols = k). NVFP4 uses the dynamic per-tensor
  * scale, written to *out->tensor_scale. k must be a multiple of the block.
  */
@@ -117,7 +120,7 @@ fp4_status fp4_quantize_weight(int32_t fmt, const void *w_bf16, int64_t n, int64
                                hipStream_t stream);
 
 /*
- * Quantize activations A bf16 [m, k] into `out` (CANONICAL). NVFP4:
+ * Quantize activations A bf16 [m, k] into `out` (CANONICAL or TILED). NVFP4:
  * static_scale == NULL selects the dynamic per-tensor scale; otherwise
  * *static_scale (device FP32, > 0, finite) is used as S_t and block scales
  * saturate at 448. MXFP4 requires static_scale == NULL.
@@ -126,20 +129,23 @@ fp4_status fp4_quantize_act(int32_t fmt, const void *a_bf16, int64_t m, int64_t 
                             const float *static_scale, fp4_tensor *out, void *workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace for fp4_gemm (split-K partial sums and their counters). */
+/* Workspace for fp4_gemm. The current kernels need none (returns 0); the
+ * arguments are kept so that a future kernel can use one without an ABI
+ * change. */
 size_t fp4_gemm_workspace_bytes(int32_t fmt, int64_t m, int64_t n, int64_t k);
 
 /*
  * C[m, n] (bf16, row stride ldc elements) = bf16_RNE(alpha * sum_k a^'[m,k] w^'[n,k]),
  * with a^' = q * s_b (per-tensor factors pulled into alpha = S_tA * S_tW for
- * NVFP4, alpha = 1 for MXFP4). `a` is CANONICAL, `w` is WEIGHT_TILED, same
- * format and K. Accumulation is FP32. `workspace` may be NULL (then
- * workspace_bytes must be 0 and no split-K is used).
+ * NVFP4, alpha = 1 for MXFP4). `a` is CANONICAL or TILED, `w` is TILED,
+ * same format and K. Accumulation is FP32. `workspace` may be NULL.
  */
 fp4_status fp4_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c_bf16, int64_t ldc,
                     void *workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace for fp4_linear: quantized activations, reduction scratch, split-K. */
+/* Workspace for fp4_linear: the quantized activations and the quantizer's
+ * scratch. Same contract as the quantize workspace: zero-filled before its
+ * first use, left reusable by every call, not shared by overlapping calls. */
 size_t fp4_linear_workspace_bytes(int32_t fmt, int64_t m, int64_t n, int64_t k);
 
 /*
@@ -152,7 +158,7 @@ fp4_status fp4_linear(const void *x_bf16, int64_t m, const fp4_tensor *w,
                       size_t workspace_bytes, hipStream_t stream);
 
 /* Test aids (not on the hot path). */
-/* Copy a WEIGHT_TILED tensor into a CANONICAL one of the same format/shape
+/* Copy a TILED tensor into a CANONICAL one of the same format/shape
  * (including the tensor scale when both pointers are set). */
 fp4_status fp4_export_canonical(const fp4_tensor *tiled, fp4_tensor *canonical,
                                 hipStream_t stream);

@@ -34,17 +34,19 @@ def test_sizes_and_pitches():
     assert L.fp4_scales_bytes(fp4.NVFP4, fp4.CANONICAL, 3, 2880) == 3 * 2944 // 16
     assert L.fp4_scales_bytes(fp4.MXFP4, fp4.CANONICAL, 3, 2880) == 3 * 2944 // 32
     # tiled: rows padded to 16
-    assert L.fp4_codes_bytes(fp4.NVFP4, fp4.WEIGHT_TILED, 17, 256) == 32 * 128
-    assert L.fp4_scales_bytes(fp4.MXFP4, fp4.WEIGHT_TILED, 17, 256) == 32 * 8
+    assert L.fp4_codes_bytes(fp4.NVFP4, fp4.TILED, 17, 256) == 32 * 128
+    assert L.fp4_scales_bytes(fp4.MXFP4, fp4.TILED, 17, 256) == 32 * 8
     # 4.5 and 4.25 bits per value when nothing is padded
     k, n = 5120, 5120
     for fmt, bits in ((fp4.NVFP4, 4.5), (fp4.MXFP4, 4.25)):
-        tot = L.fp4_codes_bytes(fmt, fp4.WEIGHT_TILED, n, k) + L.fp4_scales_bytes(fmt, fp4.WEIGHT_TILED, n, k)
+        tot = L.fp4_codes_bytes(fmt, fp4.TILED, n, k) + L.fp4_scales_bytes(fmt, fp4.TILED, n, k)
         assert tot * 8 / (n * k) == bits
     assert L.fp4_block_size(fp4.NVFP4) == 16 and L.fp4_block_size(fp4.MXFP4) == 32
     assert L.fp4_block_size(7) == 0
     assert L.fp4_codes_bytes(9, 0, 4, 32) == 0
     assert L.fp4_quantize_workspace_bytes(fp4.NVFP4, 8, 64) >= 4096
+    assert L.fp4_quantize_workspace_bytes(fp4.MXFP4, 8, 64) == 0
+    assert L.fp4_gemm_workspace_bytes(fp4.NVFP4, 8, 64, 64) == 0
     assert L.fp4_linear_workspace_bytes(fp4.NVFP4, 8, 5120, 5120) > 0
 
 
@@ -75,7 +77,7 @@ def test_host_validation_rejects_before_launch():
     good = fp4.fp4_tensor()
     assert L.fp4_tensor_init(ctypes.byref(good), fp4.NVFP4, fp4.CANONICAL, 4, 64, 4096, 8192, 64) == 0
     w = fp4.fp4_tensor()
-    assert L.fp4_tensor_init(ctypes.byref(w), fp4.NVFP4, fp4.WEIGHT_TILED, 32, 64, 4096, 8192, 64) == 0
+    assert L.fp4_tensor_init(ctypes.byref(w), fp4.NVFP4, fp4.TILED, 32, 64, 4096, 8192, 64) == 0
     # null input
     assert L.fp4_quantize_act(0, None, 4, 64, None, ctypes.byref(good), 1024, 4096, None) == 1
     # K not a multiple of the block
@@ -88,14 +90,16 @@ def test_host_validation_rejects_before_launch():
     mx = fp4.fp4_tensor()
     assert L.fp4_tensor_init(ctypes.byref(mx), fp4.MXFP4, fp4.CANONICAL, 4, 64, 4096, 8192, 0) == 0
     assert L.fp4_quantize_act(1, 4096, 4, 64, 64, ctypes.byref(mx), 0, 0, None) == 1
-    # layout mismatch: activation into a tiled descriptor
-    assert L.fp4_quantize_act(0, 4096, 32, 64, None, ctypes.byref(w), 1024, 4096, None) == 5
+    # descriptor of another shape
+    assert L.fp4_quantize_act(0, 4096, 16, 64, None, ctypes.byref(w), 1024, 8192, None) == 5
+    # weights go to the tiled layout only
+    assert L.fp4_quantize_weight(0, 4096, 4, 64, ctypes.byref(good), 1024, 8192, None) == 5
     # gemm: format mismatch, K mismatch, null output, small ldc
     wmx = fp4.fp4_tensor()
-    assert L.fp4_tensor_init(ctypes.byref(wmx), fp4.MXFP4, fp4.WEIGHT_TILED, 32, 64, 4096, 8192, 0) == 0
+    assert L.fp4_tensor_init(ctypes.byref(wmx), fp4.MXFP4, fp4.TILED, 32, 64, 4096, 8192, 0) == 0
     assert L.fp4_gemm(ctypes.byref(good), ctypes.byref(wmx), 4096, 32, None, 0, None) == 5
     w128 = fp4.fp4_tensor()
-    assert L.fp4_tensor_init(ctypes.byref(w128), fp4.NVFP4, fp4.WEIGHT_TILED, 32, 128, 4096, 8192, 64) == 0
+    assert L.fp4_tensor_init(ctypes.byref(w128), fp4.NVFP4, fp4.TILED, 32, 128, 4096, 8192, 64) == 0
     assert L.fp4_gemm(ctypes.byref(good), ctypes.byref(w128), 4096, 32, None, 0, None) == 2
     assert L.fp4_gemm(ctypes.byref(good), ctypes.byref(w), None, 32, None, 0, None) == 1
     assert L.fp4_gemm(ctypes.byref(good), ctypes.byref(w), 4096, 16, None, 0, None) == 2

@@ -109,3 +109,70 @@ def test_gemm_deterministic(fmt):
     y1, y2 = fp4.fp4_linear(x, wq), fp4.fp4_linear(x, wq)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m", [8, 32, 64])
+def test_graph_replay_matches_eager(fmt, m):
+    """fp4_linear captured in a HIP graph: every replay (with eager work and
+    synchronizations in between) equals the eager result bit for bit."""
+    k, n = 1024, 2048
+    a = synth.normal((m, k), 1.0, 8, m)
+    w = synth.normal((n, k), 0.02, 8, n)
+    wq = fp4.fp4_quantize_weight(to_dev(w), F[fmt])
+    x = to_dev(a)
+    ws = torch.zeros(fp4.fp4_linear_workspace_bytes(F[fmt], m, n, k), dtype=torch.uint8, device="cuda")
+    out = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    eager = fp4.fp4_linear(x, wq, out=torch.empty_like(out), workspace=ws).clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fp4.fp4_linear(x, wq, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fp4.fp4_linear(x, wq, out=out, workspace=ws)
+    for rep in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} differs from eager"
+        other = fp4.fp4_linear(x, wq)       # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(other, eager)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_decode_without_split_workspace(fmt):
+    """fp4_gemm given no room for split-K runs one split per tile (several K
+    chunks per wave) and still matches."""
+    m, n, k = 8, 320, 17408
+    f = F[fmt]
+    a = synth.normal((m, k), 1.0, 12, 1)
+    w = synth.normal((n, k), 0.02, 12, 2)
+    qa_ref, qw_ref = oracle.quantize(f, a), oracle.quantize(f, w)
+    c_ref, l_ref = oracle.gemm(qa_ref, qw_ref)
+    wq = fp4.fp4_quantize_weight(to_dev(w), f)
+    qa = fp4.fp4_quantize_act(to_dev(a), f)
+    tiny = torch.zeros(1, dtype=torch.uint8, device="cuda")
+    c = bf16_out_to_f64(fp4.fp4_gemm(qa, wq, workspace=tiny))
+    assert_gemm_close(c, c_ref, l_ref, "decode, single split")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m", [1, 32])
+def test_workspace_reused_across_calls(fmt, m):
+    """The split-K slots clean themselves: one zeroed workspace serves many calls."""
+    n, k = 640, 5120
+    f = F[fmt]
+    w = synth.normal((n, k), 0.02, 13, 1)
+    qw_ref = oracle.quantize(f, w)
+    wq = fp4.fp4_quantize_weight(to_dev(w), f)
+    ws = torch.zeros(fp4.fp4_linear_workspace_bytes(f, m, n, k), dtype=torch.uint8, device="cuda")
+    for call in range(3):
+        a = synth.normal((m, k), 1.0 + call, 13, 10 + call)
+        c_ref, l_ref = oracle.gemm(oracle.quantize(f, a), qw_ref)
+        y = bf16_out_to_f64(fp4.fp4_linear(to_dev(a), wq, workspace=ws))
+        assert_gemm_close(y, c_ref, l_ref, f"call {call}")
+    torch.cuda.synchronize()

@@ -118,3 +118,38 @@ def test_quantize_is_deterministic(fmt):
     q2 = fp4.fp4_quantize_act(x, F[fmt])
     torch.cuda.synchronize()
     assert torch.equal(q1.codes, q2.codes) and torch.equal(q1.scales, q2.scales)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m,k", [(1, 5120), (8, 17408), (32, 17408), (17, 2880), (300, 544)])
+def test_tiled_activation_layout(fmt, m, k):
+    """Activations quantized into the fragment-tiled layout hold the same bytes."""
+    print(f"[quant-act-tiled] fmt={fmt} m={m} k={k}", flush=True)
+    f = F[fmt]
+    bits = synth.normal((m, k), 1.0, 14, m * 7 + k)
+    ref = oracle.quantize(f, bits)
+    q = fp4.fp4_quantize_act(to_dev(bits), f, layout=fp4.TILED)
+    assert_canonical_equal(fp4.fp4_export_canonical(q), ref, f, what=f"tiled act {m}x{k}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_single_launch_limit(fmt):
+    """Both sides of the single-launch / two-launch switch (2^17 blocks per call)."""
+    f = F[fmt]
+    for m in (64, 65) if fmt == "nvfp4" else (128, 129):
+        bits = synth.normal((m, 32768), 1.0, 15, m)
+        print(f"[quant-limit] fmt={fmt} m={m}", flush=True)
+        _act_case(fmt, bits, f"limit m={m}")
+
+
+def test_workspace_shared_across_calls():
+    """One zero-filled workspace serves a sequence of dynamic NVFP4 calls of
+    different shapes and both code paths (the max-exchange words recycle)."""
+    ws = torch.zeros(fp4.lib().fp4_quantize_workspace_bytes(0, 1, 16), dtype=torch.uint8, device="cuda")
+    shapes = [(1, 5120), (32, 17408), (4, 64), (96, 32768), (8, 256), (1, 16), (300, 2880)]
+    for rep in range(2):
+        for i, (m, k) in enumerate(shapes):
+            bits = synth.normal((m, k), 0.5 + i, 16, rep * 100 + i)
+            ref = oracle.quantize_nvfp4(bits)
+            q = fp4.fp4_quantize_act(to_dev(bits), 0, workspace=ws)
+            assert_canonical_equal(q, ref, 0, what=f"shared workspace call {rep}/{i} {m}x{k}")
