@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--kernel-reps", type=int, default=50)
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-mib", type=int, default=0,
+                   help="also run one plain device copy of this many MiB (a reference for "
+                        "hardware byte counters)")
     return p.parse_args()
 
 
@@ -119,6 +122,12 @@ def main():
         wss[(m, k, n)] = torch.zeros(max(1, fp4.fp4_linear_workspace_bytes(fmt, m, n, k)),
                                      dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
+    if args.copy_mib:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(i):
         for cfg in configs:
@@ -165,25 +174,18 @@ def main():
     flops = sum(2.0 * m * n * k for (m, k, n) in configs)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
 
-    # ---- dominant kernel: the GEMM launch alone, back-to-back in a graph,
-    # timed with events on the stream the launches go to.
-    kern = {}
-    reps = max(copies, args.kernel_reps)
-    for cfg in configs:
-        m, k, n = cfg
-        # the activation layout fp4_linear uses internally (fragment-tiled)
-        qa = fp4.fp4_quantize_act(xs[cfg], fmt, layout=fp4.TILED)
-        gws = torch.zeros(max(1, fp4.lib().fp4_gemm_workspace_bytes(fmt, m, n, k)),
-                          dtype=torch.uint8, device=dev)
-        wl = weights[(k, n)]
-        fp4.fp4_gemm(qa, wl[0], out=outs[cfg], workspace=gws)
+    # ---- dominant kernel: the skinny GEMM (fused with the activation
+    # quantization when fp4_linear runs as one launch), timed alone: R
+    # back-to-back launches captured in a graph, HIP events on the launch stream.
+    def graph_time(fn, reps):
+        fn(0)
         torch.cuda.synchronize()
         s = torch.cuda.Stream()
         with torch.cuda.stream(s):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=s):
                 for r in range(reps):
-                    fp4.fp4_gemm(qa, wl[r % copies], out=outs[cfg], workspace=gws)
+                    fn(r)
             g.replay()
             s.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -191,32 +193,52 @@ def main():
             g.replay()
             e1.record(s)
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
-        if m <= 32:
-            name = "k_gemm_decode<%s,MG=%d>" % (args.fmt, 1 if m <= 16 else 2)
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    reps = max(copies, args.kernel_reps)
+    kern, per_cfg = {}, []
+    bs = 16 if fmt == 0 else 32
+    for cfg in configs:
+        m, k, n = cfg
+        wl = weights[(k, n)]
+        w_bytes = n * (k // 2 + k // bs)
+        lin_us = graph_time(lambda r: fp4.fp4_linear(xs[cfg], wl[r % copies], out=outs[cfg],
+                                                     workspace=wss[cfg]), reps)
+        if fp4.fp4_linear_launches(fmt, m, n, k) == 1:
+            name = "k_linear_decode<%s>" % args.fmt
+            us = lin_us
+            nbytes = w_bytes + 2 * m * k + 2 * m * n          # W + bf16 A + bf16 C
         else:
-            name = "k_gemm_prefill<%s>" % args.fmt
-        d = kern.setdefault(name, {"launches": 0, "us": 0.0, "bytes": 0.0, "flops": 0.0, "per_cfg": []})
+            # the activation layout fp4_linear uses internally (fragment-tiled)
+            qa = fp4.fp4_quantize_act(xs[cfg], fmt, layout=fp4.TILED)
+            name = ("k_gemm_decode<%s,MG=%d>" % (args.fmt, 1 if m <= 16 else 2)) if m <= 32 \
+                else "k_gemm_prefill<%s>" % args.fmt
+            us = graph_time(lambda r: fp4.fp4_gemm(qa, wl[r % copies], out=outs[cfg]), reps)
+            nbytes = w_bytes + m * (k // 2 + k // bs) + 2 * m * n  # W + FP4 A + bf16 C
+        d = kern.setdefault(name, {"launches": 0, "us": 0.0, "bytes": 0.0, "flops": 0.0})
         d["launches"] += 1
         d["us"] += us
-        d["bytes"] += gemm_bytes(m, k, n, fmt)
+        d["bytes"] += nbytes
         d["flops"] += 2.0 * m * n * k
-        d["per_cfg"].append({"m": m, "k": k, "n": n, "us": round(us, 3),
-                             "GBps": round(gemm_bytes(m, k, n, fmt) / (us * 1e-6) / 1e9, 1)})
-    dom_name = max(kern, key=lambda nm: kern[nm]["us"])
-    dk = kern[dom_name]
-    avg_us = dk["us"] / dk["launches"]
-    if args.workload == "decode" or "decode" in dom_name:
-        achieved = dk["bytes"] / dk["launches"] / (avg_us * 1e-6) / 1e9
+        per_cfg.append({"m": m, "k": k, "n": n, "kernel": name, "kernel_us": round(us, 3),
+                        "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "linear_us": round(lin_us, 3)})
+    tot_us = sum(d["us"] for d in kern.values())
+    tot_launch = sum(d["launches"] for d in kern.values())
+    if args.workload == "decode":
+        achieved = sum(d["bytes"] for d in kern.values()) / (tot_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
     else:
-        achieved = dk["flops"] / dk["launches"] / (avg_us * 1e-6) / 1e12
+        achieved = sum(d["flops"] for d in kern.values()) / (tot_us * 1e-6) / 1e12
         peak = FP4_PEAK_TFLOPS if fmt == 1 else F16_PEAK_TFLOPS
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": None}
-    roof.update({"kernel": dom_name, "avg_launch_us": round(avg_us, 3), "launches_per_step": dk["launches"],
-                 "per_config": dk["per_cfg"]})
+    roof.update({"kernel": " + ".join(sorted(kern)), "avg_launch_us": round(tot_us / tot_launch, 3),
+                 "launches_per_step": tot_launch,
+                 "per_kernel": {nm: {"launches": d["launches"], "avg_us": round(d["us"] / d["launches"], 3),
+                                     "GBps": round(d["bytes"] / (d["us"] * 1e-6) / 1e9, 1)}
+                                for nm, d in kern.items()},
+                 "per_config": per_cfg})
 
     result = {
         "metric": METRIC,

@@ -75,6 +75,7 @@ def lib():
             "fp4_gemm": (I32, [T, T, P, I64, P, SZ, P]),
             "fp4_linear_workspace_bytes": (SZ, [I32, I64, I64, I64]),
             "fp4_linear": (I32, [P, I64, T, P, P, P, SZ, P]),
+            "fp4_linear_launches": (I32, [I32, I64, I64, I64, I32]),
             "fp4_export_canonical": (I32, [T, T, P]),
             "fp4_dequantize": (I32, [T, P, I64, P]),
             "fp4_status_string": (ctypes.c_char_p, [I32]),
@@ -188,15 +189,20 @@ def fp4_gemm(a: Fp4Tensor, w: Fp4Tensor, out: torch.Tensor | None = None,
     if out is None:
         out = torch.empty(m, n, dtype=torch.bfloat16, device=a.device)
     nws = L.fp4_gemm_workspace_bytes(a.fmt, m, n, a.k)
-    if workspace is None:   # zero-filled once, as the C ABI requires
-        workspace = torch.zeros(max(nws, 1), dtype=torch.uint8, device=a.device)
+    if workspace is None and nws > 0:   # zero-filled once, as the C ABI requires
+        workspace = torch.zeros(nws, dtype=torch.uint8, device=a.device)
     _check(L.fp4_gemm(ctypes.byref(a.desc), ctypes.byref(w.desc), _ptr(out), out.stride(0),
-                      _ptr(workspace), workspace.numel(), _stream(a.device)))
+                      _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                      _stream(a.device)))
     return out
 
 
 def fp4_linear_workspace_bytes(fmt, m: int, n: int, k: int) -> int:
     return lib().fp4_linear_workspace_bytes(_fmt(fmt), m, n, k)
+
+
+def fp4_linear_launches(fmt, m: int, n: int, k: int, static_scale: bool = False) -> int:
+    return lib().fp4_linear_launches(_fmt(fmt), m, n, k, int(bool(static_scale)))
 
 
 def fp4_linear(x: torch.Tensor, w: Fp4Tensor, static_scale: torch.Tensor | None = None,

@@ -283,6 +283,13 @@ fp4_status fp4_linear(const void *x_bf16, int64_t m, const fp4_tensor *w,
   if (!aligned16(workspace)) return fail(FP4_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
   if ((st = check_device()) != FP4_OK) return st;
 
+  if (linear_fused_ok(fmt, m, n, k)) {
+    hipError_t e = launch_linear_fused(fmt, (const uint16_t *)x_bf16, m, k, static_scale,
+                                       (const uint8_t *)w->codes, (const uint8_t *)w->scales,
+                                       w->tensor_scale, n, (uint16_t *)y_bf16, n, stream);
+    if (e != hipSuccess) return hip_fail(e, "fused linear launch");
+    return ok();
+  }
   char *ws = (char *)workspace;
   fp4_tensor a;
   a.fmt = fmt;
@@ -298,6 +305,13 @@ fp4_status fp4_linear(const void *x_bf16, int64_t m, const fp4_tensor *w,
   if (st != FP4_OK) return st;
   st = run_gemm(&a, w, y_bf16, n, stream);
   return st == FP4_OK ? ok() : st;
+}
+
+int32_t fp4_linear_launches(int32_t fmt, int64_t m, int64_t n, int64_t k, int32_t static_scale) {
+  if (!valid_fmt(fmt) || m <= 0 || n <= 0 || k <= 0 || k % block_of(fmt) != 0) return 0;
+  if (linear_fused_ok(fmt, m, n, k)) return 1;
+  if (fmt == FP4_NVFP4 && !static_scale && !quant_fits_small(fmt, m, k, 1)) return 3;
+  return 2;
 }
 
 fp4_status fp4_export_canonical(const fp4_tensor *tiled, fp4_tensor *canonical,

@@ -144,15 +144,117 @@ __device__ __forceinline__ uint32_t mx_encode8(int e, uint4 v) {
   uint32_t out = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    float lo = ldexpf(bf16_bits_to_f32(w[i] & 0xFFFFu), -e);
-    float hi = ldexpf(bf16_bits_to_f32(w[i] >> 16), -e);
-    uint32_t byte = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, lo, hi, 1.0f, 0) & 0xFFu;
-    out |= byte << (8 * i);
+    const float lo = ldexpf(bf16_bits_to_f32(w[i] & 0xFFFFu), -e);
+    const float hi = ldexpf(bf16_bits_to_f32(w[i] >> 16), -e);
+    // the byte-select operand writes byte i of `out` and keeps the others
+    switch (i) {
+      case 0: out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, lo, hi, 1.0f, 0); break;
+      case 1: out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, lo, hi, 1.0f, 1); break;
+      case 2: out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, lo, hi, 1.0f, 2); break;
+      default: out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, lo, hi, 1.0f, 3); break;
+    }
   }
   return out;
 }
 
+// ---- block helpers shared by the quantizers and the fused linear ----
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return v;
+}
+
+// Workgroup-wide max of v (every thread receives it); lds holds one word per wave.
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t *lds) {
+  v = wave_max_u32(v);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) lds[wave] = v;
+  __syncthreads();
+  uint32_t r = lds[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = max(r, lds[i]);
+  return r;
+}
+
+// |x| max of 8 bf16 values as a bit pattern (magnitudes order like their bits).
+__device__ __forceinline__ uint32_t absmax_bits8(uint4 v) {
+  uint32_t m = 0;
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m = max(m, w[i] & 0x7FFFu);
+    m = max(m, (w[i] >> 16) & 0x7FFFu);
+  }
+  return m;
+}
+
+// Fast NVFP4 element codes for 8 values with a bracket test. z = x * r with
+// r ~ 1/d_b (relative error < 2^-22 in total), so the exact quotient x / d_b
+// lies strictly inside [z (1 - 2^-20), z (1 + 2^-20)]. The hardware convert
+// rounds both ends exactly (nearest, ties to even, saturating); when they give
+// the same code, rounding is monotonic, so that code is the exact quotient's.
+// When they differ the quotient is within 2^-20 of a rounding midpoint (or on
+// it) and the exact comparisons decide. Returns the 8 nibbles.
+__device__ __forceinline__ uint32_t nv_encode8_fast(const NvBlockEnc &e, float r, uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t out = 0, diff = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float x = __uint_as_float(h ? (w[i] & 0xFFFF0000u) : (w[i] << 16));
+      const float z = x * r;
+      const uint32_t b =
+          __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, z * 0x1.ffffep-1f, z * 0x1.00001p+0f, 1.0f, 0);
+      diff |= (b ^ (b >> 4)) & 0xFu;
+      out |= (b & 0xFu) << (4 * (2 * i + h));
+    }
+  }
+  if (diff) out = nv_encode8(e, v);  // near a midpoint: exact comparisons
+  return out;
+}
+
+// One NVFP4 block (16 values in v0, v1) under tensor scale st: 8 code bytes
+// and the E4M3 scale byte.
+__device__ __forceinline__ void nv_encode_block(uint4 v0, uint4 v1, float st, uint2 &codes,
+                                                uint32_t &sbyte) {
+  const uint32_t abits = max(absmax_bits8(v0), absmax_bits8(v1));
+  const double q = (double)bf16_bits_to_f32(abits) / (6.0 * (double)st);
+  sbyte = e4m3_rne_sat(q);
+  const NvBlockEnc enc = nv_block_encoder(sbyte, st);
+  if (sbyte != 0u && st >= 0x1p-100f) {
+    // d_b = s_b * S_t >= 2^-109, so its reciprocal is a finite normal float;
+    // rounding d_b and the reciprocal add < 2^-22 relative error to z.
+    const float r = __builtin_amdgcn_rcpf(e4m3_to_f32(sbyte) * st);
+    codes = make_uint2(nv_encode8_fast(enc, r, v0), nv_encode8_fast(enc, r, v1));
+  } else {
+    codes = make_uint2(nv_encode8(enc, v0), nv_encode8(enc, v1));
+  }
+}
+
+// One MXFP4 block (32 values in v[0..3]): 16 code bytes and the E8M0 byte.
+__device__ __forceinline__ void mx_encode_block(const uint4 (&v)[4], uint4 &codes,
+                                                uint32_t &sbyte) {
+  const uint32_t abits = max(max(absmax_bits8(v[0]), absmax_bits8(v[1])),
+                             max(absmax_bits8(v[2]), absmax_bits8(v[3])));
+  const int e = mx_exponent_from_bits(abits);
+  codes = make_uint4(mx_encode8(e, v[0]), mx_encode8(e, v[1]), mx_encode8(e, v[2]),
+                     mx_encode8(e, v[3]));
+  sbyte = (uint32_t)(e + 127);
+}
+
 // ---- decode side ----
+
+// Two FP4 codes (byte b of q) -> two f16 values q * 2^8 (exact).
+__device__ __forceinline__ h2v fp4x2_to_h2_times256(uint32_t q, int b) {
+  switch (b) {
+    case 0: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 256.0f, 0);
+    case 1: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 256.0f, 1);
+    case 2: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 256.0f, 2);
+    default: return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 256.0f, 3);
+  }
+}
 
 // E4M3 scale byte -> f16 bits of s_b * 2^-8 in both halves (exact: the E4M3
 // exponent and mantissa fields land in the f16 fields with a bias offset of 8).
@@ -174,12 +276,25 @@ __device__ __forceinline__ void nv_dequant32(uint4 q, uint32_t s2, h8v out[4]) {
     h2v sc = d < 2 ? sc0 : sc1;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      h2v v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[d] >> (8 * b), 256.0f, 0);
-      v = v * sc;
+      // the byte-select operand picks byte b (values 2b, 2b+1 of this dword)
+      h2v v = fp4x2_to_h2_times256(w[d], b) * sc;
       out[d][2 * b] = v[0];
       out[d][2 * b + 1] = v[1];
     }
   }
+}
+
+// Dequantize 8 NVFP4 codes (one dword, value j in nibble j) with E4M3 scale
+// byte sbyte into 8 exact f16 values q * s_b (returned as a uint4).
+__device__ __forceinline__ uint4 nv_dequant8_u4(uint32_t q, uint32_t sbyte) {
+  const h2v sc = e4m3_scaled_h2(sbyte);
+  uint32_t r[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    h2v v = fp4x2_to_h2_times256(q, b) * sc;
+    r[b] = __builtin_bit_cast(uint32_t, v);
+  }
+  return make_uint4(r[0], r[1], r[2], r[3]);
 }
 
 __device__ __forceinline__ v8i frag_v8i(uint4 q) {

@@ -21,8 +21,8 @@ inline int frag_scale_bytes(int fmt) { return fmt == 0 ? 128 : 64; }
 constexpr int kActGrid = 128;         // workgroups of the single-launch quantizer
 constexpr int kActBpt = 4;            // blocks per thread in the single-launch quantizer
 // Quantize scratch: kMaxAmaxParts partial maxima, then the single-launch
-// quantizer's {arrival counter, max word 0, max word 1} (zero-filled once).
-constexpr size_t kQuantScratchBytes = (kMaxAmaxParts + 64) * sizeof(uint32_t);
+// quantizer's kActGrid tagged maximum words (zero-filled once).
+constexpr size_t kQuantScratchBytes = (kMaxAmaxParts + kActGrid) * sizeof(uint32_t);
 
 // Number of partial maxima the large-tensor path produces for n elements.
 int amax_parts(int64_t n);
@@ -63,5 +63,15 @@ struct GemmArgs {
 
 hipError_t launch_gemm_prefill(const GemmArgs &g, hipStream_t stream);
 hipError_t launch_gemm_decode(const GemmArgs &g, hipStream_t stream);
+
+// Single-launch linear (activation quantization fused) for small activations.
+constexpr int kFusedMaxM = 16;
+constexpr int64_t kFusedMaxMK = 65536;        // M * K_pad bound (LDS staging, MXFP4)
+constexpr int64_t kFusedMaxWork = 16 << 20;   // M * K_pad * N tiles bound
+bool linear_fused_ok(int fmt, int64_t m, int64_t n, int64_t k);
+hipError_t launch_linear_fused(int fmt, const uint16_t *x, int64_t m, int64_t k,
+                               const float *static_scale, const uint8_t *w_codes,
+                               const uint8_t *w_scales, const float *w_ts, int64_t n,
+                               uint16_t *y, int64_t ldy, hipStream_t stream);
 
 }  // namespace fp4i

@@ -242,6 +242,143 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(
   }
 }
 
+// --------------------------------------------------------- fused linear
+//
+// Skinny linear with the activation quantization fused in, for activations
+// small enough that every workgroup can quantize all of them itself (the
+// bf16 tensor is L2-resident): each workgroup issues the loads of its first
+// weight fragments, takes the activations' maximum (NVFP4), encodes every
+// block exactly as the standalone quantizer does and stages the result in LDS,
+// then runs the decode main loop with the activation operand read from LDS.
+// No value crosses workgroups and there is no separate quantize launch.
+//   NVFP4: LDS holds the activations already dequantized to f16 (q * s_b is
+//          exact in f16), so the main loop converts only the weight operand.
+//   MXFP4: LDS holds codes and E8M0 bytes for the scaled matrix instruction.
+// LDS rows are padded by 16 bytes so the rows of a fragment use other banks.
+template <int FMT>
+__global__ __launch_bounds__(64 * kDecWaves) void k_linear_decode(
+    const uint16_t *__restrict__ x, int m, int k, const float *__restrict__ static_scale,
+    const uint8_t *__restrict__ w_codes, const uint8_t *__restrict__ w_sc,
+    const float *__restrict__ w_ts, int n, int kt_n, uint16_t *__restrict__ y, int64_t ldy) {
+  constexpr int NW = kDecWaves, FM = kDecFrags;
+  constexpr int B = FMT == 0 ? 16 : 32, V = B / 8;
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ float red[NW][4][64];
+  __shared__ uint32_t lmax[NW];
+  // NVFP4: f16 rows of K_pad values; MXFP4: code rows then scale rows
+  const int ap = FMT == 0 ? kt_n * 256 + 16 : kt_n * 64 + 16;
+  const int sp = kt_n * 4;
+  uint8_t *lscales = smem + (size_t)m * ap;
+  const int nt = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+
+  uint4 wq[2][FM];
+  uint32_t ws[2][FM];
+  auto load = [&](int buf, int base) {
+#pragma unroll
+    for (int u = 0; u < FM; ++u) {
+      const int kt = base + NW * u;
+      if (kt < kt_n) load_w<FMT>(w_codes, w_sc, (int64_t)nt * kt_n + kt, lane, wq[buf][u], ws[buf][u]);
+    }
+  };
+  load(0, wave);
+
+  const int nb = k / B, nb_pad = kt_n * (128 / B), total = m * nb_pad;
+  float st = 1.0f;
+  if (FMT == 0) {
+    if (static_scale) {
+      st = *static_scale;
+    } else {
+      uint32_t amax = 0;
+      for (int t = threadIdx.x; t < m * nb; t += 64 * NW) {
+        const int r = t / nb, c = t - r * nb;
+        const uint4 *src = (const uint4 *)(x + (int64_t)r * k + c * B);
+        amax = max(amax, max(absmax_bits8(src[0]), absmax_bits8(src[1])));
+      }
+      st = tensor_scale_from_amax(bf16_bits_to_f32(block_max_u32(amax, lmax)));
+    }
+  }
+#pragma unroll 1
+  for (int t = threadIdx.x; t < total; t += 64 * NW) {
+    const int r = t / nb_pad, c = t - r * nb_pad;
+    uint4 v[V];
+    if (c < nb) {
+      const uint4 *src = (const uint4 *)(x + (int64_t)r * k + c * B);
+#pragma unroll
+      for (int i = 0; i < V; ++i) v[i] = src[i];
+    }
+    if constexpr (FMT == 0) {
+      uint4 *dst = (uint4 *)(smem + r * ap + c * 32);
+      if (c < nb) {
+        uint2 q;
+        uint32_t sbyte;
+        nv_encode_block(v[0], v[1], st, q, sbyte);
+        dst[0] = nv_dequant8_u4(q.x, sbyte);
+        dst[1] = nv_dequant8_u4(q.y, sbyte);
+      } else {
+        dst[0] = make_uint4(0u, 0u, 0u, 0u);
+        dst[1] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    } else {
+      uint4 q = make_uint4(0u, 0u, 0u, 0u);
+      uint32_t sbyte = 0;
+      if (c < nb) mx_encode_block(v, q, sbyte);
+      *(uint4 *)(smem + r * ap + c * 16) = q;
+      lscales[r * sp + c] = (uint8_t)sbyte;
+    }
+  }
+  __syncthreads();
+
+  const int row = lane & 15, lc = lane >> 4;
+  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int buf, int base) {
+#pragma unroll
+    for (int u = 0; u < FM; ++u) {
+      const int kt = base + NW * u;
+      if (kt >= kt_n) break;  // wave-uniform
+      if constexpr (FMT == 1) {
+        uint4 aq = make_uint4(0u, 0u, 0u, 0u);
+        uint32_t as = 0u;
+        if (row < m) {
+          aq = *(const uint4 *)(smem + row * ap + kt * 64 + lc * 16);
+          as = lscales[row * sp + kt * 4 + lc];
+        }
+        acc = mfma_mx(wq[buf][u], aq, acc, ws[buf][u], as);
+      } else {
+        h8v wh[4], ah[4];
+        nv_dequant32(wq[buf][u], ws[buf][u], wh);
+        const uint4 *arow = (const uint4 *)(smem + row * ap + kt * 256 + lc * 64);
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          ah[g] = __builtin_bit_cast(h8v, row < m ? arow[g] : make_uint4(0u, 0u, 0u, 0u));
+        acc = mfma_nv(wh, ah, acc);
+      }
+    }
+  };
+  constexpr int STEP = NW * FM;
+  for (int base = wave; base < kt_n; base += 2 * STEP) {
+    load(1, base + STEP);
+    compute(0, base);
+    if (base + STEP >= kt_n) break;
+    load(0, base + 2 * STEP);
+    compute(1, base + STEP);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[wave][r][lane] = acc[r];
+  __syncthreads();
+  if (wave != 0) return;
+  const float alpha = FMT == 0 ? st * w_ts[0] : 1.0f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float sum = red[0][r][lane];
+#pragma unroll
+    for (int w2 = 1; w2 < NW; ++w2) sum += red[w2][r][lane];
+    const int ncol = nt * 16 + 4 * lc + r;
+    if (row < m && ncol < n) y[(int64_t)row * ldy + ncol] = f32_to_bf16_rne(sum * alpha);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_prefill(const GemmArgs &g, hipStream_t stream) {
@@ -276,6 +413,31 @@ hipError_t launch_gemm_decode(const GemmArgs &g, hipStream_t stream) {
   else FP4_DEC_T(1, 2);
 #undef FP4_DEC_T
 #undef FP4_DEC
+  return hipGetLastError();
+}
+
+bool linear_fused_ok(int fmt, int64_t m, int64_t n, int64_t k) {
+  const int64_t mk = m * k_pad(k);
+  // LDS staging bound, and a bound on the redundant quantization work that
+  // every weight tile's workgroup repeats.
+  return m <= kFusedMaxM && mk <= (fmt == 0 ? kFusedMaxMK / 2 : kFusedMaxMK) &&
+         mk * (round_up(n, 16) / 16) <= kFusedMaxWork;
+}
+
+hipError_t launch_linear_fused(int fmt, const uint16_t *x, int64_t m, int64_t k,
+                               const float *static_scale, const uint8_t *w_codes,
+                               const uint8_t *w_scales, const float *w_ts, int64_t n,
+                               uint16_t *y, int64_t ldy, hipStream_t stream) {
+  const int kt_n = (int)(k_pad(k) / kFragK);
+  const int nt_n = (int)(round_up(n, 16) / 16);
+  const size_t lds = fmt == 0 ? (size_t)m * (kt_n * 256 + 16)
+                              : (size_t)m * (kt_n * 64 + 16) + (size_t)m * kt_n * 4;
+  if (fmt == 0)
+    hipLaunchKernelGGL(k_linear_decode<0>, dim3(nt_n), dim3(64 * kDecWaves), lds, stream, x,
+                       (int)m, (int)k, static_scale, w_codes, w_scales, w_ts, (int)n, kt_n, y, ldy);
+  else
+    hipLaunchKernelGGL(k_linear_decode<1>, dim3(nt_n), dim3(64 * kDecWaves), lds, stream, x,
+                       (int)m, (int)k, static_scale, w_codes, w_scales, w_ts, (int)n, kt_n, y, ldy);
   return hipGetLastError();
 }
 

@@ -13,13 +13,10 @@
 // before any block can be encoded. Two ways are used:
 //   * small tensors (activations of skinny GEMMs): one launch of a fixed grid
 //     of kActGrid workgroups. Each workgroup keeps its blocks in registers,
-//     publishes its maximum with a device-scope atomic max, then arrives at a
-//     counter and waits (bounded spin) until all workgroups have arrived. Only
-//     one 32-bit value crosses workgroups, inside atomics, so no cache
-//     writeback is needed. The counter grows by kActGrid per call; a call's
-//     epoch (counter / kActGrid) selects one of two maximum words, and the
-//     first arrival clears the other one for the next call. Zero-filled words
-//     are the initial state.
+//     publishes its maximum in its own tagged word and waits (bounded) until
+//     every workgroup's word carries this call's tag (grid_max_u32). Only
+//     these 32-bit words cross workgroups, through device-coherent accesses,
+//     so no cache writeback is needed. Zero-filled words are the initial state.
 //   * large tensors: partial maxima per workgroup, then a second launch in
 //     which every workgroup folds the (at most 1024) partials itself.
 // Both are deterministic: a maximum does not depend on evaluation order.
@@ -32,36 +29,6 @@ using namespace fp4d;
 namespace {
 
 constexpr int kThreads = 256;
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
-  return v;
-}
-
-// Workgroup-wide max of v (all threads receive it).
-__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t *lds4) {
-  v = wave_max_u32(v);
-  int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane == 0) lds4[wave] = v;
-  __syncthreads();
-  uint32_t r = lds4[0];
-  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = max(r, lds4[i]);
-  return r;
-}
-
-// |x| max as bf16 bit patterns (magnitudes order like their bit patterns).
-__device__ __forceinline__ uint32_t absmax_bits8(uint4 v) {
-  uint32_t m = 0;
-  uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m = max(m, w[i] & 0x7FFFu);
-    m = max(m, (w[i] >> 16) & 0x7FFFu);
-  }
-  return m;
-}
 
 template <int FMT>
 struct Blk {
@@ -107,19 +74,17 @@ __device__ __forceinline__ uint32_t block_absmax(const uint4 (&v)[Blk<FMT>::V]) 
 template <int FMT>
 __device__ __forceinline__ void encode_store(const uint4 (&v)[Blk<FMT>::V], float st,
                                              uint8_t *cdst, uint8_t *sdst) {
-  const uint32_t abits = block_absmax<FMT>(v);
-  if (FMT == 0) {
-    const double q = (double)bf16_bits_to_f32(abits) / (6.0 * (double)st);
-    const uint32_t sbyte = e4m3_rne_sat(q);
-    const NvBlockEnc enc = nv_block_encoder(sbyte, st);
-    *(uint2 *)cdst = make_uint2(nv_encode8(enc, v[0]), nv_encode8(enc, v[1]));
-    *sdst = (uint8_t)sbyte;
+  uint32_t sbyte;
+  if constexpr (FMT == 0) {
+    uint2 c;
+    nv_encode_block(v[0], v[1], st, c, sbyte);
+    *(uint2 *)cdst = c;
   } else {
-    const int e = mx_exponent_from_bits(abits);
-    *(uint4 *)cdst = make_uint4(mx_encode8(e, v[0]), mx_encode8(e, v[1]), mx_encode8(e, v[2]),
-                                mx_encode8(e, v[3]));
-    *sdst = (uint8_t)(e + 127);
+    uint4 c;
+    mx_encode_block(v, c, sbyte);
+    *(uint4 *)cdst = c;
   }
+  *sdst = (uint8_t)sbyte;
 }
 
 template <int FMT>
@@ -183,32 +148,28 @@ __global__ __launch_bounds__(kThreads) void k_quant(
 
 // ------------------------------------------------------------------ small
 
-// Maximum over every workgroup of the grid (see the file comment). `sync`
-// holds {arrival counter, max word 0, max word 1}, zero-filled initially.
-__device__ __forceinline__ uint32_t grid_max_u32(uint32_t wg_max, uint32_t *sync,
-                                                 uint32_t *result_lds) {
-  if (threadIdx.x == 0) {
-    const uint32_t g = gridDim.x;
-    const uint32_t epoch =
-        __hip_atomic_load(&sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) / g;
-    uint32_t *slot = &sync[1 + (epoch & 1u)];
-    const uint32_t old = atomicMax(slot, wg_max);
-    // the arrival depends on the returned value, so it is issued only after
-    // the maximum has been performed
-    const uint32_t ticket = atomicAdd(&sync[0], old == 0xFFFFFFFFu ? 2u : 1u);
-    if (ticket == epoch * g)  // first arrival clears the next call's word
-      __hip_atomic_store(&sync[1 + ((epoch + 1u) & 1u)], 0u, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t target = (epoch + 1u) * g;
+// Maximum over every workgroup of the grid. slots[g] is workgroup g's word:
+// (call tag << 16) | its maximum's bf16 bits (< 2^15). A call's tag is one
+// more than the previous call's, read from the workgroup's own slot (every
+// call rewrites every slot; a zero-filled array is tag 0). Each workgroup
+// publishes its word with one device-coherent store; then thread t < grid
+// size polls slot t (bounded) until it carries this call's tag, and the
+// workgroup takes the maximum. The exchanged values travel in the polled
+// words themselves, so no cache writeback or fence is involved.
+__device__ __forceinline__ uint32_t grid_max_u32(uint32_t wg_max, uint32_t tag,
+                                                 uint32_t *slots, uint32_t *lds) {
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&slots[blockIdx.x], (tag << 16) | wg_max, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  uint32_t v = 0;
+  if (threadIdx.x < gridDim.x) {
     for (uint32_t it = 0; it < (1u << 22); ++it) {
-      const uint32_t now = __hip_atomic_load(&sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if ((int32_t)(now - target) >= 0) break;
-      __builtin_amdgcn_s_sleep(2);
+      v = __hip_atomic_load(&slots[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((v >> 16) == tag) break;
+      __builtin_amdgcn_s_sleep(1);
     }
-    *result_lds = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __syncthreads();
-  return *result_lds;
+  return block_max_u32(v & 0xFFFFu, lds);
 }
 
 // Single-launch quantization of a tensor of at most kActGrid * 256 * kActBpt
@@ -222,10 +183,13 @@ __global__ __launch_bounds__(kThreads) void k_quant_small(
     uint32_t *__restrict__ sync) {
   using K = Blk<FMT>;
   __shared__ uint32_t lds[4];
-  __shared__ uint32_t gmax;
   const int64_t nb = k / K::B, nb_pad = kt_n * K::BPF, total = rows_pad * nb_pad;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t tag = 0;
+  if (DYN)  // this call's tag, from the previous call's word of this workgroup
+    tag = ((__hip_atomic_load(&sync[blockIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 16) +
+           1u) & 0xFFFFu;
   uint4 v[kActBpt][K::V];
   uint32_t m = 0;
 #pragma unroll
@@ -244,7 +208,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_small(
   }
   float st = 1.0f;
   if (FMT == 0) {
-    if (DYN) st = tensor_scale_from_amax(bf16_bits_to_f32(grid_max_u32(block_max_u32(m, lds), sync, &gmax)));
+    if (DYN) st = tensor_scale_from_amax(bf16_bits_to_f32(grid_max_u32(block_max_u32(m, lds), tag, sync, lds)));
     else st = *static_scale;
     if (blockIdx.x == 0 && threadIdx.x == 0 && ts_out) *ts_out = st;
   }

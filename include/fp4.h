@@ -157,6 +157,12 @@ fp4_status fp4_linear(const void *x_bf16, int64_t m, const fp4_tensor *w,
                       const float *static_scale, void *y_bf16, void *workspace,
                       size_t workspace_bytes, hipStream_t stream);
 
+/* Number of kernel launches fp4_linear makes for this shape: 1 when the
+ * activation quantization is fused into the skinny GEMM (small M * K), 2 for
+ * quantize + GEMM, 3 when the quantizer needs a separate reduction launch
+ * (large NVFP4 activations with a dynamic scale). 0 for invalid arguments. */
+int32_t fp4_linear_launches(int32_t fmt, int64_t m, int64_t n, int64_t k, int32_t static_scale);
+
 /* Test aids (not on the hot path). */
 /* Copy a TILED tensor into a CANONICAL one of the same format/shape
  * (including the tensor scale when both pointers are set). */

@@ -110,3 +110,17 @@ def test_host_validation_rejects_before_launch():
     assert L.fp4_tensor_init(ctypes.byref(bad), fp4.NVFP4, fp4.CANONICAL, 4, 64, 4096, 8192, None) == 0
     assert L.fp4_gemm(ctypes.byref(bad), ctypes.byref(w), 4096, 32, None, 0, None) == 1
     assert b"tensor_scale" in L.fp4_last_error()
+
+
+def test_linear_launch_count():
+    L = fp4.lib()
+    # M = 1 decode shapes run as one fused launch
+    for k, n in ((5120, 5120), (5120, 17408), (17408, 5120)):
+        assert L.fp4_linear_launches(fp4.NVFP4, 1, n, k, 0) == 1
+        assert L.fp4_linear_launches(fp4.MXFP4, 1, n, k, 0) == 1
+    # larger activations: quantize + GEMM (NVFP4 dynamic may need a reduction launch)
+    assert L.fp4_linear_launches(fp4.NVFP4, 32, 5120, 5120, 0) == 2
+    assert L.fp4_linear_launches(fp4.NVFP4, 4096, 3072, 3072, 0) == 3
+    assert L.fp4_linear_launches(fp4.NVFP4, 4096, 3072, 3072, 1) == 2
+    assert L.fp4_linear_launches(fp4.MXFP4, 4096, 3072, 3072, 0) == 2
+    assert L.fp4_linear_launches(fp4.NVFP4, 4, 64, 40, 0) == 0

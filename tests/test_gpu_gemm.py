@@ -176,3 +176,21 @@ def test_workspace_reused_across_calls(fmt, m):
         y = bf16_out_to_f64(fp4.fp4_linear(to_dev(a), wq, workspace=ws))
         assert_gemm_close(y, c_ref, l_ref, f"call {call}")
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("m,k", [(1, 17408), (8, 5120), (16, 4096), (17, 2880), (64, 1024)])
+def test_linear_static_scale(m, k):
+    """fp4_linear with a caller-given per-tensor scale (saturating block scales),
+    on both the fused single-launch path and the quantize-then-GEMM path."""
+    n = 272
+    a, w = synth.prefill_inputs("k", seed=2, m=m)
+    a = a[:, :k] if a.shape[1] >= k else synth.student_t((m, k), 3.0, 4.0, 2, 77, plant=3616.0, n_plant=2)
+    w = synth.normal((n, k), 0.02, 2, 78)
+    st = float(np.float32(0.25))
+    qa_ref = oracle.quantize_nvfp4(a, mode=oracle.STATIC, static_scale=st)
+    qw_ref = oracle.quantize_nvfp4(w)
+    c_ref, l_ref = oracle.gemm(qa_ref, qw_ref)
+    wq = fp4.fp4_quantize_weight(to_dev(w), 0)
+    y = bf16_out_to_f64(fp4.fp4_linear(to_dev(np.ascontiguousarray(a)), wq,
+                                       static_scale=torch.tensor([st], dtype=torch.float32, device="cuda")))
+    assert_gemm_close(y, c_ref, l_ref, f"static-scale linear {m}x{k}")
