@@ -101,11 +101,16 @@ def main():
     step_w_bytes = sum(n * (k // 2 + k // (16 if fmt == 0 else 32)) for (k, n) in shapes)
     copies = max(1, -(-ROTATE_BYTES // step_w_bytes)) if args.workload == "decode" else 1
     weights, w_host, a_host = {}, {}, {}
+    layer_of = {kn: name for name, kn in synth.PREFILL_LAYERS.items()}
     for (k, n) in shapes:
         if args.workload == "decode":
             w_bits = synth.decode_inputs(1, k, n, seed=0)[1]
+        elif args.workload == "prefill":
+            w_bits = synth.prefill_inputs(layer_of[(k, n)], seed=0, m=16)[1]
+        elif args.workload == "square8192":
+            w_bits = synth.square_inputs(k, seed=0)[1]
         else:
-            w_bits = synth.normal((n, k), 0.02, 0, 500 + n + k)
+            w_bits = synth.single_gemm_inputs(0)[1]
         w_host[(k, n)] = w_bits
         w_dev = to_dev(w_bits)
         weights[(k, n)] = [fp4.fp4_quantize_weight(w_dev, fmt) for _ in range(copies)]
@@ -114,8 +119,12 @@ def main():
     for (m, k, n) in configs:
         if args.workload == "decode":
             a_bits = synth.normal((m, k), 1.0, 0, 2 * k + 1)   # the activation decode_inputs draws
+        elif args.workload == "prefill":
+            a_bits = synth.prefill_inputs(layer_of[(k, n)], seed=0, m=m)[0]
+        elif args.workload == "square8192":
+            a_bits = synth.square_inputs(k, seed=0)[0]
         else:
-            a_bits = synth.normal((m, k), 1.0, 0, 600 + m + k)
+            a_bits = synth.single_gemm_inputs(0)[0]
         a_host[(m, k, n)] = a_bits
         xs[(m, k, n)] = to_dev(a_bits)
         outs[(m, k, n)] = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
@@ -211,8 +220,11 @@ def main():
         else:
             # the activation layout fp4_linear uses internally (fragment-tiled)
             qa = fp4.fp4_quantize_act(xs[cfg], fmt, layout=fp4.TILED)
-            name = ("k_gemm_decode<%s,MG=%d>" % (args.fmt, 1 if m <= 16 else 2)) if m <= 32 \
-                else "k_gemm_prefill<%s>" % args.fmt
+            if m <= 32:
+                name = "k_gemm_decode<%s,MG=%d>" % (args.fmt, 1 if m <= 16 else 2)
+            else:   # LDS-staged tiles; 256 x 256 when that fills the 256 CUs
+                big = -(-m // 256) * -(-n // 256) >= 256
+                name = "k_gemm_tile<%s,%s>" % (args.fmt, "256x256" if big else "128x128")
             us = graph_time(lambda r: fp4.fp4_gemm(qa, wl[r % copies], out=outs[cfg]), reps)
             nbytes = w_bytes + m * (k // 2 + k // bs) + 2 * m * n  # W + FP4 A + bf16 C
         d = kern.setdefault(name, {"launches": 0, "us": 0.0, "bytes": 0.0, "flops": 0.0})

@@ -141,7 +141,11 @@ fp4_status run_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c, int64_t l
   g.w_ts = w->tensor_scale;
   g.m = a->rows; g.n = w->rows; g.k = a->cols;
   g.c = (uint16_t *)c; g.ldc = ldc;
-  hipError_t e = g.m <= kDecodeMaxM ? launch_gemm_decode(g, stream) : launch_gemm_prefill(g, stream);
+  // skinny M: stream W once; large M with tiled activations: LDS-staged
+  // tiles; large M with canonical activations: direct-load tiles
+  hipError_t e = g.m <= kDecodeMaxM ? launch_gemm_decode(g, stream)
+                 : g.a_tiled        ? launch_gemm_tile(g, 0, stream)
+                                    : launch_gemm_prefill(g, stream);
   if (e != hipSuccess) return hip_fail(e, "gemm launch");
   return FP4_OK;
 }

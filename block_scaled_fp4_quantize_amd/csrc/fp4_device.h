@@ -42,6 +42,22 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// The GEMM output scale alpha = S_tA * S_tW (NVFP4; 1 for MXFP4), held as
+// m * 2^e with m = fl(mA * mW) from the two scales' frexp mantissas, so that
+// scaling an accumulator neither underflows nor overflows in an intermediate
+// step: out = ldexp(acc * m, e), the power of two applied exactly (rounded
+// once if the result is subnormal).
+struct Alpha {
+  float m;
+  int e;
+};
+__device__ __forceinline__ Alpha make_alpha(float sa, float sw) {
+  int ea, ew;
+  const float ma = frexpf(sa, &ea), mw = frexpf(sw, &ew);
+  return Alpha{ma * mw, ea + ew};
+}
+__device__ __forceinline__ float apply_alpha(float v, Alpha a) { return ldexpf(v * a.m, a.e); }
+
 // E4M3 byte (sign clear, not NaN) -> exact FP32 value.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
   uint32_t e = (byte >> 3) & 15u, m = byte & 7u;

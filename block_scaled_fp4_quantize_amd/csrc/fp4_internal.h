@@ -64,6 +64,11 @@ struct GemmArgs {
 hipError_t launch_gemm_prefill(const GemmArgs &g, hipStream_t stream);
 hipError_t launch_gemm_decode(const GemmArgs &g, hipStream_t stream);
 
+// LDS-staged GEMM for large M; both operands fragment-tiled. cfg selects the
+// workgroup tile (88: 256 x 256, 44: 128 x 128; 0: by shape).
+int gemm_tile_config(int fmt, int64_t m, int64_t n);
+hipError_t launch_gemm_tile(const GemmArgs &g, int cfg, hipStream_t stream);
+
 // Single-launch linear (activation quantization fused) for small activations.
 constexpr int kFusedMaxM = 16;
 constexpr int64_t kFusedMaxMK = 65536;        // M * K_pad bound (LDS staging, MXFP4)

@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256) void k_gemm_prefill(
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma_nv(ah[i], wh[j], acc[i][j]);
     }
   }
-  const float alpha = FMT == 0 ? a_ts[0] * w_ts[0] : 1.0f;
+  const Alpha alpha = FMT == 0 ? make_alpha(a_ts[0], w_ts[0]) : Alpha{1.0f, 0};
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256) void k_gemm_prefill(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         int row = m0 + 16 * i + 4 * lc + r;
-        if (row < m) c[(int64_t)row * ldc + col] = f32_to_bf16_rne(acc[i][j][r] * alpha);
+        if (row < m) c[(int64_t)row * ldc + col] = f32_to_bf16_rne(apply_alpha(acc[i][j][r], alpha));
       }
     }
 }
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(
   __syncthreads();
   const int tg = threadIdx.x >> 6;  // accumulator group reduced by this wave
   if (tg >= MG) return;
-  const float alpha = FMT == 0 ? a_ts[0] * w_ts[0] : 1.0f;
+  const Alpha alpha = FMT == 0 ? make_alpha(a_ts[0], w_ts[0]) : Alpha{1.0f, 0};
   const int col = 16 * tg + (lane & 15);  // activation row m
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(
 #pragma unroll
     for (int w2 = 1; w2 < NW; ++w2) v += red[w2][tg][r][lane];
     const int row = nt * 16 + 4 * (lane >> 4) + r;  // output column n
-    if (col < m && row < n) c[(int64_t)col * ldc + row] = f32_to_bf16_rne(v * alpha);
+    if (col < m && row < n) c[(int64_t)col * ldc + row] = f32_to_bf16_rne(apply_alpha(v, alpha));
   }
 }
 
@@ -368,14 +368,14 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_linear_decode(
   for (int r = 0; r < 4; ++r) red[wave][r][lane] = acc[r];
   __syncthreads();
   if (wave != 0) return;
-  const float alpha = FMT == 0 ? st * w_ts[0] : 1.0f;
+  const Alpha alpha = FMT == 0 ? make_alpha(st, w_ts[0]) : Alpha{1.0f, 0};
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     float sum = red[0][r][lane];
 #pragma unroll
     for (int w2 = 1; w2 < NW; ++w2) sum += red[w2][r][lane];
     const int ncol = nt * 16 + 4 * lc + r;
-    if (row < m && ncol < n) y[(int64_t)row * ldy + ncol] = f32_to_bf16_rne(sum * alpha);
+    if (row < m && ncol < n) y[(int64_t)row * ldy + ncol] = f32_to_bf16_rne(apply_alpha(sum, alpha));
   }
 }
 

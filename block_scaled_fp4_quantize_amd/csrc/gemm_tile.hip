@@ -1,0 +1,388 @@
+// gemm_tile.hip -- LDS-staged W4A4 GEMM for large M (prefill and square
+// shapes), gfx950.
+//
+// Same product as the other GEMM kernels: C[m, n] = alpha * sum_k
+// (q_a s_a)[m, k] (q_w s_w)[n, k], FP32 accumulation, bf16 output (forum post
+// on a standalone FP4 GEMM library, opening paragraphs: weights quantized once
+// into a cache, activations per call).
+//
+// Both operands are in the fragment-tiled layout (16 rows x 128 values per
+// fragment, 1 KB of codes in the matrix instruction's lane order, then the
+// fragment's scale bytes in a separate array), so a stage of the K loop is a
+// set of whole 1 KB fragments. They are copied global -> LDS with the direct
+// LDS load (global_load_lds_dwordx4: lane i of the wave writes bytes
+// 16i..16i+15 of a 1 KB LDS run), which needs no registers and no LDS store
+// instructions. A four-stage ring: while stage s is consumed, the copies of
+// stages s+1 and s+2 are in flight and those of s+3 are issued; the copies
+// and the LDS reads of the next stage are spread between the matrix
+// instructions so the matrix unit is not left idle while they issue.
+//
+// Workgroup: four waves in a 2 x 2 grid; wave tile TM x TN fragments
+// (16 TM rows of A by 16 TN rows of W). The weight fragment is the matrix
+// instruction's A operand and the activation fragment its B operand, so each
+// lane ends with four consecutive output columns of one row (one 8-byte
+// store).
+//   MXFP4: V_MFMA_SCALE_F32_16X16X128_F8F6F4, E8M0 byte per lane.
+//   NVFP4: exact f16 dequantization of each lane's codes (q * s_b has at most
+//          6 significant bits) and V_MFMA_F32_16X16X32_F16, as in the other
+//          kernels.
+// Workgroups are numbered so that consecutive tiles land on the same XCD
+// (the hardware deals workgroups to the eight XCDs round-robin), and tiles are
+// walked in groups of tile rows, so the tiles an XCD runs at one time share
+// A and W K-slices in that XCD's L2.
+#include "fp4_device.h"
+#include "fp4_internal.h"
+
+#include <type_traits>
+
+// clang notes that M0 is a reserved register when it appears in an inline
+// assembly clobber list (the direct-LDS copies below set it); no
+// compiler-generated code in these kernels uses M0.
+#pragma clang diagnostic ignored "-Winline-asm"
+
+namespace fp4i {
+using namespace fp4d;
+
+namespace {
+
+constexpr int kStages = 4;
+constexpr int kXcds = 8;
+constexpr int kGroupRows = 8;
+
+template <int FMT, int TM, int TN>
+struct TileCfg {
+  static constexpr int FA = 2 * TM, FW = 2 * TN, NF = FA + FW;  // fragments per stage
+  static constexpr int SCB = FMT == 0 ? 128 : 64;                // scale bytes per fragment
+  static constexpr int SC_DW = NF * SCB / 4;                     // scale dwords per stage
+  // scale copies (64 dwords each), rounded up so every wave issues as many
+  static constexpr int SC_INSTR = ((SC_DW + 63) / 64 + 3) / 4 * 4;
+  static constexpr int CODE_BYTES = NF * kFragCodeBytes;
+  static constexpr int STAGE = CODE_BYTES + SC_INSTR * 256;
+  // copies per wave per stage: NF / 4 code fragments + SC_INSTR / 4 scale runs
+  static constexpr int PS = NF / 4 + SC_INSTR / 4;
+  static_assert(NF % 4 == 0, "fragments per stage must split over four waves");
+  static_assert(2 * PS < 64, "vmcnt range");
+};
+
+// s_waitcnt vmcnt(N), other counters left alone (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for LDS only: this wave's LDS reads are complete, then
+// s_barrier. (The LDS copies are waited for explicitly with vmcnt; a fence
+// here would also wait for every copy still in flight.) The wait is the
+// builtin so that the compiler's own counter bookkeeping sees it; the empty
+// asm statements keep the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt at their maxima
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Direct global -> LDS copies: lane i writes bytes [size*i, size*i + size) of
+// the wave's LDS run starting at the wave-uniform LDS address dst (M0). They
+// are written as assembly so that the compiler does not treat every later LDS
+// read as dependent on every copy still in flight (it cannot tell the ring's
+// stages apart and would wait for all of them); the K loop waits for exactly
+// the copies it needs with vmcnt. The copies have no register results.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
+}
+__device__ __forceinline__ void lds_copy16(const void *src, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(dst) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_copy4(const void *src, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(dst) : "memory", "m0");
+}
+
+__device__ __forceinline__ v4f mma_mx(uint4 w, uint4 a, v4f c, uint32_t sw, uint32_t sa) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(frag_v8i(w), frag_v8i(a), c, 4, 4, 0,
+                                                           (int)sw, 0, (int)sa);
+}
+
+template <int S>
+using Stage = std::integral_constant<int, S>;
+
+// Two floats -> two bf16 (round to nearest even; v_cvt_pk_bf16_f32), packed.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){lo, hi}, b2));
+}
+
+template <int FMT, int TM, int TN>
+__global__ __launch_bounds__(256) void k_gemm_tile(
+    const uint8_t *__restrict__ a_codes, const uint8_t *__restrict__ a_sc,
+    const float *__restrict__ a_ts, const uint8_t *__restrict__ w_codes,
+    const uint8_t *__restrict__ w_sc, const float *__restrict__ w_ts, int m, int n, int kt_n,
+    int ga_n, int nt_n, int tiles_m, int tiles_n, uint16_t *__restrict__ c, int64_t ldc,
+    int vec_store) {
+  using C = TileCfg<FMT, TM, TN>;
+  // One LDS array per ring stage and a K loop unrolled four times, so every
+  // stage buffer is a compile-time constant in its body (with a run-time
+  // stage index the accumulators were shuffled between register files).
+  __shared__ __align__(1024) uint8_t lds0[C::STAGE];
+  __shared__ __align__(1024) uint8_t lds1[C::STAGE];
+  __shared__ __align__(1024) uint8_t lds2[C::STAGE];
+  __shared__ __align__(1024) uint8_t lds3[C::STAGE];
+  auto stage_ptr = [&](auto sc) __attribute__((always_inline)) -> uint8_t * {
+    constexpr int S = decltype(sc)::value % kStages;
+    if constexpr (S == 0) return lds0;
+    else if constexpr (S == 1) return lds1;
+    else if constexpr (S == 2) return lds2;
+    else return lds3;
+  };
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+
+  // ---- tile of this workgroup (XCD-contiguous, grouped by tile rows)
+  int tm, tn;
+  {
+    const int nwg = tiles_m * tiles_n, b = blockIdx.x;
+    const int xcd = b % kXcds, slot = b / kXcds, q = nwg / kXcds, r = nwg % kXcds;
+    const int L = xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+    const int per_group = kGroupRows * tiles_n, grp = L / per_group, first = grp * kGroupRows;
+    const int gsz = min(tiles_m - first, kGroupRows), in = L - grp * per_group;
+    tm = first + in % gsz;
+    tn = in / gsz;
+  }
+  const int g0 = tm * C::FA, n0 = tn * C::FW;
+
+  // ---- this wave's share of every stage's copies: code fragments
+  // wave + 4u (one 16-byte copy per lane, 1 KB per wave), then scale runs
+  // wave + 4v (one dword per lane). Fragment rows past the operand (A rows
+  // >= m, W rows >= n, rounded to 16) copy the last valid fragment instead:
+  // they only feed output rows/columns that are never stored, and every wave
+  // issues the same number of copies at every stage.
+  constexpr int NCP = C::NF / 4, NSP = C::SC_INSTR / 4;
+  auto frag_row = [&](int f, const uint8_t *a, const uint8_t *w, int bytes)
+      __attribute__((always_inline)) -> const uint8_t * {
+    return f < C::FA ? a + (int64_t)min(g0 + f, ga_n - 1) * kt_n * bytes
+                     : w + (int64_t)min(n0 + f - C::FA, nt_n - 1) * kt_n * bytes;
+  };
+  const uint8_t *code_src[NCP];
+#pragma unroll
+  for (int u = 0; u < NCP; ++u)
+    code_src[u] = frag_row(wave + 4 * u, a_codes, w_codes, kFragCodeBytes) + lane * 16;
+  const uint8_t *sc_src[NSP];
+#pragma unroll
+  for (int v = 0; v < NSP; ++v) {
+    const int p = min(64 * (wave + 4 * v) + lane, C::SC_DW - 1);  // scale dword of the stage
+    const int f = p / (C::SCB / 4), pc = p % (C::SCB / 4);
+    sc_src[v] = frag_row(f, a_sc, w_sc, C::SCB) + pc * 4;
+  }
+
+  // copy unit u of this wave's share of stage kt: units 0..NCP-1 are code
+  // fragments, NCP..NCP+NSP-1 scale runs
+  constexpr int NU = NCP + NSP;
+  auto issue_unit = [&](uint8_t *st, int kt, int u) __attribute__((always_inline)) {
+    if (u < NCP)
+      lds_copy16(code_src[u] + (int64_t)kt * kFragCodeBytes,
+                 lds_addr(st + (wave + 4 * u) * kFragCodeBytes));
+    else
+      lds_copy4(sc_src[u - NCP] + (int64_t)kt * C::SCB,
+                lds_addr(st + C::CODE_BYTES + (wave + 4 * (u - NCP)) * 256));
+  };
+  auto issue = [&](auto sc, int kt) __attribute__((always_inline)) {
+    uint8_t *st = stage_ptr(sc);
+#pragma unroll
+    for (int u = 0; u < NU; ++u) issue_unit(st, kt, u);
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int fa0 = wm * TM, fw0 = C::FA + wn * TN;  // this wave's first fragments in a stage
+
+  v4f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  struct Ops {
+    uint4 aq[TM], wq[TN];
+    uint32_t as[TM], ws[TN];
+  };
+  // read unit r of a stage into registers: A fragment r (r < TM) or W
+  // fragment r - TM, with its scale bytes
+  auto read_unit = [&](const uint8_t *st, Ops &o, int r) __attribute__((always_inline)) {
+    const int f = r < TM ? fa0 + r : fw0 + r - TM;
+    const uint4 q = *(const uint4 *)(st + f * kFragCodeBytes + lane * 16);
+    const uint32_t sv = FMT == 0 ? (uint32_t) * (const uint16_t *)(st + C::CODE_BYTES + f * 128 + lane * 2)
+                                 : (uint32_t)st[C::CODE_BYTES + f * 64 + lane];
+    if (r < TM) {
+      o.aq[r] = q;
+      o.as[r] = sv;
+    } else {
+      o.wq[r - TM] = q;
+      o.ws[r - TM] = sv;
+    }
+  };
+  auto read = [&](auto sc, Ops &o) __attribute__((always_inline)) {
+    const uint8_t *st = stage_ptr(sc);
+#pragma unroll
+    for (int r = 0; r < TM + TN; ++r) read_unit(st, o, r);
+  };
+
+  auto mma = [&](const Ops &o) __attribute__((always_inline)) {
+    if constexpr (FMT == 1) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mma_mx(o.wq[j], o.aq[i], acc[i][j], o.ws[j], o.as[i]);
+    } else {
+      // K sub-block g: dword g of every lane's 16 code bytes (values
+      // 8g..8g+7 of its 32), the same permutation of K for both operands.
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        h8v ah[TM], wh[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const uint32_t d = g == 0 ? o.aq[i].x : g == 1 ? o.aq[i].y : g == 2 ? o.aq[i].z : o.aq[i].w;
+          ah[i] = __builtin_bit_cast(h8v, nv_dequant8_u4(d, g < 2 ? (o.as[i] & 0xFFu) : (o.as[i] >> 8)));
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const uint32_t d = g == 0 ? o.wq[j].x : g == 1 ? o.wq[j].y : g == 2 ? o.wq[j].z : o.wq[j].w;
+          wh[j] = __builtin_bit_cast(h8v, nv_dequant8_u4(d, g < 2 ? (o.ws[j] & 0xFFu) : (o.ws[j] >> 8)));
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh[j], ah[i], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  // ---- K loop over a four-stage ring. Stages kt+1 and kt+2 are in flight
+  // while stage kt is waited for; stage kt+3 is issued after the barrier into
+  // the buffer stage kt-1 used. Past the last stage the copies repeat the
+  // last stage into buffers nobody reads any more, so every iteration issues
+  // the same copies and waits for the same count (no branches in the loop
+  // body). MXFP4 reads stage kt+1 into registers while stage kt's matrix
+  // instructions run.
+  auto src_kt = [&](int kt) __attribute__((always_inline)) { return min(kt, kt_n - 1); };
+  issue(Stage<0>{}, 0);
+  issue(Stage<1>{}, src_kt(1));
+  issue(Stage<2>{}, src_kt(2));
+
+  Ops ops[2];
+  constexpr bool kDouble = FMT == 1;
+  if constexpr (kDouble) {
+    wait_vm<2 * C::PS>();
+    lds_barrier();
+    read(Stage<0>{}, ops[0]);
+  }
+  auto body = [&](auto sc, int kt) __attribute__((always_inline)) {
+    constexpr int S = decltype(sc)::value;
+    if constexpr (kDouble) {
+      wait_vm<C::PS>();  // stage kt+1 has landed (kt+2 may be in flight)
+      lds_barrier();
+      // Stage kt's matrix instructions, with the copies of stage kt+3 and the
+      // register reads of stage kt+1 spread between them: each copy or LDS
+      // read issues while a matrix instruction runs instead of holding the
+      // matrix unit idle. The scheduling barriers keep that order. (After the
+      // last stage the reads fetch values that are never used.)
+      constexpr int NQ = TM * TN;
+      constexpr int DMA_EVERY = NQ / NU > 0 ? NQ / NU : 1;
+      constexpr int RD_EVERY = NQ / (TM + TN) > 0 ? NQ / (TM + TN) : 1;
+      const int kcopy = src_kt(kt + 3);
+      uint8_t *st_copy = stage_ptr(Stage<S + 3>{});
+      const uint8_t *st_read = stage_ptr(Stage<S + 1>{});
+      const Ops &cur = ops[S & 1];
+      Ops &nxt = ops[(S + 1) & 1];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        if (q % DMA_EVERY == 0 && q / DMA_EVERY < NU) issue_unit(st_copy, kcopy, q / DMA_EVERY);
+        if (q % RD_EVERY == RD_EVERY - 1 && q / RD_EVERY < TM + TN) read_unit(st_read, nxt, q / RD_EVERY);
+        const int i = q / TN, j = q % TN;
+        acc[i][j] = mma_mx(cur.wq[j], cur.aq[i], acc[i][j], cur.ws[j], cur.as[i]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      wait_vm<2 * C::PS>();  // stage kt has landed (kt+1, kt+2 may be in flight)
+      lds_barrier();
+      issue(Stage<S + 3>{}, src_kt(kt + 3));
+      read(sc, ops[0]);
+      mma(ops[0]);
+    }
+  };
+  for (int kt = 0; kt < kt_n; kt += kStages) {
+    body(Stage<0>{}, kt);
+    if (kt + 1 < kt_n) body(Stage<1>{}, kt + 1);
+    if (kt + 2 < kt_n) body(Stage<2>{}, kt + 2);
+    if (kt + 3 < kt_n) body(Stage<3>{}, kt + 3);
+  }
+  // every copy has landed before the workgroup can end (its LDS is then
+  // handed to the next workgroup)
+  wait_vm<0>();
+
+  // ---- epilogue: lane holds C[row][col0 .. col0+3] of each 16 x 16 tile
+  const Alpha alpha = FMT == 0 ? make_alpha(a_ts[0], w_ts[0]) : Alpha{1.0f, 0};
+  const int rl = lane & 15, cl = 4 * (lane >> 4);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int row = (g0 + fa0 + i) * 16 + rl;
+    if (row >= m) continue;
+    uint16_t *crow = c + (int64_t)row * ldc;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col0 = (n0 + wn * TN + j) * 16 + cl;
+      const v4f &a = acc[i][j];
+      const uint32_t lo = pack_bf16x2(apply_alpha(a[0], alpha), apply_alpha(a[1], alpha));
+      const uint32_t hi = pack_bf16x2(apply_alpha(a[2], alpha), apply_alpha(a[3], alpha));
+      if (vec_store && col0 + 3 < n) {
+        *(uint2 *)(crow + col0) = make_uint2(lo, hi);
+      } else {
+        if (col0 < n) crow[col0] = (uint16_t)lo;
+        if (col0 + 1 < n) crow[col0 + 1] = (uint16_t)(lo >> 16);
+        if (col0 + 2 < n) crow[col0 + 2] = (uint16_t)hi;
+        if (col0 + 3 < n) crow[col0 + 3] = (uint16_t)(hi >> 16);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+int gemm_tile_config(int fmt, int64_t m, int64_t n) {
+  // 256 x 256 tiles when they give every CU (256) at least one tile; 128 x
+  // 128 otherwise (measured on the prefill and square shapes: the smaller
+  // tile wins whenever the larger one leaves CUs idle).
+  (void)fmt;
+  const int64_t t88 = ((m + 255) / 256) * ((n + 255) / 256);
+  return t88 >= 256 ? 88 : 44;
+}
+
+hipError_t launch_gemm_tile(const GemmArgs &g, int cfg, hipStream_t stream) {
+  const int kt_n = (int)(k_pad(g.k) / kFragK);
+  const int ga_n = (int)(round_up(g.m, 16) / 16);
+  const int nt_n = (int)(round_up(g.n, 16) / 16);
+  if (cfg == 0) cfg = gemm_tile_config(g.fmt, g.m, g.n);
+  const int bm = cfg == 88 ? 256 : 128, bn = bm;
+  const int tiles_m = (int)((g.m + bm - 1) / bm), tiles_n = (int)((g.n + bn - 1) / bn);
+  const int vec = (g.ldc % 4 == 0) && ((uintptr_t)g.c % 8 == 0);
+  dim3 grid((unsigned)(tiles_m * tiles_n));
+#define FP4_TILE(F, A, B)                                                                       \
+  hipLaunchKernelGGL((k_gemm_tile<F, A, B>), grid, dim3(256), 0, stream, g.a_codes, g.a_scales, \
+                     g.a_ts, g.w_codes, g.w_scales, g.w_ts, (int)g.m, (int)g.n, kt_n, ga_n,      \
+                     nt_n, tiles_m, tiles_n, g.c, g.ldc, vec)
+  if (g.fmt == 1) {
+    if (cfg == 88) FP4_TILE(1, 8, 8);
+    else FP4_TILE(1, 4, 4);
+  } else {
+    if (cfg == 88) FP4_TILE(0, 8, 8);
+    else FP4_TILE(0, 4, 4);
+  }
+#undef FP4_TILE
+  return hipGetLastError();
+}
+
+}  // namespace fp4i

@@ -194,3 +194,23 @@ def test_linear_static_scale(m, k):
     y = bf16_out_to_f64(fp4.fp4_linear(to_dev(np.ascontiguousarray(a)), wq,
                                        static_scale=torch.tensor([st], dtype=torch.float32, device="cuda")))
     assert_gemm_close(y, c_ref, l_ref, f"static-scale linear {m}x{k}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m", [1, 8, 32, 300])
+def test_extreme_tensor_scales(fmt, m):
+    """Operands scaled by 2^-60 and 2^-70: the NVFP4 output scale S_tA * S_tW
+    is below FP32's range (~2^-155) while the outputs themselves are around
+    2^-130 (bf16 subnormals); every path (fused, decode, tiled) must keep them."""
+    k, n = 1024, 272
+    a = synth.normal((m, k), 1.0, 31, m)
+    w = synth.normal((n, k), 0.02, 31, 1000 + m)
+    a = synth.bf16_bits(synth.bf16_to_f32(a) * np.float32(2.0 ** -60))
+    w = synth.bf16_bits(synth.bf16_to_f32(w) * np.float32(2.0 ** -70))
+    f = F[fmt]
+    qa_ref, qw_ref = oracle.quantize(f, a), oracle.quantize(f, w)
+    c_ref, l_ref = oracle.gemm(qa_ref, qw_ref)
+    assert np.abs(c_ref).max() > 2.0 ** -133, "outputs must not all sit below the tolerance floor"
+    wq = fp4.fp4_quantize_weight(to_dev(w), f)
+    y = bf16_out_to_f64(fp4.fp4_linear(to_dev(a), wq))
+    assert_gemm_close(y, c_ref, l_ref, f"tiny scales m={m}")

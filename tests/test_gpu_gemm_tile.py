@@ -1,0 +1,167 @@
+"""GPU parity of the LDS-staged GEMM for large M (both operands fragment-tiled).
+
+fp4_gemm takes this kernel when M > 32 and the activations are in the tiled
+layout (the layout fp4_linear quantizes into). The cases cover each workgroup
+tile (256x256 and 128x128, chosen by the output's shape), ragged M and
+N, and K loops of 1, 2, 3, 4, 5 and 33 steps of 128 (the ring's prologue and
+the unrolled loop's tails). Full-size prefill and square shapes are checked on
+sampled outputs against the oracle's k-ordered binary64 sums.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp4_quantize_amd as fp4
+import oracle
+import synth
+from tests.gpu_helpers import F, assert_gemm_close, bf16_out_to_f64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+FMTS = ["nvfp4", "mxfp4"]
+
+
+def tile_config(m, n):
+    """The workgroup tile the library picks for an M x N output (256 CUs)."""
+    return 88 if -(-m // 256) * -(-n // 256) >= 256 else 44
+
+
+def _tiled_case(fmt, a_bits, w_bits, what):
+    m, k = a_bits.shape
+    n = w_bits.shape[0]
+    print(f"[tile] {what} fmt={fmt} m={m} n={n} k={k} cfg={tile_config(m, n)}", flush=True)
+    f = F[fmt]
+    qa_ref, qw_ref = oracle.quantize(f, a_bits), oracle.quantize(f, w_bits)
+    c_ref, l_ref = oracle.gemm(qa_ref, qw_ref)
+    wq = fp4.fp4_quantize_weight(to_dev(w_bits), f)
+    x = to_dev(a_bits)
+    qa = fp4.fp4_quantize_act(x, f, layout=fp4.TILED)
+    c = bf16_out_to_f64(fp4.fp4_gemm(qa, wq))
+    assert_gemm_close(c, c_ref, l_ref, what + " gemm (tiled A)")
+    y = bf16_out_to_f64(fp4.fp4_linear(x, wq))
+    assert_gemm_close(y, c_ref, l_ref, what + " linear")
+    return c
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m,n,k", [
+    (4096, 4096, 256),      # 256 x 256 tiles, 2 K steps
+    (4100, 4104, 384),      # 256 x 256 tiles, ragged M and N, 3 K steps
+    (4096, 3072, 640),      # 128 x 128 tiles, 5 K steps
+    (4111, 2056, 128),      # 128 x 128 tiles, ragged, 1 K step
+    (520, 1000, 4160),      # 128 x 128 tiles, 33 K steps (K tail 64)
+    (33, 17, 512),          # one partial 128 x 128 tile, 4 K steps
+])
+def test_tile_configs(fmt, m, n, k):
+    a = synth.normal((m, k), 1.0, 21, m * 31 + k)
+    w = synth.normal((n, k), 0.02, 21, n * 17 + k)
+    _tiled_case(fmt, a, w, f"tile cfg {tile_config(m, n)}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_tile_outliers_and_zero_rows(fmt):
+    """Planted +-3616 outliers and whole zero rows/blocks in A and W."""
+    m, n, k = 300, 700, 1024
+    a = synth.student_t((m, k), 3.0, 4.0, 22, 1, plant=3616.0, n_plant=8)
+    w = synth.normal((n, k), 0.02, 22, 2)
+    a[5] = 0
+    a[:, 64:96] = 0
+    w[13] = 0
+    _tiled_case(fmt, a, w, "outliers + zero rows")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_tile_all_ones_closed_form(fmt):
+    """Every value 1.0 through the tiled path: C = K exactly."""
+    m, n, k = 260, 300, 2048
+    a = np.full((m, k), 0x3F80, np.uint16)
+    w = np.full((n, k), 0x3F80, np.uint16)
+    c = _tiled_case(fmt, a, w, "all ones")
+    assert np.all(c == k)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_tile_unaligned_output_pitch(fmt):
+    """An output row pitch that is not a multiple of 4 elements takes the
+    element-wise stores; the result is the same as with a dense output."""
+    m, n, k = 100, 130, 512
+    f = F[fmt]
+    a = synth.normal((m, k), 1.0, 23, 1)
+    w = synth.normal((n, k), 0.02, 23, 2)
+    wq = fp4.fp4_quantize_weight(to_dev(w), f)
+    qa = fp4.fp4_quantize_act(to_dev(a), f, layout=fp4.TILED)
+    dense = fp4.fp4_gemm(qa, wq)
+    big = torch.full((m, n + 3), 7.0, dtype=torch.bfloat16, device="cuda")
+    view = big[:, :n]
+    fp4.fp4_gemm(qa, wq, out=view)
+    torch.cuda.synchronize()
+    assert torch.equal(view, dense)
+    assert torch.all(big[:, n:] == 7.0), "stores past N"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_tile_deterministic_and_graph(fmt):
+    """Two eager calls agree bit for bit, and so does every replay of a graph
+    holding the call (with eager work between replays)."""
+    m, n, k = 1024, 2048, 1024
+    f = F[fmt]
+    a = synth.normal((m, k), 1.0, 24, 1)
+    w = synth.normal((n, k), 0.02, 24, 2)
+    wq = fp4.fp4_quantize_weight(to_dev(w), f)
+    x = to_dev(a)
+    ws = torch.zeros(fp4.fp4_linear_workspace_bytes(f, m, n, k), dtype=torch.uint8, device="cuda")
+    e1 = fp4.fp4_linear(x, wq, workspace=ws).clone()
+    e2 = fp4.fp4_linear(x, wq, workspace=ws).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(e1, e2)
+    out = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fp4.fp4_linear(x, wq, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fp4.fp4_linear(x, wq, out=out, workspace=ws)
+    for rep in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, e1), f"replay {rep} differs"
+        assert torch.equal(fp4.fp4_linear(x, wq), e1)
+
+
+def _sampled_full(fmt, a, w, what, nsamp=4096, seed=0):
+    m, k = a.shape
+    n = w.shape[0]
+    print(f"[tile-full] {what} fmt={fmt} m={m} n={n} k={k}", flush=True)
+    f = F[fmt]
+    qa_ref, qw_ref = oracle.quantize(f, a), oracle.quantize(f, w)
+    wq = fp4.fp4_quantize_weight(to_dev(w), f)
+    y = fp4.fp4_linear(to_dev(a), wq)
+    rng = np.random.default_rng(seed + m + n + k)
+    rows = rng.integers(0, m, nsamp)
+    cols = rng.integers(0, n, nsamp)
+    # include the corners of the output
+    rows[:4] = [0, 0, m - 1, m - 1]
+    cols[:4] = [0, n - 1, 0, n - 1]
+    c_ref, l_ref = oracle.gemm_sampled(qa_ref, qw_ref, rows, cols)
+    yv = bf16_out_to_f64(y)[rows, cols]
+    assert_gemm_close(yv, c_ref, l_ref, what)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("layer", list(synth.PREFILL_LAYERS))
+def test_prefill_full_size_sampled(fmt, layer):
+    """Llama-style 3B block prefill GEMMs (M = 4096, t(3)*4 activations with
+    planted 3616 outliers), as the benchmark runs them."""
+    a, w = synth.prefill_inputs(layer, seed=0)
+    _sampled_full(fmt, a, w, f"prefill {layer}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_square_8192_sampled(fmt):
+    """M = N = K = 8192, operands ~N(0, 1)."""
+    a, w = synth.square_inputs(8192, seed=0)
+    _sampled_full(fmt, a, w, "square 8192")
