@@ -49,6 +49,12 @@ def parse():
     p.add_argument("--copy-mib", type=int, default=0,
                    help="also run one plain device copy of this many MiB (a reference for "
                         "hardware byte counters)")
+    p.add_argument("--pmc-step", action="store_true",
+                   help="run the copy (--copy-mib) and one eager step only, for hardware "
+                        "counter passes (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)")
+    p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="no GPU: turn the two counter passes of --pmc-step into the traffic "
+                        "summary under profiles/")
     return p.parse_args()
 
 
@@ -73,8 +79,127 @@ def gemm_bytes(m, k, n, fmt):
     return n * q + m * q + 2 * m * n
 
 
+DOMINANT = ("k_gemm_decode", "k_linear_decode", "k_gemm_tile")
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources: stored counter figures apply only to the build
+    they were taken from."""
+    import hashlib
+    d = os.path.join(ROOT, "block_scaled_fp4_quantize_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(workload, fmt):
+    return os.path.join(ROOT, "profiles", f"{workload}_{fmt}_hbm_traffic.md")
+
+
+def stored_traffic(workload, fmt):
+    """HBM bytes per launch of the dominant kernels from the committed counter
+    summary, or None when there is none or the kernels changed since."""
+    try:
+        with open(traffic_path(workload, fmt)) as fh:
+            for line in fh:
+                if line.startswith("<!-- traffic-json: "):
+                    rec = json.loads(line[len("<!-- traffic-json: "):].rsplit(" -->", 1)[0])
+                    if rec.get("src_hash") == kernel_source_hash():
+                        return rec["bytes_per_launch"]
+    except OSError:
+        pass
+    return None
+
+
+def summarize_pmc(args):
+    """Scale the per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of one eager step by
+    what the same counters read for the calibration copy (N MiB read, N MiB
+    written) and write the summary the benchmark reads its traffic from."""
+    import csv
+    import re
+    fetch_csv, write_csv = args.summarize_pmc
+
+    def load(path, counter):
+        rows = []
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") != counter:
+                    continue
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+        rows.sort()
+        return rows
+
+    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    calib_kib = args.copy_mib * 1024.0
+
+    def scale(rows, what):
+        cal = [v for (_, name, v) in rows if "neg" in name.lower()]
+        if len(cal) != 1:
+            raise SystemExit(f"expected one calibration copy in the {what} pass, found {len(cal)}")
+        return calib_kib / cal[0], cal[0], [(name, v) for (_, name, v) in rows
+                                             if any(d in name for d in DOMINANT)]
+
+    f_fac, f_cal, f_dom = scale(fetch, "FETCH_SIZE")
+    w_fac, w_cal, w_dom = scale(write, "WRITE_SIZE")
+    configs, _ = workload_configs(args.workload)
+    if len(f_dom) != len(configs) or len(w_dom) != len(configs):
+        raise SystemExit(f"expected {len(configs)} dominant-kernel dispatches, found "
+                         f"{len(f_dom)} / {len(w_dom)}")
+    fmt = 0 if args.fmt == "nvfp4" else 1
+    bs = 16 if fmt == 0 else 32
+    per, tot_meas, tot_alg = [], 0.0, 0.0
+    for (m, k, n), (fname, fv), (_, wv) in zip(configs, f_dom, w_dom):
+        meas = (fv * f_fac + wv * w_fac) * 1024.0
+        w_bytes = n * (k // 2 + k // bs)
+        alg = w_bytes + (2 * m * k if "linear" in fname else m * (k // 2 + k // bs)) + 2 * m * n
+        short = re.search(r"(k_[a-z_]+<[^>]*>)", fname)
+        per.append({"m": m, "k": k, "n": n, "kernel": short.group(1) if short else fname, "fetch_kib": round(fv, 1),
+                    "write_kib": round(wv, 1), "hbm_bytes": round(meas), "algorithmic_bytes": alg,
+                    "ratio": round(meas / alg, 3)})
+        tot_meas += meas
+        tot_alg += alg
+    rec = {"workload": args.workload, "fmt": args.fmt, "src_hash": kernel_source_hash(),
+           "bytes_per_launch": round(tot_meas / len(configs)),
+           "algorithmic_bytes_per_launch": round(tot_alg / len(configs)),
+           "calibration": {"copy_mib": args.copy_mib, "fetch_kib": f_cal, "write_kib": w_cal,
+                           "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)},
+           "per_config": per}
+    out = traffic_path(args.workload, args.fmt)
+    lines = [f"# HBM traffic of the dominant kernels: {args.workload}, {args.fmt}", "",
+             "Per-dispatch hardware counters from two rocprofv3 passes over one eager step,",
+             "scaled by what the same counters read for a plain copy kernel of known size.", "",
+             "```",
+             "cd /tmp && export TMPDIR=/tmp",
+             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/fetch -o fetch -- python3 bench.py "
+             f"--workload {args.workload} --fmt {args.fmt} --pmc-step --copy-mib {args.copy_mib}",
+             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/write -o write -- python3 bench.py "
+             f"--workload {args.workload} --fmt {args.fmt} --pmc-step --copy-mib {args.copy_mib}",
+             f"python3 bench.py --workload {args.workload} --fmt {args.fmt} --copy-mib {args.copy_mib} "
+             "--summarize-pmc <fetch csv> <write csv>",
+             "```", "",
+             f"Calibration: a {args.copy_mib} MiB float32 negate read {f_cal:.0f} KiB (FETCH_SIZE) and "
+             f"wrote {w_cal:.0f} KiB (WRITE_SIZE) for {calib_kib:.0f} KiB each way: factors "
+             f"{f_fac:.4f} and {w_fac:.4f}.", "",
+             "| M | K | N | kernel | FETCH KiB | WRITE KiB | HBM bytes (scaled) | algorithmic bytes | ratio |",
+             "|---:|---:|---:|---|---:|---:|---:|---:|---:|"]
+    for p in per:
+        lines.append(f"| {p['m']} | {p['k']} | {p['n']} | `{p['kernel']}` | {p['fetch_kib']} | "
+                     f"{p['write_kib']} | {p['hbm_bytes']} | {p['algorithmic_bytes']} | {p['ratio']} |")
+    lines += ["", f"Average per launch: {rec['bytes_per_launch']} HBM bytes for "
+              f"{rec['algorithmic_bytes_per_launch']} algorithmic bytes.", "",
+              "<!-- traffic-json: " + json.dumps(rec) + " -->", ""]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines))
+    print(out)
+
+
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path).", file=sys.stderr)
@@ -132,9 +257,11 @@ def main():
                                      dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     if args.copy_mib:
-        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        # one elementwise kernel that reads N MiB and writes N MiB (float32 negate)
+        src = torch.ones((args.copy_mib << 20) // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
@@ -142,6 +269,12 @@ def main():
         for cfg in configs:
             m, k, n = cfg
             fp4.fp4_linear(xs[cfg], weights[(k, n)][i % copies], out=outs[cfg], workspace=wss[cfg])
+
+    if args.pmc_step:
+        step(0)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_step": desc, "configs": configs}), flush=True)
+        return
 
     # ---- graphs: one per weight copy (each replays one full step)
     use_graph = not args.no_graph
@@ -245,6 +378,7 @@ def main():
         peak = FP4_PEAK_TFLOPS if fmt == 1 else F16_PEAK_TFLOPS
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": None}
+    roof["traffic"] = stored_traffic(args.workload, args.fmt)
     roof.update({"kernel": " + ".join(sorted(kern)), "avg_launch_us": round(tot_us / tot_launch, 3),
                  "launches_per_step": tot_launch,
                  "per_kernel": {nm: {"launches": d["launches"], "avg_us": round(d["us"] / d["launches"], 3),

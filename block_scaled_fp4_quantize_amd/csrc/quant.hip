@@ -148,19 +148,20 @@ __global__ __launch_bounds__(kThreads) void k_quant(
 
 // ------------------------------------------------------------------ small
 
-// Maximum over every workgroup of the grid. slots[g] is workgroup g's word:
-// (call tag << 16) | its maximum's bf16 bits (< 2^15). A call's tag is one
-// more than the previous call's, read from the workgroup's own slot (every
-// call rewrites every slot; a zero-filled array is tag 0). Each workgroup
-// publishes its word with one device-coherent store; then thread t < grid
-// size polls slot t (bounded) until it carries this call's tag, and the
-// workgroup takes the maximum. The exchanged values travel in the polled
-// words themselves, so no cache writeback or fence is involved.
+// Maximum over every workgroup of the grid. The kActGrid slots are 32-bit
+// words (call tag << 16) | a workgroup maximum's bf16 bits (< 2^15); workgroup
+// g writes slots g, g + G, g + 2G, ... (G = grid size), so every call rewrites
+// every slot whatever its grid size, and after any call all slots carry that
+// call's tag. A call's tag is therefore one more than any slot's tag at its
+// start (a zero-filled array is tag 0). Thread t < G polls slot t (bounded)
+// until it carries this call's tag, and the workgroup takes the maximum. The
+// exchanged values travel in the polled words themselves, so no cache
+// writeback or fence is involved.
 __device__ __forceinline__ uint32_t grid_max_u32(uint32_t wg_max, uint32_t tag,
                                                  uint32_t *slots, uint32_t *lds) {
-  if (threadIdx.x == 0)
-    __hip_atomic_store(&slots[blockIdx.x], (tag << 16) | wg_max, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+  for (uint32_t s = blockIdx.x + threadIdx.x * gridDim.x; s < (uint32_t)kActGrid;
+       s += blockDim.x * gridDim.x)
+    __hip_atomic_store(&slots[s], (tag << 16) | wg_max, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   uint32_t v = 0;
   if (threadIdx.x < gridDim.x) {
     for (uint32_t it = 0; it < (1u << 22); ++it) {
@@ -173,9 +174,11 @@ __device__ __forceinline__ uint32_t grid_max_u32(uint32_t wg_max, uint32_t tag,
 }
 
 // Single-launch quantization of a tensor of at most kActGrid * 256 * kActBpt
-// blocks. Every thread loads its blocks first, so the values are in registers
-// while the maximum is exchanged.
-template <int FMT, int TILED, int DYN>
+// blocks. Every thread loads its (at most BPT) blocks first, so the values are
+// in registers while the maximum is exchanged; the dynamic-scale form runs as
+// few workgroups as hold the tensor, so that small tensors need little or no
+// exchange.
+template <int FMT, int TILED, int DYN, int BPT>
 __global__ __launch_bounds__(kThreads) void k_quant_small(
     const uint16_t *__restrict__ x, int64_t rows, int64_t k, int64_t rows_pad, int64_t kt_n,
     const float *__restrict__ static_scale, uint8_t *__restrict__ codes, int64_t cpitch,
@@ -187,13 +190,13 @@ __global__ __launch_bounds__(kThreads) void k_quant_small(
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   uint32_t tag = 0;
-  if (DYN)  // this call's tag, from the previous call's word of this workgroup
+  if (DYN)  // this call's tag: one more than the previous call's (any slot)
     tag = ((__hip_atomic_load(&sync[blockIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 16) +
            1u) & 0xFFFFu;
-  uint4 v[kActBpt][K::V];
+  uint4 v[BPT][K::V];
   uint32_t m = 0;
 #pragma unroll
-  for (int i = 0; i < kActBpt; ++i) {
+  for (int i = 0; i < BPT; ++i) {
     const int64_t t = t0 + i * stride;
     const int64_t r = t / nb_pad, b = t - r * nb_pad;
     if (t < total && r < rows && b < nb) {
@@ -213,7 +216,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_small(
     if (blockIdx.x == 0 && threadIdx.x == 0 && ts_out) *ts_out = st;
   }
 #pragma unroll
-  for (int i = 0; i < kActBpt; ++i) {
+  for (int i = 0; i < BPT; ++i) {
     const int64_t t = t0 + i * stride;
     if (t >= total) break;
     const int64_t r = t / nb_pad, b = t - r * nb_pad;
@@ -283,16 +286,22 @@ template <int FMT, int TILED>
 void launch_small(const uint16_t *x, int64_t rows, int64_t k, int64_t rows_pad, int64_t kt_n,
                   const float *static_scale, uint8_t *codes, int64_t cpitch, uint8_t *scales,
                   int64_t spitch, float *ts_out, uint32_t *sync, hipStream_t stream) {
+  // One block per thread where the grid allows: encoding is the costly part
+  // and spreads over as many CUs as there are blocks. The dynamic-scale form
+  // also exchanges its maximum among the workgroups, so it stops at kActGrid
+  // workgroups (up to kActBpt blocks per thread); fewer workgroups also means
+  // fewer polls of the exchange words.
+  const int64_t total = rows_pad * kt_n * Blk<FMT>::BPF;
+  const int64_t per_wg = (total + kThreads - 1) / kThreads;
   if (FMT == 0 && !static_scale) {
-    hipLaunchKernelGGL((k_quant_small<FMT, TILED, 1>), dim3(kActGrid), dim3(kThreads), 0, stream,
-                       x, rows, k, rows_pad, kt_n, static_scale, codes, cpitch, scales, spitch,
-                       ts_out, sync);
+    const int grid = (int)(per_wg < kActGrid ? per_wg : kActGrid);
+    hipLaunchKernelGGL((k_quant_small<FMT, TILED, 1, kActBpt>), dim3(grid), dim3(kThreads), 0,
+                       stream, x, rows, k, rows_pad, kt_n, static_scale, codes, cpitch, scales,
+                       spitch, ts_out, sync);
   } else {
-    const int64_t total = rows_pad * kt_n * Blk<FMT>::BPF;
-    const int grid = (int)((total + kThreads * kActBpt - 1) / (kThreads * kActBpt));
-    hipLaunchKernelGGL((k_quant_small<FMT, TILED, 0>), dim3(grid), dim3(kThreads), 0, stream, x,
-                       rows, k, rows_pad, kt_n, static_scale, codes, cpitch, scales, spitch,
-                       ts_out, sync);
+    hipLaunchKernelGGL((k_quant_small<FMT, TILED, 0, 1>), dim3((unsigned)per_wg), dim3(kThreads), 0,
+                       stream, x, rows, k, rows_pad, kt_n, static_scale, codes, cpitch, scales,
+                       spitch, ts_out, sync);
   }
 }
 

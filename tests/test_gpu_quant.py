@@ -153,3 +153,7 @@ def test_workspace_shared_across_calls():
             ref = oracle.quantize_nvfp4(bits)
             q = fp4.fp4_quantize_act(to_dev(bits), 0, workspace=ws)
             assert_canonical_equal(q, ref, 0, what=f"shared workspace call {rep}/{i} {m}x{k}")
+            # the tiled layout (rows padded to 16: another grid size) on the same words
+            qt = fp4.fp4_quantize_act(to_dev(bits), 0, layout=fp4.TILED, workspace=ws)
+            assert_canonical_equal(fp4.fp4_export_canonical(qt), ref, 0,
+                                   what=f"shared workspace tiled call {rep}/{i} {m}x{k}")
