@@ -14,7 +14,7 @@ bytes per launch over its average duration, timed with HIP events on the
 launch stream) and the CPU oracle timed on a bounded sample of the same work.
 
     python bench.py [--steps K] [--warmup W] [--fmt nvfp4|mxfp4]
-                    [--workload decode|prefill|square8192|single]
+                    [--workload decode|prefill|square8192|single|forward]
 """
 from __future__ import annotations
 
@@ -41,7 +41,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--fmt", default="nvfp4", choices=["nvfp4", "mxfp4"])
-    p.add_argument("--workload", default="decode", choices=["decode", "prefill", "square8192", "single"])
+    p.add_argument("--workload", default="decode",
+                   choices=["decode", "prefill", "square8192", "single", "forward"])
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     p.add_argument("--kernel-reps", type=int, default=50)
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
@@ -216,6 +217,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     fmt = fp4.FORMATS[args.fmt]
+    if args.workload == "forward":
+        bench_forward(args, fmt)
+        return
     configs, desc = workload_configs(args.workload)
 
     def to_dev(bits):
@@ -407,6 +411,127 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(configs, fmt, args, a_host, w_host)
+    print(json.dumps(result), flush=True)
+
+
+def bench_forward(args, fmt):
+    """Synthetic 24-layer forward: per layer Q, K, V, O and four (up, down)
+    pairs, 288 W4A4 linear calls per forward, at M = 1, 8, 32 and 128. The
+    weights (3.82 G values, ~N(0, 0.02)) are drawn on the GPU from a seeded
+    generator and quantized once; every call gets its own pre-drawn
+    activation ~N(0, 1) (calls are not chained). One step = one forward at each
+    of the four M (HIP-graph replays); value = Σ 2·M·N·K / step time."""
+    import numpy as np
+    import torch
+
+    import block_scaled_fp4_quantize_amd as fp4
+    import synth
+    dev = torch.device("cuda:0")
+    layer, nl, ms = synth.FORWARD_LAYER, synth.FORWARD_LAYERS, synth.FORWARD_M
+    def note(msg):
+        print(f"[forward] {msg}", file=sys.stderr, flush=True)
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    note("quantizing 288 weights")
+    weights = []
+    for _ in range(nl):
+        for (_, k, n) in layer:
+            w = (torch.randn(n, k, generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+            weights.append(fp4.fp4_quantize_weight(w, fmt))
+            del w
+    calls = [(k, n) for _ in range(nl) for (_, k, n) in layer]
+    note("drawing activations, capturing graphs")
+    acts, outs, wss, graphs = {}, {}, {}, {}
+    for m in ms:
+        acts[m] = [torch.randn(m, k, generator=gen, device=dev).to(torch.bfloat16) for (k, n) in calls]
+        outs[m] = {n: torch.empty(m, n, dtype=torch.bfloat16, device=dev) for (_, n) in calls}
+        wsz = max(fp4.fp4_linear_workspace_bytes(fmt, m, n, k) for (k, n) in calls)
+        wss[m] = torch.zeros(max(1, wsz), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def forward(m):
+        for i, (k, n) in enumerate(calls):
+            fp4.fp4_linear(acts[m][i], weights[i], out=outs[m][n], workspace=wss[m])
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for m in ms:
+            forward(m)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for m in ms:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            forward(m)
+        graphs[m] = g
+    torch.cuda.synchronize()
+    note("timing")
+    for _ in range(args.warmup):
+        for m in ms:
+            graphs[m].replay()
+    torch.cuda.synchronize()
+    steps = max(1, args.steps // 10)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        for m in ms:
+            graphs[m].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = e0.elapsed_time(e1) / steps
+    per_m = {}
+    for m in ms:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            graphs[m].replay()
+        b.record()
+        torch.cuda.synchronize()
+        per_m[m] = a.elapsed_time(b) / steps
+    sum_nk = sum(n * k for (k, n) in calls)
+    flops = sum(2.0 * m * sum_nk for m in ms)
+    bs = 16 if fmt == 0 else 32
+    w_bytes = sum(n * (k // 2 + k // bs) for (k, n) in calls)
+    def call_bytes(m):   # weights + bf16 activations + bf16 outputs of one forward
+        return w_bytes + sum(2 * m * k + 2 * m * n for (k, n) in calls)
+    achieved = sum(call_bytes(m) for m in ms) / (ms_per_step * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if fmt == 0 else "fp4",
+        "data": "synthetic",
+        "config": {"workload": "synthetic 24-layer forward, 288 W4A4 linear calls per forward "
+                               "(Q 2880->4096, K/V 2880->512, O 4096->2880, 4 x (up 2880->5760, "
+                               "down 5760->2880)), one forward at each M in {1,8,32,128}",
+                   "format": args.fmt, "launch": "hip-graph replay (one graph per M)",
+                   "weight_bytes": w_bytes,
+                   "per_forward_ms": {str(m): round(per_m[m], 4) for m in ms},
+                   "per_forward_tflops": {str(m): round(2.0 * m * sum_nk / (per_m[m] * 1e-3) / 1e12, 2)
+                                          for m in ms}},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "whole fp4_linear calls (activation quantization included)",
+                     "note": "algorithmic bytes of all calls of the step over the step time"},
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        note("cpu baseline")
+        cfgs = [(8, k, n) for (_, k, n) in layer]
+        a_host = {(8, k, n): synth.forward_act(0, j, 8) for j, (_, k, n) in enumerate(layer)}
+        w_host = {(k, n): synth.forward_weight(0, j) for j, (_, k, n) in enumerate(layer)}
+        result["cpu_baseline"] = cpu_baseline(cfgs, fmt, args, a_host, w_host)
     print(json.dumps(result), flush=True)
 
 

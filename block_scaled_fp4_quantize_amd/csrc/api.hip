@@ -99,9 +99,10 @@ fp4_status check_tensor(const fp4_tensor *t, const char *name) {
 
 size_t quant_ws(int32_t fmt) { return fmt == FP4_NVFP4 ? kQuantScratchBytes : 0; }
 
-// Everything fp4_linear keeps in its workspace, at fixed offsets: the
-// activations quantized into the tiled layout, their tensor scale and the
-// quantizer's scratch.
+// Everything fp4_linear keeps in its workspace: the quantizer's scratch (its
+// exchange words persist from call to call) at offset 0 whatever the call's
+// shape, so that one workspace can serve calls of different shapes; then the
+// tensor scale and the activations quantized into the tiled layout.
 struct LinearLayout {
   size_t codes, scales, ts, scratch, total;
 };
@@ -110,10 +111,10 @@ LinearLayout linear_layout(int32_t fmt, int64_t m, int64_t k) {
   LinearLayout L;
   const int64_t mp = round_up(m, 16), kp = k_pad(k);
   size_t off = 0;
+  L.scratch = off; off = align256(off + kQuantScratchBytes);
+  L.ts = off; off = align256(off + sizeof(float));
   L.codes = off; off = align256(off + (size_t)(mp * kp / 2));
   L.scales = off; off = align256(off + (size_t)(mp * kp / block_of(fmt)));
-  L.ts = off; off = align256(off + sizeof(float));
-  L.scratch = off; off = align256(off + kQuantScratchBytes);
   L.total = off;
   return L;
 }

@@ -145,7 +145,10 @@ fp4_status fp4_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c_bf16, int6
 
 /* Workspace for fp4_linear: the quantized activations and the quantizer's
  * scratch. Same contract as the quantize workspace: zero-filled before its
- * first use, left reusable by every call, not shared by overlapping calls. */
+ * first use, left reusable by every call, not shared by overlapping calls.
+ * One workspace may serve calls of different shapes (and formats) in
+ * sequence when it is at least as large as each call requires: the words that
+ * persist between calls sit at a fixed offset. */
 size_t fp4_linear_workspace_bytes(int32_t fmt, int64_t m, int64_t n, int64_t k);
 
 /*

@@ -214,3 +214,55 @@ def test_extreme_tensor_scales(fmt, m):
     wq = fp4.fp4_quantize_weight(to_dev(w), f)
     y = bf16_out_to_f64(fp4.fp4_linear(to_dev(a), wq))
     assert_gemm_close(y, c_ref, l_ref, f"tiny scales m={m}")
+
+
+_FWD_CACHE = {}
+
+
+def _forward_weight(fmt, j):
+    """Layer 0's weight j of the 24-layer forward: oracle quantization and the
+    GPU weight cache, kept across the parametrized cases."""
+    key = (fmt, j)
+    if key not in _FWD_CACHE:
+        w = synth.forward_weight(0, j)
+        _FWD_CACHE[key] = (oracle.quantize(F[fmt], w), fp4.fp4_quantize_weight(to_dev(w), F[fmt]))
+    return _FWD_CACHE[key]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m", synth.FORWARD_M)
+def test_forward_layer_sampled(fmt, m):
+    """The 12 linear shapes of one layer of the synthetic 24-layer forward
+    (Q, K, V, O, up/down pairs) at the forward's batch sizes, through
+    fp4_linear as the benchmark calls it; 512 sampled outputs per call
+    against the oracle's k-ordered binary64 sums."""
+    for j, (name, k, n) in enumerate(synth.FORWARD_LAYER):
+        print(f"[forward] fmt={fmt} m={m} {name} {k}->{n}", flush=True)
+        qw_ref, wq = _forward_weight(fmt, j)
+        a = synth.forward_act(0, j, m)
+        qa_ref = oracle.quantize(F[fmt], a)
+        y = bf16_out_to_f64(fp4.fp4_linear(to_dev(a), wq))
+        rng = np.random.default_rng(m * 100 + j)
+        rows, cols = rng.integers(0, m, 512), rng.integers(0, n, 512)
+        c_ref, l_ref = oracle.gemm_sampled(qa_ref, qw_ref, rows, cols)
+        assert_gemm_close(y[rows, cols], c_ref, l_ref, f"forward {name} m={m}")
+
+
+def test_linear_workspace_shared_across_shapes():
+    """One zero-filled workspace, sized for the largest call, serves NVFP4
+    dynamic-scale linears of different K, M and paths in sequence (the
+    quantizer's exchange words sit at a fixed offset of the workspace)."""
+    cases = [(8, 2880, 512), (8, 5760, 2880), (1, 4096, 2880), (32, 2880, 5760), (8, 2880, 4096),
+             (128, 5760, 2880), (8, 4096, 2880), (2, 2880, 512)]
+    size = max(fp4.fp4_linear_workspace_bytes(0, m, n, k) for (m, k, n) in cases)
+    ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for i, (m, k, n) in enumerate(cases):
+            print(f"[shared-ws] rep={rep} m={m} k={k} n={n}", flush=True)
+            a = synth.normal((m, k), 1.0 + i, 41, 10 * rep + i)
+            w = synth.normal((n, k), 0.02, 41, 100 + i)
+            qa_ref, qw_ref = oracle.quantize_nvfp4(a), oracle.quantize_nvfp4(w)
+            c_ref, l_ref = oracle.gemm(qa_ref, qw_ref)
+            wq = fp4.fp4_quantize_weight(to_dev(w), 0)
+            y = bf16_out_to_f64(fp4.fp4_linear(to_dev(a), wq, workspace=ws))
+            assert_gemm_close(y, c_ref, l_ref, f"shared workspace call {rep}/{i} {m}x{k}x{n}")
