@@ -92,13 +92,15 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)p;
 }
-__device__ __forceinline__ void lds_copy16(const void *src, uint32_t dst) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(dst) : "memory", "m0");
+// The source address is a wave-uniform base (SGPR pair) plus a per-lane
+// 32-bit byte offset, which keeps the copy addresses out of vector registers.
+__device__ __forceinline__ void lds_copy16(const uint8_t *base, uint32_t off, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(base), "s"(dst) : "memory", "m0");
 }
-__device__ __forceinline__ void lds_copy4(const void *src, uint32_t dst) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :: "v"(src), "s"(dst) : "memory", "m0");
+__device__ __forceinline__ void lds_copy4(const uint8_t *base, uint32_t off, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(off), "s"(base), "s"(dst) : "memory", "m0");
 }
 
 __device__ __forceinline__ v4f mma_mx(uint4 w, uint4 a, v4f c, uint32_t sw, uint32_t sa) {
@@ -161,21 +163,30 @@ __global__ __launch_bounds__(256) void k_gemm_tile(
   // they only feed output rows/columns that are never stored, and every wave
   // issues the same number of copies at every stage.
   constexpr int NCP = C::NF / 4, NSP = C::SC_INSTR / 4;
-  auto frag_row = [&](int f, const uint8_t *a, const uint8_t *w, int bytes)
-      __attribute__((always_inline)) -> const uint8_t * {
-    return f < C::FA ? a + (int64_t)min(g0 + f, ga_n - 1) * kt_n * bytes
-                     : w + (int64_t)min(n0 + f - C::FA, nt_n - 1) * kt_n * bytes;
+  // Copy sources: a wave-uniform fragment-row base and a per-lane offset
+  // (lane * 16 for the code fragments; for the scale runs the lane's dword,
+  // relative to the run's first row: a run never crosses from A's scales into
+  // W's, A's scale dwords per stage being a multiple of 64).
+  auto row_of = [&](int f) __attribute__((always_inline)) {
+    return f < C::FA ? min(g0 + f, ga_n - 1) : min(n0 + f - C::FA, nt_n - 1);
   };
-  const uint8_t *code_src[NCP];
+  const uint8_t *code_base[NCP];
+  const uint32_t code_off = lane * 16;
 #pragma unroll
-  for (int u = 0; u < NCP; ++u)
-    code_src[u] = frag_row(wave + 4 * u, a_codes, w_codes, kFragCodeBytes) + lane * 16;
-  const uint8_t *sc_src[NSP];
+  for (int u = 0; u < NCP; ++u) {
+    const int f = wave + 4 * u;
+    code_base[u] = (f < C::FA ? a_codes : w_codes) + (int64_t)row_of(f) * kt_n * kFragCodeBytes;
+  }
+  const uint8_t *sc_base[NSP];
+  uint32_t sc_off[NSP];
 #pragma unroll
   for (int v = 0; v < NSP; ++v) {
-    const int p = min(64 * (wave + 4 * v) + lane, C::SC_DW - 1);  // scale dword of the stage
-    const int f = p / (C::SCB / 4), pc = p % (C::SCB / 4);
-    sc_src[v] = frag_row(f, a_sc, w_sc, C::SCB) + pc * 4;
+    const int j = wave + 4 * v;
+    const int p0 = min(64 * j, C::SC_DW - 1), f0 = p0 / (C::SCB / 4);
+    const int p = min(64 * j + lane, C::SC_DW - 1), f = p / (C::SCB / 4), pc = p % (C::SCB / 4);
+    const int r0 = row_of(f0);
+    sc_base[v] = (f0 < C::FA ? a_sc : w_sc) + (int64_t)r0 * kt_n * C::SCB;
+    sc_off[v] = (uint32_t)((row_of(f) - r0) * kt_n * C::SCB + pc * 4);
   }
 
   // copy unit u of this wave's share of stage kt: units 0..NCP-1 are code
@@ -183,10 +194,10 @@ __global__ __launch_bounds__(256) void k_gemm_tile(
   constexpr int NU = NCP + NSP;
   auto issue_unit = [&](uint8_t *st, int kt, int u) __attribute__((always_inline)) {
     if (u < NCP)
-      lds_copy16(code_src[u] + (int64_t)kt * kFragCodeBytes,
+      lds_copy16(code_base[u] + (int64_t)kt * kFragCodeBytes, code_off,
                  lds_addr(st + (wave + 4 * u) * kFragCodeBytes));
     else
-      lds_copy4(sc_src[u - NCP] + (int64_t)kt * C::SCB,
+      lds_copy4(sc_base[u - NCP] + (int64_t)kt * C::SCB, sc_off[u - NCP],
                 lds_addr(st + C::CODE_BYTES + (wave + 4 * (u - NCP)) * 256));
   };
   auto issue = [&](auto sc, int kt) __attribute__((always_inline)) {
@@ -238,25 +249,39 @@ __global__ __launch_bounds__(256) void k_gemm_tile(
     } else {
       // K sub-block g: dword g of every lane's 16 code bytes (values
       // 8g..8g+7 of its 32), the same permutation of K for both operands.
+      // Software-pipelined: sub-block g+1 is dequantized while sub-block g's
+      // matrix instructions run (no scheduling barrier between sub-blocks, so
+      // the scheduler interleaves the two), and the two units work side by
+      // side. The weight operands of g+1 are double-buffered; each activation
+      // row's operand for g+1 replaces its g value right after that row's
+      // instructions. (Explicit MFMA/VALU scheduling groups made the
+      // scheduler spill.)
+      auto deq_a = [&](int g, int i) __attribute__((always_inline)) {
+        const uint32_t d = g == 0 ? o.aq[i].x : g == 1 ? o.aq[i].y : g == 2 ? o.aq[i].z : o.aq[i].w;
+        return __builtin_bit_cast(h8v, nv_dequant8_u4(d, g < 2 ? (o.as[i] & 0xFFu) : (o.as[i] >> 8)));
+      };
+      auto deq_w = [&](int g, int j) __attribute__((always_inline)) {
+        const uint32_t d = g == 0 ? o.wq[j].x : g == 1 ? o.wq[j].y : g == 2 ? o.wq[j].z : o.wq[j].w;
+        return __builtin_bit_cast(h8v, nv_dequant8_u4(d, g < 2 ? (o.ws[j] & 0xFFu) : (o.ws[j] >> 8)));
+      };
+      h8v ah[TM], wh[2][TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) wh[0][j] = deq_w(0, j);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) ah[i] = deq_a(0, i);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        h8v ah[TM], wh[TN];
+        if (g < 3) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j) wh[(g + 1) & 1][j] = deq_w(g + 1, j);
+        }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-          const uint32_t d = g == 0 ? o.aq[i].x : g == 1 ? o.aq[i].y : g == 2 ? o.aq[i].z : o.aq[i].w;
-          ah[i] = __builtin_bit_cast(h8v, nv_dequant8_u4(d, g < 2 ? (o.as[i] & 0xFFu) : (o.as[i] >> 8)));
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const uint32_t d = g == 0 ? o.wq[j].x : g == 1 ? o.wq[j].y : g == 2 ? o.wq[j].z : o.wq[j].w;
-          wh[j] = __builtin_bit_cast(h8v, nv_dequant8_u4(d, g < 2 ? (o.ws[j] & 0xFFu) : (o.ws[j] >> 8)));
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh[j], ah[i], acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh[g & 1][j], ah[i], acc[i][j], 0, 0, 0);
+          if (g < 3) ah[i] = deq_a(g + 1, i);
+        }
       }
     }
   };
