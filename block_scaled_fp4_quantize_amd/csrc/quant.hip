@@ -23,6 +23,8 @@
 #include "fp4_device.h"
 #include "fp4_internal.h"
 
+#include <algorithm>
+
 namespace fp4i {
 using namespace fp4d;
 
@@ -143,6 +145,61 @@ __global__ __launch_bounds__(kThreads) void k_quant(
 #pragma unroll
     for (int i = 0; i < K::V; ++i) v[i] = src[i];
     encode_store<FMT>(v, st, cdst, sdst);
+  }
+}
+
+// Large tensors into the fragment-tiled layout: one wave per fragment of 16
+// rows x 128 values, lane l = 16c + r taking row r's values 32c .. 32c + 31 —
+// exactly the 16 code bytes and 2 (NVFP4) or 1 (MXFP4) scale bytes the lane
+// owns in the fragment. Each lane reads 64 contiguous bytes of its row (a
+// wave covers 16 rows x 256 bytes, whole cache lines) and the wave writes its
+// fragment's 1 KB of codes and its scale bytes contiguously.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_quant_tiled(
+    const uint16_t *__restrict__ x, int64_t rows, int64_t k, int64_t rows_pad, int64_t kt_n,
+    const uint32_t *__restrict__ parts, int nparts, const float *__restrict__ static_scale,
+    uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, float *__restrict__ ts_out) {
+  using K = Blk<FMT>;
+  __shared__ uint32_t lds[4];
+  float st = 1.0f;
+  if (FMT == 0) {
+    if (static_scale) {
+      st = *static_scale;
+    } else {
+      uint32_t m = 0;
+      for (int i = threadIdx.x; i < nparts; i += blockDim.x) m = max(m, parts[i]);
+      st = tensor_scale_from_amax(bf16_bits_to_f32(block_max_u32(m, lds)));
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0 && ts_out) *ts_out = st;
+  }
+  const int lane = threadIdx.x & 63, r = lane & 15, c = lane >> 4;
+  const int64_t frags = (rows_pad >> 4) * kt_n;
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  for (int64_t f = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); f < frags;
+       f += waves) {
+    const int64_t row = (f / kt_n) * 16 + r, k0 = (f % kt_n) * kFragK + 32 * c;
+    uint4 v[4];
+    const uint4 *src = (const uint4 *)(x + row * k + k0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)  // values k0 + 8j .. k0 + 8j + 7 (blocks never straddle k)
+      v[j] = (row < rows && k0 + 8 * j < k) ? src[j] : make_uint4(0u, 0u, 0u, 0u);
+    uint4 q;
+    uint32_t sc;
+    if constexpr (FMT == 0) {
+      uint2 c0 = make_uint2(0u, 0u), c1 = make_uint2(0u, 0u);
+      uint32_t s0 = 0, s1 = 0;
+      if (row < rows && k0 < k) nv_encode_block(v[0], v[1], st, c0, s0);
+      if (row < rows && k0 + 16 < k) nv_encode_block(v[2], v[3], st, c1, s1);
+      q = make_uint4(c0.x, c0.y, c1.x, c1.y);
+      sc = s0 | (s1 << 8);
+      *(uint16_t *)(scales + f * K::SFB + lane * 2) = (uint16_t)sc;
+    } else {
+      q = make_uint4(0u, 0u, 0u, 0u);
+      sc = 0;
+      if (row < rows && k0 < k) mx_encode_block(v, q, sc);
+      scales[f * K::SFB + lane] = (uint8_t)sc;
+    }
+    *(uint4 *)(codes + f * kFragCodeBytes + lane * 16) = q;
   }
 }
 
@@ -310,6 +367,13 @@ void launch_large(const uint16_t *x, int64_t rows, int64_t k, int64_t rows_pad, 
                   const uint32_t *parts, int nparts, const float *static_scale, uint8_t *codes,
                   int64_t cpitch, uint8_t *scales, int64_t spitch, float *ts_out,
                   hipStream_t stream) {
+  if (TILED) {  // one wave per fragment, four waves per workgroup, grid-stride
+    const int64_t frags = (rows_pad >> 4) * kt_n;
+    const int grid = (int)std::min<int64_t>((frags + 3) / 4, 8192);
+    hipLaunchKernelGGL((k_quant_tiled<FMT>), dim3(grid), dim3(kThreads), 0, stream, x, rows, k,
+                       rows_pad, kt_n, parts, nparts, static_scale, codes, scales, ts_out);
+    return;
+  }
   const int grid = grid_for(rows_pad * kt_n * Blk<FMT>::BPF, 8192);
   hipLaunchKernelGGL((k_quant<FMT, TILED>), dim3(grid), dim3(kThreads), 0, stream, x, rows, k,
                      rows_pad, kt_n, parts, nparts, static_scale, codes, cpitch, scales, spitch,
