@@ -21,8 +21,10 @@ inline int frag_scale_bytes(int fmt) { return fmt == 0 ? 128 : 64; }
 constexpr int kActGrid = 128;         // workgroups of the single-launch quantizer
 constexpr int kActBpt = 4;            // blocks per thread in the single-launch quantizer
 // Quantize scratch: kMaxAmaxParts partial maxima, then the single-launch
-// quantizer's kActGrid tagged maximum words (zero-filled once).
-constexpr size_t kQuantScratchBytes = (kMaxAmaxParts + kActGrid) * sizeof(uint32_t);
+// quantizer's kActGrid tagged maximum words, one per 128-byte line
+// (zero-filled once).
+constexpr int kSlotStride = 32;
+constexpr size_t kQuantScratchBytes = (kMaxAmaxParts + kActGrid * kSlotStride) * sizeof(uint32_t);
 
 // Number of partial maxima the large-tensor path produces for n elements.
 int amax_parts(int64_t n);
@@ -73,6 +75,7 @@ hipError_t launch_gemm_tile(const GemmArgs &g, int cfg, hipStream_t stream);
 constexpr int kFusedMaxM = 16;
 constexpr int64_t kFusedMaxMK = 65536;        // M * K_pad bound (LDS staging, MXFP4)
 constexpr int64_t kFusedMaxWork = 16 << 20;   // M * K_pad * N tiles bound
+constexpr int64_t kFusedMaxTilesNv = 512;      // NVFP4: at most this many weight tiles
 bool linear_fused_ok(int fmt, int64_t m, int64_t n, int64_t k);
 hipError_t launch_linear_fused(int fmt, const uint16_t *x, int64_t m, int64_t k,
                                const float *static_scale, const uint8_t *w_codes,

@@ -420,8 +420,11 @@ bool linear_fused_ok(int fmt, int64_t m, int64_t n, int64_t k) {
   const int64_t mk = m * k_pad(k);
   // LDS staging bound, and a bound on the redundant quantization work that
   // every weight tile's workgroup repeats.
+  // NVFP4's encoding prologue (maximum pass + exact encode) is long enough
+  // that only about two workgroups per CU (512 weight tiles) should repeat it.
+  const int64_t nt = round_up(n, 16) / 16;
   return m <= kFusedMaxM && mk <= (fmt == 0 ? kFusedMaxMK / 2 : kFusedMaxMK) &&
-         mk * (round_up(n, 16) / 16) <= kFusedMaxWork;
+         mk * nt <= kFusedMaxWork && (fmt != 0 || nt <= kFusedMaxTilesNv);
 }
 
 hipError_t launch_linear_fused(int fmt, const uint16_t *x, int64_t m, int64_t k,

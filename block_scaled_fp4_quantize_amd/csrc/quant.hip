@@ -214,15 +214,19 @@ __global__ __launch_bounds__(kThreads) void k_quant_tiled(
 // until it carries this call's tag, and the workgroup takes the maximum. The
 // exchanged values travel in the polled words themselves, so no cache
 // writeback or fence is involved.
+// Each word has a 128-byte line of its own (kSlotStride words apart), so that
+// the polls of different words go to different lines.
 __device__ __forceinline__ uint32_t grid_max_u32(uint32_t wg_max, uint32_t tag,
                                                  uint32_t *slots, uint32_t *lds) {
   for (uint32_t s = blockIdx.x + threadIdx.x * gridDim.x; s < (uint32_t)kActGrid;
        s += blockDim.x * gridDim.x)
-    __hip_atomic_store(&slots[s], (tag << 16) | wg_max, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&slots[s * kSlotStride], (tag << 16) | wg_max, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   uint32_t v = 0;
   if (threadIdx.x < gridDim.x) {
     for (uint32_t it = 0; it < (1u << 22); ++it) {
-      v = __hip_atomic_load(&slots[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      v = __hip_atomic_load(&slots[threadIdx.x * kSlotStride], __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_AGENT);
       if ((v >> 16) == tag) break;
       __builtin_amdgcn_s_sleep(1);
     }
@@ -248,8 +252,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_small(
   const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   uint32_t tag = 0;
   if (DYN)  // this call's tag: one more than the previous call's (any slot)
-    tag = ((__hip_atomic_load(&sync[blockIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 16) +
-           1u) & 0xFFFFu;
+    tag = ((__hip_atomic_load(&sync[blockIdx.x * kSlotStride], __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT) >> 16) + 1u) & 0xFFFFu;
   uint4 v[BPT][K::V];
   uint32_t m = 0;
 #pragma unroll
