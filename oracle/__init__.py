@@ -15,7 +15,10 @@ Conventions (the same as the C file):
 
 Parity status: every function here is pinned by a test under ``tests/`` against
 values the pages print, closed forms or brute force, except the MXFP4 block
-exponent rule, which the pages do not print (pinned by invariants only).
+exponent rule, which the pages do not print (pinned by invariants only). The
+block rotation is pinned against an exact integer matrix product with the
+library Sylvester Hadamard matrix and against closed forms; the OAS exponent
+against a brute-force search.
 """
 from __future__ import annotations
 
@@ -83,6 +86,14 @@ def _load():
                                            P, P, P]
         lib.orc_quantize_mxfp4.restype = ctypes.c_int
         lib.orc_quantize_mxfp4.argtypes = [P, I64, I64, P, P]
+        lib.orc_quantize_mxfp4_rule.restype = ctypes.c_int
+        lib.orc_quantize_mxfp4_rule.argtypes = [P, I64, I64, ctypes.c_int, P, P]
+        lib.orc_mx_exponent_oas.restype = ctypes.c_int
+        lib.orc_mx_exponent_oas.argtypes = [ctypes.c_double]
+        lib.orc_hadamard_norm.restype = ctypes.c_float
+        lib.orc_hadamard_norm.argtypes = [ctypes.c_int]
+        lib.orc_hadamard_bf16.restype = ctypes.c_int
+        lib.orc_hadamard_bf16.argtypes = [P, I64, I64, ctypes.c_int, P]
         lib.orc_dequantize.restype = None
         lib.orc_dequantize.argtypes = [ctypes.c_int, P, P, ctypes.c_float, I64, I64, P]
         lib.orc_gemm.restype = None
@@ -179,23 +190,52 @@ def quantize_nvfp4(x, mode: int = DYNAMIC, static_scale: float | None = None) ->
     return Quantized(NVFP4, codes, scales, ts[0], k)
 
 
-def quantize_mxfp4(x) -> Quantized:
+def quantize_mxfp4(x, oas: bool = False) -> Quantized:
     x = _bf16(x)
     r, k = x.shape
     codes = np.zeros((r, k // 2), dtype=np.uint8)
     scales = np.zeros((r, k // 32), dtype=np.uint8)
-    rc = _load().orc_quantize_mxfp4(_ptr(x), r, k, _ptr(codes), _ptr(scales))
+    rc = _load().orc_quantize_mxfp4_rule(_ptr(x), r, k, int(bool(oas)), _ptr(codes),
+                                         _ptr(scales))
     if rc != 0:
         raise ValueError("oracle MXFP4 quantize rejected its arguments")
     return Quantized(MXFP4, codes, scales, 1.0, k)
 
 
-def quantize(fmt: int, x, mode: int = DYNAMIC, static_scale=None) -> Quantized:
+def mx_exponent_oas(amax: float) -> int:
+    """Overflow-aware MXFP4 block exponent (smallest e with amax <= 6 * 2^e)."""
+    return _load().orc_mx_exponent_oas(float(amax))
+
+
+def hadamard_norm(bs: int) -> np.float32:
+    return np.float32(_load().orc_hadamard_norm(int(bs)))
+
+
+def hadamard(x, bs: int) -> np.ndarray:
+    """Block rotation of bf16 rows: H_bs x / sqrt(bs) per block of bs values
+    along k, binary32 fast transform, rounded to bf16 (uint16 bit patterns)."""
+    x = _bf16(x)
+    r, k = x.shape
+    out = np.zeros((r, k), dtype=np.uint16)
+    rc = _load().orc_hadamard_bf16(_ptr(x), r, k, int(bs), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle rotation rejected its arguments")
+    return out
+
+
+def quantize(fmt: int, x, mode: int = DYNAMIC, static_scale=None, rotate: bool = False,
+             oas: bool = False) -> Quantized:
+    """Quantize x; rotate=True applies the block rotation (size = the block)
+    first; oas=True (MXFP4) takes the overflow-aware block exponent."""
+    if rotate:
+        x = hadamard(x, BLOCK[fmt])
     if fmt == NVFP4:
+        if oas:
+            raise ValueError("OAS is an MXFP4 scale rule")
         return quantize_nvfp4(x, mode, static_scale)
     if mode != DYNAMIC or static_scale is not None:
         raise ValueError("MXFP4 has no per-tensor scale")
-    return quantize_mxfp4(x)
+    return quantize_mxfp4(x, oas)
 
 
 def dequantize(q: Quantized) -> np.ndarray:

@@ -25,6 +25,13 @@
  *             weight cache (opening paragraphs): weights are quantized once,
  *             activations per call, and the product runs on the quantized
  *             operands.
+ *   [REALFP4] "FP4 on a consumer RTX 5090: the Blackwell headline loses to
+ *             plain int4", section "Finding 3 - the real-FP4 path (QuTLASS
+ *             MXFP4)": the MXFP4 path rotates activations with an online
+ *             Hadamard transform before quantizing them.
+ *   [DIALECT], section "L'ecart de qualite - et comment il se reduit": the
+ *             overflow-aware scaling variant (OAS) picks the per-block scale
+ *             so that the block's extreme values do not saturate.
  *
  * Readings where the pages are silent (each is listed in the design notes):
  *   - E2M1 bit layout S|EE|M with exponent bias 1 (the only IEEE-style layout
@@ -48,6 +55,20 @@
  *     specification without printing its rule, so this rule is pinned only by
  *     invariants (block max lands on 4 or 6, nothing saturates), not by a value
  *     the pages print.
+ *   - Rotation (optional, either format): within each quantization block of
+ *     B values along k, y = H_B x / sqrt(B) with H_B the Sylvester Hadamard
+ *     matrix (H[i][j] = (-1)^popcount(i & j)); the pages give no rotation
+ *     size, and B keeps each rotation inside the block it feeds. The
+ *     rotation's output decides codes, so it is computed in the precision the
+ *     GPU path uses: binary32, as the fast transform (stages pairing i with
+ *     i + 1, then i + 2, i + 4, ...: a + b and a - b), one multiply by
+ *     RN_fp32(1/sqrt(B)) (exactly 1/4 for B = 16), then rounded to bf16
+ *     (nearest even), the activation type the quantizer takes. The weights
+ *     are rotated the same way, so the GEMM of the two rotated operands
+ *     approximates the unrotated product (H H^T / B = I).
+ *   - OAS (MXFP4 only): e_b = the smallest exponent with a_b <= 6 * 2^e_b
+ *     (clamped to [-127, 127]), so no element saturates; the default rule
+ *     lets block maxima in (6, 8) * 2^e_b saturate to 6 * 2^e_b.
  *
  * Precision: every decision is taken on exact values. bf16 inputs, E4M3 scales,
  * FP32 tensor scales and the thresholds t * s_b * S_t (<= 31 significant bits)
@@ -276,13 +297,26 @@ int orc_mx_exponent(double ab)
     return e;
 }
 
+/* OAS block exponent [DIALECT, quality-gap section]: the smallest e with
+ * ab <= 6 * 2^e, clamped to [-127, 127]. The default exponent leaves
+ * ab / 2^e in [4, 8); when that quotient exceeds 6 one more step brings it
+ * into (3, 4). 6 * 2^e is exact, so the comparison is exact. */
+int orc_mx_exponent_oas(double ab)
+{
+    int e = orc_mx_exponent(ab);
+    if (ab > 6.0 * ldexp(1.0, e) && e < 127)
+        e += 1;
+    return e;
+}
+
 /*
  * MXFP4 quantization [DIALECT]: blocks of 32 along k share one E8M0 scale
  * 2^e_b; elements are the nearest E2M1 codes of |x| / 2^e_b (same rounding
  * as NVFP4). Outputs codes[rows][k/2], scales[rows][k/32] (byte e_b + 127).
+ * oas != 0 takes the overflow-aware exponent instead of the default one.
  */
-int orc_quantize_mxfp4(const uint16_t *x, int64_t rows, int64_t k,
-                       uint8_t *codes, uint8_t *scales)
+int orc_quantize_mxfp4_rule(const uint16_t *x, int64_t rows, int64_t k, int oas,
+                            uint8_t *codes, uint8_t *scales)
 {
     if (k <= 0 || rows < 0 || k % 32 != 0)
         return -1;
@@ -292,13 +326,72 @@ int orc_quantize_mxfp4(const uint16_t *x, int64_t rows, int64_t k,
     for (int64_t r = 0; r < rows; ++r) {
         const uint16_t *xr = x + r * k;
         for (int64_t b = 0; b < k / 32; ++b) {
-            int e = orc_mx_exponent(orc_amax(xr + b * 32, 32));
+            double ab = orc_amax(xr + b * 32, 32);
+            int e = oas ? orc_mx_exponent_oas(ab) : orc_mx_exponent(ab);
             scales[r * (k / 32) + b] = (uint8_t)(e + 127);
             encode_block(xr + b * 32, 32, ldexp(1.0, e), nib + b * 32);
         }
         pack_row(nib, k, codes + r * (k / 2));
     }
     free(nib);
+    return 0;
+}
+
+int orc_quantize_mxfp4(const uint16_t *x, int64_t rows, int64_t k,
+                       uint8_t *codes, uint8_t *scales)
+{
+    return orc_quantize_mxfp4_rule(x, rows, k, 0, codes, scales);
+}
+
+/* --------------------------------------------------------------- rotation */
+
+/* binary32 -> bf16, nearest with ties to even (finite input; values past the
+ * bf16 range round to infinity). */
+static uint16_t f32_to_bf16_nearest_even(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    uint32_t lower = u & 0xFFFFu, upper = u >> 16;
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
+        upper += 1;
+    return (uint16_t)upper;
+}
+
+/* RN_fp32(1/sqrt(bs)): exactly 0.25 for 16; for 32 the binary64 value of
+ * 1/sqrt(32) is rounded to binary32 (a test checks it is the binary32 value
+ * nearest to the real 1/sqrt(32)). */
+float orc_hadamard_norm(int bs)
+{
+    return bs == 16 ? 0.25f : (float)(1.0 / sqrt((double)bs));
+}
+
+/*
+ * Rotation reading in the header [REALFP4]: out[r][b*bs + i] =
+ * bf16_RNE(fl32(sum_j H[i][j] x[r][b*bs + j]) * RN_fp32(1/sqrt(bs))), the sums
+ * formed by the binary32 fast transform. bs is 16 or 32, k a multiple of bs.
+ * Returns 0, or -1 on a bad argument.
+ */
+int orc_hadamard_bf16(const uint16_t *x, int64_t rows, int64_t k, int bs, uint16_t *out)
+{
+    if ((bs != 16 && bs != 32) || k <= 0 || rows < 0 || k % bs != 0)
+        return -1;
+    const float c = orc_hadamard_norm(bs);
+    float y[32];
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < k / bs; ++b) {
+            const uint16_t *xb = x + r * k + b * bs;
+            for (int i = 0; i < bs; ++i)
+                y[i] = (float)orc_bf16_value(xb[i]);   /* exact */
+            for (int span = 1; span < bs; span *= 2)
+                for (int i = 0; i < bs; ++i)
+                    if ((i & span) == 0) {
+                        float lo = y[i], hi = y[i + span];
+                        y[i] = lo + hi;
+                        y[i + span] = lo - hi;
+                    }
+            for (int i = 0; i < bs; ++i)
+                out[r * k + b * bs + i] = f32_to_bf16_nearest_even(y[i] * c);
+        }
     return 0;
 }
 

@@ -457,3 +457,151 @@ def test_bf16_ulp_and_tolerance():
     assert oracle.bf16_ulp(np.array([0.0]))[0] == 2.0 ** -133
     t = oracle.gemm_tolerance(np.array([2.0]), np.array([100.0]))
     assert t[0] == 1e-3 + 2.0 ** -6
+
+
+# ------------------------------------------------ block rotation (Hadamard)
+
+def _bf16_rne_of_f32(v32: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of float32 values, nearest even (numpy integer ops)."""
+    u = np.asarray(v32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lower, upper = u & 0xFFFF, u >> 16
+    up = (lower > 0x8000) | ((lower == 0x8000) & ((upper & 1) == 1))
+    return (upper + up).astype(np.uint16)
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_hadamard_matches_exact_sylvester_product(bs):
+    """Integer-valued blocks: the butterfly network equals the exact product
+    with scipy's Sylvester Hadamard matrix (every partial sum is an integer
+    below 2^24, so the binary32 transform is exact); then one binary32
+    multiply by the norm and one bf16 rounding."""
+    from scipy.linalg import hadamard as sylvester
+    rng = np.random.default_rng(31)
+    xi = rng.integers(-100, 101, (24, 4 * bs))
+    x = bf16_bits(xi.astype(np.float32))
+    assert np.array_equal(bf16_to_f32(x), xi.astype(np.float32))
+    h = sylvester(bs).astype(np.int64)
+    s = (xi.reshape(24, 4, bs) @ h.T).reshape(24, 4 * bs)           # exact integers
+    expect = _bf16_rne_of_f32(s.astype(np.float32) * oracle.hadamard_norm(bs))
+    assert np.array_equal(oracle.hadamard(x, bs), expect)
+    if bs == 16:   # the norm is exactly 1/4: a single rounding of the exact value
+        exact = s / 4.0
+        assert np.array_equal(oracle.hadamard(x, bs), _bf16_rne_of_f32(exact.astype(np.float32)))
+
+
+def test_hadamard_norm_is_nearest_binary32():
+    assert oracle.hadamard_norm(16) == np.float32(0.25)
+    c = oracle.hadamard_norm(32)
+    lo = Fraction(float(np.nextafter(c, np.float32(0))))
+    hi = Fraction(float(np.nextafter(c, np.float32(1))))
+    cf = Fraction(float(c))
+    # 1/sqrt(32) lies strictly between the midpoints around c
+    assert ((lo + cf) / 2) ** 2 < Fraction(1, 32) < ((cf + hi) / 2) ** 2
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_hadamard_closed_forms(bs):
+    """A constant block maps to (sqrt(bs) v, 0, ..., 0); a one-hot block at j
+    maps to v (-1)^popcount(i & j) / sqrt(bs) at every i."""
+    v = 1.5
+    const = np.full((1, bs), bf16_bits(np.float32([v]))[0], dtype=np.uint16)
+    out = bf16_to_f32(oracle.hadamard(const, bs)).astype(np.float64)[0]
+    assert abs(out[0] - v * math.sqrt(bs)) <= 2.0 ** -7 * v * math.sqrt(bs)
+    if bs == 16:
+        assert out[0] == 6.0
+    assert np.all(out[1:] == 0.0)
+    for j in range(bs):
+        x = np.zeros((1, bs), dtype=np.uint16)
+        x[0, j] = bf16_bits(np.float32([v]))[0]
+        y = bf16_to_f32(oracle.hadamard(x, bs)).astype(np.float64)[0]
+        signs = np.array([(-1) ** bin(i & j).count("1") for i in range(bs)])
+        assert np.array_equal(np.sign(y), signs)
+        assert np.all(np.abs(np.abs(y) - v / math.sqrt(bs)) <= 2.0 ** -8 * v / math.sqrt(bs))
+        if bs == 16:
+            assert np.array_equal(y, signs * v / 4)
+
+
+def test_hadamard_is_an_involution_on_exact_blocks():
+    """H_16 H_16 / 16 = I: rotating a one-hot block twice returns it exactly
+    (every intermediate value is exact in binary32 and bf16)."""
+    rng = np.random.default_rng(7)
+    for _ in range(20):
+        x = np.zeros((1, 16), dtype=np.float32)
+        x[0, rng.integers(16)] = rng.choice([-3.0, 0.75, 2.5, -40.0])
+        xb = bf16_bits(x)
+        assert np.array_equal(oracle.hadamard(oracle.hadamard(xb, 16), 16), xb)
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_hadamard_error_bound_on_gaussian_data(bs):
+    """General inputs: within one bf16 rounding plus the binary32 transform's
+    error (log2(bs) additions and one multiply, each <= 2^-24 relative of the
+    running magnitudes) of the exact real rotation."""
+    from scipy.linalg import hadamard as sylvester
+    rng = np.random.default_rng(5)
+    x = bf16_bits((rng.standard_normal((16, 8 * bs)) * 2.0 ** rng.uniform(-10, 10, (16, 1)))
+                  .astype(np.float32))
+    xv = bf16_to_f32(x).astype(np.float64).reshape(16, 8, bs)
+    exact = (xv @ sylvester(bs).T.astype(np.float64)) / math.sqrt(bs)   # exact to ~2^-50
+    mag = np.abs(xv).sum(axis=-1, keepdims=True) / math.sqrt(bs)
+    got = bf16_to_f32(oracle.hadamard(x, bs)).astype(np.float64).reshape(16, 8, bs)
+    bound = 2.0 ** -8 * np.abs(exact) + (math.log2(bs) + 2) * 2.0 ** -24 * mag * 1.01
+    assert np.all(np.abs(got - exact) <= bound)
+
+
+# -------------------------------------------------------------- MXFP4 OAS
+
+def _oas_brute(a: float) -> int:
+    """Smallest e in [-127, 127] with a <= 6 * 2^e, by search."""
+    for e in range(-127, 128):
+        if Fraction(a) <= 6 * Fraction(2) ** e:
+            return e
+    return 127
+
+
+def test_mx_oas_exponent_brute_force():
+    rng = np.random.default_rng(17)
+    vals = list(bf16_to_f32(rng.integers(1, 0x7F80, 3000).astype(np.uint16)).astype(np.float64))
+    for e in (-120, -3, 0, 1, 5, 100):
+        vals += [6 * 2.0 ** e, np.nextafter(6 * 2.0 ** e, np.inf), 4 * 2.0 ** e, 7 * 2.0 ** e]
+    for a in vals:
+        assert oracle.mx_exponent_oas(a) == _oas_brute(a), a
+    assert oracle.mx_exponent_oas(0.0) == -127
+
+
+def test_mx_oas_block_of_seven():
+    """A block whose maximum is 7: the default rule saturates it to 6 (scale 1),
+    the overflow-aware rule takes scale 2 and codes it as 4 * 2 = 8 (7/2 = 3.5
+    is the 3|4 midpoint, tie to the even index)."""
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, 0], x[0, 1] = 7.0, 1.0
+    xb = bf16_bits(x)
+    qd, qo = oracle.quantize_mxfp4(xb), oracle.quantize_mxfp4(xb, oas=True)
+    assert E8M0_TABLE[qd.scales[0, 0]] == 1.0 and oracle.dequantize(qd)[0, 0] == 6.0
+    assert E8M0_TABLE[qo.scales[0, 0]] == 2.0 and oracle.dequantize(qo)[0, 0] == 8.0
+    assert oracle.dequantize(qo)[0, 1] == 1.0
+
+
+def test_mx_oas_never_saturates():
+    rng = np.random.default_rng(19)
+    x = bf16_bits((rng.standard_normal((32, 1024)) * 2.0 ** rng.uniform(-20, 20, (32, 1)))
+                  .astype(np.float32))
+    q = oracle.quantize_mxfp4(x, oas=True)
+    xv = np.abs(bf16_to_f32(x).astype(np.float64)).reshape(32, 32, 32)
+    scale = E8M0_TABLE[q.scales]
+    ab = xv.max(axis=2)
+    assert np.all(ab <= 6 * scale) and np.all(ab > 3 * scale)
+    # where the default rule keeps the maximum at or below 6 the rules agree
+    qd = oracle.quantize_mxfp4(x)
+    same = (ab / E8M0_TABLE[qd.scales]) <= 6
+    assert np.array_equal(q.scales[same], qd.scales[same])
+    assert np.array_equal(unpack(q.codes).reshape(32, 32, 32)[same],
+                          unpack(qd.codes).reshape(32, 32, 32)[same])
+
+
+def test_rotated_quantize_composes_rotation_and_quantizer():
+    x = bf16_bits(np.random.default_rng(3).standard_normal((8, 256)).astype(np.float32))
+    for fmt in (oracle.NVFP4, oracle.MXFP4):
+        q = oracle.quantize(fmt, x, rotate=True)
+        q2 = oracle.quantize(fmt, oracle.hadamard(x, oracle.BLOCK[fmt]))
+        assert np.array_equal(q.codes, q2.codes) and np.array_equal(q.scales, q2.scales)
