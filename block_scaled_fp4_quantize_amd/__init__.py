@@ -23,6 +23,9 @@ import threading
 import torch
 
 NVFP4, MXFP4 = 0, 1
+# recipe flags OR-ed into a format (include/fp4.h): block Hadamard rotation
+# before quantization; MXFP4 overflow-aware block exponent
+ROTATE, MX_OAS = 0x100, 0x200
 CANONICAL, TILED = 0, 1
 WEIGHT_TILED = TILED
 FORMATS = {"nvfp4": NVFP4, "mxfp4": MXFP4}
@@ -109,11 +112,18 @@ def _ptr(t: torch.Tensor | None):
 
 
 def _fmt(fmt) -> int:
+    """A format: NVFP4/MXFP4 (or "nvfp4"/"mxfp4", optionally with "+rotate"
+    and "+oas" suffixes), possibly OR-ed with ROTATE / MX_OAS."""
     if isinstance(fmt, str):
-        return FORMATS[fmt.lower()]
-    if fmt not in (NVFP4, MXFP4):
-        raise ValueError("format must be NVFP4 (0) or MXFP4 (1)")
-    return int(fmt)
+        parts = fmt.lower().split("+")
+        flags = {"rotate": ROTATE, "oas": MX_OAS}
+        fmt = FORMATS[parts[0]]
+        for p in parts[1:]:
+            fmt |= flags[p]
+    fmt = int(fmt)
+    if fmt & 0xFF not in (NVFP4, MXFP4) or fmt & ~(0xFF | ROTATE | MX_OAS):
+        raise ValueError("format must be NVFP4 (0) or MXFP4 (1), optionally | ROTATE | MX_OAS")
+    return fmt
 
 
 def _bf16_2d(x: torch.Tensor, name: str) -> torch.Tensor:

@@ -59,7 +59,23 @@ fp4_status check_device() {
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
-bool valid_fmt(int32_t f) { return f == FP4_NVFP4 || f == FP4_MXFP4; }
+
+// A format value is a base format (low byte) with optional recipe flags.
+int base_fmt(int32_t f) { return f & 0xFF; }
+uint32_t recipe_of(int32_t f) {
+  return ((f & FP4_ROTATE) ? kRecipeRotate : 0u) | ((f & FP4_MX_OAS) ? kRecipeOas : 0u);
+}
+bool valid_fmt(int32_t f) {
+  const int b = base_fmt(f);
+  if (b != FP4_NVFP4 && b != FP4_MXFP4) return false;
+  if (f & ~(0xFF | FP4_ROTATE | FP4_MX_OAS)) return false;
+  return !(f & FP4_MX_OAS) || b == FP4_MXFP4;
+}
+// Operands of one product: same base format and both rotated or neither (the
+// block exponent rule may differ).
+bool same_product_fmt(int32_t a, int32_t w) {
+  return base_fmt(a) == base_fmt(w) && (a & FP4_ROTATE) == (w & FP4_ROTATE);
+}
 bool valid_layout(int32_t l) { return l == FP4_LAYOUT_CANONICAL || l == FP4_LAYOUT_TILED; }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -69,9 +85,9 @@ fp4_status check_shape(int32_t fmt, int64_t rows, int64_t k) {
   if (rows <= 0 || k <= 0) return fail(FP4_ERR_INVALID_ARG, "rows and k must be positive");
   if (rows > (int64_t)1 << 30 || k > (int64_t)1 << 30)
     return fail(FP4_ERR_SHAPE, "rows or k too large");
-  if (k % block_of(fmt) != 0)
-    return fail(FP4_ERR_SHAPE, "k=%lld is not a multiple of the block size %d", (long long)k,
-                block_of(fmt));
+  const int bs = block_of(base_fmt(fmt));
+  if (k % bs != 0)
+    return fail(FP4_ERR_SHAPE, "k=%lld is not a multiple of the block size %d", (long long)k, bs);
   return FP4_OK;
 }
 
@@ -84,20 +100,21 @@ fp4_status check_tensor(const fp4_tensor *t, const char *name) {
   if (!t->codes || !t->scales) return fail(FP4_ERR_INVALID_ARG, "%s: null buffer", name);
   if (!aligned16(t->codes) || !aligned16(t->scales))
     return fail(FP4_ERR_ALIGNMENT, "%s: buffers must be 16-byte aligned", name);
-  if (t->fmt == FP4_NVFP4 && !t->tensor_scale)
+  const int base = base_fmt(t->fmt);
+  if (base == FP4_NVFP4 && !t->tensor_scale)
     return fail(FP4_ERR_INVALID_ARG, "%s: NVFP4 needs a tensor_scale pointer", name);
   if (t->layout == FP4_LAYOUT_CANONICAL) {
     int64_t kp = k_pad(t->cols);
-    if (t->codes_pitch < kp / 2 || t->scales_pitch < kp / block_of(t->fmt))
+    if (t->codes_pitch < kp / 2 || t->scales_pitch < kp / block_of(base))
       return fail(FP4_ERR_SHAPE, "%s: pitch smaller than K_pad", name);
-    if (t->codes_pitch % 16 != 0 || (t->fmt == FP4_NVFP4 && t->scales_pitch % 2 != 0))
+    if (t->codes_pitch % 16 != 0 || (base == FP4_NVFP4 && t->scales_pitch % 2 != 0))
       return fail(FP4_ERR_ALIGNMENT, "%s: codes pitch must be a multiple of 16 bytes and "
                   "NVFP4 scales pitch even", name);
   }
   return FP4_OK;
 }
 
-size_t quant_ws(int32_t fmt) { return fmt == FP4_NVFP4 ? kQuantScratchBytes : 0; }
+size_t quant_ws(int32_t fmt) { return base_fmt(fmt) == FP4_NVFP4 ? kQuantScratchBytes : 0; }
 
 // Everything fp4_linear keeps in its workspace: the quantizer's scratch (its
 // exchange words persist from call to call) at offset 0 whatever the call's
@@ -114,7 +131,7 @@ LinearLayout linear_layout(int32_t fmt, int64_t m, int64_t k) {
   L.scratch = off; off = align256(off + kQuantScratchBytes);
   L.ts = off; off = align256(off + sizeof(float));
   L.codes = off; off = align256(off + (size_t)(mp * kp / 2));
-  L.scales = off; off = align256(off + (size_t)(mp * kp / block_of(fmt)));
+  L.scales = off; off = align256(off + (size_t)(mp * kp / block_of(base_fmt(fmt))));
   L.total = off;
   return L;
 }
@@ -122,9 +139,11 @@ LinearLayout linear_layout(int32_t fmt, int64_t m, int64_t k) {
 fp4_status run_quant(int32_t fmt, int tiled, const void *x, int64_t rows, int64_t k,
                      const float *static_scale, const fp4_tensor *out, void *scratch,
                      hipStream_t stream) {
-  hipError_t e = launch_quantize(fmt, tiled, (const uint16_t *)x, rows, k, static_scale,
-                                 (uint8_t *)out->codes, out->codes_pitch, (uint8_t *)out->scales,
-                                 out->scales_pitch, fmt == FP4_NVFP4 ? out->tensor_scale : nullptr,
+  const int base = base_fmt(fmt);
+  hipError_t e = launch_quantize(base, recipe_of(fmt), tiled, (const uint16_t *)x, rows, k,
+                                 static_scale, (uint8_t *)out->codes, out->codes_pitch,
+                                 (uint8_t *)out->scales, out->scales_pitch,
+                                 base == FP4_NVFP4 ? out->tensor_scale : nullptr,
                                  (uint32_t *)scratch, stream);
   if (e != hipSuccess) return hip_fail(e, "quantize launch");
   return FP4_OK;
@@ -133,7 +152,7 @@ fp4_status run_quant(int32_t fmt, int tiled, const void *x, int64_t rows, int64_
 fp4_status run_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c, int64_t ldc,
                     hipStream_t stream) {
   GemmArgs g;
-  g.fmt = a->fmt;
+  g.fmt = base_fmt(a->fmt);
   g.a_tiled = a->layout == FP4_LAYOUT_TILED;
   g.a_codes = (const uint8_t *)a->codes; g.a_cpitch = a->codes_pitch;
   g.a_scales = (const uint8_t *)a->scales; g.a_spitch = a->scales_pitch;
@@ -155,7 +174,7 @@ fp4_status run_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c, int64_t l
 
 extern "C" {
 
-int32_t fp4_block_size(int32_t fmt) { return valid_fmt(fmt) ? block_of(fmt) : 0; }
+int32_t fp4_block_size(int32_t fmt) { return valid_fmt(fmt) ? block_of(base_fmt(fmt)) : 0; }
 
 size_t fp4_codes_bytes(int32_t fmt, int32_t layout, int64_t rows, int64_t k) {
   if (!valid_fmt(fmt) || !valid_layout(layout) || rows <= 0 || k <= 0) return 0;
@@ -166,7 +185,7 @@ size_t fp4_codes_bytes(int32_t fmt, int32_t layout, int64_t rows, int64_t k) {
 size_t fp4_scales_bytes(int32_t fmt, int32_t layout, int64_t rows, int64_t k) {
   if (!valid_fmt(fmt) || !valid_layout(layout) || rows <= 0 || k <= 0) return 0;
   int64_t r = layout == FP4_LAYOUT_TILED ? round_up(rows, 16) : rows;
-  return (size_t)(r * (k_pad(k) / block_of(fmt)));
+  return (size_t)(r * (k_pad(k) / block_of(base_fmt(fmt))));
 }
 
 fp4_status fp4_tensor_init(fp4_tensor *t, int32_t fmt, int32_t layout, int64_t rows, int64_t k,
@@ -180,7 +199,7 @@ fp4_status fp4_tensor_init(fp4_tensor *t, int32_t fmt, int32_t layout, int64_t r
   t->rows = rows;
   t->cols = k;
   t->codes_pitch = layout == FP4_LAYOUT_CANONICAL ? k_pad(k) / 2 : 0;
-  t->scales_pitch = layout == FP4_LAYOUT_CANONICAL ? k_pad(k) / block_of(fmt) : 0;
+  t->scales_pitch = layout == FP4_LAYOUT_CANONICAL ? k_pad(k) / block_of(base_fmt(fmt)) : 0;
   t->codes = codes;
   t->scales = scales;
   t->tensor_scale = tensor_scale;
@@ -224,7 +243,7 @@ fp4_status fp4_quantize_act(int32_t fmt, const void *a_bf16, int64_t m, int64_t 
   if ((st = check_tensor(out, "out")) != FP4_OK) return st;
   if (out->fmt != fmt || out->rows != m || out->cols != k)
     return fail(FP4_ERR_FORMAT_MISMATCH, "out descriptor does not match format/shape");
-  if (fmt == FP4_MXFP4 && static_scale)
+  if (base_fmt(fmt) == FP4_MXFP4 && static_scale)
     return fail(FP4_ERR_INVALID_ARG, "MXFP4 has no per-tensor scale");
   size_t need = static_scale ? 0 : quant_ws(fmt);
   if (workspace_bytes < need || (need && !workspace))
@@ -251,7 +270,8 @@ fp4_status fp4_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c_bf16, int6
   if ((st = check_tensor(w, "w")) != FP4_OK) return st;
   if (w->layout != FP4_LAYOUT_TILED)
     return fail(FP4_ERR_FORMAT_MISMATCH, "w must be in the TILED layout");
-  if (a->fmt != w->fmt) return fail(FP4_ERR_FORMAT_MISMATCH, "a and w differ in format");
+  if (!same_product_fmt(a->fmt, w->fmt))
+    return fail(FP4_ERR_FORMAT_MISMATCH, "a and w differ in format or rotation");
   if (a->cols != w->cols) return fail(FP4_ERR_SHAPE, "a and w differ in K");
   if (!c_bf16) return fail(FP4_ERR_INVALID_ARG, "output pointer is null");
   if (ldc < w->rows) return fail(FP4_ERR_SHAPE, "ldc smaller than N");
@@ -280,7 +300,8 @@ fp4_status fp4_linear(const void *x_bf16, int64_t m, const fp4_tensor *w,
   if (!x_bf16 || !y_bf16) return fail(FP4_ERR_INVALID_ARG, "null input or output");
   if (!aligned16(x_bf16)) return fail(FP4_ERR_ALIGNMENT, "input must be 16-byte aligned");
   if (((uintptr_t)y_bf16 & 1u) != 0) return fail(FP4_ERR_ALIGNMENT, "output must be 2-byte aligned");
-  if (fmt == FP4_MXFP4 && static_scale)
+  const int base = base_fmt(fmt);
+  if (base == FP4_MXFP4 && static_scale)
     return fail(FP4_ERR_INVALID_ARG, "MXFP4 has no per-tensor scale");
   const LinearLayout L = linear_layout(fmt, m, k);
   if (!workspace || workspace_bytes < L.total)
@@ -288,8 +309,9 @@ fp4_status fp4_linear(const void *x_bf16, int64_t m, const fp4_tensor *w,
   if (!aligned16(workspace)) return fail(FP4_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
   if ((st = check_device()) != FP4_OK) return st;
 
-  if (linear_fused_ok(fmt, m, n, k)) {
-    hipError_t e = launch_linear_fused(fmt, (const uint16_t *)x_bf16, m, k, static_scale,
+  if (linear_fused_ok(base, m, n, k)) {
+    hipError_t e = launch_linear_fused(base, recipe_of(fmt), (const uint16_t *)x_bf16, m, k,
+                                       static_scale,
                                        (const uint8_t *)w->codes, (const uint8_t *)w->scales,
                                        w->tensor_scale, n, (uint16_t *)y_bf16, n, stream);
     if (e != hipSuccess) return hip_fail(e, "fused linear launch");
@@ -313,9 +335,11 @@ fp4_status fp4_linear(const void *x_bf16, int64_t m, const fp4_tensor *w,
 }
 
 int32_t fp4_linear_launches(int32_t fmt, int64_t m, int64_t n, int64_t k, int32_t static_scale) {
-  if (!valid_fmt(fmt) || m <= 0 || n <= 0 || k <= 0 || k % block_of(fmt) != 0) return 0;
-  if (linear_fused_ok(fmt, m, n, k)) return 1;
-  if (fmt == FP4_NVFP4 && !static_scale && !quant_fits_small(fmt, m, k, 1)) return 3;
+  if (!valid_fmt(fmt) || m <= 0 || n <= 0 || k <= 0) return 0;
+  const int base = base_fmt(fmt);
+  if (k % block_of(base) != 0) return 0;
+  if (linear_fused_ok(base, m, n, k)) return 1;
+  if (base == FP4_NVFP4 && !static_scale && !quant_fits_small(base, m, k, 1)) return 3;
   return 2;
 }
 
@@ -330,12 +354,13 @@ fp4_status fp4_export_canonical(const fp4_tensor *tiled, fp4_tensor *canonical,
       tiled->cols != canonical->cols)
     return fail(FP4_ERR_FORMAT_MISMATCH, "descriptors differ in format or shape");
   if ((st = check_device()) != FP4_OK) return st;
+  const int base = base_fmt(tiled->fmt);
   hipError_t e = launch_export_canonical(
-      tiled->fmt, (const uint8_t *)tiled->codes, (const uint8_t *)tiled->scales, tiled->rows,
+      base, (const uint8_t *)tiled->codes, (const uint8_t *)tiled->scales, tiled->rows,
       tiled->cols, (uint8_t *)canonical->codes, canonical->codes_pitch,
       (uint8_t *)canonical->scales, canonical->scales_pitch,
-      tiled->fmt == FP4_NVFP4 ? tiled->tensor_scale : nullptr,
-      tiled->fmt == FP4_NVFP4 ? canonical->tensor_scale : nullptr, stream);
+      base == FP4_NVFP4 ? tiled->tensor_scale : nullptr,
+      base == FP4_NVFP4 ? canonical->tensor_scale : nullptr, stream);
   if (e != hipSuccess) return hip_fail(e, "export launch");
   return ok();
 }
@@ -347,10 +372,11 @@ fp4_status fp4_dequantize(const fp4_tensor *t, float *out_f32, int64_t ldo, hipS
   if (ldo < t->cols) return fail(FP4_ERR_SHAPE, "ldo smaller than K");
   if (((uintptr_t)out_f32 & 3u) != 0) return fail(FP4_ERR_ALIGNMENT, "output must be 4-byte aligned");
   if ((st = check_device()) != FP4_OK) return st;
-  hipError_t e = launch_dequant(t->fmt, t->layout == FP4_LAYOUT_TILED,
+  const int base = base_fmt(t->fmt);
+  hipError_t e = launch_dequant(base, t->layout == FP4_LAYOUT_TILED,
                                 (const uint8_t *)t->codes, t->codes_pitch,
                                 (const uint8_t *)t->scales, t->scales_pitch,
-                                t->fmt == FP4_NVFP4 ? t->tensor_scale : nullptr, t->rows, t->cols,
+                                base == FP4_NVFP4 ? t->tensor_scale : nullptr, t->rows, t->cols,
                                 out_f32, ldo, stream);
   if (e != hipSuccess) return hip_fail(e, "dequantize launch");
   return ok();

@@ -147,9 +147,14 @@ __device__ __forceinline__ uint32_t nv_encode8(const NvBlockEnc &e, uint4 v) {
 // MXFP4 block exponent from the block maximum's bf16 bits (sign clear):
 // e = clamp(floor(log2 a) - 2, -127, 127); the scale byte is e + 127.
 // bf16 subnormals and zero have floor(log2 a) <= -127, so they clamp to -127.
-__device__ __forceinline__ int mx_exponent_from_bits(uint32_t abits) {
+// The overflow-aware rule (oas) takes the smallest e with a <= 6 * 2^e: with
+// a = m * 2^E (m in [1, 2)) the default quotient a / 2^e is 4m, so one more
+// step is needed exactly when m > 1.5, i.e. when the 7 stored mantissa bits
+// exceed 0x40 (for the blocks that clamp to -127, a < 4 * 2^-127 already).
+__device__ __forceinline__ int mx_exponent_from_bits(uint32_t abits, bool oas = false) {
   int ef = (int)(abits >> 7);      // biased exponent field
   int e = ef - 129;                // floor(log2 a) - 2 for normal a
+  if (oas && (abits & 0x7Fu) > 0x40u) e += 1;
   return e < -127 ? -127 : e;
 }
 
@@ -249,15 +254,61 @@ __device__ __forceinline__ void nv_encode_block(uint4 v0, uint4 v1, float st, ui
   }
 }
 
-// One MXFP4 block (32 values in v[0..3]): 16 code bytes and the E8M0 byte.
+// One MXFP4 block (32 values in v[0..3]): 16 code bytes and the E8M0 byte;
+// oas selects the overflow-aware block exponent.
 __device__ __forceinline__ void mx_encode_block(const uint4 (&v)[4], uint4 &codes,
-                                                uint32_t &sbyte) {
+                                                uint32_t &sbyte, bool oas = false) {
   const uint32_t abits = max(max(absmax_bits8(v[0]), absmax_bits8(v[1])),
                              max(absmax_bits8(v[2]), absmax_bits8(v[3])));
-  const int e = mx_exponent_from_bits(abits);
+  const int e = mx_exponent_from_bits(abits, oas);
   codes = make_uint4(mx_encode8(e, v[0]), mx_encode8(e, v[1]), mx_encode8(e, v[2]),
                      mx_encode8(e, v[3]));
   sbyte = (uint32_t)(e + 127);
+}
+
+// ---- block rotation ----
+//
+// y = H_B x / sqrt(B) over one block of B bf16 values held as B/8 uint4 (value
+// 8i + 2j + h in the h-th half of dword j of v[i]), H_B the Sylvester Hadamard
+// matrix, as the MXFP4 path of "FP4 on a consumer RTX 5090: the Blackwell
+// headline loses to plain int4" (section "Finding 3") rotates activations
+// before quantizing them. The rotation size is the block, so every rotation
+// stays inside the block it feeds. Binary32 fast transform (stages pairing
+// i with i + 1, i + 2, i + 4, ...: a + b, a - b; no contraction, as the
+// library is built), one multiply by RN_fp32(1/sqrt(B)) (exactly 1/4 for
+// B = 16), then bf16 nearest-even: the values the block encoders take.
+template <int B>
+__device__ __forceinline__ void hadamard_block(uint4 (&v)[B / 8]) {
+  static_assert(B == 16 || B == 32, "rotation size is a block: 16 or 32 values");
+  float y[B];
+#pragma unroll
+  for (int i = 0; i < B / 8; ++i) {
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      y[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+      y[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  }
+#pragma unroll
+  for (int span = 1; span < B; span *= 2)
+#pragma unroll
+    for (int i = 0; i < B; ++i)
+      if ((i & span) == 0) {
+        const float lo = y[i], hi = y[i + span];
+        y[i] = lo + hi;
+        y[i + span] = lo - hi;
+      }
+  const float c = B == 16 ? 0.25f : 0x1.6a09e6p-3f;  // RN_fp32(1/sqrt(32))
+#pragma unroll
+  for (int i = 0; i < B / 8; ++i) {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = (uint32_t)f32_to_bf16_rne(y[8 * i + 2 * j] * c) |
+             ((uint32_t)f32_to_bf16_rne(y[8 * i + 2 * j + 1] * c) << 16);
+    v[i] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
 }
 
 // ---- decode side ----

@@ -33,12 +33,18 @@ bool quant_fits_small(int fmt, int64_t rows, int64_t k, int tiled);
 
 // ---- launchers (all asynchronous on `stream`) ----
 
+// Quantization recipe bits: rotate every block (block Hadamard) before it is
+// quantized; MXFP4 overflow-aware block exponent.
+constexpr uint32_t kRecipeRotate = 1u;
+constexpr uint32_t kRecipeOas = 2u;
+
 // Quantize x [rows, k] (bf16, row-major) into the canonical (tiled = 0) or
 // fragment-tiled (tiled = 1) layout; fmt 0 = NVFP4, 1 = MXFP4. NVFP4 takes S_t
-// from *static_scale when non-null, else from the tensor's maximum; writes
-// *ts_out when non-null. `scratch` holds kQuantScratchBytes.
-hipError_t launch_quantize(int fmt, int tiled, const uint16_t *x, int64_t rows, int64_t k,
-                           const float *static_scale, uint8_t *codes, int64_t cpitch,
+// from *static_scale when non-null, else from the tensor's maximum (of the
+// rotated values when rotating); writes *ts_out when non-null. `scratch` holds
+// kQuantScratchBytes.
+hipError_t launch_quantize(int fmt, uint32_t recipe, int tiled, const uint16_t *x, int64_t rows,
+                           int64_t k, const float *static_scale, uint8_t *codes, int64_t cpitch,
                            uint8_t *scales, int64_t spitch, float *ts_out, uint32_t *scratch,
                            hipStream_t stream);
 
@@ -77,7 +83,7 @@ constexpr int64_t kFusedMaxMK = 65536;        // M * K_pad bound (LDS staging, M
 constexpr int64_t kFusedMaxWork = 16 << 20;   // M * K_pad * N tiles bound
 constexpr int64_t kFusedMaxTilesNv = 512;      // NVFP4: at most this many weight tiles
 bool linear_fused_ok(int fmt, int64_t m, int64_t n, int64_t k);
-hipError_t launch_linear_fused(int fmt, const uint16_t *x, int64_t m, int64_t k,
+hipError_t launch_linear_fused(int fmt, uint32_t recipe, const uint16_t *x, int64_t m, int64_t k,
                                const float *static_scale, const uint8_t *w_codes,
                                const uint8_t *w_scales, const float *w_ts, int64_t n,
                                uint16_t *y, int64_t ldy, hipStream_t stream);

@@ -259,9 +259,11 @@ template <int FMT>
 __global__ __launch_bounds__(64 * kDecWaves) void k_linear_decode(
     const uint16_t *__restrict__ x, int m, int k, const float *__restrict__ static_scale,
     const uint8_t *__restrict__ w_codes, const uint8_t *__restrict__ w_sc,
-    const float *__restrict__ w_ts, int n, int kt_n, uint16_t *__restrict__ y, int64_t ldy) {
+    const float *__restrict__ w_ts, int n, int kt_n, uint16_t *__restrict__ y, int64_t ldy,
+    uint32_t recipe) {
   constexpr int NW = kDecWaves, FM = kDecFrags;
   constexpr int B = FMT == 0 ? 16 : 32, V = B / 8;
+  const bool rot = recipe & kRecipeRotate;
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ float red[NW][4][64];
   __shared__ uint32_t lmax[NW];
@@ -294,7 +296,9 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_linear_decode(
       for (int t = threadIdx.x; t < m * nb; t += 64 * NW) {
         const int r = t / nb, c = t - r * nb;
         const uint4 *src = (const uint4 *)(x + (int64_t)r * k + c * B);
-        amax = max(amax, max(absmax_bits8(src[0]), absmax_bits8(src[1])));
+        uint4 v[2] = {src[0], src[1]};
+        if (rot) hadamard_block<16>(v);
+        amax = max(amax, max(absmax_bits8(v[0]), absmax_bits8(v[1])));
       }
       st = tensor_scale_from_amax(bf16_bits_to_f32(block_max_u32(amax, lmax)));
     }
@@ -307,6 +311,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_linear_decode(
       const uint4 *src = (const uint4 *)(x + (int64_t)r * k + c * B);
 #pragma unroll
       for (int i = 0; i < V; ++i) v[i] = src[i];
+      if (rot) hadamard_block<B>(v);
     }
     if constexpr (FMT == 0) {
       uint4 *dst = (uint4 *)(smem + r * ap + c * 32);
@@ -323,7 +328,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_linear_decode(
     } else {
       uint4 q = make_uint4(0u, 0u, 0u, 0u);
       uint32_t sbyte = 0;
-      if (c < nb) mx_encode_block(v, q, sbyte);
+      if (c < nb) mx_encode_block(v, q, sbyte, recipe & kRecipeOas);
       *(uint4 *)(smem + r * ap + c * 16) = q;
       lscales[r * sp + c] = (uint8_t)sbyte;
     }
@@ -427,7 +432,7 @@ bool linear_fused_ok(int fmt, int64_t m, int64_t n, int64_t k) {
          mk * nt <= kFusedMaxWork && (fmt != 0 || nt <= kFusedMaxTilesNv);
 }
 
-hipError_t launch_linear_fused(int fmt, const uint16_t *x, int64_t m, int64_t k,
+hipError_t launch_linear_fused(int fmt, uint32_t recipe, const uint16_t *x, int64_t m, int64_t k,
                                const float *static_scale, const uint8_t *w_codes,
                                const uint8_t *w_scales, const float *w_ts, int64_t n,
                                uint16_t *y, int64_t ldy, hipStream_t stream) {
@@ -437,10 +442,12 @@ hipError_t launch_linear_fused(int fmt, const uint16_t *x, int64_t m, int64_t k,
                               : (size_t)m * (kt_n * 64 + 16) + (size_t)m * kt_n * 4;
   if (fmt == 0)
     hipLaunchKernelGGL(k_linear_decode<0>, dim3(nt_n), dim3(64 * kDecWaves), lds, stream, x,
-                       (int)m, (int)k, static_scale, w_codes, w_scales, w_ts, (int)n, kt_n, y, ldy);
+                       (int)m, (int)k, static_scale, w_codes, w_scales, w_ts, (int)n, kt_n, y, ldy,
+                       recipe);
   else
     hipLaunchKernelGGL(k_linear_decode<1>, dim3(nt_n), dim3(64 * kDecWaves), lds, stream, x,
-                       (int)m, (int)k, static_scale, w_codes, w_scales, w_ts, (int)n, kt_n, y, ldy);
+                       (int)m, (int)k, static_scale, w_codes, w_scales, w_ts, (int)n, kt_n, y, ldy,
+                       recipe);
   return hipGetLastError();
 }
 

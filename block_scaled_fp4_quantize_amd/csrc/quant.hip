@@ -72,10 +72,20 @@ __device__ __forceinline__ uint32_t block_absmax(const uint4 (&v)[Blk<FMT>::V]) 
   return m;
 }
 
+// Recipe bits (a kernel argument, uniform over the grid): rotate each block
+// before anything else looks at its values; MXFP4 overflow-aware exponent.
+__device__ __forceinline__ bool rotates(uint32_t recipe) { return recipe & kRecipeRotate; }
+__device__ __forceinline__ bool oas_rule(uint32_t recipe) { return recipe & kRecipeOas; }
+
+template <int FMT>
+__device__ __forceinline__ void maybe_rotate(uint4 (&v)[Blk<FMT>::V], uint32_t recipe) {
+  if (rotates(recipe)) hadamard_block<Blk<FMT>::B>(v);
+}
+
 // Encode one block (values in v) and store codes + scale byte.
 template <int FMT>
 __device__ __forceinline__ void encode_store(const uint4 (&v)[Blk<FMT>::V], float st,
-                                             uint8_t *cdst, uint8_t *sdst) {
+                                             uint8_t *cdst, uint8_t *sdst, uint32_t recipe) {
   uint32_t sbyte;
   if constexpr (FMT == 0) {
     uint2 c;
@@ -83,7 +93,7 @@ __device__ __forceinline__ void encode_store(const uint4 (&v)[Blk<FMT>::V], floa
     *(uint2 *)cdst = c;
   } else {
     uint4 c;
-    mx_encode_block(v, c, sbyte);
+    mx_encode_block(v, c, sbyte, oas_rule(recipe));
     *(uint4 *)cdst = c;
   }
   *sdst = (uint8_t)sbyte;
@@ -109,6 +119,24 @@ __global__ __launch_bounds__(kThreads) void k_amax_parts(const uint4 *__restrict
   if (threadIdx.x == 0) parts[blockIdx.x] = m;
 }
 
+// Partial maxima of the rotated tensor (NVFP4 with rotation): block by block,
+// each block rotated first. nblocks = rows * k / 16 (blocks never straddle
+// rows, k being a multiple of 16).
+__global__ __launch_bounds__(kThreads) void k_amax_parts_rot(const uint4 *__restrict__ x,
+                                                             int64_t nblocks,
+                                                             uint32_t *__restrict__ parts) {
+  __shared__ uint32_t lds[4];
+  uint32_t m = 0;
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nblocks; i += stride) {
+    uint4 v[2] = {x[2 * i], x[2 * i + 1]};
+    hadamard_block<16>(v);
+    m = max(m, max(absmax_bits8(v[0]), absmax_bits8(v[1])));
+  }
+  m = block_max_u32(m, lds);
+  if (threadIdx.x == 0) parts[blockIdx.x] = m;
+}
+
 // Grid-stride over every block of the padded output; S_t (NVFP4) from the
 // static value or the fold of the partial maxima.
 template <int FMT, int TILED>
@@ -116,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void k_quant(
     const uint16_t *__restrict__ x, int64_t rows, int64_t k, int64_t rows_pad, int64_t kt_n,
     const uint32_t *__restrict__ parts, int nparts, const float *__restrict__ static_scale,
     uint8_t *__restrict__ codes, int64_t cpitch, uint8_t *__restrict__ scales, int64_t spitch,
-    float *__restrict__ ts_out) {
+    float *__restrict__ ts_out, uint32_t recipe) {
   using K = Blk<FMT>;
   __shared__ uint32_t lds[4];
   float st = 1.0f;
@@ -144,7 +172,8 @@ __global__ __launch_bounds__(kThreads) void k_quant(
     const uint4 *src = (const uint4 *)(x + r * k + b * K::B);
 #pragma unroll
     for (int i = 0; i < K::V; ++i) v[i] = src[i];
-    encode_store<FMT>(v, st, cdst, sdst);
+    maybe_rotate<FMT>(v, recipe);
+    encode_store<FMT>(v, st, cdst, sdst, recipe);
   }
 }
 
@@ -158,7 +187,8 @@ template <int FMT>
 __global__ __launch_bounds__(kThreads) void k_quant_tiled(
     const uint16_t *__restrict__ x, int64_t rows, int64_t k, int64_t rows_pad, int64_t kt_n,
     const uint32_t *__restrict__ parts, int nparts, const float *__restrict__ static_scale,
-    uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, float *__restrict__ ts_out) {
+    uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, float *__restrict__ ts_out,
+    uint32_t recipe) {
   using K = Blk<FMT>;
   __shared__ uint32_t lds[4];
   float st = 1.0f;
@@ -183,6 +213,16 @@ __global__ __launch_bounds__(kThreads) void k_quant_tiled(
 #pragma unroll
     for (int j = 0; j < 4; ++j)  // values k0 + 8j .. k0 + 8j + 7 (blocks never straddle k)
       v[j] = (row < rows && k0 + 8 * j < k) ? src[j] : make_uint4(0u, 0u, 0u, 0u);
+    if (rotates(recipe)) {  // whole blocks only: a padding block stays zero
+      if constexpr (FMT == 0) {
+        uint4 b0[2] = {v[0], v[1]}, b1[2] = {v[2], v[3]};
+        hadamard_block<16>(b0);
+        hadamard_block<16>(b1);
+        v[0] = b0[0]; v[1] = b0[1]; v[2] = b1[0]; v[3] = b1[1];
+      } else {
+        hadamard_block<32>(v);
+      }
+    }
     uint4 q;
     uint32_t sc;
     if constexpr (FMT == 0) {
@@ -196,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_tiled(
     } else {
       q = make_uint4(0u, 0u, 0u, 0u);
       sc = 0;
-      if (row < rows && k0 < k) mx_encode_block(v, q, sc);
+      if (row < rows && k0 < k) mx_encode_block(v, q, sc, oas_rule(recipe));
       scales[f * K::SFB + lane] = (uint8_t)sc;
     }
     *(uint4 *)(codes + f * kFragCodeBytes + lane * 16) = q;
@@ -244,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_small(
     const uint16_t *__restrict__ x, int64_t rows, int64_t k, int64_t rows_pad, int64_t kt_n,
     const float *__restrict__ static_scale, uint8_t *__restrict__ codes, int64_t cpitch,
     uint8_t *__restrict__ scales, int64_t spitch, float *__restrict__ ts_out,
-    uint32_t *__restrict__ sync) {
+    uint32_t *__restrict__ sync, uint32_t recipe) {
   using K = Blk<FMT>;
   __shared__ uint32_t lds[4];
   const int64_t nb = k / K::B, nb_pad = kt_n * K::BPF, total = rows_pad * nb_pad;
@@ -268,6 +308,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_small(
 #pragma unroll
       for (int j = 0; j < K::V; ++j) v[i][j] = make_uint4(0u, 0u, 0u, 0u);
     }
+    maybe_rotate<FMT>(v[i], recipe);
     m = max(m, block_absmax<FMT>(v[i]));
   }
   float st = 1.0f;
@@ -284,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_small(
     uint8_t *cdst, *sdst;
     block_dst<FMT, TILED>(r, b, kt_n, codes, cpitch, scales, spitch, cdst, sdst);
     if (r >= rows || b >= nb) zero_store<FMT>(cdst, sdst);
-    else encode_store<FMT>(v[i], st, cdst, sdst);
+    else encode_store<FMT>(v[i], st, cdst, sdst, recipe);
   }
 }
 
@@ -346,7 +387,8 @@ int grid_for(int64_t work, int cap) {
 template <int FMT, int TILED>
 void launch_small(const uint16_t *x, int64_t rows, int64_t k, int64_t rows_pad, int64_t kt_n,
                   const float *static_scale, uint8_t *codes, int64_t cpitch, uint8_t *scales,
-                  int64_t spitch, float *ts_out, uint32_t *sync, hipStream_t stream) {
+                  int64_t spitch, float *ts_out, uint32_t *sync, uint32_t recipe,
+                  hipStream_t stream) {
   // One block per thread where the grid allows: encoding is the costly part
   // and spreads over as many CUs as there are blocks. The dynamic-scale form
   // also exchanges its maximum among the workgroups, so it stops at kActGrid
@@ -358,30 +400,30 @@ void launch_small(const uint16_t *x, int64_t rows, int64_t k, int64_t rows_pad, 
     const int grid = (int)(per_wg < kActGrid ? per_wg : kActGrid);
     hipLaunchKernelGGL((k_quant_small<FMT, TILED, 1, kActBpt>), dim3(grid), dim3(kThreads), 0,
                        stream, x, rows, k, rows_pad, kt_n, static_scale, codes, cpitch, scales,
-                       spitch, ts_out, sync);
+                       spitch, ts_out, sync, recipe);
   } else {
     hipLaunchKernelGGL((k_quant_small<FMT, TILED, 0, 1>), dim3((unsigned)per_wg), dim3(kThreads), 0,
                        stream, x, rows, k, rows_pad, kt_n, static_scale, codes, cpitch, scales,
-                       spitch, ts_out, sync);
+                       spitch, ts_out, sync, recipe);
   }
 }
 
 template <int FMT, int TILED>
 void launch_large(const uint16_t *x, int64_t rows, int64_t k, int64_t rows_pad, int64_t kt_n,
                   const uint32_t *parts, int nparts, const float *static_scale, uint8_t *codes,
-                  int64_t cpitch, uint8_t *scales, int64_t spitch, float *ts_out,
+                  int64_t cpitch, uint8_t *scales, int64_t spitch, float *ts_out, uint32_t recipe,
                   hipStream_t stream) {
   if (TILED) {  // one wave per fragment, four waves per workgroup, grid-stride
     const int64_t frags = (rows_pad >> 4) * kt_n;
     const int grid = (int)std::min<int64_t>((frags + 3) / 4, 8192);
     hipLaunchKernelGGL((k_quant_tiled<FMT>), dim3(grid), dim3(kThreads), 0, stream, x, rows, k,
-                       rows_pad, kt_n, parts, nparts, static_scale, codes, scales, ts_out);
+                       rows_pad, kt_n, parts, nparts, static_scale, codes, scales, ts_out, recipe);
     return;
   }
   const int grid = grid_for(rows_pad * kt_n * Blk<FMT>::BPF, 8192);
   hipLaunchKernelGGL((k_quant<FMT, TILED>), dim3(grid), dim3(kThreads), 0, stream, x, rows, k,
                      rows_pad, kt_n, parts, nparts, static_scale, codes, cpitch, scales, spitch,
-                     ts_out);
+                     ts_out, recipe);
 }
 
 }  // namespace
@@ -400,8 +442,8 @@ bool quant_fits_small(int fmt, int64_t rows, int64_t k, int tiled) {
   return blocks <= (int64_t)kActGrid * kThreads * kActBpt;
 }
 
-hipError_t launch_quantize(int fmt, int tiled, const uint16_t *x, int64_t rows, int64_t k,
-                           const float *static_scale, uint8_t *codes, int64_t cpitch,
+hipError_t launch_quantize(int fmt, uint32_t recipe, int tiled, const uint16_t *x, int64_t rows,
+                           int64_t k, const float *static_scale, uint8_t *codes, int64_t cpitch,
                            uint8_t *scales, int64_t spitch, float *ts_out, uint32_t *scratch,
                            hipStream_t stream) {
   const int64_t rows_pad = tiled ? round_up(rows, 16) : rows;
@@ -409,7 +451,7 @@ hipError_t launch_quantize(int fmt, int tiled, const uint16_t *x, int64_t rows, 
   if (quant_fits_small(fmt, rows, k, tiled)) {
     uint32_t *sync = scratch + kMaxAmaxParts;
 #define FP4_QS(F, T) launch_small<F, T>(x, rows, k, rows_pad, kt_n, static_scale, codes, cpitch, \
-                                        scales, spitch, ts_out, sync, stream)
+                                        scales, spitch, ts_out, sync, recipe, stream)
     if (fmt == 0 && !tiled) FP4_QS(0, 0);
     else if (fmt == 0) FP4_QS(0, 1);
     else if (!tiled) FP4_QS(1, 0);
@@ -420,13 +462,17 @@ hipError_t launch_quantize(int fmt, int tiled, const uint16_t *x, int64_t rows, 
   int nparts = 0;
   if (fmt == 0 && !static_scale) {
     nparts = amax_parts(rows * k);
-    hipLaunchKernelGGL(k_amax_parts, dim3(nparts), dim3(kThreads), 0, stream, (const uint4 *)x,
-                       rows * k / 8, scratch);
+    if (recipe & kRecipeRotate)
+      hipLaunchKernelGGL(k_amax_parts_rot, dim3(nparts), dim3(kThreads), 0, stream,
+                         (const uint4 *)x, rows * k / 16, scratch);
+    else
+      hipLaunchKernelGGL(k_amax_parts, dim3(nparts), dim3(kThreads), 0, stream, (const uint4 *)x,
+                         rows * k / 8, scratch);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
 #define FP4_QL(F, T) launch_large<F, T>(x, rows, k, rows_pad, kt_n, scratch, nparts, static_scale, \
-                                        codes, cpitch, scales, spitch, ts_out, stream)
+                                        codes, cpitch, scales, spitch, ts_out, recipe, stream)
   if (fmt == 0 && !tiled) FP4_QL(0, 0);
   else if (fmt == 0) FP4_QL(0, 1);
   else if (!tiled) FP4_QL(1, 0);

@@ -50,6 +50,35 @@ extern "C" {
 
 typedef enum { FP4_NVFP4 = 0, FP4_MXFP4 = 1 } fp4_format;
 
+/*
+ * Quantization recipe flags, OR-ed into a format value wherever an int32_t
+ * fmt is taken (fp4_format | flags). They change how values are quantized,
+ * not the stored format, its layout or its sizes. A tensor descriptor keeps
+ * the flags it was quantized with; fp4_linear quantizes the activations with
+ * the weight's flags.
+ *
+ * FP4_ROTATE: before quantization, each block of B values along K (B = the
+ *   format's block: 16 or 32) is rotated, y = H_B x / sqrt(B), H_B the
+ *   Sylvester Hadamard matrix: the online rotation the MXFP4 path applies to
+ *   activations ("FP4 on a consumer RTX 5090: the Blackwell headline loses to
+ *   plain int4", section "Finding 3 - the real-FP4 path"; the page gives no
+ *   rotation size, the block is the one used here). The transform runs in
+ *   binary32 (fast transform in Sylvester order, then one multiply by
+ *   RN_fp32(1/sqrt(B))) and is rounded to bf16 before the block is
+ *   quantized. Weights and activations must both be rotated, or neither:
+ *   then H_B H_B^T / B = I and the GEMM approximates the unrotated product.
+ *   fp4_gemm rejects operands that differ in this flag. The NVFP4 dynamic
+ *   tensor scale is taken over the rotated values. fp4_dequantize returns the
+ *   rotated-domain values. Inputs must satisfy |x| < 2^120 (no overflow in
+ *   the transform).
+ * FP4_MX_OAS (MXFP4 only): overflow-aware block exponent, the smallest e with
+ *   max|x| <= 6 * 2^e (clamped to [-127, 127]), so no element saturates
+ *   ("FP4 n'existe pas ...", section "L'ecart de qualite - et comment il se
+ *   reduit"); the default exponent floor(log2 max|x|) - 2 lets block maxima
+ *   in (6, 8) * 2^e saturate. Operands may differ in this flag.
+ */
+enum { FP4_ROTATE = 0x100, FP4_MX_OAS = 0x200 };
+
 typedef enum {
     FP4_OK = 0,
     FP4_ERR_INVALID_ARG = 1,     /* null pointer, bad enum, non-positive size */

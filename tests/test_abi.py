@@ -125,3 +125,35 @@ def test_linear_launch_count():
     assert L.fp4_linear_launches(fp4.NVFP4, 4096, 3072, 3072, 1) == 2
     assert L.fp4_linear_launches(fp4.MXFP4, 4096, 3072, 3072, 0) == 2
     assert L.fp4_linear_launches(fp4.NVFP4, 4, 64, 40, 0) == 0
+
+
+def test_recipe_flags_validation():
+    """Recipe flags ride in the format value: sizes ignore them, bad
+    combinations are rejected, and a rotated operand never meets an unrotated
+    one in a GEMM."""
+    L = fp4.lib()
+    for base in (fp4.NVFP4, fp4.MXFP4):
+        for flags in (fp4.ROTATE,):
+            assert L.fp4_codes_bytes(base | flags, fp4.TILED, 17, 256) == L.fp4_codes_bytes(base, fp4.TILED, 17, 256)
+            assert L.fp4_scales_bytes(base | flags, fp4.CANONICAL, 3, 2880) == L.fp4_scales_bytes(base, fp4.CANONICAL, 3, 2880)
+            assert L.fp4_block_size(base | flags) == L.fp4_block_size(base)
+    assert L.fp4_block_size(fp4.MXFP4 | fp4.MX_OAS | fp4.ROTATE) == 32
+    # OAS is an MXFP4 rule; unknown bits are rejected
+    assert L.fp4_block_size(fp4.NVFP4 | fp4.MX_OAS) == 0
+    assert L.fp4_block_size(fp4.MXFP4 | 0x400) == 0
+    t = fp4.fp4_tensor()
+    assert L.fp4_tensor_init(ctypes.byref(t), fp4.NVFP4 | fp4.MX_OAS, fp4.CANONICAL, 4, 64, 4096, 8192, 64) == 1
+    # a rotated activation with an unrotated weight (and the reverse)
+    a_rot, w_rot, a, w = fp4.fp4_tensor(), fp4.fp4_tensor(), fp4.fp4_tensor(), fp4.fp4_tensor()
+    assert L.fp4_tensor_init(ctypes.byref(a_rot), fp4.MXFP4 | fp4.ROTATE, fp4.CANONICAL, 4, 64, 4096, 8192, 0) == 0
+    assert L.fp4_tensor_init(ctypes.byref(w_rot), fp4.MXFP4 | fp4.ROTATE, fp4.TILED, 32, 64, 4096, 8192, 0) == 0
+    assert L.fp4_tensor_init(ctypes.byref(a), fp4.MXFP4, fp4.CANONICAL, 4, 64, 4096, 8192, 0) == 0
+    assert L.fp4_tensor_init(ctypes.byref(w), fp4.MXFP4 | fp4.MX_OAS, fp4.TILED, 32, 64, 4096, 8192, 0) == 0
+    assert L.fp4_gemm(ctypes.byref(a_rot), ctypes.byref(w), 4096, 32, None, 0, None) == 5
+    assert b"rotation" in L.fp4_last_error()
+    assert L.fp4_gemm(ctypes.byref(a), ctypes.byref(w_rot), 4096, 32, None, 0, None) == 5
+    # the binding's string form
+    assert fp4._fmt("mxfp4+rotate+oas") == fp4.MXFP4 | fp4.ROTATE | fp4.MX_OAS
+    assert fp4._fmt("nvfp4+rotate") == fp4.NVFP4 | fp4.ROTATE
+    with pytest.raises(ValueError):
+        fp4._fmt(fp4.MXFP4 | 0x800)
