@@ -102,6 +102,12 @@ def _load():
         lib.orc_gemm_sampled.restype = None
         lib.orc_gemm_sampled.argtypes = [ctypes.c_int, P, P, ctypes.c_float, P, P,
                                          ctypes.c_float, I64, P, P, I64, P, P]
+        lib.orc_gemm_w4a16.restype = None
+        lib.orc_gemm_w4a16.argtypes = [ctypes.c_int, P, P, P, ctypes.c_float, I64, I64, I64,
+                                       P, P]
+        lib.orc_gemm_w4a16_sampled.restype = None
+        lib.orc_gemm_w4a16_sampled.argtypes = [ctypes.c_int, P, P, P, ctypes.c_float, I64,
+                                               P, P, I64, P, P]
         _lib = lib
         return lib
 
@@ -300,6 +306,40 @@ def gemm_sampled(a: Quantized, w: Quantized, rows, cols):
     _load().orc_gemm_sampled(a.fmt, _ptr(a.codes), _ptr(a.scales), float(a.tensor_scale),
                              _ptr(w.codes), _ptr(w.scales), float(w.tensor_scale), a.k,
                              _ptr(rows), _ptr(cols), rows.size, _ptr(c), _ptr(l))
+    return c, l
+
+
+def gemm_w4a16(x, w: Quantized):
+    """Weight-only product: C = S_tW * x W'^T with bf16 activations x [M, K]
+    and the quantized weight (binary64, k-ordered); L = the magnitude sum."""
+    x = _bf16(x)
+    m, k = x.shape
+    if k != w.k:
+        raise ValueError("x and w differ in K")
+    n = w.rows
+    c = np.empty((m, n), dtype=np.float64)
+    l = np.empty((m, n), dtype=np.float64)
+    _load().orc_gemm_w4a16(w.fmt, _ptr(x), _ptr(w.codes), _ptr(w.scales), float(w.tensor_scale),
+                           m, n, k, _ptr(c), _ptr(l))
+    return c, l
+
+
+def gemm_w4a16_sampled(x, w: Quantized, rows, cols):
+    x = _bf16(x)
+    m, k = x.shape
+    if k != w.k:
+        raise ValueError("x and w differ in K")
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    if rows.shape != cols.shape:
+        raise ValueError("rows and cols differ in length")
+    if rows.size and (rows.min() < 0 or rows.max() >= m or cols.min() < 0 or cols.max() >= w.rows):
+        raise IndexError("sample index out of range")
+    c = np.empty(rows.size, dtype=np.float64)
+    l = np.empty(rows.size, dtype=np.float64)
+    _load().orc_gemm_w4a16_sampled(w.fmt, _ptr(x), _ptr(w.codes), _ptr(w.scales),
+                                   float(w.tensor_scale), k, _ptr(rows), _ptr(cols), rows.size,
+                                   _ptr(c), _ptr(l))
     return c, l
 
 

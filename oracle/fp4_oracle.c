@@ -480,6 +480,56 @@ void orc_gemm_sampled(int fmt, const uint8_t *a_codes, const uint8_t *a_scales, 
                    c ? c + i : NULL, l ? l + i : NULL);
 }
 
+/*
+ * Weight-only variant (W4A16): the activations stay bf16 and only the cached
+ * weight is quantized [SPEECH, section "Weights are safe" (the W4A16
+ * checkpoint) and section "Two Triton kernels for the SM120 gaps" (a W4A16
+ * GEMM of bf16 activations with pre-packed FP4 weights)].
+ * C[m][n] = S_tW * sum_k x[m][k] * (q * s_b)[n][k] (S_tW = 1 for MXFP4),
+ * binary64, increasing k; L the same sum of magnitudes. x is bf16 [M][K],
+ * the weight canonical (codes [N][K/2], scales [N][K/B]).
+ */
+static void gemm_w4a16_entry(int fmt, const uint16_t *x, const uint8_t *w_codes,
+                             const uint8_t *w_scales, int64_t k, int64_t m, int64_t n,
+                             double alpha, double *c_out, double *l_out)
+{
+    int64_t bs = (fmt == ORC_NVFP4) ? 16 : 32;
+    const uint16_t *xr = x + m * k;
+    const uint8_t *wc = w_codes + n * (k / 2), *ws = w_scales + n * (k / bs);
+    double acc = 0.0, mag = 0.0;
+    for (int64_t kk = 0; kk < k; ++kk) {
+        double p = orc_bf16_value(xr[kk]) * element_value(fmt, wc, ws, kk);
+        acc += p;
+        mag += fabs(p);
+    }
+    if (c_out)
+        *c_out = alpha * acc;
+    if (l_out)
+        *l_out = alpha * mag;
+}
+
+void orc_gemm_w4a16(int fmt, const uint16_t *x, const uint8_t *w_codes,
+                    const uint8_t *w_scales, float w_ts, int64_t M, int64_t N, int64_t K,
+                    double *c, double *l)
+{
+    double alpha = (fmt == ORC_NVFP4) ? (double)w_ts : 1.0;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n)
+            gemm_w4a16_entry(fmt, x, w_codes, w_scales, K, m, n, alpha,
+                             c ? c + m * N + n : NULL, l ? l + m * N + n : NULL);
+}
+
+void orc_gemm_w4a16_sampled(int fmt, const uint16_t *x, const uint8_t *w_codes,
+                            const uint8_t *w_scales, float w_ts, int64_t K,
+                            const int64_t *rows, const int64_t *cols, int64_t count,
+                            double *c, double *l)
+{
+    double alpha = (fmt == ORC_NVFP4) ? (double)w_ts : 1.0;
+    for (int64_t i = 0; i < count; ++i)
+        gemm_w4a16_entry(fmt, x, w_codes, w_scales, K, rows[i], cols[i], alpha,
+                         c ? c + i : NULL, l ? l + i : NULL);
+}
+
 /* Vector helper for the pins: RNE to E4M3 of n reals. */
 void orc_e4m3_from_real_array(const double *v, int64_t n, int saturate, uint8_t *out)
 {

@@ -632,3 +632,40 @@ def test_rotation_preserves_the_product_and_spreads_outliers(fmt):
     err_rot = np.sqrt(np.mean((c_rot - exact) ** 2))
     if fmt == oracle.MXFP4:
         assert err_rot < 0.8 * err_plain, (err_rot, err_plain)
+
+
+@pytest.mark.parametrize("fmt", [oracle.NVFP4, oracle.MXFP4])
+def test_w4a16_equals_textbook_matmul(fmt):
+    """Weight-only product: the k-ordered loop equals a library matmul of the
+    bf16 activations (torch's decode) and the dequantized weight (torch's
+    float8 decoders), with the weight's tensor scale as the only factor."""
+    rng = np.random.default_rng(23)
+    a = bf16_bits(rng.standard_normal((7, 96)).astype(np.float32))
+    w = bf16_bits((rng.standard_normal((5, 96)) * 0.02).astype(np.float32))
+    qw = oracle.quantize(fmt, w)
+    ad = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).double().numpy()
+    wd = _torch_dequant(qw)
+    alpha = float(qw.tensor_scale) if fmt == oracle.NVFP4 else 1.0
+    ref, refl = alpha * (ad @ wd.T), alpha * (np.abs(ad) @ np.abs(wd).T)
+    c, l = oracle.gemm_w4a16(a, qw)
+    assert np.allclose(c, ref, rtol=0, atol=1e-12 * refl.max())
+    assert np.allclose(l, refl, rtol=1e-14)
+    rows, cols = np.array([0, 6, 3]), np.array([4, 0, 2])
+    cs, ls = oracle.gemm_w4a16_sampled(a, qw, rows, cols)
+    assert np.array_equal(cs, c[rows, cols]) and np.array_equal(ls, l[rows, cols])
+
+
+def test_w4a16_closed_form():
+    """Activations 0.75 everywhere, weight codes 1.0 with unit block scales and
+    tensor scale 1.5: C = 0.75 * K * 1.5 exactly; with a negated activation row
+    the sign follows."""
+    k = 256
+    x = np.full((2, k), bf16_bits(np.float32([0.75]))[0], np.uint16)
+    x[1] = bf16_bits(np.float32([-0.75]))[0]
+    for fmt, sbyte, ts in ((oracle.NVFP4, 0x38, 1.5), (oracle.MXFP4, 127, 1.0)):
+        bs = oracle.BLOCK[fmt]
+        q = oracle.Quantized(fmt, np.full((3, k // 2), 0x22, np.uint8),
+                             np.full((3, k // bs), sbyte, np.uint8), ts, k)
+        c, l = oracle.gemm_w4a16(x, q)
+        assert np.all(c[0] == 0.75 * k * ts) and np.all(c[1] == -0.75 * k * ts)
+        assert np.all(l == 0.75 * k * ts)
