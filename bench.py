@@ -41,6 +41,11 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--fmt", default="nvfp4", choices=["nvfp4", "mxfp4"])
+    p.add_argument("--recipe", default="", choices=["", "rotate", "oas", "rotate+oas"],
+                   help="quantization recipe flags for weights and activations: block "
+                        "Hadamard rotation, MXFP4 overflow-aware exponent")
+    p.add_argument("--w4a16", action="store_true",
+                   help="time the weight-only linear (bf16 activations x FP4 weights) instead")
     p.add_argument("--workload", default="decode",
                    choices=["decode", "prefill", "square8192", "single", "forward"])
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
@@ -217,8 +222,10 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     fmt = fp4.FORMATS[args.fmt]
+    # qfmt: the format value with the recipe flags, given to every library call
+    qfmt = fp4._fmt(args.fmt + ("+" + args.recipe if args.recipe else ""))
     if args.workload == "forward":
-        bench_forward(args, fmt)
+        bench_forward(args, fmt, qfmt)
         return
     configs, desc = workload_configs(args.workload)
 
@@ -242,7 +249,7 @@ def main():
             w_bits = synth.single_gemm_inputs(0)[1]
         w_host[(k, n)] = w_bits
         w_dev = to_dev(w_bits)
-        weights[(k, n)] = [fp4.fp4_quantize_weight(w_dev, fmt) for _ in range(copies)]
+        weights[(k, n)] = [fp4.fp4_quantize_weight(w_dev, qfmt) for _ in range(copies)]
         del w_dev
     xs, outs, wss = {}, {}, {}
     for (m, k, n) in configs:
@@ -257,7 +264,7 @@ def main():
         a_host[(m, k, n)] = a_bits
         xs[(m, k, n)] = to_dev(a_bits)
         outs[(m, k, n)] = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
-        wss[(m, k, n)] = torch.zeros(max(1, fp4.fp4_linear_workspace_bytes(fmt, m, n, k)),
+        wss[(m, k, n)] = torch.zeros(max(1, fp4.fp4_linear_workspace_bytes(qfmt, m, n, k)),
                                      dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     if args.copy_mib:
@@ -269,10 +276,16 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    def linear(cfg, w):
+        if args.w4a16:
+            fp4.fp4_linear_w4a16(xs[cfg], w, out=outs[cfg])
+        else:
+            fp4.fp4_linear(xs[cfg], w, out=outs[cfg], workspace=wss[cfg])
+
     def step(i):
         for cfg in configs:
             m, k, n = cfg
-            fp4.fp4_linear(xs[cfg], weights[(k, n)][i % copies], out=outs[cfg], workspace=wss[cfg])
+            linear(cfg, weights[(k, n)][i % copies])
 
     if args.pmc_step:
         step(0)
@@ -348,15 +361,19 @@ def main():
         m, k, n = cfg
         wl = weights[(k, n)]
         w_bytes = n * (k // 2 + k // bs)
-        lin_us = graph_time(lambda r: fp4.fp4_linear(xs[cfg], wl[r % copies], out=outs[cfg],
-                                                     workspace=wss[cfg]), reps)
-        if fp4.fp4_linear_launches(fmt, m, n, k) == 1:
+        lin_us = graph_time(lambda r: linear(cfg, wl[r % copies]), reps)
+        if args.w4a16:
+            name = ("k_w4a16_decode<%s,MG=%d>" % (args.fmt, 1 if m <= 16 else 2) if m <= 32
+                    else "k_w4a16_tile<%s>" % args.fmt)
+            us = lin_us
+            nbytes = w_bytes + 2 * m * k + 2 * m * n          # W + bf16 A + bf16 C
+        elif fp4.fp4_linear_launches(qfmt, m, n, k) == 1:
             name = "k_linear_decode<%s>" % args.fmt
             us = lin_us
             nbytes = w_bytes + 2 * m * k + 2 * m * n          # W + bf16 A + bf16 C
         else:
             # the activation layout fp4_linear uses internally (fragment-tiled)
-            qa = fp4.fp4_quantize_act(xs[cfg], fmt, layout=fp4.TILED)
+            qa = fp4.fp4_quantize_act(xs[cfg], qfmt, layout=fp4.TILED)
             if m <= 32:
                 name = "k_gemm_decode<%s,MG=%d>" % (args.fmt, 1 if m <= 16 else 2)
             else:   # LDS-staged tiles; 256 x 256 when that fills the 256 CUs
@@ -382,7 +399,8 @@ def main():
         peak = FP4_PEAK_TFLOPS if fmt == 1 else F16_PEAK_TFLOPS
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": None}
-    roof["traffic"] = stored_traffic(args.workload, args.fmt)
+    # the counter summaries are taken for the W4A4 kernels without recipe flags
+    roof["traffic"] = None if (args.recipe or args.w4a16) else stored_traffic(args.workload, args.fmt)
     roof.update({"kernel": " + ".join(sorted(kern)), "avg_launch_us": round(tot_us / tot_launch, 3),
                  "launches_per_step": tot_launch,
                  "per_kernel": {nm: {"launches": d["launches"], "avg_us": round(d["us"] / d["launches"], 3),
@@ -401,9 +419,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16" if fmt == 0 else "fp4",
+        "dtype": "bf16" if args.w4a16 else ("f16" if fmt == 0 else "fp4"),
         "data": "synthetic",
-        "config": {"workload": desc, "format": args.fmt, "launch": "hip-graph replay" if use_graph else "eager",
+        "config": {"workload": desc + (" (weight-only: bf16 activations)" if args.w4a16 else ""),
+                   "format": args.fmt, "recipe": args.recipe or "none",
+                   "launch": "hip-graph replay" if use_graph else "eager",
                    "weight_copies": copies, "calls_per_step": len(configs),
                    "fraction_of_fp4_peak": round(tflops / FP4_PEAK_TFLOPS, 6)},
         "roofline": roof,
@@ -414,7 +434,7 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def bench_forward(args, fmt):
+def bench_forward(args, fmt, qfmt):
     """Synthetic 24-layer forward: per layer Q, K, V, O and four (up, down)
     pairs, 288 W4A4 linear calls per forward, at M = 1, 8, 32 and 128. The
     weights (3.82 G values, ~N(0, 0.02)) are drawn on the GPU from a seeded
@@ -438,7 +458,7 @@ def bench_forward(args, fmt):
     for _ in range(nl):
         for (_, k, n) in layer:
             w = (torch.randn(n, k, generator=gen, device=dev) * 0.02).to(torch.bfloat16)
-            weights.append(fp4.fp4_quantize_weight(w, fmt))
+            weights.append(fp4.fp4_quantize_weight(w, qfmt))
             del w
     calls = [(k, n) for _ in range(nl) for (_, k, n) in layer]
     note("drawing activations, capturing graphs")
@@ -446,7 +466,7 @@ def bench_forward(args, fmt):
     for m in ms:
         acts[m] = [torch.randn(m, k, generator=gen, device=dev).to(torch.bfloat16) for (k, n) in calls]
         outs[m] = {n: torch.empty(m, n, dtype=torch.bfloat16, device=dev) for (_, n) in calls}
-        wsz = max(fp4.fp4_linear_workspace_bytes(fmt, m, n, k) for (k, n) in calls)
+        wsz = max(fp4.fp4_linear_workspace_bytes(qfmt, m, n, k) for (k, n) in calls)
         wss[m] = torch.zeros(max(1, wsz), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
@@ -515,7 +535,8 @@ def bench_forward(args, fmt):
         "config": {"workload": "synthetic 24-layer forward, 288 W4A4 linear calls per forward "
                                "(Q 2880->4096, K/V 2880->512, O 4096->2880, 4 x (up 2880->5760, "
                                "down 5760->2880)), one forward at each M in {1,8,32,128}",
-                   "format": args.fmt, "launch": "hip-graph replay (one graph per M)",
+                   "format": args.fmt, "recipe": args.recipe or "none",
+                   "launch": "hip-graph replay (one graph per M)",
                    "weight_bytes": w_bytes,
                    "per_forward_ms": {str(m): round(per_m[m], 4) for m in ms},
                    "per_forward_tflops": {str(m): round(2.0 * m * sum_nk / (per_m[m] * 1e-3) / 1e12, 2)
@@ -541,36 +562,42 @@ def cpu_baseline(configs, fmt, args, a_host, w_host):
     on a subset of output columns (weights quantized beforehand, untimed, as on
     the GPU). Reported in the metric's unit: sampled flops / oracle seconds."""
     import oracle
+    rk = {"rotate": "rotate" in args.recipe, "oas": "oas" in args.recipe}
     budget = args.cpu_seconds / len(configs)
     tot_flops, tot_s, parts = 0.0, 0.0, []
     wq_cache = {}
     for (m, k, n) in configs:
         a_bits, w_bits = a_host[(m, k, n)], w_host[(k, n)]
         if (k, n) not in wq_cache:
-            wq_cache[(k, n)] = oracle.quantize(fmt, w_bits)
+            wq_cache[(k, n)] = oracle.quantize(fmt, w_bits, **rk)
         qw = wq_cache[(k, n)]
         # estimate the per-output cost, then size the column sample to the budget
+        def run(cols):   # activation quantization (W4A4) + the product on `cols` columns
+            sub = oracle.Quantized(fmt, qw.codes[:cols], qw.scales[:cols], qw.tensor_scale, k)
+            if args.w4a16:
+                oracle.gemm_w4a16(a_bits, sub)
+            else:
+                oracle.gemm_loop(oracle.quantize(fmt, a_bits, **rk), sub)
         t = time.perf_counter()
-        qa = oracle.quantize(fmt, a_bits)
+        if not args.w4a16:
+            oracle.quantize(fmt, a_bits, **rk)
         t_q = time.perf_counter() - t
         probe = min(n, 4)
         t = time.perf_counter()
-        sub = oracle.Quantized(fmt, qw.codes[:probe], qw.scales[:probe], qw.tensor_scale, k)
-        oracle.gemm_loop(qa, sub)
-        per_col = (time.perf_counter() - t) / probe
-        cols = int(max(1, min(n, (budget - t_q) / max(per_col, 1e-9))))
+        run(probe)
+        per_col = max((time.perf_counter() - t - t_q) / probe, 1e-9)
+        cols = int(max(1, min(n, (budget - t_q) / per_col)))
         t = time.perf_counter()
-        qa = oracle.quantize(fmt, a_bits)
-        sub = oracle.Quantized(fmt, qw.codes[:cols], qw.scales[:cols], qw.tensor_scale, k)
-        oracle.gemm_loop(qa, sub)
+        run(cols)
         dt = time.perf_counter() - t
         fl = 2.0 * m * cols * k
         tot_flops += fl
         tot_s += dt
         parts.append(f"M={m},K={k}: {cols}/{n} cols")
     return {"value": tot_flops / tot_s / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": "per call: full activation quantization + k-ordered FP64 GEMM on the first "
-                      "columns of the pre-quantized weight (" + "; ".join(parts) + f"); {tot_s:.1f} s"}
+            "sample": "per call: " + ("" if args.w4a16 else "full activation quantization + ") +
+                      "k-ordered FP64 GEMM on the first columns of the pre-quantized weight (" +
+                      "; ".join(parts) + f"); {tot_s:.1f} s"}
 
 
 if __name__ == "__main__":

@@ -8,6 +8,7 @@ stream. The functions carry the C names:
     fp4_quantize_act(a, fmt, static_scale=None) -> Fp4Tensor (canonical layout)
     fp4_gemm(a_q, w_q)                          -> bf16 [M, N] = A^ W^T
     fp4_linear(x, w_q, static_scale=None)       -> bf16 [M, N]
+    fp4_linear_w4a16(x, w_q)                    -> bf16 [M, N] (bf16 activations)
     fp4_export_canonical(w_q)                   -> Fp4Tensor (canonical copy)
     fp4_dequantize(t)                           -> fp32 [rows, K]
 
@@ -78,6 +79,7 @@ def lib():
             "fp4_gemm": (I32, [T, T, P, I64, P, SZ, P]),
             "fp4_linear_workspace_bytes": (SZ, [I32, I64, I64, I64]),
             "fp4_linear": (I32, [P, I64, T, P, P, P, SZ, P]),
+            "fp4_linear_w4a16": (I32, [P, I64, T, P, I64, P]),
             "fp4_linear_launches": (I32, [I32, I64, I64, I64, I32]),
             "fp4_export_canonical": (I32, [T, T, P]),
             "fp4_dequantize": (I32, [T, P, I64, P]),
@@ -229,6 +231,19 @@ def fp4_linear(x: torch.Tensor, w: Fp4Tensor, static_scale: torch.Tensor | None 
         workspace = torch.zeros(max(nws, 1), dtype=torch.uint8, device=x.device)
     _check(L.fp4_linear(_ptr(x), m, ctypes.byref(w.desc), _ptr(static_scale), _ptr(out),
                         _ptr(workspace), workspace.numel(), _stream(x.device)))
+    return out
+
+
+def fp4_linear_w4a16(x: torch.Tensor, w: Fp4Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Weight-only linear: bf16 activations times the FP4 weight cache."""
+    x = _bf16_2d(x, "x")
+    m = x.shape[0]
+    if x.shape[1] != w.k:
+        raise ValueError("x has K=%d, weight has K=%d" % (x.shape[1], w.k))
+    if out is None:
+        out = torch.empty(m, w.rows, dtype=torch.bfloat16, device=x.device)
+    _check(lib().fp4_linear_w4a16(_ptr(x), m, ctypes.byref(w.desc), _ptr(out), out.stride(0),
+                                  _stream(x.device)))
     return out
 
 

@@ -15,7 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfp4amd.so")
-SOURCES = ["api.hip", "quant.hip", "gemm.hip", "gemm_tile.hip"]
+SOURCES = ["api.hip", "quant.hip", "gemm.hip", "gemm_tile.hip", "gemm_w4a16.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

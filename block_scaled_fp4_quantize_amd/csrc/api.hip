@@ -114,6 +114,14 @@ fp4_status check_tensor(const fp4_tensor *t, const char *name) {
   return FP4_OK;
 }
 
+// The fused skinny linear repeats the activation quantization in every
+// weight tile's workgroup; with the rotation that repeated work pays off only
+// for one or two activation rows (measured on the decode shapes: at M = 8 the
+// separate quantizer plus the skinny GEMM is faster).
+bool use_fused(int32_t fmt, int64_t m, int64_t n, int64_t k) {
+  return linear_fused_ok(base_fmt(fmt), m, n, k) && (!(fmt & FP4_ROTATE) || m <= 2);
+}
+
 size_t quant_ws(int32_t fmt) { return base_fmt(fmt) == FP4_NVFP4 ? kQuantScratchBytes : 0; }
 
 // Everything fp4_linear keeps in its workspace: the quantizer's scratch (its
@@ -309,7 +317,7 @@ fp4_status fp4_linear(const void *x_bf16, int64_t m, const fp4_tensor *w,
   if (!aligned16(workspace)) return fail(FP4_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
   if ((st = check_device()) != FP4_OK) return st;
 
-  if (linear_fused_ok(base, m, n, k)) {
+  if (use_fused(fmt, m, n, k)) {
     hipError_t e = launch_linear_fused(base, recipe_of(fmt), (const uint16_t *)x_bf16, m, k,
                                        static_scale,
                                        (const uint8_t *)w->codes, (const uint8_t *)w->scales,
@@ -334,11 +342,35 @@ fp4_status fp4_linear(const void *x_bf16, int64_t m, const fp4_tensor *w,
   return st == FP4_OK ? ok() : st;
 }
 
+fp4_status fp4_linear_w4a16(const void *x_bf16, int64_t m, const fp4_tensor *w, void *y_bf16,
+                            int64_t ldy, hipStream_t stream) {
+  fp4_status st;
+  if ((st = check_tensor(w, "w")) != FP4_OK) return st;
+  if (w->layout != FP4_LAYOUT_TILED)
+    return fail(FP4_ERR_FORMAT_MISMATCH, "w must be in the TILED layout");
+  if (w->fmt & FP4_ROTATE)
+    return fail(FP4_ERR_FORMAT_MISMATCH,
+                "a rotated weight needs rotated activations: use fp4_linear");
+  const int64_t k = w->cols, n = w->rows;
+  if ((st = check_shape(w->fmt, m, k)) != FP4_OK) return st;
+  if (!x_bf16 || !y_bf16) return fail(FP4_ERR_INVALID_ARG, "null input or output");
+  if (!aligned16(x_bf16)) return fail(FP4_ERR_ALIGNMENT, "input must be 16-byte aligned");
+  if (((uintptr_t)y_bf16 & 1u) != 0) return fail(FP4_ERR_ALIGNMENT, "output must be 2-byte aligned");
+  if (ldy < n) return fail(FP4_ERR_SHAPE, "ldy smaller than N");
+  if (m > INT32_MAX || n > INT32_MAX) return fail(FP4_ERR_SHAPE, "too many rows");
+  if ((st = check_device()) != FP4_OK) return st;
+  hipError_t e = launch_linear_w4a16(base_fmt(w->fmt), (const uint16_t *)x_bf16, k, m, k,
+                                     (const uint8_t *)w->codes, (const uint8_t *)w->scales,
+                                     w->tensor_scale, n, (uint16_t *)y_bf16, ldy, stream);
+  if (e != hipSuccess) return hip_fail(e, "w4a16 launch");
+  return ok();
+}
+
 int32_t fp4_linear_launches(int32_t fmt, int64_t m, int64_t n, int64_t k, int32_t static_scale) {
   if (!valid_fmt(fmt) || m <= 0 || n <= 0 || k <= 0) return 0;
   const int base = base_fmt(fmt);
   if (k % block_of(base) != 0) return 0;
-  if (linear_fused_ok(base, m, n, k)) return 1;
+  if (use_fused(fmt, m, n, k)) return 1;
   if (base == FP4_NVFP4 && !static_scale && !quant_fits_small(base, m, k, 1)) return 3;
   return 2;
 }

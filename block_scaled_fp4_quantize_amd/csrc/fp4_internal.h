@@ -88,4 +88,10 @@ hipError_t launch_linear_fused(int fmt, uint32_t recipe, const uint16_t *x, int6
                                const uint8_t *w_scales, const float *w_ts, int64_t n,
                                uint16_t *y, int64_t ldy, hipStream_t stream);
 
+// Weight-only linear (W4A16): y[m, n] = S_tW * x[m, :] . (q s_b)[n, :], x bf16
+// with row pitch ldx elements (a multiple of 8), the weight in the tiled cache.
+hipError_t launch_linear_w4a16(int fmt, const uint16_t *x, int64_t ldx, int64_t m, int64_t k,
+                               const uint8_t *w_codes, const uint8_t *w_scales, const float *w_ts,
+                               int64_t n, uint16_t *y, int64_t ldy, hipStream_t stream);
+
 }  // namespace fp4i

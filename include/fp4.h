@@ -189,6 +189,21 @@ fp4_status fp4_linear(const void *x_bf16, int64_t m, const fp4_tensor *w,
                       const float *static_scale, void *y_bf16, void *workspace,
                       size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Weight-only linear (W4A16): y[m, N] (bf16, row stride ldy elements) =
+ * bf16_RNE(S_tW * sum_k x[m, k] * (q * s_b)[n, k]) with the activations x
+ * [m, K] kept in bf16 (contiguous, 16-byte aligned) and only the cached weight
+ * `w` (TILED) in FP4; FP32 accumulation ("Hardware FP4 inference for speech
+ * on Blackwell", section "Weights are safe" for the W4A16 regime, and section
+ * "Two Triton kernels for the SM120 gaps" for a W4A16 GEMM on pre-packed FP4
+ * weights). S_tW = 1 for MXFP4. One launch, no workspace. A rotated weight
+ * (FP4_ROTATE) is rejected (FP4_ERR_FORMAT_MISMATCH): its activations would
+ * need the same rotation, which fp4_linear applies. MXFP4 weights must stay
+ * below 2^127 in magnitude (their dequantized values are formed in bf16).
+ */
+fp4_status fp4_linear_w4a16(const void *x_bf16, int64_t m, const fp4_tensor *w, void *y_bf16,
+                            int64_t ldy, hipStream_t stream);
+
 /* Number of kernel launches fp4_linear makes for this shape: 1 when the
  * activation quantization is fused into the skinny GEMM (small M * K), 2 for
  * quantize + GEMM, 3 when the quantizer needs a separate reduction launch

@@ -157,3 +157,20 @@ def test_recipe_flags_validation():
     assert fp4._fmt("nvfp4+rotate") == fp4.NVFP4 | fp4.ROTATE
     with pytest.raises(ValueError):
         fp4._fmt(fp4.MXFP4 | 0x800)
+
+
+def test_w4a16_host_validation():
+    L = fp4.lib()
+    w = fp4.fp4_tensor()
+    assert L.fp4_tensor_init(ctypes.byref(w), fp4.NVFP4, fp4.TILED, 32, 64, 4096, 8192, 64) == 0
+    wr = fp4.fp4_tensor()
+    assert L.fp4_tensor_init(ctypes.byref(wr), fp4.MXFP4 | fp4.ROTATE, fp4.TILED, 32, 64, 4096, 8192, 0) == 0
+    assert L.fp4_linear_w4a16(4096, 4, ctypes.byref(wr), 8192, 32, None) == 5     # rotated weight
+    assert b"rotated" in L.fp4_last_error()
+    assert L.fp4_linear_w4a16(None, 4, ctypes.byref(w), 8192, 32, None) == 1      # null input
+    assert L.fp4_linear_w4a16(4097, 4, ctypes.byref(w), 8192, 32, None) == 3      # misaligned
+    assert L.fp4_linear_w4a16(4096, 4, ctypes.byref(w), 8192, 16, None) == 2      # ldy < N
+    assert L.fp4_linear_w4a16(4096, 0, ctypes.byref(w), 8192, 32, None) == 1      # m = 0
+    c = fp4.fp4_tensor()
+    assert L.fp4_tensor_init(ctypes.byref(c), fp4.NVFP4, fp4.CANONICAL, 32, 64, 4096, 8192, 64) == 0
+    assert L.fp4_linear_w4a16(4096, 4, ctypes.byref(c), 8192, 32, None) == 5      # not tiled
