@@ -12,7 +12,12 @@
 // set of whole 1 KB fragments. They are copied global -> LDS with the direct
 // LDS load (global_load_lds_dwordx4: lane i of the wave writes bytes
 // 16i..16i+15 of a 1 KB LDS run), which needs no registers and no LDS store
-// instructions. A four-stage ring: while stage s is consumed, the copies of
+// instructions. The scale bytes are copied a dword at a time (one dword holds
+// the scales of 4 lanes (MXFP4) or 2 lanes (NVFP4) of one fragment) and
+// regrouped on the way: each lane's copy reads whichever global dword the LDS
+// order wants, and the stage stores them as [operand][lane group][fragment],
+// so that a lane finds its scales for all of its fragments in consecutive
+// dwords (a few 16-byte LDS reads instead of one byte read per fragment). A four-stage ring: while stage s is consumed, the copies of
 // stages s+1 and s+2 are in flight and those of s+3 are issued; the copies
 // and the LDS reads of the next stage are spread between the matrix
 // instructions so the matrix unit is not left idle while they issue.
@@ -177,13 +182,36 @@ __global__ __launch_bounds__(256) void k_gemm_tile(
     const int f = wave + 4 * u;
     code_base[u] = (f < C::FA ? a_codes : w_codes) + (int64_t)row_of(f) * kt_n * kFragCodeBytes;
   }
+  // Stage scale region. Grouped (GS, the MXFP4 256 x 256 tile): dword d <
+  // A_DW is A's chunk d / FA (lane group) of fragment d % FA; the W section
+  // follows with FW fragments per chunk. A_DW is a multiple of 64, so a copy
+  // run (64 dwords) never mixes A and W. Otherwise the global order is kept
+  // (fragment-major, one byte (MXFP4) or byte pair (NVFP4) per lane): the
+  // 128 x 128 tiles and NVFP4 measured no faster with the grouped order.
+  constexpr bool GS = FMT == 1 && TM == 8 && TN == 8;
+  constexpr int DPF = C::SCB / 4;            // scale dwords per fragment
+  constexpr int A_DW = DPF * C::FA;
+  static_assert(!GS || A_DW % 64 == 0, "a scale copy run stays within one operand");
+  auto frag_chunk = [&](int d, int &f, int &pc) __attribute__((always_inline)) {
+    if (!GS) {
+      f = d / DPF;
+      pc = d % DPF;
+    } else if (d < A_DW) {
+      pc = d / C::FA;
+      f = d % C::FA;
+    } else {
+      pc = (d - A_DW) / C::FW;
+      f = C::FA + (d - A_DW) % C::FW;
+    }
+  };
   const uint8_t *sc_base[NSP];
   uint32_t sc_off[NSP];
 #pragma unroll
   for (int v = 0; v < NSP; ++v) {
     const int j = wave + 4 * v;
-    const int p0 = min(64 * j, C::SC_DW - 1), f0 = p0 / (C::SCB / 4);
-    const int p = min(64 * j + lane, C::SC_DW - 1), f = p / (C::SCB / 4), pc = p % (C::SCB / 4);
+    int f0, pc0, f, pc;
+    frag_chunk(min(64 * j, C::SC_DW - 1), f0, pc0);
+    frag_chunk(min(64 * j + lane, C::SC_DW - 1), f, pc);
     const int r0 = row_of(f0);
     sc_base[v] = (f0 < C::FA ? a_sc : w_sc) + (int64_t)r0 * kt_n * C::SCB;
     sc_off[v] = (uint32_t)((row_of(f) - r0) * kt_n * C::SCB + pc * 4);
@@ -220,24 +248,61 @@ __global__ __launch_bounds__(256) void k_gemm_tile(
     uint32_t as[TM], ws[TN];
   };
   // read unit r of a stage into registers: A fragment r (r < TM) or W
-  // fragment r - TM, with its scale bytes
+  // fragment r - TM, each with its scale, or in the grouped order codes only
+  // and (r = TM + TN) the lane's scales of all of them: TM and TN consecutive dwords, each holding the lane's scale
+  // byte (MXFP4) or byte pair (NVFP4) at bit 32 * (lane % LPD) / LPD. The
+  // shifted dword is kept whole: the scaled matrix instruction reads byte 0
+  // of its scale operand and the NVFP4 dequantization masks each byte.
+  static_assert(TM % 4 == 0 && TN % 4 == 0, "scale reads take 4 fragments per 16 bytes");
+  constexpr int LPD = 256 / C::SCB;          // lanes per scale dword
+  const int s_chunk = lane / LPD, s_shift = (lane % LPD) * (32 / LPD);
   auto read_unit = [&](const uint8_t *st, Ops &o, int r) __attribute__((always_inline)) {
-    const int f = r < TM ? fa0 + r : fw0 + r - TM;
-    const uint4 q = *(const uint4 *)(st + f * kFragCodeBytes + lane * 16);
-    const uint32_t sv = FMT == 0 ? (uint32_t) * (const uint16_t *)(st + C::CODE_BYTES + f * 128 + lane * 2)
-                                 : (uint32_t)st[C::CODE_BYTES + f * 64 + lane];
-    if (r < TM) {
-      o.aq[r] = q;
-      o.as[r] = sv;
-    } else {
-      o.wq[r - TM] = q;
-      o.ws[r - TM] = sv;
+    if (!GS) {  // code bytes and scale of one fragment
+      const int f = r < TM ? fa0 + r : fw0 + r - TM;
+      const uint4 q = *(const uint4 *)(st + f * kFragCodeBytes + lane * 16);
+      const uint32_t sv = FMT == 0 ? (uint32_t) * (const uint16_t *)(st + C::CODE_BYTES + f * 128 + lane * 2)
+                                   : (uint32_t)st[C::CODE_BYTES + f * 64 + lane];
+      if (r < TM) {
+        o.aq[r] = q;
+        o.as[r] = sv;
+      } else {
+        o.wq[r - TM] = q;
+        o.ws[r - TM] = sv;
+      }
+      return;
+    }
+    if (r < TM + TN) {
+      const int f = r < TM ? fa0 + r : fw0 + r - TM;
+      const uint4 q = *(const uint4 *)(st + f * kFragCodeBytes + lane * 16);
+      if (r < TM) o.aq[r] = q;
+      else o.wq[r - TM] = q;
+      return;
+    }
+    const uint32_t *sr = (const uint32_t *)(st + C::CODE_BYTES);
+    const uint4 *sa = (const uint4 *)(sr + s_chunk * C::FA + fa0);
+    const uint4 *sw = (const uint4 *)(sr + A_DW + s_chunk * C::FW + (fw0 - C::FA));
+#pragma unroll
+    for (int i = 0; i < TM / 4; ++i) {
+      const uint4 d = sa[i];
+      o.as[4 * i] = d.x >> s_shift;
+      o.as[4 * i + 1] = d.y >> s_shift;
+      o.as[4 * i + 2] = d.z >> s_shift;
+      o.as[4 * i + 3] = d.w >> s_shift;
+    }
+#pragma unroll
+    for (int j = 0; j < TN / 4; ++j) {
+      const uint4 d = sw[j];
+      o.ws[4 * j] = d.x >> s_shift;
+      o.ws[4 * j + 1] = d.y >> s_shift;
+      o.ws[4 * j + 2] = d.z >> s_shift;
+      o.ws[4 * j + 3] = d.w >> s_shift;
     }
   };
+  constexpr int NR = TM + TN + (GS ? 1 : 0);  // read units per stage
   auto read = [&](auto sc, Ops &o) __attribute__((always_inline)) {
     const uint8_t *st = stage_ptr(sc);
 #pragma unroll
-    for (int r = 0; r < TM + TN; ++r) read_unit(st, o, r);
+    for (int r = 0; r < NR; ++r) read_unit(st, o, r);
   };
 
   auto mma = [&](const Ops &o) __attribute__((always_inline)) {
@@ -317,7 +382,7 @@ __global__ __launch_bounds__(256) void k_gemm_tile(
       // last stage the reads fetch values that are never used.)
       constexpr int NQ = TM * TN;
       constexpr int DMA_EVERY = NQ / NU > 0 ? NQ / NU : 1;
-      constexpr int RD_EVERY = NQ / (TM + TN) > 0 ? NQ / (TM + TN) : 1;
+
       const int kcopy = src_kt(kt + 3);
       uint8_t *st_copy = stage_ptr(Stage<S + 3>{});
       const uint8_t *st_read = stage_ptr(Stage<S + 1>{});
@@ -326,7 +391,8 @@ __global__ __launch_bounds__(256) void k_gemm_tile(
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         if (q % DMA_EVERY == 0 && q / DMA_EVERY < NU) issue_unit(st_copy, kcopy, q / DMA_EVERY);
-        if (q % RD_EVERY == RD_EVERY - 1 && q / RD_EVERY < TM + TN) read_unit(st_read, nxt, q / RD_EVERY);
+        // read units spread evenly: unit u at the first q with (q+1) NR / NQ > u
+        if ((q + 1) * NR / NQ > q * NR / NQ) read_unit(st_read, nxt, q * NR / NQ);
         const int i = q / TN, j = q % TN;
         acc[i][j] = mma_mx(cur.wq[j], cur.aq[i], acc[i][j], cur.ws[j], cur.as[i]);
         __builtin_amdgcn_sched_barrier(0);
@@ -352,6 +418,46 @@ __global__ __launch_bounds__(256) void k_gemm_tile(
   // ---- epilogue: lane holds C[row][col0 .. col0+3] of each 16 x 16 tile
   const Alpha alpha = FMT == 0 ? make_alpha(a_ts[0], w_ts[0]) : Alpha{1.0f, 0};
   const int rl = lane & 15, cl = 4 * (lane >> 4);
+  if (vec_store == 2) {
+    // Staged through LDS: each wave writes its 16TM x 16TN quadrant as bf16
+    // rows into one ring buffer (the ring is free once every wave has left the
+    // K loop), then stores whole rows, 16 bytes per lane, so that every store
+    // instruction covers whole 128-byte lines (the accumulator layout alone
+    // gives 32-byte pieces of 16 different rows per instruction).
+    lds_barrier();
+    constexpr int QR = 16 * TM, QC = 16 * TN;
+    constexpr int QP = 2 * QC + 16;  // padded LDS row pitch in bytes
+    static_assert(QR * QP <= C::STAGE, "a wave's output quadrant fits one ring buffer");
+    uint8_t *q = wave == 0 ? lds0 : wave == 1 ? lds1 : wave == 2 ? lds2 : lds3;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const v4f &a = acc[i][j];
+        const uint32_t lo = pack_bf16x2(apply_alpha(a[0], alpha), apply_alpha(a[1], alpha));
+        const uint32_t hi = pack_bf16x2(apply_alpha(a[2], alpha), apply_alpha(a[3], alpha));
+        *(uint2 *)(q + (16 * i + rl) * QP + 2 * (16 * j + cl)) = make_uint2(lo, hi);
+      }
+    constexpr int LPR = QC / 8, RPI = 64 / LPR;  // lanes per row, rows per instruction
+    const int lr = lane / LPR, lc = 8 * (lane % LPR);
+    const int row0 = (g0 + fa0) * 16, col = (n0 + wn * TN) * 16 + lc;
+#pragma unroll 4
+    for (int it = 0; it < QR / RPI; ++it) {
+      const int r = it * RPI + lr, row = row0 + r;
+      const uint4 v = *(const uint4 *)(q + r * QP + 2 * lc);
+      if (row >= m) continue;
+      uint16_t *dst = c + (int64_t)row * ldc + col;
+      if (col + 7 < n) {
+        *(uint4 *)dst = v;
+      } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (col + e < n) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int row = (g0 + fa0 + i) * 16 + rl;
@@ -393,7 +499,10 @@ hipError_t launch_gemm_tile(const GemmArgs &g, int cfg, hipStream_t stream) {
   if (cfg == 0) cfg = gemm_tile_config(g.fmt, g.m, g.n);
   const int bm = cfg == 88 ? 256 : 128, bn = bm;
   const int tiles_m = (int)((g.m + bm - 1) / bm), tiles_n = (int)((g.n + bn - 1) / bn);
-  const int vec = (g.ldc % 4 == 0) && ((uintptr_t)g.c % 8 == 0);
+  // 2: 16-byte row stores through LDS; 1: 8-byte stores; 0: element stores
+  const int vec = (g.ldc % 8 == 0 && (uintptr_t)g.c % 16 == 0)  ? 2
+                  : (g.ldc % 4 == 0 && (uintptr_t)g.c % 8 == 0) ? 1
+                                                                : 0;
   dim3 grid((unsigned)(tiles_m * tiles_n));
 #define FP4_TILE(F, A, B)                                                                       \
   hipLaunchKernelGGL((k_gemm_tile<F, A, B>), grid, dim3(256), 0, stream, g.a_codes, g.a_scales, \
