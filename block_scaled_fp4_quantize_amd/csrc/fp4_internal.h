@@ -11,7 +11,8 @@ constexpr int kFragK = 128;          // K values per fragment (one scaled-MFMA K
 constexpr int kFragRows = 16;        // rows per fragment
 constexpr int kFragCodeBytes = 1024; // 16 rows x 128 values x 4 bits
 constexpr int kMaxAmaxParts = 1024;  // partial maxima of the per-tensor reduction
-constexpr int kDecodeMaxM = 32;      // M up to which the skinny (decode) GEMM is used
+constexpr int kDecodeMaxM = 128;     // M up to which the skinny (decode) GEMM is used
+constexpr int kW16DecodeMaxM = 32;   // the same for the weight-only (W4A16) linear
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 inline int64_t k_pad(int64_t k) { return round_up(k, kFragK); }

@@ -149,15 +149,18 @@ __global__ __launch_bounds__(256) void k_gemm_prefill(
 
 // ------------------------------------------------------------------- decode
 //
-// Skinny GEMM for M <= 32: the weight is streamed once at HBM rate. One
+// Skinny GEMM for M <= 128: the weight is streamed once at HBM rate. One
 // workgroup per 16-row weight tile covers the whole K range, so there is no
 // cross-workgroup reduction: every workgroup is resident at once and HBM
 // bandwidth is shared among them. The kDecWaves waves take interleaved
-// fragments (kt = wave + kDecWaves * j) and keep two groups of kDecFrags
-// fragments in flight (the next group's loads are issued before the current
-// group's arithmetic). The weight tile is the MFMA's A operand (rows n) and the
-// activations its B operand (columns m, MG groups of 16), so the accumulator
-// holds C^T. The waves' partial sums are added in LDS in a fixed order.
+// fragments (kt = wave + kDecWaves * j) and keep two groups of FM fragments
+// in flight (the next group's loads are issued before the current group's
+// arithmetic). The weight tile is the MFMA's A operand (rows n) and the
+// activations its B operand (columns m, MG groups of 16: 1, 2, 4 or 8), so
+// the accumulator holds C^T. The waves' partial sums are added in LDS in a
+// fixed order. Up to M = 128 this beats the tiled kernels, whose few output
+// tiles (M / 128 rows of them) leave most CUs idle; every workgroup reads the
+// (small, L2-resident) activations once.
 constexpr int kDecWaves = 8;
 constexpr int kDecFrags = 2;
 
@@ -167,7 +170,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(
     int64_t a_sp, const float *__restrict__ a_ts, const uint8_t *__restrict__ w_codes,
     const uint8_t *__restrict__ w_sc, const float *__restrict__ w_ts, int m, int n, int kt_n,
     uint16_t *__restrict__ c, int64_t ldc) {
-  constexpr int NW = kDecWaves, FM = kDecFrags;
+  // fragments per group: two, or one for eight activation groups (registers)
+  constexpr int NW = kDecWaves, FM = MG >= 8 ? 1 : kDecFrags;
   __shared__ float red[NW][MG][4][64];
   const int nt = blockIdx.x;
   // readfirstlane makes the wave index (and every fragment guard derived from
@@ -405,17 +409,24 @@ hipError_t launch_gemm_prefill(const GemmArgs &g, hipStream_t stream) {
 hipError_t launch_gemm_decode(const GemmArgs &g, hipStream_t stream) {
   const int kt_n = (int)(k_pad(g.k) / kFragK);
   const int nt_n = (int)(round_up(g.n, 16) / 16);
-  const int mg = g.m <= 16 ? 1 : 2;
+  const int mg = g.m <= 16 ? 1 : g.m <= 32 ? 2 : g.m <= 64 ? 4 : 8;
   dim3 grid((unsigned)nt_n);
 #define FP4_DEC(F, G, T)                                                                        \
   hipLaunchKernelGGL((k_gemm_decode<F, G, T>), grid, dim3(64 * kDecWaves), 0, stream,          \
                      g.a_codes, g.a_cpitch, g.a_scales, g.a_spitch, g.a_ts, g.w_codes,         \
                      g.w_scales, g.w_ts, (int)g.m, (int)g.n, kt_n, g.c, g.ldc)
 #define FP4_DEC_T(F, G) do { if (g.a_tiled) FP4_DEC(F, G, 1); else FP4_DEC(F, G, 0); } while (0)
-  if (g.fmt == 0 && mg == 1) FP4_DEC_T(0, 1);
-  else if (g.fmt == 0) FP4_DEC_T(0, 2);
-  else if (mg == 1) FP4_DEC_T(1, 1);
-  else FP4_DEC_T(1, 2);
+  if (g.fmt == 0) {
+    if (mg == 1) FP4_DEC_T(0, 1);
+    else if (mg == 2) FP4_DEC_T(0, 2);
+    else if (mg == 4) FP4_DEC_T(0, 4);
+    else FP4_DEC_T(0, 8);
+  } else {
+    if (mg == 1) FP4_DEC_T(1, 1);
+    else if (mg == 2) FP4_DEC_T(1, 2);
+    else if (mg == 4) FP4_DEC_T(1, 4);
+    else FP4_DEC_T(1, 8);
+  }
 #undef FP4_DEC_T
 #undef FP4_DEC
   return hipGetLastError();

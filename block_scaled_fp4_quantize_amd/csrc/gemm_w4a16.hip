@@ -269,7 +269,7 @@ hipError_t launch_linear_w4a16(int fmt, const uint16_t *x, int64_t ldx, int64_t 
                                int64_t n, uint16_t *y, int64_t ldy, hipStream_t stream) {
   const int kt_n = (int)(k_pad(k) / kFragK);
   const int nt_n = (int)(round_up(n, 16) / 16);
-  if (m <= kDecodeMaxM) {
+  if (m <= kW16DecodeMaxM) {
     const int mg = m <= 16 ? 1 : 2;
 #define FP4_W16D(F, G)                                                                          \
   hipLaunchKernelGGL((k_w4a16_decode<F, G>), dim3((unsigned)nt_n), dim3(64 * kW16Waves), 0,    \

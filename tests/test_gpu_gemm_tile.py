@@ -1,6 +1,6 @@
 """GPU parity of the LDS-staged GEMM for large M (both operands fragment-tiled).
 
-fp4_gemm takes this kernel when M > 32 and the activations are in the tiled
+fp4_gemm takes this kernel when M > 128 and the activations are in the tiled
 layout (the layout fp4_linear quantizes into). The cases cover each workgroup
 tile (256x256 and 128x128, chosen by the output's shape), ragged M and
 N, and K loops of 1, 2, 3, 4, 5 and 33 steps of 128 (the ring's prologue and
@@ -50,7 +50,7 @@ def _tiled_case(fmt, a_bits, w_bits, what):
     (4096, 3072, 640),      # 128 x 128 tiles, 5 K steps
     (4111, 2056, 128),      # 128 x 128 tiles, ragged, 1 K step
     (520, 1000, 4160),      # 128 x 128 tiles, 33 K steps (K tail 64)
-    (33, 17, 512),          # one partial 128 x 128 tile, 4 K steps
+    (129, 17, 512),         # two partial 128 x 128 tiles, 4 K steps
 ])
 def test_tile_configs(fmt, m, n, k):
     a = synth.normal((m, k), 1.0, 21, m * 31 + k)
