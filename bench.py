@@ -293,9 +293,13 @@ def main():
         print(json.dumps({"pmc_step": desc, "configs": configs}), flush=True)
         return
 
-    # ---- graphs: one per weight copy (each replays one full step)
+    # ---- graphs: a long graph replays G consecutive steps (the weight copies
+    # in turn), so a graph launch is paid once per G steps, as in a serving
+    # loop that captures many layers in one graph; one-step graphs (one per
+    # copy) run any remainder, so that exactly the requested steps run.
     use_graph = not args.no_graph
-    graphs = []
+    G = copies * max(1, -(-16 // copies))
+    one, long_graph = [], None
     if use_graph:
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -308,24 +312,31 @@ def main():
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 step(i)
-            graphs.append(g)
+            one.append(g)
+        long_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(long_graph):
+            for i in range(G):
+                step(i)
         torch.cuda.synchronize()
 
-    def run(i):
-        if use_graph:
-            graphs[i % copies].replay()
-        else:
-            step(i)
+    def run_steps(count):
+        if not use_graph:
+            for i in range(count):
+                step(i)
+            return
+        q, r = divmod(count, G)
+        for _ in range(q):
+            long_graph.replay()
+        for i in range(r):
+            one[i % copies].replay()
 
-    for i in range(args.warmup):
-        run(i)
+    run_steps(args.warmup)
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t0.record()
-    for i in range(args.steps):
-        run(i)
+    run_steps(args.steps)
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -424,7 +435,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": desc + (" (weight-only: bf16 activations)" if args.w4a16 else ""),
                    "format": args.fmt, "recipe": args.recipe or "none",
-                   "launch": "hip-graph replay" if use_graph else "eager",
+                   "launch": ("hip-graph replay, %d steps per graph" % G) if use_graph else "eager",
                    "weight_copies": copies, "calls_per_step": len(configs),
                    "fraction_of_fp4_peak": round(tflops / FP4_PEAK_TFLOPS, 6)},
         "roofline": roof,
