@@ -58,6 +58,9 @@ def parse():
     p.add_argument("--pmc-step", action="store_true",
                    help="run the copy (--copy-mib) and one eager step only, for hardware "
                         "counter passes (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)")
+    p.add_argument("--summarize-util", metavar="CSV",
+                   help="no GPU: turn a rocprofv3 --pmc MfmaUtil VALUBusy LdsUtil LDSBankConflict "
+                        "pass of --pmc-step into the utilization summary under profiles/")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="no GPU: turn the two counter passes of --pmc-step into the traffic "
                         "summary under profiles/")
@@ -117,6 +120,46 @@ def stored_traffic(workload, fmt):
     except OSError:
         pass
     return None
+
+
+UTIL_COUNTERS = ("MfmaUtil", "VALUBusy", "LdsUtil", "LDSBankConflict")
+
+
+def summarize_util(args):
+    """Per-dispatch utilization of the dominant kernels (rocprofv3's derived
+    counters, percent of the kernel's active cycles) from one counter pass over
+    an eager step, written under profiles/."""
+    import csv
+    import re
+    vals = {}
+    with open(args.summarize_util) as fh:
+        for r in csv.DictReader(fh):
+            if r.get("Counter_Name") in UTIL_COUNTERS and any(d in r["Kernel_Name"] for d in DOMINANT):
+                vals.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]})[r["Counter_Name"]] = \
+                    float(r["Counter_Value"])
+    configs, desc = workload_configs(args.workload)
+    disp = [vals[d] for d in sorted(vals)]
+    if len(disp) != len(configs):
+        raise SystemExit(f"expected {len(configs)} dominant-kernel dispatches, found {len(disp)}")
+    lines = [f"# Utilization of the dominant kernels: {args.workload}, {args.fmt}", "",
+             "rocprofv3 derived counters per dispatch over one eager step, in percent of the",
+             "kernel's active GPU cycles: MfmaUtil (matrix-unit busy cycles per SIMD), VALUBusy",
+             "(vector-ALU instruction cycles per CU), LdsUtil (LDS busy), LDSBankConflict.", "",
+             "```", "cd /tmp && export TMPDIR=/tmp",
+             f"rocprofv3 --pmc {' '.join(UTIL_COUNTERS)} --output-format csv -d <out>/util -o util -- "
+             f"python3 bench.py --workload {args.workload} --fmt {args.fmt} --pmc-step",
+             f"python3 bench.py --workload {args.workload} --fmt {args.fmt} --summarize-util <util csv>",
+             "```", "", f"Workload: {desc}.", "",
+             "| M | K | N | kernel | " + " | ".join(UTIL_COUNTERS) + " |",
+             "|---:|---:|---:|---|" + "---:|" * len(UTIL_COUNTERS)]
+    for (m, k, n), d in zip(configs, disp):
+        short = re.search(r"(k_[a-z_]+<[^>]*>)", d["name"])
+        lines.append(f"| {m} | {k} | {n} | `{short.group(1) if short else d['name']}` | " +
+                     " | ".join(f"{d.get(c, float('nan')):.1f}" for c in UTIL_COUNTERS) + " |")
+    out = os.path.join(ROOT, "profiles", f"{args.workload}_{args.fmt}_utilization.md")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(out)
 
 
 def summarize_pmc(args):
@@ -205,6 +248,9 @@ def main():
     args = parse()
     if args.summarize_pmc:
         summarize_pmc(args)
+        return
+    if args.summarize_util:
+        summarize_util(args)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
