@@ -156,10 +156,33 @@ def summarize_util(args):
         short = re.search(r"(k_[a-z_]+<[^>]*>)", d["name"])
         lines.append(f"| {m} | {k} | {n} | `{short.group(1) if short else d['name']}` | " +
                      " | ".join(f"{d.get(c, float('nan')):.1f}" for c in UTIL_COUNTERS) + " |")
-    out = os.path.join(ROOT, "profiles", f"{args.workload}_{args.fmt}_utilization.md")
+    mean = {c: round(sum(d.get(c, 0.0) for d in disp) / len(disp), 2) for c in UTIL_COUNTERS}
+    lines += ["", "Mean over the dispatches: " + ", ".join(f"{c} {v}" for c, v in mean.items()) + ".", "",
+              "<!-- util-json: " + json.dumps({"workload": args.workload, "fmt": args.fmt,
+                                                "src_hash": kernel_source_hash(), "mean": mean}) + " -->"]
+    out = util_path(args.workload, args.fmt)
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(out)
+
+
+def util_path(workload, fmt):
+    return os.path.join(ROOT, "profiles", f"{workload}_{fmt}_utilization.md")
+
+
+def stored_util(workload, fmt):
+    """Mean utilization counters of the dominant kernels from the committed
+    summary, or None when there is none or the kernels changed since."""
+    try:
+        with open(util_path(workload, fmt)) as fh:
+            for line in fh:
+                if line.startswith("<!-- util-json: "):
+                    rec = json.loads(line[len("<!-- util-json: "):].rsplit(" -->", 1)[0])
+                    if rec.get("src_hash") == kernel_source_hash():
+                        return rec["mean"]
+    except OSError:
+        pass
+    return None
 
 
 def summarize_pmc(args):
@@ -458,7 +481,10 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": None}
     # the counter summaries are taken for the W4A4 kernels without recipe flags
-    roof["traffic"] = None if (args.recipe or args.w4a16) else stored_traffic(args.workload, args.fmt)
+    plain = not (args.recipe or args.w4a16)
+    roof["traffic"] = stored_traffic(args.workload, args.fmt) if plain else None
+    # rocprofv3 MfmaUtil / VALUBusy / LdsUtil (percent) of the same kernels
+    roof["counters_pct"] = stored_util(args.workload, args.fmt) if plain else None
     roof.update({"kernel": " + ".join(sorted(kern)), "avg_launch_us": round(tot_us / tot_launch, 3),
                  "launches_per_step": tot_launch,
                  "per_kernel": {nm: {"launches": d["launches"], "avg_us": round(d["us"] / d["launches"], 3),
