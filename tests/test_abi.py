@@ -174,3 +174,36 @@ def test_w4a16_host_validation():
     c = fp4.fp4_tensor()
     assert L.fp4_tensor_init(ctypes.byref(c), fp4.NVFP4, fp4.CANONICAL, 32, 64, 4096, 8192, 64) == 0
     assert L.fp4_linear_w4a16(4096, 4, ctypes.byref(c), 8192, 32, None) == 5      # not tiled
+
+
+def test_last_error_is_per_thread():
+    """fp4_last_error() belongs to the calling thread: threads that fail in
+    different ways, interleaved, each read their own message."""
+    import threading
+    L = fp4.lib()
+    desc = fp4.fp4_tensor()
+    assert L.fp4_tensor_init(ctypes.byref(desc), fp4.NVFP4, fp4.CANONICAL, 4, 64, 4096, 8192, 64) == 0
+    results, barrier = {}, threading.Barrier(8)
+
+    def worker(i):
+        barrier.wait()
+        out = []
+        for _ in range(200):
+            if i % 2 == 0:   # null activations
+                st = L.fp4_quantize_act(0, None, 4, 64, None, ctypes.byref(desc), 1024, 4096, None)
+            else:            # K not a multiple of the block
+                st = L.fp4_quantize_act(0, 4096, 4, 40, None, ctypes.byref(desc), 1024, 4096, None)
+            out.append((st, L.fp4_last_error()))
+        results[i] = out
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    for i, out in results.items():
+        for st, msg in out:
+            if i % 2 == 0:
+                assert st == 1 and b"null" in msg, msg
+            else:
+                assert st == 2 and b"multiple" in msg, msg

@@ -165,3 +165,18 @@ def test_square_8192_sampled(fmt):
     """M = N = K = 8192, operands ~N(0, 1)."""
     a, w = synth.square_inputs(8192, seed=0)
     _sampled_full(fmt, a, w, "square 8192")
+
+
+_SQ16 = {}
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_square_16384_sampled(fmt):
+    """M = N = K = 16384 (the largest square configuration), operands ~N(0, 1);
+    the inputs are drawn once for both formats."""
+    if "ab" not in _SQ16:
+        _SQ16["ab"] = synth.square_inputs(16384, seed=0)
+    a, w = _SQ16["ab"]
+    _sampled_full(fmt, a, w, "square 16384", nsamp=2048)
+    if fmt == FMTS[-1]:
+        _SQ16.clear()
