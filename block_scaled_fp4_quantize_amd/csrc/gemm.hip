@@ -164,33 +164,40 @@ __global__ __launch_bounds__(256) void k_gemm_prefill(
 constexpr int kDecWaves = 8;
 constexpr int kDecFrags = 2;
 
-template <int FMT, int MG, int ATILED>
+template <int FMT, int MG, int ATILED, int NT>
 __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(
     const uint8_t *__restrict__ a_codes, int64_t a_cp, const uint8_t *__restrict__ a_sc,
     int64_t a_sp, const float *__restrict__ a_ts, const uint8_t *__restrict__ w_codes,
     const uint8_t *__restrict__ w_sc, const float *__restrict__ w_ts, int m, int n, int kt_n,
-    uint16_t *__restrict__ c, int64_t ldc) {
+    int nt_n, uint16_t *__restrict__ c, int64_t ldc) {
   // fragments per group: two, or one for eight activation groups (registers)
   constexpr int NW = kDecWaves, FM = MG >= 8 ? 1 : kDecFrags;
-  __shared__ float red[NW][MG][4][64];
-  const int nt = blockIdx.x;
+  __shared__ float red[NW][NT * MG][4][64];
+  const int nt0 = blockIdx.x * NT;  // first of this workgroup's NT weight tiles
   // readfirstlane makes the wave index (and every fragment guard derived from
   // it) a scalar, so the guards compile to branches around the matrix
   // instructions rather than to EXEC masks they would not honour.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  v4f acc[MG];
+  v4f acc[NT][MG];
 #pragma unroll
-  for (int g = 0; g < MG; ++g) acc[g] = v4f{0.f, 0.f, 0.f, 0.f};
-  uint4 wq[2][FM], aq[2][FM][MG];
-  uint32_t ws[2][FM], as[2][FM][MG];
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int g = 0; g < MG; ++g) acc[t][g] = v4f{0.f, 0.f, 0.f, 0.f};
+  uint4 wq[2][FM][NT], aq[2][FM][MG];
+  uint32_t ws[2][FM][NT], as[2][FM][MG];
 
   auto load = [&](int buf, int base) {
 #pragma unroll
     for (int u = 0; u < FM; ++u) {
       const int kt = base + NW * u;
       if (kt < kt_n) {
-        load_w<FMT>(w_codes, w_sc, (int64_t)nt * kt_n + kt, lane, wq[buf][u], ws[buf][u]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          // a tile past the last one reads the last again (its sums are never stored)
+          const int nt = min(nt0 + t, nt_n - 1);
+          load_w<FMT>(w_codes, w_sc, (int64_t)nt * kt_n + kt, lane, wq[buf][u][t], ws[buf][u][t]);
+        }
 #pragma unroll
         for (int g = 0; g < MG; ++g)
           load_a<FMT, ATILED>(a_codes, a_cp, a_sc, a_sp, kt_n, g, kt, lane, m, aq[buf][u][g],
@@ -204,16 +211,21 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(
       if (base + NW * u >= kt_n) break;  // wave-uniform
       if (FMT == 1) {
 #pragma unroll
-        for (int g = 0; g < MG; ++g)
-          acc[g] = mfma_mx(wq[buf][u], aq[buf][u][g], acc[g], ws[buf][u], as[buf][u][g]);
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int g = 0; g < MG; ++g)
+            acc[t][g] = mfma_mx(wq[buf][u][t], aq[buf][u][g], acc[t][g], ws[buf][u][t], as[buf][u][g]);
       } else {
-        h8v wh[4];
-        nv_dequant32(wq[buf][u], ws[buf][u], wh);
+        // each activation group is dequantized once for the NT weight tiles
+        h8v wh[NT][4];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) nv_dequant32(wq[buf][u][t], ws[buf][u][t], wh[t]);
 #pragma unroll
         for (int g = 0; g < MG; ++g) {
           h8v ah[4];
           nv_dequant32(aq[buf][u][g], as[buf][u][g], ah);
-          acc[g] = mfma_nv(wh, ah, acc[g]);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) acc[t][g] = mfma_nv(wh[t], ah, acc[t][g]);
         }
       }
     }
@@ -228,20 +240,23 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(
     compute(1, base + STEP);
   }
 #pragma unroll
-  for (int g = 0; g < MG; ++g)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][g][r][lane] = acc[g][r];
+    for (int g = 0; g < MG; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][t * MG + g][r][lane] = acc[t][g][r];
   __syncthreads();
   const int tg = threadIdx.x >> 6;  // accumulator group reduced by this wave
-  if (tg >= MG) return;
+  if (tg >= NT * MG) return;
+  const int t = tg / MG, g = tg % MG;
   const Alpha alpha = FMT == 0 ? make_alpha(a_ts[0], w_ts[0]) : Alpha{1.0f, 0};
-  const int col = 16 * tg + (lane & 15);  // activation row m
+  const int col = 16 * g + (lane & 15);  // activation row m
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     float v = red[0][tg][r][lane];
 #pragma unroll
     for (int w2 = 1; w2 < NW; ++w2) v += red[w2][tg][r][lane];
-    const int row = nt * 16 + 4 * (lane >> 4) + r;  // output column n
+    const int row = (nt0 + t) * 16 + 4 * (lane >> 4) + r;  // output column n
     if (col < m && row < n) c[(int64_t)col * ldc + row] = f32_to_bf16_rne(apply_alpha(v, alpha));
   }
 }
@@ -410,22 +425,29 @@ hipError_t launch_gemm_decode(const GemmArgs &g, hipStream_t stream) {
   const int kt_n = (int)(k_pad(g.k) / kFragK);
   const int nt_n = (int)(round_up(g.n, 16) / 16);
   const int mg = g.m <= 16 ? 1 : g.m <= 32 ? 2 : g.m <= 64 ? 4 : 8;
-  dim3 grid((unsigned)nt_n);
-#define FP4_DEC(F, G, T)                                                                        \
-  hipLaunchKernelGGL((k_gemm_decode<F, G, T>), grid, dim3(64 * kDecWaves), 0, stream,          \
+  // MXFP4 with 17-32 activation rows: two weight tiles per workgroup when
+  // that still leaves >= 256 workgroups, so the activations are read once per
+  // two tiles (measured: 17.7 -> 15.8 us at M = 32, N = 17408). NVFP4 keeps
+  // one tile: its second tile's dequantization registers cost occupancy and
+  // the same shape ran 2.8 us slower.
+  const int nt_per = (g.fmt == 1 && mg == 2 && nt_n >= 512) ? 2 : 1;
+  dim3 grid((unsigned)((nt_n + nt_per - 1) / nt_per));
+#define FP4_DEC(F, G, T, P)                                                                     \
+  hipLaunchKernelGGL((k_gemm_decode<F, G, T, P>), grid, dim3(64 * kDecWaves), 0, stream,       \
                      g.a_codes, g.a_cpitch, g.a_scales, g.a_spitch, g.a_ts, g.w_codes,         \
-                     g.w_scales, g.w_ts, (int)g.m, (int)g.n, kt_n, g.c, g.ldc)
-#define FP4_DEC_T(F, G) do { if (g.a_tiled) FP4_DEC(F, G, 1); else FP4_DEC(F, G, 0); } while (0)
+                     g.w_scales, g.w_ts, (int)g.m, (int)g.n, kt_n, nt_n, g.c, g.ldc)
+#define FP4_DEC_T(F, G, P) do { if (g.a_tiled) FP4_DEC(F, G, 1, P); else FP4_DEC(F, G, 0, P); } while (0)
   if (g.fmt == 0) {
-    if (mg == 1) FP4_DEC_T(0, 1);
-    else if (mg == 2) FP4_DEC_T(0, 2);
-    else if (mg == 4) FP4_DEC_T(0, 4);
-    else FP4_DEC_T(0, 8);
+    if (mg == 1) FP4_DEC_T(0, 1, 1);
+    else if (mg == 2) FP4_DEC_T(0, 2, 1);
+    else if (mg == 4) FP4_DEC_T(0, 4, 1);
+    else FP4_DEC_T(0, 8, 1);
   } else {
-    if (mg == 1) FP4_DEC_T(1, 1);
-    else if (mg == 2) FP4_DEC_T(1, 2);
-    else if (mg == 4) FP4_DEC_T(1, 4);
-    else FP4_DEC_T(1, 8);
+    if (mg == 1) FP4_DEC_T(1, 1, 1);
+    else if (mg == 2 && nt_per == 2) FP4_DEC_T(1, 2, 2);
+    else if (mg == 2) FP4_DEC_T(1, 2, 1);
+    else if (mg == 4) FP4_DEC_T(1, 4, 1);
+    else FP4_DEC_T(1, 8, 1);
   }
 #undef FP4_DEC_T
 #undef FP4_DEC

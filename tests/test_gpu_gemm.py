@@ -43,7 +43,9 @@ def test_single_gemm_config(fmt):
                                    (5, 520, 5120), (2, 48, 17408),
                                    # four and eight activation groups of 16 (M up to 128)
                                    (48, 300, 1024), (64, 1040, 2880), (65, 100, 512),
-                                   (100, 520, 4160), (128, 257, 640), (128, 48, 17408)])
+                                   (100, 520, 4160), (128, 257, 640), (128, 48, 17408),
+                                   # two weight tiles per workgroup (>= 512 tiles), odd count
+                                   (5, 8200, 256), (20, 8200, 512), (32, 8192, 128)])
 def test_decode_path(fmt, m, n, k):
     a = synth.normal((m, k), 1.0, 3, m * 31 + k)
     w = synth.normal((n, k), 0.02, 3, n * 17 + k)
