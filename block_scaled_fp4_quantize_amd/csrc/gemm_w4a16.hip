@@ -139,42 +139,52 @@ __device__ __forceinline__ v4f mma_bf16(bf8v a, uint4 b, v4f c) {
 
 // ------------------------------------------------------------------ decode
 //
-// M <= 32: one workgroup per 16-row weight tile covering all of K, eight waves
-// taking interleaved K steps (kt = wave + 8 j), the next step's loads issued
-// before the current step's arithmetic; partial sums added in LDS in a fixed
-// order. The weight tile is the matrix instruction's A operand, so the
-// accumulator holds y^T (rows n, columns m).
+// M <= 32: one workgroup per NT 16-row weight tiles covering all of K, eight
+// waves taking interleaved K steps (kt = wave + 8 j), the next step's loads
+// issued before the current step's arithmetic; partial sums added in LDS in a
+// fixed order. The weight tile is the matrix instruction's A operand, so the
+// accumulator holds y^T (rows n, columns m). Every workgroup reads the bf16
+// activation rows of the whole K from L2, which bounds the kernel once there
+// are many rows: NT > 1 tiles per workgroup read them once for NT tiles.
 constexpr int kW16Waves = 8;
 
-template <int FMT, int MG>
+template <int FMT, int MG, int NT>
 __global__ __launch_bounds__(64 * kW16Waves) void k_w4a16_decode(
     const uint16_t *__restrict__ x, int64_t ldx, const uint8_t *__restrict__ w_codes,
     const uint8_t *__restrict__ w_sc, const float *__restrict__ w_ts, int m, int n, int k,
-    int kt_n, uint16_t *__restrict__ y, int64_t ldy) {
+    int kt_n, int nt_n, uint16_t *__restrict__ y, int64_t ldy) {
   constexpr int NW = kW16Waves;
-  __shared__ float red[NW][MG][4][64];
-  const int nt = blockIdx.x;
+  __shared__ float red[NW][NT * MG][4][64];
+  const int nt0 = blockIdx.x * NT;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  v4f acc[MG];
+  v4f acc[NT][MG];
 #pragma unroll
-  for (int g = 0; g < MG; ++g) acc[g] = v4f{0.f, 0.f, 0.f, 0.f};
-  uint4 wq[2], xa[2][MG][4];
-  uint32_t ws[2];
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int g = 0; g < MG; ++g) acc[t][g] = v4f{0.f, 0.f, 0.f, 0.f};
+  uint4 wq[2][NT], xa[2][MG][4];
+  uint32_t ws[2][NT];
   auto load = [&](int buf, int kt) __attribute__((always_inline)) {
     if (kt < kt_n) {
-      load_wfrag<FMT>(w_codes, w_sc, (int64_t)nt * kt_n + kt, lane, wq[buf], ws[buf]);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)  // a tile past the last reads the last again (never stored)
+        load_wfrag<FMT>(w_codes, w_sc, (int64_t)min(nt0 + t, nt_n - 1) * kt_n + kt, lane,
+                        wq[buf][t], ws[buf][t]);
 #pragma unroll
       for (int g = 0; g < MG; ++g) load_x(x, ldx, 16 * g + (lane & 15), m, k, kt, lane, xa[buf][g]);
     }
   };
   auto compute = [&](int buf) __attribute__((always_inline)) {
-    bf8v wh[4];
-    deq_w32<FMT>(wq[buf], ws[buf], wh);
 #pragma unroll
-    for (int g = 0; g < MG; ++g)
+    for (int t = 0; t < NT; ++t) {
+      bf8v wh[4];
+      deq_w32<FMT>(wq[buf][t], ws[buf][t], wh);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) acc[g] = mma_bf16(wh[s], xa[buf][g][s], acc[g]);
+      for (int g = 0; g < MG; ++g)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc[t][g] = mma_bf16(wh[s], xa[buf][g][s], acc[t][g]);
+    }
   };
   load(0, wave);
   for (int kt = wave; kt < kt_n; kt += 2 * NW) {
@@ -185,20 +195,23 @@ __global__ __launch_bounds__(64 * kW16Waves) void k_w4a16_decode(
     compute(1);
   }
 #pragma unroll
-  for (int g = 0; g < MG; ++g)
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][g][r][lane] = acc[g][r];
+    for (int g = 0; g < MG; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][t * MG + g][r][lane] = acc[t][g][r];
   __syncthreads();
   const int tg = threadIdx.x >> 6;
-  if (tg >= MG) return;
+  if (tg >= NT * MG) return;
+  const int t = tg / MG, g = tg % MG;
   const Alpha alpha = FMT == 0 ? make_alpha(1.0f, w_ts[0]) : Alpha{1.0f, 0};
-  const int col = 16 * tg + (lane & 15);  // activation row m
+  const int col = 16 * g + (lane & 15);  // activation row m
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     float v = red[0][tg][r][lane];
 #pragma unroll
     for (int w2 = 1; w2 < NW; ++w2) v += red[w2][tg][r][lane];
-    const int row = nt * 16 + 4 * (lane >> 4) + r;  // output column n
+    const int row = (nt0 + t) * 16 + 4 * (lane >> 4) + r;  // output column n
     if (col < m && row < n) y[(int64_t)col * ldy + row] = f32_to_bf16_rne(apply_alpha(v, alpha));
   }
 }
@@ -271,14 +284,24 @@ hipError_t launch_linear_w4a16(int fmt, const uint16_t *x, int64_t ldx, int64_t 
   const int nt_n = (int)(round_up(n, 16) / 16);
   if (m <= kW16DecodeMaxM) {
     const int mg = m <= 16 ? 1 : 2;
-#define FP4_W16D(F, G)                                                                          \
-  hipLaunchKernelGGL((k_w4a16_decode<F, G>), dim3((unsigned)nt_n), dim3(64 * kW16Waves), 0,    \
-                     stream, x, ldx, w_codes, w_scales, w_ts, (int)m, (int)n, (int)k, kt_n, y, \
-                     ldy)
-    if (fmt == 0 && mg == 1) FP4_W16D(0, 1);
-    else if (fmt == 0) FP4_W16D(0, 2);
-    else if (mg == 1) FP4_W16D(1, 1);
-    else FP4_W16D(1, 2);
+    // weight tiles per workgroup (measured on the decode shapes): with 17-32
+    // rows the activation reads from L2 dominate, so 4 tiles (>= 1024 tiles)
+    // or 2 (>= 256, leaving 128+ workgroups); MXFP4 from 8 rows also gains
+    // with 4; otherwise one (fewer, longer workgroups lost at M = 1, and for
+    // NVFP4, whose weight dequantization is the heavier part, at M = 8).
+    const int per = mg == 2 ? (nt_n >= 1024 ? 4 : nt_n >= 256 ? 2 : 1)
+                            : (fmt == 1 && m >= 8 && nt_n >= 1024 ? 4 : 1);
+#define FP4_W16D(F, G, T)                                                                      \
+  hipLaunchKernelGGL((k_w4a16_decode<F, G, T>), dim3((unsigned)((nt_n + T - 1) / T)),         \
+                     dim3(64 * kW16Waves), 0, stream, x, ldx, w_codes, w_scales, w_ts, (int)m, \
+                     (int)n, (int)k, kt_n, nt_n, y, ldy)
+#define FP4_W16P(F, G) do { if (per == 4) FP4_W16D(F, G, 4); else if (per == 2) FP4_W16D(F, G, 2); \
+                            else FP4_W16D(F, G, 1); } while (0)
+    if (fmt == 0 && mg == 1) FP4_W16P(0, 1);
+    else if (fmt == 0) FP4_W16P(0, 2);
+    else if (mg == 1) FP4_W16P(1, 1);
+    else FP4_W16P(1, 2);
+#undef FP4_W16P
 #undef FP4_W16D
     return hipGetLastError();
   }

@@ -40,6 +40,7 @@ def _case(fmt, a, w, what, sample=None):
     (1, 256, 256), (5, 2880, 520), (16, 1056, 100), (17, 4160, 64), (32, 5120, 1000),
     (1, 48, 33), (3, 16, 17),           # K below one fragment; NVFP4 K tail of 16
     (33, 512, 17), (300, 1024, 700), (520, 4160, 1000), (129, 2880, 4096),
+    (8, 256, 16400), (20, 512, 8200), (24, 1024, 4100),  # 4 / 2 tiles per workgroup, odd counts
 ])
 def test_w4a16_shapes(fmt, m, k, n):
     if fmt == "mxfp4" and k % 32:
