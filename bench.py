@@ -455,8 +455,8 @@ def main():
             # the activation layout fp4_linear uses internally (fragment-tiled)
             qa = fp4.fp4_quantize_act(xs[cfg], qfmt, layout=fp4.TILED)
             if m <= 128:
-                name = "k_gemm_decode<%s,MG=%d>" % (args.fmt, 1 if m <= 16 else 2 if m <= 32 else
-                                                     4 if m <= 64 else 8)
+                name = "%s<%s,MG=%d>" % ("k_gemm_decode_ring" if qfmt == fp4.NVFP4 else "k_gemm_decode",
+                                         args.fmt, 1 if m <= 16 else 2 if m <= 32 else 4 if m <= 64 else 8)
             else:   # LDS-staged tiles; 256 x 256 when that fills the 256 CUs
                 big = -(-m // 256) * -(-n // 256) >= 256
                 name = "k_gemm_tile<%s,%s>" % (args.fmt, "256x256" if big else "128x128")

@@ -22,6 +22,8 @@
 #include "fp4_device.h"
 #include "fp4_internal.h"
 
+#include <algorithm>
+
 namespace fp4i {
 using namespace fp4d;
 
@@ -153,9 +155,13 @@ __global__ __launch_bounds__(256) void k_gemm_prefill(
 // workgroup per 16-row weight tile covers the whole K range, so there is no
 // cross-workgroup reduction: every workgroup is resident at once and HBM
 // bandwidth is shared among them. The kDecWaves waves take interleaved
-// fragments (kt = wave + kDecWaves * j) and keep two groups of FM fragments
-// in flight (the next group's loads are issued before the current group's
-// arithmetic). The weight tile is the MFMA's A operand (rows n) and the
+// fragments (kt = wave + kDecWaves * j) in groups of FM; the next group's loads
+// are issued before the current group's arithmetic, whose wait then covers
+// both groups (the fragment guards put loads under branches, and the compiler
+// merges their wait counts), so a wave drains its loads every group. MXFP4
+// uses this kernel: for its one-instruction fragments it measured faster than
+// every deeper pipeline tried (the ring kernel below). The weight tile is the
+// MFMA's A operand (rows n) and the
 // activations its B operand (columns m, MG groups of 16: 1, 2, 4 or 8), so
 // the accumulator holds C^T. The waves' partial sums are added in LDS in a
 // fixed order. Up to M = 128 this beats the tiled kernels, whose few output
@@ -258,6 +264,169 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(
     for (int w2 = 1; w2 < NW; ++w2) v += red[w2][tg][r][lane];
     const int row = (nt0 + t) * 16 + 4 * (lane >> 4) + r;  // output column n
     if (col < m && row < n) c[(int64_t)col * ldc + row] = f32_to_bf16_rne(apply_alpha(v, alpha));
+  }
+}
+
+// ------------------------------------------------------------ decode, ring
+//
+// The same skinny GEMM (one workgroup per 16-row weight tile, kRingWaves waves
+// over K, partial sums added in LDS in a fixed order) with its operands read
+// through a ring of kRingDepth register slots per wave: slot d is consumed and
+// at once refilled with the fragment kRingDepth steps ahead. Every operand is
+// read with a buffer load whose resource ends at the operand's last valid
+// byte; reads past it (fragments past K, activation rows past M, tiles past N)
+// return zero. The loop body has no memory access under a branch, which keeps
+// the compiler's wait counts exact: a slot waits only for its own loads. NVFP4
+// uses it: its per-fragment dequantization then overlaps the next fragments'
+// loads (decode benchmark, GEMM kernels only: 142 -> 131 us per step). MXFP4,
+// whose fragments cost one matrix instruction, measured slower with any ring
+// depth than with the group-of-two loads of k_gemm_decode (97 us: 104, 109,
+// 113 and 125 us at depths 1 to 4).
+constexpr int kRingWaves = 8;
+constexpr int kRingDepth = 2;
+
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+
+// Buffer resource over `bytes` bytes at p (raw, stride 0; gfx9 word 3).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u4v v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <int FMT>
+__device__ __forceinline__ uint32_t buf_load_scale(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if (FMT == 0) return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
+}
+
+// The operand pointers are not declared __restrict__: the compiler would then
+// take the buffer loads as invariant and move them across the ordering
+// statements below.
+template <int FMT, int MG, int ATILED, int NT>
+__global__ __launch_bounds__(64 * kRingWaves) void k_gemm_decode_ring(
+    const uint8_t *a_codes, int64_t a_cp, const uint8_t *a_sc, int64_t a_sp,
+    const float *__restrict__ a_ts, const uint8_t *w_codes, const uint8_t *w_sc,
+    const float *__restrict__ w_ts, int m, int n, int kt_n, int nt_n, uint16_t *c, int64_t ldc) {
+  constexpr int NW = kRingWaves, D = kRingDepth;
+  constexpr int SFB = FMT == 0 ? 128 : 64;  // scale bytes per fragment
+  __shared__ float red[NW][NT * MG][4][64];
+  const int nt0 = blockIdx.x * NT;  // first of this workgroup's NT weight tiles
+  // readfirstlane makes the wave index (and every guard derived from it) a
+  // scalar, so guards compile to branches rather than to EXEC masks that a
+  // matrix instruction would not honour.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int tiles = min(NT, nt_n - nt0);
+  const __amdgpu_buffer_rsrc_t wr = buf_rsrc(w_codes + (int64_t)nt0 * kt_n * kFragCodeBytes,
+                                             (uint32_t)(tiles * kt_n * kFragCodeBytes));
+  const __amdgpu_buffer_rsrc_t wsr = buf_rsrc(w_sc + (int64_t)nt0 * kt_n * SFB,
+                                              (uint32_t)(tiles * kt_n * SFB));
+  // Activations: tiled = ceil(m / 16) groups of kt_n fragments; canonical =
+  // m rows of pitch a_cp (codes) and a_sp (scales).
+  const int ag = (m + 15) >> 4;
+  const __amdgpu_buffer_rsrc_t ar =
+      buf_rsrc(a_codes, (uint32_t)(ATILED ? (int64_t)ag * kt_n * kFragCodeBytes : (int64_t)m * a_cp));
+  const __amdgpu_buffer_rsrc_t asr =
+      buf_rsrc(a_sc, (uint32_t)(ATILED ? (int64_t)ag * kt_n * SFB : (int64_t)m * a_sp));
+  const int lr = lane & 15, lc = lane >> 4;
+
+  v4f acc[NT][MG];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int g = 0; g < MG; ++g) acc[t][g] = v4f{0.f, 0.f, 0.f, 0.f};
+  uint4 wq[D][NT], aq[D][MG];
+  uint32_t ws[D][NT], as[D][MG];
+
+  // Byte offsets of fragment kt. Loads that must not happen (kt >= kt_n,
+  // activation rows >= m) take an offset past every resource's end (each is
+  // below 2^31 bytes), so they return zero without reading memory.
+  constexpr uint32_t kOut = 0x80000000u;
+  auto issue = [&](int d, int kt) {
+    const bool kin = kt < kt_n;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint32_t f = (uint32_t)(t * kt_n + kt);
+      wq[d][t] = buf_load16(wr, kin ? f * kFragCodeBytes + lane * 16 : kOut);
+      ws[d][t] = buf_load_scale<FMT>(wsr, kin ? f * SFB + lane * (FMT == 0 ? 2 : 1) : kOut);
+    }
+#pragma unroll
+    for (int g = 0; g < MG; ++g) {
+      const int row = 16 * g + lr;
+      uint32_t co = kOut, so = kOut;
+      if (kin && row < m) {
+        if (ATILED) {
+          const uint32_t f = (uint32_t)(g * kt_n + kt);
+          co = f * kFragCodeBytes + lane * 16;
+          so = f * SFB + lane * (FMT == 0 ? 2 : 1);
+        } else {
+          co = (uint32_t)((int64_t)row * a_cp + kt * 64 + lc * 16);
+          so = (uint32_t)((int64_t)row * a_sp + kt * (FMT == 0 ? 8 : 4) + lc * (FMT == 0 ? 2 : 1));
+        }
+      }
+      aq[d][g] = buf_load16(ar, co);
+      as[d][g] = buf_load_scale<FMT>(asr, so);
+    }
+  };
+  auto compute = [&](int d) {
+    if (FMT == 1) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int g = 0; g < MG; ++g) acc[t][g] = mfma_mx(wq[d][t], aq[d][g], acc[t][g], ws[d][t], as[d][g]);
+    } else {
+      // each activation group is dequantized once for the NT weight tiles
+      h8v wh[NT][4];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) nv_dequant32(wq[d][t], ws[d][t], wh[t]);
+#pragma unroll
+      for (int g = 0; g < MG; ++g) {
+        h8v ah[4];
+        nv_dequant32(aq[d][g], as[d][g], ah);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t][g] = mfma_nv(wh[t], ah, acc[t][g]);
+      }
+    }
+  };
+
+  const int J = wave < kt_n ? (kt_n - 1 - wave) / NW + 1 : 0;  // this wave's fragments
+  // An empty asm statement with a memory clobber between slots keeps the
+  // slots' loads in slot order (the order in which they are consumed), so
+  // that each slot waits only for its own and older loads.
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    issue(d, wave + NW * d);
+    asm volatile("" ::: "memory");
+  }
+  for (int j0 = 0; j0 < J; j0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (j0 + d < J) compute(d);  // wave-uniform; no memory access inside
+      issue(d, wave + NW * (j0 + d + D));
+      asm volatile("" ::: "memory");
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int g = 0; g < MG; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][t * MG + g][r][lane] = acc[t][g][r];
+  __syncthreads();
+  const Alpha alpha = FMT == 0 ? make_alpha(a_ts[0], w_ts[0]) : Alpha{1.0f, 0};
+  for (int tg = wave; tg < NT * MG; tg += NW) {  // accumulator groups reduced by this wave
+    const int t = tg / MG, g = tg % MG;
+    const int col = 16 * g + lr;  // activation row m
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v = red[0][tg][r][lane];
+#pragma unroll
+      for (int w2 = 1; w2 < NW; ++w2) v += red[w2][tg][r][lane];
+      const int row = (nt0 + t) * 16 + 4 * lc + r;  // output column n
+      if (col < m && row < n) c[(int64_t)col * ldc + row] = f32_to_bf16_rne(apply_alpha(v, alpha));
+    }
   }
 }
 
@@ -425,30 +594,41 @@ hipError_t launch_gemm_decode(const GemmArgs &g, hipStream_t stream) {
   const int kt_n = (int)(k_pad(g.k) / kFragK);
   const int nt_n = (int)(round_up(g.n, 16) / 16);
   const int mg = g.m <= 16 ? 1 : g.m <= 32 ? 2 : g.m <= 64 ? 4 : 8;
+  if (g.fmt == 0) {
+    // the ring kernel's buffer resources (and offsets) stay below 2^31 bytes
+    const int64_t a_bytes = g.a_tiled ? round_up(g.m, 16) / 16 * kt_n * kFragCodeBytes
+                                      : g.m * std::max(g.a_cpitch, g.a_spitch) + (int64_t)kt_n * 64;
+    if (a_bytes >= (int64_t(1) << 31) || (int64_t)kt_n * kFragCodeBytes >= (int64_t(1) << 30))
+      return hipErrorInvalidValue;
+    dim3 grid((unsigned)nt_n);
+#define FP4_RING(G, T)                                                                          \
+  hipLaunchKernelGGL((k_gemm_decode_ring<0, G, T, 1>), grid, dim3(64 * kRingWaves), 0, stream, \
+                     g.a_codes, g.a_cpitch, g.a_scales, g.a_spitch, g.a_ts, g.w_codes,         \
+                     g.w_scales, g.w_ts, (int)g.m, (int)g.n, kt_n, nt_n, g.c, g.ldc)
+#define FP4_RING_T(G) do { if (g.a_tiled) FP4_RING(G, 1); else FP4_RING(G, 0); } while (0)
+    if (mg == 1) FP4_RING_T(1);
+    else if (mg == 2) FP4_RING_T(2);
+    else if (mg == 4) FP4_RING_T(4);
+    else FP4_RING_T(8);
+#undef FP4_RING_T
+#undef FP4_RING
+    return hipGetLastError();
+  }
   // MXFP4 with 17-32 activation rows: two weight tiles per workgroup when
   // that still leaves >= 256 workgroups, so the activations are read once per
-  // two tiles (measured: 17.7 -> 15.8 us at M = 32, N = 17408). NVFP4 keeps
-  // one tile: its second tile's dequantization registers cost occupancy and
-  // the same shape ran 2.8 us slower.
-  const int nt_per = (g.fmt == 1 && mg == 2 && nt_n >= 512) ? 2 : 1;
+  // two tiles (measured: 17.7 -> 15.8 us at M = 32, N = 17408).
+  const int nt_per = (mg == 2 && nt_n >= 512) ? 2 : 1;
   dim3 grid((unsigned)((nt_n + nt_per - 1) / nt_per));
 #define FP4_DEC(F, G, T, P)                                                                     \
   hipLaunchKernelGGL((k_gemm_decode<F, G, T, P>), grid, dim3(64 * kDecWaves), 0, stream,       \
                      g.a_codes, g.a_cpitch, g.a_scales, g.a_spitch, g.a_ts, g.w_codes,         \
                      g.w_scales, g.w_ts, (int)g.m, (int)g.n, kt_n, nt_n, g.c, g.ldc)
 #define FP4_DEC_T(F, G, P) do { if (g.a_tiled) FP4_DEC(F, G, 1, P); else FP4_DEC(F, G, 0, P); } while (0)
-  if (g.fmt == 0) {
-    if (mg == 1) FP4_DEC_T(0, 1, 1);
-    else if (mg == 2) FP4_DEC_T(0, 2, 1);
-    else if (mg == 4) FP4_DEC_T(0, 4, 1);
-    else FP4_DEC_T(0, 8, 1);
-  } else {
-    if (mg == 1) FP4_DEC_T(1, 1, 1);
-    else if (mg == 2 && nt_per == 2) FP4_DEC_T(1, 2, 2);
-    else if (mg == 2) FP4_DEC_T(1, 2, 1);
-    else if (mg == 4) FP4_DEC_T(1, 4, 1);
-    else FP4_DEC_T(1, 8, 1);
-  }
+  if (mg == 1) FP4_DEC_T(1, 1, 1);
+  else if (mg == 2 && nt_per == 2) FP4_DEC_T(1, 2, 2);
+  else if (mg == 2) FP4_DEC_T(1, 2, 1);
+  else if (mg == 4) FP4_DEC_T(1, 4, 1);
+  else FP4_DEC_T(1, 8, 1);
 #undef FP4_DEC_T
 #undef FP4_DEC
   return hipGetLastError();
