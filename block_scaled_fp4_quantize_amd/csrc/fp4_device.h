@@ -210,30 +210,50 @@ __device__ __forceinline__ uint32_t absmax_bits8(uint4 v) {
   return m;
 }
 
-// Fast NVFP4 element codes for 8 values with a bracket test. z = x * r with
-// r ~ 1/d_b (relative error < 2^-22 in total), so the exact quotient x / d_b
-// lies strictly inside [z (1 - 2^-20), z (1 + 2^-20)]. The hardware convert
-// rounds both ends exactly (nearest, ties to even, saturating); when they give
-// the same code, rounding is monotonic, so that code is the exact quotient's.
-// When they differ the quotient is within 2^-20 of a rounding midpoint (or on
-// it) and the exact comparisons decide. Returns the 8 nibbles.
-__device__ __forceinline__ uint32_t nv_encode8_fast(const NvBlockEnc &e, float r, uint4 v) {
+// Fast NVFP4 element codes for 8 values with a bracket test. r ~ 1/d_b has a
+// relative error below 2^-22, so r_lo = RN(r (1 - 2^-20)) and
+// r_hi = RN(r (1 + 2^-20)) are strictly below and above 1/d_b, and the once-
+// rounded products x r_lo and x r_hi strictly bracket the exact quotient
+// x / d_b (their own rounding adds at most 2^-24). The hardware convert rounds
+// two values at a time (nearest, ties to even, saturating) into one code byte,
+// so each dword of bf16 pairs costs two converts, one per bracket end. When
+// both ends give the same 8 codes, rounding is monotonic, so those are the
+// exact quotient's codes; otherwise a quotient lies within 2^-19 of a rounding
+// midpoint (or on it) and the exact comparisons decide. Returns the 8 nibbles.
+__device__ __forceinline__ uint32_t nv_encode8_fast(uint32_t sbyte, float st, float r_lo,
+                                                    float r_hi, uint4 v) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t out = 0, diff = 0;
+  uint32_t lo = 0, hi = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const float x = __uint_as_float(h ? (w[i] & 0xFFFF0000u) : (w[i] << 16));
-      const float z = x * r;
-      const uint32_t b =
-          __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, z * 0x1.ffffep-1f, z * 0x1.00001p+0f, 1.0f, 0);
-      diff |= (b ^ (b >> 4)) & 0xFu;
-      out |= (b & 0xFu) << (4 * (2 * i + h));
+    const float x0 = __uint_as_float(w[i] << 16), x1 = __uint_as_float(w[i] & 0xFFFF0000u);
+    // the byte-select operand writes byte i and keeps the others
+    switch (i) {
+      case 0:
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, x0 * r_lo, x1 * r_lo, 1.0f, 0);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, x0 * r_hi, x1 * r_hi, 1.0f, 0);
+        break;
+      case 1:
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, x0 * r_lo, x1 * r_lo, 1.0f, 1);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, x0 * r_hi, x1 * r_hi, 1.0f, 1);
+        break;
+      case 2:
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, x0 * r_lo, x1 * r_lo, 1.0f, 2);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, x0 * r_hi, x1 * r_hi, 1.0f, 2);
+        break;
+      default:
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, x0 * r_lo, x1 * r_lo, 1.0f, 3);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, x0 * r_hi, x1 * r_hi, 1.0f, 3);
+        break;
     }
   }
-  if (diff) out = nv_encode8(e, v);  // near a midpoint: exact comparisons
-  return out;
+  if (lo != hi) {  // near a midpoint: exact comparisons
+    // The empty statement hides v's value from the optimizer, so that the
+    // exact path's per-value work is not hoisted into the common path.
+    asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+    lo = nv_encode8(nv_block_encoder(sbyte, st), v);
+  }
+  return lo;
 }
 
 // One NVFP4 block (16 values in v0, v1) under tensor scale st: 8 code bytes
@@ -243,13 +263,15 @@ __device__ __forceinline__ void nv_encode_block(uint4 v0, uint4 v1, float st, ui
   const uint32_t abits = max(absmax_bits8(v0), absmax_bits8(v1));
   const double q = (double)bf16_bits_to_f32(abits) / (6.0 * (double)st);
   sbyte = e4m3_rne_sat(q);
-  const NvBlockEnc enc = nv_block_encoder(sbyte, st);
   if (sbyte != 0u && st >= 0x1p-100f) {
     // d_b = s_b * S_t >= 2^-109, so its reciprocal is a finite normal float;
-    // rounding d_b and the reciprocal add < 2^-22 relative error to z.
+    // rounding d_b and the reciprocal add < 2^-22 relative error to it.
     const float r = __builtin_amdgcn_rcpf(e4m3_to_f32(sbyte) * st);
-    codes = make_uint2(nv_encode8_fast(enc, r, v0), nv_encode8_fast(enc, r, v1));
+    const float r_lo = r * 0x1.ffffep-1f, r_hi = r * 0x1.00001p+0f;
+    codes = make_uint2(nv_encode8_fast(sbyte, st, r_lo, r_hi, v0),
+                       nv_encode8_fast(sbyte, st, r_lo, r_hi, v1));
   } else {
+    const NvBlockEnc enc = nv_block_encoder(sbyte, st);
     codes = make_uint2(nv_encode8(enc, v0), nv_encode8(enc, v1));
   }
 }
