@@ -88,7 +88,7 @@ def gemm_bytes(m, k, n, fmt):
     return n * q + m * q + 2 * m * n
 
 
-DOMINANT = ("k_gemm_decode", "k_linear_decode", "k_gemm_tile")
+DOMINANT = ("k_gemm_decode", "k_linear_decode", "k_gemm_tile", "k_w4a16_decode", "k_w4a16_tile")
 
 
 def kernel_source_hash():
@@ -103,15 +103,28 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_path(workload, fmt):
-    return os.path.join(ROOT, "profiles", f"{workload}_{fmt}_hbm_traffic.md")
+def variant_tag(args):
+    """Profile-file suffix of a run: the weight-only linear and the recipe flags
+    have summaries of their own ("" for plain W4A4)."""
+    parts = (["w4a16"] if args.w4a16 else []) + ([args.recipe.replace("+", "_")] if args.recipe else [])
+    return "".join("_" + x for x in parts)
 
 
-def stored_traffic(workload, fmt):
+def variant_flags(args):
+    """The bench.py flags that select the same variant (for the commands quoted
+    in the summaries)."""
+    return (" --w4a16" if args.w4a16 else "") + (f" --recipe {args.recipe}" if args.recipe else "")
+
+
+def traffic_path(workload, fmt, tag=""):
+    return os.path.join(ROOT, "profiles", f"{workload}_{fmt}{tag}_hbm_traffic.md")
+
+
+def stored_traffic(workload, fmt, tag=""):
     """HBM bytes per launch of the dominant kernels from the committed counter
     summary, or None when there is none or the kernels changed since."""
     try:
-        with open(traffic_path(workload, fmt)) as fh:
+        with open(traffic_path(workload, fmt, tag)) as fh:
             for line in fh:
                 if line.startswith("<!-- traffic-json: "):
                     rec = json.loads(line[len("<!-- traffic-json: "):].rsplit(" -->", 1)[0])
@@ -141,14 +154,15 @@ def summarize_util(args):
     disp = [vals[d] for d in sorted(vals)]
     if len(disp) != len(configs):
         raise SystemExit(f"expected {len(configs)} dominant-kernel dispatches, found {len(disp)}")
-    lines = [f"# Utilization of the dominant kernels: {args.workload}, {args.fmt}", "",
+    tag, flags = variant_tag(args), variant_flags(args)
+    lines = [f"# Utilization of the dominant kernels: {args.workload}, {args.fmt}{tag.replace('_', ' ')}", "",
              "rocprofv3 derived counters per dispatch over one eager step, in percent of the",
              "kernel's active GPU cycles: MfmaUtil (matrix-unit busy cycles per SIMD), VALUBusy",
              "(vector-ALU instruction cycles per CU), LdsUtil (LDS busy), LDSBankConflict.", "",
              "```", "cd /tmp && export TMPDIR=/tmp",
              f"rocprofv3 --pmc {' '.join(UTIL_COUNTERS)} --output-format csv -d <out>/util -o util -- "
-             f"python3 bench.py --workload {args.workload} --fmt {args.fmt} --pmc-step",
-             f"python3 bench.py --workload {args.workload} --fmt {args.fmt} --summarize-util <util csv>",
+             f"python3 bench.py --workload {args.workload} --fmt {args.fmt}{flags} --pmc-step",
+             f"python3 bench.py --workload {args.workload} --fmt {args.fmt}{flags} --summarize-util <util csv>",
              "```", "", f"Workload: {desc}.", "",
              "| M | K | N | kernel | " + " | ".join(UTIL_COUNTERS) + " |",
              "|---:|---:|---:|---|" + "---:|" * len(UTIL_COUNTERS)]
@@ -158,23 +172,23 @@ def summarize_util(args):
                      " | ".join(f"{d.get(c, float('nan')):.1f}" for c in UTIL_COUNTERS) + " |")
     mean = {c: round(sum(d.get(c, 0.0) for d in disp) / len(disp), 2) for c in UTIL_COUNTERS}
     lines += ["", "Mean over the dispatches: " + ", ".join(f"{c} {v}" for c, v in mean.items()) + ".", "",
-              "<!-- util-json: " + json.dumps({"workload": args.workload, "fmt": args.fmt,
+              "<!-- util-json: " + json.dumps({"workload": args.workload, "fmt": args.fmt, "variant": tag,
                                                 "src_hash": kernel_source_hash(), "mean": mean}) + " -->"]
-    out = util_path(args.workload, args.fmt)
+    out = util_path(args.workload, args.fmt, tag)
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(out)
 
 
-def util_path(workload, fmt):
-    return os.path.join(ROOT, "profiles", f"{workload}_{fmt}_utilization.md")
+def util_path(workload, fmt, tag=""):
+    return os.path.join(ROOT, "profiles", f"{workload}_{fmt}{tag}_utilization.md")
 
 
-def stored_util(workload, fmt):
+def stored_util(workload, fmt, tag=""):
     """Mean utilization counters of the dominant kernels from the committed
     summary, or None when there is none or the kernels changed since."""
     try:
-        with open(util_path(workload, fmt)) as fh:
+        with open(util_path(workload, fmt, tag)) as fh:
             for line in fh:
                 if line.startswith("<!-- util-json: "):
                     rec = json.loads(line[len("<!-- util-json: "):].rsplit(" -->", 1)[0])
@@ -225,30 +239,32 @@ def summarize_pmc(args):
     for (m, k, n), (fname, fv), (_, wv) in zip(configs, f_dom, w_dom):
         meas = (fv * f_fac + wv * w_fac) * 1024.0
         w_bytes = n * (k // 2 + k // bs)
-        alg = w_bytes + (2 * m * k if "linear" in fname else m * (k // 2 + k // bs)) + 2 * m * n
+        bf16_act = "linear" in fname or "w4a16" in fname   # the kernel reads bf16 activations
+        alg = w_bytes + (2 * m * k if bf16_act else m * (k // 2 + k // bs)) + 2 * m * n
         short = re.search(r"(k_[a-z_]+<[^>]*>)", fname)
         per.append({"m": m, "k": k, "n": n, "kernel": short.group(1) if short else fname, "fetch_kib": round(fv, 1),
                     "write_kib": round(wv, 1), "hbm_bytes": round(meas), "algorithmic_bytes": alg,
                     "ratio": round(meas / alg, 3)})
         tot_meas += meas
         tot_alg += alg
-    rec = {"workload": args.workload, "fmt": args.fmt, "src_hash": kernel_source_hash(),
+    tag, flags = variant_tag(args), variant_flags(args)
+    rec = {"workload": args.workload, "fmt": args.fmt, "variant": tag, "src_hash": kernel_source_hash(),
            "bytes_per_launch": round(tot_meas / len(configs)),
            "algorithmic_bytes_per_launch": round(tot_alg / len(configs)),
            "calibration": {"copy_mib": args.copy_mib, "fetch_kib": f_cal, "write_kib": w_cal,
                            "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)},
            "per_config": per}
-    out = traffic_path(args.workload, args.fmt)
-    lines = [f"# HBM traffic of the dominant kernels: {args.workload}, {args.fmt}", "",
+    out = traffic_path(args.workload, args.fmt, tag)
+    lines = [f"# HBM traffic of the dominant kernels: {args.workload}, {args.fmt}{tag.replace('_', ' ')}", "",
              "Per-dispatch hardware counters from two rocprofv3 passes over one eager step,",
              "scaled by what the same counters read for a plain copy kernel of known size.", "",
              "```",
              "cd /tmp && export TMPDIR=/tmp",
              f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/fetch -o fetch -- python3 bench.py "
-             f"--workload {args.workload} --fmt {args.fmt} --pmc-step --copy-mib {args.copy_mib}",
+             f"--workload {args.workload} --fmt {args.fmt}{flags} --pmc-step --copy-mib {args.copy_mib}",
              f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/write -o write -- python3 bench.py "
-             f"--workload {args.workload} --fmt {args.fmt} --pmc-step --copy-mib {args.copy_mib}",
-             f"python3 bench.py --workload {args.workload} --fmt {args.fmt} --copy-mib {args.copy_mib} "
+             f"--workload {args.workload} --fmt {args.fmt}{flags} --pmc-step --copy-mib {args.copy_mib}",
+             f"python3 bench.py --workload {args.workload} --fmt {args.fmt}{flags} --copy-mib {args.copy_mib} "
              "--summarize-pmc <fetch csv> <write csv>",
              "```", "",
              f"Calibration: a {args.copy_mib} MiB float32 negate read {f_cal:.0f} KiB (FETCH_SIZE) and "
@@ -480,11 +496,10 @@ def main():
         peak = FP4_PEAK_TFLOPS if fmt == 1 else F16_PEAK_TFLOPS
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": None}
-    # the counter summaries are taken for the W4A4 kernels without recipe flags
-    plain = not (args.recipe or args.w4a16)
-    roof["traffic"] = stored_traffic(args.workload, args.fmt) if plain else None
+    # HBM bytes per launch from the committed counter summary of this variant
+    roof["traffic"] = stored_traffic(args.workload, args.fmt, variant_tag(args))
     # rocprofv3 MfmaUtil / VALUBusy / LdsUtil (percent) of the same kernels
-    roof["counters_pct"] = stored_util(args.workload, args.fmt) if plain else None
+    roof["counters_pct"] = stored_util(args.workload, args.fmt, variant_tag(args))
     roof.update({"kernel": " + ".join(sorted(kern)), "avg_launch_us": round(tot_us / tot_launch, 3),
                  "launches_per_step": tot_launch,
                  "per_kernel": {nm: {"launches": d["launches"], "avg_us": round(d["us"] / d["launches"], 3),
