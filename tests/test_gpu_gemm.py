@@ -271,3 +271,36 @@ def test_linear_workspace_shared_across_shapes():
             wq = fp4.fp4_quantize_weight(to_dev(w), 0)
             y = bf16_out_to_f64(fp4.fp4_linear(to_dev(a), wq, workspace=ws))
             assert_gemm_close(y, c_ref, l_ref, f"shared workspace call {rep}/{i} {m}x{k}x{n}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m,n,k", [(1, 272, 640), (8, 520, 2880), (20, 8200, 512), (33, 100, 256)])
+def test_decode_canonical_wide_pitch(fmt, m, n, k):
+    """fp4_gemm on canonical activations whose rows are wider than they need
+    to be (codes pitch + 80 bytes, scales pitch + 24): the skinny kernels must
+    read only each row's own bytes, whatever lies between the rows."""
+    print(f"[gemm] canonical wide pitch fmt={fmt} m={m} n={n} k={k}", flush=True)
+    f = F[fmt]
+    a = synth.normal((m, k), 1.0, 7, m * 29 + k)
+    w = synth.normal((n, k), 0.02, 7, n * 13 + k)
+    qa_ref, qw_ref = oracle.quantize(f, a), oracle.quantize(f, w)
+    c_ref, l_ref = oracle.gemm(qa_ref, qw_ref)
+    wq = fp4.fp4_quantize_weight(to_dev(w), f)
+    qa = fp4.fp4_quantize_act(to_dev(a), f)
+    cp, sp = qa.desc.codes_pitch, qa.desc.scales_pitch
+    # copy the rows into wider buffers whose gaps hold bytes that would wreck
+    # the result if read (0xFF: NaN E8M0 scales, -6 codes)
+    codes = torch.full((m, cp + 80), 0xFF, dtype=torch.uint8, device=qa.codes.device)
+    scales = torch.full((m, sp + 24), 0xFF, dtype=torch.uint8, device=qa.codes.device)
+    codes[:, :cp] = qa.codes_2d()
+    scales[:, :sp] = qa.scales_2d()
+    wide = fp4.Fp4Tensor.__new__(fp4.Fp4Tensor)
+    wide.fmt, wide.layout, wide.rows, wide.k = qa.fmt, qa.layout, qa.rows, qa.k
+    wide.codes, wide.scales, wide.tensor_scale = codes, scales, qa.tensor_scale
+    wide.desc = fp4.fp4_tensor()
+    wide.desc.fmt, wide.desc.layout, wide.desc.rows, wide.desc.cols = qa.desc.fmt, qa.desc.layout, m, k
+    wide.desc.codes_pitch, wide.desc.scales_pitch = cp + 80, sp + 24
+    wide.desc.codes, wide.desc.scales = codes.data_ptr(), scales.data_ptr()
+    wide.desc.tensor_scale = qa.tensor_scale.data_ptr()
+    c = bf16_out_to_f64(fp4.fp4_gemm(wide, wq))
+    assert_gemm_close(c, c_ref, l_ref, "decode canonical wide pitch")
