@@ -13,6 +13,8 @@
 #include "../../include/fp4.h"
 #include "fp4_internal.h"
 
+#include <algorithm>
+
 using namespace fp4i;
 
 namespace {
@@ -285,6 +287,10 @@ fp4_status fp4_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c_bf16, int6
   if (ldc < w->rows) return fail(FP4_ERR_SHAPE, "ldc smaller than N");
   if (((uintptr_t)c_bf16 & 1u) != 0) return fail(FP4_ERR_ALIGNMENT, "output must be 2-byte aligned");
   if (a->rows > INT32_MAX || w->rows > INT32_MAX) return fail(FP4_ERR_SHAPE, "too many rows");
+  // the skinny kernels address canonical activation rows with 32-bit offsets
+  if (a->rows <= kDecodeMaxM && a->layout == FP4_LAYOUT_CANONICAL &&
+      a->rows * std::max(a->codes_pitch, a->scales_pitch) >= (int64_t(1) << 31))
+    return fail(FP4_ERR_SHAPE, "a: rows * pitch must stay below 2^31 bytes for M <= %d", kDecodeMaxM);
   if ((st = check_device()) != FP4_OK) return st;
   st = run_gemm(a, w, c_bf16, ldc, stream);
   return st == FP4_OK ? ok() : st;

@@ -168,6 +168,8 @@ size_t fp4_gemm_workspace_bytes(int32_t fmt, int64_t m, int64_t n, int64_t k);
  * with a^' = q * s_b (per-tensor factors pulled into alpha = S_tA * S_tW for
  * NVFP4, alpha = 1 for MXFP4). `a` is CANONICAL or TILED, `w` is TILED,
  * same format and K. Accumulation is FP32. `workspace` may be NULL.
+ * FP4_ERR_SHAPE when M <= 128 with CANONICAL `a` whose M * max(codes pitch,
+ * scales pitch) reaches 2^31 bytes (the skinny kernels use 32-bit offsets).
  */
 fp4_status fp4_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c_bf16, int64_t ldc,
                     void *workspace, size_t workspace_bytes, hipStream_t stream);

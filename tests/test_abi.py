@@ -110,6 +110,12 @@ def test_host_validation_rejects_before_launch():
     assert L.fp4_tensor_init(ctypes.byref(bad), fp4.NVFP4, fp4.CANONICAL, 4, 64, 4096, 8192, None) == 0
     assert L.fp4_gemm(ctypes.byref(bad), ctypes.byref(w), 4096, 32, None, 0, None) == 1
     assert b"tensor_scale" in L.fp4_last_error()
+    # skinny path: canonical activation rows addressed past 2^31 bytes
+    wide = fp4.fp4_tensor()
+    assert L.fp4_tensor_init(ctypes.byref(wide), fp4.NVFP4, fp4.CANONICAL, 4, 64, 4096, 8192, 64) == 0
+    wide.codes_pitch = 1 << 29
+    assert L.fp4_gemm(ctypes.byref(wide), ctypes.byref(w), 4096, 32, None, 0, None) == 2
+    assert b"2^31" in L.fp4_last_error()
 
 
 def test_linear_launch_count():
