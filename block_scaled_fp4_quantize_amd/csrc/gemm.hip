@@ -152,21 +152,20 @@ __global__ __launch_bounds__(256) void k_gemm_prefill(
 // ------------------------------------------------------------------- decode
 //
 // Skinny GEMM for M <= 128: the weight is streamed once at HBM rate. One
-// workgroup per 16-row weight tile covers the whole K range, so there is no
-// cross-workgroup reduction: every workgroup is resident at once and HBM
+// workgroup per NT 16-row weight tiles covers the whole K range, so there is
+// no cross-workgroup reduction: every workgroup is resident at once and HBM
 // bandwidth is shared among them. The kDecWaves waves take interleaved
-// fragments (kt = wave + kDecWaves * j) in groups of FM; the next group's loads
-// are issued before the current group's arithmetic, whose wait then covers
-// both groups (the fragment guards put loads under branches, and the compiler
-// merges their wait counts), so a wave drains its loads every group. MXFP4
-// uses this kernel: for its one-instruction fragments it measured faster than
-// every deeper pipeline tried (the ring kernel below). The weight tile is the
-// MFMA's A operand (rows n) and the
-// activations its B operand (columns m, MG groups of 16: 1, 2, 4 or 8), so
-// the accumulator holds C^T. The waves' partial sums are added in LDS in a
-// fixed order. Up to M = 128 this beats the tiled kernels, whose few output
-// tiles (M / 128 rows of them) leave most CUs idle; every workgroup reads the
-// (small, L2-resident) activations once.
+// fragments (kt = wave + kDecWaves * j) in groups of FM; the next group's
+// loads are issued before the current group's arithmetic, whose wait then
+// covers both groups (the fragment guards put loads under branches, and the
+// compiler merges their wait counts), so a wave drains its loads every group.
+// MXFP4 uses this kernel: for its one-instruction fragments it measured faster
+// than every deeper pipeline tried (the ring kernel below). The weight tile is
+// the MFMA's A operand (rows n) and the activations its B operand (columns m,
+// MG groups of 16: 1, 2, 4 or 8), so the accumulator holds C^T. The waves'
+// partial sums are added in LDS in a fixed order. Up to M = 128 this beats the
+// tiled kernels, whose few output tiles (M / 128 rows of them) leave most CUs
+// idle; every workgroup reads the (small, L2-resident) activations once.
 constexpr int kDecWaves = 8;
 constexpr int kDecFrags = 2;
 
