@@ -304,3 +304,33 @@ def test_decode_canonical_wide_pitch(fmt, m, n, k):
     wide.desc.tensor_scale = qa.tensor_scale.data_ptr()
     c = bf16_out_to_f64(fp4.fp4_gemm(wide, wq))
     assert_gemm_close(c, c_ref, l_ref, "decode canonical wide pitch")
+
+
+@pytest.mark.parametrize("fmt,m,n,k", [("nvfp4", 1, 16, 16), ("nvfp4", 3, 40, 48), ("mxfp4", 1, 16, 32),
+                                       ("mxfp4", 5, 48, 96), ("nvfp4", 17, 33, 16), ("mxfp4", 33, 20, 32)])
+def test_one_block_deep(fmt, m, n, k):
+    """K of one or a few blocks (a single, mostly padded fragment along K)."""
+    a = synth.normal((m, k), 1.0, 13, m * 7 + k)
+    w = synth.normal((n, k), 0.02, 13, n * 5 + k)
+    _gemm_case(fmt, a, w, "one-block K")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m,k,n", [(1, 5120, 272), (8, 2880, 520), (32, 1024, 1040), (200, 512, 300)])
+def test_zero_activations_give_zero_output(fmt, m, k, n):
+    """All-zero activations: every block scale is zero (NVFP4 takes S_t = 1),
+    every code +0, and every output a zero, on each linear path."""
+    print(f"[gemm] zero activations fmt={fmt} m={m} k={k} n={n}", flush=True)
+    f = F[fmt]
+    w = synth.normal((n, k), 0.02, 14, n + k)
+    wq = fp4.fp4_quantize_weight(to_dev(w), f)
+    x = torch.zeros(m, k, dtype=torch.bfloat16, device="cuda")
+    y = fp4.fp4_linear(x, wq)
+    qa = fp4.fp4_quantize_act(x, f)
+    c = fp4.fp4_gemm(qa, wq)
+    torch.cuda.synchronize()
+    for out, what in ((y, "linear"), (c, "gemm")):
+        bits = out.view(torch.int16).cpu().numpy()
+        assert ((bits & 0x7FFF) == 0).all(), f"{what}: nonzero output for zero activations"
+    assert (qa.codes_2d().cpu().numpy()[:, : k // 2] == 0).all()
+    assert (qa.scales_2d().cpu().numpy()[:, : k // oracle.BLOCK[f]] == 0).all()
