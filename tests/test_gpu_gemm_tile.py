@@ -161,6 +161,13 @@ def test_prefill_full_size_sampled(fmt, layer):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+def test_square_4096_sampled(fmt):
+    """M = N = K = 4096 (the smallest square configuration), operands ~N(0, 1)."""
+    a, w = synth.square_inputs(4096, seed=0)
+    _sampled_full(fmt, a, w, "square 4096")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_square_8192_sampled(fmt):
     """M = N = K = 8192, operands ~N(0, 1)."""
     a, w = synth.square_inputs(8192, seed=0)
