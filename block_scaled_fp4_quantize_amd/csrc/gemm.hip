@@ -268,8 +268,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(
 
 // ------------------------------------------------------------ decode, ring
 //
-// The same skinny GEMM (one workgroup per 16-row weight tile, kRingWaves waves
-// over K, partial sums added in LDS in a fixed order) with its operands read
+// The same skinny GEMM (one workgroup per one or two 16-row weight tiles, its
+// waves split over K, partial sums added in LDS in a fixed order) with its operands read
 // through a ring of kRingDepth register slots per wave: slot d is consumed and
 // at once refilled with the fragment kRingDepth steps ahead. Every operand is
 // read with a buffer load whose resource ends at the operand's last valid
@@ -303,12 +303,12 @@ __device__ __forceinline__ uint32_t buf_load_scale(__amdgpu_buffer_rsrc_t r, uin
 // The operand pointers are not declared __restrict__: the compiler would then
 // take the buffer loads as invariant and move them across the ordering
 // statements below.
-template <int FMT, int MG, int ATILED, int NT>
-__global__ __launch_bounds__(64 * kRingWaves) void k_gemm_decode_ring(
+template <int FMT, int MG, int ATILED, int NT, int NWT>
+__global__ __launch_bounds__(64 * NWT) void k_gemm_decode_ring(
     const uint8_t *a_codes, int64_t a_cp, const uint8_t *a_sc, int64_t a_sp,
     const float *__restrict__ a_ts, const uint8_t *w_codes, const uint8_t *w_sc,
     const float *__restrict__ w_ts, int m, int n, int kt_n, int nt_n, uint16_t *c, int64_t ldc) {
-  constexpr int NW = kRingWaves, D = kRingDepth;
+  constexpr int NW = NWT, D = kRingDepth;
   constexpr int SFB = FMT == 0 ? 128 : 64;  // scale bytes per fragment
   __shared__ float red[NW][NT * MG][4][64];
   const int nt0 = blockIdx.x * NT;  // first of this workgroup's NT weight tiles
@@ -599,21 +599,29 @@ hipError_t launch_gemm_decode(const GemmArgs &g, hipStream_t stream) {
                                       : g.m * std::max(g.a_cpitch, g.a_spitch) + (int64_t)kt_n * 64;
     if (a_bytes >= (int64_t(1) << 31) || (int64_t)kt_n * kFragCodeBytes >= (int64_t(1) << 30))
       return hipErrorInvalidValue;
-    // 17-32 activation rows: two weight tiles per workgroup when that still
-    // leaves >= 256 workgroups (measured at M = 32, N = 17408: 20.4 -> 18.4 us;
-    // with 1-16 rows the second tile measured slower)
-    const bool two = mg == 2 && nt_n >= 512;
+    // Two weight tiles per workgroup, so that the activations are loaded and
+    // dequantized once per two tiles:
+    //  - 1-16 activation rows, 256-511 tiles: 16 waves per workgroup keep the
+    //    waves per CU of one tile per 8-wave workgroup (decode shapes with
+    //    N = 5120: 7.0 -> 6.5 us at K = 5120, 17.7 -> 14.9 us at K = 17408);
+    //    with >= 512 tiles the second tile measured slower at 8 and 16 waves;
+    //  - 17-32 activation rows, >= 256 tiles (N = 5120, M = 32: 9.0 -> 7.5 us
+    //    at K = 5120, 23.9 -> 18.3 us at K = 17408; N = 17408: 20.4 -> 18.4 us).
+    const bool two1 = mg == 1 && nt_n >= 256 && nt_n < 512;
+    const bool two2 = mg == 2 && nt_n >= 256;
+    const bool two = two1 || two2;
     dim3 grid((unsigned)(two ? (nt_n + 1) / 2 : nt_n));
-#define FP4_RING1(G, T, P)                                                                          \
-  hipLaunchKernelGGL((k_gemm_decode_ring<0, G, T, P>), grid, dim3(64 * kRingWaves), 0, stream, \
-                     g.a_codes, g.a_cpitch, g.a_scales, g.a_spitch, g.a_ts, g.w_codes,         \
+#define FP4_RING1(G, T, P, W)                                                                   \
+  hipLaunchKernelGGL((k_gemm_decode_ring<0, G, T, P, W>), grid, dim3(64 * W), 0, stream,    \
+                     g.a_codes, g.a_cpitch, g.a_scales, g.a_spitch, g.a_ts, g.w_codes,      \
                      g.w_scales, g.w_ts, (int)g.m, (int)g.n, kt_n, nt_n, g.c, g.ldc)
-#define FP4_RING_T(G, P) do { if (g.a_tiled) FP4_RING1(G, 1, P); else FP4_RING1(G, 0, P); } while (0)
-    if (mg == 1) FP4_RING_T(1, 1);
-    else if (mg == 2 && two) FP4_RING_T(2, 2);
-    else if (mg == 2) FP4_RING_T(2, 1);
-    else if (mg == 4) FP4_RING_T(4, 1);
-    else FP4_RING_T(8, 1);
+#define FP4_RING_T(G, P, W) do { if (g.a_tiled) FP4_RING1(G, 1, P, W); else FP4_RING1(G, 0, P, W); } while (0)
+    if (two1) FP4_RING_T(1, 2, 2 * kRingWaves);
+    else if (mg == 1) FP4_RING_T(1, 1, kRingWaves);
+    else if (two2) FP4_RING_T(2, 2, kRingWaves);
+    else if (mg == 2) FP4_RING_T(2, 1, kRingWaves);
+    else if (mg == 4) FP4_RING_T(4, 1, kRingWaves);
+    else FP4_RING_T(8, 1, kRingWaves);
 #undef FP4_RING_T
 #undef FP4_RING1
     return hipGetLastError();
@@ -621,6 +629,8 @@ hipError_t launch_gemm_decode(const GemmArgs &g, hipStream_t stream) {
   // MXFP4 with 17-32 activation rows: two weight tiles per workgroup when
   // that still leaves >= 256 workgroups, so the activations are read once per
   // two tiles (measured: 17.7 -> 15.8 us at M = 32, N = 17408).
+  // (at 256-511 tiles it measured mixed: M = 32, N = 5120: 5.7 -> 5.9 us at
+  // K = 5120, 18.3 -> 17.4 us at K = 17408)
   const int nt_per = (mg == 2 && nt_n >= 512) ? 2 : 1;
   dim3 grid((unsigned)((nt_n + nt_per - 1) / nt_per));
 #define FP4_DEC(F, G, T, P)                                                                     \

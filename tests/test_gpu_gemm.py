@@ -45,7 +45,11 @@ def test_single_gemm_config(fmt):
                                    (48, 300, 1024), (64, 1040, 2880), (65, 100, 512),
                                    (100, 520, 4160), (128, 257, 640), (128, 48, 17408),
                                    # two weight tiles per workgroup (>= 512 tiles), odd count
-                                   (5, 8200, 256), (20, 8200, 512), (32, 8192, 128)])
+                                   (5, 8200, 256), (20, 8200, 512), (32, 8192, 128),
+                                   # two tiles per workgroup at 256-511 tiles: odd and ragged
+                                   # tile counts, fewer K fragments than waves
+                                   (3, 4112, 640), (16, 4100, 2880), (1, 8176, 128),
+                                   (24, 4112, 640), (17, 4100, 5120), (32, 4096, 96)])
 def test_decode_path(fmt, m, n, k):
     a = synth.normal((m, k), 1.0, 3, m * 31 + k)
     w = synth.normal((n, k), 0.02, 3, n * 17 + k)
@@ -274,7 +278,8 @@ def test_linear_workspace_shared_across_shapes():
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("m,n,k", [(1, 272, 640), (8, 520, 2880), (20, 8200, 512), (33, 100, 256)])
+@pytest.mark.parametrize("m,n,k", [(1, 272, 640), (8, 520, 2880), (20, 8200, 512), (33, 100, 256),
+                                   (4, 4112, 640), (30, 4100, 512)])
 def test_decode_canonical_wide_pitch(fmt, m, n, k):
     """fp4_gemm on canonical activations whose rows are wider than they need
     to be (codes pitch + 80 bytes, scales pitch + 24): the skinny kernels must
