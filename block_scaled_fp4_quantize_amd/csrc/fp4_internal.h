@@ -82,6 +82,7 @@ hipError_t launch_gemm_tile(const GemmArgs &g, int cfg, hipStream_t stream);
 constexpr int kFusedMaxM = 16;
 constexpr int64_t kFusedMaxMK = 65536;        // M * K_pad bound (LDS staging, MXFP4)
 constexpr int64_t kFusedMaxWork = 16 << 20;   // M * K_pad * N tiles bound
+constexpr int64_t kFusedMaxWorkNv = 4 << 20;  // NVFP4: M * K_pad * N tiles bound
 constexpr int64_t kFusedMaxTilesNv = 512;      // NVFP4: at most this many weight tiles
 bool linear_fused_ok(int fmt, int64_t m, int64_t n, int64_t k);
 hipError_t launch_linear_fused(int fmt, uint32_t recipe, const uint16_t *x, int64_t m, int64_t k,

@@ -653,10 +653,16 @@ bool linear_fused_ok(int fmt, int64_t m, int64_t n, int64_t k) {
   // LDS staging bound, and a bound on the redundant quantization work that
   // every weight tile's workgroup repeats.
   // NVFP4's encoding prologue (maximum pass + exact encode) is long enough
-  // that only about two workgroups per CU (512 weight tiles) should repeat it.
+  // that only about two workgroups per CU (512 weight tiles) should repeat it,
+  // and the separate quantizer plus the skinny GEMM wins once M * K_pad * tiles
+  // passes about 4M (320 tiles, measured: K = 5120 fused at M = 2, 11.9 us
+  // against 13.5; separate at M = 4, 13.4 us against 15.5, and at M = 1 with
+  // K = 17408, 22.4 us against 23.0).
   const int64_t nt = round_up(n, 16) / 16;
-  return m <= kFusedMaxM && mk <= (fmt == 0 ? kFusedMaxMK / 2 : kFusedMaxMK) &&
-         mk * nt <= kFusedMaxWork && (fmt != 0 || nt <= kFusedMaxTilesNv);
+  if (fmt == 0)
+    return m <= kFusedMaxM && mk <= kFusedMaxMK / 2 && mk * nt <= kFusedMaxWorkNv &&
+           nt <= kFusedMaxTilesNv;
+  return m <= kFusedMaxM && mk <= kFusedMaxMK && mk * nt <= kFusedMaxWork;
 }
 
 hipError_t launch_linear_fused(int fmt, uint32_t recipe, const uint16_t *x, int64_t m, int64_t k,
