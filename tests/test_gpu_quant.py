@@ -74,9 +74,18 @@ def test_nvfp4_ties_and_midpoints():
         mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0]) * s
         blk = np.concatenate([[6 * s], rng.choice(mids, 15) * rng.choice([-1, 1], 15)])
         rows.append(blk)
-    x = synth.bf16_bits(np.array(rows, np.float32).reshape(16, 256))
+    xf = np.array(rows, np.float32).reshape(16, 256)
+    x = synth.bf16_bits(xf)
     _act_case("nvfp4", x, "midpoints, dynamic")
     _act_case("nvfp4", x, "midpoints, static 1/448", static=float(np.float32(1 / 448)))
+    # power-of-two S_t: block scales come out exact (s_b = s, or 2s up to the
+    # 448 saturation) and quotients land exactly on the midpoints (ties)
+    _act_case("nvfp4", x, "midpoints, static 1 (exact ties)", static=1.0)
+    _act_case("nvfp4", x, "midpoints, static 1/2 (exact ties)", static=0.5)
+    # dynamic with an exact S_t: amax = 42 = 2688 * 2^-6 gives S_t = 2^-6
+    xd = xf * np.float32(2.0 ** -6)
+    xd[0, 0] = 42.0
+    _act_case("nvfp4", synth.bf16_bits(xd), "midpoints, dynamic S_t = 2^-6 (exact ties)")
 
 
 def test_prefill_planted_outliers_two_level():
