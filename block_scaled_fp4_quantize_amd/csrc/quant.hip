@@ -274,11 +274,40 @@ __device__ __forceinline__ uint32_t grid_max_u32(uint32_t wg_max, uint32_t tag,
   return block_max_u32(v & 0xFFFFu, lds);
 }
 
+// Largest magnitude (bf16 bits) of the whole tensor, taken by one workgroup
+// alone: its threads read every block (rotated first when the recipe says
+// so) and the workgroup takes the maximum. Four blocks per thread are loaded
+// before any is used; past the end the last block is read again, which the
+// maximum does not mind.
+template <int FMT>
+__device__ __forceinline__ uint32_t tensor_absmax_wg(const uint16_t *x, int64_t nblk,
+                                                     uint32_t recipe, uint32_t *lds) {
+  using K = Blk<FMT>;
+  uint32_t m = 0;
+  for (int64_t t = threadIdx.x; t < nblk; t += 4 * (int64_t)blockDim.x) {
+    uint4 u[4][K::V];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t b = min(t + j * (int64_t)blockDim.x, nblk - 1);
+      const uint4 *src = (const uint4 *)(x + b * K::B);
+#pragma unroll
+      for (int i = 0; i < K::V; ++i) u[j][i] = src[i];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      maybe_rotate<FMT>(u[j], recipe);
+      m = max(m, block_absmax<FMT>(u[j]));
+    }
+  }
+  return block_max_u32(m, lds);
+}
+
 // Single-launch quantization of a tensor of at most kActGrid * 256 * kActBpt
 // blocks. Every thread loads its (at most BPT) blocks first, so the values are
-// in registers while the maximum is exchanged; the dynamic-scale form runs as
-// few workgroups as hold the tensor, so that small tensors need little or no
-// exchange.
+// in registers while the maximum is found. The dynamic-scale form runs as few
+// workgroups as hold the tensor; with DYN = 1 they exchange their maxima,
+// with DYN = 2 (small tensors) each workgroup reads the whole tensor and
+// takes the maximum itself, with no exchange.
 template <int FMT, int TILED, int DYN, int BPT>
 __global__ __launch_bounds__(kThreads) void k_quant_small(
     const uint16_t *__restrict__ x, int64_t rows, int64_t k, int64_t rows_pad, int64_t kt_n,
@@ -291,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_small(
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   uint32_t tag = 0;
-  if (DYN)  // this call's tag: one more than the previous call's (any slot)
+  if (DYN == 1)  // this call's tag: one more than the previous call's (any slot)
     tag = ((__hip_atomic_load(&sync[blockIdx.x * kSlotStride], __ATOMIC_RELAXED,
                               __HIP_MEMORY_SCOPE_AGENT) >> 16) + 1u) & 0xFFFFu;
   uint4 v[BPT][K::V];
@@ -313,7 +342,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_small(
   }
   float st = 1.0f;
   if (FMT == 0) {
-    if (DYN) st = tensor_scale_from_amax(bf16_bits_to_f32(grid_max_u32(block_max_u32(m, lds), tag, sync, lds)));
+    if (DYN == 1)
+      st = tensor_scale_from_amax(bf16_bits_to_f32(grid_max_u32(block_max_u32(m, lds), tag, sync, lds)));
+    else if (DYN == 2)
+      st = tensor_scale_from_amax(bf16_bits_to_f32(tensor_absmax_wg<FMT>(x, rows * nb, recipe, lds)));
     else st = *static_scale;
     if (blockIdx.x == 0 && threadIdx.x == 0 && ts_out) *ts_out = st;
   }
@@ -401,13 +433,18 @@ void launch_small(const uint16_t *x, int64_t rows, int64_t k, int64_t rows_pad, 
     // encode steps of the unused ones still cost time (1 instead of 4 blocks
     // per thread: 0.4-0.6 us per call on the decode shapes)
     const int grid = (int)(per_wg < kActGrid ? per_wg : kActGrid);
-#define FP4_QS(BPT)                                                                            \
-  hipLaunchKernelGGL((k_quant_small<FMT, TILED, 1, BPT>), dim3(grid), dim3(kThreads), 0, stream, \
+#define FP4_QS(D, BPT)                                                                         \
+  hipLaunchKernelGGL((k_quant_small<FMT, TILED, D, BPT>), dim3(grid), dim3(kThreads), 0, stream, \
                      x, rows, k, rows_pad, kt_n, static_scale, codes, cpitch, scales, spitch,   \
                      ts_out, sync, recipe)
-    if (per_wg <= kActGrid) FP4_QS(1);
-    else if (per_wg <= 2 * kActGrid) FP4_QS(2);
-    else FP4_QS(kActBpt);
+    // Small tensors: every workgroup reads the whole tensor for its maximum
+    // rather than exchanging it (measured per call: M = 1, K = 5120: 4.9 ->
+    // 3.9 us; M = 8, K = 5120: 5.15 -> 4.8 us; at M * K = 139264 it lost,
+    // 5.2 -> 6.9 us, as each workgroup's reads grow).
+    if (rows * k <= kActRedundantMaxValues && per_wg <= kActGrid) FP4_QS(2, 1);
+    else if (per_wg <= kActGrid) FP4_QS(1, 1);
+    else if (per_wg <= 2 * kActGrid) FP4_QS(1, 2);
+    else FP4_QS(1, kActBpt);
 #undef FP4_QS
   } else {
     hipLaunchKernelGGL((k_quant_small<FMT, TILED, 0, 1>), dim3((unsigned)per_wg), dim3(kThreads), 0,

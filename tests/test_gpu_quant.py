@@ -31,7 +31,10 @@ def test_single_gemm_activation(fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("m,k", [(1, 32), (3, 96), (17, 2880), (40, 5120), (129, 544), (1, 17408)])
+@pytest.mark.parametrize("m,k", [(1, 32), (3, 96), (17, 2880), (40, 5120), (129, 544), (1, 17408),
+                                 # NVFP4 dynamic: the largest M * K whose workgroups each take
+                                 # the whole tensor's maximum, and the next size up
+                                 (8, 6144), (8, 6176)])
 def test_ragged_shapes(fmt, m, k):
     bits = synth.normal((m, k), 1.0, 1, m * 100003 + k)
     _act_case(fmt, bits, f"ragged {m}x{k}")
