@@ -20,7 +20,7 @@ inline int block_of(int fmt) { return fmt == 0 ? 16 : 32; }
 inline int frag_scale_bytes(int fmt) { return fmt == 0 ? 128 : 64; }
 
 constexpr int kActGrid = 128;         // workgroups of the single-launch quantizer
-constexpr int kActBpt = 4;            // blocks per thread in the single-launch quantizer
+constexpr int kActBpt = 4;            // single-launch quantizer capacity: kActGrid * 256 * kActBpt blocks
 constexpr int64_t kActRedundantMaxValues = 49152;  // M * K up to which each workgroup finds the maximum alone
 // Quantize scratch: kMaxAmaxParts partial maxima, then the single-launch
 // quantizer's kActGrid tagged maximum words, one per 128-byte line

@@ -303,19 +303,19 @@ __device__ __forceinline__ uint32_t tensor_absmax_wg(const uint16_t *x, int64_t 
 }
 
 // Single-launch quantization of a tensor of at most kActGrid * 256 * kActBpt
-// blocks. Every thread loads its (at most BPT) blocks first, so the values are
+// (= kActGrid * 512 * 2) blocks. Every thread loads its (at most BPT) blocks first, so the values are
 // in registers while the maximum is found. The dynamic-scale form runs as few
 // workgroups as hold the tensor; with DYN = 1 they exchange their maxima,
 // with DYN = 2 (small tensors) each workgroup reads the whole tensor and
 // takes the maximum itself, with no exchange.
-template <int FMT, int TILED, int DYN, int BPT>
-__global__ __launch_bounds__(kThreads) void k_quant_small(
+template <int FMT, int TILED, int DYN, int BPT, int NTH = kThreads>
+__global__ __launch_bounds__(NTH) void k_quant_small(
     const uint16_t *__restrict__ x, int64_t rows, int64_t k, int64_t rows_pad, int64_t kt_n,
     const float *__restrict__ static_scale, uint8_t *__restrict__ codes, int64_t cpitch,
     uint8_t *__restrict__ scales, int64_t spitch, float *__restrict__ ts_out,
     uint32_t *__restrict__ sync, uint32_t recipe) {
   using K = Blk<FMT>;
-  __shared__ uint32_t lds[4];
+  __shared__ uint32_t lds[NTH / 64];
   const int64_t nb = k / K::B, nb_pad = kt_n * K::BPF, total = rows_pad * nb_pad;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -424,27 +424,34 @@ void launch_small(const uint16_t *x, int64_t rows, int64_t k, int64_t rows_pad, 
   // One block per thread where the grid allows: encoding is the costly part
   // and spreads over as many CUs as there are blocks. The dynamic-scale form
   // also exchanges its maximum among the workgroups, so it stops at kActGrid
-  // workgroups (up to kActBpt blocks per thread); fewer workgroups also means
-  // fewer polls of the exchange words.
+  // workgroups (of up to 512 threads with two blocks each); fewer workgroups
+  // also means fewer polls of the exchange words.
   const int64_t total = rows_pad * kt_n * Blk<FMT>::BPF;
   const int64_t per_wg = (total + kThreads - 1) / kThreads;
   if (FMT == 0 && !static_scale) {
     // as few blocks per thread as the grid allows: the unrolled load and
-    // encode steps of the unused ones still cost time (1 instead of 4 blocks
-    // per thread: 0.4-0.6 us per call on the decode shapes)
-    const int grid = (int)(per_wg < kActGrid ? per_wg : kActGrid);
-#define FP4_QS(D, BPT)                                                                         \
-  hipLaunchKernelGGL((k_quant_small<FMT, TILED, D, BPT>), dim3(grid), dim3(kThreads), 0, stream, \
-                     x, rows, k, rows_pad, kt_n, static_scale, codes, cpitch, scales, spitch,   \
+    // encode steps of unused ones still cost time (1 instead of 4 blocks per
+    // thread: 0.4-0.6 us per call on the decode shapes)
+    int grid = (int)(per_wg < kActGrid ? per_wg : kActGrid);
+#define FP4_QS(D, BPT, NTH)                                                                     \
+  hipLaunchKernelGGL((k_quant_small<FMT, TILED, D, BPT, NTH>), dim3(grid), dim3(NTH), 0, stream, \
+                     x, rows, k, rows_pad, kt_n, static_scale, codes, cpitch, scales, spitch,    \
                      ts_out, sync, recipe)
     // Small tensors: every workgroup reads the whole tensor for its maximum
     // rather than exchanging it (measured per call: M = 1, K = 5120: 4.9 ->
     // 3.9 us; M = 8, K = 5120: 5.15 -> 4.8 us; at M * K = 139264 it lost,
     // 5.2 -> 6.9 us, as each workgroup's reads grow).
-    if (rows * k <= kActRedundantMaxValues && per_wg <= kActGrid) FP4_QS(2, 1);
-    else if (per_wg <= kActGrid) FP4_QS(1, 1);
-    else if (per_wg <= 2 * kActGrid) FP4_QS(1, 2);
-    else FP4_QS(1, kActBpt);
+    if (rows * k <= kActRedundantMaxValues && per_wg <= kActGrid) FP4_QS(2, 1, kThreads);
+    else if (per_wg <= kActGrid) FP4_QS(1, 1, kThreads);
+    else {
+      // past 256 blocks per workgroup, 512-thread workgroups before two
+      // blocks per thread (M = 32, K = 17408: 6.3 -> 5.85 us; with fewer
+      // blocks the larger workgroups measured 0.5 us slower)
+      const int64_t per_wg2 = (total + 2 * kThreads - 1) / (2 * kThreads);
+      grid = (int)(per_wg2 < kActGrid ? per_wg2 : kActGrid);
+      if (per_wg2 <= kActGrid) FP4_QS(1, 1, 2 * kThreads);
+      else FP4_QS(1, 2, 2 * kThreads);
+    }
 #undef FP4_QS
   } else {
     hipLaunchKernelGGL((k_quant_small<FMT, TILED, 0, 1>), dim3((unsigned)per_wg), dim3(kThreads), 0,
