@@ -257,6 +257,18 @@ def test_forward_layer_sampled(fmt, m):
         assert_gemm_close(y[rows, cols], c_ref, l_ref, f"forward {name} m={m}")
 
 
+@pytest.mark.parametrize("m,k,n,launches", [(2, 5120, 5120, 1), (3, 5120, 5120, 2),
+                                            (1, 16384, 4096, 1), (1, 16384, 4112, 2)])
+def test_nvfp4_fused_bound(m, k, n, launches):
+    """NVFP4 fp4_linear on both sides of the fused path's M * K_pad * tiles
+    bound (4M): the fused single launch and quantize + GEMM agree with the
+    oracle alike."""
+    assert fp4.fp4_linear_launches("nvfp4", m, n, k) == launches
+    a = synth.normal((m, k), 1.0, 11, m * 7 + k)
+    w = synth.normal((n, k), 0.02, 11, n * 5 + k)
+    _gemm_case("nvfp4", a, w, f"fused bound ({launches} launch(es))")
+
+
 def test_linear_workspace_shared_across_shapes():
     """One zero-filled workspace, sized for the largest call, serves NVFP4
     dynamic-scale linears of different K, M and paths in sequence (the
