@@ -346,11 +346,15 @@ def test_bits_per_value():
 
 # --------------------------------------------- brute force on tiny tensors
 
-def _brute_nvfp4(xbits):
-    """Whole NVFP4 dynamic quantization by exact rational search (tiny inputs)."""
+def _brute_nvfp4(xbits, static_scale=None):
+    """Whole NVFP4 quantization by exact rational search (tiny inputs): the
+    dynamic tensor scale, or a given one (static), block scales saturating."""
     vals = [Fraction(float(v)) for v in bf16_to_f32(xbits).reshape(-1)]
     g = max(abs(v) for v in vals)
-    st = Fraction(float(_fp32_round_exact(g / 2688))) if g > 0 else Fraction(1)
+    if static_scale is not None:
+        st = Fraction(float(np.float32(static_scale)))
+    else:
+        st = Fraction(float(_fp32_round_exact(g / 2688))) if g > 0 else Fraction(1)
     r, k = xbits.shape
     finite = [(b, Fraction(float(E4M3_TABLE[b]))) for b in range(0x7F)]
     codes, scales = np.zeros((r, k), np.uint8), np.zeros((r, k // 16), np.uint8)
@@ -384,6 +388,76 @@ def test_nvfp4_tiny_brute_force(seed):
     assert q.tensor_scale == st
     assert np.array_equal(q.scales, scales)
     assert np.array_equal(unpack(q.codes), codes)
+
+
+# Static (caller-given) tensor scale: the hardware recipe's per-tensor scale
+# with saturating block scales ("Hardware FP4 inference for speech on
+# Blackwell", section "NVFP4, and the two ways it fails", overflow paragraph).
+STATIC_SCALES = [2.0 ** -100, float(np.float32(1e-30)), 1.0, 3.5]
+
+
+@pytest.mark.parametrize("st", STATIC_SCALES)
+def test_nvfp4_static_brute_force(st):
+    """Static S_t: codes and scales equal an exact rational search at that S_t,
+    S_t is returned unchanged, and blocks past 6 * 448 * S_t saturate."""
+    rng = np.random.default_rng(int(st * 1e6) % 1000 + 7)
+    # magnitudes around S_t: tiny (scale underflows), ordinary, and up to ~30x
+    # past the 2688 * S_t overflow point; one block per row is forced past it
+    x = rng.standard_normal((3, 64)) * st * 2.0 ** rng.uniform(-12, 13, (3, 64))
+    x[:, 16] = np.float32(st) * 6000.0 * np.array([1.0, -1.0, 1.0])
+    xb = bf16_bits(x.astype(np.float32))
+    q = oracle.quantize_nvfp4(xb, oracle.STATIC, static_scale=st)
+    codes, scales, _ = _brute_nvfp4(xb, static_scale=st)
+    assert q.tensor_scale == np.float32(st)
+    assert np.array_equal(q.scales, scales)
+    assert np.array_equal(unpack(q.codes), codes)
+    # the overflowing blocks: scale 448 and the block maximum clipped to +-6 * d_b
+    assert np.all(q.scales[:, 1] == 0x7E)
+    nib = unpack(q.codes)[:, 16]
+    assert np.all(nib & 7 == 7)
+
+
+def test_nvfp4_static_quotient_464_tie_and_clip():
+    """a_b / (6 S_t) exactly 464 is the tie between 448 and the next grid point
+    past the E4M3 range: it rounds to 448 (0x7E), and the element at 2784 * S_t
+    is clipped to 6 * 448 * S_t; just below and above the 448 boundary."""
+    for st in (1.0, 0.5, 2.0 ** -20):
+        a_b = 2784.0 * st                      # 7 significant bits: exact in bf16
+        row = np.zeros((1, 16), np.float32)
+        row[0, 0], row[0, 1], row[0, 2] = a_b, -a_b / 2, a_b / 3
+        xb = bf16_bits(row)
+        assert float(bf16_to_f32(xb)[0, 0]) == a_b
+        q = oracle.quantize_nvfp4(xb, oracle.STATIC, static_scale=st)
+        assert q.scales[0, 0] == 0x7E
+        assert unpack(q.codes)[0, 0] == 7
+        xhat = oracle.dequantize(q)
+        assert xhat[0, 0] == 6 * 448 * st      # clipped, not 2784 * S_t
+        codes, scales, _ = _brute_nvfp4(xb, static_scale=st)
+        assert np.array_equal(q.scales, scales) and np.array_equal(unpack(q.codes), codes)
+    # E4M3 spacing is 32 in [256, 448]: quotient 440 -> 448 and 424 -> 416
+    # (nearest); 432 is the tie of 416 (odd mantissa) and 448 -> 448; 400 the
+    # tie of 384 (even) and 416 -> 384; 416 exactly -> 416
+    for a_b, want in ((2640.0, 0x7E), (2544.0, 0x7D), (2592.0, 0x7E), (2400.0, 0x7C),
+                      (2496.0, 0x7D)):
+        row = np.zeros((1, 16), np.float32)
+        row[0, 5] = a_b
+        q = oracle.quantize_nvfp4(bf16_bits(row), oracle.STATIC, static_scale=1.0)
+        assert q.scales[0, 0] == want, (a_b, hex(int(q.scales[0, 0])))
+
+
+def test_nvfp4_static_at_dynamic_scale_reproduces_dynamic():
+    """Given the tensor's own dynamic S_t, static quantization is the dynamic one."""
+    rng = np.random.default_rng(5)
+    x = bf16_bits((rng.standard_t(3, (9, 160)) * 40.0).astype(np.float32))
+    qd = oracle.quantize_nvfp4(x)
+    qs = oracle.quantize_nvfp4(x, oracle.STATIC, static_scale=float(qd.tensor_scale))
+    assert qs.tensor_scale == qd.tensor_scale
+    assert np.array_equal(qs.codes, qd.codes) and np.array_equal(qs.scales, qd.scales)
+    # a different S_t gives different scales: the static path does not take S_t
+    # from the tensor
+    qh = oracle.quantize_nvfp4(x, oracle.STATIC, static_scale=float(qd.tensor_scale) * 4)
+    assert qh.tensor_scale == qd.tensor_scale * 4
+    assert not np.array_equal(qh.scales, qd.scales)
 
 
 # ------------------------------------------------------------------ GEMM
