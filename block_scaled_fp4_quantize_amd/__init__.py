@@ -83,6 +83,8 @@ def lib():
             "fp4_linear_launches": (I32, [I32, I64, I64, I64, I32]),
             "fp4_export_canonical": (I32, [T, T, P]),
             "fp4_dequantize": (I32, [T, P, I64, P]),
+            "fp4_workspace_flags": (I32, [P, SZ, ctypes.POINTER(ctypes.c_uint32), I32, P]),
+            "fp4_set_exchange_spin_limit": (ctypes.c_uint32, [ctypes.c_uint32]),
             "fp4_status_string": (ctypes.c_char_p, [I32]),
             "fp4_last_error": (ctypes.c_char_p, []),
         }
@@ -245,6 +247,24 @@ def fp4_linear_w4a16(x: torch.Tensor, w: Fp4Tensor, out: torch.Tensor | None = N
     _check(lib().fp4_linear_w4a16(_ptr(x), m, ctypes.byref(w.desc), _ptr(out), out.stride(0),
                                   _stream(x.device)))
     return out
+
+
+WS_EXCHANGE_TIMEOUT = 1
+
+
+def fp4_workspace_flags(workspace: torch.Tensor, clear: bool = False) -> int:
+    """Sticky error flags recorded in a quantize or linear workspace (waits for
+    the current stream); clear=True clears them."""
+    flags = ctypes.c_uint32(0)
+    _check(lib().fp4_workspace_flags(_ptr(workspace), workspace.numel(), ctypes.byref(flags),
+                                     int(bool(clear)), _stream(workspace.device)))
+    return flags.value
+
+
+def fp4_set_exchange_spin_limit(polls: int) -> int:
+    """Test aid: polls before a workgroup of the quantizer's maximum exchange
+    gives up (0: at once). Returns the previous value."""
+    return lib().fp4_set_exchange_spin_limit(int(polls))
 
 
 def fp4_export_canonical(t: Fp4Tensor) -> Fp4Tensor:

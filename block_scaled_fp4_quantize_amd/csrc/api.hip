@@ -420,6 +420,31 @@ fp4_status fp4_dequantize(const fp4_tensor *t, float *out_f32, int64_t ldo, hipS
   return ok();
 }
 
+fp4_status fp4_workspace_flags(const void *workspace, size_t workspace_bytes, uint32_t *flags,
+                               int32_t clear, hipStream_t stream) {
+  if (!workspace || !flags) return fail(FP4_ERR_INVALID_ARG, "null workspace or flags pointer");
+  if (workspace_bytes < kQuantScratchBytes)
+    return fail(FP4_ERR_WORKSPACE, "workspace smaller than the %zu bytes that hold the flags",
+                kQuantScratchBytes);
+  fp4_status st_check;
+  if ((st_check = check_device()) != FP4_OK) return st_check;
+  uint32_t *word = (uint32_t *)workspace + kErrWord;
+  uint32_t host = 0;
+  hipError_t e = hipMemcpyAsync(&host, word, sizeof host, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "reading the workspace flags");
+  *flags = host;
+  if (clear && host) {
+    const uint32_t zero = 0;
+    e = hipMemcpyAsync(word, &zero, sizeof zero, hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "clearing the workspace flags");
+  }
+  return ok();
+}
+
+uint32_t fp4_set_exchange_spin_limit(uint32_t polls) { return set_exchange_spin_limit(polls); }
+
 const char *fp4_status_string(int32_t s) {
   switch (s) {
     case FP4_OK: return "FP4_OK";

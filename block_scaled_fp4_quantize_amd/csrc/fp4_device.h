@@ -325,47 +325,187 @@ __device__ __forceinline__ void mx_encode_block(const uint4 (&v)[4], uint4 &code
 
 // ---- block rotation ----
 //
-// y = H_B x / sqrt(B) over one block of B bf16 values held as B/8 uint4 (value
-// 8i + 2j + h in the h-th half of dword j of v[i]), H_B the Sylvester Hadamard
-// matrix, as the MXFP4 path of "FP4 on a consumer RTX 5090: the Blackwell
-// headline loses to plain int4" (section "Finding 3") rotates activations
-// before quantizing them. The rotation size is the block, so every rotation
-// stays inside the block it feeds. Binary32 fast transform (stages pairing
-// i with i + 1, i + 2, i + 4, ...: a + b, a - b; no contraction, as the
-// library is built), one multiply by RN_fp32(1/sqrt(B)) (exactly 1/4 for
-// B = 16), then bf16 nearest-even: the values the block encoders take.
+// y_i = RN_bf16(c * sum_j H[i][j] x_j) over one block of B bf16 values, H_B
+// the Sylvester Hadamard matrix (H[i][j] = (-1)^popcount(i & j)) and
+// c = RN_fp32(1/sqrt(B)) (1/4 for B = 16, 0xB504F3 * 2^-26 for B = 32), as
+// the MXFP4 path of "FP4 on a consumer RTX 5090: the Blackwell headline loses
+// to plain int4" (section "Finding 3") rotates activations before quantizing
+// them; the rotation size is the block, so every rotation stays inside the
+// block it feeds. The sum and the product are exact and the bf16 rounding
+// (nearest, ties to even) is the only one, so the result does not depend on
+// the order of the additions; an exact zero gives +0.
+//
+// Fast path: every value is a multiple of the smallest quantum q_min in the
+// block and every partial sum of a Walsh-Hadamard transform is below
+// B * 2^(e_max + 1), so the binary64 transform is exact when the nonzero
+// values' exponent fields differ by at most 45 - log2(B) (41 or 40 binades;
+// wider only for crafted inputs); c * S is then split exactly into
+// hi = RN(c S) and lo = fma(c, S, -hi). Other blocks take an exact integer
+// path (rot_exact_one).
+
+// bf16 bits of the real h + l rounded to nearest, ties to even, where
+// h = RN_fp64(h + l) and l is the exact remainder (0 when h is exact). A
+// binary64 bf16 midpoint h is decided by the sign of l. |h| >= 2^-137 or 0.
+__device__ __forceinline__ uint32_t bf16_of_exact(double h, double l) {
+  const uint64_t u = (uint64_t)__double_as_longlong(h);
+  const uint32_t neg = (uint32_t)(u >> 63);
+  const int ef = (int)((u >> 52) & 0x7FFu);
+  if (ef == 0) return 0u;                              // exact zero: +0
+  const int e = ef - 1023;                             // floor(log2 |h|)
+  const uint64_t sig = (u & 0xFFFFFFFFFFFFFull) | (1ull << 52);
+  const int q = e - 7 > -133 ? e - 7 : -133;           // exponent of the bf16 quantum
+  int drop = 52 - e + q;                               // 45 (normal) .. 56 (subnormal)
+  if (drop > 62) drop = 62;
+  uint64_t r = sig >> drop;
+  const uint64_t rem = sig & ((1ull << drop) - 1ull), half = 1ull << (drop - 1);
+  const bool tie_up = l != 0.0 ? ((l < 0.0) == (neg != 0u)) : (r & 1ull) != 0ull;
+  if (rem > half || (rem == half && tie_up)) r += 1ull;
+  // r * 2^q as bf16: exponent field q + 134 over the 8-bit significand r
+  // (a carry to 256, or a subnormal r, land in the right fields by themselves)
+  return (((uint32_t)(q + 133) << 7) + (uint32_t)r) | (neg << 15);
+}
+
+// Exact rotation output i of a block (bf16 bits in vals[0 .. B-1]) with
+// integer arithmetic: |x| = n * 2^-133 with n < 2^261, the signed sum in a
+// 320-bit two's complement integer (ten 32-bit words), multiplied by the
+// norm's integer significand cint and rounded to bf16 with the value's scale
+// 2^sexp. Kept out of line: only blocks with a wide magnitude range get here.
+__device__ __attribute__((noinline)) uint32_t rot_exact_one(const uint32_t *vals, int nvals, int i,
+                                                            uint32_t cint, int sexp) {
+  constexpr int NW = 10;
+  uint32_t a[NW];
+  for (int t = 0; t < NW; ++t) a[t] = 0u;
+  for (int j = 0; j < nvals; ++j) {
+    const uint32_t b = vals[j], f = (b >> 7) & 0xFFu, m = b & 0x7Fu;
+    if (f == 0u && m == 0u) continue;
+    const uint32_t sig = f ? (m | 0x80u) : m;
+    const int sh = f ? (int)f - 1 : 0;
+    const bool sub = ((b >> 15) ^ (uint32_t)(__popc((uint32_t)(i & j)) & 1)) != 0u;
+    const int w0 = sh >> 5, off = sh & 31;
+    uint64_t t = (uint64_t)sig << off;                // <= 40 bits over words w0, w0 + 1
+    uint32_t carry = 0u;
+    for (int w = w0; w < NW; ++w) {
+      const uint64_t part = t & 0xFFFFFFFFull;
+      t >>= 32;
+      uint64_t r;
+      if (!sub) {
+        r = (uint64_t)a[w] + part + carry;
+        carry = (uint32_t)(r >> 32);
+      } else {
+        r = (uint64_t)a[w] - part - carry;
+        carry = (uint32_t)((r >> 63) & 1ull);
+      }
+      a[w] = (uint32_t)r;
+      if (t == 0ull && carry == 0u) break;
+    }
+  }
+  const uint32_t neg = a[NW - 1] >> 31;
+  if (neg) {                                          // magnitude of a negative sum
+    uint32_t c = 1u;
+    for (int w = 0; w < NW; ++w) {
+      const uint64_t r = (uint64_t)(~a[w]) + c;
+      a[w] = (uint32_t)r;
+      c = (uint32_t)(r >> 32);
+    }
+  }
+  {
+    uint64_t c = 0ull;                                // times the norm (< 2^24)
+    for (int w = 0; w < NW; ++w) {
+      const uint64_t r = (uint64_t)a[w] * cint + c;
+      a[w] = (uint32_t)r;
+      c = r >> 32;
+    }
+  }
+  int top = NW - 1;
+  while (top >= 0 && a[top] == 0u) --top;
+  if (top < 0) return 0u;                             // exact zero: +0
+  const int len = 32 * top + 32 - __clz(a[top]);
+  const int q = len - 1 + sexp - 7 > -133 ? len - 1 + sexp - 7 : -133;
+  const int drop = q - sexp;                          // >= 1: bits below the quantum
+  auto bit = [&](int p) -> uint32_t { return p < 0 ? 0u : (a[p >> 5] >> (p & 31)) & 1u; };
+  uint32_t r = 0u;
+  for (int p = drop + 8; p >= drop; --p) r = (r << 1) | bit(p);
+  const uint32_t half = bit(drop - 1);
+  bool sticky = false;
+  const int lim = drop - 1;                           // bits [0, lim) decide a tie
+  for (int w = 0; w < NW && 32 * w < lim; ++w) {
+    const uint32_t mask = 32 * w + 32 <= lim ? 0xFFFFFFFFu : ((1u << (lim - 32 * w)) - 1u);
+    sticky |= (a[w] & mask) != 0u;
+  }
+  if (half && (sticky || (r & 1u))) r += 1u;
+  return (((uint32_t)(q + 133) << 7) + r) | (neg << 15);
+}
+
 template <int B>
 __device__ __forceinline__ void hadamard_block(uint4 (&v)[B / 8]) {
   static_assert(B == 16 || B == 32, "rotation size is a block: 16 or 32 values");
-  float y[B];
+  constexpr int kLog2B = B == 16 ? 4 : 5;
+  uint32_t w[B / 2];
 #pragma unroll
   for (int i = 0; i < B / 8; ++i) {
-    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      y[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
-      y[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-    }
+    w[4 * i] = v[i].x; w[4 * i + 1] = v[i].y; w[4 * i + 2] = v[i].z; w[4 * i + 3] = v[i].w;
   }
+  // exponent fields of the nonzero values (subnormals count as field 1: the
+  // same quantum, 2^-133)
+  int fmax = 0, fmin = 255;
 #pragma unroll
-  for (int span = 1; span < B; span *= 2)
+  for (int j = 0; j < B / 2; ++j)
 #pragma unroll
-    for (int i = 0; i < B; ++i)
-      if ((i & span) == 0) {
-        const float lo = y[i], hi = y[i + span];
-        y[i] = lo + hi;
-        y[i + span] = lo - hi;
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t b = (w[j] >> (16 * h)) & 0xFFFFu;
+      const int f = max((int)((b >> 7) & 0xFFu), 1);
+      if (b & 0x7FFFu) {
+        fmax = max(fmax, f);
+        fmin = min(fmin, f);
       }
-  const float c = B == 16 ? 0.25f : 0x1.6a09e6p-3f;  // RN_fp32(1/sqrt(32))
+    }
+  uint32_t out[B / 2];
+  if (fmax - fmin <= 45 - kLog2B) {
+    double y[B];
 #pragma unroll
-  for (int i = 0; i < B / 8; ++i) {
-    uint32_t w[4];
+    for (int j = 0; j < B / 2; ++j) {
+      y[2 * j] = (double)__uint_as_float(w[j] << 16);
+      y[2 * j + 1] = (double)__uint_as_float(w[j] & 0xFFFF0000u);
+    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      w[j] = (uint32_t)f32_to_bf16_rne(y[8 * i + 2 * j] * c) |
-             ((uint32_t)f32_to_bf16_rne(y[8 * i + 2 * j + 1] * c) << 16);
-    v[i] = make_uint4(w[0], w[1], w[2], w[3]);
+    for (int span = 1; span < B; span *= 2)
+#pragma unroll
+      for (int i = 0; i < B; ++i)
+        if ((i & span) == 0) {
+          const double lo = y[i], hi = y[i + span];
+          y[i] = lo + hi;
+          y[i + span] = lo - hi;
+        }
+    uint32_t r[B];
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      if constexpr (B == 16) {
+        r[i] = bf16_of_exact(y[i] * 0.25, 0.0);          // exact product
+      } else {
+        const double c = (double)0x1.6a09e6p-3f;         // RN_fp32(1/sqrt(32))
+        const double hi = y[i] * c;
+        r[i] = bf16_of_exact(hi, __builtin_fma(y[i], c, -hi));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < B / 2; ++j) out[j] = r[2 * j] | (r[2 * j + 1] << 16);
+  } else {
+    uint32_t vals[B];
+#pragma unroll
+    for (int j = 0; j < B / 2; ++j) {
+      vals[2 * j] = w[j] & 0xFFFFu;
+      vals[2 * j + 1] = w[j] >> 16;
+    }
+    // value = n * cint * 2^sexp: 2^-135 * n (B = 16), 0xB504F3 * 2^-159 * n (B = 32)
+    const uint32_t cint = B == 16 ? 1u : 0xB504F3u;
+    const int sexp = B == 16 ? -135 : -159;
+    for (int j = 0; j < B / 2; ++j)
+      out[j] = rot_exact_one(vals, B, 2 * j, cint, sexp) |
+               (rot_exact_one(vals, B, 2 * j + 1, cint, sexp) << 16);
   }
+#pragma unroll
+  for (int i = 0; i < B / 8; ++i)
+    v[i] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
 }
 
 // ---- decode side ----

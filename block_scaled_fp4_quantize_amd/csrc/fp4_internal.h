@@ -22,11 +22,20 @@ inline int frag_scale_bytes(int fmt) { return fmt == 0 ? 128 : 64; }
 constexpr int kActGrid = 128;         // workgroups of the single-launch quantizer
 constexpr int kActBpt = 4;            // single-launch quantizer capacity: kActGrid * 256 * kActBpt blocks
 constexpr int64_t kActRedundantMaxValues = 49152;  // M * K up to which each workgroup finds the maximum alone
-// Quantize scratch: kMaxAmaxParts partial maxima, then the single-launch
-// quantizer's kActGrid tagged maximum words, one per 128-byte line
-// (zero-filled once).
+// Quantize scratch (32-bit words, zero-filled once): kMaxAmaxParts partial
+// maxima; the single-launch quantizer's kActGrid tagged maximum words, one per
+// 128-byte line; a line holding the sticky error flags; a line holding the
+// exchange's arrival count (reset by the last workgroup of every call).
 constexpr int kSlotStride = 32;
-constexpr size_t kQuantScratchBytes = (kMaxAmaxParts + kActGrid * kSlotStride) * sizeof(uint32_t);
+constexpr int kErrWord = kMaxAmaxParts + kActGrid * kSlotStride;
+constexpr int kArriveWord = kErrWord + kSlotStride;
+constexpr size_t kQuantScratchBytes = (size_t)(kArriveWord + kSlotStride) * sizeof(uint32_t);
+// Error flag: a workgroup of the maximum exchange gave up waiting.
+constexpr uint32_t kErrExchangeTimeout = 1u;
+constexpr uint32_t kDefaultSpinLimit = 1u << 22;
+// Polls of the maximum exchange before a workgroup gives up (test hook).
+uint32_t exchange_spin_limit();
+uint32_t set_exchange_spin_limit(uint32_t polls);
 
 // Number of partial maxima the large-tensor path produces for n elements.
 int amax_parts(int64_t n);

@@ -24,6 +24,7 @@
 #include "fp4_internal.h"
 
 #include <algorithm>
+#include <atomic>
 
 namespace fp4i {
 using namespace fp4d;
@@ -250,28 +251,37 @@ __global__ __launch_bounds__(kThreads) void k_quant_tiled(
 // g writes slots g, g + G, g + 2G, ... (G = grid size), so every call rewrites
 // every slot whatever its grid size, and after any call all slots carry that
 // call's tag. A call's tag is therefore one more than any slot's tag at its
-// start (a zero-filled array is tag 0). Thread t < G polls slot t (bounded)
-// until it carries this call's tag, and the workgroup takes the maximum. The
-// exchanged values travel in the polled words themselves, so no cache
-// writeback or fence is involved.
-// Each word has a 128-byte line of its own (kSlotStride words apart), so that
-// the polls of different words go to different lines.
-__device__ __forceinline__ uint32_t grid_max_u32(uint32_t wg_max, uint32_t tag,
-                                                 uint32_t *slots, uint32_t *lds) {
+// start (a zero-filled array is tag 0). Thread t < G polls slot t until it
+// carries this call's tag, and the workgroup takes the maximum. The exchanged
+// values travel in the polled words themselves, so no cache writeback or fence
+// is involved. Each word has a 128-byte line of its own (kSlotStride words
+// apart), so that the polls of different words go to different lines.
+// The wait assumes every workgroup of the grid (at most kActGrid of at most
+// 512 threads) runs at the same time; it is bounded by spin_limit polls per
+// slot. A slot that does not arrive in time counts as 0xFFFF, so a result at
+// or above 0x8000 (no bf16 magnitude is) tells the caller this workgroup gave
+// up.
+__device__ __forceinline__ uint32_t grid_max_u32(uint32_t wg_max, uint32_t tag, uint32_t *slots,
+                                                 uint32_t spin_limit, uint32_t *lds) {
   for (uint32_t s = blockIdx.x + threadIdx.x * gridDim.x; s < (uint32_t)kActGrid;
        s += blockDim.x * gridDim.x)
     __hip_atomic_store(&slots[s * kSlotStride], (tag << 16) | wg_max, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   uint32_t v = 0;
   if (threadIdx.x < gridDim.x) {
-    for (uint32_t it = 0; it < (1u << 22); ++it) {
+    bool arrived = false;
+    for (uint32_t it = 0; it < spin_limit; ++it) {
       v = __hip_atomic_load(&slots[threadIdx.x * kSlotStride], __ATOMIC_RELAXED,
                             __HIP_MEMORY_SCOPE_AGENT);
-      if ((v >> 16) == tag) break;
+      if ((v >> 16) == tag) {
+        arrived = true;
+        break;
+      }
       __builtin_amdgcn_s_sleep(1);
     }
+    v = arrived ? (v & 0xFFFFu) : 0xFFFFu;
   }
-  return block_max_u32(v & 0xFFFFu, lds);
+  return block_max_u32(v, lds);
 }
 
 // Largest magnitude (bf16 bits) of the whole tensor, taken by one workgroup
@@ -308,12 +318,18 @@ __device__ __forceinline__ uint32_t tensor_absmax_wg(const uint16_t *x, int64_t 
 // workgroups as hold the tensor; with DYN = 1 they exchange their maxima,
 // with DYN = 2 (small tensors) each workgroup reads the whole tensor and
 // takes the maximum itself, with no exchange.
+//
+// When a workgroup of the exchange gives up (grid_max_u32), it encodes with a
+// NaN tensor scale (zero codes and scales), sets kErrExchangeTimeout in the
+// workspace's sticky error word, and the tensor scale written for the call is
+// NaN: the last workgroup to finish writes S_t, and it knows from the arrival
+// count (which also counts the workgroups that gave up) whether any did.
 template <int FMT, int TILED, int DYN, int BPT, int NTH = kThreads>
 __global__ __launch_bounds__(NTH) void k_quant_small(
     const uint16_t *__restrict__ x, int64_t rows, int64_t k, int64_t rows_pad, int64_t kt_n,
     const float *__restrict__ static_scale, uint8_t *__restrict__ codes, int64_t cpitch,
     uint8_t *__restrict__ scales, int64_t spitch, float *__restrict__ ts_out,
-    uint32_t *__restrict__ sync, uint32_t recipe) {
+    uint32_t *__restrict__ sync, uint32_t recipe, uint32_t spin_limit) {
   using K = Blk<FMT>;
   __shared__ uint32_t lds[NTH / 64];
   const int64_t nb = k / K::B, nb_pad = kt_n * K::BPF, total = rows_pad * nb_pad;
@@ -341,13 +357,29 @@ __global__ __launch_bounds__(NTH) void k_quant_small(
     m = max(m, block_absmax<FMT>(v[i]));
   }
   float st = 1.0f;
+  bool gave_up = false;
+  uint32_t arrived_before = 0;
   if (FMT == 0) {
-    if (DYN == 1)
-      st = tensor_scale_from_amax(bf16_bits_to_f32(grid_max_u32(block_max_u32(m, lds), tag, sync, lds)));
-    else if (DYN == 2)
+    if (DYN == 1) {
+      const uint32_t g = grid_max_u32(block_max_u32(m, lds), tag, sync, spin_limit, lds);
+      gave_up = g >= 0x8000u;
+      st = gave_up ? __builtin_nanf("") : tensor_scale_from_amax(bf16_bits_to_f32(g));
+      if (threadIdx.x == 0) {
+        if (gave_up)
+          __hip_atomic_fetch_or(&sync[kErrWord - kMaxAmaxParts], kErrExchangeTimeout,
+                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // arrivals in the low half, workgroups that gave up in the high half;
+        // the result is first needed after the encoding below
+        arrived_before = __hip_atomic_fetch_add(&sync[kArriveWord - kMaxAmaxParts],
+                                                gave_up ? 0x10001u : 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else if (DYN == 2) {
       st = tensor_scale_from_amax(bf16_bits_to_f32(tensor_absmax_wg<FMT>(x, rows * nb, recipe, lds)));
-    else st = *static_scale;
-    if (blockIdx.x == 0 && threadIdx.x == 0 && ts_out) *ts_out = st;
+    } else {
+      st = *static_scale;
+    }
+    if (DYN != 1 && blockIdx.x == 0 && threadIdx.x == 0 && ts_out) *ts_out = st;
   }
 #pragma unroll
   for (int i = 0; i < BPT; ++i) {
@@ -358,6 +390,13 @@ __global__ __launch_bounds__(NTH) void k_quant_small(
     block_dst<FMT, TILED>(r, b, kt_n, codes, cpitch, scales, spitch, cdst, sdst);
     if (r >= rows || b >= nb) zero_store<FMT>(cdst, sdst);
     else encode_store<FMT>(v[i], st, cdst, sdst, recipe);
+  }
+  if (FMT == 0 && DYN == 1 && threadIdx.x == 0 && (arrived_before & 0xFFFFu) == gridDim.x - 1) {
+    // the last workgroup: every other one has taken its decision
+    const bool any_gave_up = gave_up || (arrived_before >> 16) != 0u;
+    if (ts_out) *ts_out = any_gave_up ? __builtin_nanf("") : st;
+    __hip_atomic_store(&sync[kArriveWord - kMaxAmaxParts], 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -416,11 +455,14 @@ int grid_for(int64_t work, int cap) {
   return (int)g;
 }
 
+std::atomic<uint32_t> g_spin_limit{kDefaultSpinLimit};
+
 template <int FMT, int TILED>
 void launch_small(const uint16_t *x, int64_t rows, int64_t k, int64_t rows_pad, int64_t kt_n,
                   const float *static_scale, uint8_t *codes, int64_t cpitch, uint8_t *scales,
                   int64_t spitch, float *ts_out, uint32_t *sync, uint32_t recipe,
                   hipStream_t stream) {
+  const uint32_t spin = g_spin_limit.load(std::memory_order_relaxed);
   // One block per thread where the grid allows: encoding is the costly part
   // and spreads over as many CUs as there are blocks. The dynamic-scale form
   // also exchanges its maximum among the workgroups, so it stops at kActGrid
@@ -436,7 +478,7 @@ void launch_small(const uint16_t *x, int64_t rows, int64_t k, int64_t rows_pad, 
 #define FP4_QS(D, BPT, NTH)                                                                     \
   hipLaunchKernelGGL((k_quant_small<FMT, TILED, D, BPT, NTH>), dim3(grid), dim3(NTH), 0, stream, \
                      x, rows, k, rows_pad, kt_n, static_scale, codes, cpitch, scales, spitch,    \
-                     ts_out, sync, recipe)
+                     ts_out, sync, recipe, spin)
     // Small tensors: every workgroup reads the whole tensor for its maximum
     // rather than exchanging it (measured per call: M = 1, K = 5120: 4.9 ->
     // 3.9 us; M = 8, K = 5120: 5.15 -> 4.8 us; at M * K = 139264 it lost,
@@ -456,7 +498,7 @@ void launch_small(const uint16_t *x, int64_t rows, int64_t k, int64_t rows_pad, 
   } else {
     hipLaunchKernelGGL((k_quant_small<FMT, TILED, 0, 1>), dim3((unsigned)per_wg), dim3(kThreads), 0,
                        stream, x, rows, k, rows_pad, kt_n, static_scale, codes, cpitch, scales,
-                       spitch, ts_out, sync, recipe);
+                       spitch, ts_out, sync, recipe, spin);
   }
 }
 
@@ -479,6 +521,12 @@ void launch_large(const uint16_t *x, int64_t rows, int64_t k, int64_t rows_pad, 
 }
 
 }  // namespace
+
+uint32_t exchange_spin_limit() { return g_spin_limit.load(std::memory_order_relaxed); }
+
+uint32_t set_exchange_spin_limit(uint32_t polls) {
+  return g_spin_limit.exchange(polls, std::memory_order_relaxed);
+}
 
 int amax_parts(int64_t n) {
   int64_t per = (int64_t)kThreads * 8 * 4;  // >= 4 uint4 loads per thread

@@ -62,10 +62,11 @@ typedef enum { FP4_NVFP4 = 0, FP4_MXFP4 = 1 } fp4_format;
  *   Sylvester Hadamard matrix: the online rotation the MXFP4 path applies to
  *   activations ("FP4 on a consumer RTX 5090: the Blackwell headline loses to
  *   plain int4", section "Finding 3 - the real-FP4 path"; the page gives no
- *   rotation size, the block is the one used here). The transform runs in
- *   binary32 (fast transform in Sylvester order, then one multiply by
- *   RN_fp32(1/sqrt(B))) and is rounded to bf16 before the block is
- *   quantized. Weights and activations must both be rotated, or neither:
+ *   rotation size, the block is the one used here). Each rotated value is
+ *   the exact real RN_fp32(1/sqrt(B)) * sum_j H[i][j] x[j] rounded once to
+ *   bf16 (nearest, ties to even; an exact zero gives +0), so the result does
+ *   not depend on the order of the additions; the block is quantized from
+ *   those bf16 values. Weights and activations must both be rotated, or neither:
  *   then H_B H_B^T / B = I and the GEMM approximates the unrotated product.
  *   fp4_gemm rejects operands that differ in this flag. The NVFP4 dynamic
  *   tensor scale is taken over the rotated values. fp4_dequantize returns the
@@ -211,6 +212,28 @@ fp4_status fp4_linear_w4a16(const void *x_bf16, int64_t m, const fp4_tensor *w, 
  * quantize + GEMM, 3 when the quantizer needs a separate reduction launch
  * (large NVFP4 activations with a dynamic scale). 0 for invalid arguments. */
 int32_t fp4_linear_launches(int32_t fmt, int64_t m, int64_t n, int64_t k, int32_t static_scale);
+
+/*
+ * Sticky error flags that kernels record in a quantize or linear workspace
+ * (the flags sit at the same offset in both). FP4_WS_EXCHANGE_TIMEOUT: a
+ * workgroup of the single-launch NVFP4 quantizer (dynamic scale, activations
+ * of up to 2^17 blocks) gave up waiting for the other workgroups' maxima. That
+ * exchange assumes every workgroup of its grid (at most 128 workgroups of at
+ * most 512 threads) is resident at once; a workgroup that is not, for as long
+ * as the bounded wait lasts (about 2^22 polls), makes the call fail visibly:
+ * its tensor scale is NaN (so is every product computed from it) and the flag
+ * is set. The flags stay set until cleared here.
+ * Waits for `stream`, writes the flags to *flags and, when clear != 0, clears
+ * them. Not for use inside a stream capture.
+ */
+enum { FP4_WS_EXCHANGE_TIMEOUT = 1 };
+fp4_status fp4_workspace_flags(const void *workspace, size_t workspace_bytes, uint32_t *flags,
+                               int32_t clear, hipStream_t stream);
+
+/* Test aid: the number of polls after which a workgroup of that exchange gives
+ * up (default 2^22; 0 gives up at once, which makes every such call fail as
+ * described above). Process-wide; returns the previous value. */
+uint32_t fp4_set_exchange_spin_limit(uint32_t polls);
 
 /* Test aids (not on the hot path). */
 /* Copy a TILED tensor into a CANONICAL one of the same format/shape

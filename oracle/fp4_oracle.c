@@ -58,14 +58,14 @@
  *   - Rotation (optional, either format): within each quantization block of
  *     B values along k, y = H_B x / sqrt(B) with H_B the Sylvester Hadamard
  *     matrix (H[i][j] = (-1)^popcount(i & j)); the pages give no rotation
- *     size, and B keeps each rotation inside the block it feeds. The
- *     rotation's output decides codes, so it is computed in the precision the
- *     GPU path uses: binary32, as the fast transform (stages pairing i with
- *     i + 1, then i + 2, i + 4, ...: a + b and a - b), one multiply by
- *     RN_fp32(1/sqrt(B)) (exactly 1/4 for B = 16), then rounded to bf16
- *     (nearest even), the activation type the quantizer takes. The weights
- *     are rotated the same way, so the GEMM of the two rotated operands
- *     approximates the unrotated product (H H^T / B = I).
+ *     size, and B keeps each rotation inside the block it feeds. The pages
+ *     give no precision either; the rotation's output decides codes, so it is
+ *     defined without any order-dependent rounding: the exact real
+ *     c * sum_j H[i][j] x[j], c = RN_fp32(1/sqrt(B)) (exactly 1/4 for B = 16),
+ *     rounded once to bf16 (nearest even), the activation type the quantizer
+ *     takes; an exact zero gives +0. The weights are rotated the same way, so
+ *     the GEMM of the two rotated operands approximates the unrotated product
+ *     (H H^T / B = I).
  *   - OAS (MXFP4 only): e_b = the smallest exponent with a_b <= 6 * 2^e_b
  *     (clamped to [-127, 127]), so no element saturates; the default rule
  *     lets block maxima in (6, 8) * 2^e_b saturate to 6 * 2^e_b.
@@ -345,18 +345,6 @@ int orc_quantize_mxfp4(const uint16_t *x, int64_t rows, int64_t k,
 
 /* --------------------------------------------------------------- rotation */
 
-/* binary32 -> bf16, nearest with ties to even (finite input; values past the
- * bf16 range round to infinity). */
-static uint16_t f32_to_bf16_nearest_even(float f)
-{
-    uint32_t u;
-    memcpy(&u, &f, sizeof u);
-    uint32_t lower = u & 0xFFFFu, upper = u >> 16;
-    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
-        upper += 1;
-    return (uint16_t)upper;
-}
-
 /* RN_fp32(1/sqrt(bs)): exactly 0.25 for 16; for 32 the binary64 value of
  * 1/sqrt(32) is rounded to binary32 (a test checks it is the binary32 value
  * nearest to the real 1/sqrt(32)). */
@@ -366,31 +354,155 @@ float orc_hadamard_norm(int bs)
 }
 
 /*
- * Rotation reading in the header [REALFP4]: out[r][b*bs + i] =
- * bf16_RNE(fl32(sum_j H[i][j] x[r][b*bs + j]) * RN_fp32(1/sqrt(bs))), the sums
- * formed by the binary32 fast transform. bs is 16 or 32, k a multiple of bs.
- * Returns 0, or -1 on a bad argument.
+ * Exact rotation sums. A finite bf16 value is an integer multiple of 2^-133
+ * (its smallest subnormal): |x| = N * 2^-133 with N < 2^261. A row of H_bs
+ * applied to a block is a signed sum of at most 32 such integers (< 2^266),
+ * and multiplying by the 24-bit significand of RN_fp32(1/sqrt(bs)) stays
+ * below 2^290. Those integers are held here as little-endian arrays of
+ * 32-bit words, wide enough for 320 bits.
+ */
+#define ROT_WORDS 10
+
+typedef struct { uint32_t w[ROT_WORDS]; } rot_int;
+
+/* a += m * 2^shift (m < 2^9, shift <= 253). */
+static void rot_add(rot_int *a, uint32_t m, int shift)
+{
+    int i = shift / 32;
+    uint64_t carry = (uint64_t)m << (shift % 32);
+    while (carry != 0 && i < ROT_WORDS) {
+        uint64_t t = (uint64_t)a->w[i] + (carry & 0xFFFFFFFFu);
+        a->w[i] = (uint32_t)t;
+        carry = (carry >> 32) + (t >> 32);
+        ++i;
+    }
+}
+
+/* -1, 0, +1 as a <, =, > b. */
+static int rot_cmp(const rot_int *a, const rot_int *b)
+{
+    for (int i = ROT_WORDS - 1; i >= 0; --i)
+        if (a->w[i] != b->w[i])
+            return a->w[i] < b->w[i] ? -1 : 1;
+    return 0;
+}
+
+/* a -= b, given a >= b. */
+static void rot_sub(rot_int *a, const rot_int *b)
+{
+    uint64_t borrow = 0;
+    for (int i = 0; i < ROT_WORDS; ++i) {
+        uint64_t t = (uint64_t)a->w[i] - b->w[i] - borrow;
+        a->w[i] = (uint32_t)t;
+        borrow = (t >> 63) & 1u;
+    }
+}
+
+/* a *= c (c < 2^24). */
+static void rot_mul(rot_int *a, uint32_t c)
+{
+    uint64_t carry = 0;
+    for (int i = 0; i < ROT_WORDS; ++i) {
+        uint64_t t = (uint64_t)a->w[i] * c + carry;
+        a->w[i] = (uint32_t)t;
+        carry = t >> 32;
+    }
+}
+
+static int rot_bit(const rot_int *a, int i)
+{
+    return i < 0 ? 0 : (int)((a->w[i / 32] >> (i % 32)) & 1u);
+}
+
+/* Number of significant bits (0 for zero). */
+static int rot_bitlen(const rot_int *a)
+{
+    for (int i = ROT_WORDS - 1; i >= 0; --i)
+        if (a->w[i])
+            for (int b = 31; b >= 0; --b)
+                if ((a->w[i] >> b) & 1u)
+                    return 32 * i + b + 1;
+    return 0;
+}
+
+/* bf16 bits of (-1)^neg * a * 2^scale_exp rounded to nearest, ties to even
+ * (a > 0; the result is finite for the inputs accepted below). bf16 keeps 8
+ * significant bits down to 2^-126 and a fixed quantum of 2^-133 below. */
+static uint16_t rot_round_bf16(const rot_int *a, int scale_exp, int neg)
+{
+    int len = rot_bitlen(a);
+    int top = len - 1 + scale_exp;                 /* floor(log2 |value|) */
+    int q = top - 7 > -133 ? top - 7 : -133;       /* exponent of the bf16 quantum */
+    int drop = q - scale_exp;                      /* bits of a below the quantum */
+    uint32_t r = 0;
+    for (int i = 8; i >= 0; --i)                   /* a >> drop has at most 9 bits */
+        r = (r << 1) | (uint32_t)rot_bit(a, drop + i);
+    int half = rot_bit(a, drop - 1), sticky = 0;
+    for (int i = drop - 2; i >= 0 && !sticky; --i)
+        sticky = rot_bit(a, i);
+    if (half && (sticky || (r & 1u)))
+        r += 1;                                    /* may carry into the next binade */
+    float f = ldexpf((float)r, q);                 /* exact: r <= 256 */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)((u >> 16) | (neg ? 0x8000u : 0u));
+}
+
+static int popcount_parity(int v)
+{
+    int p = 0;
+    for (; v; v >>= 1)
+        p ^= v & 1;
+    return p;
+}
+
+/*
+ * Rotation reading in the header [REALFP4]: within each block of bs values
+ * along k, out[i] = RN_bf16( c * sum_j H[i][j] x[j] ) with
+ * H[i][j] = (-1)^popcount(i & j) (Sylvester order) and c = RN_fp32(1/sqrt(bs)):
+ * the sum and the product are exact and the bf16 rounding (nearest, ties to
+ * even) is the only one, so the result does not depend on the order in which
+ * a transform adds. An exact zero sum gives +0. bs is 16 or 32, k a multiple
+ * of bs, inputs finite with |x| < 2^120. Returns 0, or -1 on a bad argument.
  */
 int orc_hadamard_bf16(const uint16_t *x, int64_t rows, int64_t k, int bs, uint16_t *out)
 {
     if ((bs != 16 && bs != 32) || k <= 0 || rows < 0 || k % bs != 0)
         return -1;
-    const float c = orc_hadamard_norm(bs);
-    float y[32];
+    /* c = C * 2^(ce - 24) with C the 24-bit integer significand */
+    int ce;
+    double cf = frexp((double)orc_hadamard_norm(bs), &ce);
+    uint32_t cint = (uint32_t)ldexp(cf, 24);
     for (int64_t r = 0; r < rows; ++r)
         for (int64_t b = 0; b < k / bs; ++b) {
             const uint16_t *xb = x + r * k + b * bs;
-            for (int i = 0; i < bs; ++i)
-                y[i] = (float)orc_bf16_value(xb[i]);   /* exact */
-            for (int span = 1; span < bs; span *= 2)
-                for (int i = 0; i < bs; ++i)
-                    if ((i & span) == 0) {
-                        float lo = y[i], hi = y[i + span];
-                        y[i] = lo + hi;
-                        y[i + span] = lo - hi;
-                    }
-            for (int i = 0; i < bs; ++i)
-                out[r * k + b * bs + i] = f32_to_bf16_nearest_even(y[i] * c);
+            for (int i = 0; i < bs; ++i) {
+                rot_int pos, neg;
+                memset(&pos, 0, sizeof pos);
+                memset(&neg, 0, sizeof neg);
+                for (int j = 0; j < bs; ++j) {
+                    uint32_t bits = xb[j], e = (bits >> 7) & 0xFFu, m = bits & 0x7Fu;
+                    if (e == 0 && m == 0)
+                        continue;                  /* +-0 */
+                    /* |x| = N * 2^-133: N = m (subnormal) or (128 + m) << (e - 1) */
+                    uint32_t sig = e ? (128u | m) : m;
+                    int shift = e ? (int)e - 1 : 0;
+                    int negative = (int)(bits >> 15) ^ popcount_parity(i & j);
+                    rot_add(negative ? &neg : &pos, sig, shift);
+                }
+                int c = rot_cmp(&pos, &neg);
+                uint16_t y = 0;
+                if (c > 0) {
+                    rot_sub(&pos, &neg);
+                    rot_mul(&pos, cint);
+                    y = rot_round_bf16(&pos, -133 + ce - 24, 0);
+                } else if (c < 0) {
+                    rot_sub(&neg, &pos);
+                    rot_mul(&neg, cint);
+                    y = rot_round_bf16(&neg, -133 + ce - 24, 1);
+                }
+                out[r * k + b * bs + i] = y;
+            }
         }
     return 0;
 }

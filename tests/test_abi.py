@@ -216,3 +216,18 @@ def test_last_error_is_per_thread():
                 assert st == 1 and b"null" in msg, msg
             else:
                 assert st == 2 and b"multiple" in msg, msg
+
+
+def test_workspace_flags_and_spin_limit_host_side():
+    """The flag query validates on the host; the spin-limit hook returns the
+    previous value (no device needed for either)."""
+    L = fp4.lib()
+    flags = ctypes.c_uint32(7)
+    assert L.fp4_workspace_flags(None, 1 << 20, ctypes.byref(flags), 0, None) == 1
+    buf = ctypes.create_string_buffer(64)
+    assert L.fp4_workspace_flags(buf, 64, ctypes.byref(flags), 0, None) == 4
+    assert b"flags" in L.fp4_last_error()
+    assert L.fp4_workspace_flags(buf, 1 << 20, None, 0, None) == 1
+    prev = L.fp4_set_exchange_spin_limit(5)
+    assert prev == 1 << 22
+    assert L.fp4_set_exchange_spin_limit(prev) == 5

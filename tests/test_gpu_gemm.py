@@ -95,7 +95,7 @@ def test_decode_full_size_sampled(fmt, m, k, n):
     y = fp4.fp4_linear(x, wq)
     y2 = fp4.fp4_linear(x, wq)
     torch.cuda.synchronize()
-    assert torch.equal(y, y2), "split-K result differs between runs"
+    assert torch.equal(y, y2), "results differ between runs"
     rng = np.random.default_rng(m * 7 + n)
     rows = rng.integers(0, m, 4096)
     cols = rng.integers(0, n, 4096)
@@ -153,9 +153,9 @@ def test_graph_replay_matches_eager(fmt, m):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-def test_decode_without_split_workspace(fmt):
-    """fp4_gemm given no room for split-K runs one split per tile (several K
-    chunks per wave) and still matches."""
+def test_skinny_gemm_with_one_byte_workspace(fmt):
+    """The skinny GEMM (one workgroup per weight tile over the whole K) needs
+    no workspace: fp4_gemm with a one-byte workspace matches the oracle."""
     m, n, k = 8, 320, 17408
     f = F[fmt]
     a = synth.normal((m, k), 1.0, 12, 1)
@@ -166,13 +166,14 @@ def test_decode_without_split_workspace(fmt):
     qa = fp4.fp4_quantize_act(to_dev(a), f)
     tiny = torch.zeros(1, dtype=torch.uint8, device="cuda")
     c = bf16_out_to_f64(fp4.fp4_gemm(qa, wq, workspace=tiny))
-    assert_gemm_close(c, c_ref, l_ref, "decode, single split")
+    assert_gemm_close(c, c_ref, l_ref, "skinny GEMM, one-byte workspace")
 
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("m", [1, 32])
 def test_workspace_reused_across_calls(fmt, m):
-    """The split-K slots clean themselves: one zeroed workspace serves many calls."""
+    """One zeroed linear workspace (the quantizer's exchange words and the tiled
+    activations) serves many calls in sequence."""
     n, k = 640, 5120
     f = F[fmt]
     w = synth.normal((n, k), 0.02, 13, 1)

@@ -169,3 +169,46 @@ def test_workspace_shared_across_calls():
             qt = fp4.fp4_quantize_act(to_dev(bits), 0, layout=fp4.TILED, workspace=ws)
             assert_canonical_equal(fp4.fp4_export_canonical(qt), ref, 0,
                                    what=f"shared workspace tiled call {rep}/{i} {m}x{k}")
+
+
+@pytest.mark.parametrize("m,k", [(32, 5120), (32, 17408)])
+def test_exchange_give_up_is_visible(m, k):
+    """The single-launch NVFP4 quantizer's workgroups wait (bounded) for each
+    other's maxima. A workgroup that gives up must not encode with a stale
+    maximum: the call's tensor scale is NaN (so is every product made with it)
+    and the workspace's sticky flag is set until cleared. Forced from the host
+    with a wait of zero polls, so that no kernel waits at all; the same
+    workspaces then serve correct calls."""
+    n = 256
+    print(f"[quant-act] exchange give-up m={m} k={k}", flush=True)
+    a = synth.normal((m, k), 1.0, 21, m + k)
+    w = synth.normal((n, k), 0.02, 21, 2)
+    assert fp4.fp4_linear_launches(fp4.NVFP4, m, n, k) == 2   # quantizer with the exchange
+    wq = fp4.fp4_quantize_weight(to_dev(w), fp4.NVFP4)
+    x = to_dev(a)
+    ws_q = torch.zeros(fp4.lib().fp4_quantize_workspace_bytes(fp4.NVFP4, m, k), dtype=torch.uint8,
+                       device="cuda")
+    ws_l = torch.zeros(fp4.fp4_linear_workspace_bytes(fp4.NVFP4, m, n, k), dtype=torch.uint8,
+                       device="cuda")
+    prev = fp4.fp4_set_exchange_spin_limit(0)
+    try:
+        q = fp4.fp4_quantize_act(x, fp4.NVFP4, workspace=ws_q)
+        y = fp4.fp4_linear(x, wq, workspace=ws_l)
+        torch.cuda.synchronize()
+    finally:
+        fp4.fp4_set_exchange_spin_limit(prev)
+    assert np.isnan(q.tensor_scale.cpu().item())
+    assert torch.isnan(y.float()).all()
+    assert fp4.fp4_workspace_flags(ws_q) == fp4.WS_EXCHANGE_TIMEOUT
+    assert fp4.fp4_workspace_flags(ws_l, clear=True) == fp4.WS_EXCHANGE_TIMEOUT
+    assert fp4.fp4_workspace_flags(ws_l) == 0
+    assert fp4.fp4_workspace_flags(ws_q, clear=True) == fp4.WS_EXCHANGE_TIMEOUT
+    # with the default wait the same workspaces give the oracle's results
+    ref = oracle.quantize(oracle.NVFP4, a)
+    q2 = fp4.fp4_quantize_act(x, fp4.NVFP4, workspace=ws_q)
+    assert_canonical_equal(q2, ref, oracle.NVFP4, what="after a give-up")
+    c_ref, l_ref = oracle.gemm(ref, oracle.quantize(oracle.NVFP4, w))
+    y2 = fp4.fp4_linear(x, wq, workspace=ws_l).float().cpu().numpy().astype(np.float64)
+    tol = oracle.gemm_tolerance(c_ref, l_ref)
+    assert np.all(np.abs(y2 - c_ref) <= tol)
+    assert fp4.fp4_workspace_flags(ws_q) == 0 and fp4.fp4_workspace_flags(ws_l) == 0

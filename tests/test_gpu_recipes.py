@@ -70,6 +70,33 @@ def test_rotated_every_finite_bf16_value(fmt):
     assert_canonical_equal(q, _ref(fmt, x, True, False), F[fmt], what="rotated every bf16")
 
 
+def _wide_range_rows(rows, k, seed):
+    """Blocks whose nonzero magnitudes span up to 2^250, with large values that
+    cancel exactly inside a rotation sum, subnormals and zeros: the rotation's
+    exact integer path (a binary64 transform is not exact on them)."""
+    rng = np.random.default_rng(seed)
+    e = rng.integers(-133, 119, (rows, k))
+    x = rng.choice([-1.0, 1.0], (rows, k)) * rng.integers(1, 256, (rows, k)) * 2.0 ** (e - 7)
+    x[rng.random((rows, k)) < 0.1] = 0.0
+    big = 2.0 ** rng.integers(60, 110, (rows, 1))
+    x[:, 0::16], x[:, 1::16] = big, -big
+    x[::2, 2::32] = 2.0 ** -133
+    return synth.bf16_bits(x.astype(np.float32))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m,k", [(5, 256), (48, 4096), (320, 2880)])
+def test_rotated_wide_range_blocks(fmt, m, k):
+    print(f"[recipe-rot] wide-range fmt={fmt} m={m} k={k}", flush=True)
+    bits = _wide_range_rows(m, k, 7 * m + k)
+    ref = _ref(fmt, bits, True, False)
+    for lay in (fp4.CANONICAL, fp4.TILED):
+        q = fp4.fp4_quantize_act(to_dev(bits), _flags(fmt, True, False), layout=lay)
+        if lay == fp4.TILED:
+            q = fp4.fp4_export_canonical(q)
+        assert_canonical_equal(q, ref, F[fmt], what=f"rotated wide-range {m}x{k} layout {lay}")
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("n,k", [(33, 96), (520, 2880)])
 def test_rotated_weight_cache(fmt, n, k):

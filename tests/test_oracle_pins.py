@@ -543,12 +543,47 @@ def _bf16_rne_of_f32(v32: np.ndarray) -> np.ndarray:
     return (upper + up).astype(np.uint16)
 
 
+def _rn_bf16_exact(v: Fraction) -> int:
+    """bf16 bits of the real v rounded to nearest, ties to even (exact rational
+    arithmetic): 8 significant bits from 2^-126 up, a fixed quantum of 2^-133
+    below; +0 for an exact zero, the sign kept when a nonzero value rounds to 0."""
+    if v == 0:
+        return 0
+    neg, a = v < 0, abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1                                       # e = floor(log2 a)
+    q = max(e - 7, -133)
+    n = a / Fraction(2) ** q
+    r = n.numerator // n.denominator
+    rem = n - r
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and r % 2 == 1):
+        r += 1
+    bits = int(np.array([float(r * Fraction(2) ** q)], np.float32).view(np.uint32)[0]) >> 16
+    return bits | (0x8000 if neg else 0)
+
+
+def _rotate_exact(xbits: np.ndarray, bs: int) -> np.ndarray:
+    """The rotation as defined: RN_bf16(c * (H x)) per block with scipy's
+    Sylvester matrix, c = the binary32 norm, every sum and product exact."""
+    from scipy.linalg import hadamard as sylvester
+    h = sylvester(bs).astype(int)
+    c = Fraction(float(oracle.hadamard_norm(bs)))
+    vals = bf16_to_f32(xbits).astype(np.float64)
+    out = np.zeros(xbits.shape, dtype=np.uint16)
+    for r in range(xbits.shape[0]):
+        for b in range(xbits.shape[1] // bs):
+            xs = [Fraction(float(v)) for v in vals[r, b * bs:(b + 1) * bs]]
+            for i in range(bs):
+                acc = sum((xs[j] if h[i, j] > 0 else -xs[j]) for j in range(bs))
+                out[r, b * bs + i] = _rn_bf16_exact(c * acc)
+    return out
+
+
 @pytest.mark.parametrize("bs", [16, 32])
 def test_hadamard_matches_exact_sylvester_product(bs):
-    """Integer-valued blocks: the butterfly network equals the exact product
-    with scipy's Sylvester Hadamard matrix (every partial sum is an integer
-    below 2^24, so the binary32 transform is exact); then one binary32
-    multiply by the norm and one bf16 rounding."""
+    """Integer-valued blocks: the rotation equals the exact integer product with
+    scipy's Sylvester Hadamard matrix, times the norm, rounded once to bf16."""
     from scipy.linalg import hadamard as sylvester
     rng = np.random.default_rng(31)
     xi = rng.integers(-100, 101, (24, 4 * bs))
@@ -556,11 +591,45 @@ def test_hadamard_matches_exact_sylvester_product(bs):
     assert np.array_equal(bf16_to_f32(x), xi.astype(np.float32))
     h = sylvester(bs).astype(np.int64)
     s = (xi.reshape(24, 4, bs) @ h.T).reshape(24, 4 * bs)           # exact integers
-    expect = _bf16_rne_of_f32(s.astype(np.float32) * oracle.hadamard_norm(bs))
+    c = Fraction(float(oracle.hadamard_norm(bs)))
+    expect = np.array([[_rn_bf16_exact(int(v) * c) for v in row] for row in s], dtype=np.uint16)
     assert np.array_equal(oracle.hadamard(x, bs), expect)
-    if bs == 16:   # the norm is exactly 1/4: a single rounding of the exact value
-        exact = s / 4.0
-        assert np.array_equal(oracle.hadamard(x, bs), _bf16_rne_of_f32(exact.astype(np.float32)))
+    if bs == 16:   # the norm is exactly 1/4: the float32 quotient is exact too
+        assert np.array_equal(oracle.hadamard(x, bs), _bf16_rne_of_f32((s / 4.0).astype(np.float32)))
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_hadamard_bit_exact_on_general_data(bs):
+    """General (non-integer) inputs, bit for bit against the exact rational
+    product: Gaussian blocks over many binades; blocks whose magnitudes span
+    up to 2^250 with large values that cancel exactly (an order-dependent
+    binary32 or binary64 transform would lose the small ones); values whose
+    rotated sum is a bf16 rounding tie; subnormal inputs whose rotation
+    rounds to a signed zero."""
+    rng = np.random.default_rng(11 + bs)
+    gauss = rng.standard_normal((6, 4 * bs)) * 2.0 ** rng.uniform(-30, 30, (6, 1))
+    wide = np.zeros((6, 4 * bs))
+    for r in range(6):
+        e = rng.integers(-133, 119, 4 * bs)
+        wide[r] = rng.choice([-1.0, 1.0], 4 * bs) * rng.integers(1, 256, 4 * bs) * 2.0 ** (e - 7)
+        big = rng.integers(60, 110)
+        wide[r, 0], wide[r, 1] = 2.0 ** big, -(2.0 ** big)    # cancel in the first row of H
+        wide[r, bs + 2], wide[r, bs + 3] = 3.0 * 2.0 ** big, 3.0 * 2.0 ** big
+    ties = np.zeros((2, 4 * bs))
+    ties[:, 0], ties[0, 1], ties[1, 1], ties[:, 2] = 256.0, 1.0, 3.0, 0.0   # sums 257, 259
+    tiny = np.zeros((2, 4 * bs))
+    tiny[0, 1] = 2.0 ** -133                    # H[i][1] = -1 for odd i
+    tiny[1, :bs] = rng.integers(1, 128, bs) * 2.0 ** -133
+    x = np.concatenate([gauss, wide, ties, tiny]).astype(np.float64)
+    xb = bf16_bits(x.astype(np.float32))
+    # the wide blocks' values were chosen bf16-exact except where float32 rounds
+    got = oracle.hadamard(xb, bs)
+    want = _rotate_exact(xb, bs)
+    assert np.array_equal(got, want)
+    assert np.any(got[14:16] == 0x8000)          # a negative result that rounds to zero
+    if bs == 16:
+        assert bf16_to_f32(got[12:13, :1])[0, 0] == 64.0    # 257 / 4: tie to even
+        assert bf16_to_f32(got[13:14, :1])[0, 0] == 65.0    # 259 / 4: tie to even
 
 
 def test_hadamard_norm_is_nearest_binary32():
@@ -608,9 +677,8 @@ def test_hadamard_is_an_involution_on_exact_blocks():
 
 @pytest.mark.parametrize("bs", [16, 32])
 def test_hadamard_error_bound_on_gaussian_data(bs):
-    """General inputs: within one bf16 rounding plus the binary32 transform's
-    error (log2(bs) additions and one multiply, each <= 2^-24 relative of the
-    running magnitudes) of the exact real rotation."""
+    """General inputs: within one bf16 rounding of the real rotation with the
+    exact 1/sqrt(bs) (the binary32 norm differs from it by < 2^-25 relative)."""
     from scipy.linalg import hadamard as sylvester
     rng = np.random.default_rng(5)
     x = bf16_bits((rng.standard_normal((16, 8 * bs)) * 2.0 ** rng.uniform(-10, 10, (16, 1)))
@@ -619,7 +687,7 @@ def test_hadamard_error_bound_on_gaussian_data(bs):
     exact = (xv @ sylvester(bs).T.astype(np.float64)) / math.sqrt(bs)   # exact to ~2^-50
     mag = np.abs(xv).sum(axis=-1, keepdims=True) / math.sqrt(bs)
     got = bf16_to_f32(oracle.hadamard(x, bs)).astype(np.float64).reshape(16, 8, bs)
-    bound = 2.0 ** -8 * np.abs(exact) + (math.log2(bs) + 2) * 2.0 ** -24 * mag * 1.01
+    bound = 2.0 ** -8 * np.abs(exact) + 2.0 ** -25 * mag * 1.01 + 2.0 ** -134
     assert np.all(np.abs(got - exact) <= bound)
 
 
