@@ -1,20 +1,28 @@
 """Benchmark of the W4A4 block-scaled FP4 linear on one MI355X.
 
-Default workload (one step): the decode-shaped NVFP4 W4A4 linear at every
-M in {1, 8, 32} and (K, N) in {(5120, 5120), (5120, 17408), (17408, 5120)} --
-nine fp4_linear calls (activation quantization + GEMM). Weights are bf16
-~N(0, 0.02) quantized once before timing; activations are bf16 ~N(0, 1)
-quantized inside every call. Each weight exists in several copies that the
-steps rotate through, so the bytes between two uses of one copy exceed the
-256 MB Infinity Cache and the weight stream comes from HBM.
+Default workload (one step): one square NVFP4 W4A4 linear, M = N = K = 16384
+(fp4_linear: activation quantization + GEMM), the largest single-GPU
+configuration of the metric's compute-bound half. Operands are bf16 ~N(0, 1);
+the weight is quantized once before timing, the activations inside every call.
+The same run times the GEMM alone on pre-quantized activations (fp4_gemm).
+
+Other workloads (--workload): square4096, square8192 (the rest of the square
+sweep), decode (M in {1, 8, 32} x (K, N) in {(5120, 5120), (5120, 17408),
+(17408, 5120)}: nine calls per step, each weight in enough copies that every
+shape's copies exceed 768 MB and consecutive calls never reuse one, so the
+weight stream comes from HBM rather than the 256 MB Infinity Cache), prefill
+(a Llama-style 3B block at M = 4096), single (A[16,256] x W[256,256]) and
+forward (a synthetic 24-layer forward at M = 1, 8, 32, 128).
 
 Prints one JSON line: throughput incl. activation quantization (TFLOP/s), a
-roofline entry for the dominant kernel (decode GEMM, HBM-bound: algorithmic
-bytes per launch over its average duration, timed with HIP events on the
-launch stream) and the CPU oracle timed on a bounded sample of the same work.
+roofline entry for the dominant kernel (square/prefill: the tile GEMM against
+the FP4 matrix peak, NVFP4 also against the f16 ceiling its exact products run
+at; decode: the skinny GEMM against HBM bandwidth; algorithmic work per launch
+over its average duration, timed with HIP events on the launch stream) and the
+CPU oracle timed on a bounded sample of the same work on every host core.
 
     python bench.py [--steps K] [--warmup W] [--fmt nvfp4|mxfp4]
-                    [--workload decode|prefill|square8192|single|forward]
+                    [--workload square16384|square8192|square4096|decode|prefill|single|forward]
 """
 from __future__ import annotations
 
@@ -32,25 +40,31 @@ HBM_PEAK_GBS = 8000.0              # MI355X HBM3E, published
 FP4_PEAK_TFLOPS = 10100.0          # dense FP4 MFMA, published
 F16_PEAK_TFLOPS = 2500.0           # dense f16/bf16 MFMA, published
 METRIC = "W4A4 NVFP4 GEMM TFLOPS incl. act-quant; % FP4 MFMA peak / % HBM BW"
-ROTATE_BYTES = 768 << 20           # bytes touched between two uses of one weight copy
+ROTATE_BYTES = 768 << 20           # bytes of one shape's weight copies (decode rotation)
+WORKLOADS = ["square16384", "square8192", "square4096", "decode", "prefill", "single", "forward"]
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--fmt", default="nvfp4", choices=["nvfp4", "mxfp4"])
     p.add_argument("--recipe", default="", choices=["", "rotate", "oas", "rotate+oas"],
                    help="quantization recipe flags for weights and activations: block "
                         "Hadamard rotation, MXFP4 overflow-aware exponent")
     p.add_argument("--w4a16", action="store_true",
                    help="time the weight-only linear (bf16 activations x FP4 weights) instead")
-    p.add_argument("--workload", default="decode",
-                   choices=["decode", "prefill", "square8192", "single", "forward"])
+    p.add_argument("--workload", default="square16384", choices=WORKLOADS)
+    p.add_argument("--api", default="linear", choices=["linear", "canonical"],
+                   help="linear: fp4_linear per call; canonical: fp4_quantize_act into the canonical "
+                        "layout, then fp4_gemm (the two public calls)")
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     p.add_argument("--kernel-reps", type=int, default=50)
-    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target wall time of the oracle's GEMM sample in the CPU baseline")
+    p.add_argument("--cpu-threads", type=int, default=0,
+                   help="oracle threads (default: the host cores this process may use, at most 16)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="also run one plain device copy of this many MiB (a reference for "
@@ -75,8 +89,9 @@ def workload_configs(name):
     if name == "prefill":
         return [(synth.PREFILL_M, k, n) for (k, n) in synth.PREFILL_LAYERS.values()], \
             "prefill-shaped W4A4 GEMMs of a Llama-style 3B block, M=4096"
-    if name == "square8192":
-        return [(8192, 8192, 8192)], "square W4A4 GEMM M=N=K=8192"
+    if name.startswith("square"):
+        n = int(name[len("square"):])
+        return [(n, n, n)], f"square W4A4 linear M=N=K={n}"
     return [(16, 256, 256)], "single W4A4 GEMM A[16,256] x W[256,256]"
 
 
@@ -104,16 +119,18 @@ def kernel_source_hash():
 
 
 def variant_tag(args):
-    """Profile-file suffix of a run: the weight-only linear and the recipe flags
-    have summaries of their own ("" for plain W4A4)."""
-    parts = (["w4a16"] if args.w4a16 else []) + ([args.recipe.replace("+", "_")] if args.recipe else [])
+    """Profile-file suffix of a run: the weight-only linear, the recipe flags and
+    the two-call canonical API have summaries of their own ("" for plain W4A4)."""
+    parts = (["w4a16"] if args.w4a16 else []) + ([args.recipe.replace("+", "_")] if args.recipe else []) + \
+        (["canonical"] if getattr(args, "api", "linear") == "canonical" else [])
     return "".join("_" + x for x in parts)
 
 
 def variant_flags(args):
     """The bench.py flags that select the same variant (for the commands quoted
     in the summaries)."""
-    return (" --w4a16" if args.w4a16 else "") + (f" --recipe {args.recipe}" if args.recipe else "")
+    return (" --w4a16" if args.w4a16 else "") + (f" --recipe {args.recipe}" if args.recipe else "") + \
+        (" --api canonical" if getattr(args, "api", "linear") == "canonical" else "")
 
 
 def traffic_path(workload, fmt, tag=""):
@@ -319,8 +336,20 @@ def main():
 
     # ---- inputs: weights quantized once (several copies), activations per config
     shapes = sorted({(k, n) for (_, k, n) in configs})
-    step_w_bytes = sum(n * (k // 2 + k // (16 if fmt == 0 else 32)) for (k, n) in shapes)
-    copies = max(1, -(-ROTATE_BYTES // step_w_bytes)) if args.workload == "decode" else 1
+    bs = 16 if fmt == 0 else 32
+    shape_bytes = {(k, n): n * (k // 2 + k // bs) for (k, n) in shapes}
+    uses = {kn: sum(1 for (_, k, n) in configs if (k, n) == kn) for kn in shapes}
+    # Decode: each shape's copies total >= ROTATE_BYTES and a step's calls of
+    # one shape take consecutive copies, so a copy is reused only after all of
+    # that shape's copies (>= 768 MB) have been read. Every shape cycles
+    # through its copies in the same number of steps (`cycle`), so a graph of
+    # `cycle` steps (or a multiple) leaves each copy's reuse distance intact
+    # across replays.
+    if args.workload == "decode":
+        cycle = max(-(-ROTATE_BYTES // (shape_bytes[kn] * uses[kn])) for kn in shapes)
+        copies = {kn: cycle * uses[kn] for kn in shapes}
+    else:
+        cycle, copies = 1, {kn: 1 for kn in shapes}
     weights, w_host, a_host = {}, {}, {}
     layer_of = {kn: name for name, kn in synth.PREFILL_LAYERS.items()}
     for (k, n) in shapes:
@@ -328,13 +357,13 @@ def main():
             w_bits = synth.decode_inputs(1, k, n, seed=0)[1]
         elif args.workload == "prefill":
             w_bits = synth.prefill_inputs(layer_of[(k, n)], seed=0, m=16)[1]
-        elif args.workload == "square8192":
+        elif args.workload.startswith("square"):
             w_bits = synth.square_inputs(k, seed=0)[1]
         else:
             w_bits = synth.single_gemm_inputs(0)[1]
         w_host[(k, n)] = w_bits
         w_dev = to_dev(w_bits)
-        weights[(k, n)] = [fp4.fp4_quantize_weight(w_dev, qfmt) for _ in range(copies)]
+        weights[(k, n)] = [fp4.fp4_quantize_weight(w_dev, qfmt) for _ in range(copies[(k, n)])]
         del w_dev
     xs, outs, wss = {}, {}, {}
     for (m, k, n) in configs:
@@ -342,7 +371,7 @@ def main():
             a_bits = synth.normal((m, k), 1.0, 0, 2 * k + 1)   # the activation decode_inputs draws
         elif args.workload == "prefill":
             a_bits = synth.prefill_inputs(layer_of[(k, n)], seed=0, m=m)[0]
-        elif args.workload == "square8192":
+        elif args.workload.startswith("square"):
             a_bits = synth.square_inputs(k, seed=0)[0]
         else:
             a_bits = synth.single_gemm_inputs(0)[0]
@@ -361,16 +390,35 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    qcanon, qws, gws = {}, {}, {}
+    if args.api == "canonical":
+        for cfg in configs:
+            m, k, n = cfg
+            qcanon[cfg] = fp4.Fp4Tensor(qfmt, fp4.CANONICAL, m, k, dev)
+            qws[cfg] = torch.zeros(max(1, fp4.lib().fp4_quantize_workspace_bytes(qfmt, m, k)),
+                                   dtype=torch.uint8, device=dev)
+            gws[cfg] = torch.empty(max(16, fp4.lib().fp4_gemm_workspace_bytes(qfmt, m, n, k)),
+                                   dtype=torch.uint8, device=dev)
+
     def linear(cfg, w):
         if args.w4a16:
             fp4.fp4_linear_w4a16(xs[cfg], w, out=outs[cfg])
+        elif args.api == "canonical":
+            fp4.fp4_quantize_act(xs[cfg], qfmt, workspace=qws[cfg], out=qcanon[cfg])
+            fp4.fp4_gemm(qcanon[cfg], w, out=outs[cfg], workspace=gws[cfg])
         else:
             fp4.fp4_linear(xs[cfg], w, out=outs[cfg], workspace=wss[cfg])
 
+    # the j-th call of a shape in step i takes copy (i * uses + j) mod copies
+    slot = {}
+    for cfg in configs:
+        kn = cfg[1:]
+        slot[cfg] = sum(1 for c in configs[:configs.index(cfg)] if c[1:] == kn)
+
     def step(i):
         for cfg in configs:
-            m, k, n = cfg
-            linear(cfg, weights[(k, n)][i % copies])
+            kn = cfg[1:]
+            linear(cfg, weights[kn][(i * uses[kn] + slot[cfg]) % copies[kn]])
 
     if args.pmc_step:
         step(0)
@@ -378,22 +426,22 @@ def main():
         print(json.dumps({"pmc_step": desc, "configs": configs}), flush=True)
         return
 
-    # ---- graphs: a long graph replays G consecutive steps (the weight copies
-    # in turn), so a graph launch is paid once per G steps, as in a serving
-    # loop that captures many layers in one graph; one-step graphs (one per
-    # copy) run any remainder, so that exactly the requested steps run.
+    # ---- graphs: a long graph replays G consecutive steps, so a graph launch
+    # is paid once per G steps, as in a serving loop that captures many layers
+    # in one graph; one-step graphs run any remainder, so that exactly the
+    # requested steps run (G is a multiple of the copy cycle).
     use_graph = not args.no_graph
-    G = copies * max(1, -(-16 // copies))
+    G = cycle * max(1, -(-16 // cycle))
     one, long_graph = [], None
     if use_graph:
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            for i in range(copies):
+            for i in range(cycle):
                 step(i)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
-        for i in range(copies):
+        for i in range(cycle):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 step(i)
@@ -413,7 +461,7 @@ def main():
         for _ in range(q):
             long_graph.replay()
         for i in range(r):
-            one[i % copies].replay()
+            one[i % cycle].replay()
 
     run_steps(args.warmup)
     torch.cuda.synchronize()
@@ -429,9 +477,10 @@ def main():
     flops = sum(2.0 * m * n * k for (m, k, n) in configs)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
 
-    # ---- dominant kernel: the skinny GEMM (fused with the activation
-    # quantization when fp4_linear runs as one launch), timed alone: R
-    # back-to-back launches captured in a graph, HIP events on the launch stream.
+    # ---- dominant kernel: the GEMM (fused with the activation quantization
+    # when fp4_linear runs as one launch), timed alone: R back-to-back launches
+    # captured in a graph, HIP events on the launch stream; the launches rotate
+    # over the shape's weight copies as the steps do.
     def graph_time(fn, reps):
         fn(0)
         torch.cuda.synchronize()
@@ -450,14 +499,13 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / reps
 
-    reps = max(copies, args.kernel_reps)
     kern, per_cfg = {}, []
-    bs = 16 if fmt == 0 else 32
     for cfg in configs:
         m, k, n = cfg
-        wl = weights[(k, n)]
-        w_bytes = n * (k // 2 + k // bs)
-        lin_us = graph_time(lambda r: linear(cfg, wl[r % copies]), reps)
+        wl, nc = weights[(k, n)], copies[(k, n)]
+        reps = max(nc, args.kernel_reps) if m * n * k < (1 << 36) else max(nc, 5)
+        w_bytes = shape_bytes[(k, n)]
+        lin_us = graph_time(lambda r: linear(cfg, wl[r % nc]), reps)
         if args.w4a16:
             name = ("k_w4a16_decode<%s,MG=%d>" % (args.fmt, 1 if m <= 16 else 2) if m <= 32
                     else "k_w4a16_tile<%s>" % args.fmt)
@@ -476,15 +524,18 @@ def main():
             else:   # LDS-staged tiles; 256 x 256 when that fills the 256 CUs
                 big = -(-m // 256) * -(-n // 256) >= 256
                 name = "k_gemm_tile<%s,%s>" % (args.fmt, "256x256" if big else "128x128")
-            us = graph_time(lambda r: fp4.fp4_gemm(qa, wl[r % copies], out=outs[cfg]), reps)
+            us = graph_time(lambda r: fp4.fp4_gemm(qa, wl[r % nc], out=outs[cfg]), reps)
             nbytes = w_bytes + m * (k // 2 + k // bs) + 2 * m * n  # W + FP4 A + bf16 C
+            del qa
         d = kern.setdefault(name, {"launches": 0, "us": 0.0, "bytes": 0.0, "flops": 0.0})
         d["launches"] += 1
         d["us"] += us
         d["bytes"] += nbytes
         d["flops"] += 2.0 * m * n * k
         per_cfg.append({"m": m, "k": k, "n": n, "kernel": name, "kernel_us": round(us, 3),
-                        "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "linear_us": round(lin_us, 3)})
+                        "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                        "TFLOPs": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 1),
+                        "linear_us": round(lin_us, 3), "weight_copies": nc})
     tot_us = sum(d["us"] for d in kern.values())
     tot_launch = sum(d["launches"] for d in kern.values())
     if args.workload == "decode":
@@ -493,9 +544,12 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
     else:
         achieved = sum(d["flops"] for d in kern.values()) / (tot_us * 1e-6) / 1e12
-        peak = FP4_PEAK_TFLOPS if fmt == 1 else F16_PEAK_TFLOPS
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": None}
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / FP4_PEAK_TFLOPS, 4), "traffic": None}
+        if fmt == 0 and not args.w4a16:
+            # exact NVFP4 products (q * s_b: up to 6 significant bits) run on the
+            # f16 matrix instructions, whose dense peak bounds this kernel
+            roof["f16_ceiling"] = {"peak": F16_PEAK_TFLOPS, "frac": round(achieved / F16_PEAK_TFLOPS, 4)}
     # HBM bytes per launch from the committed counter summary of this variant
     roof["traffic"] = stored_traffic(args.workload, args.fmt, variant_tag(args))
     # rocprofv3 MfmaUtil / VALUBusy / LdsUtil (percent) of the same kernels
@@ -503,9 +557,24 @@ def main():
     roof.update({"kernel": " + ".join(sorted(kern)), "avg_launch_us": round(tot_us / tot_launch, 3),
                  "launches_per_step": tot_launch,
                  "per_kernel": {nm: {"launches": d["launches"], "avg_us": round(d["us"] / d["launches"], 3),
-                                     "GBps": round(d["bytes"] / (d["us"] * 1e-6) / 1e9, 1)}
+                                     "GBps": round(d["bytes"] / (d["us"] * 1e-6) / 1e9, 1),
+                                     "TFLOPs": round(d["flops"] / (d["us"] * 1e-6) / 1e12, 1)}
                                 for nm, d in kern.items()},
                  "per_config": per_cfg})
+    config = {"workload": desc + (" (weight-only: bf16 activations)" if args.w4a16 else "") +
+              (" (fp4_quantize_act canonical + fp4_gemm)" if args.api == "canonical" else ""),
+              "format": args.fmt, "recipe": args.recipe or "none",
+              "launch": ("hip-graph replay, %d steps per graph" % G) if use_graph else "eager",
+              "weight_copies": {f"{k}x{n}": copies[(k, n)] for (k, n) in shapes},
+              "calls_per_step": len(configs),
+              "fraction_of_fp4_peak": round(tflops / FP4_PEAK_TFLOPS, 6)}
+    if args.workload.startswith("square") or args.workload == "prefill":
+        # the sweep's two timings: GEMM alone on pre-quantized activations, and
+        # quantization + GEMM (the value)
+        gemm_us = sum(c["kernel_us"] for c in per_cfg)
+        config["gemm_only"] = {"us_per_step": round(gemm_us, 3),
+                               "TFLOPs": round(flops / (gemm_us * 1e-6) / 1e12, 1)}
+        config["quant_plus_gemm"] = {"us_per_step": round(ms_per_step * 1e3, 3), "TFLOPs": round(tflops, 1)}
 
     result = {
         "metric": METRIC,
@@ -520,11 +589,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if args.w4a16 else ("f16" if fmt == 0 else "fp4"),
         "data": "synthetic",
-        "config": {"workload": desc + (" (weight-only: bf16 activations)" if args.w4a16 else ""),
-                   "format": args.fmt, "recipe": args.recipe or "none",
-                   "launch": ("hip-graph replay, %d steps per graph" % G) if use_graph else "eager",
-                   "weight_copies": copies, "calls_per_step": len(configs),
-                   "fraction_of_fp4_peak": round(tflops / FP4_PEAK_TFLOPS, 6)},
+        "config": config,
         "roofline": roof,
         "wall_s": round(wall, 3),
     }
@@ -655,48 +720,114 @@ def bench_forward(args, fmt, qfmt):
     print(json.dumps(result), flush=True)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(configs, fmt, args, a_host, w_host):
-    """The CPU oracle (plain C, one thread) on a bounded sample of the same
-    linear calls: full activation quantization plus the k-ordered binary64 GEMM
-    on a subset of output columns (weights quantized beforehand, untimed, as on
-    the GPU). Reported in the metric's unit: sampled flops / oracle seconds."""
+    """The CPU oracle (plain C, binary64) on the same linear calls, on every
+    host core this process may use (threads over row or column slices; the
+    oracle's C calls release the interpreter lock). Per call: the activation
+    quantization of the whole tensor (NVFP4 dynamic: the tensor's maximum, then
+    row slices quantized with that scale, which the pins show equals the
+    one-piece dynamic quantization), then the k-ordered binary64 GEMM on a
+    sample: every output when it fits the time budget, else the first R <= 64
+    activation rows (M > 128) or the first output columns (M <= 128), with the
+    full call's time extrapolated linearly from the sample. Weights are
+    quantized beforehand, untimed, as on the GPU. Reported in the metric's
+    unit: the calls' flops over their (extrapolated) oracle time."""
+    import concurrent.futures as cf
+    import numpy as np
     import oracle
+    threads = args.cpu_threads or min(16, len(os.sched_getaffinity(0)))
     rk = {"rotate": "rotate" in args.recipe, "oas": "oas" in args.recipe}
+    pool = cf.ThreadPoolExecutor(max_workers=threads)
+
+    def chunks(n, parts):
+        step = -(-n // parts)
+        return [(i, min(n, i + step)) for i in range(0, n, step)]
+
+    def quantize_par(bits):
+        """The oracle's quantization of a whole tensor, split over row slices."""
+        if fmt == oracle.NVFP4 and not rk["rotate"]:
+            st = float(oracle.tensor_scale(bits))
+            parts = list(pool.map(lambda rr: oracle.quantize(fmt, bits[rr[0]:rr[1]], mode=oracle.STATIC,
+                                                             static_scale=st),
+                                  chunks(bits.shape[0], threads)))
+            return oracle.Quantized(fmt, np.concatenate([q.codes for q in parts]),
+                                    np.concatenate([q.scales for q in parts]), st, bits.shape[1])
+        if fmt == oracle.NVFP4:   # rotated dynamic: the maximum is over the rotated tensor
+            rot = np.concatenate(list(pool.map(lambda rr: oracle.hadamard(bits[rr[0]:rr[1]], 16),
+                                               chunks(bits.shape[0], threads))))
+            st = float(oracle.tensor_scale(rot))
+            parts = list(pool.map(lambda rr: oracle.quantize(fmt, rot[rr[0]:rr[1]], mode=oracle.STATIC,
+                                                             static_scale=st),
+                                  chunks(bits.shape[0], threads)))
+            return oracle.Quantized(fmt, np.concatenate([q.codes for q in parts]),
+                                    np.concatenate([q.scales for q in parts]), st, bits.shape[1])
+        parts = list(pool.map(lambda rr: oracle.quantize(fmt, bits[rr[0]:rr[1]], **rk),
+                              chunks(bits.shape[0], threads)))
+        return oracle.Quantized(fmt, np.concatenate([q.codes for q in parts]),
+                                np.concatenate([q.scales for q in parts]), 1.0, bits.shape[1])
+
+    def gemm_par(qa, qw):
+        """k-ordered binary64 GEMM, the weight's rows (output columns) split over threads."""
+        def run(cc):
+            sub = oracle.Quantized(fmt, qw.codes[cc[0]:cc[1]], qw.scales[cc[0]:cc[1]], qw.tensor_scale, qw.k)
+            if args.w4a16:
+                return oracle.gemm_w4a16(qa, sub)
+            return oracle.gemm_loop(qa, sub)
+        list(pool.map(run, chunks(qw.rows, threads)))
+
+    def rows_of(q, r):
+        return oracle.Quantized(fmt, q.codes[:r], q.scales[:r], q.tensor_scale, q.k)
+
     budget = args.cpu_seconds / len(configs)
-    tot_flops, tot_s, parts = 0.0, 0.0, []
-    wq_cache = {}
+    tot_flops, tot_s, parts, wq_cache = 0.0, 0.0, [], {}
     for (m, k, n) in configs:
         a_bits, w_bits = a_host[(m, k, n)], w_host[(k, n)]
         if (k, n) not in wq_cache:
-            wq_cache[(k, n)] = oracle.quantize(fmt, w_bits, **rk)
+            wq_cache[(k, n)] = quantize_par(w_bits)
         qw = wq_cache[(k, n)]
-        # estimate the per-output cost, then size the column sample to the budget
-        def run(cols):   # activation quantization (W4A4) + the product on `cols` columns
-            sub = oracle.Quantized(fmt, qw.codes[:cols], qw.scales[:cols], qw.tensor_scale, k)
-            if args.w4a16:
-                oracle.gemm_w4a16(a_bits, sub)
-            else:
-                oracle.gemm_loop(oracle.quantize(fmt, a_bits, **rk), sub)
         t = time.perf_counter()
-        if not args.w4a16:
-            oracle.quantize(fmt, a_bits, **rk)
+        qa = a_bits if args.w4a16 else quantize_par(a_bits)
         t_q = time.perf_counter() - t
-        probe = min(n, 4)
+        # probe the GEMM rate on a small sample, then size the timed sample
+        pr, pc = min(m, 2), min(n, 8 * threads)
+        probe_a = a_bits[:pr] if args.w4a16 else rows_of(qa, pr)
         t = time.perf_counter()
-        run(probe)
-        per_col = max((time.perf_counter() - t - t_q) / probe, 1e-9)
-        cols = int(max(1, min(n, (budget - t_q) / per_col)))
+        gemm_par(probe_a, rows_of(qw, pc))
+        per_out = max((time.perf_counter() - t) / (pr * pc), 1e-9)
+        full = m * n * per_out
+        if full <= budget:
+            rows, cols = m, n
+        elif m > 128:
+            rows, cols = max(1, min(64, int(budget / (n * per_out)))), n
+        else:
+            rows, cols = m, max(threads, min(n, int(budget / (m * per_out))))
+        sample_a = a_bits[:rows] if args.w4a16 else rows_of(qa, rows)
         t = time.perf_counter()
-        run(cols)
-        dt = time.perf_counter() - t
-        fl = 2.0 * m * cols * k
-        tot_flops += fl
-        tot_s += dt
-        parts.append(f"M={m},K={k}: {cols}/{n} cols")
-    return {"value": tot_flops / tot_s / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": "per call: " + ("" if args.w4a16 else "full activation quantization + ") +
-                      "k-ordered FP64 GEMM on the first columns of the pre-quantized weight (" +
-                      "; ".join(parts) + f"); {tot_s:.1f} s"}
+        gemm_par(sample_a, rows_of(qw, cols))
+        t_g = time.perf_counter() - t
+        est = t_q + t_g * (m / rows) * (n / cols)
+        tot_flops += 2.0 * m * n * k
+        tot_s += est
+        what = "all outputs" if (rows, cols) == (m, n) else \
+            (f"{rows}/{m} rows" if rows < m else f"{cols}/{n} columns")
+        parts.append(f"{m}x{k}x{n}: quantize {t_q:.2f} s, GEMM on {what} {t_g:.2f} s")
+    pool.shutdown()
+    return {"value": tot_flops / tot_s / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "sample": ("per call: " + ("" if args.w4a16 else "activation quantization of the whole tensor + ")
+                       + "k-ordered binary64 GEMM on a sample, the call's time extrapolated from it ("
+                       + "; ".join(parts) + f"); total {tot_s:.1f} s estimated for the full calls")}
 
 
 if __name__ == "__main__":

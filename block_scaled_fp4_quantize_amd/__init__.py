@@ -181,12 +181,16 @@ def fp4_quantize_weight(w: torch.Tensor, fmt=NVFP4) -> Fp4Tensor:
 
 
 def fp4_quantize_act(a: torch.Tensor, fmt=NVFP4, static_scale: torch.Tensor | None = None,
-                     layout: int = CANONICAL, workspace: torch.Tensor | None = None) -> Fp4Tensor:
+                     layout: int = CANONICAL, workspace: torch.Tensor | None = None,
+                     out: Fp4Tensor | None = None) -> Fp4Tensor:
+    """Quantize activations into a new tensor, or into `out` (same format,
+    layout and shape)."""
     fmt = _fmt(fmt)
     a = _bf16_2d(a, "a")
     m, k = a.shape
     L = lib()
-    out = Fp4Tensor(fmt, layout, m, k, a.device)
+    if out is None:
+        out = Fp4Tensor(fmt, layout, m, k, a.device)
     nws = L.fp4_quantize_workspace_bytes(fmt, m, k)
     ws = workspace
     if ws is None:   # zero-filled once, as the C ABI requires
@@ -203,8 +207,9 @@ def fp4_gemm(a: Fp4Tensor, w: Fp4Tensor, out: torch.Tensor | None = None,
     if out is None:
         out = torch.empty(m, n, dtype=torch.bfloat16, device=a.device)
     nws = L.fp4_gemm_workspace_bytes(a.fmt, m, n, a.k)
-    if workspace is None and nws > 0:   # zero-filled once, as the C ABI requires
-        workspace = torch.zeros(nws, dtype=torch.uint8, device=a.device)
+    if workspace is None and nws > 0 and a.layout == CANONICAL:
+        # room for the tiled copy of large canonical activations
+        workspace = torch.empty(nws, dtype=torch.uint8, device=a.device)
     _check(L.fp4_gemm(ctypes.byref(a.desc), ctypes.byref(w.desc), _ptr(out), out.stride(0),
                       _ptr(workspace), 0 if workspace is None else workspace.numel(),
                       _stream(a.device)))

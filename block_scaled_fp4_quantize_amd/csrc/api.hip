@@ -159,6 +159,21 @@ fp4_status run_quant(int32_t fmt, int tiled, const void *x, int64_t rows, int64_
   return FP4_OK;
 }
 
+// fp4_gemm's workspace: canonical activations with M > kDecodeMaxM are
+// copied into the tiled layout there, so that the LDS-staged tile kernel runs.
+struct RetileLayout {
+  size_t codes, scales, total;
+};
+RetileLayout retile_layout(int32_t fmt, int64_t m, int64_t k) {
+  RetileLayout L{0, 0, 0};
+  if (m <= kDecodeMaxM) return L;
+  const int64_t mp = round_up(m, 16), kp = k_pad(k);
+  L.codes = 0;
+  L.scales = align256((size_t)(mp * kp / 2));
+  L.total = align256(L.scales + (size_t)(mp * kp / block_of(base_fmt(fmt))));
+  return L;
+}
+
 fp4_status run_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c, int64_t ldc,
                     hipStream_t stream) {
   GemmArgs g;
@@ -267,14 +282,13 @@ fp4_status fp4_quantize_act(int32_t fmt, const void *a_bf16, int64_t m, int64_t 
 }
 
 size_t fp4_gemm_workspace_bytes(int32_t fmt, int64_t m, int64_t n, int64_t k) {
-  (void)fmt; (void)m; (void)n; (void)k;
-  return 0;
+  (void)n;
+  if (!valid_fmt(fmt) || m <= 0 || k <= 0) return 0;
+  return retile_layout(fmt, m, k).total;
 }
 
 fp4_status fp4_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c_bf16, int64_t ldc,
                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   fp4_status st;
   if ((st = check_tensor(a, "a")) != FP4_OK) return st;
   if ((st = check_tensor(w, "w")) != FP4_OK) return st;
@@ -291,7 +305,27 @@ fp4_status fp4_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c_bf16, int6
   if (a->rows <= kDecodeMaxM && a->layout == FP4_LAYOUT_CANONICAL &&
       a->rows * std::max(a->codes_pitch, a->scales_pitch) >= (int64_t(1) << 31))
     return fail(FP4_ERR_SHAPE, "a: rows * pitch must stay below 2^31 bytes for M <= %d", kDecodeMaxM);
+  if (workspace && !aligned16(workspace))
+    return fail(FP4_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
   if ((st = check_device()) != FP4_OK) return st;
+  const RetileLayout R = retile_layout(a->fmt, a->rows, a->cols);
+  if (a->layout == FP4_LAYOUT_CANONICAL && R.total && workspace && workspace_bytes >= R.total) {
+    // canonical activations of a large M: tiled copy in the workspace, then
+    // the tile kernel (without the workspace: the direct-load kernel)
+    char *ws = (char *)workspace;
+    hipError_t e = launch_import_tiled(base_fmt(a->fmt), (const uint8_t *)a->codes, a->codes_pitch,
+                                       (const uint8_t *)a->scales, a->scales_pitch, a->rows,
+                                       a->cols, (uint8_t *)ws + R.codes, (uint8_t *)ws + R.scales,
+                                       stream);
+    if (e != hipSuccess) return hip_fail(e, "activation re-tiling launch");
+    fp4_tensor t = *a;
+    t.layout = FP4_LAYOUT_TILED;
+    t.codes_pitch = t.scales_pitch = 0;
+    t.codes = ws + R.codes;
+    t.scales = ws + R.scales;
+    st = run_gemm(&t, w, c_bf16, ldc, stream);
+    return st == FP4_OK ? ok() : st;
+  }
   st = run_gemm(a, w, c_bf16, ldc, stream);
   return st == FP4_OK ? ok() : st;
 }

@@ -64,6 +64,12 @@ hipError_t launch_export_canonical(int fmt, const uint8_t *tcodes, const uint8_t
                                    uint8_t *scales, int64_t spitch, const float *ts_in,
                                    float *ts_out, hipStream_t stream);
 
+// Canonical [rows, k] codes/scales -> the fragment-tiled layout (rows padded
+// to 16, zero padding).
+hipError_t launch_import_tiled(int fmt, const uint8_t *codes, int64_t cpitch, const uint8_t *scales,
+                              int64_t spitch, int64_t rows, int64_t k, uint8_t *tcodes,
+                              uint8_t *tscales, hipStream_t stream);
+
 hipError_t launch_dequant(int fmt, int tiled, const uint8_t *codes, int64_t cpitch,
                           const uint8_t *scales, int64_t spitch, const float *ts, int64_t rows,
                           int64_t k, float *out, int64_t ldo, hipStream_t stream);

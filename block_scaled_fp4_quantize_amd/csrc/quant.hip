@@ -423,6 +423,31 @@ __global__ __launch_bounds__(kThreads) void k_export(
   }
 }
 
+// Canonical -> tiled copy (one thread per block of the padded tiled layout;
+// rows past the tensor and K padding come out zero).
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_import(
+    const uint8_t *__restrict__ codes, int64_t cpitch, const uint8_t *__restrict__ scales,
+    int64_t spitch, int64_t rows, int64_t rows_pad, int64_t kt_n, uint8_t *__restrict__ tc,
+    uint8_t *__restrict__ ts) {
+  using K = Blk<FMT>;
+  const int64_t nb_pad = kt_n * K::BPF, total = rows_pad * nb_pad;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
+    const int64_t r = t / nb_pad, b = t - r * nb_pad;
+    uint8_t *tcd, *tsd;
+    block_dst<FMT, 1>(r, b, kt_n, tc, 0, ts, 0, tcd, tsd);
+    if (r >= rows) {
+      zero_store<FMT>(tcd, tsd);
+      continue;
+    }
+    const uint8_t *ccd = codes + r * cpitch + b * (K::B / 2);
+    if (FMT == 0) *(uint2 *)tcd = *(const uint2 *)ccd;
+    else *(uint4 *)tcd = *(const uint4 *)ccd;
+    *tsd = scales[r * spitch + b];
+  }
+}
+
 // x^ = q * s_b * S_t rounded once to FP32. One thread per element.
 template <int FMT, int TILED>
 __global__ __launch_bounds__(kThreads) void k_dequant(
@@ -593,6 +618,20 @@ hipError_t launch_export_canonical(int fmt, const uint8_t *tcodes, const uint8_t
   else
     hipLaunchKernelGGL(k_export<1>, dim3(grid), dim3(kThreads), 0, stream, tcodes, tscales, rows,
                        kt_n, codes, cpitch, scales, spitch, ts_in, ts_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_import_tiled(int fmt, const uint8_t *codes, int64_t cpitch, const uint8_t *scales,
+                              int64_t spitch, int64_t rows, int64_t k, uint8_t *tcodes,
+                              uint8_t *tscales, hipStream_t stream) {
+  const int64_t kt_n = k_pad(k) / kFragK, rows_pad = round_up(rows, 16);
+  const int grid = grid_for(rows_pad * kt_n * (128 / block_of(fmt)), 8192);
+  if (fmt == 0)
+    hipLaunchKernelGGL(k_import<0>, dim3(grid), dim3(kThreads), 0, stream, codes, cpitch, scales,
+                       spitch, rows, rows_pad, kt_n, tcodes, tscales);
+  else
+    hipLaunchKernelGGL(k_import<1>, dim3(grid), dim3(kThreads), 0, stream, codes, cpitch, scales,
+                       spitch, rows, rows_pad, kt_n, tcodes, tscales);
   return hipGetLastError();
 }
 

@@ -159,16 +159,20 @@ fp4_status fp4_quantize_act(int32_t fmt, const void *a_bf16, int64_t m, int64_t 
                             const float *static_scale, fp4_tensor *out, void *workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace for fp4_gemm. The current kernels need none (returns 0); the
- * arguments are kept so that a future kernel can use one without an ABI
- * change. */
+/* Workspace for fp4_gemm: for CANONICAL activations with M > 128, room for a
+ * tiled copy of them (then the product runs on the LDS-staged tile kernel);
+ * 0 for M <= 128. No zero-filling or persistence is needed. */
 size_t fp4_gemm_workspace_bytes(int32_t fmt, int64_t m, int64_t n, int64_t k);
 
 /*
  * C[m, n] (bf16, row stride ldc elements) = bf16_RNE(alpha * sum_k a^'[m,k] w^'[n,k]),
  * with a^' = q * s_b (per-tensor factors pulled into alpha = S_tA * S_tW for
  * NVFP4, alpha = 1 for MXFP4). `a` is CANONICAL or TILED, `w` is TILED,
- * same format and K. Accumulation is FP32. `workspace` may be NULL.
+ * same format and K. Accumulation is FP32. CANONICAL `a` with M > 128 is
+ * first copied into the tiled layout in `workspace` when it holds
+ * fp4_gemm_workspace_bytes (16-byte aligned); with a smaller or NULL
+ * workspace such a product runs on a slower kernel that reads the canonical
+ * layout directly. Calls sharing a workspace must not overlap in time.
  * FP4_ERR_SHAPE when M <= 128 with CANONICAL `a` whose M * max(codes pitch,
  * scales pitch) reaches 2^31 bytes (the skinny kernels use 32-bit offsets).
  */

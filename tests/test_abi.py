@@ -47,6 +47,10 @@ def test_sizes_and_pitches():
     assert L.fp4_quantize_workspace_bytes(fp4.NVFP4, 8, 64) >= 4096
     assert L.fp4_quantize_workspace_bytes(fp4.MXFP4, 8, 64) == 0
     assert L.fp4_gemm_workspace_bytes(fp4.NVFP4, 8, 64, 64) == 0
+    assert L.fp4_gemm_workspace_bytes(fp4.NVFP4, 128, 64, 64) == 0
+    # M > 128: a tiled copy of the activations (rows padded to 16, K to 128)
+    assert L.fp4_gemm_workspace_bytes(fp4.NVFP4, 200, 64, 2880) >= 208 * 2944 // 2 + 208 * 2944 // 16
+    assert L.fp4_gemm_workspace_bytes(fp4.MXFP4, 200, 64, 2880) >= 208 * 2944 // 2 + 208 * 2944 // 32
     assert L.fp4_linear_workspace_bytes(fp4.NVFP4, 8, 5120, 5120) > 0
 
 

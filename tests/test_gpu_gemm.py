@@ -26,6 +26,10 @@ def _gemm_case(fmt, a_bits, w_bits, what, use_linear=True):
     assert_canonical_equal(qa, qa_ref, f, what=what + " (A codes)")
     c = bf16_out_to_f64(fp4.fp4_gemm(qa, wq))
     assert_gemm_close(c, c_ref, l_ref, what + " gemm")
+    if m > 128:   # without the re-tiling workspace: the direct-load kernel
+        tiny = torch.zeros(16, dtype=torch.uint8, device="cuda")
+        c2 = bf16_out_to_f64(fp4.fp4_gemm(qa, wq, workspace=tiny))
+        assert_gemm_close(c2, c_ref, l_ref, what + " gemm, no workspace")
     if use_linear:
         y = bf16_out_to_f64(fp4.fp4_linear(x, wq))
         assert_gemm_close(y, c_ref, l_ref, what + " linear")
@@ -292,11 +296,14 @@ def test_linear_workspace_shared_across_shapes():
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("m,n,k", [(1, 272, 640), (8, 520, 2880), (20, 8200, 512), (33, 100, 256),
-                                   (4, 4112, 640), (30, 4100, 512)])
+                                   (4, 4112, 640), (30, 4100, 512),
+                                   # M > 128: re-tiled into the workspace
+                                   (200, 272, 640), (300, 100, 2880)])
 def test_decode_canonical_wide_pitch(fmt, m, n, k):
     """fp4_gemm on canonical activations whose rows are wider than they need
-    to be (codes pitch + 80 bytes, scales pitch + 24): the skinny kernels must
-    read only each row's own bytes, whatever lies between the rows."""
+    to be (codes pitch + 80 bytes, scales pitch + 24): the skinny kernels and
+    the re-tiling copy must read only each row's own bytes, whatever lies
+    between the rows."""
     print(f"[gemm] canonical wide pitch fmt={fmt} m={m} n={n} k={k}", flush=True)
     f = F[fmt]
     a = synth.normal((m, k), 1.0, 7, m * 29 + k)
