@@ -195,6 +195,54 @@ fp4_status run_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c, int64_t l
   return FP4_OK;
 }
 
+// Arguments of a linear call (everything but the workspace).
+fp4_status linear_check(const void *x_bf16, int64_t m, const fp4_tensor *w,
+                        const float *static_scale, const void *y_bf16) {
+  fp4_status st;
+  if ((st = check_tensor(w, "w")) != FP4_OK) return st;
+  if (w->layout != FP4_LAYOUT_TILED)
+    return fail(FP4_ERR_FORMAT_MISMATCH, "w must be in the TILED layout");
+  if ((st = check_shape(w->fmt, m, w->cols)) != FP4_OK) return st;
+  if (!x_bf16 || !y_bf16) return fail(FP4_ERR_INVALID_ARG, "null input or output");
+  if (!aligned16(x_bf16)) return fail(FP4_ERR_ALIGNMENT, "input must be 16-byte aligned");
+  if (((uintptr_t)y_bf16 & 1u) != 0) return fail(FP4_ERR_ALIGNMENT, "output must be 2-byte aligned");
+  if (base_fmt(w->fmt) == FP4_MXFP4 && static_scale)
+    return fail(FP4_ERR_INVALID_ARG, "MXFP4 has no per-tensor scale");
+  return FP4_OK;
+}
+
+// The linear's launches, with a workspace of linear_layout(...).total bytes.
+fp4_status linear_run(const void *x_bf16, int64_t m, const fp4_tensor *w,
+                      const float *static_scale, void *y_bf16, void *workspace,
+                      hipStream_t stream) {
+  const int32_t fmt = w->fmt;
+  const int64_t k = w->cols, n = w->rows;
+  const int base = base_fmt(fmt);
+  if (use_fused(fmt, m, n, k)) {
+    hipError_t e = launch_linear_fused(base, recipe_of(fmt), (const uint16_t *)x_bf16, m, k,
+                                       static_scale,
+                                       (const uint8_t *)w->codes, (const uint8_t *)w->scales,
+                                       w->tensor_scale, n, (uint16_t *)y_bf16, n, stream);
+    if (e != hipSuccess) return hip_fail(e, "fused linear launch");
+    return FP4_OK;
+  }
+  const LinearLayout L = linear_layout(fmt, m, k);
+  char *ws = (char *)workspace;
+  fp4_tensor a;
+  a.fmt = fmt;
+  a.layout = FP4_LAYOUT_TILED;
+  a.rows = m;
+  a.cols = k;
+  a.codes_pitch = 0;
+  a.scales_pitch = 0;
+  a.codes = ws + L.codes;
+  a.scales = ws + L.scales;
+  a.tensor_scale = (float *)(ws + L.ts);
+  fp4_status st = run_quant(fmt, 1, x_bf16, m, k, static_scale, &a, ws + L.scratch, stream);
+  if (st != FP4_OK) return st;
+  return run_gemm(&a, w, y_bf16, n, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -339,46 +387,13 @@ fp4_status fp4_linear(const void *x_bf16, int64_t m, const fp4_tensor *w,
                       const float *static_scale, void *y_bf16, void *workspace,
                       size_t workspace_bytes, hipStream_t stream) {
   fp4_status st;
-  if ((st = check_tensor(w, "w")) != FP4_OK) return st;
-  if (w->layout != FP4_LAYOUT_TILED)
-    return fail(FP4_ERR_FORMAT_MISMATCH, "w must be in the TILED layout");
-  const int32_t fmt = w->fmt;
-  const int64_t k = w->cols, n = w->rows;
-  if ((st = check_shape(fmt, m, k)) != FP4_OK) return st;
-  if (!x_bf16 || !y_bf16) return fail(FP4_ERR_INVALID_ARG, "null input or output");
-  if (!aligned16(x_bf16)) return fail(FP4_ERR_ALIGNMENT, "input must be 16-byte aligned");
-  if (((uintptr_t)y_bf16 & 1u) != 0) return fail(FP4_ERR_ALIGNMENT, "output must be 2-byte aligned");
-  const int base = base_fmt(fmt);
-  if (base == FP4_MXFP4 && static_scale)
-    return fail(FP4_ERR_INVALID_ARG, "MXFP4 has no per-tensor scale");
-  const LinearLayout L = linear_layout(fmt, m, k);
+  if ((st = linear_check(x_bf16, m, w, static_scale, y_bf16)) != FP4_OK) return st;
+  const LinearLayout L = linear_layout(w->fmt, m, w->cols);
   if (!workspace || workspace_bytes < L.total)
     return fail(FP4_ERR_WORKSPACE, "workspace needs %zu bytes", L.total);
   if (!aligned16(workspace)) return fail(FP4_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
   if ((st = check_device()) != FP4_OK) return st;
-
-  if (use_fused(fmt, m, n, k)) {
-    hipError_t e = launch_linear_fused(base, recipe_of(fmt), (const uint16_t *)x_bf16, m, k,
-                                       static_scale,
-                                       (const uint8_t *)w->codes, (const uint8_t *)w->scales,
-                                       w->tensor_scale, n, (uint16_t *)y_bf16, n, stream);
-    if (e != hipSuccess) return hip_fail(e, "fused linear launch");
-    return ok();
-  }
-  char *ws = (char *)workspace;
-  fp4_tensor a;
-  a.fmt = fmt;
-  a.layout = FP4_LAYOUT_TILED;
-  a.rows = m;
-  a.cols = k;
-  a.codes_pitch = 0;
-  a.scales_pitch = 0;
-  a.codes = ws + L.codes;
-  a.scales = ws + L.scales;
-  a.tensor_scale = (float *)(ws + L.ts);
-  st = run_quant(fmt, 1, x_bf16, m, k, static_scale, &a, ws + L.scratch, stream);
-  if (st != FP4_OK) return st;
-  st = run_gemm(&a, w, y_bf16, n, stream);
+  st = linear_run(x_bf16, m, w, static_scale, y_bf16, workspace, stream);
   return st == FP4_OK ? ok() : st;
 }
 
