@@ -90,6 +90,20 @@ def _load():
         lib.orc_quantize_mxfp4_rule.argtypes = [P, I64, I64, ctypes.c_int, P, P]
         lib.orc_mx_exponent_oas.restype = ctypes.c_int
         lib.orc_mx_exponent_oas.argtypes = [ctypes.c_double]
+        lib.orc_mbs_scale.restype = ctypes.c_float
+        lib.orc_mbs_scale.argtypes = [ctypes.c_double]
+        lib.orc_mbs_exponent.restype = ctypes.c_int
+        lib.orc_mbs_exponent.argtypes = [ctypes.c_double, ctypes.c_float, ctypes.c_int]
+        lib.orc_quantize_mxfp4_mbs.restype = ctypes.c_int
+        lib.orc_quantize_mxfp4_mbs.argtypes = [P, I64, I64, ctypes.c_int, P, P, P]
+        lib.orc_dequantize_ms.restype = None
+        lib.orc_dequantize_ms.argtypes = [ctypes.c_int, P, P, P, ctypes.c_float, I64, I64, P]
+        lib.orc_gemm_ms.restype = None
+        lib.orc_gemm_ms.argtypes = [ctypes.c_int, P, P, P, ctypes.c_float, P, P, P, ctypes.c_float,
+                                    I64, I64, I64, P, P]
+        lib.orc_gemm_sampled_ms.restype = None
+        lib.orc_gemm_sampled_ms.argtypes = [ctypes.c_int, P, P, P, ctypes.c_float, P, P, P,
+                                            ctypes.c_float, I64, P, P, I64, P, P]
         lib.orc_hadamard_norm.restype = ctypes.c_float
         lib.orc_hadamard_norm.argtypes = [ctypes.c_int]
         lib.orc_hadamard_bf16.restype = ctypes.c_int
@@ -126,14 +140,21 @@ def _bf16(x) -> np.ndarray:
 
 
 class Quantized:
-    """Canonical quantized tensor: codes [R, K/2], scales [R, K/B], tensor scale."""
+    """Canonical quantized tensor: codes [R, K/2], scales [R, K/B], tensor scale,
+    and for MXFP4 with macro-block scaling the FP32 scales macro [R, ceil(K/128)]
+    (None otherwise)."""
 
-    def __init__(self, fmt, codes, scales, tensor_scale, k):
+    def __init__(self, fmt, codes, scales, tensor_scale, k, macro=None):
         self.fmt = fmt
         self.codes = codes
         self.scales = scales
         self.tensor_scale = np.float32(tensor_scale)
         self.k = k
+        self.macro = None if macro is None else np.ascontiguousarray(macro, dtype=np.float32)
+
+    def row_slice(self, r0, r1):
+        return Quantized(self.fmt, self.codes[r0:r1], self.scales[r0:r1], self.tensor_scale,
+                         self.k, None if self.macro is None else self.macro[r0:r1])
 
     @property
     def rows(self):
@@ -208,6 +229,29 @@ def quantize_mxfp4(x, oas: bool = False) -> Quantized:
     return Quantized(MXFP4, codes, scales, 1.0, k)
 
 
+def quantize_mxfp4_mbs(x, oas: bool = False) -> Quantized:
+    """MXFP4 with macro-block scaling: 128-value segments along k each get an
+    FP32 scale in [1, 2) (see the C file's header for the reading)."""
+    x = _bf16(x)
+    r, k = x.shape
+    codes = np.zeros((r, k // 2), dtype=np.uint8)
+    scales = np.zeros((r, k // 32), dtype=np.uint8)
+    macro = np.zeros((r, (k + 127) // 128), dtype=np.float32)
+    rc = _load().orc_quantize_mxfp4_mbs(_ptr(x), r, k, int(bool(oas)), _ptr(codes), _ptr(scales),
+                                        _ptr(macro))
+    if rc != 0:
+        raise ValueError("oracle MXFP4 (MBS) quantize rejected its arguments")
+    return Quantized(MXFP4, codes, scales, 1.0, k, macro)
+
+
+def mbs_scale(g: float) -> np.float32:
+    return np.float32(_load().orc_mbs_scale(float(g)))
+
+
+def mbs_exponent(ab: float, s, oas: bool = False) -> int:
+    return _load().orc_mbs_exponent(float(ab), float(s), int(bool(oas)))
+
+
 def mx_exponent_oas(amax: float) -> int:
     """Overflow-aware MXFP4 block exponent (smallest e with amax <= 6 * 2^e)."""
     return _load().orc_mx_exponent_oas(float(amax))
@@ -230,33 +274,39 @@ def hadamard(x, bs: int) -> np.ndarray:
 
 
 def quantize(fmt: int, x, mode: int = DYNAMIC, static_scale=None, rotate: bool = False,
-             oas: bool = False) -> Quantized:
+             oas: bool = False, mbs: bool = False) -> Quantized:
     """Quantize x; rotate=True applies the block rotation (size = the block)
-    first; oas=True (MXFP4) takes the overflow-aware block exponent."""
+    first; oas=True (MXFP4) takes the overflow-aware block exponent; mbs=True
+    (MXFP4) adds the macro-block scales."""
     if rotate:
         x = hadamard(x, BLOCK[fmt])
     if fmt == NVFP4:
-        if oas:
-            raise ValueError("OAS is an MXFP4 scale rule")
+        if oas or mbs:
+            raise ValueError("OAS and MBS are MXFP4 scale rules")
         return quantize_nvfp4(x, mode, static_scale)
     if mode != DYNAMIC or static_scale is not None:
         raise ValueError("MXFP4 has no per-tensor scale")
-    return quantize_mxfp4(x, oas)
+    return quantize_mxfp4_mbs(x, oas) if mbs else quantize_mxfp4(x, oas)
+
+
+def _mptr(q: Quantized):
+    return None if q.macro is None else _ptr(q.macro)
 
 
 def dequantize(q: Quantized) -> np.ndarray:
-    """x^ in binary64, [R, K] (includes the NVFP4 per-tensor factor)."""
+    """x^ in binary64, [R, K] (includes the NVFP4 per-tensor factor and the
+    macro-block scales)."""
     out = np.empty((q.rows, q.k), dtype=np.float64)
-    _load().orc_dequantize(q.fmt, _ptr(q.codes), _ptr(q.scales), float(q.tensor_scale),
-                           q.rows, q.k, _ptr(out))
+    _load().orc_dequantize_ms(q.fmt, _ptr(q.codes), _ptr(q.scales), _mptr(q),
+                              float(q.tensor_scale), q.rows, q.k, _ptr(out))
     return out
 
 
 def _unit(q: Quantized) -> np.ndarray:
-    """q * s_b without the per-tensor factor (what the GEMM contracts)."""
+    """q * s_b (times S_mb) without the per-tensor factor (what the GEMM contracts)."""
     out = np.empty((q.rows, q.k), dtype=np.float64)
-    _load().orc_dequantize(q.fmt, _ptr(q.codes), _ptr(q.scales), 1.0, q.rows, q.k,
-                           _ptr(out))
+    _load().orc_dequantize_ms(q.fmt, _ptr(q.codes), _ptr(q.scales), _mptr(q), 1.0, q.rows,
+                              q.k, _ptr(out))
     return out
 
 
@@ -269,6 +319,8 @@ def alpha(a: Quantized, w: Quantized) -> float:
 def _check_pair(a: Quantized, w: Quantized):
     if a.fmt != w.fmt or a.k != w.k:
         raise ValueError("operands differ in format or K")
+    if (a.macro is None) != (w.macro is None):
+        raise ValueError("operands differ in macro-block scaling")
 
 
 def gemm_loop(a: Quantized, w: Quantized):
@@ -277,9 +329,9 @@ def gemm_loop(a: Quantized, w: Quantized):
     m, n = a.rows, w.rows
     c = np.empty((m, n), dtype=np.float64)
     l = np.empty((m, n), dtype=np.float64)
-    _load().orc_gemm(a.fmt, _ptr(a.codes), _ptr(a.scales), float(a.tensor_scale),
-                     _ptr(w.codes), _ptr(w.scales), float(w.tensor_scale), m, n, a.k,
-                     _ptr(c), _ptr(l))
+    _load().orc_gemm_ms(a.fmt, _ptr(a.codes), _ptr(a.scales), _mptr(a), float(a.tensor_scale),
+                        _ptr(w.codes), _ptr(w.scales), _mptr(w), float(w.tensor_scale), m, n,
+                        a.k, _ptr(c), _ptr(l))
     return c, l
 
 
@@ -303,13 +355,20 @@ def gemm_sampled(a: Quantized, w: Quantized, rows, cols):
         raise IndexError("sample index out of range")
     c = np.empty(rows.size, dtype=np.float64)
     l = np.empty(rows.size, dtype=np.float64)
-    _load().orc_gemm_sampled(a.fmt, _ptr(a.codes), _ptr(a.scales), float(a.tensor_scale),
-                             _ptr(w.codes), _ptr(w.scales), float(w.tensor_scale), a.k,
-                             _ptr(rows), _ptr(cols), rows.size, _ptr(c), _ptr(l))
+    _load().orc_gemm_sampled_ms(a.fmt, _ptr(a.codes), _ptr(a.scales), _mptr(a),
+                                float(a.tensor_scale), _ptr(w.codes), _ptr(w.scales), _mptr(w),
+                                float(w.tensor_scale), a.k, _ptr(rows), _ptr(cols), rows.size,
+                                _ptr(c), _ptr(l))
     return c, l
 
 
 def gemm_w4a16(x, w: Quantized):
+    if w.macro is not None:
+        raise ValueError("the weight-only product takes no macro-block scales")
+    return _gemm_w4a16(x, w)
+
+
+def _gemm_w4a16(x, w: Quantized):
     """Weight-only product: C = S_tW * x W'^T with bf16 activations x [M, K]
     and the quantized weight (binary64, k-ordered); L = the magnitude sum."""
     x = _bf16(x)

@@ -69,6 +69,21 @@
  *   - OAS (MXFP4 only): e_b = the smallest exponent with a_b <= 6 * 2^e_b
  *     (clamped to [-127, 127]), so no element saturates; the default rule
  *     lets block maxima in (6, 8) * 2^e_b saturate to 6 * 2^e_b.
+ *   - MBS (MXFP4 only; [DIALECT], same section: a second-level scale over a
+ *     macro-block grouping several 32-value blocks, bringing MXFP4 closer to
+ *     two-level scaling without changing the base format). The pages give
+ *     neither the macro-block size nor the scale's format or rule. Reading:
+ *     a macro-block is the 32-value blocks of one 128-value segment of a row
+ *     along k (the last segment shorter when k % 128 != 0); its scale is an
+ *     FP32 number in [1, 2), S_mb = RN_fp32(g / (6 * 2^j)) with g the
+ *     segment's largest magnitude and j = floor(log2(g / 6)) (S_mb = 1 when
+ *     g = 0), the non-power-of-two factor that puts the segment's largest
+ *     value on the top code 6 * 2^j, as a two-level scale puts a block's on
+ *     6 * s_b. Each block then takes the MX exponent of its values divided by
+ *     S_mb: e_b = clamp(floor(log2(a_b / S_mb)) - 2, -127, 127) (with OAS the
+ *     smallest e with a_b <= 6 * 2^e * S_mb); its decode step is
+ *     d_b = 2^e_b * S_mb and x^ = q * 2^e_b * S_mb. The E2M1 codes and E8M0
+ *     bytes keep their format; the S_mb are stored beside them.
  *
  * Precision: every decision is taken on exact values. bf16 inputs, E4M3 scales,
  * FP32 tensor scales and the thresholds t * s_b * S_t (<= 31 significant bits)
@@ -343,6 +358,77 @@ int orc_quantize_mxfp4(const uint16_t *x, int64_t rows, int64_t k,
     return orc_quantize_mxfp4_rule(x, rows, k, 0, codes, scales);
 }
 
+/* Macro-block scale of a segment whose largest magnitude is g (reading in the
+ * header). g / 6 in binary64 never rounds across a power of two (g has 8
+ * significant bits, so g < 6 * 2^j implies g <= 6 * 2^j (1 - 2^-8)), and
+ * g / 6 = g / (3 * 2) has a period-2 binary expansion (or terminates), so
+ * its binary64 value never lies on a binary32 rounding midpoint it was not
+ * already on: rounding it to binary32 equals rounding the real quotient. */
+float orc_mbs_scale(double g)
+{
+    if (g == 0.0)
+        return 1.0f;
+    double q = g / 6.0;
+    int e2;
+    frexp(q, &e2);                     /* floor(log2 q) = e2 - 1 */
+    return (float)ldexp(q, -(e2 - 1));
+}
+
+/* MX block exponent of a_b / s for s in [1, 2), exactly: floor(log2(a_b / s))
+ * is floor(log2 a_b) or one less, decided by a_b >= s * 2^floor(log2 a_b)
+ * (an exact binary64 product). OAS: one more step while a_b > 6 * 2^e * s. */
+int orc_mbs_exponent(double ab, float s, int oas)
+{
+    if (ab == 0.0)
+        return -127;
+    int e2;
+    frexp(ab, &e2);
+    int fl = e2 - 1;
+    if (ab < (double)s * ldexp(1.0, fl))
+        fl -= 1;
+    int e = fl - 2;
+    if (e < -127)
+        e = -127;
+    if (e > 127)
+        e = 127;
+    if (oas && ab > 6.0 * ldexp(1.0, e) * (double)s && e < 127)
+        e += 1;
+    return e;
+}
+
+/*
+ * MXFP4 with macro-block scaling (reading in the header): codes [rows][k/2],
+ * E8M0 bytes [rows][k/32] as for MXFP4, and the FP32 macro-block scales
+ * mscales [rows][ceil(k/128)]. Elements are the nearest E2M1 codes of
+ * |x| / d_b with d_b = 2^e_b * S_mb (exact in binary64), ties to even.
+ */
+int orc_quantize_mxfp4_mbs(const uint16_t *x, int64_t rows, int64_t k, int oas,
+                           uint8_t *codes, uint8_t *scales, float *mscales)
+{
+    if (k <= 0 || rows < 0 || k % 32 != 0)
+        return -1;
+    int64_t nseg = (k + 127) / 128;
+    uint8_t *nib = (uint8_t *)malloc((size_t)k);
+    if (!nib)
+        return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t *xr = x + r * k;
+        for (int64_t sgi = 0; sgi < nseg; ++sgi) {
+            int64_t k0 = sgi * 128, k1 = k0 + 128 < k ? k0 + 128 : k;
+            float smb = orc_mbs_scale(orc_amax(xr + k0, k1 - k0));
+            mscales[r * nseg + sgi] = smb;
+            for (int64_t b = k0 / 32; b < k1 / 32; ++b) {
+                int e = orc_mbs_exponent(orc_amax(xr + b * 32, 32), smb, oas);
+                scales[r * (k / 32) + b] = (uint8_t)(e + 127);
+                encode_block(xr + b * 32, 32, ldexp(1.0, e) * (double)smb, nib + b * 32);
+            }
+        }
+        pack_row(nib, k, codes + r * (k / 2));
+    }
+    free(nib);
+    return 0;
+}
+
 /* --------------------------------------------------------------- rotation */
 
 /* RN_fp32(1/sqrt(bs)): exactly 0.25 for 16; for 32 the binary64 value of
@@ -509,29 +595,41 @@ int orc_hadamard_bf16(const uint16_t *x, int64_t rows, int64_t k, int bs, uint16
 
 /* --------------------------------------------------------- dequantization */
 
-/* One dequantized element without the per-tensor factor: v(code) * s_b. */
+/* One dequantized element without the per-tensor factor: v(code) * s_b, times
+ * the macro-block scale S_mb when the row has them (macro_row != NULL;
+ * MXFP4 with MBS). Exact in binary64 (2 + 1 + 24 significant bits at most). */
 static double element_value(int fmt, const uint8_t *codes_row, const uint8_t *scales_row,
-                            int64_t kk)
+                            const float *macro_row, int64_t kk)
 {
     int byte = codes_row[kk / 2];
     int code = (kk % 2 == 0) ? (byte & 15) : (byte >> 4);
     double q = orc_e2m1_value(code);
     double s = (fmt == ORC_NVFP4) ? orc_e4m3_value(scales_row[kk / 16])
                                   : orc_e8m0_value(scales_row[kk / 32]);
+    if (macro_row)
+        s *= (double)macro_row[kk / 128];
     return q * s;
 }
 
-/* x^ = q * s_b * S_t (NVFP4) or q * 2^e_b (MXFP4), exact in binary64.
+/* x^ = q * s_b * S_t (NVFP4), q * 2^e_b (MXFP4) or q * 2^e_b * S_mb (MXFP4
+ * with MBS: mscales [rows][ceil(k/128)], else NULL), exact in binary64.
  * out[rows][k]. tensor_scale is ignored for MXFP4. */
-void orc_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales,
-                    float tensor_scale, int64_t rows, int64_t k, double *out)
+void orc_dequantize_ms(int fmt, const uint8_t *codes, const uint8_t *scales,
+                       const float *mscales, float tensor_scale, int64_t rows, int64_t k,
+                       double *out)
 {
-    int64_t bs = (fmt == ORC_NVFP4) ? 16 : 32;
+    int64_t bs = (fmt == ORC_NVFP4) ? 16 : 32, nseg = (k + 127) / 128;
     double st = (fmt == ORC_NVFP4) ? (double)tensor_scale : 1.0;
     for (int64_t r = 0; r < rows; ++r)
         for (int64_t kk = 0; kk < k; ++kk)
-            out[r * k + kk] = element_value(fmt, codes + r * (k / 2),
-                                            scales + r * (k / bs), kk) * st;
+            out[r * k + kk] = element_value(fmt, codes + r * (k / 2), scales + r * (k / bs),
+                                            mscales ? mscales + r * nseg : NULL, kk) * st;
+}
+
+void orc_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales,
+                    float tensor_scale, int64_t rows, int64_t k, double *out)
+{
+    orc_dequantize_ms(fmt, codes, scales, NULL, tensor_scale, rows, k, out);
 }
 
 /* ------------------------------------------------------------------- GEMM */
@@ -544,16 +642,17 @@ void orc_dequantize(int fmt, const uint8_t *codes, const uint8_t *scales,
  * tolerance is stated against. Either output pointer may be NULL.
  */
 static void gemm_entry(int fmt, const uint8_t *a_codes, const uint8_t *a_scales,
-                       const uint8_t *w_codes, const uint8_t *w_scales,
-                       int64_t k, int64_t m, int64_t n, double alpha,
+                       const float *a_ms, const uint8_t *w_codes, const uint8_t *w_scales,
+                       const float *w_ms, int64_t k, int64_t m, int64_t n, double alpha,
                        double *c_out, double *l_out)
 {
-    int64_t bs = (fmt == ORC_NVFP4) ? 16 : 32;
+    int64_t bs = (fmt == ORC_NVFP4) ? 16 : 32, nseg = (k + 127) / 128;
     const uint8_t *ac = a_codes + m * (k / 2), *as = a_scales + m * (k / bs);
     const uint8_t *wc = w_codes + n * (k / 2), *ws = w_scales + n * (k / bs);
+    const float *am = a_ms ? a_ms + m * nseg : NULL, *wm = w_ms ? w_ms + n * nseg : NULL;
     double acc = 0.0, mag = 0.0;
     for (int64_t kk = 0; kk < k; ++kk) {
-        double p = element_value(fmt, ac, as, kk) * element_value(fmt, wc, ws, kk);
+        double p = element_value(fmt, ac, as, am, kk) * element_value(fmt, wc, ws, wm, kk);
         acc += p;
         mag += fabs(p);
     }
@@ -568,28 +667,46 @@ static double gemm_alpha(int fmt, float a_ts, float w_ts)
     return (fmt == ORC_NVFP4) ? (double)a_ts * (double)w_ts : 1.0;
 }
 
-/* Full GEMM: c[M][N], l[M][N]. */
-void orc_gemm(int fmt, const uint8_t *a_codes, const uint8_t *a_scales, float a_ts,
-              const uint8_t *w_codes, const uint8_t *w_scales, float w_ts,
-              int64_t M, int64_t N, int64_t K, double *c, double *l)
+/* Full GEMM: c[M][N], l[M][N]; a_ms / w_ms are the operands' macro-block
+ * scales (MXFP4 with MBS) or NULL. */
+void orc_gemm_ms(int fmt, const uint8_t *a_codes, const uint8_t *a_scales, const float *a_ms,
+                 float a_ts, const uint8_t *w_codes, const uint8_t *w_scales, const float *w_ms,
+                 float w_ts, int64_t M, int64_t N, int64_t K, double *c, double *l)
 {
     double alpha = gemm_alpha(fmt, a_ts, w_ts);
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < N; ++n)
-            gemm_entry(fmt, a_codes, a_scales, w_codes, w_scales, K, m, n, alpha,
+            gemm_entry(fmt, a_codes, a_scales, a_ms, w_codes, w_scales, w_ms, K, m, n, alpha,
                        c ? c + m * N + n : NULL, l ? l + m * N + n : NULL);
 }
 
+void orc_gemm(int fmt, const uint8_t *a_codes, const uint8_t *a_scales, float a_ts,
+              const uint8_t *w_codes, const uint8_t *w_scales, float w_ts,
+              int64_t M, int64_t N, int64_t K, double *c, double *l)
+{
+    orc_gemm_ms(fmt, a_codes, a_scales, NULL, a_ts, w_codes, w_scales, NULL, w_ts, M, N, K, c, l);
+}
+
 /* Sampled GEMM: entries (rows[i], cols[i]) for i < count. */
+void orc_gemm_sampled_ms(int fmt, const uint8_t *a_codes, const uint8_t *a_scales,
+                         const float *a_ms, float a_ts, const uint8_t *w_codes,
+                         const uint8_t *w_scales, const float *w_ms, float w_ts, int64_t K,
+                         const int64_t *rows, const int64_t *cols, int64_t count,
+                         double *c, double *l)
+{
+    double alpha = gemm_alpha(fmt, a_ts, w_ts);
+    for (int64_t i = 0; i < count; ++i)
+        gemm_entry(fmt, a_codes, a_scales, a_ms, w_codes, w_scales, w_ms, K, rows[i], cols[i],
+                   alpha, c ? c + i : NULL, l ? l + i : NULL);
+}
+
 void orc_gemm_sampled(int fmt, const uint8_t *a_codes, const uint8_t *a_scales, float a_ts,
                       const uint8_t *w_codes, const uint8_t *w_scales, float w_ts,
                       int64_t K, const int64_t *rows, const int64_t *cols, int64_t count,
                       double *c, double *l)
 {
-    double alpha = gemm_alpha(fmt, a_ts, w_ts);
-    for (int64_t i = 0; i < count; ++i)
-        gemm_entry(fmt, a_codes, a_scales, w_codes, w_scales, K, rows[i], cols[i], alpha,
-                   c ? c + i : NULL, l ? l + i : NULL);
+    orc_gemm_sampled_ms(fmt, a_codes, a_scales, NULL, a_ts, w_codes, w_scales, NULL, w_ts, K,
+                        rows, cols, count, c, l);
 }
 
 /*
@@ -610,7 +727,7 @@ static void gemm_w4a16_entry(int fmt, const uint16_t *x, const uint8_t *w_codes,
     const uint8_t *wc = w_codes + n * (k / 2), *ws = w_scales + n * (k / bs);
     double acc = 0.0, mag = 0.0;
     for (int64_t kk = 0; kk < k; ++kk) {
-        double p = orc_bf16_value(xr[kk]) * element_value(fmt, wc, ws, kk);
+        double p = orc_bf16_value(xr[kk]) * element_value(fmt, wc, ws, NULL, kk);
         acc += p;
         mag += fabs(p);
     }

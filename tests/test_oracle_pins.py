@@ -811,3 +811,125 @@ def test_w4a16_closed_form():
         c, l = oracle.gemm_w4a16(x, q)
         assert np.all(c[0] == 0.75 * k * ts) and np.all(c[1] == -0.75 * k * ts)
         assert np.all(l == 0.75 * k * ts)
+
+
+# ------------------------------------------------------ MXFP4 macro-block scaling
+# "FP4 n'existe pas ...", section "L'ecart de qualite - et comment il se
+# reduit": a second-level scale over a macro-block of several 32-value blocks.
+# Reading (the oracle's header): 128-value segments along k, FP32 scale in
+# [1, 2) putting the segment's largest value on the top code.
+
+def _floor_log2(fr: Fraction) -> int:
+    e = fr.numerator.bit_length() - fr.denominator.bit_length()
+    if Fraction(2) ** e > fr:
+        e -= 1
+    return e
+
+
+def _brute_mbs(xbits, oas=False):
+    """MXFP4 + macro-block scales by exact rational arithmetic and search."""
+    vals = bf16_to_f32(xbits).astype(np.float64)
+    r, k = xbits.shape
+    nseg = (k + 127) // 128
+    codes = np.zeros((r, k), np.uint8)
+    scales = np.zeros((r, k // 32), np.uint8)
+    macro = np.zeros((r, nseg), np.float32)
+    for i in range(r):
+        for sgi in range(nseg):
+            seg = [Fraction(float(v)) for v in vals[i, sgi * 128: min(k, sgi * 128 + 128)]]
+            g = max(abs(v) for v in seg)
+            if g == 0:
+                s = Fraction(1)
+            else:
+                j = _floor_log2(g / 6)
+                s = Fraction(float(_fp32_round_exact(g / (6 * Fraction(2) ** j))))
+            macro[i, sgi] = np.float32(float(s))
+            for b in range(sgi * 4, min(k // 32, sgi * 4 + 4)):
+                blk = [Fraction(float(v)) for v in vals[i, b * 32: b * 32 + 32]]
+                ab = max(abs(v) for v in blk)
+                if ab == 0:
+                    e = -127
+                else:
+                    e = max(-127, min(127, _floor_log2(ab / s) - 2))
+                    if oas and ab > 6 * Fraction(2) ** e * s:
+                        e += 1                    # smallest e with ab <= 6 * 2^e * s
+                scales[i, b] = e + 127
+                d = Fraction(2) ** e * s
+                for t, v in enumerate(blk):
+                    dist = [(abs(abs(v) - Fraction(float(mm)) * d), c % 2, c)
+                            for c, mm in enumerate(PRINTED_MAGS)]
+                    mag = min(dist)[2]
+                    sign = int(xbits[i, b * 32 + t]) >> 15
+                    codes[i, b * 32 + t] = (sign << 3) | mag
+    return codes, scales, macro
+
+
+@pytest.mark.parametrize("oas", [False, True])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_mbs_brute_force(oas, seed):
+    rng = np.random.default_rng(40 + seed)
+    x = rng.standard_t(2, (3, 320)) * 2.0 ** rng.uniform(-20, 20, (3, 1))
+    x[1, 130:140] = 0.0
+    x[2, 256:] = 0.0                                   # an all-zero final segment
+    xb = bf16_bits(x.astype(np.float32))
+    q = oracle.quantize_mxfp4_mbs(xb, oas=oas)
+    codes, scales, macro = _brute_mbs(xb, oas)
+    assert np.array_equal(q.macro.view(np.uint32), macro.view(np.uint32))
+    assert np.array_equal(q.scales, scales)
+    assert np.array_equal(unpack(q.codes), codes)
+    assert q.macro.shape == (3, 3) and q.macro[2, 2] == 1.0
+
+
+def test_mbs_segment_maximum_lands_on_the_top_code():
+    """The segment's largest magnitude gets code 6 and is reconstructed to
+    within the FP32 rounding of its scale; scales lie in [1, 2)."""
+    rng = np.random.default_rng(9)
+    x = bf16_bits((rng.standard_t(3, (8, 512)) * 3.0).astype(np.float32))
+    q = oracle.quantize_mxfp4_mbs(x)
+    xv = bf16_to_f32(x).astype(np.float64)
+    xhat = oracle.dequantize(q)
+    nib = unpack(q.codes)
+    assert np.all((q.macro >= 1.0) & (q.macro < 2.0))
+    for i in range(8):
+        for sgi in range(4):
+            seg = np.abs(xv[i, sgi * 128:(sgi + 1) * 128])
+            j = int(np.argmax(seg))
+            assert nib[i, sgi * 128 + j] & 7 == 7
+            assert abs(abs(xhat[i, sgi * 128 + j]) - seg[j]) <= 2.0 ** -24 * seg[j]
+
+
+def test_mbs_scale_equivariance_and_error_reduction():
+    """x -> 2^i x shifts every E8M0 byte by i and keeps codes and macro scales;
+    on heavy-tailed data the macro scales lower the squared error of plain
+    MXFP4 (the quality gap the section says MBS closes)."""
+    rng = np.random.default_rng(12)
+    x = bf16_bits((rng.standard_t(3, (16, 1024)) * 2.0).astype(np.float32))
+    q = oracle.quantize_mxfp4_mbs(x)
+    x8 = bf16_bits(bf16_to_f32(x) * np.float32(2.0 ** 8))
+    q8 = oracle.quantize_mxfp4_mbs(x8)
+    assert np.array_equal(q8.codes, q.codes) and np.array_equal(q8.macro, q.macro)
+    assert np.array_equal(q8.scales.astype(int), q.scales.astype(int) + 8)
+    xv = bf16_to_f32(x).astype(np.float64)
+    err_mbs = ((oracle.dequantize(q) - xv) ** 2).sum()
+    err_mx = ((oracle.dequantize(oracle.quantize_mxfp4(x)) - xv) ** 2).sum()
+    assert err_mbs < 0.9 * err_mx
+
+
+def test_mbs_gemm_equals_textbook_matmul():
+    """The contraction includes the macro scales: a library matmul of operands
+    decoded with torch's tables, times the macro scale of each 128-segment."""
+    rng = np.random.default_rng(23)
+    a = bf16_bits(rng.standard_normal((5, 320)).astype(np.float32))
+    w = bf16_bits((rng.standard_normal((7, 320)) * 0.02).astype(np.float32))
+    qa, qw = oracle.quantize_mxfp4_mbs(a), oracle.quantize_mxfp4_mbs(w)
+
+    def decode(q):
+        return _torch_dequant(q) * q.macro.astype(np.float64).repeat(128, axis=1)[:, :q.k]
+    ad, wd = decode(qa), decode(qw)
+    c, l = oracle.gemm_loop(qa, qw)
+    assert np.allclose(c, ad @ wd.T, rtol=0, atol=1e-12 * (np.abs(ad) @ np.abs(wd).T).max())
+    assert np.allclose(l, np.abs(ad) @ np.abs(wd).T, rtol=1e-14)
+    c2, _ = oracle.gemm(qa, qw)
+    assert np.allclose(c2, c, rtol=0, atol=1e-12 * l.max())
+    cs, ls = oracle.gemm_sampled(qa, qw, np.array([4, 0]), np.array([6, 3]))
+    assert cs[0] == c[4, 6] and cs[1] == c[0, 3]
