@@ -786,8 +786,8 @@ def cpu_baseline(configs, fmt, args, a_host, w_host):
             return oracle.gemm_loop(qa, sub)
         list(pool.map(run, chunks(qw.rows, threads)))
 
-    def rows_of(q, r):
-        return oracle.Quantized(fmt, q.codes[:r], q.scales[:r], q.tensor_scale, q.k)
+    def w_rows(q, r0, r1):
+        return oracle.Quantized(fmt, q.codes[r0:r1], q.scales[r0:r1], q.tensor_scale, q.k)
 
     budget = args.cpu_seconds / len(configs)
     tot_flops, tot_s, parts, wq_cache = 0.0, 0.0, [], {}
@@ -798,24 +798,29 @@ def cpu_baseline(configs, fmt, args, a_host, w_host):
         qw = wq_cache[(k, n)]
         t = time.perf_counter()
         qa = a_bits if args.w4a16 else quantize_par(a_bits)
+
+        def a_rows(r0, r1):
+            return a_bits[r0:r1] if args.w4a16 else w_rows(qa, r0, r1)
         t_q = time.perf_counter() - t
-        # probe the GEMM rate on a small sample, then size the timed sample
-        pr, pc = min(m, 2), min(n, 8 * threads)
-        probe_a = a_bits[:pr] if args.w4a16 else rows_of(qa, pr)
-        t = time.perf_counter()
-        gemm_par(probe_a, rows_of(qw, pc))
-        per_out = max((time.perf_counter() - t) / (pr * pc), 1e-9)
-        full = m * n * per_out
-        if full <= budget:
-            rows, cols = m, n
-        elif m > 128:
-            rows, cols = max(1, min(64, int(budget / (n * per_out)))), n
+
+        def timed(a_part, w_part):
+            t0 = time.perf_counter()
+            gemm_par(a_part, w_part)
+            return time.perf_counter() - t0
+        # The sample grows until it fills the budget: large M takes whole
+        # activation rows (every output column; at most 64 rows), small M takes
+        # every row and the first output columns.
+        if m > 128:
+            t_g = timed(a_rows(0, 1), qw)
+            rows, cols = min(m, 64, max(1, int(budget / max(t_g, 1e-6)))), n
+            if rows > 1:
+                t_g += timed(a_rows(1, rows), qw)
         else:
-            rows, cols = m, max(threads, min(n, int(budget / (m * per_out))))
-        sample_a = a_bits[:rows] if args.w4a16 else rows_of(qa, rows)
-        t = time.perf_counter()
-        gemm_par(sample_a, rows_of(qw, cols))
-        t_g = time.perf_counter() - t
+            c1 = min(n, 16 * threads)
+            t_g = timed(a_rows(0, m), w_rows(qw, 0, c1))
+            rows, cols = m, min(n, max(c1, int(c1 * budget / max(t_g, 1e-6))))
+            if cols > c1:
+                t_g += timed(a_rows(0, m), w_rows(qw, c1, cols))
         est = t_q + t_g * (m / rows) * (n / cols)
         tot_flops += 2.0 * m * n * k
         tot_s += est
