@@ -79,6 +79,7 @@ def lib():
             "fp4_gemm": (I32, [T, T, P, I64, P, SZ, P]),
             "fp4_linear_workspace_bytes": (SZ, [I32, I64, I64, I64]),
             "fp4_linear": (I32, [P, I64, T, P, P, P, SZ, P]),
+            "fp4_linear_noalloc": (I32, [P, I64, T, P, P, P]),
             "fp4_linear_w4a16": (I32, [P, I64, T, P, I64, P]),
             "fp4_linear_launches": (I32, [I32, I64, I64, I64, I32]),
             "fp4_export_canonical": (I32, [T, T, P]),
@@ -238,6 +239,24 @@ def fp4_linear(x: torch.Tensor, w: Fp4Tensor, static_scale: torch.Tensor | None 
         workspace = torch.zeros(max(nws, 1), dtype=torch.uint8, device=x.device)
     _check(L.fp4_linear(_ptr(x), m, ctypes.byref(w.desc), _ptr(static_scale), _ptr(out),
                         _ptr(workspace), workspace.numel(), _stream(x.device)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def fp4_linear_noalloc(x: torch.Tensor, w: Fp4Tensor, static_scale: torch.Tensor | None = None,
+                       out: torch.Tensor | None = None) -> torch.Tensor:
+    """fp4_linear whose workspace is the library's own device array (the C call
+    allocates nothing; pass `out` to allocate nothing here either)."""
+    x = _bf16_2d(x, "x")
+    m = x.shape[0]
+    if x.shape[1] != w.k:
+        raise ValueError("x has K=%d, weight has K=%d" % (x.shape[1], w.k))
+    if out is None:
+        out = torch.empty(m, w.rows, dtype=torch.bfloat16, device=x.device)
+    _check(lib().fp4_linear_noalloc(_ptr(x), m, ctypes.byref(w.desc), _ptr(static_scale), _ptr(out),
+                                    _stream(x.device)))
     return out
 
 

@@ -195,6 +195,48 @@ fp4_status run_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c, int64_t l
   return FP4_OK;
 }
 
+// ---- allocation-free linear: the workspace is a device array of the library
+//
+// One copy per GPU (the code object is loaded on every device it runs on),
+// held until the process ends. In host code `scratch` only names the array:
+// its device address on the current device comes from hipGetSymbolAddress,
+// taken once per device with that device current, and only that address is
+// handed to kernels.
+static __device__ __align__(256) uint8_t scratch[FP4_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64];  // per device: the address of `scratch` there
+
+__global__ __launch_bounds__(256) void k_zero_words(uint32_t *p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// The array's address on the current device (validated as gfx950). The first
+// call on a device also clears, on `stream`, the words that persist from call
+// to call (the quantizer's exchange words and flags), with a kernel rather than
+// a memset so that it may be captured.
+fp4_status noalloc_scratch(hipStream_t stream, void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || ((uintptr_t)p & 255u)) return fail(FP4_ERR_HIP, "scratch array has no aligned address");
+    const int64_t words = (int64_t)(kQuantScratchBytes / sizeof(uint32_t));
+    hipLaunchKernelGGL(k_zero_words, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
+                       (uint32_t *)p, words);
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "scratch clear launch");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FP4_OK;
+}
+
 // Arguments of a linear call (everything but the workspace).
 fp4_status linear_check(const void *x_bf16, int64_t m, const fp4_tensor *w,
                         const float *static_scale, const void *y_bf16) {
@@ -394,6 +436,22 @@ fp4_status fp4_linear(const void *x_bf16, int64_t m, const fp4_tensor *w,
   if (!aligned16(workspace)) return fail(FP4_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
   if ((st = check_device()) != FP4_OK) return st;
   st = linear_run(x_bf16, m, w, static_scale, y_bf16, workspace, stream);
+  return st == FP4_OK ? ok() : st;
+}
+
+fp4_status fp4_linear_noalloc(const void *x_bf16, int64_t m, const fp4_tensor *w,
+                              const float *static_scale, void *y_bf16, hipStream_t stream) {
+  fp4_status st;
+  if ((st = linear_check(x_bf16, m, w, static_scale, y_bf16)) != FP4_OK) return st;
+  const LinearLayout L = linear_layout(w->fmt, m, w->cols);
+  if (L.total > FP4_NOALLOC_SCRATCH_BYTES)
+    return fail(FP4_ERR_WORKSPACE,
+                "this call needs %zu bytes of workspace; the library's device array holds %zu "
+                "(use fp4_linear with a workspace)", L.total, (size_t)FP4_NOALLOC_SCRATCH_BYTES);
+  if ((st = check_device()) != FP4_OK) return st;
+  void *ws = nullptr;
+  if ((st = noalloc_scratch(stream, &ws)) != FP4_OK) return st;
+  st = linear_run(x_bf16, m, w, static_scale, y_bf16, ws, stream);
   return st == FP4_OK ? ok() : st;
 }
 

@@ -197,6 +197,23 @@ fp4_status fp4_linear(const void *x_bf16, int64_t m, const fp4_tensor *w,
                       size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * fp4_linear for callers that cannot allocate device memory: code under
+ * stream capture, tight serving loops, harnesses that forbid allocation. The
+ * same computation and kernels as fp4_linear, without a workspace argument:
+ * the workspace is a device array inside the library, FP4_NOALLOC_SCRATCH_BYTES
+ * on every GPU the library runs on, held until the process ends. The call
+ * allocates nothing. A call that would need more workspace than that
+ * (fp4_linear_workspace_bytes) returns FP4_ERR_WORKSPACE before launching
+ * anything. All calls on one GPU share that GPU's array, which keeps what the
+ * last call left there: calls that overlap in time on one GPU (other streams
+ * or threads) race and must be serialized by the caller. The first call on a
+ * GPU clears the array's persistent words with a kernel on its stream.
+ */
+#define FP4_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+fp4_status fp4_linear_noalloc(const void *x_bf16, int64_t m, const fp4_tensor *w,
+                              const float *static_scale, void *y_bf16, hipStream_t stream);
+
+/*
  * Weight-only linear (W4A16): y[m, N] (bf16, row stride ldy elements) =
  * bf16_RNE(S_tW * sum_k x[m, k] * (q * s_b)[n, k]) with the activations x
  * [m, K] kept in bf16 (contiguous, 16-byte aligned) and only the cached weight
