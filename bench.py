@@ -50,9 +50,9 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--fmt", default="nvfp4", choices=["nvfp4", "mxfp4"])
-    p.add_argument("--recipe", default="", choices=["", "rotate", "oas", "rotate+oas"],
+    p.add_argument("--recipe", default="", choices=["", "rotate", "oas", "rotate+oas", "mbs"],
                    help="quantization recipe flags for weights and activations: block "
-                        "Hadamard rotation, MXFP4 overflow-aware exponent")
+                        "Hadamard rotation, MXFP4 overflow-aware exponent, MXFP4 macro-block scales")
     p.add_argument("--w4a16", action="store_true",
                    help="time the weight-only linear (bf16 activations x FP4 weights) instead")
     p.add_argument("--workload", default="square16384", choices=WORKLOADS)
@@ -521,6 +521,8 @@ def main():
             if m <= 128:
                 name = "%s<%s,MG=%d>" % ("k_gemm_decode_ring" if qfmt == fp4.NVFP4 else "k_gemm_decode",
                                          args.fmt, 1 if m <= 16 else 2 if m <= 32 else 4 if m <= 64 else 8)
+            elif "mbs" in args.recipe:   # macro-block scales: direct-load tiles
+                name = "k_gemm_prefill<%s,MB>" % args.fmt
             else:   # LDS-staged tiles; 256 x 256 when that fills the 256 CUs
                 big = -(-m // 256) * -(-n // 256) >= 256
                 name = "k_gemm_tile<%s,%s>" % (args.fmt, "256x256" if big else "128x128")
@@ -747,7 +749,7 @@ def cpu_baseline(configs, fmt, args, a_host, w_host):
     import numpy as np
     import oracle
     threads = args.cpu_threads or min(16, len(os.sched_getaffinity(0)))
-    rk = {"rotate": "rotate" in args.recipe, "oas": "oas" in args.recipe}
+    rk = {"rotate": "rotate" in args.recipe, "oas": "oas" in args.recipe, "mbs": "mbs" in args.recipe}
     pool = cf.ThreadPoolExecutor(max_workers=threads)
 
     def chunks(n, parts):
@@ -775,19 +777,20 @@ def cpu_baseline(configs, fmt, args, a_host, w_host):
         parts = list(pool.map(lambda rr: oracle.quantize(fmt, bits[rr[0]:rr[1]], **rk),
                               chunks(bits.shape[0], threads)))
         return oracle.Quantized(fmt, np.concatenate([q.codes for q in parts]),
-                                np.concatenate([q.scales for q in parts]), 1.0, bits.shape[1])
+                                np.concatenate([q.scales for q in parts]), 1.0, bits.shape[1],
+                                np.concatenate([q.macro for q in parts]) if rk["mbs"] else None)
 
     def gemm_par(qa, qw):
         """k-ordered binary64 GEMM, the weight's rows (output columns) split over threads."""
         def run(cc):
-            sub = oracle.Quantized(fmt, qw.codes[cc[0]:cc[1]], qw.scales[cc[0]:cc[1]], qw.tensor_scale, qw.k)
+            sub = qw.row_slice(cc[0], cc[1])
             if args.w4a16:
                 return oracle.gemm_w4a16(qa, sub)
             return oracle.gemm_loop(qa, sub)
         list(pool.map(run, chunks(qw.rows, threads)))
 
     def w_rows(q, r0, r1):
-        return oracle.Quantized(fmt, q.codes[r0:r1], q.scales[r0:r1], q.tensor_scale, q.k)
+        return q.row_slice(r0, r1)
 
     budget = args.cpu_seconds / len(configs)
     tot_flops, tot_s, parts, wq_cache = 0.0, 0.0, [], {}

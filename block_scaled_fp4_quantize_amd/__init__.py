@@ -26,7 +26,7 @@ import torch
 NVFP4, MXFP4 = 0, 1
 # recipe flags OR-ed into a format (include/fp4.h): block Hadamard rotation
 # before quantization; MXFP4 overflow-aware block exponent
-ROTATE, MX_OAS = 0x100, 0x200
+ROTATE, MX_OAS, MX_MBS = 0x100, 0x200, 0x400
 CANONICAL, TILED = 0, 1
 WEIGHT_TILED = TILED
 FORMATS = {"nvfp4": NVFP4, "mxfp4": MXFP4}
@@ -121,13 +121,13 @@ def _fmt(fmt) -> int:
     and "+oas" suffixes), possibly OR-ed with ROTATE / MX_OAS."""
     if isinstance(fmt, str):
         parts = fmt.lower().split("+")
-        flags = {"rotate": ROTATE, "oas": MX_OAS}
+        flags = {"rotate": ROTATE, "oas": MX_OAS, "mbs": MX_MBS}
         fmt = FORMATS[parts[0]]
         for p in parts[1:]:
             fmt |= flags[p]
     fmt = int(fmt)
-    if fmt & 0xFF not in (NVFP4, MXFP4) or fmt & ~(0xFF | ROTATE | MX_OAS):
-        raise ValueError("format must be NVFP4 (0) or MXFP4 (1), optionally | ROTATE | MX_OAS")
+    if fmt & 0xFF not in (NVFP4, MXFP4) or fmt & ~(0xFF | ROTATE | MX_OAS | MX_MBS):
+        raise ValueError("format must be NVFP4 (0) or MXFP4 (1), optionally | ROTATE | MX_OAS | MX_MBS")
     return fmt
 
 
@@ -165,7 +165,14 @@ class Fp4Tensor:
 
     def scales_2d(self) -> torch.Tensor:
         assert self.layout == CANONICAL
-        return self.scales.view(self.rows, self.desc.scales_pitch)
+        return self.scales[: self.rows * self.desc.scales_pitch].view(self.rows, self.desc.scales_pitch)
+
+    def macro_2d(self) -> torch.Tensor:
+        """Canonical macro-block scales (MX_MBS) as float32 [rows, K_pad/128]."""
+        assert self.layout == CANONICAL and self.fmt & MX_MBS
+        off = -(-self.rows * self.desc.scales_pitch // 16) * 16
+        mp = -(-self.k // 128)
+        return self.scales[off: off + self.rows * mp * 4].view(torch.float32).view(self.rows, mp)
 
 
 def fp4_quantize_weight(w: torch.Tensor, fmt=NVFP4) -> Fp4Tensor:

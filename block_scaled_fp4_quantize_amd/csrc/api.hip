@@ -65,18 +65,36 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 // A format value is a base format (low byte) with optional recipe flags.
 int base_fmt(int32_t f) { return f & 0xFF; }
 uint32_t recipe_of(int32_t f) {
-  return ((f & FP4_ROTATE) ? kRecipeRotate : 0u) | ((f & FP4_MX_OAS) ? kRecipeOas : 0u);
+  return ((f & FP4_ROTATE) ? kRecipeRotate : 0u) | ((f & FP4_MX_OAS) ? kRecipeOas : 0u) |
+         ((f & FP4_MX_MBS) ? kRecipeMbs : 0u);
 }
+bool has_mbs(int32_t f) { return (f & FP4_MX_MBS) != 0; }
 bool valid_fmt(int32_t f) {
   const int b = base_fmt(f);
   if (b != FP4_NVFP4 && b != FP4_MXFP4) return false;
-  if (f & ~(0xFF | FP4_ROTATE | FP4_MX_OAS)) return false;
-  return !(f & FP4_MX_OAS) || b == FP4_MXFP4;
+  if (f & ~(0xFF | FP4_ROTATE | FP4_MX_OAS | FP4_MX_MBS)) return false;
+  return !(f & (FP4_MX_OAS | FP4_MX_MBS)) || b == FP4_MXFP4;
 }
-// Operands of one product: same base format and both rotated or neither (the
-// block exponent rule may differ).
+// Operands of one product: same base format, both rotated or neither, both
+// with macro-block scales or neither (the block exponent rule may differ).
 bool same_product_fmt(int32_t a, int32_t w) {
-  return base_fmt(a) == base_fmt(w) && (a & FP4_ROTATE) == (w & FP4_ROTATE);
+  return base_fmt(a) == base_fmt(w) && (a & FP4_ROTATE) == (w & FP4_ROTATE) &&
+         has_mbs(a) == has_mbs(w);
+}
+
+// Macro-block scales (MXFP4 with MBS) follow a tensor's E8M0 bytes in its
+// scales buffer: tiled, 16 floats per fragment after the fragments' E8M0
+// bytes; canonical, [rows][K_pad / 128] floats from the first 16-byte
+// boundary past rows * scales_pitch bytes.
+int64_t macro_pitch(int64_t k) { return k_pad(k) / kFragK; }
+size_t macro_offset(int32_t layout, int64_t rows, int64_t k, int64_t scales_pitch) {
+  if (layout == FP4_LAYOUT_TILED)
+    return (size_t)(round_up(rows, 16) / 16 * (k_pad(k) / kFragK) * 64);
+  return (size_t)round_up(rows * scales_pitch, 16);
+}
+float *macro_of(const fp4_tensor *t) {
+  if (!has_mbs(t->fmt)) return nullptr;
+  return (float *)((uint8_t *)t->scales + macro_offset(t->layout, t->rows, t->cols, t->scales_pitch));
 }
 bool valid_layout(int32_t l) { return l == FP4_LAYOUT_CANONICAL || l == FP4_LAYOUT_TILED; }
 
@@ -121,7 +139,8 @@ fp4_status check_tensor(const fp4_tensor *t, const char *name) {
 // for one or two activation rows (measured on the decode shapes: at M = 8 the
 // separate quantizer plus the skinny GEMM is faster).
 bool use_fused(int32_t fmt, int64_t m, int64_t n, int64_t k) {
-  return linear_fused_ok(base_fmt(fmt), m, n, k) && (!(fmt & FP4_ROTATE) || m <= 2);
+  return linear_fused_ok(base_fmt(fmt), m, n, k) && (!(fmt & FP4_ROTATE) || m <= 2) &&
+         !has_mbs(fmt);
 }
 
 size_t quant_ws(int32_t fmt) { return base_fmt(fmt) == FP4_NVFP4 ? kQuantScratchBytes : 0; }
@@ -134,6 +153,12 @@ struct LinearLayout {
   size_t codes, scales, ts, scratch, total;
 };
 
+// Bytes of a tiled tensor's scales buffer (with the macro-block scales).
+size_t tiled_scales_bytes(int32_t fmt, int64_t rows, int64_t k) {
+  const int64_t mp = round_up(rows, 16), kp = k_pad(k);
+  return (size_t)(mp * kp / block_of(base_fmt(fmt))) + (has_mbs(fmt) ? (size_t)(mp * kp / 32) : 0);
+}
+
 LinearLayout linear_layout(int32_t fmt, int64_t m, int64_t k) {
   LinearLayout L;
   const int64_t mp = round_up(m, 16), kp = k_pad(k);
@@ -141,7 +166,7 @@ LinearLayout linear_layout(int32_t fmt, int64_t m, int64_t k) {
   L.scratch = off; off = align256(off + kQuantScratchBytes);
   L.ts = off; off = align256(off + sizeof(float));
   L.codes = off; off = align256(off + (size_t)(mp * kp / 2));
-  L.scales = off; off = align256(off + (size_t)(mp * kp / block_of(base_fmt(fmt))));
+  L.scales = off; off = align256(off + tiled_scales_bytes(fmt, m, k));
   L.total = off;
   return L;
 }
@@ -152,8 +177,8 @@ fp4_status run_quant(int32_t fmt, int tiled, const void *x, int64_t rows, int64_
   const int base = base_fmt(fmt);
   hipError_t e = launch_quantize(base, recipe_of(fmt), tiled, (const uint16_t *)x, rows, k,
                                  static_scale, (uint8_t *)out->codes, out->codes_pitch,
-                                 (uint8_t *)out->scales, out->scales_pitch,
-                                 base == FP4_NVFP4 ? out->tensor_scale : nullptr,
+                                 (uint8_t *)out->scales, out->scales_pitch, macro_of(out),
+                                 macro_pitch(k), base == FP4_NVFP4 ? out->tensor_scale : nullptr,
                                  (uint32_t *)scratch, stream);
   if (e != hipSuccess) return hip_fail(e, "quantize launch");
   return FP4_OK;
@@ -170,7 +195,7 @@ RetileLayout retile_layout(int32_t fmt, int64_t m, int64_t k) {
   const int64_t mp = round_up(m, 16), kp = k_pad(k);
   L.codes = 0;
   L.scales = align256((size_t)(mp * kp / 2));
-  L.total = align256(L.scales + (size_t)(mp * kp / block_of(base_fmt(fmt))));
+  L.total = align256(L.scales + tiled_scales_bytes(fmt, m, k));
   return L;
 }
 
@@ -186,11 +211,14 @@ fp4_status run_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c, int64_t l
   g.w_ts = w->tensor_scale;
   g.m = a->rows; g.n = w->rows; g.k = a->cols;
   g.c = (uint16_t *)c; g.ldc = ldc;
+  g.a_ms = macro_of(a); g.a_mpitch = macro_pitch(a->cols);
+  g.w_ms = macro_of(w);
   // skinny M: stream W once; large M with tiled activations: LDS-staged
-  // tiles; large M with canonical activations: direct-load tiles
-  hipError_t e = g.m <= kDecodeMaxM ? launch_gemm_decode(g, stream)
-                 : g.a_tiled        ? launch_gemm_tile(g, 0, stream)
-                                    : launch_gemm_prefill(g, stream);
+  // tiles; large M with canonical activations (or macro-block scales):
+  // direct-load tiles
+  hipError_t e = g.m <= kDecodeMaxM           ? launch_gemm_decode(g, stream)
+                 : g.a_tiled && !has_mbs(a->fmt) ? launch_gemm_tile(g, 0, stream)
+                                              : launch_gemm_prefill(g, stream);
   if (e != hipSuccess) return hip_fail(e, "gemm launch");
   return FP4_OK;
 }
@@ -299,8 +327,10 @@ size_t fp4_codes_bytes(int32_t fmt, int32_t layout, int64_t rows, int64_t k) {
 
 size_t fp4_scales_bytes(int32_t fmt, int32_t layout, int64_t rows, int64_t k) {
   if (!valid_fmt(fmt) || !valid_layout(layout) || rows <= 0 || k <= 0) return 0;
-  int64_t r = layout == FP4_LAYOUT_TILED ? round_up(rows, 16) : rows;
-  return (size_t)(r * (k_pad(k) / block_of(base_fmt(fmt))));
+  if (layout == FP4_LAYOUT_TILED) return tiled_scales_bytes(fmt, rows, k);
+  const int64_t pitch = k_pad(k) / block_of(base_fmt(fmt));
+  if (!has_mbs(fmt)) return (size_t)(rows * pitch);
+  return macro_offset(layout, rows, k, pitch) + (size_t)(rows * macro_pitch(k)) * sizeof(float);
 }
 
 fp4_status fp4_tensor_init(fp4_tensor *t, int32_t fmt, int32_t layout, int64_t rows, int64_t k,
@@ -385,7 +415,7 @@ fp4_status fp4_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c_bf16, int6
   if (w->layout != FP4_LAYOUT_TILED)
     return fail(FP4_ERR_FORMAT_MISMATCH, "w must be in the TILED layout");
   if (!same_product_fmt(a->fmt, w->fmt))
-    return fail(FP4_ERR_FORMAT_MISMATCH, "a and w differ in format or rotation");
+    return fail(FP4_ERR_FORMAT_MISMATCH, "a and w differ in format, rotation or macro-block scaling");
   if (a->cols != w->cols) return fail(FP4_ERR_SHAPE, "a and w differ in K");
   if (!c_bf16) return fail(FP4_ERR_INVALID_ARG, "output pointer is null");
   if (ldc < w->rows) return fail(FP4_ERR_SHAPE, "ldc smaller than N");
@@ -403,16 +433,17 @@ fp4_status fp4_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c_bf16, int6
     // canonical activations of a large M: tiled copy in the workspace, then
     // the tile kernel (without the workspace: the direct-load kernel)
     char *ws = (char *)workspace;
-    hipError_t e = launch_import_tiled(base_fmt(a->fmt), (const uint8_t *)a->codes, a->codes_pitch,
-                                       (const uint8_t *)a->scales, a->scales_pitch, a->rows,
-                                       a->cols, (uint8_t *)ws + R.codes, (uint8_t *)ws + R.scales,
-                                       stream);
-    if (e != hipSuccess) return hip_fail(e, "activation re-tiling launch");
     fp4_tensor t = *a;
     t.layout = FP4_LAYOUT_TILED;
     t.codes_pitch = t.scales_pitch = 0;
     t.codes = ws + R.codes;
     t.scales = ws + R.scales;
+    hipError_t e = launch_import_tiled(base_fmt(a->fmt), (const uint8_t *)a->codes, a->codes_pitch,
+                                       (const uint8_t *)a->scales, a->scales_pitch, macro_of(a),
+                                       macro_pitch(a->cols), a->rows, a->cols,
+                                       (uint8_t *)t.codes, (uint8_t *)t.scales, macro_of(&t),
+                                       stream);
+    if (e != hipSuccess) return hip_fail(e, "activation re-tiling launch");
     st = run_gemm(&t, w, c_bf16, ldc, stream);
     return st == FP4_OK ? ok() : st;
   }
@@ -464,6 +495,9 @@ fp4_status fp4_linear_w4a16(const void *x_bf16, int64_t m, const fp4_tensor *w, 
   if (w->fmt & FP4_ROTATE)
     return fail(FP4_ERR_FORMAT_MISMATCH,
                 "a rotated weight needs rotated activations: use fp4_linear");
+  if (has_mbs(w->fmt))
+    return fail(FP4_ERR_FORMAT_MISMATCH,
+                "the weight-only linear takes no macro-block scales: use fp4_linear");
   const int64_t k = w->cols, n = w->rows;
   if ((st = check_shape(w->fmt, m, k)) != FP4_OK) return st;
   if (!x_bf16 || !y_bf16) return fail(FP4_ERR_INVALID_ARG, "null input or output");
@@ -501,10 +535,10 @@ fp4_status fp4_export_canonical(const fp4_tensor *tiled, fp4_tensor *canonical,
   if ((st = check_device()) != FP4_OK) return st;
   const int base = base_fmt(tiled->fmt);
   hipError_t e = launch_export_canonical(
-      base, (const uint8_t *)tiled->codes, (const uint8_t *)tiled->scales, tiled->rows,
-      tiled->cols, (uint8_t *)canonical->codes, canonical->codes_pitch,
-      (uint8_t *)canonical->scales, canonical->scales_pitch,
-      base == FP4_NVFP4 ? tiled->tensor_scale : nullptr,
+      base, (const uint8_t *)tiled->codes, (const uint8_t *)tiled->scales, macro_of(tiled),
+      tiled->rows, tiled->cols, (uint8_t *)canonical->codes, canonical->codes_pitch,
+      (uint8_t *)canonical->scales, canonical->scales_pitch, macro_of(canonical),
+      macro_pitch(canonical->cols), base == FP4_NVFP4 ? tiled->tensor_scale : nullptr,
       base == FP4_NVFP4 ? canonical->tensor_scale : nullptr, stream);
   if (e != hipSuccess) return hip_fail(e, "export launch");
   return ok();
@@ -520,9 +554,9 @@ fp4_status fp4_dequantize(const fp4_tensor *t, float *out_f32, int64_t ldo, hipS
   const int base = base_fmt(t->fmt);
   hipError_t e = launch_dequant(base, t->layout == FP4_LAYOUT_TILED,
                                 (const uint8_t *)t->codes, t->codes_pitch,
-                                (const uint8_t *)t->scales, t->scales_pitch,
-                                base == FP4_NVFP4 ? t->tensor_scale : nullptr, t->rows, t->cols,
-                                out_f32, ldo, stream);
+                                (const uint8_t *)t->scales, t->scales_pitch, macro_of(t),
+                                macro_pitch(t->cols), base == FP4_NVFP4 ? t->tensor_scale : nullptr,
+                                t->rows, t->cols, out_f32, ldo, stream);
   if (e != hipSuccess) return hip_fail(e, "dequantize launch");
   return ok();
 }

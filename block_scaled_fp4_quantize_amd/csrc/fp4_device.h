@@ -323,6 +323,88 @@ __device__ __forceinline__ void mx_encode_block(const uint4 (&v)[4], uint4 &code
   sbyte = (uint32_t)(e + 127);
 }
 
+// ---- MXFP4 macro-block scaling (MBS) ----
+//
+// "FP4 n'existe pas ..." (section "L'ecart de qualite - et comment il se
+// reduit") adds to MXFP4 a second-level scale over a macro-block of several
+// 32-value blocks. Here a macro-block is the four blocks of one 128-value
+// segment of a row along K (one fragment of the tiled layout), and its scale
+// is the FP32 number S_mb in [1, 2) that puts the segment's largest magnitude
+// g on the top code: S_mb = RN_fp32(g / (6 * 2^j)), j = floor(log2(g / 6))
+// (1 when g = 0). Each block's E8M0 exponent is the MX rule applied to its
+// values divided by S_mb, and elements round against d_b = 2^e_b * S_mb.
+
+// S_mb from the segment maximum's bf16 bits (sign clear). g / 6 is a correctly
+// rounded binary64 division; it never rounds across a power of two (g has 8
+// significant bits) and its binary expansion (g / 3 / 2) never lies on a
+// binary32 midpoint it was not on exactly, so the binary32 rounding of it is
+// that of the real quotient.
+__device__ __forceinline__ float mbs_scale_from_bits(uint32_t gbits) {
+  if (gbits == 0u) return 1.0f;
+  const double q = (double)bf16_bits_to_f32(gbits) / 6.0;
+  int e2;
+  (void)frexp(q, &e2);
+  return (float)ldexp(q, 1 - e2);
+}
+
+// E8M0 exponent of a block with maximum bits abits under S_mb = s:
+// clamp(floor(log2(a_b / s)) - 2, -127, 127), floor(log2(a_b / s)) being
+// floor(log2 a_b) or one less as a_b < s * 2^floor(log2 a_b) (an exact
+// binary64 product); oas: the smallest e with a_b <= 6 * 2^e * s.
+__device__ __forceinline__ int mbs_exponent(uint32_t abits, float s, bool oas) {
+  if (abits == 0u) return -127;
+  const double ab = (double)bf16_bits_to_f32(abits);
+  int e2;
+  (void)frexp(ab, &e2);
+  int fl = e2 - 1;
+  if (ab < (double)s * ldexp(1.0, fl)) fl -= 1;
+  int e = fl - 2;
+  e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  if (oas && e < 127 && ab > 6.0 * ldexp(1.0, e) * (double)s) e += 1;
+  return e;
+}
+
+// E2M1 codes of 8 bf16 values against d_b = 2^e * s (s in [1, 2)): with
+// y = |x| * 2^-e (exact, or below 2^-126 where every code is 0 anyway), the
+// midpoint tests compare y with t * s. Both are multiples of 2^-25 wherever
+// y >= 2^-18 (t has two fraction bits, s 23; y keeps 8 significant bits), so
+// the nonzero difference fma(t, s, -y) keeps its sign through the rounding;
+// below that y < t * s for every t. Ties go to the even index, 6 saturates.
+__device__ __forceinline__ uint32_t mbs_encode8(int e, float s, uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t out = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t b = (w[i] >> (16 * h)) & 0xFFFFu;
+      const float y = ldexpf(bf16_bits_to_f32(b & 0x7FFFu), -e);
+      uint32_t m = 0;
+      m += (__builtin_fmaf(0.25f, s, -y) < 0.0f);
+      m += (__builtin_fmaf(0.75f, s, -y) <= 0.0f);
+      m += (__builtin_fmaf(1.25f, s, -y) < 0.0f);
+      m += (__builtin_fmaf(1.75f, s, -y) <= 0.0f);
+      m += (__builtin_fmaf(2.5f, s, -y) < 0.0f);
+      m += (__builtin_fmaf(3.5f, s, -y) <= 0.0f);
+      m += (__builtin_fmaf(5.0f, s, -y) < 0.0f);
+      out |= (m | ((b >> 12) & 8u)) << (4 * (2 * i + h));
+    }
+  }
+  return out;
+}
+
+// One MXFP4 block (32 values) under macro-block scale s: 16 code bytes and
+// the E8M0 byte.
+__device__ __forceinline__ void mbs_encode_block(const uint4 (&v)[4], float s, uint4 &codes,
+                                                 uint32_t &sbyte, bool oas) {
+  const uint32_t abits = max(max(absmax_bits8(v[0]), absmax_bits8(v[1])),
+                             max(absmax_bits8(v[2]), absmax_bits8(v[3])));
+  const int e = mbs_exponent(abits, s, oas);
+  codes = make_uint4(mbs_encode8(e, s, v[0]), mbs_encode8(e, s, v[1]), mbs_encode8(e, s, v[2]),
+                     mbs_encode8(e, s, v[3]));
+  sbyte = (uint32_t)(e + 127);
+}
+
 // ---- block rotation ----
 //
 // y_i = RN_bf16(c * sum_j H[i][j] x_j) over one block of B bf16 values, H_B

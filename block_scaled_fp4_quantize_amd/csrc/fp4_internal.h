@@ -48,31 +48,39 @@ bool quant_fits_small(int fmt, int64_t rows, int64_t k, int tiled);
 // quantized; MXFP4 overflow-aware block exponent.
 constexpr uint32_t kRecipeRotate = 1u;
 constexpr uint32_t kRecipeOas = 2u;
+constexpr uint32_t kRecipeMbs = 4u;   // MXFP4 macro-block scales (one FP32 per 128-value segment)
 
 // Quantize x [rows, k] (bf16, row-major) into the canonical (tiled = 0) or
 // fragment-tiled (tiled = 1) layout; fmt 0 = NVFP4, 1 = MXFP4. NVFP4 takes S_t
 // from *static_scale when non-null, else from the tensor's maximum (of the
 // rotated values when rotating); writes *ts_out when non-null. `scratch` holds
-// kQuantScratchBytes.
+// kQuantScratchBytes. MXFP4 with kRecipeMbs writes the macro-block scales to
+// `macro`: canonical [rows][mpitch] floats, tiled [fragment][16 rows] floats.
 hipError_t launch_quantize(int fmt, uint32_t recipe, int tiled, const uint16_t *x, int64_t rows,
                            int64_t k, const float *static_scale, uint8_t *codes, int64_t cpitch,
-                           uint8_t *scales, int64_t spitch, float *ts_out, uint32_t *scratch,
-                           hipStream_t stream);
+                           uint8_t *scales, int64_t spitch, float *macro, int64_t mpitch,
+                           float *ts_out, uint32_t *scratch, hipStream_t stream);
 
+// Macro-block scale arrays (MBS) travel with the codes in the export, import
+// and dequantization: tiled [fragment][16] floats, canonical [rows][mpitch]
+// floats; nullptr without MBS.
 hipError_t launch_export_canonical(int fmt, const uint8_t *tcodes, const uint8_t *tscales,
-                                   int64_t rows, int64_t k, uint8_t *codes, int64_t cpitch,
-                                   uint8_t *scales, int64_t spitch, const float *ts_in,
-                                   float *ts_out, hipStream_t stream);
+                                   const float *tmacro, int64_t rows, int64_t k, uint8_t *codes,
+                                   int64_t cpitch, uint8_t *scales, int64_t spitch, float *macro,
+                                   int64_t mpitch, const float *ts_in, float *ts_out,
+                                   hipStream_t stream);
 
 // Canonical [rows, k] codes/scales -> the fragment-tiled layout (rows padded
 // to 16, zero padding).
 hipError_t launch_import_tiled(int fmt, const uint8_t *codes, int64_t cpitch, const uint8_t *scales,
-                              int64_t spitch, int64_t rows, int64_t k, uint8_t *tcodes,
-                              uint8_t *tscales, hipStream_t stream);
+                              int64_t spitch, const float *macro, int64_t mpitch, int64_t rows,
+                              int64_t k, uint8_t *tcodes, uint8_t *tscales, float *tmacro,
+                              hipStream_t stream);
 
 hipError_t launch_dequant(int fmt, int tiled, const uint8_t *codes, int64_t cpitch,
-                          const uint8_t *scales, int64_t spitch, const float *ts, int64_t rows,
-                          int64_t k, float *out, int64_t ldo, hipStream_t stream);
+                          const uint8_t *scales, int64_t spitch, const float *macro,
+                          int64_t mpitch, const float *ts, int64_t rows, int64_t k, float *out,
+                          int64_t ldo, hipStream_t stream);
 
 struct GemmArgs {
   int fmt;
@@ -84,6 +92,10 @@ struct GemmArgs {
   const float *w_ts;
   int64_t m, n, k;
   uint16_t *c; int64_t ldc;
+  // MXFP4 macro-block scales (both operands, or neither): A tiled
+  // [fragment][16] or canonical [m][a_mpitch] floats, W tiled [fragment][16]
+  const float *a_ms = nullptr; int64_t a_mpitch = 0;
+  const float *w_ms = nullptr;
 };
 
 hipError_t launch_gemm_prefill(const GemmArgs &g, hipStream_t stream);

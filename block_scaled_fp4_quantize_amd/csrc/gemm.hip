@@ -40,6 +40,29 @@ __device__ __forceinline__ v4f mfma_nv(const h8v a[4], const h8v b[4], v4f c) {
   return c;
 }
 
+// MXFP4 with macro-block scales: one fragment (K = 128, one 128-value segment
+// of both operands) as its own product, added with the segment scales of its
+// output rows and columns: acc += p * (s4 * s1), s4 the scales of the lane's
+// four accumulator rows, s1 that of its column.
+__device__ __forceinline__ v4f mfma_mx_mbs(uint4 a, uint4 b, v4f c, uint32_t sa, uint32_t sb,
+                                           float4 s4, float s1) {
+  const v4f p = mfma_mx(a, b, v4f{0.f, 0.f, 0.f, 0.f}, sa, sb);
+  c[0] = __builtin_fmaf(p[0], s4.x * s1, c[0]);
+  c[1] = __builtin_fmaf(p[1], s4.y * s1, c[1]);
+  c[2] = __builtin_fmaf(p[2], s4.z * s1, c[2]);
+  c[3] = __builtin_fmaf(p[3], s4.w * s1, c[3]);
+  return c;
+}
+
+// Macro-block scale of activation row `row` at fragment kt (0 past m).
+template <int ATILED>
+__device__ __forceinline__ float a_macro(const float *a_ms, int64_t a_mp, int kt_n, int row, int kt,
+                                         int m) {
+  if (row >= m) return 0.f;
+  return ATILED ? a_ms[((int64_t)(row >> 4) * kt_n + kt) * 16 + (row & 15)]
+                : a_ms[(int64_t)row * a_mp + kt];
+}
+
 // One lane's part of the A fragment (16 rows from 16*g, K values 128*kt ..
 // 128*kt+127): 16 bytes of codes and its scale bytes, from the canonical
 // layout (row-major, 64 bytes of a row per fragment) or the tiled layout (the
@@ -84,12 +107,14 @@ __device__ __forceinline__ void load_w(const uint8_t *__restrict__ w_codes,
 // operand registers: an A fragment lane l reads 16 bytes of row (l % 16) at
 // K offset 32 (l / 16) of the canonical layout; a W fragment is one 1 KB
 // contiguous tile of the weight cache.
-template <int FMT, int ATILED>
+// MB: MXFP4 with macro-block scales (a_ms, w_ms).
+template <int FMT, int ATILED, int MB = 0>
 __global__ __launch_bounds__(256) void k_gemm_prefill(
     const uint8_t *__restrict__ a_codes, int64_t a_cp, const uint8_t *__restrict__ a_sc,
     int64_t a_sp, const float *__restrict__ a_ts, const uint8_t *__restrict__ w_codes,
     const uint8_t *__restrict__ w_sc, const float *__restrict__ w_ts, int m, int n, int kt_n,
-    int nt_n, uint16_t *__restrict__ c, int64_t ldc) {
+    int nt_n, uint16_t *__restrict__ c, int64_t ldc, const float *__restrict__ a_ms,
+    int64_t a_mp, const float *__restrict__ w_ms) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int m0 = blockIdx.y * 128 + (wave >> 1) * 64;
@@ -117,7 +142,28 @@ __global__ __launch_bounds__(256) void k_gemm_prefill(
         ws[j] = 0u;
       }
     }
-    if (FMT == 1) {
+    if (FMT == 1 && MB) {
+      // accumulator rows are activation rows 16 i + 4 lc + r, its column the
+      // weight row 16 j + lr
+      float4 sa[4];
+      float sw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r0 = m0 + 16 * i + 4 * lc;
+        sa[i] = make_float4(a_macro<ATILED>(a_ms, a_mp, kt_n, r0, kt, m),
+                            a_macro<ATILED>(a_ms, a_mp, kt_n, r0 + 1, kt, m),
+                            a_macro<ATILED>(a_ms, a_mp, kt_n, r0 + 2, kt, m),
+                            a_macro<ATILED>(a_ms, a_mp, kt_n, r0 + 3, kt, m));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sw[j] = nt0 + j < nt_n ? w_ms[((int64_t)(nt0 + j) * kt_n + kt) * 16 + lr] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = mfma_mx_mbs(aq[i], wq[j], acc[i][j], as[i], ws[j], sa[i], sw[j]);
+    } else if (FMT == 1) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -169,12 +215,15 @@ __global__ __launch_bounds__(256) void k_gemm_prefill(
 constexpr int kDecWaves = 8;
 constexpr int kDecFrags = 2;
 
-template <int FMT, int MG, int ATILED, int NT>
+// MB: MXFP4 with macro-block scales (a_ms, w_ms): each fragment's product is
+// added with its rows' and columns' segment scales.
+template <int FMT, int MG, int ATILED, int NT, int MB = 0>
 __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(
     const uint8_t *__restrict__ a_codes, int64_t a_cp, const uint8_t *__restrict__ a_sc,
     int64_t a_sp, const float *__restrict__ a_ts, const uint8_t *__restrict__ w_codes,
     const uint8_t *__restrict__ w_sc, const float *__restrict__ w_ts, int m, int n, int kt_n,
-    int nt_n, uint16_t *__restrict__ c, int64_t ldc) {
+    int nt_n, uint16_t *__restrict__ c, int64_t ldc, const float *__restrict__ a_ms,
+    int64_t a_mp, const float *__restrict__ w_ms) {
   // fragments per group: two, or one for eight activation groups (registers)
   constexpr int NW = kDecWaves, FM = MG >= 8 ? 1 : kDecFrags;
   __shared__ float red[NW][NT * MG][4][64];
@@ -191,6 +240,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(
     for (int g = 0; g < MG; ++g) acc[t][g] = v4f{0.f, 0.f, 0.f, 0.f};
   uint4 wq[2][FM][NT], aq[2][FM][MG];
   uint32_t ws[2][FM][NT], as[2][FM][MG];
+  float4 wm[2][FM][NT];   // MB: the lane's four weight rows' segment scales
+  float am[2][FM][MG];    // MB: its activation row's
 
   auto load = [&](int buf, int base) {
 #pragma unroll
@@ -202,11 +253,15 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(
           // a tile past the last one reads the last again (its sums are never stored)
           const int nt = min(nt0 + t, nt_n - 1);
           load_w<FMT>(w_codes, w_sc, (int64_t)nt * kt_n + kt, lane, wq[buf][u][t], ws[buf][u][t]);
+          if (MB)
+            wm[buf][u][t] = *(const float4 *)(w_ms + ((int64_t)nt * kt_n + kt) * 16 + 4 * (lane >> 4));
         }
 #pragma unroll
-        for (int g = 0; g < MG; ++g)
+        for (int g = 0; g < MG; ++g) {
           load_a<FMT, ATILED>(a_codes, a_cp, a_sc, a_sp, kt_n, g, kt, lane, m, aq[buf][u][g],
                               as[buf][u][g]);
+          if (MB) am[buf][u][g] = a_macro<ATILED>(a_ms, a_mp, kt_n, 16 * g + (lane & 15), kt, m);
+        }
       }
     }
   };
@@ -214,7 +269,14 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(
 #pragma unroll
     for (int u = 0; u < FM; ++u) {
       if (base + NW * u >= kt_n) break;  // wave-uniform
-      if (FMT == 1) {
+      if (FMT == 1 && MB) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int g = 0; g < MG; ++g)
+            acc[t][g] = mfma_mx_mbs(wq[buf][u][t], aq[buf][u][g], acc[t][g], ws[buf][u][t],
+                                    as[buf][u][g], wm[buf][u][t], am[buf][u][g]);
+      } else if (FMT == 1) {
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -577,14 +639,17 @@ hipError_t launch_gemm_prefill(const GemmArgs &g, hipStream_t stream) {
   const int kt_n = (int)(k_pad(g.k) / kFragK);
   const int nt_n = (int)(round_up(g.n, 16) / 16);
   dim3 grid((unsigned)((g.n + 127) / 128), (unsigned)((g.m + 127) / 128));
-#define FP4_PRE(F, T)                                                                          \
-  hipLaunchKernelGGL((k_gemm_prefill<F, T>), grid, dim3(256), 0, stream, g.a_codes,           \
+#define FP4_PRE(F, T, MB)                                                                      \
+  hipLaunchKernelGGL((k_gemm_prefill<F, T, MB>), grid, dim3(256), 0, stream, g.a_codes,       \
                      g.a_cpitch, g.a_scales, g.a_spitch, g.a_ts, g.w_codes, g.w_scales, g.w_ts, \
-                     (int)g.m, (int)g.n, kt_n, nt_n, g.c, g.ldc)
-  if (g.fmt == 0 && !g.a_tiled) FP4_PRE(0, 0);
-  else if (g.fmt == 0) FP4_PRE(0, 1);
-  else if (!g.a_tiled) FP4_PRE(1, 0);
-  else FP4_PRE(1, 1);
+                     (int)g.m, (int)g.n, kt_n, nt_n, g.c, g.ldc, g.a_ms, g.a_mpitch, g.w_ms)
+  const bool mb = g.fmt == 1 && g.w_ms;
+  if (g.fmt == 0 && !g.a_tiled) FP4_PRE(0, 0, 0);
+  else if (g.fmt == 0) FP4_PRE(0, 1, 0);
+  else if (mb && !g.a_tiled) FP4_PRE(1, 0, 1);
+  else if (mb) FP4_PRE(1, 1, 1);
+  else if (!g.a_tiled) FP4_PRE(1, 0, 0);
+  else FP4_PRE(1, 1, 0);
 #undef FP4_PRE
   return hipGetLastError();
 }
@@ -633,11 +698,19 @@ hipError_t launch_gemm_decode(const GemmArgs &g, hipStream_t stream) {
   // K = 5120, 18.3 -> 17.4 us at K = 17408)
   const int nt_per = (mg == 2 && nt_n >= 512) ? 2 : 1;
   dim3 grid((unsigned)((nt_n + nt_per - 1) / nt_per));
-#define FP4_DEC(F, G, T, P)                                                                     \
-  hipLaunchKernelGGL((k_gemm_decode<F, G, T, P>), grid, dim3(64 * kDecWaves), 0, stream,       \
+#define FP4_DEC(F, G, T, P, MB)                                                                 \
+  hipLaunchKernelGGL((k_gemm_decode<F, G, T, P, MB>), grid, dim3(64 * kDecWaves), 0, stream,   \
                      g.a_codes, g.a_cpitch, g.a_scales, g.a_spitch, g.a_ts, g.w_codes,         \
-                     g.w_scales, g.w_ts, (int)g.m, (int)g.n, kt_n, nt_n, g.c, g.ldc)
-#define FP4_DEC_T(F, G, P) do { if (g.a_tiled) FP4_DEC(F, G, 1, P); else FP4_DEC(F, G, 0, P); } while (0)
+                     g.w_scales, g.w_ts, (int)g.m, (int)g.n, kt_n, nt_n, g.c, g.ldc, g.a_ms,   \
+                     g.a_mpitch, g.w_ms)
+#define FP4_DEC_T(F, G, P)                                                 \
+  do {                                                                     \
+    if (g.w_ms) {                                                          \
+      if (g.a_tiled) FP4_DEC(F, G, 1, P, 1); else FP4_DEC(F, G, 0, P, 1); \
+    } else {                                                               \
+      if (g.a_tiled) FP4_DEC(F, G, 1, P, 0); else FP4_DEC(F, G, 0, P, 0); \
+    }                                                                      \
+  } while (0)
   if (mg == 1) FP4_DEC_T(1, 1, 1);
   else if (mg == 2 && nt_per == 2) FP4_DEC_T(1, 2, 2);
   else if (mg == 2) FP4_DEC_T(1, 2, 1);

@@ -74,9 +74,29 @@ __device__ __forceinline__ uint32_t block_absmax(const uint4 (&v)[Blk<FMT>::V]) 
 }
 
 // Recipe bits (a kernel argument, uniform over the grid): rotate each block
-// before anything else looks at its values; MXFP4 overflow-aware exponent.
+// before anything else looks at its values; MXFP4 overflow-aware exponent;
+// MXFP4 macro-block scales.
 __device__ __forceinline__ bool rotates(uint32_t recipe) { return recipe & kRecipeRotate; }
 __device__ __forceinline__ bool oas_rule(uint32_t recipe) { return recipe & kRecipeOas; }
+__device__ __forceinline__ bool mbs(uint32_t recipe) { return recipe & kRecipeMbs; }
+
+// Macro-block scale of a 128-value segment whose four blocks sit on lanes
+// lane ^ {0, D, 2D, 3D} (D = 1: one block per thread, consecutive threads;
+// D = 16: the tiled kernel's lane groups), from each lane's block maximum.
+template <int D>
+__device__ __forceinline__ float segment_mbs_scale(uint32_t bmax) {
+  uint32_t g = max(bmax, (uint32_t)__shfl_xor((int)bmax, D, 64));
+  g = max(g, (uint32_t)__shfl_xor((int)g, 2 * D, 64));
+  return mbs_scale_from_bits(g);
+}
+
+// Where the macro-block scale of segment seg of row r goes.
+template <int TILED>
+__device__ __forceinline__ float *macro_dst(int64_t r, int64_t seg, int64_t kt_n, float *macro,
+                                            int64_t mpitch) {
+  if (!TILED) return macro + r * mpitch + seg;
+  return macro + ((r >> 4) * kt_n + seg) * 16 + (r & 15);
+}
 
 template <int FMT>
 __device__ __forceinline__ void maybe_rotate(uint4 (&v)[Blk<FMT>::V], uint32_t recipe) {
@@ -84,8 +104,9 @@ __device__ __forceinline__ void maybe_rotate(uint4 (&v)[Blk<FMT>::V], uint32_t r
 }
 
 // Encode one block (values in v) and store codes + scale byte.
+// smb: the block's macro-block scale (MXFP4 with MBS).
 template <int FMT>
-__device__ __forceinline__ void encode_store(const uint4 (&v)[Blk<FMT>::V], float st,
+__device__ __forceinline__ void encode_store(const uint4 (&v)[Blk<FMT>::V], float st, float smb,
                                              uint8_t *cdst, uint8_t *sdst, uint32_t recipe) {
   uint32_t sbyte;
   if constexpr (FMT == 0) {
@@ -94,7 +115,8 @@ __device__ __forceinline__ void encode_store(const uint4 (&v)[Blk<FMT>::V], floa
     *(uint2 *)cdst = c;
   } else {
     uint4 c;
-    mx_encode_block(v, c, sbyte, oas_rule(recipe));
+    if (mbs(recipe)) mbs_encode_block(v, smb, c, sbyte, oas_rule(recipe));
+    else mx_encode_block(v, c, sbyte, oas_rule(recipe));
     *(uint4 *)cdst = c;
   }
   *sdst = (uint8_t)sbyte;
@@ -145,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void k_quant(
     const uint16_t *__restrict__ x, int64_t rows, int64_t k, int64_t rows_pad, int64_t kt_n,
     const uint32_t *__restrict__ parts, int nparts, const float *__restrict__ static_scale,
     uint8_t *__restrict__ codes, int64_t cpitch, uint8_t *__restrict__ scales, int64_t spitch,
-    float *__restrict__ ts_out, uint32_t recipe) {
+    float *__restrict__ ts_out, uint32_t recipe, float *__restrict__ macro, int64_t mpitch) {
   using K = Blk<FMT>;
   __shared__ uint32_t lds[4];
   float st = 1.0f;
@@ -161,20 +183,30 @@ __global__ __launch_bounds__(kThreads) void k_quant(
   }
   const int64_t nb = k / K::B, nb_pad = kt_n * K::BPF, total = rows_pad * nb_pad;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  // (with MBS the four blocks of a segment are four consecutive threads of
+  // one iteration: nb_pad and the stride are multiples of 4)
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
     const int64_t r = t / nb_pad, b = t - r * nb_pad;
     uint8_t *cdst, *sdst;
     block_dst<FMT, TILED>(r, b, kt_n, codes, cpitch, scales, spitch, cdst, sdst);
-    if (r >= rows || b >= nb) {
-      zero_store<FMT>(cdst, sdst);
-      continue;
-    }
+    const bool pad = r >= rows || b >= nb;
     uint4 v[K::V];
-    const uint4 *src = (const uint4 *)(x + r * k + b * K::B);
+    if (!pad) {
+      const uint4 *src = (const uint4 *)(x + r * k + b * K::B);
 #pragma unroll
-    for (int i = 0; i < K::V; ++i) v[i] = src[i];
-    maybe_rotate<FMT>(v, recipe);
-    encode_store<FMT>(v, st, cdst, sdst, recipe);
+      for (int i = 0; i < K::V; ++i) v[i] = src[i];
+      maybe_rotate<FMT>(v, recipe);
+    } else {
+#pragma unroll
+      for (int i = 0; i < K::V; ++i) v[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    float smb = 1.0f;
+    if (FMT == 1 && mbs(recipe)) {
+      smb = segment_mbs_scale<1>(block_absmax<FMT>(v));
+      if ((b & 3) == 0) *macro_dst<TILED>(r, b >> 2, kt_n, macro, mpitch) = smb;
+    }
+    if (pad) zero_store<FMT>(cdst, sdst);
+    else encode_store<FMT>(v, st, smb, cdst, sdst, recipe);
   }
 }
 
@@ -189,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_tiled(
     const uint16_t *__restrict__ x, int64_t rows, int64_t k, int64_t rows_pad, int64_t kt_n,
     const uint32_t *__restrict__ parts, int nparts, const float *__restrict__ static_scale,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, float *__restrict__ ts_out,
-    uint32_t recipe) {
+    uint32_t recipe, float *__restrict__ macro) {
   using K = Blk<FMT>;
   __shared__ uint32_t lds[4];
   float st = 1.0f;
@@ -237,7 +269,15 @@ __global__ __launch_bounds__(kThreads) void k_quant_tiled(
     } else {
       q = make_uint4(0u, 0u, 0u, 0u);
       sc = 0;
-      if (row < rows && k0 < k) mx_encode_block(v, q, sc, oas_rule(recipe));
+      if (mbs(recipe)) {
+        // lanes r, r + 16, r + 32, r + 48 hold the segment's four blocks
+        const float smb = segment_mbs_scale<16>(max(max(absmax_bits8(v[0]), absmax_bits8(v[1])),
+                                                    max(absmax_bits8(v[2]), absmax_bits8(v[3]))));
+        if (row < rows && k0 < k) mbs_encode_block(v, smb, q, sc, oas_rule(recipe));
+        if (c == 0) macro[f * 16 + r] = smb;
+      } else if (row < rows && k0 < k) {
+        mx_encode_block(v, q, sc, oas_rule(recipe));
+      }
       scales[f * K::SFB + lane] = (uint8_t)sc;
     }
     *(uint4 *)(codes + f * kFragCodeBytes + lane * 16) = q;
@@ -329,7 +369,8 @@ __global__ __launch_bounds__(NTH) void k_quant_small(
     const uint16_t *__restrict__ x, int64_t rows, int64_t k, int64_t rows_pad, int64_t kt_n,
     const float *__restrict__ static_scale, uint8_t *__restrict__ codes, int64_t cpitch,
     uint8_t *__restrict__ scales, int64_t spitch, float *__restrict__ ts_out,
-    uint32_t *__restrict__ sync, uint32_t recipe, uint32_t spin_limit) {
+    uint32_t *__restrict__ sync, uint32_t recipe, uint32_t spin_limit, float *__restrict__ macro,
+    int64_t mpitch) {
   using K = Blk<FMT>;
   __shared__ uint32_t lds[NTH / 64];
   const int64_t nb = k / K::B, nb_pad = kt_n * K::BPF, total = rows_pad * nb_pad;
@@ -340,6 +381,7 @@ __global__ __launch_bounds__(NTH) void k_quant_small(
     tag = ((__hip_atomic_load(&sync[blockIdx.x * kSlotStride], __ATOMIC_RELAXED,
                               __HIP_MEMORY_SCOPE_AGENT) >> 16) + 1u) & 0xFFFFu;
   uint4 v[BPT][K::V];
+  float smb[BPT];
   uint32_t m = 0;
 #pragma unroll
   for (int i = 0; i < BPT; ++i) {
@@ -354,7 +396,11 @@ __global__ __launch_bounds__(NTH) void k_quant_small(
       for (int j = 0; j < K::V; ++j) v[i][j] = make_uint4(0u, 0u, 0u, 0u);
     }
     maybe_rotate<FMT>(v[i], recipe);
-    m = max(m, block_absmax<FMT>(v[i]));
+    const uint32_t bm = block_absmax<FMT>(v[i]);
+    m = max(m, bm);
+    // a segment's four blocks are four consecutive threads (nb_pad and the
+    // grid stride are multiples of 4)
+    smb[i] = (FMT == 1 && mbs(recipe)) ? segment_mbs_scale<1>(bm) : 1.0f;
   }
   float st = 1.0f;
   bool gave_up = false;
@@ -389,7 +435,9 @@ __global__ __launch_bounds__(NTH) void k_quant_small(
     uint8_t *cdst, *sdst;
     block_dst<FMT, TILED>(r, b, kt_n, codes, cpitch, scales, spitch, cdst, sdst);
     if (r >= rows || b >= nb) zero_store<FMT>(cdst, sdst);
-    else encode_store<FMT>(v[i], st, cdst, sdst, recipe);
+    else encode_store<FMT>(v[i], st, smb[i], cdst, sdst, recipe);
+    if (FMT == 1 && mbs(recipe) && (b & 3) == 0)
+      *macro_dst<TILED>(r, b >> 2, kt_n, macro, mpitch) = smb[i];
   }
   if (FMT == 0 && DYN == 1 && threadIdx.x == 0 && (arrived_before & 0xFFFFu) == gridDim.x - 1) {
     // the last workgroup: every other one has taken its decision
@@ -407,7 +455,8 @@ template <int FMT>
 __global__ __launch_bounds__(kThreads) void k_export(
     const uint8_t *__restrict__ tc, const uint8_t *__restrict__ ts, int64_t rows, int64_t kt_n,
     uint8_t *__restrict__ codes, int64_t cpitch, uint8_t *__restrict__ scales, int64_t spitch,
-    const float *__restrict__ tsc_in, float *__restrict__ tsc_out) {
+    const float *__restrict__ tsc_in, float *__restrict__ tsc_out,
+    const float *__restrict__ tmacro, float *__restrict__ macro, int64_t mpitch) {
   using K = Blk<FMT>;
   if (blockIdx.x == 0 && threadIdx.x == 0 && tsc_in && tsc_out) *tsc_out = *tsc_in;
   const int64_t nb_pad = kt_n * K::BPF, total = rows * nb_pad;
@@ -420,6 +469,8 @@ __global__ __launch_bounds__(kThreads) void k_export(
     if (FMT == 0) *(uint2 *)ccd = *(const uint2 *)tcd;
     else *(uint4 *)ccd = *(const uint4 *)tcd;
     *csd = *tsd;
+    if (tmacro && (b & 3) == 0) *macro_dst<0>(r, b >> 2, kt_n, macro, mpitch) =
+        *macro_dst<1>(r, b >> 2, kt_n, (float *)tmacro, 0);
   }
 }
 
@@ -429,7 +480,8 @@ template <int FMT>
 __global__ __launch_bounds__(kThreads) void k_import(
     const uint8_t *__restrict__ codes, int64_t cpitch, const uint8_t *__restrict__ scales,
     int64_t spitch, int64_t rows, int64_t rows_pad, int64_t kt_n, uint8_t *__restrict__ tc,
-    uint8_t *__restrict__ ts) {
+    uint8_t *__restrict__ ts, const float *__restrict__ macro, int64_t mpitch,
+    float *__restrict__ tmacro) {
   using K = Blk<FMT>;
   const int64_t nb_pad = kt_n * K::BPF, total = rows_pad * nb_pad;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -437,6 +489,9 @@ __global__ __launch_bounds__(kThreads) void k_import(
     const int64_t r = t / nb_pad, b = t - r * nb_pad;
     uint8_t *tcd, *tsd;
     block_dst<FMT, 1>(r, b, kt_n, tc, 0, ts, 0, tcd, tsd);
+    if (macro && (b & 3) == 0)   // padding rows: the scale of an all-zero segment
+      *macro_dst<1>(r, b >> 2, kt_n, tmacro, 0) =
+          r < rows ? *macro_dst<0>(r, b >> 2, kt_n, (float *)macro, mpitch) : 1.0f;
     if (r >= rows) {
       zero_store<FMT>(tcd, tsd);
       continue;
@@ -448,12 +503,13 @@ __global__ __launch_bounds__(kThreads) void k_import(
   }
 }
 
-// x^ = q * s_b * S_t rounded once to FP32. One thread per element.
+// x^ = q * s_b * S_t (NVFP4) or q * 2^e_b (* S_mb with macro-block scales)
+// rounded once to FP32. One thread per element.
 template <int FMT, int TILED>
 __global__ __launch_bounds__(kThreads) void k_dequant(
     const uint8_t *__restrict__ codes, int64_t cpitch, const uint8_t *__restrict__ scales,
     int64_t spitch, const float *__restrict__ tsc, int64_t rows, int64_t k, int64_t kt_n,
-    float *__restrict__ out, int64_t ldo) {
+    float *__restrict__ out, int64_t ldo, const float *__restrict__ macro, int64_t mpitch) {
   using K = Blk<FMT>;
   const double st = (FMT == 0 && tsc) ? (double)*tsc : 1.0;
   const int64_t total = rows * k;
@@ -467,7 +523,8 @@ __global__ __launch_bounds__(kThreads) void k_dequant(
     const uint32_t code = (kk & 1) ? (byte >> 4) : (byte & 15u);
     const uint32_t ee = (code >> 1) & 3u, mm = code & 1u;
     const float qmag = ee == 0 ? 0.5f * (float)mm : ldexpf(1.0f + 0.5f * (float)mm, (int)ee - 1);
-    const double s = FMT == 0 ? (double)e4m3_to_f32(*sd) : ldexp(1.0, (int)*sd - 127);
+    double s = FMT == 0 ? (double)e4m3_to_f32(*sd) : ldexp(1.0, (int)*sd - 127);
+    if (macro) s *= (double)*macro_dst<TILED>(r, kk / 128, kt_n, (float *)macro, mpitch);
     const double val = (double)qmag * s * st;
     out[r * ldo + kk] = (code & 8u) ? -(float)val : (float)val;
   }
@@ -485,8 +542,8 @@ std::atomic<uint32_t> g_spin_limit{kDefaultSpinLimit};
 template <int FMT, int TILED>
 void launch_small(const uint16_t *x, int64_t rows, int64_t k, int64_t rows_pad, int64_t kt_n,
                   const float *static_scale, uint8_t *codes, int64_t cpitch, uint8_t *scales,
-                  int64_t spitch, float *ts_out, uint32_t *sync, uint32_t recipe,
-                  hipStream_t stream) {
+                  int64_t spitch, float *ts_out, uint32_t *sync, uint32_t recipe, float *macro,
+                  int64_t mpitch, hipStream_t stream) {
   const uint32_t spin = g_spin_limit.load(std::memory_order_relaxed);
   // One block per thread where the grid allows: encoding is the costly part
   // and spreads over as many CUs as there are blocks. The dynamic-scale form
@@ -503,7 +560,7 @@ void launch_small(const uint16_t *x, int64_t rows, int64_t k, int64_t rows_pad, 
 #define FP4_QS(D, BPT, NTH)                                                                     \
   hipLaunchKernelGGL((k_quant_small<FMT, TILED, D, BPT, NTH>), dim3(grid), dim3(NTH), 0, stream, \
                      x, rows, k, rows_pad, kt_n, static_scale, codes, cpitch, scales, spitch,    \
-                     ts_out, sync, recipe, spin)
+                     ts_out, sync, recipe, spin, macro, mpitch)
     // Small tensors: every workgroup reads the whole tensor for its maximum
     // rather than exchanging it (measured per call: M = 1, K = 5120: 4.9 ->
     // 3.9 us; M = 8, K = 5120: 5.15 -> 4.8 us; at M * K = 139264 it lost,
@@ -523,7 +580,7 @@ void launch_small(const uint16_t *x, int64_t rows, int64_t k, int64_t rows_pad, 
   } else {
     hipLaunchKernelGGL((k_quant_small<FMT, TILED, 0, 1>), dim3((unsigned)per_wg), dim3(kThreads), 0,
                        stream, x, rows, k, rows_pad, kt_n, static_scale, codes, cpitch, scales,
-                       spitch, ts_out, sync, recipe, spin);
+                       spitch, ts_out, sync, recipe, spin, macro, mpitch);
   }
 }
 
@@ -531,18 +588,19 @@ template <int FMT, int TILED>
 void launch_large(const uint16_t *x, int64_t rows, int64_t k, int64_t rows_pad, int64_t kt_n,
                   const uint32_t *parts, int nparts, const float *static_scale, uint8_t *codes,
                   int64_t cpitch, uint8_t *scales, int64_t spitch, float *ts_out, uint32_t recipe,
-                  hipStream_t stream) {
+                  float *macro, int64_t mpitch, hipStream_t stream) {
   if (TILED) {  // one wave per fragment, four waves per workgroup, grid-stride
     const int64_t frags = (rows_pad >> 4) * kt_n;
     const int grid = (int)std::min<int64_t>((frags + 3) / 4, 8192);
     hipLaunchKernelGGL((k_quant_tiled<FMT>), dim3(grid), dim3(kThreads), 0, stream, x, rows, k,
-                       rows_pad, kt_n, parts, nparts, static_scale, codes, scales, ts_out, recipe);
+                       rows_pad, kt_n, parts, nparts, static_scale, codes, scales, ts_out, recipe,
+                       macro);
     return;
   }
   const int grid = grid_for(rows_pad * kt_n * Blk<FMT>::BPF, 8192);
   hipLaunchKernelGGL((k_quant<FMT, TILED>), dim3(grid), dim3(kThreads), 0, stream, x, rows, k,
                      rows_pad, kt_n, parts, nparts, static_scale, codes, cpitch, scales, spitch,
-                     ts_out, recipe);
+                     ts_out, recipe, macro, mpitch);
 }
 
 }  // namespace
@@ -569,14 +627,14 @@ bool quant_fits_small(int fmt, int64_t rows, int64_t k, int tiled) {
 
 hipError_t launch_quantize(int fmt, uint32_t recipe, int tiled, const uint16_t *x, int64_t rows,
                            int64_t k, const float *static_scale, uint8_t *codes, int64_t cpitch,
-                           uint8_t *scales, int64_t spitch, float *ts_out, uint32_t *scratch,
-                           hipStream_t stream) {
+                           uint8_t *scales, int64_t spitch, float *macro, int64_t mpitch,
+                           float *ts_out, uint32_t *scratch, hipStream_t stream) {
   const int64_t rows_pad = tiled ? round_up(rows, 16) : rows;
   const int64_t kt_n = k_pad(k) / kFragK;
   if (quant_fits_small(fmt, rows, k, tiled)) {
     uint32_t *sync = scratch + kMaxAmaxParts;
 #define FP4_QS(F, T) launch_small<F, T>(x, rows, k, rows_pad, kt_n, static_scale, codes, cpitch, \
-                                        scales, spitch, ts_out, sync, recipe, stream)
+                                        scales, spitch, ts_out, sync, recipe, macro, mpitch, stream)
     if (fmt == 0 && !tiled) FP4_QS(0, 0);
     else if (fmt == 0) FP4_QS(0, 1);
     else if (!tiled) FP4_QS(1, 0);
@@ -597,7 +655,8 @@ hipError_t launch_quantize(int fmt, uint32_t recipe, int tiled, const uint16_t *
     if (e != hipSuccess) return e;
   }
 #define FP4_QL(F, T) launch_large<F, T>(x, rows, k, rows_pad, kt_n, scratch, nparts, static_scale, \
-                                        codes, cpitch, scales, spitch, ts_out, recipe, stream)
+                                        codes, cpitch, scales, spitch, ts_out, recipe, macro,       \
+                                        mpitch, stream)
   if (fmt == 0 && !tiled) FP4_QL(0, 0);
   else if (fmt == 0) FP4_QL(0, 1);
   else if (!tiled) FP4_QL(1, 0);
@@ -607,42 +666,46 @@ hipError_t launch_quantize(int fmt, uint32_t recipe, int tiled, const uint16_t *
 }
 
 hipError_t launch_export_canonical(int fmt, const uint8_t *tcodes, const uint8_t *tscales,
-                                   int64_t rows, int64_t k, uint8_t *codes, int64_t cpitch,
-                                   uint8_t *scales, int64_t spitch, const float *ts_in,
-                                   float *ts_out, hipStream_t stream) {
+                                   const float *tmacro, int64_t rows, int64_t k, uint8_t *codes,
+                                   int64_t cpitch, uint8_t *scales, int64_t spitch, float *macro,
+                                   int64_t mpitch, const float *ts_in, float *ts_out,
+                                   hipStream_t stream) {
   const int64_t kt_n = k_pad(k) / kFragK;
   const int grid = grid_for(rows * kt_n * (128 / block_of(fmt)), 8192);
   if (fmt == 0)
     hipLaunchKernelGGL(k_export<0>, dim3(grid), dim3(kThreads), 0, stream, tcodes, tscales, rows,
-                       kt_n, codes, cpitch, scales, spitch, ts_in, ts_out);
+                       kt_n, codes, cpitch, scales, spitch, ts_in, ts_out, nullptr, nullptr,
+                       (int64_t)0);
   else
     hipLaunchKernelGGL(k_export<1>, dim3(grid), dim3(kThreads), 0, stream, tcodes, tscales, rows,
-                       kt_n, codes, cpitch, scales, spitch, ts_in, ts_out);
+                       kt_n, codes, cpitch, scales, spitch, ts_in, ts_out, tmacro, macro, mpitch);
   return hipGetLastError();
 }
 
 hipError_t launch_import_tiled(int fmt, const uint8_t *codes, int64_t cpitch, const uint8_t *scales,
-                              int64_t spitch, int64_t rows, int64_t k, uint8_t *tcodes,
-                              uint8_t *tscales, hipStream_t stream) {
+                              int64_t spitch, const float *macro, int64_t mpitch, int64_t rows,
+                              int64_t k, uint8_t *tcodes, uint8_t *tscales, float *tmacro,
+                              hipStream_t stream) {
   const int64_t kt_n = k_pad(k) / kFragK, rows_pad = round_up(rows, 16);
   const int grid = grid_for(rows_pad * kt_n * (128 / block_of(fmt)), 8192);
   if (fmt == 0)
     hipLaunchKernelGGL(k_import<0>, dim3(grid), dim3(kThreads), 0, stream, codes, cpitch, scales,
-                       spitch, rows, rows_pad, kt_n, tcodes, tscales);
+                       spitch, rows, rows_pad, kt_n, tcodes, tscales, nullptr, (int64_t)0, nullptr);
   else
     hipLaunchKernelGGL(k_import<1>, dim3(grid), dim3(kThreads), 0, stream, codes, cpitch, scales,
-                       spitch, rows, rows_pad, kt_n, tcodes, tscales);
+                       spitch, rows, rows_pad, kt_n, tcodes, tscales, macro, mpitch, tmacro);
   return hipGetLastError();
 }
 
 hipError_t launch_dequant(int fmt, int tiled, const uint8_t *codes, int64_t cpitch,
-                          const uint8_t *scales, int64_t spitch, const float *ts, int64_t rows,
-                          int64_t k, float *out, int64_t ldo, hipStream_t stream) {
+                          const uint8_t *scales, int64_t spitch, const float *macro,
+                          int64_t mpitch, const float *ts, int64_t rows, int64_t k, float *out,
+                          int64_t ldo, hipStream_t stream) {
   const int64_t kt_n = k_pad(k) / kFragK;
   const int grid = grid_for(rows * k, 8192);
 #define FP4_DQ(F, T)                                                                       \
   hipLaunchKernelGGL((k_dequant<F, T>), dim3(grid), dim3(kThreads), 0, stream, codes, cpitch, \
-                     scales, spitch, ts, rows, k, kt_n, out, ldo)
+                     scales, spitch, ts, rows, k, kt_n, out, ldo, macro, mpitch)
   if (fmt == 0 && !tiled) FP4_DQ(0, 0);
   else if (fmt == 0) FP4_DQ(0, 1);
   else if (!tiled) FP4_DQ(1, 0);

@@ -77,8 +77,26 @@ typedef enum { FP4_NVFP4 = 0, FP4_MXFP4 = 1 } fp4_format;
  *   ("FP4 n'existe pas ...", section "L'ecart de qualite - et comment il se
  *   reduit"); the default exponent floor(log2 max|x|) - 2 lets block maxima
  *   in (6, 8) * 2^e saturate. Operands may differ in this flag.
+ * FP4_MX_MBS (MXFP4 only): macro-block scaling, a second-level scale over a
+ *   macro-block of several 32-value blocks that brings MXFP4 closer to
+ *   two-level scaling without changing its base format ("FP4 n'existe
+ *   pas ...", same section; the page gives neither the macro-block size nor
+ *   the scale's format). Here a macro-block is the four blocks of one
+ *   128-value segment of a row along K, and its scale is the FP32 number
+ *   S_mb = RN_fp32(g / (6 * 2^j)) in [1, 2), g the segment's largest
+ *   magnitude and j = floor(log2(g / 6)) (1 when g = 0), which puts the
+ *   segment's largest value on the top code. Each block's E8M0 exponent is
+ *   the rule above applied to its values divided by S_mb, and elements round
+ *   against 2^e_b * S_mb: x^ = q * 2^e_b * S_mb. The S_mb are stored after the
+ *   E8M0 bytes in the scales buffer (fp4_scales_bytes includes them): TILED,
+ *   16 floats per fragment (one per fragment row) after all fragments' E8M0
+ *   bytes; CANONICAL, [rows][K_pad / 128] floats starting at the first
+ *   16-byte boundary past rows * scales_pitch bytes. Both operands of a
+ *   product must carry this flag, or neither (fp4_gemm: FP4_ERR_FORMAT_MISMATCH);
+ *   the weight-only linear rejects it. Combines with FP4_ROTATE and FP4_MX_OAS
+ *   (with OAS: the smallest e with a_b <= 6 * 2^e * S_mb).
  */
-enum { FP4_ROTATE = 0x100, FP4_MX_OAS = 0x200 };
+enum { FP4_ROTATE = 0x100, FP4_MX_OAS = 0x200, FP4_MX_MBS = 0x400 };
 
 typedef enum {
     FP4_OK = 0,

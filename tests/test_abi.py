@@ -153,7 +153,7 @@ def test_recipe_flags_validation():
     assert L.fp4_block_size(fp4.MXFP4 | fp4.MX_OAS | fp4.ROTATE) == 32
     # OAS is an MXFP4 rule; unknown bits are rejected
     assert L.fp4_block_size(fp4.NVFP4 | fp4.MX_OAS) == 0
-    assert L.fp4_block_size(fp4.MXFP4 | 0x400) == 0
+    assert L.fp4_block_size(fp4.MXFP4 | 0x800) == 0
     t = fp4.fp4_tensor()
     assert L.fp4_tensor_init(ctypes.byref(t), fp4.NVFP4 | fp4.MX_OAS, fp4.CANONICAL, 4, 64, 4096, 8192, 64) == 1
     # a rotated activation with an unrotated weight (and the reverse)
@@ -235,3 +235,18 @@ def test_workspace_flags_and_spin_limit_host_side():
     prev = L.fp4_set_exchange_spin_limit(5)
     assert prev == 1 << 22
     assert L.fp4_set_exchange_spin_limit(prev) == 5
+
+
+def test_mbs_flag_sizes_and_validity():
+    """MXFP4 | FP4_MX_MBS: the scales buffer also holds one float per row and
+    128-value segment (tiled: 16 per fragment; canonical: after the E8M0 rows,
+    16-byte aligned); NVFP4 rejects the flag."""
+    L = fp4.lib()
+    mbs = fp4.MXFP4 | fp4.MX_MBS
+    assert L.fp4_scales_bytes(mbs, fp4.TILED, 17, 256) == 32 * 8 + 32 * 2 * 4
+    assert L.fp4_scales_bytes(mbs, fp4.CANONICAL, 3, 2880) == 288 + 3 * 23 * 4   # round_up(3 * 92, 16)
+    assert L.fp4_scales_bytes(fp4.NVFP4 | fp4.MX_MBS, fp4.TILED, 16, 256) == 0
+    t = fp4.fp4_tensor()
+    assert L.fp4_tensor_init(ctypes.byref(t), fp4.NVFP4 | fp4.MX_MBS, fp4.CANONICAL, 4, 64, 16, 32, 64) == 1
+    assert L.fp4_tensor_init(ctypes.byref(t), mbs | fp4.ROTATE | fp4.MX_OAS, fp4.CANONICAL, 4, 64, 16, 32, 0) == 0
+    assert L.fp4_linear_workspace_bytes(mbs, 8, 64, 5120) > L.fp4_linear_workspace_bytes(fp4.MXFP4, 8, 64, 5120)

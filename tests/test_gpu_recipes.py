@@ -177,3 +177,82 @@ def test_oas_linear(m, k, n):
     qg = fp4.fp4_quantize_act(to_dev(a), fp4.MXFP4 | fp4.MX_OAS, layout=fp4.TILED)
     c_ref2, l_ref2 = oracle.gemm(qa, _ref("mxfp4", w, False, False))
     assert_gemm_close(bf16_out_to_f64(fp4.fp4_gemm(qg, wd)), c_ref2, l_ref2, "oas act x default weight")
+
+
+# ------------------------------------------------ MXFP4 macro-block scaling
+
+def _mbs_flags(rotate=False, oas=False):
+    return fp4.MXFP4 | fp4.MX_MBS | (fp4.ROTATE if rotate else 0) | (fp4.MX_OAS if oas else 0)
+
+
+def _assert_mbs_equal(q, ref, what):
+    """Codes and E8M0 bytes (byte for byte) and macro-block scales (bit for bit)."""
+    if q.layout == fp4.TILED:
+        q = fp4.fp4_export_canonical(q)
+    assert_canonical_equal(q, ref, oracle.MXFP4, what=what)
+    torch.cuda.synchronize()
+    got = q.macro_2d().cpu().numpy()
+    assert got.shape == ref.macro.shape, what
+    diff = np.argwhere(got.view(np.uint32) != ref.macro.view(np.uint32))
+    assert len(diff) == 0, f"{what}: {len(diff)} macro scales differ, first {tuple(diff[0])}: " \
+                           f"gpu {got[tuple(diff[0])]!r} ref {ref.macro[tuple(diff[0])]!r}"
+
+
+@pytest.mark.parametrize("m,k", [(1, 32), (3, 96), (17, 2880), (40, 5120), (320, 16384)])
+@pytest.mark.parametrize("layout", ["canonical", "tiled"])
+@pytest.mark.parametrize("rotate,oas", [(False, False), (False, True), (True, False)])
+def test_mbs_activation_quantization(m, k, layout, rotate, oas):
+    print(f"[recipe-mbs] m={m} k={k} layout={layout} rotate={rotate} oas={oas}", flush=True)
+    bits = synth.student_t((m, k), 3.0, 2.0, 61, m * 37 + k, plant=200.0, n_plant=max(1, m * k // 700))
+    ref = oracle.quantize(oracle.MXFP4, bits, rotate=rotate, oas=oas, mbs=True)
+    lay = fp4.TILED if layout == "tiled" else fp4.CANONICAL
+    q = fp4.fp4_quantize_act(to_dev(bits), _mbs_flags(rotate, oas), layout=lay)
+    _assert_mbs_equal(q, ref, f"mbs act {m}x{k} {layout}")
+
+
+@pytest.mark.parametrize("n,k", [(33, 96), (520, 2880), (256, 16384)])
+def test_mbs_weight_cache_and_dequantize(n, k):
+    w = synth.normal((n, k), 0.02, 62, n + k)
+    ref = oracle.quantize(oracle.MXFP4, w, mbs=True)
+    wq = fp4.fp4_quantize_weight(to_dev(w), _mbs_flags())
+    _assert_mbs_equal(wq, ref, f"mbs weight {n}x{k}")
+    # x^ = q * 2^e_b * S_mb, rounded once to FP32
+    got = fp4.fp4_dequantize(wq).cpu().numpy()
+    want = oracle.dequantize(ref).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 272, 640), (8, 520, 2880), (32, 1040, 5120), (100, 300, 1024),
+                                   (33, 8200, 256), (300, 520, 2880), (256, 384, 3072)])
+def test_mbs_gemm_and_linear(m, n, k):
+    """Products of macro-block-scaled operands: fp4_linear, fp4_gemm on tiled
+    and canonical activations (with and without the re-tiling workspace)."""
+    print(f"[recipe-mbs] gemm m={m} n={n} k={k}", flush=True)
+    a = synth.student_t((m, k), 3.0, 2.0, 63, m * 31 + k, plant=150.0, n_plant=3)
+    w = synth.normal((n, k), 0.02, 63, n * 17 + k)
+    qa_ref = oracle.quantize(oracle.MXFP4, a, mbs=True)
+    qw_ref = oracle.quantize(oracle.MXFP4, w, mbs=True)
+    c_ref, l_ref = oracle.gemm(qa_ref, qw_ref)
+    wq = fp4.fp4_quantize_weight(to_dev(w), _mbs_flags())
+    x = to_dev(a)
+    y = bf16_out_to_f64(fp4.fp4_linear(x, wq))
+    assert_gemm_close(y, c_ref, l_ref, f"mbs linear {m}x{n}x{k}")
+    for lay in (fp4.TILED, fp4.CANONICAL):
+        qa = fp4.fp4_quantize_act(x, _mbs_flags(), layout=lay)
+        c = bf16_out_to_f64(fp4.fp4_gemm(qa, wq))
+        assert_gemm_close(c, c_ref, l_ref, f"mbs gemm layout {lay}")
+        if lay == fp4.CANONICAL and m > 128:
+            tiny = torch.zeros(16, dtype=torch.uint8, device="cuda")
+            c2 = bf16_out_to_f64(fp4.fp4_gemm(qa, wq, workspace=tiny))
+            assert_gemm_close(c2, c_ref, l_ref, "mbs gemm canonical, no workspace")
+
+
+def test_mbs_operands_must_match():
+    w = synth.normal((64, 256), 0.02, 64, 1)
+    a = synth.normal((8, 256), 1.0, 64, 2)
+    wq = fp4.fp4_quantize_weight(to_dev(w), _mbs_flags())
+    qa = fp4.fp4_quantize_act(to_dev(a), fp4.MXFP4)
+    with pytest.raises(fp4.Fp4Error, match="FORMAT_MISMATCH"):
+        fp4.fp4_gemm(qa, wq)
+    with pytest.raises(fp4.Fp4Error, match="FORMAT_MISMATCH"):
+        fp4.fp4_linear_w4a16(to_dev(a), wq)
