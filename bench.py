@@ -59,6 +59,15 @@ def parse():
     p.add_argument("--api", default="linear", choices=["linear", "canonical"],
                    help="linear: fp4_linear per call; canonical: fp4_quantize_act into the canonical "
                         "layout, then fp4_gemm (the two public calls)")
+    p.add_argument("--nv-tile", default="", choices=["", "registers", "lds"],
+                   help="NVFP4 256 x 256 tiles: convert codes to f16 in each wave's registers "
+                        "or once per workgroup in LDS (default: the library's)")
+    p.add_argument("--no-fuse-large", action="store_true",
+                   help="large M: quantize the activations in a launch of their own instead of "
+                        "inside the GEMM launch (static NVFP4 scale or MXFP4)")
+    p.add_argument("--static-scale", type=float, default=0.0,
+                   help="NVFP4: quantize the activations with this static tensor scale instead of "
+                        "their dynamic one")
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     p.add_argument("--kernel-reps", type=int, default=50)
     p.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -323,9 +332,15 @@ def main():
         __graft_entry__.build()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.nv_tile:
+        fp4.fp4_set_nvfp4_tile_mode(fp4.NV_TILE_LDS if args.nv_tile == "lds" else fp4.NV_TILE_REGISTERS)
+    if args.no_fuse_large:
+        fp4.fp4_set_large_linear_fusion(False)
     fmt = fp4.FORMATS[args.fmt]
     # qfmt: the format value with the recipe flags, given to every library call
     qfmt = fp4._fmt(args.fmt + ("+" + args.recipe if args.recipe else ""))
+    st_dev = (torch.tensor([args.static_scale], dtype=torch.float32, device=dev)
+              if args.static_scale and fmt == 0 else None)
     if args.workload == "forward":
         bench_forward(args, fmt, qfmt)
         return
@@ -407,7 +422,7 @@ def main():
             fp4.fp4_quantize_act(xs[cfg], qfmt, workspace=qws[cfg], out=qcanon[cfg])
             fp4.fp4_gemm(qcanon[cfg], w, out=outs[cfg], workspace=gws[cfg])
         else:
-            fp4.fp4_linear(xs[cfg], w, out=outs[cfg], workspace=wss[cfg])
+            fp4.fp4_linear(xs[cfg], w, static_scale=st_dev, out=outs[cfg], workspace=wss[cfg])
 
     # the j-th call of a shape in step i takes copy (i * uses + j) mod copies
     slot = {}
@@ -511,7 +526,8 @@ def main():
                     else "k_w4a16_tile<%s>" % args.fmt)
             us = lin_us
             nbytes = w_bytes + 2 * m * k + 2 * m * n          # W + bf16 A + bf16 C
-        elif fp4.fp4_linear_launches(qfmt, m, n, k) == 1:
+        elif m <= 128 and fp4.fp4_linear_launches(qfmt, m, n, k, st_dev is not None) == 1:
+            # one launch: quantization inside the skinny GEMM
             name = "k_linear_decode<%s>" % args.fmt
             us = lin_us
             nbytes = w_bytes + 2 * m * k + 2 * m * n          # W + bf16 A + bf16 C
@@ -564,6 +580,7 @@ def main():
                                 for nm, d in kern.items()},
                  "per_config": per_cfg})
     config = {"workload": desc + (" (weight-only: bf16 activations)" if args.w4a16 else "") +
+              (f" (static activation scale {args.static_scale})" if st_dev is not None else "") +
               (" (fp4_quantize_act canonical + fp4_gemm)" if args.api == "canonical" else ""),
               "format": args.fmt, "recipe": args.recipe or "none",
               "launch": ("hip-graph replay, %d steps per graph" % G) if use_graph else "eager",

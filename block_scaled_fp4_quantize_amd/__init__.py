@@ -86,6 +86,8 @@ def lib():
             "fp4_dequantize": (I32, [T, P, I64, P]),
             "fp4_workspace_flags": (I32, [P, SZ, ctypes.POINTER(ctypes.c_uint32), I32, P]),
             "fp4_set_exchange_spin_limit": (ctypes.c_uint32, [ctypes.c_uint32]),
+            "fp4_set_nvfp4_tile_mode": (I32, [I32]),
+            "fp4_set_large_linear_fusion": (I32, [I32]),
             "fp4_status_string": (ctypes.c_char_p, [I32]),
             "fp4_last_error": (ctypes.c_char_p, []),
         }
@@ -296,6 +298,25 @@ def fp4_set_exchange_spin_limit(polls: int) -> int:
     """Test aid: polls before a workgroup of the quantizer's maximum exchange
     gives up (0: at once). Returns the previous value."""
     return lib().fp4_set_exchange_spin_limit(int(polls))
+
+
+def fp4_set_large_linear_fusion(on: bool) -> bool:
+    """Whether fp4_linear quantizes large-M activations inside the GEMM launch
+    (static NVFP4 scale or MXFP4). Process-wide; returns the previous setting."""
+    return bool(lib().fp4_set_large_linear_fusion(int(bool(on))))
+
+
+NV_TILE_REGISTERS, NV_TILE_LDS = 0, 1
+
+
+def fp4_set_nvfp4_tile_mode(mode: int) -> int:
+    """Where the NVFP4 256 x 256 tile GEMM converts codes to f16: NV_TILE_REGISTERS
+    (each wave that uses a fragment) or NV_TILE_LDS (once per workgroup, into
+    LDS). Process-wide; returns the previous mode."""
+    prev = lib().fp4_set_nvfp4_tile_mode(int(mode))
+    if prev < 0:
+        raise ValueError("mode must be NV_TILE_REGISTERS or NV_TILE_LDS")
+    return prev
 
 
 def fp4_export_canonical(t: Fp4Tensor) -> Fp4Tensor:

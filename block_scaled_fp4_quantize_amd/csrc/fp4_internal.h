@@ -29,7 +29,11 @@ constexpr int64_t kActRedundantMaxValues = 49152;  // M * K up to which each wor
 constexpr int kSlotStride = 32;
 constexpr int kErrWord = kMaxAmaxParts + kActGrid * kSlotStride;
 constexpr int kArriveWord = kErrWord + kSlotStride;
-constexpr size_t kQuantScratchBytes = (size_t)(kArriveWord + kSlotStride) * sizeof(uint32_t);
+// The fused large-M linear's per-panel words: (ready count, finished count)
+// for each row panel of output tiles, reset by the panel's last consumer.
+constexpr int kPanelWords = kArriveWord + kSlotStride;
+constexpr int kMaxPanels = 1024;
+constexpr size_t kQuantScratchBytes = (size_t)(kPanelWords + 2 * kMaxPanels) * sizeof(uint32_t);
 // Error flag: a workgroup of the maximum exchange gave up waiting.
 constexpr uint32_t kErrExchangeTimeout = 1u;
 constexpr uint32_t kDefaultSpinLimit = 1u << 22;
@@ -104,7 +108,28 @@ hipError_t launch_gemm_decode(const GemmArgs &g, hipStream_t stream);
 // LDS-staged GEMM for large M; both operands fragment-tiled. cfg selects the
 // workgroup tile (88: 256 x 256, 44: 128 x 128; 0: by shape).
 int gemm_tile_config(int fmt, int64_t m, int64_t n);
+// NVFP4 256 x 256 tiles: 0 = conversion in registers by each wave that uses a
+// fragment, 1 = conversion once per workgroup into LDS (k_gemm_tile_nvlds).
+int nvfp4_tile_mode();
+int set_nvfp4_tile_mode(int mode);
 hipError_t launch_gemm_tile(const GemmArgs &g, int cfg, hipStream_t stream);
+
+// Single-launch linear for large M (NVFP4 with a static tensor scale, or
+// MXFP4 without macro-block scales): the first workgroups quantize the bf16
+// activations x [m, k] into the tiled layout at g.a_codes / g.a_scales (each
+// row panel of output tiles split along K among several of them), the others
+// compute the output tiles, each waiting (bounded) for its panel. `scratch` is
+// the quantize scratch (kQuantScratchBytes, zero-filled once): its panel words
+// and error flags. Whether it applies: linear_fused_large_ok.
+bool linear_fused_large_ok(int fmt, uint32_t recipe, int64_t m, int64_t n, int64_t k,
+                           bool static_scale);
+// Whether fp4_linear uses it when it applies (1, the default) or quantizes in
+// a separate launch (0).
+int large_linear_fusion();
+int set_large_linear_fusion(int on);
+hipError_t launch_linear_fused_large(const GemmArgs &g, const uint16_t *x,
+                                     const float *static_scale, uint32_t recipe,
+                                     uint32_t *scratch, hipStream_t stream);
 
 // Single-launch linear (activation quantization fused) for small activations.
 constexpr int kFusedMaxM = 16;

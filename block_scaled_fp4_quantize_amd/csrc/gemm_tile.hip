@@ -38,6 +38,8 @@
 #include "fp4_device.h"
 #include "fp4_internal.h"
 
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 // clang notes that M0 is a reserved register when it appears in an inline
@@ -123,13 +125,94 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){lo, hi}, b2));
 }
 
-template <int FMT, int TM, int TN>
+// The fused linear's extra arguments (k_gemm_tile with FUSED = 1).
+struct Fused {
+  const uint16_t *x;        // bf16 activations [m, k]
+  const float *st;          // NVFP4 static tensor scale (device)
+  uint32_t *panel;          // per panel: ready count, finished count
+  uint32_t *err;            // sticky error flags
+  int nprod, parts;         // producer workgroups; producers per panel
+  int k;
+  uint32_t recipe, spin;
+};
+
+// Device-coherent stores (write through to memory, the cache policy of
+// device-scope atomics), so that a consumer on another XCD reads them.
+__device__ __forceinline__ void store16_dev(uint8_t *p, uint4 v) {
+  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(p, 0, 16, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(u4{v.x, v.y, v.z, v.w}, r, 0, 0, 16);
+}
+__device__ __forceinline__ void store2_dev(uint8_t *p, uint32_t v) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(p, 0, 2, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, 0, 0, 16);
+}
+__device__ __forceinline__ void store1_dev(uint8_t *p, uint32_t v) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(p, 0, 1, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b8((unsigned char)v, r, 0, 0, 16);
+}
+
+// Producer of the fused linear: quantizes part `part` (of `parts`) of row
+// panel `panel` of the activations into the tiled layout, one wave per
+// fragment (lane 16c + r: row r, values 32c .. 32c + 31), with the same
+// encoders as the quantize kernels; then counts itself in the panel's ready
+// word once its stores are complete.
+template <int FMT, int FA>
+__device__ void fused_produce(const Fused &fz, int panel, int part, int m, int kt_n, int ga_n,
+                             uint8_t *a_codes, uint8_t *a_sc) {
+  constexpr int SCB = FMT == 0 ? 128 : 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, c = lane >> 4;
+  const int g_lo = panel * FA, g_hi = min(g_lo + FA, ga_n);
+  const int nfr = (g_hi - g_lo) * kt_n, per = (nfr + fz.parts - 1) / fz.parts;
+  const int f_lo = part * per, f_hi = min(f_lo + per, nfr);
+  const float st = FMT == 0 ? *fz.st : 1.0f;
+  for (int i = f_lo + wave; i < f_hi; i += 4) {
+    const int g = g_lo + i / kt_n, kt = i % kt_n;
+    const int64_t f = (int64_t)g * kt_n + kt;
+    const int row = g * 16 + r, k0 = kt * kFragK + 32 * c;
+    uint4 v[4];
+    const uint4 *src = (const uint4 *)(fz.x + (int64_t)row * fz.k + k0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      v[j] = (row < m && k0 + 8 * j < fz.k) ? src[j] : make_uint4(0u, 0u, 0u, 0u);
+    if (fz.recipe & kRecipeRotate) {
+      if constexpr (FMT == 0) {
+        uint4 b0[2] = {v[0], v[1]}, b1[2] = {v[2], v[3]};
+        hadamard_block<16>(b0);
+        hadamard_block<16>(b1);
+        v[0] = b0[0]; v[1] = b0[1]; v[2] = b1[0]; v[3] = b1[1];
+      } else {
+        hadamard_block<32>(v);
+      }
+    }
+    uint4 q = make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (FMT == 0) {
+      uint2 c0 = make_uint2(0u, 0u), c1 = make_uint2(0u, 0u);
+      uint32_t s0 = 0, s1 = 0;
+      if (row < m && k0 < fz.k) nv_encode_block(v[0], v[1], st, c0, s0);
+      if (row < m && k0 + 16 < fz.k) nv_encode_block(v[2], v[3], st, c1, s1);
+      q = make_uint4(c0.x, c0.y, c1.x, c1.y);
+      store2_dev(a_sc + f * SCB + lane * 2, s0 | (s1 << 8));
+    } else {
+      uint32_t sc = 0;
+      if (row < m && k0 < fz.k) mx_encode_block(v, q, sc, fz.recipe & kRecipeOas);
+      store1_dev(a_sc + f * SCB + lane, sc);
+    }
+    store16_dev(a_codes + f * kFragCodeBytes + lane * 16, q);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(&fz.panel[2 * panel], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int FMT, int TM, int TN, int FUSED = 0>
 __global__ __launch_bounds__(256) void k_gemm_tile(
     const uint8_t *__restrict__ a_codes, const uint8_t *__restrict__ a_sc,
     const float *__restrict__ a_ts, const uint8_t *__restrict__ w_codes,
     const uint8_t *__restrict__ w_sc, const float *__restrict__ w_ts, int m, int n, int kt_n,
     int ga_n, int nt_n, int tiles_m, int tiles_n, uint16_t *__restrict__ c, int64_t ldc,
-    int vec_store) {
+    int vec_store, Fused fz) {
   using C = TileCfg<FMT, TM, TN>;
   // One LDS array per ring stage and a K loop unrolled four times, so every
   // stage buffer is a compile-time constant in its body (with a run-time
@@ -148,10 +231,20 @@ __global__ __launch_bounds__(256) void k_gemm_tile(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
 
+  // ---- fused linear: the first nprod workgroups quantize the activations
+  // (they run before any tile workgroup of their XCD: dispatch follows the
+  // workgroup index) and end; the rest are the tiles, numbered from 0
+  // (nprod is a multiple of the XCD count, so the XCD of tile b is still b % 8)
+  if (FUSED && (int)blockIdx.x < fz.nprod) {
+    fused_produce<FMT, C::FA>(fz, blockIdx.x / fz.parts, blockIdx.x % fz.parts, m, kt_n, ga_n,
+                              (uint8_t *)a_codes, (uint8_t *)a_sc);
+    return;
+  }
+
   // ---- tile of this workgroup (XCD-contiguous, grouped by tile rows)
   int tm, tn;
   {
-    const int nwg = tiles_m * tiles_n, b = blockIdx.x;
+    const int nwg = tiles_m * tiles_n, b = blockIdx.x - (FUSED ? fz.nprod : 0);
     const int xcd = b % kXcds, slot = b / kXcds, q = nwg / kXcds, r = nwg % kXcds;
     const int L = xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
     const int per_group = kGroupRows * tiles_n, grp = L / per_group, first = grp * kGroupRows;
@@ -160,6 +253,29 @@ __global__ __launch_bounds__(256) void k_gemm_tile(
     tn = in / gsz;
   }
   const int g0 = tm * C::FA, n0 = tn * C::FW;
+
+  // ---- fused linear: wait (bounded) until every producer of this tile row's
+  // activation panel has finished; the panel's fragments are then read with
+  // ordinary loads, this kernel having read none of them before. A wait that
+  // gives up sets the sticky error flag and makes the tile's output NaN.
+  __shared__ uint32_t gave_up_s;
+  if (FUSED) {
+    if (threadIdx.x == 0) {
+      uint32_t ok = 0;
+      for (uint32_t it = 0; it < fz.spin; ++it) {
+        if (__hip_atomic_load(&fz.panel[2 * tm], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >=
+            (uint32_t)fz.parts) {
+          ok = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (!ok)
+        __hip_atomic_fetch_or(fz.err, kErrExchangeTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      gave_up_s = !ok;
+    }
+    __syncthreads();
+  }
 
   // ---- this wave's share of every stage's copies: code fragments
   // wave + 4u (one 16-byte copy per lane, 1 KB per wave), then scale runs
@@ -415,8 +531,22 @@ __global__ __launch_bounds__(256) void k_gemm_tile(
   // handed to the next workgroup)
   wait_vm<0>();
 
+  Alpha alpha = FMT == 0 ? make_alpha(a_ts[0], w_ts[0]) : Alpha{1.0f, 0};
+  if (FUSED) {
+    // this tile reads no more activations: count it finished; the panel's
+    // last tile resets the panel's words for the next call
+    if (gave_up_s) alpha.m = __builtin_nanf("");
+    if (threadIdx.x == 0) {
+      const uint32_t done = __hip_atomic_fetch_add(&fz.panel[2 * tm + 1], 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      if (done == (uint32_t)tiles_n - 1) {
+        __hip_atomic_store(&fz.panel[2 * tm], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&fz.panel[2 * tm + 1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+
   // ---- epilogue: lane holds C[row][col0 .. col0+3] of each 16 x 16 tile
-  const Alpha alpha = FMT == 0 ? make_alpha(a_ts[0], w_ts[0]) : Alpha{1.0f, 0};
   const int rl = lane & 15, cl = 4 * (lane >> 4);
   if (vec_store == 2) {
     // Staged through LDS: each wave writes its 16TM x 16TN quadrant as bf16
@@ -481,7 +611,248 @@ __global__ __launch_bounds__(256) void k_gemm_tile(
   }
 }
 
+// ---------------------------------------------------------------------------
+// NVFP4 with the conversion in LDS: every fragment of a stage is dequantized
+// once per workgroup (in the kernel above, each A and W fragment is converted
+// by both waves that use it). Per K = 32 sub-block (dword g of every lane's
+// 16 code bytes, the same K permutation for both operands), each wave converts
+// eight of the stage's fragments to exact f16 q * s_b and writes them to a
+// double-buffered f16 area (1 KB per fragment, in operand lane order); after a
+// barrier every wave reads its TM + TN f16 operands back and runs its TM x TN
+// matrix instructions while the next sub-block is converted into the other
+// buffer. The FP4 ring has two stages (LDS: 2 x 36 KB ring + 2 x 32 KB f16);
+// stage s is copied while stages s - 2 and s - 1 are consumed, its codes read
+// into registers at the last sub-block of stage s - 1.
+template <int TM, int TN>
+__global__ __launch_bounds__(256) void k_gemm_tile_nvlds(
+    const uint8_t *__restrict__ a_codes, const uint8_t *__restrict__ a_sc,
+    const float *__restrict__ a_ts, const uint8_t *__restrict__ w_codes,
+    const uint8_t *__restrict__ w_sc, const float *__restrict__ w_ts, int m, int n, int kt_n,
+    int ga_n, int nt_n, int tiles_m, int tiles_n, uint16_t *__restrict__ c, int64_t ldc,
+    int vec_store) {
+  using C = TileCfg<0, TM, TN>;
+  constexpr int F16B = C::NF * kFragCodeBytes;            // one sub-block's f16 operands
+  constexpr int QR = 16 * TM, QC = 16 * TN, QP = 2 * QC + 16;
+  constexpr int RING = C::STAGE;
+  constexpr int USE = 2 * RING + 2 * F16B;
+  constexpr int TOTAL = USE > 4 * QR * QP ? USE : 4 * QR * QP;
+  static_assert(C::NF == 32 && TOTAL <= 160 * 1024, "256 x 256 tile: 32 fragments per stage");
+  __shared__ __align__(1024) uint8_t smem[TOTAL];
+  auto ring = [&](auto r) __attribute__((always_inline)) -> uint8_t * {
+    return smem + (decltype(r)::value & 1) * RING;
+  };
+  auto f16buf = [&](auto b) __attribute__((always_inline)) -> uint8_t * {
+    return smem + 2 * RING + (decltype(b)::value & 1) * F16B;
+  };
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+
+  // ---- tile of this workgroup (XCD-contiguous, grouped by tile rows)
+  int tm, tn;
+  {
+    const int nwg = tiles_m * tiles_n, b = blockIdx.x;
+    const int xcd = b % kXcds, slot = b / kXcds, q = nwg / kXcds, r = nwg % kXcds;
+    const int L = xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+    const int per_group = kGroupRows * tiles_n, grp = L / per_group, first = grp * kGroupRows;
+    const int gsz = min(tiles_m - first, kGroupRows), in = L - grp * per_group;
+    tm = first + in % gsz;
+    tn = in / gsz;
+  }
+  const int g0 = tm * C::FA, n0 = tn * C::FW;
+
+  // ---- copies: code fragments wave + 4u, scale runs wave + 4v (as above)
+  constexpr int NCP = C::NF / 4, NSP = C::SC_INSTR / 4;
+  auto row_of = [&](int f) __attribute__((always_inline)) {
+    return f < C::FA ? min(g0 + f, ga_n - 1) : min(n0 + f - C::FA, nt_n - 1);
+  };
+  const uint8_t *code_base[NCP];
+  const uint32_t code_off = lane * 16;
+#pragma unroll
+  for (int u = 0; u < NCP; ++u) {
+    const int f = wave + 4 * u;
+    code_base[u] = (f < C::FA ? a_codes : w_codes) + (int64_t)row_of(f) * kt_n * kFragCodeBytes;
+  }
+  constexpr int DPF = C::SCB / 4;
+  const uint8_t *sc_base[NSP];
+  uint32_t sc_off[NSP];
+#pragma unroll
+  for (int v = 0; v < NSP; ++v) {
+    const int j = wave + 4 * v;
+    const int d0 = min(64 * j, C::SC_DW - 1), d = min(64 * j + lane, C::SC_DW - 1);
+    const int f0 = d0 / DPF, f = d / DPF;
+    const int r0 = row_of(f0);
+    sc_base[v] = (f0 < C::FA ? a_sc : w_sc) + (int64_t)r0 * kt_n * C::SCB;
+    sc_off[v] = (uint32_t)((row_of(f) - r0) * kt_n * C::SCB + (d % DPF) * 4);
+  }
+  auto issue = [&](uint8_t *st, int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NCP; ++u)
+      lds_copy16(code_base[u] + (int64_t)kt * kFragCodeBytes, code_off,
+                 lds_addr(st + (wave + 4 * u) * kFragCodeBytes));
+#pragma unroll
+    for (int v = 0; v < NSP; ++v)
+      lds_copy4(sc_base[v] + (int64_t)kt * C::SCB, sc_off[v],
+                lds_addr(st + C::CODE_BYTES + (wave + 4 * v) * 256));
+  };
+  auto src_kt = [&](int kt) __attribute__((always_inline)) { return min(kt, kt_n - 1); };
+
+  // ---- this wave's conversions: fragments wave + 4d, d = 0..7
+  constexpr int ND = C::NF / 4;
+  uint4 cq[ND];
+  uint32_t cs[ND / 2];   // scale byte pairs of fragments 2e (low half) and 2e + 1
+  auto read_codes = [&](const uint8_t *st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      const int f = wave + 4 * d;
+      cq[d] = *(const uint4 *)(st + f * kFragCodeBytes + lane * 16);
+      const uint32_t sp = *(const uint16_t *)(st + C::CODE_BYTES + f * 128 + lane * 2);
+      if (d & 1) cs[d / 2] |= sp << 16;
+      else cs[d / 2] = sp;
+    }
+  };
+  auto convert = [&](auto gc, uint8_t *dst) __attribute__((always_inline)) {
+    constexpr int G = decltype(gc)::value;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      const uint32_t q = G == 0 ? cq[d].x : G == 1 ? cq[d].y : G == 2 ? cq[d].z : cq[d].w;
+      const uint32_t sp = cs[d / 2] >> (16 * (d & 1));
+      const uint32_t sb = G < 2 ? (sp & 0xFFu) : ((sp >> 8) & 0xFFu);
+      *(uint4 *)(dst + (wave + 4 * d) * kFragCodeBytes + lane * 16) = nv_dequant8_u4(q, sb);
+    }
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int fa0 = wm * TM, fw0 = C::FA + wn * TN;
+  v4f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  // the activation operands are held, the weight operands streamed one at a
+  // time (registers: the accumulators fill the AGPRs)
+  auto mma_sub = [&](const uint8_t *src) __attribute__((always_inline)) {
+    h8v ah[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) ah[i] = *(const h8v *)(src + (fa0 + i) * kFragCodeBytes + lane * 16);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const h8v wh = *(const h8v *)(src + (fw0 + j) * kFragCodeBytes + lane * 16);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wh, ah[i], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // ---- prologue: stages 0 and 1 copied, stage 0's first sub-block converted
+  issue(ring(Stage<0>{}), 0);
+  issue(ring(Stage<1>{}), src_kt(1));
+  wait_vm<C::PS>();
+  lds_barrier();
+  read_codes(ring(Stage<0>{}));
+  convert(Stage<0>{}, f16buf(Stage<0>{}));
+  lds_barrier();
+  issue(ring(Stage<0>{}), src_kt(2));
+
+  // stage kt (ring R = kt % 2): sub-blocks 0..3 from the f16 buffers 0, 1, 0, 1
+  // while sub-blocks 1..3 and the next stage's sub-block 0 are converted
+  auto stage = [&](auto rc, int kt) __attribute__((always_inline)) {
+    constexpr int R = decltype(rc)::value;
+    mma_sub(f16buf(Stage<0>{}));
+    convert(Stage<1>{}, f16buf(Stage<1>{}));
+    lds_barrier();
+    mma_sub(f16buf(Stage<1>{}));
+    convert(Stage<2>{}, f16buf(Stage<0>{}));
+    lds_barrier();
+    mma_sub(f16buf(Stage<0>{}));
+    convert(Stage<3>{}, f16buf(Stage<1>{}));
+    lds_barrier();
+    // the next stage's copies have landed (the one after may be in flight)
+    wait_vm<C::PS>();
+    lds_barrier();
+    const bool more = kt + 1 < kt_n;
+    if (more) read_codes(ring(Stage<R + 1>{}));
+    mma_sub(f16buf(Stage<1>{}));
+    if (more) convert(Stage<0>{}, f16buf(Stage<0>{}));
+    lds_barrier();
+    // stage kt + 1's codes are in registers: its ring takes stage kt + 3
+    issue(ring(Stage<R + 1>{}), src_kt(kt + 3));
+  };
+  for (int kt = 0; kt < kt_n; kt += 2) {
+    stage(Stage<0>{}, kt);
+    if (kt + 1 < kt_n) stage(Stage<1>{}, kt + 1);
+  }
+  wait_vm<0>();
+
+  // ---- epilogue: as in the kernel above (quadrants staged through LDS)
+  const Alpha alpha = make_alpha(a_ts[0], w_ts[0]);
+  const int rl = lane & 15, cl = 4 * (lane >> 4);
+  if (vec_store == 2) {
+    lds_barrier();
+    uint8_t *q = smem + wave * (QR * QP);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const v4f &a = acc[i][j];
+        const uint32_t lo = pack_bf16x2(apply_alpha(a[0], alpha), apply_alpha(a[1], alpha));
+        const uint32_t hi = pack_bf16x2(apply_alpha(a[2], alpha), apply_alpha(a[3], alpha));
+        *(uint2 *)(q + (16 * i + rl) * QP + 2 * (16 * j + cl)) = make_uint2(lo, hi);
+      }
+    constexpr int LPR = QC / 8, RPI = 64 / LPR;
+    const int lr = lane / LPR, lc = 8 * (lane % LPR);
+    const int row0 = (g0 + fa0) * 16, col = (n0 + wn * TN) * 16 + lc;
+#pragma unroll 4
+    for (int it = 0; it < QR / RPI; ++it) {
+      const int r = it * RPI + lr, row = row0 + r;
+      const uint4 v = *(const uint4 *)(q + r * QP + 2 * lc);
+      if (row >= m) continue;
+      uint16_t *dst = c + (int64_t)row * ldc + col;
+      if (col + 7 < n) {
+        *(uint4 *)dst = v;
+      } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (col + e < n) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int row = (g0 + fa0 + i) * 16 + rl;
+    if (row >= m) continue;
+    uint16_t *crow = c + (int64_t)row * ldc;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col0 = (n0 + wn * TN + j) * 16 + cl;
+      const v4f &a = acc[i][j];
+      const uint32_t lo = pack_bf16x2(apply_alpha(a[0], alpha), apply_alpha(a[1], alpha));
+      const uint32_t hi = pack_bf16x2(apply_alpha(a[2], alpha), apply_alpha(a[3], alpha));
+      if (vec_store && col0 + 3 < n) {
+        *(uint2 *)(crow + col0) = make_uint2(lo, hi);
+      } else {
+        if (col0 < n) crow[col0] = (uint16_t)lo;
+        if (col0 + 1 < n) crow[col0 + 1] = (uint16_t)(lo >> 16);
+        if (col0 + 2 < n) crow[col0 + 2] = (uint16_t)hi;
+        if (col0 + 3 < n) crow[col0 + 3] = (uint16_t)(hi >> 16);
+      }
+    }
+  }
+}
+
 }  // namespace
+
+namespace {
+std::atomic<int> g_nv_tile_mode{0};
+std::atomic<int> g_fuse_large{1};
+}  // namespace
+
+int large_linear_fusion() { return g_fuse_large.load(std::memory_order_relaxed); }
+int set_large_linear_fusion(int on) { return g_fuse_large.exchange(on ? 1 : 0, std::memory_order_relaxed); }
+
+int nvfp4_tile_mode() { return g_nv_tile_mode.load(std::memory_order_relaxed); }
+int set_nvfp4_tile_mode(int mode) { return g_nv_tile_mode.exchange(mode, std::memory_order_relaxed); }
 
 int gemm_tile_config(int fmt, int64_t m, int64_t n) {
   // 256 x 256 tiles when they give every CU (256) at least one tile; 128 x
@@ -507,15 +878,71 @@ hipError_t launch_gemm_tile(const GemmArgs &g, int cfg, hipStream_t stream) {
 #define FP4_TILE(F, A, B)                                                                       \
   hipLaunchKernelGGL((k_gemm_tile<F, A, B>), grid, dim3(256), 0, stream, g.a_codes, g.a_scales, \
                      g.a_ts, g.w_codes, g.w_scales, g.w_ts, (int)g.m, (int)g.n, kt_n, ga_n,      \
-                     nt_n, tiles_m, tiles_n, g.c, g.ldc, vec)
+                     nt_n, tiles_m, tiles_n, g.c, g.ldc, vec, Fused{})
   if (g.fmt == 1) {
     if (cfg == 88) FP4_TILE(1, 8, 8);
     else FP4_TILE(1, 4, 4);
   } else {
-    if (cfg == 88) FP4_TILE(0, 8, 8);
+    if (cfg == 88 && nvfp4_tile_mode() == 1)
+      hipLaunchKernelGGL((k_gemm_tile_nvlds<8, 8>), grid, dim3(256), 0, stream, g.a_codes,
+                         g.a_scales, g.a_ts, g.w_codes, g.w_scales, g.w_ts, (int)g.m, (int)g.n,
+                         kt_n, ga_n, nt_n, tiles_m, tiles_n, g.c, g.ldc, vec);
+    else if (cfg == 88) FP4_TILE(0, 8, 8);
     else FP4_TILE(0, 4, 4);
   }
 #undef FP4_TILE
+  return hipGetLastError();
+}
+
+bool linear_fused_large_ok(int fmt, uint32_t recipe, int64_t m, int64_t n, int64_t k,
+                           bool static_scale) {
+  (void)k;
+  if (!large_linear_fusion() || m <= kDecodeMaxM || (recipe & kRecipeMbs)) return false;
+  if (fmt == 0 && !static_scale) return false;   // a dynamic scale needs the whole tensor first
+  const int bm = gemm_tile_config(fmt, m, n) == 88 ? 256 : 128;
+  return (m + bm - 1) / bm <= kMaxPanels;
+}
+
+hipError_t launch_linear_fused_large(const GemmArgs &g, const uint16_t *x,
+                                     const float *static_scale, uint32_t recipe,
+                                     uint32_t *scratch, hipStream_t stream) {
+  const int kt_n = (int)(k_pad(g.k) / kFragK);
+  const int ga_n = (int)(round_up(g.m, 16) / 16);
+  const int nt_n = (int)(round_up(g.n, 16) / 16);
+  const int cfg = gemm_tile_config(g.fmt, g.m, g.n);
+  const int bm = cfg == 88 ? 256 : 128;
+  const int tiles_m = (int)((g.m + bm - 1) / bm), tiles_n = (int)((g.n + bm - 1) / bm);
+  // about one producer per CU, each panel split along K among `parts` of them;
+  // a multiple of the XCD count in all, so the tiles' XCD numbering holds
+  int parts = std::max(1, std::min(16, 256 / tiles_m));
+  while ((tiles_m * parts) % kXcds) ++parts;
+  const int nprod = tiles_m * parts;
+  const int vec = (g.ldc % 8 == 0 && (uintptr_t)g.c % 16 == 0)  ? 2
+                  : (g.ldc % 4 == 0 && (uintptr_t)g.c % 8 == 0) ? 1
+                                                                : 0;
+  Fused fz;
+  fz.x = x;
+  fz.st = static_scale;
+  fz.panel = scratch + kPanelWords;
+  fz.err = scratch + kErrWord;
+  fz.nprod = nprod;
+  fz.parts = parts;
+  fz.k = (int)g.k;
+  fz.recipe = recipe;
+  fz.spin = exchange_spin_limit();
+  dim3 grid((unsigned)(nprod + tiles_m * tiles_n));
+#define FP4_FTILE(F, A, B)                                                                        \
+  hipLaunchKernelGGL((k_gemm_tile<F, A, B, 1>), grid, dim3(256), 0, stream, g.a_codes, g.a_scales, \
+                     g.a_ts, g.w_codes, g.w_scales, g.w_ts, (int)g.m, (int)g.n, kt_n, ga_n,         \
+                     nt_n, tiles_m, tiles_n, g.c, g.ldc, vec, fz)
+  if (g.fmt == 1) {
+    if (cfg == 88) FP4_FTILE(1, 8, 8);
+    else FP4_FTILE(1, 4, 4);
+  } else {
+    if (cfg == 88) FP4_FTILE(0, 8, 8);
+    else FP4_FTILE(0, 4, 4);
+  }
+#undef FP4_FTILE
   return hipGetLastError();
 }
 

@@ -209,6 +209,13 @@ size_t fp4_linear_workspace_bytes(int32_t fmt, int64_t m, int64_t n, int64_t k);
  * y[m, N] (bf16, contiguous) = x[m, K] (bf16) through the cached weight `w`:
  * quantize x as fp4_quantize_act would (same static_scale rule), then
  * fp4_gemm. All intermediate data lives in `workspace`.
+ * For M > 128 with a static NVFP4 scale, or MXFP4 without macro-block scales,
+ * this is one launch: its first workgroups quantize the activations (each row
+ * panel of output tiles once, split along K among several workgroups) and
+ * the tile workgroups wait for their panel before reading it. That wait is
+ * bounded like the quantizer's maximum exchange: a tile that gives up makes
+ * its outputs NaN and sets FP4_WS_EXCHANGE_TIMEOUT (fp4_workspace_flags);
+ * the workspace must then be zero-filled again before it is reused.
  */
 fp4_status fp4_linear(const void *x_bf16, int64_t m, const fp4_tensor *w,
                       const float *static_scale, void *y_bf16, void *workspace,
@@ -247,9 +254,11 @@ fp4_status fp4_linear_w4a16(const void *x_bf16, int64_t m, const fp4_tensor *w, 
                             int64_t ldy, hipStream_t stream);
 
 /* Number of kernel launches fp4_linear makes for this shape: 1 when the
- * activation quantization is fused into the skinny GEMM (small M * K), 2 for
- * quantize + GEMM, 3 when the quantizer needs a separate reduction launch
- * (large NVFP4 activations with a dynamic scale). 0 for invalid arguments. */
+ * activation quantization is fused into the GEMM (small M * K on the skinny
+ * path; M > 128 with a static NVFP4 scale, or MXFP4 without macro-block
+ * scales, on the tile path), 2 for quantize + GEMM, 3 when the quantizer needs
+ * a separate reduction launch (large NVFP4 activations with a dynamic scale).
+ * 0 for invalid arguments. */
 int32_t fp4_linear_launches(int32_t fmt, int64_t m, int64_t n, int64_t k, int32_t static_scale);
 
 /*
@@ -273,6 +282,18 @@ fp4_status fp4_workspace_flags(const void *workspace, size_t workspace_bytes, ui
  * up (default 2^22; 0 gives up at once, which makes every such call fail as
  * described above). Process-wide; returns the previous value. */
 uint32_t fp4_set_exchange_spin_limit(uint32_t polls);
+
+/* Whether fp4_linear quantizes large-M activations inside the GEMM launch
+ * where it can (1, the default) or in a launch of its own (0). Same results
+ * either way. Process-wide; returns the previous setting. */
+int32_t fp4_set_large_linear_fusion(int32_t on);
+
+/* Where the NVFP4 product on 256 x 256 output tiles (large M) converts codes
+ * to exact f16 values: 0 = in the registers of each wave that uses a fragment
+ * (two waves per fragment), 1 = once per workgroup into LDS, the waves then
+ * reading f16 operands. Same results either way. Process-wide; returns the
+ * previous mode, or -1 for an invalid mode (nothing changed). */
+int32_t fp4_set_nvfp4_tile_mode(int32_t mode);
 
 /* Test aids (not on the hot path). */
 /* Copy a TILED tensor into a CANONICAL one of the same format/shape

@@ -99,6 +99,44 @@ def test_tile_unaligned_output_pitch(fmt):
     assert torch.all(big[:, n:] == 7.0), "stores past N"
 
 
+@pytest.fixture
+def nv_tile_lds():
+    """The NVFP4 256 x 256 tiles with the conversion in LDS for one test."""
+    prev = fp4.fp4_set_nvfp4_tile_mode(fp4.NV_TILE_LDS)
+    yield
+    fp4.fp4_set_nvfp4_tile_mode(prev)
+
+
+@pytest.mark.parametrize("m,n,k", [
+    (4096, 4096, 256),      # 2 K steps (one pass of the two-stage ring)
+    (4100, 4104, 384),      # ragged M and N, 3 K steps (odd stage count)
+    (4096, 4352, 128),      # 1 K step
+    (4224, 4096, 1152),     # 9 K steps
+    (4096, 4100, 2944),     # 23 K steps, K tail of 64 (K = 2880)
+])
+def test_nvfp4_tile_lds_conversion(nv_tile_lds, m, n, k):
+    """The NVFP4 tile with every fragment converted once per workgroup into
+    LDS matches the oracle, and matches the in-register conversion bit for bit
+    (both sum the same exact f16 products in the same order)."""
+    kk = 2880 if k == 2944 else k
+    a = synth.student_t((m, kk), 3.0, 4.0, 25, m + kk, plant=3616.0, n_plant=4)
+    w = synth.normal((n, kk), 0.02, 25, n * 3 + kk)
+    c_lds = _tiled_case("nvfp4", a, w, "nvfp4 tile, conversion in LDS")
+    prev = fp4.fp4_set_nvfp4_tile_mode(fp4.NV_TILE_REGISTERS)
+    try:
+        wq = fp4.fp4_quantize_weight(to_dev(w), fp4.NVFP4)
+        qa = fp4.fp4_quantize_act(to_dev(a), fp4.NVFP4, layout=fp4.TILED)
+        c_reg = bf16_out_to_f64(fp4.fp4_gemm(qa, wq))
+    finally:
+        fp4.fp4_set_nvfp4_tile_mode(prev)
+    assert np.array_equal(c_lds, c_reg)
+
+
+def test_nvfp4_tile_lds_square_8192_sampled(nv_tile_lds):
+    a, w = synth.square_inputs(8192, seed=0)
+    _sampled_full("nvfp4", a, w, "square 8192, conversion in LDS")
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 def test_tile_deterministic_and_graph(fmt):
     """Two eager calls agree bit for bit, and so does every replay of a graph
@@ -187,3 +225,73 @@ def test_square_16384_sampled(fmt):
     _sampled_full(fmt, a, w, "square 16384", nsamp=2048)
     if fmt == FMTS[-1]:
         _SQ16.clear()
+
+
+# ------------------------------------------- single-launch linear for large M
+
+@pytest.mark.parametrize("fmt,m,n,k,rotate", [
+    ("nvfp4", 4096, 4096, 256, False),     # 256 x 256 tiles, 16 panels
+    ("nvfp4", 4100, 4104, 384, False),     # ragged M and N
+    ("nvfp4", 300, 520, 2880, False),      # 128 x 128 tiles, K tail of 64
+    ("nvfp4", 4096, 3072, 3072, True),     # rotated
+    ("mxfp4", 4096, 4096, 1152, False),
+    ("mxfp4", 129, 1000, 4160, False),     # two panels, 33 K steps
+    ("mxfp4", 4224, 4096, 640, True),
+])
+def test_fused_large_linear(fmt, m, n, k, rotate):
+    """fp4_linear at M > 128 as one launch (the first workgroups quantize each
+    row panel of activations, split along K; the tiles wait for their panel):
+    within the tolerance of the oracle, and bit for bit the quantize + GEMM
+    result (the same codes and the same kernel arithmetic)."""
+    print(f"[fused-large] fmt={fmt} m={m} n={n} k={k} rotate={rotate}", flush=True)
+    f = F[fmt] | (fp4.ROTATE if rotate else 0)
+    a = synth.student_t((m, k), 3.0, 4.0, 26, m + 7 * k, plant=3616.0, n_plant=4)
+    w = synth.normal((n, k), 0.02, 26, n * 5 + k)
+    st_val = float(np.float32(1.5))
+    st = torch.tensor([st_val], dtype=torch.float32, device="cuda") if fmt == "nvfp4" else None
+    mode = oracle.STATIC if fmt == "nvfp4" else oracle.DYNAMIC
+    qa_ref = oracle.quantize(F[fmt], a, mode=mode, static_scale=st_val if st is not None else None,
+                             rotate=rotate)
+    qw_ref = oracle.quantize(F[fmt], w, rotate=rotate)
+    c_ref, l_ref = oracle.gemm(qa_ref, qw_ref)
+    assert fp4.fp4_linear_launches(f, m, n, k, st is not None) == 1
+    wq = fp4.fp4_quantize_weight(to_dev(w), f)
+    x = to_dev(a)
+    ws = torch.zeros(fp4.fp4_linear_workspace_bytes(f, m, n, k), dtype=torch.uint8, device="cuda")
+    y = fp4.fp4_linear(x, wq, static_scale=st, workspace=ws)
+    y2 = fp4.fp4_linear(x, wq, static_scale=st, workspace=ws)     # the panel words reset
+    assert_gemm_close(bf16_out_to_f64(y), c_ref, l_ref, "fused large linear")
+    prev = fp4.fp4_set_large_linear_fusion(False)
+    try:
+        assert fp4.fp4_linear_launches(f, m, n, k, st is not None) >= 2
+        y3 = fp4.fp4_linear(x, wq, static_scale=st)
+    finally:
+        fp4.fp4_set_large_linear_fusion(prev)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2) and torch.equal(y, y3)
+    assert fp4.fp4_workspace_flags(ws) == 0
+
+
+def test_fused_large_linear_give_up_is_visible():
+    """Tiles that give up waiting for their activation panel (forced from the
+    host: zero polls) output NaN and set the workspace flag; a re-zeroed
+    workspace then serves a correct call."""
+    m, n, k = 4096, 4096, 512
+    a = synth.normal((m, k), 1.0, 27, 1)
+    w = synth.normal((n, k), 0.02, 27, 2)
+    wq = fp4.fp4_quantize_weight(to_dev(w), fp4.MXFP4)
+    x = to_dev(a)
+    ws = torch.zeros(fp4.fp4_linear_workspace_bytes(fp4.MXFP4, m, n, k), dtype=torch.uint8, device="cuda")
+    prev = fp4.fp4_set_exchange_spin_limit(0)
+    try:
+        y = fp4.fp4_linear(x, wq, workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        fp4.fp4_set_exchange_spin_limit(prev)
+    assert torch.isnan(y.float()).all()
+    assert fp4.fp4_workspace_flags(ws) == fp4.WS_EXCHANGE_TIMEOUT
+    ws.zero_()
+    c_ref, l_ref = oracle.gemm(oracle.quantize(oracle.MXFP4, a), oracle.quantize(oracle.MXFP4, w))
+    y2 = fp4.fp4_linear(x, wq, workspace=ws)
+    assert_gemm_close(bf16_out_to_f64(y2), c_ref, l_ref, "after a give-up")
+    assert fp4.fp4_workspace_flags(ws) == 0
