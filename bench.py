@@ -62,9 +62,9 @@ def parse():
     p.add_argument("--nv-tile", default="", choices=["", "registers", "lds"],
                    help="NVFP4 256 x 256 tiles: convert codes to f16 in each wave's registers "
                         "or once per workgroup in LDS (default: the library's)")
-    p.add_argument("--no-fuse-large", action="store_true",
-                   help="large M: quantize the activations in a launch of their own instead of "
-                        "inside the GEMM launch (static NVFP4 scale or MXFP4)")
+    p.add_argument("--fuse-large", action="store_true",
+                   help="large M: quantize the activations inside the GEMM launch (static NVFP4 "
+                        "scale or MXFP4) instead of in a launch of their own")
     p.add_argument("--static-scale", type=float, default=0.0,
                    help="NVFP4: quantize the activations with this static tensor scale instead of "
                         "their dynamic one")
@@ -334,8 +334,8 @@ def main():
     dev = torch.device("cuda:0")
     if args.nv_tile:
         fp4.fp4_set_nvfp4_tile_mode(fp4.NV_TILE_LDS if args.nv_tile == "lds" else fp4.NV_TILE_REGISTERS)
-    if args.no_fuse_large:
-        fp4.fp4_set_large_linear_fusion(False)
+    if args.fuse_large:
+        fp4.fp4_set_large_linear_fusion(True)
     fmt = fp4.FORMATS[args.fmt]
     # qfmt: the format value with the recipe flags, given to every library call
     qfmt = fp4._fmt(args.fmt + ("+" + args.recipe if args.recipe else ""))

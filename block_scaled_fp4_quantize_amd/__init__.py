@@ -302,7 +302,8 @@ def fp4_set_exchange_spin_limit(polls: int) -> int:
 
 def fp4_set_large_linear_fusion(on: bool) -> bool:
     """Whether fp4_linear quantizes large-M activations inside the GEMM launch
-    (static NVFP4 scale or MXFP4). Process-wide; returns the previous setting."""
+    (static NVFP4 scale or MXFP4; off by default). Process-wide; returns the
+    previous setting."""
     return bool(lib().fp4_set_large_linear_fusion(int(bool(on))))
 
 

@@ -137,19 +137,23 @@ struct Fused {
 };
 
 // Device-coherent stores (write through to memory, the cache policy of
-// device-scope atomics), so that a consumer on another XCD reads them.
-__device__ __forceinline__ void store16_dev(uint8_t *p, uint4 v) {
+// device-scope atomics), so that a consumer on another XCD reads them. The
+// buffer resource is built from a wave-uniform base (a fragment's first byte)
+// and each lane passes its byte offset: a resource is a scalar operand, and
+// one built from a per-lane address makes the compiler issue the store once
+// per distinct lane value.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(uint8_t *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void store16_dev(__amdgpu_buffer_rsrc_t r, int off, uint4 v) {
   typedef unsigned int u4 __attribute__((ext_vector_type(4)));
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(p, 0, 16, 0x00020000);
-  __builtin_amdgcn_raw_buffer_store_b128(u4{v.x, v.y, v.z, v.w}, r, 0, 0, 16);
+  __builtin_amdgcn_raw_buffer_store_b128(u4{v.x, v.y, v.z, v.w}, r, off, 0, 16);
 }
-__device__ __forceinline__ void store2_dev(uint8_t *p, uint32_t v) {
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(p, 0, 2, 0x00020000);
-  __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, 0, 0, 16);
+__device__ __forceinline__ void store2_dev(__amdgpu_buffer_rsrc_t r, int off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, off, 0, 16);
 }
-__device__ __forceinline__ void store1_dev(uint8_t *p, uint32_t v) {
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(p, 0, 1, 0x00020000);
-  __builtin_amdgcn_raw_buffer_store_b8((unsigned char)v, r, 0, 0, 16);
+__device__ __forceinline__ void store1_dev(__amdgpu_buffer_rsrc_t r, int off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b8((unsigned char)v, r, off, 0, 16);
 }
 
 // Producer of the fused linear: quantizes part `part` (of `parts`) of row
@@ -161,44 +165,62 @@ template <int FMT, int FA>
 __device__ void fused_produce(const Fused &fz, int panel, int part, int m, int kt_n, int ga_n,
                              uint8_t *a_codes, uint8_t *a_sc) {
   constexpr int SCB = FMT == 0 ? 128 : 64;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, c = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, r = lane & 15, c = lane >> 4;
   const int g_lo = panel * FA, g_hi = min(g_lo + FA, ga_n);
   const int nfr = (g_hi - g_lo) * kt_n, per = (nfr + fz.parts - 1) / fz.parts;
   const int f_lo = part * per, f_hi = min(f_lo + per, nfr);
   const float st = FMT == 0 ? *fz.st : 1.0f;
-  for (int i = f_lo + wave; i < f_hi; i += 4) {
-    const int g = g_lo + i / kt_n, kt = i % kt_n;
-    const int64_t f = (int64_t)g * kt_n + kt;
-    const int row = g * 16 + r, k0 = kt * kFragK + 32 * c;
-    uint4 v[4];
-    const uint4 *src = (const uint4 *)(fz.x + (int64_t)row * fz.k + k0);
+  // U fragments per wave in flight: all their loads are issued before the
+  // first is encoded (a producer workgroup holds the tile kernel's LDS, so
+  // few of them share a CU and each must keep many loads outstanding); two
+  // for the 128-row tiles, whose kernels keep two waves per SIMD
+  constexpr int U = FA >= 16 ? 4 : 2;
+  for (int i0 = f_lo + wave; i0 < f_hi; i0 += 4 * U) {
+    uint4 v[U][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      v[j] = (row < m && k0 + 8 * j < fz.k) ? src[j] : make_uint4(0u, 0u, 0u, 0u);
-    if (fz.recipe & kRecipeRotate) {
-      if constexpr (FMT == 0) {
-        uint4 b0[2] = {v[0], v[1]}, b1[2] = {v[2], v[3]};
-        hadamard_block<16>(b0);
-        hadamard_block<16>(b1);
-        v[0] = b0[0]; v[1] = b0[1]; v[2] = b1[0]; v[3] = b1[1];
-      } else {
-        hadamard_block<32>(v);
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + 4 * u;
+      const int g = g_lo + i / kt_n, kt = i % kt_n;
+      const int row = g * 16 + r, k0 = kt * kFragK + 32 * c;
+      const bool live = i < f_hi && row < m;
+      const uint4 *src = (const uint4 *)(fz.x + (int64_t)row * fz.k + k0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        v[u][j] = (live && k0 + 8 * j < fz.k) ? src[j] : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + 4 * u;
+      if (i >= f_hi) break;
+      const int g = g_lo + i / kt_n, kt = i % kt_n;
+      const int64_t f = (int64_t)g * kt_n + kt;
+      const int row = g * 16 + r, k0 = kt * kFragK + 32 * c;
+      if (fz.recipe & kRecipeRotate) {
+        if constexpr (FMT == 0) {
+          uint4 b0[2] = {v[u][0], v[u][1]}, b1[2] = {v[u][2], v[u][3]};
+          hadamard_block<16>(b0);
+          hadamard_block<16>(b1);
+          v[u][0] = b0[0]; v[u][1] = b0[1]; v[u][2] = b1[0]; v[u][3] = b1[1];
+        } else {
+          hadamard_block<32>(v[u]);
+        }
       }
+      uint4 q = make_uint4(0u, 0u, 0u, 0u);
+      if constexpr (FMT == 0) {
+        uint2 c0 = make_uint2(0u, 0u), c1 = make_uint2(0u, 0u);
+        uint32_t s0 = 0, s1 = 0;
+        if (row < m && k0 < fz.k) nv_encode_block(v[u][0], v[u][1], st, c0, s0);
+        if (row < m && k0 + 16 < fz.k) nv_encode_block(v[u][2], v[u][3], st, c1, s1);
+        q = make_uint4(c0.x, c0.y, c1.x, c1.y);
+        store2_dev(dev_rsrc(a_sc + f * SCB, SCB), lane * 2, s0 | (s1 << 8));
+      } else {
+        uint32_t sc = 0;
+        if (row < m && k0 < fz.k) mx_encode_block(v[u], q, sc, fz.recipe & kRecipeOas);
+        store1_dev(dev_rsrc(a_sc + f * SCB, SCB), lane, sc);
+      }
+      store16_dev(dev_rsrc(a_codes + f * kFragCodeBytes, kFragCodeBytes), lane * 16, q);
     }
-    uint4 q = make_uint4(0u, 0u, 0u, 0u);
-    if constexpr (FMT == 0) {
-      uint2 c0 = make_uint2(0u, 0u), c1 = make_uint2(0u, 0u);
-      uint32_t s0 = 0, s1 = 0;
-      if (row < m && k0 < fz.k) nv_encode_block(v[0], v[1], st, c0, s0);
-      if (row < m && k0 + 16 < fz.k) nv_encode_block(v[2], v[3], st, c1, s1);
-      q = make_uint4(c0.x, c0.y, c1.x, c1.y);
-      store2_dev(a_sc + f * SCB + lane * 2, s0 | (s1 << 8));
-    } else {
-      uint32_t sc = 0;
-      if (row < m && k0 < fz.k) mx_encode_block(v, q, sc, fz.recipe & kRecipeOas);
-      store1_dev(a_sc + f * SCB + lane, sc);
-    }
-    store16_dev(a_codes + f * kFragCodeBytes + lane * 16, q);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores are complete
   __syncthreads();
@@ -845,7 +867,7 @@ __global__ __launch_bounds__(256) void k_gemm_tile_nvlds(
 
 namespace {
 std::atomic<int> g_nv_tile_mode{0};
-std::atomic<int> g_fuse_large{1};
+std::atomic<int> g_fuse_large{0};
 }  // namespace
 
 int large_linear_fusion() { return g_fuse_large.load(std::memory_order_relaxed); }

@@ -209,13 +209,14 @@ size_t fp4_linear_workspace_bytes(int32_t fmt, int64_t m, int64_t n, int64_t k);
  * y[m, N] (bf16, contiguous) = x[m, K] (bf16) through the cached weight `w`:
  * quantize x as fp4_quantize_act would (same static_scale rule), then
  * fp4_gemm. All intermediate data lives in `workspace`.
- * For M > 128 with a static NVFP4 scale, or MXFP4 without macro-block scales,
- * this is one launch: its first workgroups quantize the activations (each row
- * panel of output tiles once, split along K among several workgroups) and
- * the tile workgroups wait for their panel before reading it. That wait is
- * bounded like the quantizer's maximum exchange: a tile that gives up makes
- * its outputs NaN and sets FP4_WS_EXCHANGE_TIMEOUT (fp4_workspace_flags);
- * the workspace must then be zero-filled again before it is reused.
+ * With fp4_set_large_linear_fusion(1), M > 128 with a static NVFP4 scale, or
+ * MXFP4 without macro-block scales, is one launch: its first workgroups
+ * quantize the activations (each row panel of output tiles once, split along
+ * K among several workgroups) and the tile workgroups wait for their panel
+ * before reading it. That wait is bounded like the quantizer's maximum
+ * exchange: a tile that gives up makes its outputs NaN and sets
+ * FP4_WS_EXCHANGE_TIMEOUT (fp4_workspace_flags); the workspace must then be
+ * zero-filled again before it is reused.
  */
 fp4_status fp4_linear(const void *x_bf16, int64_t m, const fp4_tensor *w,
                       const float *static_scale, void *y_bf16, void *workspace,
@@ -284,8 +285,11 @@ fp4_status fp4_workspace_flags(const void *workspace, size_t workspace_bytes, ui
 uint32_t fp4_set_exchange_spin_limit(uint32_t polls);
 
 /* Whether fp4_linear quantizes large-M activations inside the GEMM launch
- * where it can (1, the default) or in a launch of its own (0). Same results
- * either way. Process-wide; returns the previous setting. */
+ * where it can (1) or in a launch of its own (0, the default: the separate
+ * quantizer keeps many waves on every CU, the producers inside the GEMM only
+ * as many as the tile kernel does, and the two-launch form measured as fast
+ * or faster). Same results either way. Process-wide; returns the previous
+ * setting. */
 int32_t fp4_set_large_linear_fusion(int32_t on);
 
 /* Where the NVFP4 product on 256 x 256 output tiles (large M) converts codes

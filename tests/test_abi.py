@@ -135,14 +135,19 @@ def test_linear_launch_count():
     # larger activations: quantize + GEMM (NVFP4 dynamic may need a reduction launch)
     assert L.fp4_linear_launches(fp4.NVFP4, 32, 5120, 5120, 0) == 2
     assert L.fp4_linear_launches(fp4.NVFP4, 4096, 3072, 3072, 0) == 3
-    # large M with a static scale (NVFP4) or MXFP4: quantization inside the GEMM launch
-    assert L.fp4_linear_launches(fp4.NVFP4, 4096, 3072, 3072, 1) == 1
-    assert L.fp4_linear_launches(fp4.MXFP4, 4096, 3072, 3072, 0) == 1
-    assert L.fp4_linear_launches(fp4.MXFP4 | fp4.MX_MBS, 4096, 3072, 3072, 0) == 2
-    prev = L.fp4_set_large_linear_fusion(0)
-    assert prev == 1
+    # large M with a static scale (NVFP4) or MXFP4: quantize + GEMM by default,
+    # quantization inside the GEMM launch once fusion is switched on
+    assert L.fp4_linear_launches(fp4.NVFP4, 4096, 3072, 3072, 1) == 2
     assert L.fp4_linear_launches(fp4.MXFP4, 4096, 3072, 3072, 0) == 2
-    assert L.fp4_set_large_linear_fusion(prev) == 0
+    prev = L.fp4_set_large_linear_fusion(1)
+    assert prev == 0
+    try:
+        assert L.fp4_linear_launches(fp4.NVFP4, 4096, 3072, 3072, 1) == 1
+        assert L.fp4_linear_launches(fp4.MXFP4, 4096, 3072, 3072, 0) == 1
+        assert L.fp4_linear_launches(fp4.MXFP4 | fp4.MX_MBS, 4096, 3072, 3072, 0) == 2
+        assert L.fp4_linear_launches(fp4.NVFP4, 4096, 3072, 3072, 0) == 3
+    finally:
+        assert L.fp4_set_large_linear_fusion(prev) == 1
     assert L.fp4_linear_launches(fp4.NVFP4, 4, 64, 40, 0) == 0
 
 

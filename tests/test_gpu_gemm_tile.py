@@ -229,6 +229,15 @@ def test_square_16384_sampled(fmt):
 
 # ------------------------------------------- single-launch linear for large M
 
+@pytest.fixture
+def large_fusion():
+    """fp4_linear with large-M quantization inside the GEMM launch (off by
+    default), restored afterwards."""
+    prev = fp4.fp4_set_large_linear_fusion(True)
+    yield
+    fp4.fp4_set_large_linear_fusion(prev)
+
+
 @pytest.mark.parametrize("fmt,m,n,k,rotate", [
     ("nvfp4", 4096, 4096, 256, False),     # 256 x 256 tiles, 16 panels
     ("nvfp4", 4100, 4104, 384, False),     # ragged M and N
@@ -238,7 +247,7 @@ def test_square_16384_sampled(fmt):
     ("mxfp4", 129, 1000, 4160, False),     # two panels, 33 K steps
     ("mxfp4", 4224, 4096, 640, True),
 ])
-def test_fused_large_linear(fmt, m, n, k, rotate):
+def test_fused_large_linear(fmt, m, n, k, rotate, large_fusion):
     """fp4_linear at M > 128 as one launch (the first workgroups quantize each
     row panel of activations, split along K; the tiles wait for their panel):
     within the tolerance of the oracle, and bit for bit the quantize + GEMM
@@ -267,12 +276,24 @@ def test_fused_large_linear(fmt, m, n, k, rotate):
         y3 = fp4.fp4_linear(x, wq, static_scale=st)
     finally:
         fp4.fp4_set_large_linear_fusion(prev)
+    assert fp4.fp4_linear_launches(f, m, n, k, st is not None) == 1
+    # other activations through the same workspace: the panels written by this
+    # call, not the lines the previous call left in any cache, are what the
+    # tiles read
+    x2 = to_dev(synth.normal((m, k), 2.0, 26, m + 11 * k))
+    y4 = fp4.fp4_linear(x2, wq, static_scale=st, workspace=ws)
+    fp4.fp4_set_large_linear_fusion(False)
+    try:
+        y5 = fp4.fp4_linear(x2, wq, static_scale=st)
+    finally:
+        fp4.fp4_set_large_linear_fusion(True)
     torch.cuda.synchronize()
     assert torch.equal(y, y2) and torch.equal(y, y3)
+    assert torch.equal(y4, y5) and not torch.equal(y4, y)
     assert fp4.fp4_workspace_flags(ws) == 0
 
 
-def test_fused_large_linear_give_up_is_visible():
+def test_fused_large_linear_give_up_is_visible(large_fusion):
     """Tiles that give up waiting for their activation panel (forced from the
     host: zero polls) output NaN and set the workspace flag; a re-zeroed
     workspace then serves a correct call."""
