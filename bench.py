@@ -65,6 +65,9 @@ def parse():
     p.add_argument("--fuse-large", action="store_true",
                    help="large M: quantize the activations inside the GEMM launch (static NVFP4 "
                         "scale or MXFP4) instead of in a launch of their own")
+    p.add_argument("--fuse-decode", action="store_true",
+                   help="1-32 rows: quantize the activations inside the skinny GEMM's launch "
+                        "instead of in a launch of their own")
     p.add_argument("--static-scale", type=float, default=0.0,
                    help="NVFP4: quantize the activations with this static tensor scale instead of "
                         "their dynamic one")
@@ -336,6 +339,8 @@ def main():
         fp4.fp4_set_nvfp4_tile_mode(fp4.NV_TILE_LDS if args.nv_tile == "lds" else fp4.NV_TILE_REGISTERS)
     if args.fuse_large:
         fp4.fp4_set_large_linear_fusion(True)
+    if args.fuse_decode:
+        fp4.fp4_set_decode_linear_fusion(True)
     fmt = fp4.FORMATS[args.fmt]
     # qfmt: the format value with the recipe flags, given to every library call
     qfmt = fp4._fmt(args.fmt + ("+" + args.recipe if args.recipe else ""))
@@ -527,8 +532,20 @@ def main():
             us = lin_us
             nbytes = w_bytes + 2 * m * k + 2 * m * n          # W + bf16 A + bf16 C
         elif m <= 128 and fp4.fp4_linear_launches(qfmt, m, n, k, st_dev is not None) == 1:
-            # one launch: quantization inside the skinny GEMM
-            name = "k_linear_decode<%s>" % args.fmt
+            # one launch: quantization inside the skinny GEMM, by every
+            # workgroup (k_linear_decode, small activations) or by producer
+            # workgroups ahead of the GEMM workgroups
+            prev = fp4.fp4_set_decode_linear_fusion(False)
+            try:
+                every_wg = fp4.fp4_linear_launches(qfmt, m, n, k, st_dev is not None) == 1
+            finally:
+                fp4.fp4_set_decode_linear_fusion(prev)
+            if every_wg:
+                name = "k_linear_decode<%s>" % args.fmt
+            else:
+                name = "%s<%s,MG=%d,producers>" % (
+                    "k_gemm_decode_ring" if qfmt == fp4.NVFP4 else "k_gemm_decode", args.fmt,
+                    1 if m <= 16 else 2)
             us = lin_us
             nbytes = w_bytes + 2 * m * k + 2 * m * n          # W + bf16 A + bf16 C
         else:

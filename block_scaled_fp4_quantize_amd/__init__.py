@@ -88,6 +88,7 @@ def lib():
             "fp4_set_exchange_spin_limit": (ctypes.c_uint32, [ctypes.c_uint32]),
             "fp4_set_nvfp4_tile_mode": (I32, [I32]),
             "fp4_set_large_linear_fusion": (I32, [I32]),
+            "fp4_set_decode_linear_fusion": (I32, [I32]),
             "fp4_status_string": (ctypes.c_char_p, [I32]),
             "fp4_last_error": (ctypes.c_char_p, []),
         }
@@ -305,6 +306,13 @@ def fp4_set_large_linear_fusion(on: bool) -> bool:
     (static NVFP4 scale or MXFP4; off by default). Process-wide; returns the
     previous setting."""
     return bool(lib().fp4_set_large_linear_fusion(int(bool(on))))
+
+
+def fp4_set_decode_linear_fusion(on: bool) -> bool:
+    """Whether fp4_linear with at most 32 activation rows quantizes them inside
+    the skinny GEMM's launch (off by default). Process-wide; returns the
+    previous setting."""
+    return bool(lib().fp4_set_decode_linear_fusion(int(bool(on))))
 
 
 NV_TILE_REGISTERS, NV_TILE_LDS = 0, 1

@@ -308,6 +308,23 @@ fp4_status linear_run(const void *x_bf16, int64_t m, const fp4_tensor *w,
   a.codes = ws + L.codes;
   a.scales = ws + L.scales;
   a.tensor_scale = (float *)(ws + L.ts);
+  if (linear_fused_decode_ok(base, recipe_of(fmt), m, n, k)) {
+    // one launch: quantization by the first workgroups of the skinny GEMM
+    GemmArgs g;
+    g.fmt = base;
+    g.a_tiled = 1;
+    g.a_codes = (const uint8_t *)a.codes; g.a_cpitch = 0;
+    g.a_scales = (const uint8_t *)a.scales; g.a_spitch = 0;
+    g.a_ts = static_scale ? static_scale : a.tensor_scale;
+    g.w_codes = (const uint8_t *)w->codes; g.w_scales = (const uint8_t *)w->scales;
+    g.w_ts = w->tensor_scale;
+    g.m = m; g.n = n; g.k = k;
+    g.c = (uint16_t *)y_bf16; g.ldc = n;
+    hipError_t e = launch_linear_fused_decode(g, (const uint16_t *)x_bf16, static_scale,
+                                              recipe_of(fmt), (uint32_t *)(ws + L.scratch), stream);
+    if (e != hipSuccess) return hip_fail(e, "fused decode linear launch");
+    return FP4_OK;
+  }
   if (linear_fused_large_ok(base, recipe_of(fmt), m, n, k, static_scale != nullptr)) {
     // one launch: quantization by the first workgroups, tiles by the rest
     GemmArgs g;
@@ -535,6 +552,7 @@ int32_t fp4_linear_launches(int32_t fmt, int64_t m, int64_t n, int64_t k, int32_
   const int base = base_fmt(fmt);
   if (k % block_of(base) != 0) return 0;
   if (use_fused(fmt, m, n, k)) return 1;
+  if (linear_fused_decode_ok(base, recipe_of(fmt), m, n, k)) return 1;
   if (linear_fused_large_ok(base, recipe_of(fmt), m, n, k, static_scale != 0)) return 1;
   if (base == FP4_NVFP4 && !static_scale && !quant_fits_small(base, m, k, 1)) return 3;
   return 2;
@@ -605,6 +623,8 @@ fp4_status fp4_workspace_flags(const void *workspace, size_t workspace_bytes, ui
 uint32_t fp4_set_exchange_spin_limit(uint32_t polls) { return set_exchange_spin_limit(polls); }
 
 int32_t fp4_set_large_linear_fusion(int32_t on) { return set_large_linear_fusion(on); }
+
+int32_t fp4_set_decode_linear_fusion(int32_t on) { return set_decode_linear_fusion(on); }
 
 int32_t fp4_set_nvfp4_tile_mode(int32_t mode) {
   if (mode != 0 && mode != 1) return -1;

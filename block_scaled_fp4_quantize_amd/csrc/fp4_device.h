@@ -199,6 +199,63 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t *lds) {
   return r;
 }
 
+// Maximum over a group of G workgroups (this one is member g) through NS
+// tagged 32-bit slots, ST words apart (one 128-byte line each, so that polls
+// of different slots go to different lines): (call tag << 16) | a member's
+// maximum as bf16 bits (< 2^15). Member g writes slots g, g + G, g + 2G, ...,
+// so every call rewrites every slot whatever its group size, and after any
+// call all slots carry that call's tag; a call's tag is therefore one more
+// than any slot's tag at its start (a zero-filled array is tag 0). Thread
+// t < G polls slot t until it carries this call's tag, and the workgroup takes
+// the maximum. The values travel in the polled words themselves, so no cache
+// writeback or fence is involved. The wait assumes every member runs at the
+// same time; it is bounded by spin_limit polls per slot. A slot that does not
+// arrive in time counts as 0xFFFF, so a result at or above 0x8000 (no bf16
+// magnitude is) tells the caller this workgroup gave up.
+template <int NS, int ST>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t wg_max, uint32_t tag, uint32_t *slots,
+                                                  uint32_t g, uint32_t G, uint32_t spin_limit,
+                                                  uint32_t *lds) {
+  for (uint32_t s = g + threadIdx.x * G; s < (uint32_t)NS; s += blockDim.x * G)
+    __hip_atomic_store(&slots[s * ST], (tag << 16) | wg_max, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  uint32_t v = 0;
+  if (threadIdx.x < G) {
+    bool arrived = false;
+    for (uint32_t it = 0; it < spin_limit; ++it) {
+      v = __hip_atomic_load(&slots[threadIdx.x * ST], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((v >> 16) == tag) {
+        arrived = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    v = arrived ? (v & 0xFFFFu) : 0xFFFFu;
+  }
+  return block_max_u32(v, lds);
+}
+
+// Device-coherent stores (write through to memory, the cache policy of
+// device-scope atomics), so that a reader in another workgroup of the same
+// launch, on any XCD, sees them once the writer's stores are complete and it
+// has said so through a device-scope atomic. The buffer resource is built
+// from a wave-uniform base (a fragment's first byte) and each lane passes its
+// byte offset: a resource is a scalar operand, and one built from a per-lane
+// address makes the compiler issue the store once per distinct lane value.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(void *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void store16_dev(__amdgpu_buffer_rsrc_t r, int off, uint4 v) {
+  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(u4{v.x, v.y, v.z, v.w}, r, off, 0, 16);
+}
+__device__ __forceinline__ void store2_dev(__amdgpu_buffer_rsrc_t r, int off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, off, 0, 16);
+}
+__device__ __forceinline__ void store1_dev(__amdgpu_buffer_rsrc_t r, int off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b8((unsigned char)v, r, off, 0, 16);
+}
+
 // |x| max of 8 bf16 values as a bit pattern (magnitudes order like their bits).
 __device__ __forceinline__ uint32_t absmax_bits8(uint4 v) {
   uint32_t m = 0;

@@ -123,13 +123,28 @@ hipError_t launch_gemm_tile(const GemmArgs &g, int cfg, hipStream_t stream);
 // and error flags. Whether it applies: linear_fused_large_ok.
 bool linear_fused_large_ok(int fmt, uint32_t recipe, int64_t m, int64_t n, int64_t k,
                            bool static_scale);
-// Whether fp4_linear uses it when it applies (1, the default) or quantizes in
-// a separate launch (0).
+// Whether fp4_linear uses it when it applies (1) or quantizes in a separate
+// launch (0, the default).
 int large_linear_fusion();
 int set_large_linear_fusion(int on);
 hipError_t launch_linear_fused_large(const GemmArgs &g, const uint16_t *x,
                                      const float *static_scale, uint32_t recipe,
                                      uint32_t *scratch, hipStream_t stream);
+
+// Single-launch linear for 1-32 activation rows (no macro-block scales): the
+// skinny GEMM's launch, whose first workgroups quantize x [m, k] into the
+// tiled layout at g.a_codes / g.a_scales while the GEMM workgroups issue their
+// first weight loads and wait (bounded) for them. g.a_ts: the static NVFP4
+// scale, or the word the dynamic S_t is written to. `scratch`: the quantize
+// scratch (kQuantScratchBytes, zero-filled once). Whether fp4_linear uses it
+// (where k_linear_decode does not apply): decode_linear_fusion() (0, the
+// default: quantize + GEMM measured faster).
+bool linear_fused_decode_ok(int fmt, uint32_t recipe, int64_t m, int64_t n, int64_t k);
+int decode_linear_fusion();
+int set_decode_linear_fusion(int on);
+hipError_t launch_linear_fused_decode(const GemmArgs &g, const uint16_t *x,
+                                      const float *static_scale, uint32_t recipe,
+                                      uint32_t *scratch, hipStream_t stream);
 
 // Single-launch linear (activation quantization fused) for small activations.
 constexpr int kFusedMaxM = 16;

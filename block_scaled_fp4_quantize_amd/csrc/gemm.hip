@@ -23,6 +23,7 @@
 #include "fp4_internal.h"
 
 #include <algorithm>
+#include <atomic>
 
 namespace fp4i {
 using namespace fp4d;
@@ -98,6 +99,174 @@ __device__ __forceinline__ void load_w(const uint8_t *__restrict__ w_codes,
   q = *(const uint4 *)(w_codes + f * kFragCodeBytes + lane * 16);
   sc = FMT == 0 ? (uint32_t)*(const uint16_t *)(w_sc + f * 128 + lane * 2)
                 : (uint32_t)w_sc[f * 64 + lane];
+}
+
+// ------------------------------------------------- decode, single launch
+//
+// fp4_linear for 1-32 activation rows as one launch of the skinny GEMM: its
+// first nprod workgroups quantize the activations into the workspace's tiled
+// layout, one wave per 16-row fragment, with device-coherent stores, and
+// count themselves in a ready word once their stores are complete; the GEMM
+// workgroups (numbered after them) issue their first weight loads, wait,
+// bounded, for the count, and only then load the activations. The count is
+// kept in kReadyCopies words on lines of their own (producers add to all, GEMM
+// workgroup b polls copy b % kReadyCopies with one wave): with every wave of
+// a thousand resident workgroups polling one word, the polls swamped that
+// word's memory channel and the decode calls ran 1.3-3x slower. Dispatch
+// follows the workgroup index, so the producers are running before any
+// GEMM workgroup waits for them. NVFP4 with a dynamic tensor scale: the
+// producers first exchange their maxima (group_max_u32), as the single-launch
+// quantizer's workgroups do, and the last to arrive publishes S_t. A wait
+// that gives up sets the sticky error flag and makes the output NaN; the last
+// GEMM workgroup to pass its wait resets the ready word for the next call.
+struct DecFused {
+  const uint16_t *x;   // bf16 activations [m, k]
+  const float *st;     // NVFP4 static tensor scale (device), or null
+  uint32_t *ts_out;    // NVFP4 dynamic: the tensor scale's bits go here
+  uint32_t *slots;     // tagged maximum slots (kActGrid, kSlotStride words apart)
+  uint32_t *err;       // sticky error flags
+  uint32_t *arrive;    // producers past the exchange (low half), gave up (high half)
+  uint32_t *ready;     // [r * kSlotStride] (r < kReadyCopies) producers done;
+                       // [kReadyCopies * kSlotStride] GEMM workgroups past their wait
+  int nprod, k;
+  uint32_t recipe, spin;
+};
+
+// Fragments per producer wave at most: one, so that the producers' registers
+// stay below the GEMM workgroups' (the kernel's count is the larger of the two).
+constexpr int kDecProdFrags = 1;
+constexpr int kReadyCopies = 16;
+static_assert((kReadyCopies + 1) * kSlotStride <= 2 * kMaxPanels,
+              "the ready words fit the quantize scratch's panel words");
+
+// Producer p of the single-launch decode linear: fragments p * NW + wave +
+// u * nprod * NW (u < kDecProdFrags) of the activations' tiled layout.
+template <int FMT, int NW>
+__device__ void decode_produce(const DecFused &fz, int m, int kt_n, uint8_t *a_codes,
+                               uint8_t *a_sc, uint32_t *lds) {
+  constexpr int SCB = FMT == 0 ? 128 : 64, U = kDecProdFrags;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, r = lane & 15, c = lane >> 4;
+  const int nfr = ((m + 15) >> 4) * kt_n, P = fz.nprod, p = blockIdx.x;
+  uint4 v[U][4];
+  uint32_t amax = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int f = p * NW + wave + u * P * NW;
+    const int row = (f / kt_n) * 16 + r, k0 = (f % kt_n) * kFragK + 32 * c;
+    const bool live = f < nfr && row < m;
+    const uint4 *src = (const uint4 *)(fz.x + (int64_t)row * fz.k + k0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      v[u][j] = (live && k0 + 8 * j < fz.k) ? src[j] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  // (no rotation here: its code would raise the kernel's register count for
+  // every call; rotated activations take the two-launch path)
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) amax = max(amax, absmax_bits8(v[u][j]));
+  float st = 1.0f;
+  if (FMT == 0) {
+    if (fz.st) {
+      st = *fz.st;
+    } else {
+      // this call's tag: one more than the previous call's (slot p is written
+      // only by producer p)
+      const uint32_t tag = ((__hip_atomic_load(&fz.slots[p * kSlotStride], __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT) >> 16) + 1u) & 0xFFFFu;
+      const uint32_t g = group_max_u32<kActGrid, kSlotStride>(block_max_u32(amax, lds), tag,
+                                                              fz.slots, p, P, fz.spin, lds);
+      const bool gave_up = g >= 0x8000u;
+      st = gave_up ? __builtin_nanf("") : tensor_scale_from_amax(bf16_bits_to_f32(g));
+      if (threadIdx.x == 0) {
+        if (gave_up)
+          __hip_atomic_fetch_or(fz.err, kErrExchangeTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t before = __hip_atomic_fetch_add(fz.arrive, gave_up ? 0x10001u : 1u,
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((before & 0xFFFFu) == (uint32_t)P - 1) {
+          // the last producer past the exchange: every other one has decided
+          const bool any = gave_up || (before >> 16) != 0u;
+          __hip_atomic_store(fz.ts_out, __float_as_uint(any ? __builtin_nanf("") : st),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(fz.arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int f = p * NW + wave + u * P * NW;
+    if (f >= nfr) break;  // wave-uniform
+    const int row = (f / kt_n) * 16 + r, k0 = (f % kt_n) * kFragK + 32 * c;
+    uint4 q = make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (FMT == 0) {
+      uint2 c0 = make_uint2(0u, 0u), c1 = make_uint2(0u, 0u);
+      uint32_t s0 = 0, s1 = 0;
+      if (row < m && k0 < fz.k) nv_encode_block(v[u][0], v[u][1], st, c0, s0);
+      if (row < m && k0 + 16 < fz.k) nv_encode_block(v[u][2], v[u][3], st, c1, s1);
+      q = make_uint4(c0.x, c0.y, c1.x, c1.y);
+      store2_dev(dev_rsrc(a_sc + (int64_t)f * SCB, SCB), lane * 2, s0 | (s1 << 8));
+    } else {
+      uint32_t sc = 0;
+      if (row < m && k0 < fz.k) mx_encode_block(v[u], q, sc, fz.recipe & kRecipeOas);
+      store1_dev(dev_rsrc(a_sc + (int64_t)f * SCB, SCB), lane, sc);
+    }
+    store16_dev(dev_rsrc(a_codes + (int64_t)f * kFragCodeBytes, kFragCodeBytes), lane * 16, q);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores are complete
+  __syncthreads();
+  if (threadIdx.x < kReadyCopies)
+    __hip_atomic_fetch_add(&fz.ready[threadIdx.x * kSlotStride], 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A GEMM workgroup's wait for the producers: wave 0 polls its copy of the
+// count (bounded), the workgroup's barrier releases the other waves. Returns
+// whether the wait gave up (every thread gets the answer), having set the
+// sticky flag. `flag`: one LDS word.
+__device__ __forceinline__ bool decode_wait(const DecFused &fz, uint32_t *flag) {
+  if (threadIdx.x < 64) {
+    const uint32_t b = blockIdx.x - (uint32_t)fz.nprod;
+    const uint32_t *word = &fz.ready[(b % kReadyCopies) * kSlotStride];
+    bool ok = false;
+    for (uint32_t it = 0; it < fz.spin; ++it) {
+      if (__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (uint32_t)fz.nprod) {
+        ok = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (threadIdx.x == 0) {
+      if (!ok)
+        __hip_atomic_fetch_or(fz.err, kErrExchangeTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *flag = ok ? 0u : 1u;
+    }
+  }
+  __syncthreads();
+  return *flag != 0u;
+}
+
+// After every wave of the workgroup has passed its wait (thread 0): the last
+// GEMM workgroup resets the ready words.
+__device__ __forceinline__ void decode_finish(const DecFused &fz) {
+  const uint32_t ngemm = gridDim.x - (uint32_t)fz.nprod;
+  uint32_t *fin = &fz.ready[kReadyCopies * kSlotStride];
+  const uint32_t done = __hip_atomic_fetch_add(fin, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (done == ngemm - 1) {
+    for (int r = 0; r < kReadyCopies; ++r)
+      __hip_atomic_store(&fz.ready[r * kSlotStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(fin, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// The activation pointers, as the loads after a wait must see them: an empty
+// asm statement that "changes" them, so that no load through them can be
+// moved above the wait.
+template <typename T>
+__device__ __forceinline__ T *after_wait(T *p) {
+  asm volatile("" : "+s"(p)::"memory");
+  return p;
 }
 
 // ------------------------------------------------------------------ prefill
@@ -217,17 +386,25 @@ constexpr int kDecFrags = 2;
 
 // MB: MXFP4 with macro-block scales (a_ms, w_ms): each fragment's product is
 // added with its rows' and columns' segment scales.
-template <int FMT, int MG, int ATILED, int NT, int MB = 0>
+// FUSED: the single-launch linear (DecFused): the first fz.nprod workgroups
+// quantize the activations, the rest wait for them after their first weight
+// loads.
+template <int FMT, int MG, int ATILED, int NT, int MB = 0, int FUSED = 0>
 __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(
     const uint8_t *__restrict__ a_codes, int64_t a_cp, const uint8_t *__restrict__ a_sc,
     int64_t a_sp, const float *__restrict__ a_ts, const uint8_t *__restrict__ w_codes,
     const uint8_t *__restrict__ w_sc, const float *__restrict__ w_ts, int m, int n, int kt_n,
     int nt_n, uint16_t *__restrict__ c, int64_t ldc, const float *__restrict__ a_ms,
-    int64_t a_mp, const float *__restrict__ w_ms) {
+    int64_t a_mp, const float *__restrict__ w_ms, DecFused fz) {
   // fragments per group: two, or one for eight activation groups (registers)
   constexpr int NW = kDecWaves, FM = MG >= 8 ? 1 : kDecFrags;
   __shared__ float red[NW][NT * MG][4][64];
-  const int nt0 = blockIdx.x * NT;  // first of this workgroup's NT weight tiles
+  if (FUSED && (int)blockIdx.x < fz.nprod) {
+    decode_produce<FMT, NW>(fz, m, kt_n, (uint8_t *)a_codes, (uint8_t *)a_sc, (uint32_t *)red);
+    return;
+  }
+  // first of this workgroup's NT weight tiles
+  const int nt0 = (FUSED ? (int)blockIdx.x - fz.nprod : (int)blockIdx.x) * NT;
   // readfirstlane makes the wave index (and every fragment guard derived from
   // it) a scalar, so the guards compile to branches around the matrix
   // instructions rather than to EXEC masks they would not honour.
@@ -243,24 +420,28 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(
   float4 wm[2][FM][NT];   // MB: the lane's four weight rows' segment scales
   float am[2][FM][MG];    // MB: its activation row's
 
-  auto load = [&](int buf, int base) {
+  auto load = [&](int buf, int base, bool lw = true, bool la = true) {
 #pragma unroll
     for (int u = 0; u < FM; ++u) {
       const int kt = base + NW * u;
       if (kt < kt_n) {
+        if (lw) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          // a tile past the last one reads the last again (its sums are never stored)
-          const int nt = min(nt0 + t, nt_n - 1);
-          load_w<FMT>(w_codes, w_sc, (int64_t)nt * kt_n + kt, lane, wq[buf][u][t], ws[buf][u][t]);
-          if (MB)
-            wm[buf][u][t] = *(const float4 *)(w_ms + ((int64_t)nt * kt_n + kt) * 16 + 4 * (lane >> 4));
+          for (int t = 0; t < NT; ++t) {
+            // a tile past the last one reads the last again (its sums are never stored)
+            const int nt = min(nt0 + t, nt_n - 1);
+            load_w<FMT>(w_codes, w_sc, (int64_t)nt * kt_n + kt, lane, wq[buf][u][t], ws[buf][u][t]);
+            if (MB)
+              wm[buf][u][t] = *(const float4 *)(w_ms + ((int64_t)nt * kt_n + kt) * 16 + 4 * (lane >> 4));
+          }
         }
+        if (la) {
 #pragma unroll
-        for (int g = 0; g < MG; ++g) {
-          load_a<FMT, ATILED>(a_codes, a_cp, a_sc, a_sp, kt_n, g, kt, lane, m, aq[buf][u][g],
-                              as[buf][u][g]);
-          if (MB) am[buf][u][g] = a_macro<ATILED>(a_ms, a_mp, kt_n, 16 * g + (lane & 15), kt, m);
+          for (int g = 0; g < MG; ++g) {
+            load_a<FMT, ATILED>(a_codes, a_cp, a_sc, a_sp, kt_n, g, kt, lane, m, aq[buf][u][g],
+                                as[buf][u][g]);
+            if (MB) am[buf][u][g] = a_macro<ATILED>(a_ms, a_mp, kt_n, 16 * g + (lane & 15), kt, m);
+          }
         }
       }
     }
@@ -298,7 +479,17 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(
     }
   };
   constexpr int STEP = NW * FM;
-  load(0, wave);
+  bool gave_up = false;
+  if (FUSED) {
+    load(0, wave, true, false);
+    __shared__ uint32_t wait_flag;
+    gave_up = decode_wait(fz, &wait_flag);
+    a_codes = after_wait(a_codes);
+    a_sc = after_wait(a_sc);
+    load(0, wave, false, true);
+  } else {
+    load(0, wave);
+  }
   for (int base = wave; base < kt_n; base += 2 * STEP) {
     load(1, base + STEP);
     compute(0, base);
@@ -311,12 +502,19 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_gemm_decode(
 #pragma unroll
     for (int g = 0; g < MG; ++g)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[wave][t * MG + g][r][lane] = acc[t][g][r];
+      for (int r = 0; r < 4; ++r)
+        red[wave][t * MG + g][r][lane] = gave_up ? __builtin_nanf("") : acc[t][g][r];
   __syncthreads();
+  if (FUSED && threadIdx.x == 0) decode_finish(fz);
   const int tg = threadIdx.x >> 6;  // accumulator group reduced by this wave
   if (tg >= NT * MG) return;
   const int t = tg / MG, g = tg % MG;
-  const Alpha alpha = FMT == 0 ? make_alpha(a_ts[0], w_ts[0]) : Alpha{1.0f, 0};
+  // (the single-launch linear's dynamic S_t is written during this launch)
+  const float sa = FMT != 0 ? 1.0f
+                   : FUSED ? __uint_as_float(__hip_atomic_load((const uint32_t *)a_ts, __ATOMIC_RELAXED,
+                                                              __HIP_MEMORY_SCOPE_AGENT))
+                           : a_ts[0];
+  const Alpha alpha = FMT == 0 ? make_alpha(sa, w_ts[0]) : Alpha{1.0f, 0};
   const int col = 16 * g + (lane & 15);  // activation row m
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -365,15 +563,22 @@ __device__ __forceinline__ uint32_t buf_load_scale(__amdgpu_buffer_rsrc_t r, uin
 // The operand pointers are not declared __restrict__: the compiler would then
 // take the buffer loads as invariant and move them across the ordering
 // statements below.
-template <int FMT, int MG, int ATILED, int NT, int NWT>
+// FUSED: the single-launch linear, as in k_gemm_decode.
+template <int FMT, int MG, int ATILED, int NT, int NWT, int FUSED = 0>
 __global__ __launch_bounds__(64 * NWT) void k_gemm_decode_ring(
     const uint8_t *a_codes, int64_t a_cp, const uint8_t *a_sc, int64_t a_sp,
     const float *__restrict__ a_ts, const uint8_t *w_codes, const uint8_t *w_sc,
-    const float *__restrict__ w_ts, int m, int n, int kt_n, int nt_n, uint16_t *c, int64_t ldc) {
+    const float *__restrict__ w_ts, int m, int n, int kt_n, int nt_n, uint16_t *c, int64_t ldc,
+    DecFused fz) {
   constexpr int NW = NWT, D = kRingDepth;
   constexpr int SFB = FMT == 0 ? 128 : 64;  // scale bytes per fragment
   __shared__ float red[NW][NT * MG][4][64];
-  const int nt0 = blockIdx.x * NT;  // first of this workgroup's NT weight tiles
+  if (FUSED && (int)blockIdx.x < fz.nprod) {
+    decode_produce<FMT, NW>(fz, m, kt_n, (uint8_t *)a_codes, (uint8_t *)a_sc, (uint32_t *)red);
+    return;
+  }
+  // first of this workgroup's NT weight tiles
+  const int nt0 = (FUSED ? (int)blockIdx.x - fz.nprod : (int)blockIdx.x) * NT;
   // readfirstlane makes the wave index (and every guard derived from it) a
   // scalar, so guards compile to branches rather than to EXEC masks that a
   // matrix instruction would not honour.
@@ -387,10 +592,10 @@ __global__ __launch_bounds__(64 * NWT) void k_gemm_decode_ring(
   // Activations: tiled = ceil(m / 16) groups of kt_n fragments; canonical =
   // m rows of pitch a_cp (codes) and a_sp (scales).
   const int ag = (m + 15) >> 4;
-  const __amdgpu_buffer_rsrc_t ar =
-      buf_rsrc(a_codes, (uint32_t)(ATILED ? (int64_t)ag * kt_n * kFragCodeBytes : (int64_t)m * a_cp));
-  const __amdgpu_buffer_rsrc_t asr =
-      buf_rsrc(a_sc, (uint32_t)(ATILED ? (int64_t)ag * kt_n * SFB : (int64_t)m * a_sp));
+  const uint32_t a_bytes = (uint32_t)(ATILED ? (int64_t)ag * kt_n * kFragCodeBytes : (int64_t)m * a_cp);
+  const uint32_t as_bytes = (uint32_t)(ATILED ? (int64_t)ag * kt_n * SFB : (int64_t)m * a_sp);
+  // (rebuilt after the wait in the single-launch linear)
+  __amdgpu_buffer_rsrc_t ar = buf_rsrc(a_codes, a_bytes), asr = buf_rsrc(a_sc, as_bytes);
   const int lr = lane & 15, lc = lane >> 4;
 
   v4f acc[NT][MG];
@@ -405,14 +610,17 @@ __global__ __launch_bounds__(64 * NWT) void k_gemm_decode_ring(
   // activation rows >= m) take an offset past every resource's end (each is
   // below 2^31 bytes), so they return zero without reading memory.
   constexpr uint32_t kOut = 0x80000000u;
-  auto issue = [&](int d, int kt) {
+  auto issue = [&](int d, int kt, bool lw = true, bool la = true) {
     const bool kin = kt < kt_n;
+    if (lw) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const uint32_t f = (uint32_t)(t * kt_n + kt);
-      wq[d][t] = buf_load16(wr, kin ? f * kFragCodeBytes + lane * 16 : kOut);
-      ws[d][t] = buf_load_scale<FMT>(wsr, kin ? f * SFB + lane * (FMT == 0 ? 2 : 1) : kOut);
+      for (int t = 0; t < NT; ++t) {
+        const uint32_t f = (uint32_t)(t * kt_n + kt);
+        wq[d][t] = buf_load16(wr, kin ? f * kFragCodeBytes + lane * 16 : kOut);
+        ws[d][t] = buf_load_scale<FMT>(wsr, kin ? f * SFB + lane * (FMT == 0 ? 2 : 1) : kOut);
+      }
     }
+    if (!la) return;
 #pragma unroll
     for (int g = 0; g < MG; ++g) {
       const int row = 16 * g + lr;
@@ -456,10 +664,28 @@ __global__ __launch_bounds__(64 * NWT) void k_gemm_decode_ring(
   // An empty asm statement with a memory clobber between slots keeps the
   // slots' loads in slot order (the order in which they are consumed), so
   // that each slot waits only for its own and older loads.
+  bool gave_up = false;
+  if (FUSED) {
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    issue(d, wave + NW * d);
-    asm volatile("" ::: "memory");
+    for (int d = 0; d < D; ++d) {
+      issue(d, wave + NW * d, true, false);
+      asm volatile("" ::: "memory");
+    }
+    __shared__ uint32_t wait_flag;
+    gave_up = decode_wait(fz, &wait_flag);
+    ar = buf_rsrc(after_wait(a_codes), a_bytes);
+    asr = buf_rsrc(after_wait(a_sc), as_bytes);
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      issue(d, wave + NW * d, false, true);
+      asm volatile("" ::: "memory");
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      issue(d, wave + NW * d);
+      asm volatile("" ::: "memory");
+    }
   }
   for (int j0 = 0; j0 < J; j0 += D) {
 #pragma unroll
@@ -474,9 +700,16 @@ __global__ __launch_bounds__(64 * NWT) void k_gemm_decode_ring(
 #pragma unroll
     for (int g = 0; g < MG; ++g)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[wave][t * MG + g][r][lane] = acc[t][g][r];
+      for (int r = 0; r < 4; ++r)
+        red[wave][t * MG + g][r][lane] = gave_up ? __builtin_nanf("") : acc[t][g][r];
   __syncthreads();
-  const Alpha alpha = FMT == 0 ? make_alpha(a_ts[0], w_ts[0]) : Alpha{1.0f, 0};
+  if (FUSED && threadIdx.x == 0) decode_finish(fz);
+  // (the single-launch linear's dynamic S_t is written during this launch)
+  const float sa = FMT != 0 ? 1.0f
+                   : FUSED ? __uint_as_float(__hip_atomic_load((const uint32_t *)a_ts, __ATOMIC_RELAXED,
+                                                              __HIP_MEMORY_SCOPE_AGENT))
+                           : a_ts[0];
+  const Alpha alpha = FMT == 0 ? make_alpha(sa, w_ts[0]) : Alpha{1.0f, 0};
   for (int tg = wave; tg < NT * MG; tg += NW) {  // accumulator groups reduced by this wave
     const int t = tg / MG, g = tg % MG;
     const int col = 16 * g + lr;  // activation row m
@@ -654,10 +887,23 @@ hipError_t launch_gemm_prefill(const GemmArgs &g, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_decode(const GemmArgs &g, hipStream_t stream) {
+namespace {
+
+// The skinny GEMM's launch; with fz, the single-launch linear (tiled
+// activations, at most 32 rows, no macro-block scales: checked by the caller),
+// whose grid is fz->nprod producers followed by the GEMM workgroups. The
+// producer count is set here from the chosen kernel's waves.
+hipError_t decode_launch(const GemmArgs &g, DecFused *fz, hipStream_t stream) {
   const int kt_n = (int)(k_pad(g.k) / kFragK);
   const int nt_n = (int)(round_up(g.n, 16) / 16);
   const int mg = g.m <= 16 ? 1 : g.m <= 32 ? 2 : g.m <= 64 ? 4 : 8;
+  const int nfr = (int)(round_up(g.m, 16) / 16) * kt_n;
+  auto producers = [&](int waves) {
+    if (!fz) return 0;
+    fz->nprod = std::min(kActGrid, (nfr + waves * kDecProdFrags - 1) / (waves * kDecProdFrags));
+    return fz->nprod;
+  };
+  const DecFused none{};
   if (g.fmt == 0) {
     // the ring kernel's buffer resources (and offsets) stay below 2^31 bytes
     const int64_t a_bytes = g.a_tiled ? round_up(g.m, 16) / 16 * kt_n * kFragCodeBytes
@@ -675,18 +921,30 @@ hipError_t launch_gemm_decode(const GemmArgs &g, hipStream_t stream) {
     const bool two1 = mg == 1 && nt_n >= 256 && nt_n < 512;
     const bool two2 = mg == 2 && nt_n >= 256;
     const bool two = two1 || two2;
-    dim3 grid((unsigned)(two ? (nt_n + 1) / 2 : nt_n));
-#define FP4_RING1(G, T, P, W)                                                                   \
-  hipLaunchKernelGGL((k_gemm_decode_ring<0, G, T, P, W>), grid, dim3(64 * W), 0, stream,    \
-                     g.a_codes, g.a_cpitch, g.a_scales, g.a_spitch, g.a_ts, g.w_codes,      \
-                     g.w_scales, g.w_ts, (int)g.m, (int)g.n, kt_n, nt_n, g.c, g.ldc)
-#define FP4_RING_T(G, P, W) do { if (g.a_tiled) FP4_RING1(G, 1, P, W); else FP4_RING1(G, 0, P, W); } while (0)
+    const int ngemm = two ? (nt_n + 1) / 2 : nt_n;
+#define FP4_RING1(G, T, P, W, FU)                                                                   \
+  hipLaunchKernelGGL((k_gemm_decode_ring<0, G, T, P, W, FU>), dim3((unsigned)(ngemm + producers(W))), \
+                     dim3(64 * W), 0, stream, g.a_codes, g.a_cpitch, g.a_scales, g.a_spitch, g.a_ts,  \
+                     g.w_codes, g.w_scales, g.w_ts, (int)g.m, (int)g.n, kt_n, nt_n, g.c, g.ldc,       \
+                     fz ? *fz : none)
+#define FP4_RING_T(G, P, W)                         \
+  do {                                              \
+    if (fz) FP4_RING1(G, 1, P, W, 1);               \
+    else if (g.a_tiled) FP4_RING1(G, 1, P, W, 0);   \
+    else FP4_RING1(G, 0, P, W, 0);                  \
+  } while (0)
+#define FP4_RING_N(G, P, W)                         \
+  do {                                              \
+    if (g.a_tiled) FP4_RING1(G, 1, P, W, 0);        \
+    else FP4_RING1(G, 0, P, W, 0);                  \
+  } while (0)
     if (two1) FP4_RING_T(1, 2, 2 * kRingWaves);
     else if (mg == 1) FP4_RING_T(1, 1, kRingWaves);
     else if (two2) FP4_RING_T(2, 2, kRingWaves);
     else if (mg == 2) FP4_RING_T(2, 1, kRingWaves);
-    else if (mg == 4) FP4_RING_T(4, 1, kRingWaves);
-    else FP4_RING_T(8, 1, kRingWaves);
+    else if (mg == 4) FP4_RING_N(4, 1, kRingWaves);
+    else FP4_RING_N(8, 1, kRingWaves);
+#undef FP4_RING_N
 #undef FP4_RING_T
 #undef FP4_RING1
     return hipGetLastError();
@@ -697,28 +955,81 @@ hipError_t launch_gemm_decode(const GemmArgs &g, hipStream_t stream) {
   // (at 256-511 tiles it measured mixed: M = 32, N = 5120: 5.7 -> 5.9 us at
   // K = 5120, 18.3 -> 17.4 us at K = 17408)
   const int nt_per = (mg == 2 && nt_n >= 512) ? 2 : 1;
-  dim3 grid((unsigned)((nt_n + nt_per - 1) / nt_per));
-#define FP4_DEC(F, G, T, P, MB)                                                                 \
-  hipLaunchKernelGGL((k_gemm_decode<F, G, T, P, MB>), grid, dim3(64 * kDecWaves), 0, stream,   \
-                     g.a_codes, g.a_cpitch, g.a_scales, g.a_spitch, g.a_ts, g.w_codes,         \
-                     g.w_scales, g.w_ts, (int)g.m, (int)g.n, kt_n, nt_n, g.c, g.ldc, g.a_ms,   \
-                     g.a_mpitch, g.w_ms)
-#define FP4_DEC_T(F, G, P)                                                 \
-  do {                                                                     \
-    if (g.w_ms) {                                                          \
-      if (g.a_tiled) FP4_DEC(F, G, 1, P, 1); else FP4_DEC(F, G, 0, P, 1); \
-    } else {                                                               \
-      if (g.a_tiled) FP4_DEC(F, G, 1, P, 0); else FP4_DEC(F, G, 0, P, 0); \
-    }                                                                      \
+  const int ngemm = (nt_n + nt_per - 1) / nt_per;
+#define FP4_DEC(F, G, T, P, MB, FU)                                                                  \
+  hipLaunchKernelGGL((k_gemm_decode<F, G, T, P, MB, FU>), dim3((unsigned)(ngemm + producers(kDecWaves))), \
+                     dim3(64 * kDecWaves), 0, stream, g.a_codes, g.a_cpitch, g.a_scales, g.a_spitch,    \
+                     g.a_ts, g.w_codes, g.w_scales, g.w_ts, (int)g.m, (int)g.n, kt_n, nt_n, g.c, g.ldc, \
+                     g.a_ms, g.a_mpitch, g.w_ms, fz ? *fz : none)
+#define FP4_DEC_N(F, G, P)                                                       \
+  do {                                                                           \
+    if (g.w_ms) {                                                                \
+      if (g.a_tiled) FP4_DEC(F, G, 1, P, 1, 0); else FP4_DEC(F, G, 0, P, 1, 0); \
+    } else {                                                                     \
+      if (g.a_tiled) FP4_DEC(F, G, 1, P, 0, 0); else FP4_DEC(F, G, 0, P, 0, 0); \
+    }                                                                            \
+  } while (0)
+#define FP4_DEC_T(F, G, P)                        \
+  do {                                            \
+    if (fz) FP4_DEC(F, G, 1, P, 0, 1);            \
+    else FP4_DEC_N(F, G, P);                      \
   } while (0)
   if (mg == 1) FP4_DEC_T(1, 1, 1);
   else if (mg == 2 && nt_per == 2) FP4_DEC_T(1, 2, 2);
   else if (mg == 2) FP4_DEC_T(1, 2, 1);
-  else if (mg == 4) FP4_DEC_T(1, 4, 1);
-  else FP4_DEC_T(1, 8, 1);
+  else if (mg == 4) FP4_DEC_N(1, 4, 1);
+  else FP4_DEC_N(1, 8, 1);
 #undef FP4_DEC_T
+#undef FP4_DEC_N
 #undef FP4_DEC
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_decode(const GemmArgs &g, hipStream_t stream) {
+  return decode_launch(g, nullptr, stream);
+}
+
+namespace {
+std::atomic<int> g_fuse_decode{0};
+}  // namespace
+
+int decode_linear_fusion() { return g_fuse_decode.load(std::memory_order_relaxed); }
+int set_decode_linear_fusion(int on) {
+  return g_fuse_decode.exchange(on ? 1 : 0, std::memory_order_relaxed);
+}
+
+static_assert(kRingWaves == kDecWaves, "the producer bound assumes eight-wave workgroups at least");
+
+bool linear_fused_decode_ok(int fmt, uint32_t recipe, int64_t m, int64_t n, int64_t k) {
+  (void)fmt;
+  (void)n;
+  // every fragment has a producer wave: at most kActGrid producers (the
+  // exchange's slots) of at least kRingWaves = kDecWaves waves
+  const int64_t nfr = round_up(m, 16) / 16 * (k_pad(k) / kFragK);
+  return decode_linear_fusion() && m <= 32 && !(recipe & (kRecipeMbs | kRecipeRotate)) &&
+         nfr <= (int64_t)kActGrid * kDecWaves * kDecProdFrags;
+}
+
+hipError_t launch_linear_fused_decode(const GemmArgs &g, const uint16_t *x,
+                                      const float *static_scale, uint32_t recipe,
+                                      uint32_t *scratch, hipStream_t stream) {
+  // g: tiled activations at g.a_codes / g.a_scales (written by this launch),
+  // g.a_ts = static_scale or the word the dynamic S_t goes to
+  DecFused fz;
+  fz.x = x;
+  fz.st = static_scale;
+  fz.ts_out = (uint32_t *)g.a_ts;
+  fz.slots = scratch + kMaxAmaxParts;
+  fz.err = scratch + kErrWord;
+  fz.arrive = scratch + kArriveWord;
+  fz.ready = scratch + kPanelWords;
+  fz.nprod = 0;
+  fz.k = (int)g.k;
+  fz.recipe = recipe;
+  fz.spin = exchange_spin_limit();
+  return decode_launch(g, &fz, stream);
 }
 
 bool linear_fused_ok(int fmt, int64_t m, int64_t n, int64_t k) {

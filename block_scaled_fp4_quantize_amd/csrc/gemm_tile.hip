@@ -136,26 +136,6 @@ struct Fused {
   uint32_t recipe, spin;
 };
 
-// Device-coherent stores (write through to memory, the cache policy of
-// device-scope atomics), so that a consumer on another XCD reads them. The
-// buffer resource is built from a wave-uniform base (a fragment's first byte)
-// and each lane passes its byte offset: a resource is a scalar operand, and
-// one built from a per-lane address makes the compiler issue the store once
-// per distinct lane value.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(uint8_t *base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000);
-}
-__device__ __forceinline__ void store16_dev(__amdgpu_buffer_rsrc_t r, int off, uint4 v) {
-  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
-  __builtin_amdgcn_raw_buffer_store_b128(u4{v.x, v.y, v.z, v.w}, r, off, 0, 16);
-}
-__device__ __forceinline__ void store2_dev(__amdgpu_buffer_rsrc_t r, int off, uint32_t v) {
-  __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, off, 0, 16);
-}
-__device__ __forceinline__ void store1_dev(__amdgpu_buffer_rsrc_t r, int off, uint32_t v) {
-  __builtin_amdgcn_raw_buffer_store_b8((unsigned char)v, r, off, 0, 16);
-}
-
 // Producer of the fused linear: quantizes part `part` (of `parts`) of row
 // panel `panel` of the activations into the tiled layout, one wave per
 // fragment (lane 16c + r: row r, values 32c .. 32c + 31), with the same

@@ -286,42 +286,13 @@ __global__ __launch_bounds__(kThreads) void k_quant_tiled(
 
 // ------------------------------------------------------------------ small
 
-// Maximum over every workgroup of the grid. The kActGrid slots are 32-bit
-// words (call tag << 16) | a workgroup maximum's bf16 bits (< 2^15); workgroup
-// g writes slots g, g + G, g + 2G, ... (G = grid size), so every call rewrites
-// every slot whatever its grid size, and after any call all slots carry that
-// call's tag. A call's tag is therefore one more than any slot's tag at its
-// start (a zero-filled array is tag 0). Thread t < G polls slot t until it
-// carries this call's tag, and the workgroup takes the maximum. The exchanged
-// values travel in the polled words themselves, so no cache writeback or fence
-// is involved. Each word has a 128-byte line of its own (kSlotStride words
-// apart), so that the polls of different words go to different lines.
-// The wait assumes every workgroup of the grid (at most kActGrid of at most
-// 512 threads) runs at the same time; it is bounded by spin_limit polls per
-// slot. A slot that does not arrive in time counts as 0xFFFF, so a result at
-// or above 0x8000 (no bf16 magnitude is) tells the caller this workgroup gave
-// up.
+// Maximum over every workgroup of the grid (group_max_u32 with the grid as
+// the group). The wait assumes every workgroup of the grid (at most kActGrid
+// of at most 512 threads) runs at the same time.
 __device__ __forceinline__ uint32_t grid_max_u32(uint32_t wg_max, uint32_t tag, uint32_t *slots,
                                                  uint32_t spin_limit, uint32_t *lds) {
-  for (uint32_t s = blockIdx.x + threadIdx.x * gridDim.x; s < (uint32_t)kActGrid;
-       s += blockDim.x * gridDim.x)
-    __hip_atomic_store(&slots[s * kSlotStride], (tag << 16) | wg_max, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-  uint32_t v = 0;
-  if (threadIdx.x < gridDim.x) {
-    bool arrived = false;
-    for (uint32_t it = 0; it < spin_limit; ++it) {
-      v = __hip_atomic_load(&slots[threadIdx.x * kSlotStride], __ATOMIC_RELAXED,
-                            __HIP_MEMORY_SCOPE_AGENT);
-      if ((v >> 16) == tag) {
-        arrived = true;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-    v = arrived ? (v & 0xFFFFu) : 0xFFFFu;
-  }
-  return block_max_u32(v, lds);
+  return group_max_u32<kActGrid, kSlotStride>(wg_max, tag, slots, blockIdx.x, gridDim.x,
+                                              spin_limit, lds);
 }
 
 // Largest magnitude (bf16 bits) of the whole tensor, taken by one workgroup

@@ -209,6 +209,14 @@ size_t fp4_linear_workspace_bytes(int32_t fmt, int64_t m, int64_t n, int64_t k);
  * y[m, N] (bf16, contiguous) = x[m, K] (bf16) through the cached weight `w`:
  * quantize x as fp4_quantize_act would (same static_scale rule), then
  * fp4_gemm. All intermediate data lives in `workspace`.
+ * Small activations (M * K small enough for every workgroup to quantize them
+ * itself) take one launch of the skinny GEMM with that quantization inside.
+ * Otherwise, for M <= 32 without macro-block scales or rotation, and with
+ * fp4_set_decode_linear_fusion(1), this is one launch of the skinny GEMM: its
+ * first workgroups quantize the activations into the workspace while the
+ * GEMM workgroups issue their first weight loads and then wait for them. That
+ * wait is bounded like the quantizer's maximum exchange (FP4_WS_EXCHANGE_TIMEOUT,
+ * NaN outputs, the workspace to be zero-filled again before reuse, as below).
  * With fp4_set_large_linear_fusion(1), M > 128 with a static NVFP4 scale, or
  * MXFP4 without macro-block scales, is one launch: its first workgroups
  * quantize the activations (each row panel of output tiles once, split along
@@ -291,6 +299,14 @@ uint32_t fp4_set_exchange_spin_limit(uint32_t polls);
  * or faster). Same results either way. Process-wide; returns the previous
  * setting. */
 int32_t fp4_set_large_linear_fusion(int32_t on);
+
+/* Whether fp4_linear with at most 32 activation rows quantizes them inside the
+ * skinny GEMM's launch (1) or in a launch of its own (0, the default: the
+ * GEMM workgroups can prefetch only their first weight fragments while they
+ * wait, and the producers' chain of loads, stores and counts took longer
+ * than a launch of its own). Same results either way. Process-wide; returns
+ * the previous setting. */
+int32_t fp4_set_decode_linear_fusion(int32_t on);
 
 /* Where the NVFP4 product on 256 x 256 output tiles (large M) converts codes
  * to exact f16 values: 0 = in the registers of each wave that uses a fragment

@@ -135,6 +135,26 @@ def test_linear_launch_count():
     # larger activations: quantize + GEMM (NVFP4 dynamic may need a reduction launch)
     assert L.fp4_linear_launches(fp4.NVFP4, 32, 5120, 5120, 0) == 2
     assert L.fp4_linear_launches(fp4.NVFP4, 4096, 3072, 3072, 0) == 3
+    # 1-32 rows with producer workgroups inside the skinny GEMM's launch, once
+    # switched on; rotated and macro-block-scaled activations excepted
+    prev = L.fp4_set_decode_linear_fusion(1)
+    assert prev == 0
+    try:
+        for k, n in ((5120, 5120), (5120, 17408), (17408, 5120)):
+            for m in (1, 2, 4, 8, 32):
+                assert L.fp4_linear_launches(fp4.NVFP4, m, n, k, 0) == 1
+                assert L.fp4_linear_launches(fp4.MXFP4, m, n, k, 0) == 1
+                assert L.fp4_linear_launches(fp4.NVFP4, m, n, k, 1) == 1
+        assert L.fp4_linear_launches(fp4.NVFP4 | fp4.ROTATE, 8, 5120, 5120, 0) == 2
+        assert L.fp4_linear_launches(fp4.MXFP4 | fp4.MX_MBS, 8, 5120, 5120, 0) == 2
+        assert L.fp4_linear_launches(fp4.MXFP4 | fp4.MX_OAS, 8, 5120, 5120, 0) == 1
+        assert L.fp4_linear_launches(fp4.NVFP4, 33, 5120, 5120, 0) == 2
+        # at most 1024 activation fragments (128 producers of eight waves)
+        assert L.fp4_linear_launches(fp4.MXFP4, 32, 256, 65536, 0) == 1
+        assert L.fp4_linear_launches(fp4.MXFP4, 32, 256, 65536 + 128, 0) == 2
+        assert L.fp4_linear_launches(fp4.NVFP4, 16, 256, 2 * 65536, 1) == 1
+    finally:
+        assert L.fp4_set_decode_linear_fusion(prev) == 1
     # large M with a static scale (NVFP4) or MXFP4: quantize + GEMM by default,
     # quantization inside the GEMM launch once fusion is switched on
     assert L.fp4_linear_launches(fp4.NVFP4, 4096, 3072, 3072, 1) == 2

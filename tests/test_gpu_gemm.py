@@ -262,12 +262,21 @@ def test_forward_layer_sampled(fmt, m):
         assert_gemm_close(y[rows, cols], c_ref, l_ref, f"forward {name} m={m}")
 
 
+@pytest.fixture
+def no_decode_fusion():
+    """fp4_linear with 1-32 rows as quantize + GEMM where the fused skinny
+    linear does not apply (the producer form switched off), restored after."""
+    prev = fp4.fp4_set_decode_linear_fusion(False)
+    yield
+    fp4.fp4_set_decode_linear_fusion(prev)
+
+
 @pytest.mark.parametrize("m,k,n,launches", [(2, 5120, 5120, 1), (3, 5120, 5120, 2),
                                             (1, 16384, 4096, 1), (1, 16384, 4112, 2)])
-def test_nvfp4_fused_bound(m, k, n, launches):
+def test_nvfp4_fused_bound(m, k, n, launches, no_decode_fusion):
     """NVFP4 fp4_linear on both sides of the fused path's M * K_pad * tiles
-    bound (4M): the fused single launch and quantize + GEMM agree with the
-    oracle alike."""
+    bound (4M), with the producer form of the skinny linear switched off: the
+    fused single launch and quantize + GEMM agree with the oracle alike."""
     assert fp4.fp4_linear_launches("nvfp4", m, n, k) == launches
     a = synth.normal((m, k), 1.0, 11, m * 7 + k)
     w = synth.normal((n, k), 0.02, 11, n * 5 + k)
@@ -359,3 +368,96 @@ def test_zero_activations_give_zero_output(fmt, m, k, n):
         assert ((bits & 0x7FFF) == 0).all(), f"{what}: nonzero output for zero activations"
     assert (qa.codes_2d().cpu().numpy()[:, : k // 2] == 0).all()
     assert (qa.scales_2d().cpu().numpy()[:, : k // oracle.BLOCK[f]] == 0).all()
+
+
+# ------------------------------------------------ single-launch decode linear
+
+# (shapes past the fused skinny linear's bounds: more than 16 rows, or M * K_pad
+# or M * K_pad * tiles above them)
+_DEC1_CASES = [(12, 5200, 5120), (8, 1040, 17408), (19, 1000, 4160), (32, 5120, 5120),
+               (17, 8200, 512),      # two weight tiles per workgroup
+               (16, 4112, 4224),     # NVFP4: 16-wave workgroups with two tiles
+               (1, 8200, 640),       # NVFP4: >= 512 tiles, one row
+               (32, 48, 128),        # fewer K fragments than waves
+               (32, 48, 65536)]      # 1024 fragments: 128 producers, the most
+
+
+@pytest.fixture
+def decode_fusion():
+    """fp4_linear with 1-32 rows as one launch with producer workgroups (off by
+    default), restored afterwards."""
+    prev = fp4.fp4_set_decode_linear_fusion(True)
+    yield
+    fp4.fp4_set_decode_linear_fusion(prev)
+
+
+@pytest.mark.parametrize("fmt,static", [("nvfp4", False), ("nvfp4", True), ("mxfp4", False),
+                                        ("mxfp4+oas", False)])
+@pytest.mark.parametrize("m,n,k", _DEC1_CASES)
+def test_decode_single_launch(fmt, static, m, n, k, decode_fusion):
+    """fp4_linear with 1-32 rows as one launch of the skinny GEMM whose first
+    workgroups quantize the activations (NVFP4 dynamic: exchanging their
+    maxima first): 2048 sampled outputs within the oracle's tolerance, the
+    whole output bit for bit the two-launch result, and a second call with
+    other activations through the same workspace reading that call's codes."""
+    print(f"[decode-1launch] fmt={fmt} static={static} m={m} n={n} k={k}", flush=True)
+    f = fp4._fmt(fmt)
+    ofmt = F[fmt.split("+")[0]]
+    oas = "oas" in fmt
+    st_val = float(np.float32(0.75))
+    st = torch.tensor([st_val], dtype=torch.float32, device="cuda") if static else None
+    a = synth.student_t((m, k), 3.0, 2.0, 51, m * 13 + k, plant=3616.0, n_plant=2)
+    a2 = synth.normal((m, k), 3.0, 51, m * 17 + k)
+    w = synth.normal((n, k), 0.02, 51, n * 7 + k)
+    assert fp4.fp4_linear_launches(f, m, n, k, static) == 1
+    wq = fp4.fp4_quantize_weight(to_dev(w), f)
+    x, x2 = to_dev(a), to_dev(a2)
+    ws = torch.zeros(fp4.fp4_linear_workspace_bytes(f, m, n, k), dtype=torch.uint8, device="cuda")
+    y = fp4.fp4_linear(x, wq, static_scale=st, workspace=ws)
+    y2 = fp4.fp4_linear(x2, wq, static_scale=st, workspace=ws)
+    fp4.fp4_set_decode_linear_fusion(False)
+    try:
+        y_two = fp4.fp4_linear(x, wq, static_scale=st)
+        y2_two = fp4.fp4_linear(x2, wq, static_scale=st)
+    finally:
+        fp4.fp4_set_decode_linear_fusion(True)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_two), "single launch differs from quantize + GEMM"
+    assert torch.equal(y2, y2_two), "second call through the same workspace"
+    assert fp4.fp4_workspace_flags(ws) == 0
+    mode = oracle.STATIC if static else oracle.DYNAMIC
+    qa_ref = oracle.quantize(ofmt, a, mode=mode, static_scale=st_val if static else None, oas=oas)
+    qw_ref = oracle.quantize(ofmt, w, oas=oas)
+    rng = np.random.default_rng(m * 3 + n)
+    rows, cols = rng.integers(0, m, 2048), rng.integers(0, n, 2048)
+    c_ref, l_ref = oracle.gemm_sampled(qa_ref, qw_ref, rows, cols)
+    assert_gemm_close(bf16_out_to_f64(y)[rows, cols], c_ref, l_ref, f"single-launch decode {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_decode_single_launch_give_up_is_visible(fmt, decode_fusion):
+    """The GEMM workgroups' wait for the producers (and, NVFP4, the producers'
+    maximum exchange) forced to give up from the host (zero polls): every
+    output NaN, the workspace flag set; re-zeroed, the workspace serves a
+    correct call."""
+    m, n, k = 32, 5120, 5120
+    print(f"[decode-1launch] give-up fmt={fmt}", flush=True)
+    a = synth.normal((m, k), 1.0, 52, 1)
+    w = synth.normal((n, k), 0.02, 52, 2)
+    assert fp4.fp4_linear_launches(F[fmt], m, n, k) == 1
+    wq = fp4.fp4_quantize_weight(to_dev(w), F[fmt])
+    x = to_dev(a)
+    ws = torch.zeros(fp4.fp4_linear_workspace_bytes(F[fmt], m, n, k), dtype=torch.uint8, device="cuda")
+    prev = fp4.fp4_set_exchange_spin_limit(0)
+    try:
+        y = fp4.fp4_linear(x, wq, workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        fp4.fp4_set_exchange_spin_limit(prev)
+    assert torch.isnan(y.float()).all()
+    assert fp4.fp4_workspace_flags(ws) == fp4.WS_EXCHANGE_TIMEOUT
+    ws.zero_()
+    c_ref, l_ref = oracle.gemm(oracle.quantize(F[fmt], a), oracle.quantize(F[fmt], w))
+    y2 = fp4.fp4_linear(x, wq, workspace=ws)
+    assert_gemm_close(bf16_out_to_f64(y2), c_ref, l_ref, "after a give-up")
+    assert fp4.fp4_workspace_flags(ws) == 0

@@ -183,7 +183,15 @@ def test_exchange_give_up_is_visible(m, k):
     print(f"[quant-act] exchange give-up m={m} k={k}", flush=True)
     a = synth.normal((m, k), 1.0, 21, m + k)
     w = synth.normal((n, k), 0.02, 21, 2)
-    assert fp4.fp4_linear_launches(fp4.NVFP4, m, n, k) == 2   # quantizer with the exchange
+    prev_fusion = fp4.fp4_set_decode_linear_fusion(False)   # the two-launch linear
+    try:
+        assert fp4.fp4_linear_launches(fp4.NVFP4, m, n, k) == 2   # quantizer with the exchange
+        _exchange_give_up(m, k, n, a, w)
+    finally:
+        fp4.fp4_set_decode_linear_fusion(prev_fusion)
+
+
+def _exchange_give_up(m, k, n, a, w):
     wq = fp4.fp4_quantize_weight(to_dev(w), fp4.NVFP4)
     x = to_dev(a)
     ws_q = torch.zeros(fp4.lib().fp4_quantize_workspace_bytes(fp4.NVFP4, m, k), dtype=torch.uint8,
