@@ -115,7 +115,8 @@ def gemm_bytes(m, k, n, fmt):
     return n * q + m * q + 2 * m * n
 
 
-DOMINANT = ("k_gemm_decode", "k_linear_decode", "k_gemm_tile", "k_w4a16_decode", "k_w4a16_tile")
+DOMINANT = ("k_gemm_decode", "k_linear_decode", "k_gemm_tile", "k_gemm_prefill", "k_w4a16_decode",
+            "k_w4a16_tile")
 
 
 def kernel_source_hash():
@@ -544,7 +545,7 @@ def main():
                 name = "k_linear_decode<%s>" % args.fmt
             else:
                 name = "%s<%s,MG=%d,producers>" % (
-                    "k_gemm_decode_ring" if qfmt == fp4.NVFP4 else "k_gemm_decode", args.fmt,
+                    "k_gemm_decode_ring" if fmt == 0 else "k_gemm_decode", args.fmt,
                     1 if m <= 16 else 2)
             us = lin_us
             nbytes = w_bytes + 2 * m * k + 2 * m * n          # W + bf16 A + bf16 C
@@ -552,7 +553,7 @@ def main():
             # the activation layout fp4_linear uses internally (fragment-tiled)
             qa = fp4.fp4_quantize_act(xs[cfg], qfmt, layout=fp4.TILED)
             if m <= 128:
-                name = "%s<%s,MG=%d>" % ("k_gemm_decode_ring" if qfmt == fp4.NVFP4 else "k_gemm_decode",
+                name = "%s<%s,MG=%d>" % ("k_gemm_decode_ring" if fmt == 0 else "k_gemm_decode",
                                          args.fmt, 1 if m <= 16 else 2 if m <= 32 else 4 if m <= 64 else 8)
             elif "mbs" in args.recipe:   # macro-block scales: direct-load tiles
                 name = "k_gemm_prefill<%s,MB>" % args.fmt

@@ -504,6 +504,20 @@ __device__ __forceinline__ uint32_t bf16_of_exact(double h, double l) {
   return (((uint32_t)(q + 133) << 7) + (uint32_t)r) | (neg << 15);
 }
 
+// The same from an FP32 pair: h = RN_fp32 of the exact value (or the value
+// itself), l the exact residual. A bf16 midpoint is an FP32 number, so h lies
+// on the exact value's side of every midpoint unless it is one; then l's sign
+// decides (none: ties to even).
+__device__ __forceinline__ uint32_t bf16_of_exact32(float h, float l) {
+  const uint32_t b = __float_as_uint(h);
+  if ((b & 0x7FFFFFFFu) == 0u) return 0u;             // exact zero: +0
+  const uint32_t neg = b >> 31, rem = b & 0xFFFFu;
+  uint32_t r = b >> 16;
+  const bool tie_up = l != 0.0f ? ((l < 0.0f) == (neg != 0u)) : (r & 1u) != 0u;
+  if (rem > 0x8000u || (rem == 0x8000u && tie_up)) r += 1u;
+  return r;
+}
+
 // Exact rotation output i of a block (bf16 bits in vals[0 .. B-1]) with
 // integer arithmetic: |x| = n * 2^-133 with n < 2^261, the signed sum in a
 // 320-bit two's complement integer (ten 32-bit words), multiplied by the
@@ -599,7 +613,47 @@ __device__ __forceinline__ void hadamard_block(uint4 (&v)[B / 8]) {
       }
     }
   uint32_t out[B / 2];
-  if (fmax - fmin <= 45 - kLog2B) {
+  // Three ways to the same result. FP32: every value is a multiple of the
+  // smallest one's quantum 2^(fmin-134) below 2^(fmax-126), so every partial
+  // sum of the transform is one below 2^(fmax-fmin+8+log2 B) quanta: exact in
+  // FP32 when that is at most 2^24, with no overflow (fmax <= 245); for
+  // B = 32 the product with c is split exactly into RN + FMA residual when
+  // no nonzero sum is below 2^-100 (fmin >= 34). Binary64: the same with 53
+  // bits, exact wherever FP32 is. Otherwise integers. A wave takes the FP32
+  // way only when all its lanes can (a wave runs every way any lane takes,
+  // and a binary64 block sits in most waves of 32-value blocks of normal
+  // data).
+  const bool f32_ok = fmax - fmin <= 16 - kLog2B && fmax <= 245 && (B == 16 || fmin >= 34);
+  if (__all(f32_ok)) {
+    float y[B];
+#pragma unroll
+    for (int j = 0; j < B / 2; ++j) {
+      y[2 * j] = __uint_as_float(w[j] << 16);
+      y[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+#pragma unroll
+    for (int span = 1; span < B; span *= 2)
+#pragma unroll
+      for (int i = 0; i < B; ++i)
+        if ((i & span) == 0) {
+          const float lo = y[i], hi = y[i + span];
+          y[i] = lo + hi;
+          y[i + span] = lo - hi;
+        }
+    uint32_t r[B];
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      if constexpr (B == 16) {
+        r[i] = bf16_of_exact32(y[i] * 0.25f, 0.0f);      // exact product
+      } else {
+        const float c = 0x1.6a09e6p-3f;                  // RN_fp32(1/sqrt(32))
+        const float hi = y[i] * c;
+        r[i] = bf16_of_exact32(hi, __builtin_fmaf(y[i], c, -hi));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < B / 2; ++j) out[j] = r[2 * j] | (r[2 * j + 1] << 16);
+  } else if (fmax - fmin <= 45 - kLog2B) {
     double y[B];
 #pragma unroll
     for (int j = 0; j < B / 2; ++j) {

@@ -101,13 +101,22 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) {
 }
 // The source address is a wave-uniform base (SGPR pair) plus a per-lane
 // 32-bit byte offset, which keeps the copy addresses out of vector registers.
+// The base is uniform by construction; it passes through readfirstlane so
+// that the compiler never hands the scalar operand a vector register (free
+// where the base already is scalar).
+__device__ __forceinline__ const uint8_t *sgpr_ptr(const uint8_t *p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return (const uint8_t *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 __device__ __forceinline__ void lds_copy16(const uint8_t *base, uint32_t off, uint32_t dst) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(off), "s"(base), "s"(dst) : "memory", "m0");
+               :: "v"(off), "s"(sgpr_ptr(base)), "s"(dst) : "memory", "m0");
 }
 __device__ __forceinline__ void lds_copy4(const uint8_t *base, uint32_t off, uint32_t dst) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
-               :: "v"(off), "s"(base), "s"(dst) : "memory", "m0");
+               :: "v"(off), "s"(sgpr_ptr(base)), "s"(dst) : "memory", "m0");
 }
 
 __device__ __forceinline__ v4f mma_mx(uint4 w, uint4 a, v4f c, uint32_t sw, uint32_t sa) {

@@ -535,8 +535,10 @@ void launch_small(const uint16_t *x, int64_t rows, int64_t k, int64_t rows_pad, 
     // Small tensors: every workgroup reads the whole tensor for its maximum
     // rather than exchanging it (measured per call: M = 1, K = 5120: 4.9 ->
     // 3.9 us; M = 8, K = 5120: 5.15 -> 4.8 us; at M * K = 139264 it lost,
-    // 5.2 -> 6.9 us, as each workgroup's reads grow).
-    if (rows * k <= kActRedundantMaxValues && per_wg <= kActGrid) FP4_QS(2, 1, kThreads);
+    // 5.2 -> 6.9 us, as each workgroup's reads grow). Not with the rotation:
+    // every workgroup would rotate the whole tensor.
+    if (rows * k <= kActRedundantMaxValues && per_wg <= kActGrid && !(recipe & kRecipeRotate))
+      FP4_QS(2, 1, kThreads);
     else if (per_wg <= kActGrid) FP4_QS(1, 1, kThreads);
     else {
       // past 256 blocks per workgroup, 512-thread workgroups before two

@@ -97,6 +97,45 @@ def test_rotated_wide_range_blocks(fmt, m, k):
         assert_canonical_equal(q, ref, F[fmt], what=f"rotated wide-range {m}x{k} layout {lay}")
 
 
+def _tier_boundary_rows(rows, k, block, seed):
+    """bf16 blocks around the rotation's FP32 / binary64 boundary: per block an
+    exponent spread of 10-13 fields (FP32 is exact up to 16 - log2(block)),
+    the smallest exponent field near 34 in half of them (the 32-value
+    rotation's FP32 product bound), significands rich in exact bf16 midpoints
+    after the transform, zeros and negative zeros."""
+    rng = np.random.default_rng(seed)
+    nb = k // block
+    spread = rng.integers(10, 14, (rows, nb, 1))
+    fmin = np.where(rng.random((rows, nb, 1)) < 0.5, rng.integers(33, 36, (rows, nb, 1)),
+                    rng.integers(60, 200, (rows, nb, 1)))
+    f = fmin + (rng.random((rows, nb, block)) * (spread + 1)).astype(np.int64)
+    f[:, :, 0] = fmin[:, :, 0]                    # the block's spread is attained
+    f[:, :, 1] = (fmin + spread)[:, :, 0]
+    m = np.where(rng.random((rows, nb, block)) < 0.5, rng.integers(0, 128, (rows, nb, block)),
+                 rng.choice([0, 0x40], (rows, nb, block)))
+    sign = rng.integers(0, 2, (rows, nb, block)) << 15
+    bits = (sign | (f << 7) | m).astype(np.uint16)
+    z = rng.random((rows, nb, block)) < 0.05
+    bits[z] = (sign[z]).astype(np.uint16)           # +0 and -0
+    return bits.reshape(rows, k)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m,k", [(8, 4096), (300, 2880)])
+def test_rotated_tier_boundary_blocks(fmt, m, k):
+    """Exact rotation across its FP32 / binary64 boundary: codes and scales
+    byte for byte the oracle's, in both layouts."""
+    print(f"[recipe-rot] tier-boundary fmt={fmt} m={m} k={k}", flush=True)
+    block = 16 if fmt == "nvfp4" else 32
+    bits = _tier_boundary_rows(m, k, block, 11 * m + k)
+    ref = _ref(fmt, bits, True, False)
+    for lay in (fp4.CANONICAL, fp4.TILED):
+        q = fp4.fp4_quantize_act(to_dev(bits), _flags(fmt, True, False), layout=lay)
+        if lay == fp4.TILED:
+            q = fp4.fp4_export_canonical(q)
+        assert_canonical_equal(q, ref, F[fmt], what=f"rotated tier-boundary {m}x{k} layout {lay}")
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("n,k", [(33, 96), (520, 2880)])
 def test_rotated_weight_cache(fmt, n, k):
