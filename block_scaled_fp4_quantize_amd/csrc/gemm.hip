@@ -745,7 +745,9 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_linear_decode(
     uint32_t recipe) {
   constexpr int NW = kDecWaves, FM = kDecFrags;
   constexpr int B = FMT == 0 ? 16 : 32, V = B / 8;
-  const bool rot = recipe & kRecipeRotate;
+  // (rotated and macro-block-scaled activations never come here: the host
+  // sends them to the separate quantizer, and leaving their code out keeps
+  // this kernel's registers low)
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ float red[NW][4][64];
   __shared__ uint32_t lmax[NW];
@@ -779,7 +781,6 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_linear_decode(
         const int r = t / nb, c = t - r * nb;
         const uint4 *src = (const uint4 *)(x + (int64_t)r * k + c * B);
         uint4 v[2] = {src[0], src[1]};
-        if (rot) hadamard_block<16>(v);
         amax = max(amax, max(absmax_bits8(v[0]), absmax_bits8(v[1])));
       }
       st = tensor_scale_from_amax(bf16_bits_to_f32(block_max_u32(amax, lmax)));
@@ -793,7 +794,6 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_linear_decode(
       const uint4 *src = (const uint4 *)(x + (int64_t)r * k + c * B);
 #pragma unroll
       for (int i = 0; i < V; ++i) v[i] = src[i];
-      if (rot) hadamard_block<B>(v);
     }
     if constexpr (FMT == 0) {
       uint4 *dst = (uint4 *)(smem + r * ap + c * 32);

@@ -162,13 +162,14 @@ __global__ __launch_bounds__(kThreads) void k_amax_parts_rot(const uint4 *__rest
 
 // Grid-stride over every block of the padded output; S_t (NVFP4) from the
 // static value or the fold of the partial maxima.
-template <int FMT, int TILED>
+template <int FMT, int TILED, int FULL>
 __global__ __launch_bounds__(kThreads) void k_quant(
     const uint16_t *__restrict__ x, int64_t rows, int64_t k, int64_t rows_pad, int64_t kt_n,
     const uint32_t *__restrict__ parts, int nparts, const float *__restrict__ static_scale,
     uint8_t *__restrict__ codes, int64_t cpitch, uint8_t *__restrict__ scales, int64_t spitch,
     float *__restrict__ ts_out, uint32_t recipe, float *__restrict__ macro, int64_t mpitch) {
   using K = Blk<FMT>;
+  if (!FULL) recipe &= kRecipeOas;  // the plain recipe: no rotation or MBS code
   __shared__ uint32_t lds[4];
   float st = 1.0f;
   if (FMT == 0) {
@@ -216,13 +217,14 @@ __global__ __launch_bounds__(kThreads) void k_quant(
 // owns in the fragment. Each lane reads 64 contiguous bytes of its row (a
 // wave covers 16 rows x 256 bytes, whole cache lines) and the wave writes its
 // fragment's 1 KB of codes and its scale bytes contiguously.
-template <int FMT>
+template <int FMT, int FULL>
 __global__ __launch_bounds__(kThreads) void k_quant_tiled(
     const uint16_t *__restrict__ x, int64_t rows, int64_t k, int64_t rows_pad, int64_t kt_n,
     const uint32_t *__restrict__ parts, int nparts, const float *__restrict__ static_scale,
     uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, float *__restrict__ ts_out,
     uint32_t recipe, float *__restrict__ macro) {
   using K = Blk<FMT>;
+  if (!FULL) recipe &= kRecipeOas;  // the plain recipe: no rotation or MBS code
   __shared__ uint32_t lds[4];
   float st = 1.0f;
   if (FMT == 0) {
@@ -335,7 +337,7 @@ __device__ __forceinline__ uint32_t tensor_absmax_wg(const uint16_t *x, int64_t 
 // workspace's sticky error word, and the tensor scale written for the call is
 // NaN: the last workgroup to finish writes S_t, and it knows from the arrival
 // count (which also counts the workgroups that gave up) whether any did.
-template <int FMT, int TILED, int DYN, int BPT, int NTH = kThreads>
+template <int FMT, int TILED, int DYN, int BPT, int NTH, int FULL>
 __global__ __launch_bounds__(NTH) void k_quant_small(
     const uint16_t *__restrict__ x, int64_t rows, int64_t k, int64_t rows_pad, int64_t kt_n,
     const float *__restrict__ static_scale, uint8_t *__restrict__ codes, int64_t cpitch,
@@ -343,6 +345,7 @@ __global__ __launch_bounds__(NTH) void k_quant_small(
     uint32_t *__restrict__ sync, uint32_t recipe, uint32_t spin_limit, float *__restrict__ macro,
     int64_t mpitch) {
   using K = Blk<FMT>;
+  if (!FULL) recipe &= kRecipeOas;  // the plain recipe: no rotation or MBS code
   __shared__ uint32_t lds[NTH / 64];
   const int64_t nb = k / K::B, nb_pad = kt_n * K::BPF, total = rows_pad * nb_pad;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -516,6 +519,9 @@ void launch_small(const uint16_t *x, int64_t rows, int64_t k, int64_t rows_pad, 
                   int64_t spitch, float *ts_out, uint32_t *sync, uint32_t recipe, float *macro,
                   int64_t mpitch, hipStream_t stream) {
   const uint32_t spin = g_spin_limit.load(std::memory_order_relaxed);
+  // the rotation and MBS code only in the kernels that need it: it holds
+  // registers whether or not it runs
+  const bool full = (recipe & (kRecipeRotate | kRecipeMbs)) != 0u;
   // One block per thread where the grid allows: encoding is the costly part
   // and spreads over as many CUs as there are blocks. The dynamic-scale form
   // also exchanges its maximum among the workgroups, so it stops at kActGrid
@@ -528,10 +534,11 @@ void launch_small(const uint16_t *x, int64_t rows, int64_t k, int64_t rows_pad, 
     // encode steps of unused ones still cost time (1 instead of 4 blocks per
     // thread: 0.4-0.6 us per call on the decode shapes)
     int grid = (int)(per_wg < kActGrid ? per_wg : kActGrid);
-#define FP4_QS(D, BPT, NTH)                                                                     \
-  hipLaunchKernelGGL((k_quant_small<FMT, TILED, D, BPT, NTH>), dim3(grid), dim3(NTH), 0, stream, \
-                     x, rows, k, rows_pad, kt_n, static_scale, codes, cpitch, scales, spitch,    \
+#define FP4_QS1(D, BPT, NTH, FU)                                                                    \
+  hipLaunchKernelGGL((k_quant_small<FMT, TILED, D, BPT, NTH, FU>), dim3(grid), dim3(NTH), 0, stream, \
+                     x, rows, k, rows_pad, kt_n, static_scale, codes, cpitch, scales, spitch,        \
                      ts_out, sync, recipe, spin, macro, mpitch)
+#define FP4_QS(D, BPT, NTH) do { if (full) FP4_QS1(D, BPT, NTH, 1); else FP4_QS1(D, BPT, NTH, 0); } while (0)
     // Small tensors: every workgroup reads the whole tensor for its maximum
     // rather than exchanging it (measured per call: M = 1, K = 5120: 4.9 ->
     // 3.9 us; M = 8, K = 5120: 5.15 -> 4.8 us; at M * K = 139264 it lost,
@@ -550,10 +557,15 @@ void launch_small(const uint16_t *x, int64_t rows, int64_t k, int64_t rows_pad, 
       else FP4_QS(1, 2, 2 * kThreads);
     }
 #undef FP4_QS
+#undef FP4_QS1
+  } else if (full) {
+    hipLaunchKernelGGL((k_quant_small<FMT, TILED, 0, 1, kThreads, 1>), dim3((unsigned)per_wg),
+                       dim3(kThreads), 0, stream, x, rows, k, rows_pad, kt_n, static_scale, codes,
+                       cpitch, scales, spitch, ts_out, sync, recipe, spin, macro, mpitch);
   } else {
-    hipLaunchKernelGGL((k_quant_small<FMT, TILED, 0, 1>), dim3((unsigned)per_wg), dim3(kThreads), 0,
-                       stream, x, rows, k, rows_pad, kt_n, static_scale, codes, cpitch, scales,
-                       spitch, ts_out, sync, recipe, spin, macro, mpitch);
+    hipLaunchKernelGGL((k_quant_small<FMT, TILED, 0, 1, kThreads, 0>), dim3((unsigned)per_wg),
+                       dim3(kThreads), 0, stream, x, rows, k, rows_pad, kt_n, static_scale, codes,
+                       cpitch, scales, spitch, ts_out, sync, recipe, spin, macro, mpitch);
   }
 }
 
@@ -562,18 +574,30 @@ void launch_large(const uint16_t *x, int64_t rows, int64_t k, int64_t rows_pad, 
                   const uint32_t *parts, int nparts, const float *static_scale, uint8_t *codes,
                   int64_t cpitch, uint8_t *scales, int64_t spitch, float *ts_out, uint32_t recipe,
                   float *macro, int64_t mpitch, hipStream_t stream) {
+  // the rotation and MBS code only in the kernels that need it: it holds
+  // registers (the MXFP4 tiled quantizer: 183 of them with it) whether or
+  // not it runs
+  const bool full = (recipe & (kRecipeRotate | kRecipeMbs)) != 0u;
   if (TILED) {  // one wave per fragment, four waves per workgroup, grid-stride
     const int64_t frags = (rows_pad >> 4) * kt_n;
     const int grid = (int)std::min<int64_t>((frags + 3) / 4, 8192);
-    hipLaunchKernelGGL((k_quant_tiled<FMT>), dim3(grid), dim3(kThreads), 0, stream, x, rows, k,
-                       rows_pad, kt_n, parts, nparts, static_scale, codes, scales, ts_out, recipe,
-                       macro);
+#define FP4_QT(FU)                                                                             \
+  hipLaunchKernelGGL((k_quant_tiled<FMT, FU>), dim3(grid), dim3(kThreads), 0, stream, x, rows, k, \
+                     rows_pad, kt_n, parts, nparts, static_scale, codes, scales, ts_out, recipe,   \
+                     macro)
+    if (full) FP4_QT(1);
+    else FP4_QT(0);
+#undef FP4_QT
     return;
   }
   const int grid = grid_for(rows_pad * kt_n * Blk<FMT>::BPF, 8192);
-  hipLaunchKernelGGL((k_quant<FMT, TILED>), dim3(grid), dim3(kThreads), 0, stream, x, rows, k,
-                     rows_pad, kt_n, parts, nparts, static_scale, codes, cpitch, scales, spitch,
-                     ts_out, recipe, macro, mpitch);
+#define FP4_QC(FU)                                                                                \
+  hipLaunchKernelGGL((k_quant<FMT, TILED, FU>), dim3(grid), dim3(kThreads), 0, stream, x, rows, k, \
+                     rows_pad, kt_n, parts, nparts, static_scale, codes, cpitch, scales, spitch,   \
+                     ts_out, recipe, macro, mpitch)
+  if (full) FP4_QC(1);
+  else FP4_QC(0);
+#undef FP4_QC
 }
 
 }  // namespace
