@@ -262,12 +262,14 @@ fp4_status fp4_linear_noalloc(const void *x_bf16, int64_t m, const fp4_tensor *w
 fp4_status fp4_linear_w4a16(const void *x_bf16, int64_t m, const fp4_tensor *w, void *y_bf16,
                             int64_t ldy, hipStream_t stream);
 
-/* Number of kernel launches fp4_linear makes for this shape: 1 when the
- * activation quantization is fused into the GEMM (small M * K on the skinny
- * path; M > 128 with a static NVFP4 scale, or MXFP4 without macro-block
- * scales, on the tile path), 2 for quantize + GEMM, 3 when the quantizer needs
- * a separate reduction launch (large NVFP4 activations with a dynamic scale).
- * 0 for invalid arguments. */
+/* Number of kernel launches fp4_linear makes for this shape under the
+ * current switches: 1 when the activation quantization is fused into the
+ * GEMM (small M * K on the skinny path without rotation or macro-block
+ * scales; with fp4_set_decode_linear_fusion(1), M <= 32 without either; with
+ * fp4_set_large_linear_fusion(1), M > 128 with a static NVFP4 scale or MXFP4
+ * without macro-block scales), 2 for quantize + GEMM, 3 when the quantizer
+ * needs a separate reduction launch (large NVFP4 activations with a dynamic
+ * scale). 0 for invalid arguments. */
 int32_t fp4_linear_launches(int32_t fmt, int64_t m, int64_t n, int64_t k, int32_t static_scale);
 
 /*
