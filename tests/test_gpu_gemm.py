@@ -461,3 +461,48 @@ def test_decode_single_launch_give_up_is_visible(fmt, decode_fusion):
     y2 = fp4.fp4_linear(x, wq, workspace=ws)
     assert_gemm_close(bf16_out_to_f64(y2), c_ref, l_ref, "after a give-up")
     assert fp4.fp4_workspace_flags(ws) == 0
+
+
+@pytest.mark.parametrize("fmt,m,n,k,switch", [("nvfp4", 32, 5120, 5120, "decode"),
+                                              ("mxfp4", 8, 5200, 5120, "decode"),
+                                              ("mxfp4", 4096, 4096, 1152, "large"),
+                                              ("nvfp4", 1024, 2048, 2048, "large")])
+def test_single_launch_graph_replay(fmt, m, n, k, switch):
+    """The single-launch linears (producer workgroups and ready counts reset by
+    the last consumer) captured in a HIP graph: every replay, with eager work
+    and synchronizations between them, equals the eager result bit for bit and
+    leaves the workspace flags clear."""
+    print(f"[graph-1launch] {switch} fmt={fmt} m={m} n={n} k={k}", flush=True)
+    setter = fp4.fp4_set_decode_linear_fusion if switch == "decode" else fp4.fp4_set_large_linear_fusion
+    prev = setter(True)
+    try:
+        st = (torch.tensor([1.25], dtype=torch.float32, device="cuda")
+              if (switch == "large" and fmt == "nvfp4") else None)
+        assert fp4.fp4_linear_launches(F[fmt], m, n, k, st is not None) == 1
+        a = synth.normal((m, k), 1.0, 61, m + k)
+        w = synth.normal((n, k), 0.02, 61, n + k)
+        wq = fp4.fp4_quantize_weight(to_dev(w), F[fmt])
+        x = to_dev(a)
+        ws = torch.zeros(fp4.fp4_linear_workspace_bytes(F[fmt], m, n, k), dtype=torch.uint8, device="cuda")
+        out = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+        eager = fp4.fp4_linear(x, wq, static_scale=st, out=torch.empty_like(out), workspace=ws).clone()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fp4.fp4_linear(x, wq, static_scale=st, out=out, workspace=ws)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fp4.fp4_linear(x, wq, static_scale=st, out=out, workspace=ws)
+        for rep in range(4):
+            out.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, eager), f"replay {rep} differs from eager"
+            other = fp4.fp4_linear(x, wq, static_scale=st, workspace=ws)   # eager, same workspace
+            torch.cuda.synchronize()
+            assert torch.equal(other, eager)
+        assert fp4.fp4_workspace_flags(ws) == 0
+    finally:
+        setter(prev)
