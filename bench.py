@@ -119,6 +119,62 @@ DOMINANT = ("k_gemm_decode", "k_linear_decode", "k_gemm_tile", "k_gemm_prefill",
             "k_w4a16_tile")
 
 
+SPEC_SCLK_MHZ = 2400.0             # MI355X peak engine clock, at which the peaks are quoted
+
+
+def sample_clocks(busy, seconds=1.5):
+    """Graphics and memory clocks (MHz) while `busy()` keeps the GPU working:
+    `amd-smi metric -c` polled from a child process for about `seconds`
+    (after every timing, so the polls perturb none). The graphics clock is
+    averaged over the XCDs of each sample. None when amd-smi is missing or
+    prints no clock."""
+    import re
+    import shutil
+    import subprocess
+    import threading
+    exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    if not os.path.exists(exe):
+        return None
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                out = subprocess.run([exe, "metric", "-c"], capture_output=True, text=True,
+                                     timeout=20).stdout
+            except Exception:
+                return
+            sec, gfx, mem = None, [], []
+            for line in out.splitlines():
+                t = line.strip()
+                m = re.match(r"(GFX|MEM)_\d+:", t)
+                if m:
+                    sec = m.group(1)
+                    continue
+                m = re.match(r"CLK:\s*(\d+)\s*MHz", t)
+                if m and sec:
+                    (gfx if sec == "GFX" else mem).append(int(m.group(1)))
+                    sec = None
+            if gfx:
+                samples.append((sum(gfx) / len(gfx), max(mem) if mem else None))
+
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end or (not samples and time.perf_counter() < t_end + 20):
+        busy()
+    stop.set()
+    th.join(timeout=30)
+    if not samples:
+        return None
+    g = sorted(x[0] for x in samples)
+    mem = [x[1] for x in samples if x[1] is not None]
+    return {"sclk_median": round(g[len(g) // 2]), "sclk_min": round(g[0]), "sclk_max": round(g[-1]),
+            "mclk": max(mem) if mem else None, "samples": len(samples),
+            "how": "amd-smi polled while the same steps replay for ~%.1f s after the timed region"
+                   % seconds}
+
+
 def kernel_source_hash():
     """Hash of the HIP sources: stored counter figures apply only to the build
     they were taken from."""
@@ -586,6 +642,15 @@ def main():
             # exact NVFP4 products (q * s_b: up to 6 significant bits) run on the
             # f16 matrix instructions, whose dense peak bounds this kernel
             roof["f16_ceiling"] = {"peak": F16_PEAK_TFLOPS, "frac": round(achieved / F16_PEAK_TFLOPS, 4)}
+    # the clocks the steps run at (a separate pass after every timing): the
+    # matrix peaks are quoted at 2.4 GHz, and sustained matrix work runs lower
+    def busy():
+        run_steps(G if use_graph else 1)
+        torch.cuda.synchronize()
+    clocks = sample_clocks(busy)
+    if clocks and roof["bound"] == "mfma":
+        roof["frac_at_measured_sclk"] = round(
+            roof["achieved"] / (roof["peak"] * clocks["sclk_median"] / SPEC_SCLK_MHZ), 4)
     # HBM bytes per launch from the committed counter summary of this variant
     roof["traffic"] = stored_traffic(args.workload, args.fmt, variant_tag(args))
     # rocprofv3 MfmaUtil / VALUBusy / LdsUtil (percent) of the same kernels
@@ -604,7 +669,8 @@ def main():
               "launch": ("hip-graph replay, %d steps per graph" % G) if use_graph else "eager",
               "weight_copies": {f"{k}x{n}": copies[(k, n)] for (k, n) in shapes},
               "calls_per_step": len(configs),
-              "fraction_of_fp4_peak": round(tflops / FP4_PEAK_TFLOPS, 6)}
+              "fraction_of_fp4_peak": round(tflops / FP4_PEAK_TFLOPS, 6),
+              "clocks_mhz": clocks}
     if args.workload.startswith("square") or args.workload == "prefill":
         # the sweep's two timings: GEMM alone on pre-quantized activations, and
         # quantization + GEMM (the value)
