@@ -1037,12 +1037,16 @@ bool linear_fused_ok(int fmt, int64_t m, int64_t n, int64_t k) {
   // LDS staging bound, and a bound on the redundant quantization work that
   // every weight tile's workgroup repeats.
   // NVFP4's encoding prologue (maximum pass + exact encode) is long enough
-  // that only about two workgroups per CU (512 weight tiles) should repeat it,
-  // and the separate quantizer plus the skinny GEMM wins once M * K_pad * tiles
-  // passes about 4M (320 tiles, measured: K = 5120 fused at M = 2, 11.9 us
-  // against 13.5; separate at M = 4, 13.4 us against 15.5, and at M = 1 with
-  // K = 17408, 22.4 us against 23.0).
+  // that with two or more rows only about two workgroups per CU (512 weight
+  // tiles) should repeat it, and the separate quantizer plus the skinny GEMM
+  // wins once M * K_pad * tiles passes about 4M (320 tiles, K = 5120,
+  // measured: fused at M = 2, 11.9 us against 13.5; separate at M = 4, 12.3
+  // us against 14.7). A single row's prologue is short enough for twice that
+  // work and any tile count (K = 5120, N = 17408: fused 19.0 us against 20.0;
+  // K = 17408, N = 5120: 20.8 against 21.1; at M = 2, N = 17408 the separate
+  // quantizer wins, 20.4 against 22.9).
   const int64_t nt = round_up(n, 16) / 16;
+  if (fmt == 0 && m == 1) return mk <= kFusedMaxMK / 2 && mk * nt <= 2 * kFusedMaxWorkNv;
   if (fmt == 0)
     return m <= kFusedMaxM && mk <= kFusedMaxMK / 2 && mk * nt <= kFusedMaxWorkNv &&
            nt <= kFusedMaxTilesNv;

@@ -124,13 +124,16 @@ def test_host_validation_rejects_before_launch():
 
 def test_linear_launch_count():
     L = fp4.lib()
-    # M = 1 decode shapes run as one fused launch, except NVFP4 where the
-    # per-workgroup encode would repeat too often: more than 512 weight tiles
-    # (N = 17408), or M * K_pad * tiles above 4M (K = 17408, N = 5120)
+    # M = 1 decode shapes run as one fused launch (NVFP4: M * K_pad * tiles up
+    # to 8M for one row; up to 4M and at most 512 weight tiles for more rows,
+    # where the per-workgroup encode would otherwise repeat too often)
     for k, n in ((5120, 5120), (5120, 17408), (17408, 5120)):
-        assert L.fp4_linear_launches(fp4.NVFP4, 1, n, k, 0) == (1 if k == n else 2)
+        assert L.fp4_linear_launches(fp4.NVFP4, 1, n, k, 0) == 1
         assert L.fp4_linear_launches(fp4.MXFP4, 1, n, k, 0) == 1
+    assert L.fp4_linear_launches(fp4.NVFP4, 1, 8192, 16384, 0) == 1
+    assert L.fp4_linear_launches(fp4.NVFP4, 1, 8208, 16384, 0) == 2
     assert L.fp4_linear_launches(fp4.NVFP4, 2, 5120, 5120, 0) == 1
+    assert L.fp4_linear_launches(fp4.NVFP4, 2, 17408, 5120, 0) == 2
     assert L.fp4_linear_launches(fp4.NVFP4, 4, 5120, 5120, 0) == 2
     # larger activations: quantize + GEMM (NVFP4 dynamic may need a reduction launch)
     assert L.fp4_linear_launches(fp4.NVFP4, 32, 5120, 5120, 0) == 2

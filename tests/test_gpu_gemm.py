@@ -272,11 +272,13 @@ def no_decode_fusion():
 
 
 @pytest.mark.parametrize("m,k,n,launches", [(2, 5120, 5120, 1), (3, 5120, 5120, 2),
-                                            (1, 16384, 4096, 1), (1, 16384, 4112, 2)])
+                                            (2, 8192, 4096, 1), (2, 8192, 4112, 2),
+                                            (1, 16384, 8192, 1), (1, 16384, 8208, 2)])
 def test_nvfp4_fused_bound(m, k, n, launches, no_decode_fusion):
     """NVFP4 fp4_linear on both sides of the fused path's M * K_pad * tiles
-    bound (4M), with the producer form of the skinny linear switched off: the
-    fused single launch and quantize + GEMM agree with the oracle alike."""
+    bounds (4M for two or more rows, 8M for one), with the producer form of
+    the skinny linear switched off: the fused single launch and quantize +
+    GEMM agree with the oracle alike."""
     assert fp4.fp4_linear_launches("nvfp4", m, n, k) == launches
     a = synth.normal((m, k), 1.0, 11, m * 7 + k)
     w = synth.normal((n, k), 0.02, 11, n * 5 + k)
@@ -377,7 +379,8 @@ def test_zero_activations_give_zero_output(fmt, m, k, n):
 _DEC1_CASES = [(12, 5200, 5120), (8, 1040, 17408), (19, 1000, 4160), (32, 5120, 5120),
                (17, 8200, 512),      # two weight tiles per workgroup
                (16, 4112, 4224),     # NVFP4: 16-wave workgroups with two tiles
-               (1, 8200, 640),       # NVFP4: >= 512 tiles, one row
+               (1, 8200, 640),       # one row, 513 tiles (NVFP4: the fused skinny linear)
+               (1, 8208, 16384),     # NVFP4: one row past the fused bound, >= 512 tiles
                (32, 48, 128),        # fewer K fragments than waves
                (32, 48, 65536)]      # 1024 fragments: 128 producers, the most
 
