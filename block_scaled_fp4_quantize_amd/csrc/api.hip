@@ -553,7 +553,9 @@ int32_t fp4_linear_launches(int32_t fmt, int64_t m, int64_t n, int64_t k, int32_
   if (use_fused(fmt, m, n, k)) return 1;
   if (linear_fused_decode_ok(base, recipe_of(fmt), m, n, k)) return 1;
   if (linear_fused_large_ok(base, recipe_of(fmt), m, n, k, static_scale != 0)) return 1;
-  if (base == FP4_NVFP4 && !static_scale && !quant_fits_small(base, m, k, 1)) return 3;
+  if (base == FP4_NVFP4 && !static_scale && !quant_fits_small(base, m, k, 1) &&
+      !quant_fits_mid(base, recipe_of(fmt), m, k, 1))
+    return 3;
   return 2;
 }
 

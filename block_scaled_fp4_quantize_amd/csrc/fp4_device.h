@@ -339,10 +339,15 @@ __device__ __forceinline__ uint32_t nv_encode8_fast(uint32_t sbyte, float st, fl
     // exact path's per-value work is not hoisted into the common path.
     asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
     const float hsv = 0.5f * e4m3_to_f32(sbyte);
-    const uint32_t up = nv_resolve_pair<0>(lo, hi, v.x, hsv, st) |
-                        nv_resolve_pair<1>(lo, hi, v.y, hsv, st) |
-                        nv_resolve_pair<2>(lo, hi, v.z, hsv, st) |
-                        nv_resolve_pair<3>(lo, hi, v.w, hsv, st);
+    // only the code bytes whose ends differ: a wave runs a pair's comparisons
+    // when any of its lanes needs them, which for one pair of values is far
+    // rarer than for the whole group of eight
+    const uint32_t diff = lo ^ hi;
+    uint32_t up = 0;
+    if (diff & 0x000000FFu) up |= nv_resolve_pair<0>(lo, hi, v.x, hsv, st);
+    if (diff & 0x0000FF00u) up |= nv_resolve_pair<1>(lo, hi, v.y, hsv, st);
+    if (diff & 0x00FF0000u) up |= nv_resolve_pair<2>(lo, hi, v.z, hsv, st);
+    if (diff & 0xFF000000u) up |= nv_resolve_pair<3>(lo, hi, v.w, hsv, st);
     lo = (lo & ~up) | (hi & up);
   }
   return lo;

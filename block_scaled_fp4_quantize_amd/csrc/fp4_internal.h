@@ -33,7 +33,15 @@ constexpr int kArriveWord = kErrWord + kSlotStride;
 // for each row panel of output tiles, reset by the panel's last consumer.
 constexpr int kPanelWords = kArriveWord + kSlotStride;
 constexpr int kMaxPanels = 1024;
-constexpr size_t kQuantScratchBytes = (size_t)(kPanelWords + 2 * kMaxPanels) * sizeof(uint32_t);
+// The one-pass quantizer of mid-size NVFP4 tensors (dynamic scale, tiled
+// layout): at most kMidGrid workgroups of kMidThreads threads, each wave
+// holding up to kMidFragsPerWave fragments, exchange their maxima through
+// kMidGrid tagged words of their own (one 128-byte line each).
+constexpr int kMidGrid = 256;
+constexpr int kMidThreads = 1024;
+constexpr int kMidFragsPerWave = 4;
+constexpr int kMidSlotWord = kPanelWords + 2 * kMaxPanels;
+constexpr size_t kQuantScratchBytes = (size_t)(kMidSlotWord + kMidGrid * kSlotStride) * sizeof(uint32_t);
 // Error flag: a workgroup of the maximum exchange gave up waiting.
 constexpr uint32_t kErrExchangeTimeout = 1u;
 constexpr uint32_t kDefaultSpinLimit = 1u << 22;
@@ -45,6 +53,9 @@ uint32_t set_exchange_spin_limit(uint32_t polls);
 int amax_parts(int64_t n);
 // Whether a [rows, k] tensor takes the single-launch path.
 bool quant_fits_small(int fmt, int64_t rows, int64_t k, int tiled);
+// Whether NVFP4 with the dynamic scale (recipe bits in `recipe`) takes the
+// one-pass mid-size path (one launch instead of maxima + encode).
+bool quant_fits_mid(int fmt, uint32_t recipe, int64_t rows, int64_t k, int tiled);
 
 // ---- launchers (all asynchronous on `stream`) ----
 

@@ -429,6 +429,77 @@ __global__ __launch_bounds__(NTH) void k_quant_small(
   }
 }
 
+// One-pass NVFP4 quantization with the dynamic tensor scale of a mid-size
+// tensor into the tiled layout: past the single-launch quantizer's capacity
+// but small enough for the registers of kMidGrid resident workgroups. Wave w
+// takes fragments w, w + W, ... (W waves in the grid; at most FPW of them),
+// one fragment per wave step as in k_quant_tiled, and loads all of them
+// before anything else; the workgroups then exchange their maxima through
+// their own tagged words and encode from the registers, so the tensor is read
+// from memory once instead of twice. A workgroup that gives up waiting
+// behaves as in k_quant_small (NaN tensor scale, sticky error flag).
+template <int FPW>
+__global__ __launch_bounds__(kMidThreads) void k_quant_tiled_x(
+    const uint16_t *__restrict__ x, int64_t rows, int64_t k, int64_t rows_pad, int64_t kt_n,
+    uint8_t *__restrict__ codes, uint8_t *__restrict__ scales, float *__restrict__ ts_out,
+    uint32_t *__restrict__ sync, uint32_t spin_limit) {
+  __shared__ uint32_t lds[kMidThreads / 64];
+  uint32_t *slots = sync + (kMidSlotWord - kMaxAmaxParts);
+  // this call's tag: one more than the previous call's (any slot)
+  const uint32_t tag = ((__hip_atomic_load(&slots[blockIdx.x * kSlotStride], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT) >> 16) + 1u) & 0xFFFFu;
+  const int lane = threadIdx.x & 63, r = lane & 15, c = lane >> 4;
+  const int64_t frags = (rows_pad >> 4) * kt_n;
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  const int64_t w0 = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  uint4 v[FPW][4];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < FPW; ++i) {
+    const int64_t f = w0 + i * waves;
+    const int64_t row = (f / kt_n) * 16 + r, k0 = (f % kt_n) * kFragK + 32 * c;
+    const bool live = f < frags && row < rows;
+    const uint4 *src = (const uint4 *)(x + row * k + k0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)  // values k0 + 8j .. k0 + 8j + 7 (blocks never straddle k)
+      v[i][j] = (live && k0 + 8 * j < k) ? src[j] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = max(m, absmax_bits8(v[i][j]));
+  }
+  const uint32_t g = group_max_u32<kMidGrid, kSlotStride>(block_max_u32(m, lds), tag, slots,
+                                                          blockIdx.x, gridDim.x, spin_limit, lds);
+  const bool gave_up = g >= 0x8000u;
+  const float st = gave_up ? __builtin_nanf("") : tensor_scale_from_amax(bf16_bits_to_f32(g));
+  uint32_t arrived_before = 0;
+  if (threadIdx.x == 0) {
+    if (gave_up)
+      __hip_atomic_fetch_or(&sync[kErrWord - kMaxAmaxParts], kErrExchangeTimeout,
+                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    arrived_before = __hip_atomic_fetch_add(&sync[kArriveWord - kMaxAmaxParts],
+                                            gave_up ? 0x10001u : 1u, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+  }
+#pragma unroll
+  for (int i = 0; i < FPW; ++i) {
+    const int64_t f = w0 + i * waves;
+    if (f >= frags) break;
+    const int64_t row = (f / kt_n) * 16 + r, k0 = (f % kt_n) * kFragK + 32 * c;
+    uint2 c0 = make_uint2(0u, 0u), c1 = make_uint2(0u, 0u);
+    uint32_t s0 = 0, s1 = 0;
+    if (row < rows && k0 < k) nv_encode_block(v[i][0], v[i][1], st, c0, s0);
+    if (row < rows && k0 + 16 < k) nv_encode_block(v[i][2], v[i][3], st, c1, s1);
+    *(uint16_t *)(scales + f * 128 + lane * 2) = (uint16_t)(s0 | (s1 << 8));
+    *(uint4 *)(codes + f * kFragCodeBytes + lane * 16) = make_uint4(c0.x, c0.y, c1.x, c1.y);
+  }
+  if (threadIdx.x == 0 && (arrived_before & 0xFFFFu) == gridDim.x - 1) {
+    // the last workgroup: every other one has taken its decision
+    const bool any_gave_up = gave_up || (arrived_before >> 16) != 0u;
+    if (ts_out) *ts_out = any_gave_up ? __builtin_nanf("") : st;
+    __hip_atomic_store(&sync[kArriveWord - kMaxAmaxParts], 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // --------------------------------------------------------------- test aids
 
 // Tiled -> canonical copy (one thread per block of the padded canonical row).
@@ -633,6 +704,15 @@ int amax_parts(int64_t n) {
   return (int)p;
 }
 
+static_assert(kMidFragsPerWave == 4, "the mid-size quantizer has instances for 1, 2 and 4 fragments per wave");
+
+bool quant_fits_mid(int fmt, uint32_t recipe, int64_t rows, int64_t k, int tiled) {
+  if (fmt != 0 || !tiled || (recipe & kRecipeRotate) || quant_fits_small(fmt, rows, k, tiled))
+    return false;
+  const int64_t frags = round_up(rows, 16) / 16 * (k_pad(k) / kFragK);
+  return frags <= (int64_t)kMidGrid * (kMidThreads / 64) * kMidFragsPerWave;
+}
+
 bool quant_fits_small(int fmt, int64_t rows, int64_t k, int tiled) {
   const int64_t rows_pad = tiled ? round_up(rows, 16) : rows;
   const int64_t blocks = rows_pad * (k_pad(k) / block_of(fmt));
@@ -654,6 +734,22 @@ hipError_t launch_quantize(int fmt, uint32_t recipe, int tiled, const uint16_t *
     else if (!tiled) FP4_QS(1, 0);
     else FP4_QS(1, 1);
 #undef FP4_QS
+    return hipGetLastError();
+  }
+  if (!static_scale && quant_fits_mid(fmt, recipe, rows, k, tiled)) {
+    // as few fragments per wave and workgroups as hold the tensor
+    const int64_t frags = (rows_pad >> 4) * kt_n, per_fpw = (int64_t)kMidGrid * (kMidThreads / 64);
+    const int fpw = frags <= per_fpw ? 1 : frags <= 2 * per_fpw ? 2 : 4;
+    const int grid = (int)((frags + fpw * (kMidThreads / 64) - 1) / (fpw * (kMidThreads / 64)));
+    uint32_t *sync = scratch + kMaxAmaxParts;
+    const uint32_t spin = exchange_spin_limit();
+#define FP4_QX(F)                                                                                  \
+  hipLaunchKernelGGL(k_quant_tiled_x<F>, dim3(grid), dim3(kMidThreads), 0, stream, x, rows, k,      \
+                     rows_pad, kt_n, codes, scales, ts_out, sync, spin)
+    if (fpw == 1) FP4_QX(1);
+    else if (fpw == 2) FP4_QX(2);
+    else FP4_QX(4);
+#undef FP4_QX
     return hipGetLastError();
   }
   int nparts = 0;

@@ -268,8 +268,9 @@ fp4_status fp4_linear_w4a16(const void *x_bf16, int64_t m, const fp4_tensor *w, 
  * scales; with fp4_set_decode_linear_fusion(1), M <= 32 without either; with
  * fp4_set_large_linear_fusion(1), M > 128 with a static NVFP4 scale or MXFP4
  * without macro-block scales), 2 for quantize + GEMM, 3 when the quantizer
- * needs a separate reduction launch (large NVFP4 activations with a dynamic
- * scale). 0 for invalid arguments. */
+ * needs a separate reduction launch (NVFP4 activations with a dynamic scale
+ * past 16384 fragments of 16 x 128 values, or rotated and past the
+ * single-launch quantizer's size). 0 for invalid arguments. */
 int32_t fp4_linear_launches(int32_t fmt, int64_t m, int64_t n, int64_t k, int32_t static_scale);
 
 /*

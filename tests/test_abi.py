@@ -135,9 +135,14 @@ def test_linear_launch_count():
     assert L.fp4_linear_launches(fp4.NVFP4, 2, 5120, 5120, 0) == 1
     assert L.fp4_linear_launches(fp4.NVFP4, 2, 17408, 5120, 0) == 2
     assert L.fp4_linear_launches(fp4.NVFP4, 4, 5120, 5120, 0) == 2
-    # larger activations: quantize + GEMM (NVFP4 dynamic may need a reduction launch)
+    # larger activations: quantize + GEMM (NVFP4 dynamic past 16384 fragments,
+    # or rotated past the single-launch size, needs a reduction launch)
     assert L.fp4_linear_launches(fp4.NVFP4, 32, 5120, 5120, 0) == 2
-    assert L.fp4_linear_launches(fp4.NVFP4, 4096, 3072, 3072, 0) == 3
+    assert L.fp4_linear_launches(fp4.NVFP4, 4096, 3072, 3072, 0) == 2
+    assert L.fp4_linear_launches(fp4.NVFP4, 4096, 3072, 8192, 0) == 2
+    assert L.fp4_linear_launches(fp4.NVFP4, 4112, 3072, 8192, 0) == 3
+    assert L.fp4_linear_launches(fp4.NVFP4 | fp4.ROTATE, 4096, 3072, 3072, 0) == 3
+    assert L.fp4_linear_launches(fp4.NVFP4, 16384, 16384, 16384, 0) == 3
     # 1-32 rows with producer workgroups inside the skinny GEMM's launch, once
     # switched on; rotated and macro-block-scaled activations excepted
     prev = L.fp4_set_decode_linear_fusion(1)
@@ -168,7 +173,8 @@ def test_linear_launch_count():
         assert L.fp4_linear_launches(fp4.NVFP4, 4096, 3072, 3072, 1) == 1
         assert L.fp4_linear_launches(fp4.MXFP4, 4096, 3072, 3072, 0) == 1
         assert L.fp4_linear_launches(fp4.MXFP4 | fp4.MX_MBS, 4096, 3072, 3072, 0) == 2
-        assert L.fp4_linear_launches(fp4.NVFP4, 4096, 3072, 3072, 0) == 3
+        assert L.fp4_linear_launches(fp4.NVFP4, 4096, 3072, 3072, 0) == 2
+        assert L.fp4_linear_launches(fp4.NVFP4, 8192, 3072, 8192, 0) == 3
     finally:
         assert L.fp4_set_large_linear_fusion(prev) == 1
     assert L.fp4_linear_launches(fp4.NVFP4, 4, 64, 40, 0) == 0

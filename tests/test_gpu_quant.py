@@ -154,11 +154,65 @@ def test_single_launch_limit(fmt):
         _act_case(fmt, bits, f"limit m={m}")
 
 
+@pytest.mark.parametrize("m,k,launches", [(300, 8192, 2), (1000, 3008, 2), (4096, 3072, 2), (4100, 4000, 2),
+                                          (4096, 8192, 2), (4112, 8192, 3)])
+def test_mid_size_one_pass(m, k, launches):
+    """NVFP4 activations with the dynamic scale past the single-launch
+    quantizer's size, into the tiled layout: up to 16384 fragments in one pass
+    (each wave holding 1, 2 or 4 fragments while the workgroups exchange their
+    maxima), past that the two-pass path; ragged rows and K included. Codes,
+    scales and S_t byte-identical to the oracle."""
+    print(f"[quant-mid] m={m} k={k}", flush=True)
+    assert fp4.fp4_linear_launches(fp4.NVFP4, m, 64, k) == launches
+    bits = synth.normal((m, k), 1.0, 17, m * 3 + k)
+    ref = oracle.quantize(0, bits)
+    q = fp4.fp4_quantize_act(to_dev(bits), 0, layout=fp4.TILED)
+    assert_canonical_equal(fp4.fp4_export_canonical(q), ref, 0, what=f"mid-size tiled {m}x{k}")
+
+
+def test_mid_size_give_up_is_visible():
+    """The one-pass mid-size quantizer's exchange gives up visibly, as the
+    single-launch one does (forced from the host with a wait of zero polls):
+    NaN tensor scale and linear outputs, the sticky flag set until cleared;
+    the same workspaces then give the oracle's results."""
+    m, k, n = 4096, 3072, 64
+    print(f"[quant-mid] give-up m={m} k={k}", flush=True)
+    a = synth.normal((m, k), 1.0, 22, 5)
+    w = synth.normal((n, k), 0.02, 22, 6)
+    assert fp4.fp4_linear_launches(fp4.NVFP4, m, n, k) == 2
+    wq = fp4.fp4_quantize_weight(to_dev(w), fp4.NVFP4)
+    x = to_dev(a)
+    ws_q = torch.zeros(fp4.lib().fp4_quantize_workspace_bytes(fp4.NVFP4, m, k), dtype=torch.uint8,
+                       device="cuda")
+    ws_l = torch.zeros(fp4.fp4_linear_workspace_bytes(fp4.NVFP4, m, n, k), dtype=torch.uint8,
+                       device="cuda")
+    prev = fp4.fp4_set_exchange_spin_limit(0)
+    try:
+        q = fp4.fp4_quantize_act(x, fp4.NVFP4, layout=fp4.TILED, workspace=ws_q)
+        y = fp4.fp4_linear(x, wq, workspace=ws_l)
+        torch.cuda.synchronize()
+    finally:
+        fp4.fp4_set_exchange_spin_limit(prev)
+    assert np.isnan(q.tensor_scale.cpu().item())
+    assert torch.isnan(y.float()).all()
+    assert fp4.fp4_workspace_flags(ws_q, clear=True) == fp4.WS_EXCHANGE_TIMEOUT
+    assert fp4.fp4_workspace_flags(ws_l, clear=True) == fp4.WS_EXCHANGE_TIMEOUT
+    ref = oracle.quantize(oracle.NVFP4, a)
+    q2 = fp4.fp4_quantize_act(x, fp4.NVFP4, layout=fp4.TILED, workspace=ws_q)
+    assert_canonical_equal(fp4.fp4_export_canonical(q2), ref, oracle.NVFP4, what="mid-size after a give-up")
+    c_ref, l_ref = oracle.gemm(ref, oracle.quantize(oracle.NVFP4, w))
+    y2 = fp4.fp4_linear(x, wq, workspace=ws_l).float().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(y2 - c_ref) <= oracle.gemm_tolerance(c_ref, l_ref))
+    assert fp4.fp4_workspace_flags(ws_q) == 0 and fp4.fp4_workspace_flags(ws_l) == 0
+
+
 def test_workspace_shared_across_calls():
     """One zero-filled workspace serves a sequence of dynamic NVFP4 calls of
-    different shapes and both code paths (the max-exchange words recycle)."""
+    different shapes and every code path (single launch, one-pass mid-size
+    in the tiled layout, two passes): the max-exchange words recycle."""
     ws = torch.zeros(fp4.lib().fp4_quantize_workspace_bytes(0, 1, 16), dtype=torch.uint8, device="cuda")
-    shapes = [(1, 5120), (32, 17408), (4, 64), (96, 32768), (8, 256), (1, 16), (300, 2880)]
+    shapes = [(1, 5120), (32, 17408), (4, 64), (96, 32768), (8, 256), (1, 16), (300, 2880), (1000, 3008),
+              (2, 96)]
     for rep in range(2):
         for i, (m, k) in enumerate(shapes):
             bits = synth.normal((m, k), 0.5 + i, 16, rep * 100 + i)
