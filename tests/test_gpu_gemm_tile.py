@@ -58,6 +58,43 @@ def test_tile_configs(fmt, m, n, k):
     _tiled_case(fmt, a, w, f"tile cfg {tile_config(m, n)}")
 
 
+@pytest.mark.parametrize("m,n,k", [
+    (8200, 4104, 1024),     # 33 x 17 tiles of 256 x 256, ragged M and N
+    (2056, 40960, 512),     # 9 x 160 tiles: several per CU
+])
+def test_mxfp4_tiles_closed_form(m, n, k):
+    """Every output of a large MXFP4 tile GEMM against a closed form: A row
+    i = 2^(i mod 7 - 3), W row j = 2^(j mod 5 - 2) quantize exactly (each
+    block is one power of two: code 4, E8M0 2^(p - 2)), so C[i, j] =
+    K * 2^(i mod 7 - 3 + j mod 5 - 2) exactly; a tile written to the wrong
+    place, a row or column shifted or a K step dropped changes outputs.
+    Eager and over graph replays."""
+    print(f"[tile-closed] m={m} n={n} k={k}", flush=True)
+    ea = (torch.arange(m, device="cuda") % 7 - 3).float()
+    ew = (torch.arange(n, device="cuda") % 5 - 2).float()
+    x = torch.pow(2.0, ea).unsqueeze(1).expand(m, k).to(torch.bfloat16).contiguous()
+    w = torch.pow(2.0, ew).unsqueeze(1).expand(n, k).to(torch.bfloat16).contiguous()
+    want = (float(k) * torch.pow(2.0, ea.unsqueeze(1) + ew.unsqueeze(0))).to(torch.bfloat16)
+    wq = fp4.fp4_quantize_weight(w, fp4.MXFP4)
+    qa = fp4.fp4_quantize_act(x, fp4.MXFP4, layout=fp4.TILED)
+    out = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    fp4.fp4_gemm(qa, wq, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, want), f"{(out != want).sum().item()} outputs differ"
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            fp4.fp4_gemm(qa, wq, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(2):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), f"replay {rep}: {(out != want).sum().item()} outputs differ"
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 def test_tile_outliers_and_zero_rows(fmt):
     """Planted +-3616 outliers and whole zero rows/blocks in A and W."""
