@@ -170,6 +170,42 @@ def test_mid_size_one_pass(m, k, launches):
     assert_canonical_equal(fp4.fp4_export_canonical(q), ref, 0, what=f"mid-size tiled {m}x{k}")
 
 
+def _sweep_shapes():
+    """Seeded (rows, K) pairs on both sides of the quantizer's path bounds:
+    the single-launch size (2^17 blocks), the one-pass mid-size bound (16384
+    fragments of 16 x 128) and the two-pass path, with ragged rows and K."""
+    g = np.random.default_rng(20261203)
+    shapes = []
+    for lo, hi in ((1, 64), (64, 600), (600, 3000), (3000, 9000)):
+        for _ in range(3):
+            rows = int(g.integers(lo, hi))
+            k = int(g.integers(1, 8192 // 32 + 1)) * 32 if rows < 3000 else int(g.integers(1, 64)) * 32
+            shapes.append((rows, k))
+    return shapes
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m,k", _sweep_shapes())
+def test_seeded_shape_sweep(fmt, m, k):
+    """Codes, scales and S_t byte-identical to the oracle in both layouts,
+    on seeded shapes spread over every quantizer path; NVFP4 also with a
+    static scale."""
+    print(f"[quant-sweep] fmt={fmt} m={m} k={k}", flush=True)
+    f = F[fmt]
+    bits = synth.student_t((m, k), 3.0, 1.5, 27, m * 11 + k)
+    ref = oracle.quantize(f, bits)
+    q = fp4.fp4_quantize_act(to_dev(bits), f)
+    assert_canonical_equal(q, ref, f, what=f"sweep canonical {m}x{k}")
+    qt = fp4.fp4_quantize_act(to_dev(bits), f, layout=fp4.TILED)
+    assert_canonical_equal(fp4.fp4_export_canonical(qt), ref, f, what=f"sweep tiled {m}x{k}")
+    if fmt == "nvfp4":
+        st = float(np.float32(0.37))
+        ref_s = oracle.quantize(f, bits, mode=oracle.STATIC, static_scale=st)
+        qs = fp4.fp4_quantize_act(to_dev(bits), f, layout=fp4.TILED,
+                                  static_scale=torch.tensor([st], dtype=torch.float32, device="cuda"))
+        assert_canonical_equal(fp4.fp4_export_canonical(qs), ref_s, f, what=f"sweep static {m}x{k}")
+
+
 def test_mid_size_give_up_is_visible():
     """The one-pass mid-size quantizer's exchange gives up visibly, as the
     single-launch one does (forced from the host with a wait of zero polls):
