@@ -262,6 +262,31 @@ def test_forward_layer_sampled(fmt, m):
         assert_gemm_close(y[rows, cols], c_ref, l_ref, f"forward {name} m={m}")
 
 
+def _linear_sweep_shapes():
+    """Seeded (M, N, K) on every GEMM path: the fused skinny linear (small
+    M * K), the skinny GEMM with 1, 2, 4 and 8 row groups, the 128 x 128 and
+    256 x 256 tiles; ragged M, N and K (K a multiple of 32)."""
+    g = np.random.default_rng(20261204)
+    shapes = []
+    for lo, hi in ((1, 17), (17, 33), (33, 129), (129, 700), (700, 1400)):
+        for _ in range(2):
+            m = int(g.integers(lo, hi))
+            n = int(g.integers(1, 160)) * 8 + int(g.integers(0, 8))
+            k = int(g.integers(1, 96)) * 32
+            shapes.append((m, n, k))
+    return shapes
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m,n,k", _linear_sweep_shapes())
+def test_seeded_linear_sweep(fmt, m, n, k):
+    """fp4_quantize_act + fp4_gemm and fp4_linear on seeded shapes over every
+    GEMM path, within the oracle's tolerance at every output."""
+    a = synth.student_t((m, k), 3.0, 1.0, 28, m * 13 + k)
+    w = synth.normal((n, k), 0.02, 28, n * 7 + k)
+    _gemm_case(fmt, a, w, "seeded sweep")
+
+
 @pytest.fixture
 def no_decode_fusion():
     """fp4_linear with 1-32 rows as quantize + GEMM where the fused skinny
