@@ -89,6 +89,8 @@ def lib():
             "fp4_set_nvfp4_tile_mode": (I32, [I32]),
             "fp4_set_large_linear_fusion": (I32, [I32]),
             "fp4_set_decode_linear_fusion": (I32, [I32]),
+            "fp4_set_mid_gemm": (I32, [I32]),
+            "fp4_linear_mid_splits": (I32, [I32, I64, I64, I64]),
             "fp4_status_string": (ctypes.c_char_p, [I32]),
             "fp4_last_error": (ctypes.c_char_p, []),
         }
@@ -218,8 +220,9 @@ def fp4_gemm(a: Fp4Tensor, w: Fp4Tensor, out: torch.Tensor | None = None,
     if out is None:
         out = torch.empty(m, n, dtype=torch.bfloat16, device=a.device)
     nws = L.fp4_gemm_workspace_bytes(a.fmt, m, n, a.k)
-    if workspace is None and nws > 0 and a.layout == CANONICAL:
-        # room for the tiled copy of large canonical activations
+    if workspace is None and nws > 0:
+        # room for the tiled copy of large canonical activations, or for the
+        # mid-size GEMM's partial sums (tiled activations, 33-128 rows)
         workspace = torch.empty(nws, dtype=torch.uint8, device=a.device)
     _check(L.fp4_gemm(ctypes.byref(a.desc), ctypes.byref(w.desc), _ptr(out), out.stride(0),
                       _ptr(workspace), 0 if workspace is None else workspace.numel(),
@@ -313,6 +316,19 @@ def fp4_set_decode_linear_fusion(on: bool) -> bool:
     the skinny GEMM's launch (off by default). Process-wide; returns the
     previous setting."""
     return bool(lib().fp4_set_decode_linear_fusion(int(bool(on))))
+
+
+def fp4_set_mid_gemm(on: bool) -> bool:
+    """Whether the GEMM of 33-128 activation rows runs on the mid-size kernel
+    (four weight tiles per workgroup, K split with an ordered FP32 combine; on
+    by default) or on the skinny kernel. Process-wide; returns the previous
+    setting."""
+    return bool(lib().fp4_set_mid_gemm(int(bool(on))))
+
+
+def fp4_linear_mid_splits(fmt, m: int, n: int, k: int) -> int:
+    """K slices of fp4_linear's mid-size GEMM for this shape (0: another kernel)."""
+    return lib().fp4_linear_mid_splits(_fmt(fmt), m, n, k)
 
 
 NV_TILE_REGISTERS, NV_TILE_LDS = 0, 1

@@ -147,9 +147,11 @@ size_t quant_ws(int32_t fmt) { return base_fmt(fmt) == FP4_NVFP4 ? kQuantScratch
 // Everything fp4_linear keeps in its workspace: the quantizer's scratch (its
 // exchange words persist from call to call) at offset 0 whatever the call's
 // shape, so that one workspace can serve calls of different shapes; then the
-// tensor scale and the activations quantized into the tiled layout.
+// tensor scale, the activations quantized into the tiled layout and, for
+// 33-128 rows, the mid-size GEMM's partial sums (`splits` slices of K).
 struct LinearLayout {
-  size_t codes, scales, ts, scratch, total;
+  size_t codes, scales, ts, scratch, part, total;
+  int splits;
 };
 
 // Bytes of a tiled tensor's scales buffer (with the macro-block scales).
@@ -158,7 +160,21 @@ size_t tiled_scales_bytes(int32_t fmt, int64_t rows, int64_t k) {
   return (size_t)(mp * kp / block_of(base_fmt(fmt))) + (has_mbs(fmt) ? (size_t)(mp * kp / 32) : 0);
 }
 
-LinearLayout linear_layout(int32_t fmt, int64_t m, int64_t k) {
+// Partial sums of the mid-size GEMM take at most kMidPartBytes, and never
+// push a linear that fits the allocation-free entry point's array past it.
+constexpr int64_t kMidPartBytes = 12 << 20;
+int mid_splits(int32_t fmt, int64_t m, int64_t n, int64_t k, size_t other_bytes) {
+  if (has_mbs(fmt)) return 0;
+  const int64_t room = (int64_t)FP4_NOALLOC_SCRATCH_BYTES - (int64_t)other_bytes;
+  const int64_t cap = room >= 0 ? std::min(kMidPartBytes, room) : kMidPartBytes;
+  return gemm_mid_splits(m, n, k, cap);
+}
+
+size_t mid_part_bytes(int splits, int64_t m, int64_t n) {
+  return align256((size_t)splits * (size_t)(m * n) * sizeof(float));
+}
+
+LinearLayout linear_layout(int32_t fmt, int64_t m, int64_t n, int64_t k) {
   LinearLayout L;
   const int64_t mp = round_up(m, 16), kp = k_pad(k);
   size_t off = 0;
@@ -166,6 +182,9 @@ LinearLayout linear_layout(int32_t fmt, int64_t m, int64_t k) {
   L.ts = off; off = align256(off + sizeof(float));
   L.codes = off; off = align256(off + (size_t)(mp * kp / 2));
   L.scales = off; off = align256(off + tiled_scales_bytes(fmt, m, k));
+  L.part = off;
+  L.splits = mid_splits(fmt, m, n, k, off);
+  if (L.splits > 1) off += mid_part_bytes(L.splits, m, n);
   L.total = off;
   return L;
 }
@@ -198,8 +217,10 @@ RetileLayout retile_layout(int32_t fmt, int64_t m, int64_t k) {
   return L;
 }
 
-fp4_status run_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c, int64_t ldc,
-                    hipStream_t stream) {
+// part / splits: the mid-size GEMM's partial-sum buffer and slice count
+// (splits 0: the shape or the caller's workspace does not allow it).
+fp4_status run_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c, int64_t ldc, float *part,
+                    int splits, hipStream_t stream) {
   GemmArgs g;
   g.fmt = base_fmt(a->fmt);
   g.a_tiled = a->layout == FP4_LAYOUT_TILED;
@@ -215,7 +236,10 @@ fp4_status run_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c, int64_t l
   // skinny M: stream W once; large M with tiled activations: LDS-staged
   // tiles; large M with canonical activations (or macro-block scales):
   // direct-load tiles
-  hipError_t e = g.m <= kDecodeMaxM           ? launch_gemm_decode(g, stream)
+  const bool mid = splits > 0 && mid_gemm() && g.a_tiled && !has_mbs(a->fmt) &&
+                   (splits == 1 || part);
+  hipError_t e = mid                          ? launch_gemm_mid(g, splits, part, stream)
+                 : g.m <= kDecodeMaxM           ? launch_gemm_decode(g, stream)
                  : g.a_tiled && !has_mbs(a->fmt) ? launch_gemm_tile(g, 0, stream)
                                               : launch_gemm_prefill(g, stream);
   if (e != hipSuccess) return hip_fail(e, "gemm launch");
@@ -295,7 +319,7 @@ fp4_status linear_run(const void *x_bf16, int64_t m, const fp4_tensor *w,
     if (e != hipSuccess) return hip_fail(e, "fused linear launch");
     return FP4_OK;
   }
-  const LinearLayout L = linear_layout(fmt, m, k);
+  const LinearLayout L = linear_layout(fmt, m, n, k);
   char *ws = (char *)workspace;
   fp4_tensor a;
   a.fmt = fmt;
@@ -343,7 +367,7 @@ fp4_status linear_run(const void *x_bf16, int64_t m, const fp4_tensor *w,
   }
   fp4_status st = run_quant(fmt, 1, x_bf16, m, k, static_scale, &a, ws + L.scratch, stream);
   if (st != FP4_OK) return st;
-  return run_gemm(&a, w, y_bf16, n, stream);
+  return run_gemm(&a, w, y_bf16, n, (float *)(ws + L.part), L.splits, stream);
 }
 
 }  // namespace
@@ -435,9 +459,10 @@ fp4_status fp4_quantize_act(int32_t fmt, const void *a_bf16, int64_t m, int64_t 
 }
 
 size_t fp4_gemm_workspace_bytes(int32_t fmt, int64_t m, int64_t n, int64_t k) {
-  (void)n;
-  if (!valid_fmt(fmt) || m <= 0 || k <= 0) return 0;
-  return retile_layout(fmt, m, k).total;
+  if (!valid_fmt(fmt) || m <= 0 || n <= 0 || k <= 0) return 0;
+  if (m > kDecodeMaxM) return retile_layout(fmt, m, k).total;
+  const int splits = has_mbs(fmt) ? 0 : gemm_mid_splits(m, n, k, kMidPartBytes);
+  return splits > 1 ? mid_part_bytes(splits, m, n) : 0;
 }
 
 fp4_status fp4_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c_bf16, int64_t ldc,
@@ -477,16 +502,21 @@ fp4_status fp4_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c_bf16, int6
                                        (uint8_t *)t.codes, (uint8_t *)t.scales, macro_of(&t),
                                        stream);
     if (e != hipSuccess) return hip_fail(e, "activation re-tiling launch");
-    st = run_gemm(&t, w, c_bf16, ldc, stream);
+    st = run_gemm(&t, w, c_bf16, ldc, nullptr, 0, stream);
     return st == FP4_OK ? ok() : st;
   }
-  st = run_gemm(a, w, c_bf16, ldc, stream);
+  // 33-128 tiled rows: the mid-size GEMM, its partial sums in the workspace
+  // when it is large enough (else the skinny kernel, unless one slice does)
+  int splits = a->layout == FP4_LAYOUT_TILED ? gemm_mid_splits(a->rows, w->rows, a->cols, kMidPartBytes) : 0;
+  if (splits > 1 && (!workspace || workspace_bytes < mid_part_bytes(splits, a->rows, w->rows)))
+    splits = 0;
+  st = run_gemm(a, w, c_bf16, ldc, (float *)workspace, splits, stream);
   return st == FP4_OK ? ok() : st;
 }
 
 size_t fp4_linear_workspace_bytes(int32_t fmt, int64_t m, int64_t n, int64_t k) {
   if (!valid_fmt(fmt) || m <= 0 || n <= 0 || k <= 0) return 0;
-  return linear_layout(fmt, m, k).total;
+  return linear_layout(fmt, m, n, k).total;
 }
 
 fp4_status fp4_linear(const void *x_bf16, int64_t m, const fp4_tensor *w,
@@ -494,7 +524,7 @@ fp4_status fp4_linear(const void *x_bf16, int64_t m, const fp4_tensor *w,
                       size_t workspace_bytes, hipStream_t stream) {
   fp4_status st;
   if ((st = linear_check(x_bf16, m, w, static_scale, y_bf16)) != FP4_OK) return st;
-  const LinearLayout L = linear_layout(w->fmt, m, w->cols);
+  const LinearLayout L = linear_layout(w->fmt, m, w->rows, w->cols);
   if (!workspace || workspace_bytes < L.total)
     return fail(FP4_ERR_WORKSPACE, "workspace needs %zu bytes", L.total);
   if (!aligned16(workspace)) return fail(FP4_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
@@ -507,7 +537,7 @@ fp4_status fp4_linear_noalloc(const void *x_bf16, int64_t m, const fp4_tensor *w
                               const float *static_scale, void *y_bf16, hipStream_t stream) {
   fp4_status st;
   if ((st = linear_check(x_bf16, m, w, static_scale, y_bf16)) != FP4_OK) return st;
-  const LinearLayout L = linear_layout(w->fmt, m, w->cols);
+  const LinearLayout L = linear_layout(w->fmt, m, w->rows, w->cols);
   if (L.total > FP4_NOALLOC_SCRATCH_BYTES)
     return fail(FP4_ERR_WORKSPACE,
                 "this call needs %zu bytes of workspace; the library's device array holds %zu "
@@ -553,10 +583,11 @@ int32_t fp4_linear_launches(int32_t fmt, int64_t m, int64_t n, int64_t k, int32_
   if (use_fused(fmt, m, n, k)) return 1;
   if (linear_fused_decode_ok(base, recipe_of(fmt), m, n, k)) return 1;
   if (linear_fused_large_ok(base, recipe_of(fmt), m, n, k, static_scale != 0)) return 1;
+  const int gemm = mid_gemm() && linear_layout(fmt, m, n, k).splits > 1 ? 2 : 1;
   if (base == FP4_NVFP4 && !static_scale && !quant_fits_small(base, m, k, 1) &&
       !quant_fits_mid(base, recipe_of(fmt), m, k, 1))
-    return 3;
-  return 2;
+    return 2 + gemm;
+  return 1 + gemm;
 }
 
 fp4_status fp4_export_canonical(const fp4_tensor *tiled, fp4_tensor *canonical,
@@ -622,6 +653,16 @@ fp4_status fp4_workspace_flags(const void *workspace, size_t workspace_bytes, ui
 }
 
 uint32_t fp4_set_exchange_spin_limit(uint32_t polls) { return set_exchange_spin_limit(polls); }
+
+int32_t fp4_set_mid_gemm(int32_t on) { return set_mid_gemm(on); }
+
+int32_t fp4_linear_mid_splits(int32_t fmt, int64_t m, int64_t n, int64_t k) {
+  if (!valid_fmt(fmt) || m <= 0 || n <= 0 || k <= 0 || k % block_of(base_fmt(fmt)) != 0) return 0;
+  if (use_fused(fmt, m, n, k) || linear_fused_decode_ok(base_fmt(fmt), recipe_of(fmt), m, n, k) ||
+      !mid_gemm())
+    return 0;
+  return linear_layout(fmt, m, n, k).splits;
+}
 
 int32_t fp4_set_large_linear_fusion(int32_t on) { return set_large_linear_fusion(on); }
 

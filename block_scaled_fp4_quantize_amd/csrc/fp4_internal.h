@@ -116,6 +116,18 @@ struct GemmArgs {
 hipError_t launch_gemm_prefill(const GemmArgs &g, hipStream_t stream);
 hipError_t launch_gemm_decode(const GemmArgs &g, hipStream_t stream);
 
+// GEMM for 33-128 activation rows with tiled activations and no macro-block
+// scales: four weight tiles per workgroup, K split into `splits` slices whose
+// FP32 partial sums go to `part` (splits * m * n floats, unused when splits
+// is 1) and are added in slice order by a second launch.
+// gemm_mid_splits: the slice count for a shape (0: the kernel does not apply),
+// with at most `cap` bytes of partial sums. mid_gemm: whether the GEMM
+// launches use it (1, the default) or the skinny kernel (0).
+int gemm_mid_splits(int64_t m, int64_t n, int64_t k, int64_t cap);
+hipError_t launch_gemm_mid(const GemmArgs &g, int splits, float *part, hipStream_t stream);
+int mid_gemm();
+int set_mid_gemm(int on);
+
 // LDS-staged GEMM for large M; both operands fragment-tiled. cfg selects the
 // workgroup tile (88: 256 x 256, 44: 128 x 128; 0: by shape).
 int gemm_tile_config(int fmt, int64_t m, int64_t n);

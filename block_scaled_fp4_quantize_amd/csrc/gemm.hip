@@ -724,6 +724,180 @@ __global__ __launch_bounds__(64 * NWT) void k_gemm_decode_ring(
   }
 }
 
+// ------------------------------------------------------------ mid-size M
+//
+// 33-128 activation rows (tiled activations, no macro-block scales). The
+// skinny kernels give each 16-row weight tile its own workgroup, so at these
+// sizes every workgroup loads all M activation rows (and, NVFP4, dequantizes
+// them) for 16 output columns: the activation side, not the weight stream,
+// bounds them. Here a workgroup takes kMidTiles consecutive weight tiles (64
+// output columns) for all the rows, over one of S slices of K, and its four
+// waves split the slice's fragments (wave w: fragments kb + w, kb + w + 4,
+// ...), so each activation fragment a wave loads and converts serves four
+// weight tiles. The waves' sums meet in LDS in a fixed order; with S > 1 each
+// workgroup writes its slice's FP32 sums to `part` [S][m][n] and k_mid_sum
+// adds the slices in order, so the result does not depend on timing.
+constexpr int kMidTiles = 4;
+constexpr int kMidWaves = 4;
+
+template <int FMT, int MG>
+__global__ __launch_bounds__(64 * kMidWaves) void k_gemm_mid(
+    const uint8_t *a_codes, const uint8_t *a_sc, const float *__restrict__ a_ts,
+    const uint8_t *w_codes, const uint8_t *w_sc, const float *__restrict__ w_ts, int m, int n,
+    int kt_n, int nt_n, int kps, uint16_t *c, int64_t ldc, float *part) {
+  constexpr int NT = kMidTiles, NW = kMidWaves, D = kRingDepth;
+  constexpr int SFB = FMT == 0 ? 128 : 64;  // scale bytes per fragment
+  constexpr int SLOTS = NT * MG * 4;         // accumulator values per lane
+  __shared__ float red[2][SLOTS][64];
+  const int nt0 = (int)blockIdx.x * NT;
+  const int split = (int)blockIdx.y;
+  const int kb = split * kps, ke = min(kt_n, kb + kps);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int tiles = min(NT, nt_n - nt0);
+  const __amdgpu_buffer_rsrc_t wr = buf_rsrc(w_codes + (int64_t)nt0 * kt_n * kFragCodeBytes,
+                                             (uint32_t)(tiles * kt_n * kFragCodeBytes));
+  const __amdgpu_buffer_rsrc_t wsr = buf_rsrc(w_sc + (int64_t)nt0 * kt_n * SFB,
+                                              (uint32_t)(tiles * kt_n * SFB));
+  const int ag = (m + 15) >> 4;
+  const __amdgpu_buffer_rsrc_t ar = buf_rsrc(a_codes, (uint32_t)(ag * kt_n * kFragCodeBytes));
+  const __amdgpu_buffer_rsrc_t asr = buf_rsrc(a_sc, (uint32_t)(ag * kt_n * SFB));
+  const int lr = lane & 15, lc = lane >> 4;
+
+  v4f acc[NT][MG];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int g = 0; g < MG; ++g) acc[t][g] = v4f{0.f, 0.f, 0.f, 0.f};
+  uint4 wq[D][NT], aq[D][MG];
+  uint32_t ws[D][NT], as[D][MG];
+
+  // Loads that must not happen (fragments past the slice, tiles past n,
+  // activation rows past m) take an offset past every resource's end (each
+  // below 2^31 bytes): they return zero without reading memory.
+  constexpr uint32_t kOut = 0x80000000u;
+  auto issue = [&](int d, int kt) {
+    const bool kin = kt < ke;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint32_t f = (uint32_t)(t * kt_n + kt);
+      const bool in = kin && t < tiles;
+      wq[d][t] = buf_load16(wr, in ? f * kFragCodeBytes + lane * 16 : kOut);
+      ws[d][t] = buf_load_scale<FMT>(wsr, in ? f * SFB + lane * (FMT == 0 ? 2 : 1) : kOut);
+    }
+#pragma unroll
+    for (int g = 0; g < MG; ++g) {
+      const uint32_t f = (uint32_t)(g * kt_n + kt);
+      const bool in = kin && 16 * g + lr < m;
+      aq[d][g] = buf_load16(ar, in ? f * kFragCodeBytes + lane * 16 : kOut);
+      as[d][g] = buf_load_scale<FMT>(asr, in ? f * SFB + lane * (FMT == 0 ? 2 : 1) : kOut);
+    }
+  };
+  auto compute = [&](int d) {
+    if (FMT == 1) {
+#pragma unroll
+      for (int g = 0; g < MG; ++g)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t][g] = mfma_mx(wq[d][t], aq[d][g], acc[t][g], ws[d][t], as[d][g]);
+    } else {
+      // each activation fragment is dequantized once for the NT weight tiles
+      h8v wh[NT][4];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) nv_dequant32(wq[d][t], ws[d][t], wh[t]);
+#pragma unroll
+      for (int g = 0; g < MG; ++g) {
+        h8v ah[4];
+        nv_dequant32(aq[d][g], as[d][g], ah);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t][g] = mfma_nv(wh[t], ah, acc[t][g]);
+      }
+    }
+  };
+
+  const int first = kb + wave;
+  const int J = first < ke ? (ke - 1 - first) / NW + 1 : 0;  // this wave's fragments
+  // (an empty asm statement with a memory clobber between slots keeps the
+  // slots' loads in the order they are consumed, as in the ring kernel)
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    issue(d, first + NW * d);
+    asm volatile("" ::: "memory");
+  }
+  for (int j0 = 0; j0 < J; j0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (j0 + d < J) compute(d);  // wave-uniform; no memory access inside
+      issue(d, first + NW * (j0 + d + D));
+      asm volatile("" ::: "memory");
+    }
+  }
+
+  // waves 2, 3 hand their sums to waves 0, 1; those then to everyone:
+  // value = (sum of waves 0 and 2) + (sum of waves 1 and 3)
+  if (wave >= 2) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int g = 0; g < MG; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave - 2][(t * MG + g) * 4 + r][lane] = acc[t][g][r];
+  }
+  __syncthreads();
+  if (wave < 2) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int g = 0; g < MG; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[t][g][r] += red[wave][(t * MG + g) * 4 + r][lane];
+  }
+  __syncthreads();
+  if (wave < 2) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int g = 0; g < MG; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][(t * MG + g) * 4 + r][lane] = acc[t][g][r];
+  }
+  __syncthreads();
+  // wave w writes weight tile nt0 + w
+  const int t = wave;
+  const int col0 = (nt0 + t) * 16 + 4 * lc;  // output columns col0 .. col0 + 3
+  const Alpha alpha = FMT == 0 ? make_alpha(a_ts[0], w_ts[0]) : Alpha{1.0f, 0};
+#pragma unroll
+  for (int g = 0; g < MG; ++g) {
+    const int row = 16 * g + lr;  // activation row
+    if (row >= m) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = (t * MG + g) * 4 + r;
+      const float v = red[0][i][lane] + red[1][i][lane];
+      const int col = col0 + r;
+      if (col >= n) continue;
+      if (part) part[((int64_t)split * m + row) * n + col] = v;
+      else c[(int64_t)row * ldc + col] = f32_to_bf16_rne(apply_alpha(v, alpha));
+    }
+  }
+}
+
+// The slices' partial sums of k_gemm_mid added in slice order, scaled and
+// rounded: c[row, col] = bf16_RNE(alpha * (((p_0 + p_1) + p_2) + ...)).
+__global__ __launch_bounds__(256) void k_mid_sum(const float *__restrict__ part, int splits, int m,
+                                                 int n, int fmt, const float *__restrict__ a_ts,
+                                                 const float *__restrict__ w_ts, uint16_t *c,
+                                                 int64_t ldc) {
+  const int64_t mn = (int64_t)m * n;
+  const Alpha alpha = fmt == 0 ? make_alpha(a_ts[0], w_ts[0]) : Alpha{1.0f, 0};
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < mn;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    float v = part[i];
+    for (int s = 1; s < splits; ++s) v += part[s * mn + i];
+    const int64_t row = i / n, col = i - row * n;
+    c[row * ldc + col] = f32_to_bf16_rne(apply_alpha(v, alpha));
+  }
+}
+
 // --------------------------------------------------------- fused linear
 //
 // Skinny linear with the activation quantization fused in, for activations
@@ -989,6 +1163,65 @@ hipError_t decode_launch(const GemmArgs &g, DecFused *fz, hipStream_t stream) {
 
 hipError_t launch_gemm_decode(const GemmArgs &g, hipStream_t stream) {
   return decode_launch(g, nullptr, stream);
+}
+
+namespace {
+std::atomic<int> g_mid{1};
+}  // namespace
+
+int mid_gemm() { return g_mid.load(std::memory_order_relaxed); }
+int set_mid_gemm(int on) { return g_mid.exchange(on ? 1 : 0, std::memory_order_relaxed); }
+
+// The slice count: at most one workgroup per CU (a workgroup holds all four
+// SIMDs' registers, so a second round of workgroups costs a whole slice:
+// measured, 270 workgroups for 256 CUs took 1.4x as long as 180), each wave
+// keeping at least one fragment, the partial sums within `cap`. The kernel is
+// used only where every wave then streams at least kMidMinWaveFrags
+// fragments: its fixed costs (the combining launch, the LDS sums, one wave
+// per SIMD waiting on its loads) are paid back only over a long stream. Measured
+// against the skinny kernel (graph replay, 64 and 128 rows): K x N = 17408 x
+// 5120 (46 fragments a slice) 1.4-1.7x faster, 5120 x 17408 (40, one slice)
+// 1.1-1.2x; 5120 x 5120 (14) and every shape of 2880-5760 (at most 12) slower.
+constexpr int kMidMinWaveFrags = 8;
+
+int gemm_mid_splits(int64_t m, int64_t n, int64_t k, int64_t cap) {
+  if (m <= 32 || m > kDecodeMaxM) return 0;
+  const int64_t kt_n = k_pad(k) / kFragK, nt_n = round_up(n, 16) / 16;
+  // 32-bit buffer offsets: the workgroup's weight tiles and all activation groups
+  if (kt_n * kFragCodeBytes * std::max(kMidTiles, 8) >= (int64_t(1) << 31)) return 0;
+  const int64_t ncol = (nt_n + kMidTiles - 1) / kMidTiles;
+  int64_t s = std::max<int64_t>(1, 256 / ncol);
+  s = std::min(s, std::max<int64_t>(1, kt_n / kMidWaves));
+  while (s > 1 && s * m * n * (int64_t)sizeof(float) > cap) --s;
+  if ((kt_n + s - 1) / s < (int64_t)kMidWaves * kMidMinWaveFrags) return 0;
+  return (int)s;
+}
+
+hipError_t launch_gemm_mid(const GemmArgs &g, int splits, float *part, hipStream_t stream) {
+  if (!g.a_tiled || g.w_ms || g.m <= 32 || g.m > kDecodeMaxM || splits < 1 || (splits > 1 && !part))
+    return hipErrorInvalidValue;
+  const int kt_n = (int)(k_pad(g.k) / kFragK);
+  const int nt_n = (int)(round_up(g.n, 16) / 16);
+  const int ncol = (nt_n + kMidTiles - 1) / kMidTiles;
+  const int kps = (kt_n + splits - 1) / splits;
+  float *p = splits > 1 ? part : nullptr;
+  const dim3 grid((unsigned)ncol, (unsigned)splits);
+#define FP4_MID(F, G)                                                                         \
+  hipLaunchKernelGGL((k_gemm_mid<F, G>), grid, dim3(64 * kMidWaves), 0, stream, g.a_codes,   \
+                     g.a_scales, g.a_ts, g.w_codes, g.w_scales, g.w_ts, (int)g.m, (int)g.n, kt_n, \
+                     nt_n, kps, g.c, g.ldc, p)
+  if (g.fmt == 0 && g.m <= 64) FP4_MID(0, 4);
+  else if (g.fmt == 0) FP4_MID(0, 8);
+  else if (g.m <= 64) FP4_MID(1, 4);
+  else FP4_MID(1, 8);
+#undef FP4_MID
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  const int64_t mn = g.m * g.n;
+  const unsigned blocks = (unsigned)std::min<int64_t>(2048, (mn + 255) / 256);
+  hipLaunchKernelGGL(k_mid_sum, dim3(blocks), dim3(256), 0, stream, part, splits, (int)g.m,
+                     (int)g.n, g.fmt, g.a_ts, g.w_ts, g.c, g.ldc);
+  return hipGetLastError();
 }
 
 namespace {

@@ -179,7 +179,9 @@ fp4_status fp4_quantize_act(int32_t fmt, const void *a_bf16, int64_t m, int64_t 
 
 /* Workspace for fp4_gemm: for CANONICAL activations with M > 128, room for a
  * tiled copy of them (then the product runs on the LDS-staged tile kernel);
- * 0 for M <= 128. No zero-filling or persistence is needed. */
+ * for TILED activations with 33 <= M <= 128 on a weight large enough for the
+ * mid-size GEMM (fp4_set_mid_gemm), room for its FP32 partial sums (K split
+ * over workgroups; 0 when the shape takes one slice); otherwise 0. No zero-filling or persistence is needed. */
 size_t fp4_gemm_workspace_bytes(int32_t fmt, int64_t m, int64_t n, int64_t k);
 
 /*
@@ -190,7 +192,10 @@ size_t fp4_gemm_workspace_bytes(int32_t fmt, int64_t m, int64_t n, int64_t k);
  * first copied into the tiled layout in `workspace` when it holds
  * fp4_gemm_workspace_bytes (16-byte aligned); with a smaller or NULL
  * workspace such a product runs on a slower kernel that reads the canonical
- * layout directly. Calls sharing a workspace must not overlap in time.
+ * layout directly. TILED `a` with 33 <= M <= 128 on a large weight runs on
+ * the mid-size kernel (fp4_set_mid_gemm) when the workspace holds
+ * fp4_gemm_workspace_bytes, else on the skinny kernel; the two agree within
+ * the GEMM tolerance. Calls sharing a workspace must not overlap in time.
  * FP4_ERR_SHAPE when M <= 128 with CANONICAL `a` whose M * max(codes pitch,
  * scales pitch) reaches 2^31 bytes (the skinny kernels use 32-bit offsets).
  */
@@ -198,7 +203,8 @@ fp4_status fp4_gemm(const fp4_tensor *a, const fp4_tensor *w, void *c_bf16, int6
                     void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace for fp4_linear: the quantized activations and the quantizer's
- * scratch. Same contract as the quantize workspace: zero-filled before its
+ * scratch (and, for 33-128 rows, the mid-size GEMM's partial sums, at most
+ * 12 MiB, within the allocation-free array where the rest fits). Same contract as the quantize workspace: zero-filled before its
  * first use, left reusable by every call, not shared by overlapping calls.
  * One workspace may serve calls of different shapes (and formats) in
  * sequence when it is at least as large as each call requires: the words that
@@ -267,10 +273,12 @@ fp4_status fp4_linear_w4a16(const void *x_bf16, int64_t m, const fp4_tensor *w, 
  * GEMM (small M * K on the skinny path without rotation or macro-block
  * scales; with fp4_set_decode_linear_fusion(1), M <= 32 without either; with
  * fp4_set_large_linear_fusion(1), M > 128 with a static NVFP4 scale or MXFP4
- * without macro-block scales), 2 for quantize + GEMM, 3 when the quantizer
- * needs a separate reduction launch (NVFP4 activations with a dynamic scale
- * past 16384 fragments of 16 x 128 values, or rotated and past the
- * single-launch quantizer's size). 0 for invalid arguments. */
+ * without macro-block scales), 2 for quantize + GEMM, one more when the
+ * quantizer needs a separate reduction launch (NVFP4 activations with a
+ * dynamic scale past 16384 fragments of 16 x 128 values, or rotated and past
+ * the single-launch quantizer's size), and one more when the mid-size GEMM
+ * (33-128 rows) splits K (its partial sums are added by a launch of their
+ * own). 0 for invalid arguments. */
 int32_t fp4_linear_launches(int32_t fmt, int64_t m, int64_t n, int64_t k, int32_t static_scale);
 
 /*
@@ -310,6 +318,26 @@ int32_t fp4_set_large_linear_fusion(int32_t on);
  * than a launch of its own). Same results either way. Process-wide; returns
  * the previous setting. */
 int32_t fp4_set_decode_linear_fusion(int32_t on);
+
+/* Whether the GEMM of 33-128 activation rows (tiled activations, no
+ * macro-block scales; fp4_linear, and fp4_gemm with a workspace of
+ * fp4_gemm_workspace_bytes) on large weights runs on the mid-size kernel (1,
+ * the default: four weight tiles per workgroup, so each activation fragment is
+ * loaded and converted once per 64 output columns; K split over at most one
+ * workgroup per CU, whose FP32 partial sums a second launch adds in a fixed
+ * order) or on the skinny kernel (0: one 16-row weight tile per workgroup
+ * over the whole K). The mid-size kernel takes a shape only when every wave
+ * streams at least 8 of K's 128-value fragments (about K * N >= 2^26 at
+ * 256 CUs); smaller shapes keep the skinny kernel either way. Results agree
+ * within the GEMM tolerance, not bit for bit (another summation order).
+ * Process-wide; returns the previous setting. */
+int32_t fp4_set_mid_gemm(int32_t on);
+
+/* Test aid: the number of K slices the mid-size GEMM of fp4_linear uses for
+ * this shape under the current switches (1: one launch that writes the
+ * output; more: a combining launch adds the slices), or 0 when fp4_linear
+ * runs another GEMM kernel (or the arguments are invalid). */
+int32_t fp4_linear_mid_splits(int32_t fmt, int64_t m, int64_t n, int64_t k);
 
 /* Where the NVFP4 product on 256 x 256 output tiles (large M) converts codes
  * to exact f16 values: 0 = in the registers of each wave that uses a fragment

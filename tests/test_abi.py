@@ -54,6 +54,55 @@ def test_sizes_and_pitches():
     assert L.fp4_linear_workspace_bytes(fp4.NVFP4, 8, 5120, 5120) > 0
 
 
+def test_mid_gemm_workspace_and_launches():
+    """33-128 rows on large weights: the mid-size GEMM, at most one workgroup
+    per CU (64 output columns each) and K split so that each of its four waves
+    streams at least 8 fragments; its FP32 partial sums (splits * M * N
+    floats, at most 12 MiB) sit in the GEMM and linear workspaces, and a
+    combining launch adds them. Smaller shapes keep the skinny kernel."""
+    L = fp4.lib()
+    mib = 1 << 20
+    # K x N = 17408 x 5120: 80 column groups -> 3 slices of 46 fragments
+    assert L.fp4_gemm_workspace_bytes(fp4.NVFP4, 128, 5120, 17408) == 3 * 128 * 5120 * 4
+    assert L.fp4_gemm_workspace_bytes(fp4.MXFP4, 64, 5120, 17408) == 3 * 64 * 5120 * 4
+    # K x N = 5120 x 17408: 272 column groups -> one slice of 40 fragments
+    assert L.fp4_gemm_workspace_bytes(fp4.NVFP4, 128, 17408, 5120) == 0
+    # macro-block scales and 32 rows keep the skinny kernel
+    assert L.fp4_gemm_workspace_bytes(fp4.MXFP4 | fp4.MX_MBS, 128, 5120, 17408) == 0
+    assert L.fp4_gemm_workspace_bytes(fp4.NVFP4, 32, 5120, 17408) == 0
+    # which GEMM fp4_linear runs: slices of the mid-size kernel, 0 for another
+    assert L.fp4_linear_mid_splits(fp4.NVFP4, 128, 5120, 17408) == 3
+    assert L.fp4_linear_mid_splits(fp4.MXFP4, 65, 17408, 5120) == 1
+    assert L.fp4_linear_mid_splits(fp4.NVFP4, 128, 5760, 2880) == 0
+    assert L.fp4_linear_mid_splits(fp4.NVFP4, 32, 5120, 17408) == 0
+    assert L.fp4_linear_mid_splits(fp4.NVFP4, 129, 5120, 17408) == 0
+    assert L.fp4_linear_mid_splits(fp4.MXFP4 | fp4.MX_MBS, 128, 5120, 17408) == 0
+    assert L.fp4_linear_mid_splits(fp4.NVFP4, 128, 5120, 17400) == 0   # K % 16
+    prev = L.fp4_set_mid_gemm(0)
+    try:
+        assert L.fp4_linear_mid_splits(fp4.NVFP4, 128, 5120, 17408) == 0
+    finally:
+        L.fp4_set_mid_gemm(prev)
+    # (K, N) -> fp4_linear's launches: quantize, GEMM, and the combine for 3 slices
+    mid = {(5120, 17408): 2, (17408, 5120): 3}
+    for fmt in (fp4.NVFP4, fp4.MXFP4):
+        for m in (33, 64, 128):
+            for (k, n) in ((2880, 4096), (2880, 512), (4096, 2880), (2880, 5760), (5760, 2880),
+                           (5120, 5120), (5120, 17408), (17408, 5120)):
+                g = L.fp4_gemm_workspace_bytes(fmt, m, n, k)
+                assert g <= 12 * mib
+                lin = L.fp4_linear_workspace_bytes(fmt, m, n, k)
+                assert lin >= g
+                # every such linear still fits the allocation-free array
+                assert lin <= fp4.NOALLOC_SCRATCH_BYTES
+                assert L.fp4_linear_launches(fmt, m, n, k, 0) == mid.get((k, n), 2)
+                prev = L.fp4_set_mid_gemm(0)
+                try:
+                    assert L.fp4_linear_launches(fmt, m, n, k, 0) == 2
+                finally:
+                    assert L.fp4_set_mid_gemm(prev) == 0
+
+
 def test_tensor_init_fills_pitches():
     L = fp4.lib()
     t = fp4.fp4_tensor()
