@@ -68,6 +68,9 @@ def parse():
     p.add_argument("--fuse-decode", action="store_true",
                    help="1-32 rows: quantize the activations inside the skinny GEMM's launch "
                         "instead of in a launch of their own")
+    p.add_argument("--no-mid", action="store_true",
+                   help="17-128 rows on large weights: run the GEMM on the skinny kernel instead of "
+                        "the mid-size kernel")
     p.add_argument("--static-scale", type=float, default=0.0,
                    help="NVFP4: quantize the activations with this static tensor scale instead of "
                         "their dynamic one")
@@ -115,8 +118,8 @@ def gemm_bytes(m, k, n, fmt):
     return n * q + m * q + 2 * m * n
 
 
-DOMINANT = ("k_gemm_decode", "k_linear_decode", "k_gemm_tile", "k_gemm_prefill", "k_w4a16_decode",
-            "k_w4a16_tile")
+DOMINANT = ("k_gemm_decode", "k_linear_decode", "k_gemm_mid", "k_gemm_tile", "k_gemm_prefill",
+            "k_w4a16_decode", "k_w4a16_tile")
 
 
 SPEC_SCLK_MHZ = 2400.0             # MI355X peak engine clock, at which the peaks are quoted
@@ -398,6 +401,8 @@ def main():
         fp4.fp4_set_large_linear_fusion(True)
     if args.fuse_decode:
         fp4.fp4_set_decode_linear_fusion(True)
+    if args.no_mid:
+        fp4.fp4_set_mid_gemm(False)
     fmt = fp4.FORMATS[args.fmt]
     # qfmt: the format value with the recipe flags, given to every library call
     qfmt = fp4._fmt(args.fmt + ("+" + args.recipe if args.recipe else ""))
@@ -608,15 +613,21 @@ def main():
         else:
             # the activation layout fp4_linear uses internally (fragment-tiled)
             qa = fp4.fp4_quantize_act(xs[cfg], qfmt, layout=fp4.TILED)
-            if m <= 128:
+            mg = 1 if m <= 16 else 2 if m <= 32 else 4 if m <= 64 else 8
+            splits = fp4.fp4_linear_mid_splits(qfmt, m, n, k) if m <= 128 else 0
+            if splits:   # the mid-size GEMM (and its slice-combining launch)
+                name = "k_gemm_mid<%s,MG=%d>%s" % (args.fmt, mg, "+k_mid_sum" if splits > 1 else "")
+            elif m <= 128:
                 name = "%s<%s,MG=%d>" % ("k_gemm_decode_ring" if fmt == 0 else "k_gemm_decode",
-                                         args.fmt, 1 if m <= 16 else 2 if m <= 32 else 4 if m <= 64 else 8)
+                                         args.fmt, mg)
             elif "mbs" in args.recipe:   # macro-block scales: direct-load tiles
                 name = "k_gemm_prefill<%s,MB>" % args.fmt
             else:   # LDS-staged tiles; 256 x 256 when that fills the 256 CUs
                 big = -(-m // 256) * -(-n // 256) >= 256
                 name = "k_gemm_tile<%s,%s>" % (args.fmt, "256x256" if big else "128x128")
-            us = graph_time(lambda r: fp4.fp4_gemm(qa, wl[r % nc], out=outs[cfg]), reps)
+            gws = torch.empty(max(16, fp4.lib().fp4_gemm_workspace_bytes(qfmt, m, n, k)),
+                              dtype=torch.uint8, device=dev)
+            us = graph_time(lambda r: fp4.fp4_gemm(qa, wl[r % nc], out=outs[cfg], workspace=gws), reps)
             nbytes = w_bytes + m * (k // 2 + k // bs) + 2 * m * n  # W + FP4 A + bf16 C
             del qa
         d = kern.setdefault(name, {"launches": 0, "us": 0.0, "bytes": 0.0, "flops": 0.0})

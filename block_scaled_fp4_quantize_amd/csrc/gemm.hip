@@ -1183,9 +1183,14 @@ int set_mid_gemm(int on) { return g_mid.exchange(on ? 1 : 0, std::memory_order_r
 // 5120 (46 fragments a slice) 1.4-1.7x faster, 5120 x 17408 (40, one slice)
 // 1.1-1.2x; 5120 x 5120 (14) and every shape of 2880-5760 (at most 12) slower.
 constexpr int kMidMinWaveFrags = 8;
+// Below 33 rows the skinny kernel already takes two weight tiles per
+// workgroup for 17-32 rows; a two-group instance of this kernel measured
+// 0.91-0.93x there on K x N = 5120 x 17408 and 1.0-1.13x on 17408 x 5120
+// (the decode benchmark within 1.5% either way), so it is not used.
+constexpr int kMidMinM = 33;
 
 int gemm_mid_splits(int64_t m, int64_t n, int64_t k, int64_t cap) {
-  if (m <= 32 || m > kDecodeMaxM) return 0;
+  if (m < kMidMinM || m > kDecodeMaxM) return 0;
   const int64_t kt_n = k_pad(k) / kFragK, nt_n = round_up(n, 16) / 16;
   // 32-bit buffer offsets: the workgroup's weight tiles and all activation groups
   if (kt_n * kFragCodeBytes * std::max(kMidTiles, 8) >= (int64_t(1) << 31)) return 0;
@@ -1198,7 +1203,7 @@ int gemm_mid_splits(int64_t m, int64_t n, int64_t k, int64_t cap) {
 }
 
 hipError_t launch_gemm_mid(const GemmArgs &g, int splits, float *part, hipStream_t stream) {
-  if (!g.a_tiled || g.w_ms || g.m <= 32 || g.m > kDecodeMaxM || splits < 1 || (splits > 1 && !part))
+  if (!g.a_tiled || g.w_ms || g.m < kMidMinM || g.m > kDecodeMaxM || splits < 1 || (splits > 1 && !part))
     return hipErrorInvalidValue;
   const int kt_n = (int)(k_pad(g.k) / kFragK);
   const int nt_n = (int)(round_up(g.n, 16) / 16);
