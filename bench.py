@@ -625,11 +625,11 @@ def main():
             else:   # LDS-staged tiles; 256 x 256 when that fills the 256 CUs
                 big = -(-m // 256) * -(-n // 256) >= 256
                 name = "k_gemm_tile<%s,%s>" % (args.fmt, "256x256" if big else "128x128")
-            gws = torch.empty(max(16, fp4.lib().fp4_gemm_workspace_bytes(qfmt, m, n, k)),
-                              dtype=torch.uint8, device=dev)
-            us = graph_time(lambda r: fp4.fp4_gemm(qa, wl[r % nc], out=outs[cfg], workspace=gws), reps)
+            part_ws = torch.empty(max(16, fp4.lib().fp4_gemm_workspace_bytes(qfmt, m, n, k)),
+                                  dtype=torch.uint8, device=dev)
+            us = graph_time(lambda r: fp4.fp4_gemm(qa, wl[r % nc], out=outs[cfg], workspace=part_ws), reps)
             nbytes = w_bytes + m * (k // 2 + k // bs) + 2 * m * n  # W + FP4 A + bf16 C
-            del qa
+            del qa, part_ws
         d = kern.setdefault(name, {"launches": 0, "us": 0.0, "bytes": 0.0, "flops": 0.0})
         d["launches"] += 1
         d["us"] += us
