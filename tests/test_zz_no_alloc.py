@@ -30,14 +30,17 @@ def _noalloc(x, wq, out, static=None):
 
 # (m, k, n) pairs: first call, then a smaller one. NVFP4 dynamic at M = 32
 # takes the quantizer whose maximum exchange keeps words in the array; M = 300
-# the tile GEMM; M = 2 the fused single launch (no workspace use).
+# the tile GEMM; M = 2 the fused single launch (no workspace use); M = 97 and
+# 65 on large weights the mid-size GEMM (three slices of K with their partial
+# sums in the array, then one slice).
 PAIRS = [((32, 5120, 2048), (8, 2880, 512)),
          ((300, 2880, 1024), (40, 1024, 640)),
-         ((16, 4096, 4096), (2, 2880, 520))]
+         ((16, 4096, 4096), (2, 2880, 520)),
+         ((97, 17504, 4100), (65, 5120, 17408))]
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
-@pytest.mark.parametrize("pair", PAIRS, ids=["decode", "tile", "fused"])
+@pytest.mark.parametrize("pair", PAIRS, ids=["decode", "tile", "fused", "mid"])
 @pytest.mark.parametrize("static", [False, True])
 def test_noalloc_matches_linear(fmt, pair, static):
     if static and fmt == "mxfp4":
@@ -48,6 +51,8 @@ def test_noalloc_matches_linear(fmt, pair, static):
         a = synth.normal((m, k), 1.0, 90 + i, m * 7 + k)
         w = synth.normal((n, k), 0.02, 91 + i, n * 5 + k)
         wq = fp4.fp4_quantize_weight(to_dev(w), f)
+        if pair == PAIRS[3]:
+            assert fp4.fp4_linear_mid_splits(f, m, n, k) == (3 if i == 0 else 1)
         x = to_dev(a)
         st_val = float(np.float32(0.0125))
         st = torch.tensor([st_val], dtype=torch.float32, device="cuda") if static else None
