@@ -382,7 +382,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path).", file=sys.stderr)
+              "(the library has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
