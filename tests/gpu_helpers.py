@@ -55,3 +55,18 @@ def assert_gemm_close(c_gpu: np.ndarray, c_ref: np.ndarray, l_ref: np.ndarray, w
         raise AssertionError(
             f"{what}: {bad.sum()} of {bad.size} outputs outside tolerance; first at {tuple(idx)}: "
             f"gpu {c_gpu[tuple(idx)]!r} ref {c_ref[tuple(idx)]!r} tol {tol[tuple(idx)]!r}")
+
+
+def mid_rule(m, n, k, cap=12 << 20):
+    """The slice count the mid-size kernel takes a shape with, restated: at
+    most one workgroup of four weight tiles per CU (256), at least four
+    fragments of K a slice, partial sums within `cap`, and used only with at
+    least 32 fragments a slice (8 a wave); 0 when it does not apply."""
+    if not 33 <= m <= 128:
+        return 0
+    kt, nt = -(-k // 128), -(-n // 16)
+    ncol = -(-nt // 4)
+    s = min(max(1, 256 // ncol), max(1, kt // 4))
+    while s > 1 and s * m * n * 4 > cap:
+        s -= 1
+    return s if -(-kt // s) >= 32 else 0

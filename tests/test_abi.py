@@ -103,6 +103,20 @@ def test_mid_gemm_workspace_and_launches():
                     assert L.fp4_set_mid_gemm(prev) == 0
 
 
+def test_mid_gemm_rule_on_seeded_shapes():
+    """The library's choice of the mid-size GEMM and its slice count equal the
+    rule restated in the tests, on 2000 seeded shapes of 1-200 rows."""
+    import numpy as np
+    from tests.gpu_helpers import mid_rule
+    L = fp4.lib()
+    g = np.random.default_rng(7)
+    for _ in range(2000):
+        m, n, k = int(g.integers(1, 201)), int(g.integers(1, 40000)), int(g.integers(1, 700)) * 32
+        want = mid_rule(m, n, k)
+        for f in (fp4.NVFP4, fp4.MXFP4):
+            assert L.fp4_linear_mid_splits(f, m, n, k) == want, (f, m, n, k)
+
+
 def test_tensor_init_fills_pitches():
     L = fp4.lib()
     t = fp4.fp4_tensor()

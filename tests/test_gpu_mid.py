@@ -10,7 +10,7 @@ import torch
 import block_scaled_fp4_quantize_amd as fp4
 import oracle
 import synth
-from tests.gpu_helpers import F, assert_gemm_close, bf16_out_to_f64, to_dev
+from tests.gpu_helpers import F, assert_gemm_close, bf16_out_to_f64, mid_rule, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -169,3 +169,35 @@ def test_mid_gemm_small_workspace_falls_back():
     c_ref, l_ref = oracle.gemm_sampled(qa_ref, qw_ref, rows, cols)
     assert_gemm_close(bf16_out_to_f64(c)[rows, cols], c_ref, l_ref, "skinny fallback")
     assert_gemm_close(bf16_out_to_f64(full)[rows, cols], c_ref, l_ref, "mid")
+
+
+def _mid_sweep_shapes():
+    """Seeded (M, N, K) that the mid-size kernel takes: 33-128 rows, ragged
+    N, K a multiple of 32, 64-100 M weight values."""
+    g = np.random.default_rng(20261205)
+    shapes = []
+    while len(shapes) < 6:
+        m = int(g.integers(33, 129))
+        n = int(g.integers(3000, 17500))
+        k = int(g.integers(64_000_000 // n, 100_000_000 // n)) // 32 * 32
+        if mid_rule(m, n, k):
+            shapes.append((m, n, k))
+    return shapes
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m,n,k", _mid_sweep_shapes())
+def test_mid_seeded_sweep(fmt, m, n, k):
+    """The library's slice count equals the restated rule; 2048 sampled
+    outputs of fp4_linear within the oracle's tolerance."""
+    f = F[fmt]
+    s = mid_rule(m, n, k)
+    print(f"[mid-sweep] fmt={fmt} m={m} n={n} k={k} splits={s}", flush=True)
+    assert _splits(m, n, k, f) == s
+    a = synth.student_t((m, k), 3.0, 1.0, 29, m * 13 + k)
+    w = synth.normal((n, k), 0.02, 29, n * 7 + k)
+    qa_ref, qw_ref = oracle.quantize(f, a), oracle.quantize(f, w)
+    rows, cols = _sample(m, n, m * 3 + k)
+    c_ref, l_ref = oracle.gemm_sampled(qa_ref, qw_ref, rows, cols)
+    y = fp4.fp4_linear(to_dev(a), fp4.fp4_quantize_weight(to_dev(w), f))
+    assert_gemm_close(bf16_out_to_f64(y)[rows, cols], c_ref, l_ref, f"mid sweep {m}x{n}x{k}")
