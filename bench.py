@@ -10,19 +10,22 @@ Other workloads (--workload): square4096, square8192 (the rest of the square
 sweep), decode (M in {1, 8, 32} x (K, N) in {(5120, 5120), (5120, 17408),
 (17408, 5120)}: nine calls per step, each weight in enough copies that every
 shape's copies exceed 768 MB and consecutive calls never reuse one, so the
-weight stream comes from HBM rather than the 256 MB Infinity Cache), prefill
-(a Llama-style 3B block at M = 4096), single (A[16,256] x W[256,256]) and
-forward (a synthetic 24-layer forward at M = 1, 8, 32, 128).
+weight stream comes from HBM rather than the 256 MB Infinity Cache), mid (M in
+{64, 128} on the two large decode weights, the mid-size GEMM's regime, weights
+rotated like decode's), prefill (a Llama-style 3B block at M = 4096), single
+(A[16,256] x W[256,256]) and forward (a synthetic 24-layer forward at M = 1,
+8, 32, 128).
 
 Prints one JSON line: throughput incl. activation quantization (TFLOP/s), a
 roofline entry for the dominant kernel (square/prefill: the tile GEMM against
 the FP4 matrix peak, NVFP4 also against the f16 ceiling its exact products run
-at; decode: the skinny GEMM against HBM bandwidth; algorithmic work per launch
+at; decode and mid: the skinny or mid-size GEMM against HBM bandwidth;
+algorithmic work per launch
 over its average duration, timed with HIP events on the launch stream) and the
 CPU oracle timed on a bounded sample of the same work on every host core.
 
     python bench.py [--steps K] [--warmup W] [--fmt nvfp4|mxfp4]
-                    [--workload square16384|square8192|square4096|decode|prefill|single|forward]
+                    [--workload square16384|square8192|square4096|decode|mid|prefill|single|forward]
 """
 from __future__ import annotations
 
@@ -41,7 +44,7 @@ FP4_PEAK_TFLOPS = 10100.0          # dense FP4 MFMA, published
 F16_PEAK_TFLOPS = 2500.0           # dense f16/bf16 MFMA, published
 METRIC = "W4A4 NVFP4 GEMM TFLOPS incl. act-quant; % FP4 MFMA peak / % HBM BW"
 ROTATE_BYTES = 768 << 20           # bytes of one shape's weight copies (decode rotation)
-WORKLOADS = ["square16384", "square8192", "square4096", "decode", "prefill", "single", "forward"]
+WORKLOADS = ["square16384", "square8192", "square4096", "decode", "mid", "prefill", "single", "forward"]
 
 
 def parse():
@@ -96,11 +99,20 @@ def parse():
     return p.parse_args()
 
 
+# 33-128 activation rows on the decode shapes whose weights are large enough
+# for the mid-size GEMM (K x N = 5120 x 17408 and 17408 x 5120)
+MID_SHAPES = [(5120, 17408), (17408, 5120)]
+MID_M = [64, 128]
+
+
 def workload_configs(name):
     import synth
     if name == "decode":
         return [(m, k, n) for (k, n) in synth.DECODE_SHAPES for m in synth.DECODE_M], \
             "decode-shaped W4A4 linear, M in {1,8,32} x (K,N) in {(5120,5120),(5120,17408),(17408,5120)}"
+    if name == "mid":
+        return [(m, k, n) for (k, n) in MID_SHAPES for m in MID_M], \
+            "mid-size W4A4 linear, M in {64,128} x (K,N) in {(5120,17408),(17408,5120)}"
     if name == "prefill":
         return [(synth.PREFILL_M, k, n) for (k, n) in synth.PREFILL_LAYERS.values()], \
             "prefill-shaped W4A4 GEMMs of a Llama-style 3B block, M=4096"
@@ -427,7 +439,7 @@ def main():
     # through its copies in the same number of steps (`cycle`), so a graph of
     # `cycle` steps (or a multiple) leaves each copy's reuse distance intact
     # across replays.
-    if args.workload == "decode":
+    if args.workload in ("decode", "mid"):
         cycle = max(-(-ROTATE_BYTES // (shape_bytes[kn] * uses[kn])) for kn in shapes)
         copies = {kn: cycle * uses[kn] for kn in shapes}
     else:
@@ -435,7 +447,7 @@ def main():
     weights, w_host, a_host = {}, {}, {}
     layer_of = {kn: name for name, kn in synth.PREFILL_LAYERS.items()}
     for (k, n) in shapes:
-        if args.workload == "decode":
+        if args.workload in ("decode", "mid"):
             w_bits = synth.decode_inputs(1, k, n, seed=0)[1]
         elif args.workload == "prefill":
             w_bits = synth.prefill_inputs(layer_of[(k, n)], seed=0, m=16)[1]
@@ -449,7 +461,7 @@ def main():
         del w_dev
     xs, outs, wss = {}, {}, {}
     for (m, k, n) in configs:
-        if args.workload == "decode":
+        if args.workload in ("decode", "mid"):
             a_bits = synth.normal((m, k), 1.0, 0, 2 * k + 1)   # the activation decode_inputs draws
         elif args.workload == "prefill":
             a_bits = synth.prefill_inputs(layer_of[(k, n)], seed=0, m=m)[0]
@@ -641,7 +653,7 @@ def main():
                         "linear_us": round(lin_us, 3), "weight_copies": nc})
     tot_us = sum(d["us"] for d in kern.values())
     tot_launch = sum(d["launches"] for d in kern.values())
-    if args.workload == "decode":
+    if args.workload in ("decode", "mid"):
         achieved = sum(d["bytes"] for d in kern.values()) / (tot_us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
