@@ -34,3 +34,17 @@ def test_stored_counter_summaries_parse():
         assert len(rec["src_hash"]) == 16, name
         found += 1
     assert found >= 10
+
+
+def test_mid_workload_takes_the_mid_size_gemm():
+    """Every call of the benchmark's `mid` workload is a shape the mid-size
+    GEMM takes (by the rule restated in the tests), so the workload measures
+    that kernel; none of the decode workload's calls is."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from tests.gpu_helpers import mid_rule
+    mid, _ = bench.workload_configs("mid")
+    assert len(mid) == 4 and all(mid_rule(m, n, k) > 0 for (m, k, n) in mid)
+    decode, _ = bench.workload_configs("decode")
+    assert all(mid_rule(m, n, k) == 0 for (m, k, n) in decode)
+
